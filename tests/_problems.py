@@ -1,0 +1,25 @@
+"""Shared test helpers: build oracle problems from the seeded workloads.
+
+The oracle quantizes the cache itself from the workload's raw inputs; no
+oracle input ever comes from the GPU library.
+"""
+import numpy as np
+
+from bit_kv_cache_03_amd import workloads as W
+
+
+def as_bf16(x):
+    return x if x.dtype == np.uint16 else W.bf16_bits(x)
+
+
+def oracle_caches(orc, w, data):
+    kc = orc.quantize(data["kc"], w.kbits, w.group)
+    vc = orc.quantize(data["vc"], w.vbits, w.group)
+    return kc, vc
+
+
+def oracle_problem(orc, w, corr="taylor", data=None, scale=0.0, caches=None):
+    data = W.generate(w) if data is None else data
+    kc, vc = oracle_caches(orc, w, data) if caches is None else caches
+    return orc.Problem(as_bf16(data["q"]), as_bf16(data["k"]), as_bf16(data["v"]), kc, vc,
+                       w.Nc, w.kbits, w.vbits, w.group, scale=scale, corr=corr)

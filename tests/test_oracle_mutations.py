@@ -1,0 +1,82 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each case compiles a copy of the oracle's C source with one plausible mistake
+(a dropped term, a wrong constant, a wrong index, a wrong sign), loads it in
+place of the real oracle, and runs the pins expected to catch it.  At least
+one of them must fail.  Everything runs on the CPU.
+"""
+import importlib
+import os
+
+import pytest
+
+import oracle
+
+# (name, text in kvq_oracle.c, replacement, [(test module, test function, kwargs)])
+MUTANTS = [
+    ("taylor_constant", "return tau * tau / 24.0 * b;", "return tau * tau / 12.0 * b;",
+     [("test_oracle_bias", "test_taylor_exact_sandwich", {}),
+      ("test_oracle_bias", "test_monte_carlo_tiny_workload", {})]),
+    ("taylor_drops_tau", "return tau * tau / 24.0 * b;", "return tau / 24.0 * b;",
+     [("test_oracle_bias", "test_taylor_exact_sandwich", {})]),
+    ("bias_sign", "s -= (a->corr == 1)", "s += (a->corr == 1)",
+     [("test_oracle_attention", "test_matches_library_sdpa", {"corr": "taylor", "wi": 0}),
+      ("test_oracle_attention", "test_current_chunk_mass_never_drops", {"corr": "taylor"})]),
+    ("exact_missing_half", "(double)step[c / group] / 2.0);", "(double)step[c / group]);",
+     [("test_oracle_bias", "test_monte_carlo_tiny_workload", {})]),
+    ("exact_wrong_group", "(double)step[c / group] / 2.0);", "(double)step[c % (d / group)] / 2.0);",
+     [("test_oracle_bias", "test_monte_carlo_two_groups", {})]),
+    ("taylor_wrong_group",
+     "for (int32_t c = g * group; c < (g + 1) * group; ++c) qn += q[c] * q[c];",
+     "for (int32_t c = g; c < d; c += d / group) qn += q[c] * q[c];",
+     [("test_oracle_bias", "test_monte_carlo_two_groups", {})]),
+    ("series_coefficient", "-1.0 / 180.0", "-1.0 / 120.0",
+     [("test_oracle_bias", "test_logsinhc_series_and_branches", {})]),
+    ("asymptote_sign", "log1p(-exp(-2.0 * a))", "log1p(exp(-2.0 * a))",
+     [("test_oracle_bias", "test_logsinhc_library_routine", {})]),
+    ("round_toward_zero", "float r = rintf(t);", "float r = truncf(t);",
+     [("test_oracle_quantizer", "test_bruteforce_nearest_grid_point", {"bits": 2, "src": "f32"})]),
+    ("step_divisor", "float step = range / (float)top;", "float step = range / (float)(top + 1);",
+     [("test_oracle_quantizer", "test_error_bound_and_extreme_codes", {"wname": "tiny_d64_int2"})]),
+    ("pack_msb_first", "out[bit / 8] |= (uint8_t)(c[k] << (bit % 8));",
+     "out[bit / 8] |= (uint8_t)(c[k] << (8 - bits - bit % 8));",
+     [("test_oracle_quantizer", "test_pack_unpack_roundtrip", {})]),
+    ("zero_sign_not_canonical", "mn = mn + 0.0f; /* canonical zero sign */", "",
+     [("test_oracle_quantizer", "test_adversarial_groups", {})]),
+    ("dequant_offset", "out[r * d + k] = (double)zero[r * ng + g] +",
+     "out[r * d + k] = (double)zero[r * ng + g] + 0.5 * (double)step[r * ng + g] +",
+     [("test_oracle_quantizer", "test_error_bound_and_extreme_codes", {"wname": "h24_int4_cache16k"})]),
+    ("gqa_mapping", "rc->hk = rc->h / (a->Hq / a->Hkv);", "rc->hk = rc->h % a->Hkv;",
+     [("test_oracle_attention", "test_matches_library_sdpa", {"corr": "off", "wi": 1})]),
+    ("default_scale", "return scale > 0.0 ? scale : 1.0 / sqrt((double)d);",
+     "return scale > 0.0 ? scale : 1.0 / (double)d;",
+     [("test_oracle_attention", "test_matches_library_sdpa", {"corr": "off", "wi": 0})]),
+    ("online_no_rescale", "      l *= alpha;\n", "",
+     [("test_oracle_attention", "test_online_matches_brute_force", {"corr": "off"})]),
+    ("value_not_dequantized_zero",
+     "v[c] = (double)a->vc_zero[base * ng + g] + ", "v[c] = ",
+     [("test_oracle_attention", "test_matches_library_sdpa", {"corr": "off", "wi": 2})]),
+]
+
+
+@pytest.mark.parametrize("name,find,repl,pins", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(orc, tmp_path, name, find, repl, pins):
+    with open(oracle._SRC) as f:
+        src = f.read()
+    assert src.count(find) == 1, f"mutation site for {name} not unique"
+    path = os.path.join(str(tmp_path), "mutant.c")
+    with open(path, "w") as f:
+        f.write(src.replace(find, repl))
+    so = oracle.compile_source(path, os.path.join(str(tmp_path), "libmutant.so"))
+    good = oracle._lib
+    oracle._lib = oracle._load(so)
+    caught = []
+    try:
+        for mod, fn, kw in pins:
+            try:
+                getattr(importlib.import_module(mod), fn)(orc=oracle, **kw)
+            except (AssertionError, ValueError):
+                caught.append(fn)
+    finally:
+        oracle._lib = good
+    assert caught, f"no pin caught the planted mistake {name}"
