@@ -1,0 +1,245 @@
+"""Benchmark of the corrected INT2/INT4 KV-cache attention hot path on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--corr taylor]
+
+One step = the whole hot path over one chunk of synthetic input, inputs
+already resident in HBM:
+  - kv_attention_corrected: the current chunk's queries against the Nc
+    cached (INT2/INT4, dequantised in-kernel) tokens and the bf16 current
+    chunk, Jensen-bias correction on cached scores, one online softmax;
+  - kv_quantize of the finished chunk's K and V, appended to the cache at
+    rows [Nc, Nc + Ncur) (rows the attention of this step does not read,
+    so every step does identical work).
+Prints ONE JSON line.  `value` is cached-key tokens x queries per second of
+whole steps; the attention kernel's own duration (HIP events on the stream
+it runs on) gives the roofline figure.  The CPU oracle, timed on a bounded
+sample of the same workload on this host's cores, is the `cpu_baseline`.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from bit_kv_cache_03_amd import workloads as W  # noqa: E402
+
+DEFAULT_WORKLOAD = "h24_int4_cache16k"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "cached-key tokens\u00b7queries/s (TFLOP/s eff.) and packed-KV HBM GB/s vs roofline"
+KERNEL_SOURCES = [os.path.join(ROOT, "bit_kv_cache_03_amd", "csrc", f) for f in ("attention.hip", "kvq_api.cpp", "kvq_internal.h")]
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def packed_bytes(w) -> int:
+    """Algorithmic bytes of the packed cache read by one attention call:
+    codes of K and V plus fp32 step and zero of both, over Nc tokens."""
+    per_tok = w.d * (w.kbits + w.vbits) // 8 + 2 * 2 * (w.d // w.group) * 4
+    return w.B * w.Hkv * w.Nc * per_tok
+
+
+def attention_flops(w) -> float:
+    """Algorithmic flops: Q K^T and P V over both segments (4 d per pair)."""
+    return 4.0 * w.d * w.B * w.Hq * w.Nq * (w.Nc + w.Ncur)
+
+
+def traffic_from_profiles(w, sha: str):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    runs, if they were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_sha") != sha:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, data, corr: str, target_s: float = 12.0):
+    """The oracle as it stands, on a bounded sample of query rows (all heads,
+    rows spread over the chunk), with the quantize of the chunk prorated."""
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    kc = oracle.quantize(data["kc"], w.kbits, w.group)
+    vc = oracle.quantize(data["vc"], w.vbits, w.group)
+    qb = lambda x: x if x.dtype == np.uint16 else W.bf16_bits(x)
+    prob = oracle.Problem(qb(data["q"]), qb(data["k"]), qb(data["v"]), kc, vc, w.Nc, w.kbits, w.vbits,
+                          w.group, corr=corr)
+    total = prob.rows_total()
+    t0 = time.perf_counter()
+    oracle.quantize(data["k"], w.kbits, w.group)
+    oracle.quantize(data["v"], w.vbits, w.group)
+    t_quant = time.perf_counter() - t0
+    # calibrate, then size the sample for about target_s seconds
+    cal = np.linspace(0, total - 1, num=max(threads, 16)).astype(np.int64)
+    t0 = time.perf_counter()
+    prob.attention(rows=cal, threads=threads)
+    per_row = (time.perf_counter() - t0) / cal.size
+    n = int(min(total, max(cal.size, target_s / max(per_row, 1e-9))))
+    rows = np.linspace(0, total - 1, num=n).astype(np.int64)
+    t0 = time.perf_counter()
+    prob.attention(rows=rows, threads=threads)
+    t_rows = time.perf_counter() - t0
+    t = t_rows + t_quant * n / total
+    return {"value": n * w.Nc / t, "unit": "cached-key tokens·queries/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n} of {total} query rows (every {total / n:.1f}th, all heads) of {w.name}, "
+                      f"fp64 oracle attention with {corr} correction over all {w.Nc}+{w.Ncur} keys, "
+                      f"plus the chunk's quantize prorated; {t:.1f} s wall on {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(W.WORKLOADS))
+    ap.add_argument("--corr", default=None, choices=["off", "taylor", "exact"])
+    ap.add_argument("--path", default="auto", choices=["auto", "long", "short"])
+    ap.add_argument("--nq", type=int, default=0, help="override query rows (and current chunk) per head")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-overhead", action="store_true", help="skip the correction-off timing")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from bit_kv_cache_03_amd import kvq
+
+    w = W.WORKLOADS[args.workload]
+    if args.nq:
+        w = w.scaled(Nq=args.nq, Ncur=args.nq)
+    corr = args.corr or w.corr
+    data = W.generate(w)
+    dev = lambda x: (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16) if x.dtype == np.uint16
+                     else torch.from_numpy(W.bf16_bits(x).view(np.int16)).view(torch.bfloat16)).cuda()
+    q, k, v = dev(data["q"]), dev(data["k"]), dev(data["v"])
+    cap = w.Nc + w.Ncur
+    kc = kvq.QCache(w.B, w.Hkv, cap, w.d, w.kbits, w.group)
+    vc = kvq.QCache(w.B, w.Hkv, cap, w.d, w.vbits, w.group)
+    chunk = max(w.Ncur, 1)
+    for off in range(0, w.Nc, chunk):
+        n = min(chunk, w.Nc - off)
+        kvq.quantize(dev(np.ascontiguousarray(data["kc"][:, :, off:off + n])), kc, off)
+        kvq.quantize(dev(np.ascontiguousarray(data["vc"][:, :, off:off + n])), vc, off)
+    out = torch.empty_like(q)
+    args_c = kvq.make_args(q, k, v, kc, vc, w.Nc, out, corr=corr, path=args.path)
+    ws_bytes = kvq.workspace_size(args_c)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    args_c = kvq.make_args(q, k, v, kc, vc, w.Nc, out, corr=corr, path=args.path, workspace=ws)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    import ctypes as C
+
+    def attention(a):
+        st = kvq.lib.kv_attention_corrected(C.byref(a), sp)
+        if st != 0:
+            raise kvq.KvqError(st, "kv_attention_corrected")
+
+    def step(a, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        attention(a)
+        if ev is not None:
+            ev[1].record(stream)
+        kvq.quantize(k, kc, w.Nc, stream)
+        kvq.quantize(v, vc, w.Nc, stream)
+
+    for _ in range(args.warmup):
+        step(args_c)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(args_c, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    quant_ms = ms_step - attn_ms
+
+    overhead = None
+    if not args.no_overhead and corr != "off":
+        a_off = kvq.make_args(q, k, v, kc, vc, w.Nc, out, corr="off", path=args.path, workspace=ws)
+        for _ in range(args.warmup):
+            attention(a_off)
+        e_off = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        e_on = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for i in range(args.steps):   # interleave so drift hits both equally
+            e_off[i][0].record(stream); attention(a_off); e_off[i][1].record(stream)
+            e_on[i][0].record(stream); attention(args_c); e_on[i][1].record(stream)
+        torch.cuda.synchronize()
+        t_off = float(np.median([a.elapsed_time(b) for a, b in e_off]))
+        t_on = float(np.median([a.elapsed_time(b) for a, b in e_on]))
+        overhead = t_on / t_off - 1.0
+
+    flops = attention_flops(w)
+    ckq = w.B * w.Hq * w.Nq * w.Nc
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    # few query rows per KV head: the packed cache read bounds the kernel
+    hbm_bound = w.rows_per_kvhead <= 64
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": packed_bytes(w) / (attn_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    sha = kernel_sha()
+    traffic = traffic_from_profiles(w, sha)
+    line = {
+        "metric": METRIC,
+        "value": ckq / (ms_step * 1e-3),
+        "unit": "cached-key tokens·queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) q/k/v with the workload's key structure, bf16; cache INT%d/INT%d group %d" % (
+            w.kbits, w.vbits, w.group),
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "Nq": w.Nq,
+                   "Ncur": w.Ncur, "Nc": w.Nc, "kbits": w.kbits, "vbits": w.vbits, "group": w.group,
+                   "corr": corr, "path": args.path},
+        "attention_ms": attn_ms,
+        "quantize_ms": quant_ms,
+        "tflops_eff": achieved,
+        "packed_kv_gbs": packed_bytes(w) / (attn_ms * 1e-3) / 1e9,
+        "correction_overhead": overhead,
+        "wall_s": wall,
+        "kernel_sha": sha,
+        "roofline": dict(roof, frac=roof["achieved"] / roof["peak"], traffic=traffic),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, data, corr)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

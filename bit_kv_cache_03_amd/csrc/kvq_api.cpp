@@ -1,0 +1,215 @@
+// Host side of libkvq.so: argument validation (before any HIP call, so every
+// error path can be exercised on a machine without a GPU), path selection
+// and kernel launch.  No allocation, no state kept between calls.
+#include <math.h>
+#include <stdlib.h>
+#include <stdio.h>
+
+#include "kvq_internal.h"
+
+namespace {
+
+using kvq::AttnLaunch;
+
+constexpr int32_t kAbiVersion = 1;
+constexpr int32_t kMaxSplits = 1024;  // grid z extent of the split path
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
+
+bool group_ok(int32_t group, int32_t d) {
+  return (group == 32 || group == 64 || group == 128) && group <= d && d % group == 0;
+}
+
+// Byte ranges [a, a+na) and [b, b+nb) overlap.
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+// Checked a*b for non-negative int64 (false on overflow).
+bool mul_ok(int64_t a, int64_t b, int64_t *out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+kv_status check_qtensor(const kv_qtensor *t, int32_t d, int64_t need_rows) {
+  if (!t) return KV_ERR_NULL;
+  if (!t->codes || !t->scale || !t->zero) return KV_ERR_NULL;
+  if (t->bits != 2 && t->bits != 4) return KV_ERR_UNSUPPORTED;
+  if (!group_ok(t->group, d)) return KV_ERR_UNSUPPORTED;
+  if (t->cap < need_rows || t->cap < 0) return KV_ERR_SHAPE;
+  if (!aligned16(t->codes) || !aligned16(t->scale) || !aligned16(t->zero)) return KV_ERR_ALIGN;
+  return KV_OK;
+}
+
+bool debug_log() {
+  const char *e = getenv("KVQ_LOG");
+  return e && e[0] == '1';
+}
+
+struct Plan {
+  int path;  // KV_PATH_LONG or KV_PATH_SHORT
+  int splits;
+  size_t workspace;
+};
+
+// Rows per KV head at or below which the split-over-cache path is used.
+constexpr int64_t kShortRows = 64;
+
+int device_cu_count() {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+  }
+  return cus;
+}
+
+kv_status validate_attention(const kv_attn_args *a) {
+  if (!a) return KV_ERR_NULL;
+  if (!a->q || !a->out) return KV_ERR_NULL;
+  if (a->B < 1 || a->Hq < 1 || a->Hkv < 1 || a->Nq < 1 || a->Ncur < 0 || a->Nc < 0) return KV_ERR_SHAPE;
+  if (a->Hq % a->Hkv != 0) return KV_ERR_SHAPE;
+  if (a->Nc + a->Ncur < 1) return KV_ERR_SHAPE;
+  if (!head_dim_ok(a->d)) return KV_ERR_UNSUPPORTED;
+  if (a->corr < KV_CORR_OFF || a->corr > KV_CORR_EXACT) return KV_ERR_UNSUPPORTED;
+  if (a->path < KV_PATH_AUTO || a->path > KV_PATH_SHORT) return KV_ERR_UNSUPPORTED;
+  if (a->splits < 0) return KV_ERR_SHAPE;
+  if (a->splits > kMaxSplits) return KV_ERR_UNSUPPORTED;
+  if (!(a->softmax_scale >= 0.0f) || !isfinite(a->softmax_scale)) return KV_ERR_SHAPE;
+  // sizes: every element count must fit comfortably in int64 and the grid
+  int64_t nq_el = 0, ncur_el = 0, t = 0;
+  if (!mul_ok(a->B, a->Hq, &t) || !mul_ok(t, a->Nq, &t) || !mul_ok(t, a->d, &nq_el)) return KV_ERR_SHAPE;
+  if (!mul_ok(a->B, a->Hkv, &t) || !mul_ok(t, a->Ncur, &t) || !mul_ok(t, a->d, &ncur_el)) return KV_ERR_SHAPE;
+  if (a->B * a->Hkv > 65535) return KV_ERR_UNSUPPORTED;
+  if ((a->Nq * (a->Hq / a->Hkv)) > (int64_t(1) << 40)) return KV_ERR_SHAPE;
+  if (!aligned16(a->q) || !aligned16(a->out)) return KV_ERR_ALIGN;
+  if (a->Ncur > 0) {
+    if (!a->k_cur || !a->v_cur) return KV_ERR_NULL;
+    if (!aligned16(a->k_cur) || !aligned16(a->v_cur)) return KV_ERR_ALIGN;
+  }
+  if (a->Nc > 0) {
+    kv_status s = check_qtensor(a->k_cache, a->d, a->Nc);
+    if (s != KV_OK) return s;
+    s = check_qtensor(a->v_cache, a->d, a->Nc);
+    if (s != KV_OK) return s;
+    if (a->k_cache->group != a->v_cache->group) return KV_ERR_UNSUPPORTED;
+    if (a->k_cache->cap != a->v_cache->cap) return KV_ERR_SHAPE;
+  }
+  // the output must not overlap any input
+  const size_t out_b = static_cast<size_t>(nq_el) * 2;
+  if (overlaps(a->out, out_b, a->q, out_b)) return KV_ERR_ALIAS;
+  if (a->Ncur > 0 && (overlaps(a->out, out_b, a->k_cur, static_cast<size_t>(ncur_el) * 2) ||
+                      overlaps(a->out, out_b, a->v_cur, static_cast<size_t>(ncur_el) * 2)))
+    return KV_ERR_ALIAS;
+  if (a->Nc > 0) {
+    const kv_qtensor *ts[2] = {a->k_cache, a->v_cache};
+    for (const kv_qtensor *c : ts) {
+      const size_t rows = static_cast<size_t>(a->B * a->Hkv * c->cap);
+      const size_t ng = static_cast<size_t>(a->d / c->group);
+      if (overlaps(a->out, out_b, c->codes, rows * static_cast<size_t>(a->d * c->bits / 8)) ||
+          overlaps(a->out, out_b, c->scale, rows * ng * 4) || overlaps(a->out, out_b, c->zero, rows * ng * 4))
+        return KV_ERR_ALIAS;
+    }
+  }
+  return KV_OK;
+}
+
+Plan plan_attention(const kv_attn_args *a, bool query_device) {
+  Plan pl{KV_PATH_LONG, 0, 0};
+  const int64_t rows = a->Nq * (a->Hq / a->Hkv);
+  int path = a->path;
+  if (path == KV_PATH_AUTO) path = (rows <= kShortRows && a->Nc > 0) ? KV_PATH_SHORT : KV_PATH_LONG;
+  pl.path = path;
+  if (path == KV_PATH_SHORT) {
+    const int cus = query_device ? device_cu_count() : 256;
+    pl.splits = a->splits > 0 ? a->splits : kvq::short_path_splits(a->B, a->Hkv, rows, a->Nc, cus);
+    pl.workspace = kvq::short_path_workspace_bytes(a->B, a->Hq, a->Nq, a->d, pl.splits);
+  }
+  return pl;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kv_status_string(kv_status s) {
+  switch (s) {
+    case KV_OK: return "ok";
+    case KV_ERR_NULL: return "a required pointer is NULL";
+    case KV_ERR_SHAPE: return "sizes are inconsistent or out of range";
+    case KV_ERR_UNSUPPORTED: return "unsupported bits, group, head dimension, correction or path";
+    case KV_ERR_WORKSPACE: return "workspace missing or too small";
+    case KV_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case KV_ERR_ALIAS: return "the output overlaps an input";
+    case KV_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t kv_version(void) { return kAbiVersion; }
+
+kv_status kv_quantize(const void *x, kv_dtype xdt, int64_t B, int64_t H, int64_t N, int32_t d,
+                      const kv_qtensor *dst, int64_t tok_offset, void *stream) {
+  if (!x || !dst) return KV_ERR_NULL;
+  if (!dst->codes || !dst->scale || !dst->zero) return KV_ERR_NULL;
+  if (xdt != KV_BF16 && xdt != KV_F32) return KV_ERR_UNSUPPORTED;
+  if (B < 1 || H < 1 || N < 0 || tok_offset < 0) return KV_ERR_SHAPE;
+  if (!head_dim_ok(d)) return KV_ERR_UNSUPPORTED;
+  if (dst->bits != 2 && dst->bits != 4) return KV_ERR_UNSUPPORTED;
+  if (!group_ok(dst->group, d)) return KV_ERR_UNSUPPORTED;
+  if (dst->cap < 0 || tok_offset > dst->cap || N > dst->cap - tok_offset) return KV_ERR_SHAPE;
+  int64_t t = 0;
+  if (!mul_ok(B, H, &t) || !mul_ok(t, N, &t) || !mul_ok(t, d, &t) || t > (int64_t(1) << 40)) return KV_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(dst->codes) || !aligned16(dst->scale) || !aligned16(dst->zero))
+    return KV_ERR_ALIGN;
+  if (N == 0) return KV_OK;
+  kvq::QuantizeLaunch p{x, static_cast<int>(xdt), B, H, N, d, dst->codes, dst->scale, dst->zero,
+                        dst->bits, dst->group, dst->cap, tok_offset};
+  return kvq::launch_quantize(p, static_cast<hipStream_t>(stream)) == hipSuccess ? KV_OK : KV_ERR_HIP;
+}
+
+size_t kv_attention_workspace_size(const kv_attn_args *a) {
+  if (validate_attention(a) != KV_OK) return 0;
+  return plan_attention(a, true).workspace;
+}
+
+kv_status kv_attention_corrected(const kv_attn_args *a, void *stream) {
+  const kv_status v = validate_attention(a);
+  if (v != KV_OK) return v;
+  const Plan pl = plan_attention(a, true);
+  if (pl.workspace > 0 && (!a->workspace || a->workspace_bytes < pl.workspace)) return KV_ERR_WORKSPACE;
+  if (pl.workspace > 0 && !aligned16(a->workspace)) return KV_ERR_ALIGN;
+
+  AttnLaunch p{};
+  p.B = a->B; p.Hq = a->Hq; p.Hkv = a->Hkv; p.Nq = a->Nq; p.Ncur = a->Ncur; p.Nc = a->Nc; p.d = a->d;
+  p.q = static_cast<const uint16_t *>(a->q);
+  p.k_cur = static_cast<const uint16_t *>(a->k_cur);
+  p.v_cur = static_cast<const uint16_t *>(a->v_cur);
+  p.out = static_cast<uint16_t *>(a->out);
+  if (a->Nc > 0) {
+    p.kc_codes = a->k_cache->codes; p.kc_scale = a->k_cache->scale; p.kc_zero = a->k_cache->zero;
+    p.vc_codes = a->v_cache->codes; p.vc_scale = a->v_cache->scale; p.vc_zero = a->v_cache->zero;
+    p.kbits = a->k_cache->bits; p.vbits = a->v_cache->bits; p.group = a->k_cache->group; p.cap = a->k_cache->cap;
+  } else {
+    p.kbits = 2; p.vbits = 2; p.group = a->d; p.cap = 0;
+  }
+  p.tau = a->softmax_scale > 0.0f ? a->softmax_scale : 1.0f / sqrtf(static_cast<float>(a->d));
+  p.corr = a->corr;
+  p.splits = pl.splits;
+  p.workspace = a->workspace;
+  if (debug_log())
+    fprintf(stderr, "kvq: attention path=%s rows/kvhead=%lld splits=%d workspace=%zu corr=%d\n",
+            pl.path == KV_PATH_SHORT ? "short" : "long", static_cast<long long>(a->Nq * (a->Hq / a->Hkv)),
+            pl.splits, pl.workspace, a->corr);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = pl.path == KV_PATH_SHORT ? kvq::launch_attention_short(p, s) : kvq::launch_attention_long(p, s);
+  return e == hipSuccess ? KV_OK : KV_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,51 @@
+// Internal declarations shared by the host entry points (kvq_api.cpp) and the
+// gfx950 kernels.  Not part of the ABI; include/kvq.h is.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kvq.h"
+
+namespace kvq {
+
+// Everything a quantize launch needs, already validated by the host.
+struct QuantizeLaunch {
+  const void *x;
+  int xdt;  // kv_dtype
+  int64_t B, H, N;
+  int32_t d;
+  uint8_t *codes;
+  float *scale;
+  float *zero;
+  int32_t bits, group;
+  int64_t cap, off;
+};
+
+// Everything an attention launch needs, already validated by the host.
+struct AttnLaunch {
+  int64_t B, Hq, Hkv, Nq, Ncur, Nc;
+  int32_t d;
+  const uint16_t *q, *k_cur, *v_cur;
+  uint16_t *out;
+  const uint8_t *kc_codes, *vc_codes;
+  const float *kc_scale, *kc_zero, *vc_scale, *vc_zero;
+  int32_t kbits, vbits, group;
+  int64_t cap;
+  float tau;   // resolved softmax scale
+  int corr;    // kv_corr
+  int splits;  // short path: resolved split count
+  void *workspace;
+};
+
+hipError_t launch_quantize(const QuantizeLaunch &p, hipStream_t stream);
+hipError_t launch_attention_long(const AttnLaunch &p, hipStream_t stream);
+hipError_t launch_attention_short(const AttnLaunch &p, hipStream_t stream);
+
+// Short path: cached-token split count chosen for a problem and the
+// workspace it needs (partials of every split for every query row).
+int short_path_splits(int64_t B, int64_t Hkv, int64_t rows_per_kvhead, int64_t Nc, int cu_count);
+size_t short_path_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int32_t d, int splits);
+
+}  // namespace kvq

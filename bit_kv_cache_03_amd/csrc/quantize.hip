@@ -1,0 +1,149 @@
+// Quantize/pack kernel for gfx950: group-wise asymmetric INT2/INT4 along the
+// head dimension, one step D and zero-point z (the group minimum) per
+// (token, group), codes packed LSB-first.
+//
+// The pages: "量化鍵值偷走注意力…" (agents-report.net), section 方法 -- one
+// step size per group (or channel) enters the correction; "QuantWM：…"
+// (pchao.org), section 方法概览 -- each cache block is quantised once after
+// it is built.  The exact formula (range / (2^bits - 1), zero = min, round
+// half to even) is this library's reading, stated in include/kvq.h.
+//
+// Mapping: one lane owns 8 consecutive values of a token row (16 B of bf16 or
+// 32 B of fp32, so a wave reads 1-2 KB contiguous), group/8 adjacent lanes
+// own one group and reduce min/max with cross-lane shuffles.  Each lane
+// writes its 8 codes as one 16-bit (INT2) or 32-bit (INT4) store, so a wave
+// writes a contiguous run of packed rows.  Pure streaming, HBM-bound.
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int LANES>
+__device__ inline float group_min(float v) {
+#pragma unroll
+  for (int o = 1; o < LANES; o <<= 1) v = fminf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+template <int LANES>
+__device__ inline float group_max(float v) {
+#pragma unroll
+  for (int o = 1; o < LANES; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+template <typename T>
+__device__ inline void load8(const T *p, float (&v)[8]);
+
+template <>
+__device__ inline void load8<uint16_t>(const uint16_t *p, float (&v)[8]) {
+  const uint4 w = *reinterpret_cast<const uint4 *>(p);
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(u[i] << 16);
+    v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+  }
+}
+
+template <>
+__device__ inline void load8<float>(const float *p, float (&v)[8]) {
+  const float4 a = *reinterpret_cast<const float4 *>(p);
+  const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// T: uint16_t (bf16 bits) or float.  LANES = group / 8.
+template <typename T, int BITS, int LANES>
+__global__ __launch_bounds__(kThreads) void quantize_pack(
+    const T *__restrict__ x, int64_t total_lanes, int32_t lanes_per_row, int64_t N,
+    uint8_t *__restrict__ codes, float *__restrict__ scale, float *__restrict__ zero,
+    int64_t cap, int64_t off, int32_t groups_per_row) {
+#pragma clang fp contract(off)
+  constexpr int TOP = (1 << BITS) - 1;
+  const int64_t gl = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const bool live = gl < total_lanes;
+  const int64_t lane_id = live ? gl : total_lanes - 1;  // dead lanes shadow a live row
+  const int64_t row = lane_id / lanes_per_row;          // (b*H + h)*N + n
+  const int32_t chunk = static_cast<int32_t>(lane_id % lanes_per_row);
+
+  float v[8];
+  load8<T>(x + lane_id * 8, v);
+
+  float mn = v[0], mx = v[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) {
+    mn = v[i] < mn ? v[i] : mn;
+    mx = v[i] > mx ? v[i] : mx;
+  }
+  mn = group_min<LANES>(mn) + 0.0f;  // + 0.0f: a zero extreme is +0
+  mx = group_max<LANES>(mx) + 0.0f;
+  const float range = mx - mn;
+  const float step = range / static_cast<float>(TOP);  // IEEE division
+
+  uint32_t packed = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t c = 0;
+    if (step > 0.0f) {
+      const float t = (v[i] - mn) / step;  // IEEE division
+      const float r = fminf(fmaxf(rintf(t), 0.0f), static_cast<float>(TOP));
+      c = static_cast<uint32_t>(r);
+    }
+    packed |= c << (i * BITS);
+  }
+
+  if (!live) return;
+  const int64_t bh = row / N;
+  const int64_t n = row - bh * N;
+  const int64_t orow = bh * cap + off + n;
+  const int64_t row_bytes = static_cast<int64_t>(lanes_per_row) * BITS;  // 8 codes * BITS / 8 per lane
+  uint8_t *dst = codes + orow * row_bytes + static_cast<int64_t>(chunk) * BITS;
+  if (BITS == 2) {
+    *reinterpret_cast<uint16_t *>(dst) = static_cast<uint16_t>(packed);
+  } else {
+    *reinterpret_cast<uint32_t *>(dst) = packed;
+  }
+  if ((chunk % LANES) == 0) {
+    const int64_t m = orow * groups_per_row + chunk / LANES;
+    scale[m] = step;
+    zero[m] = mn;
+  }
+}
+
+template <typename T, int BITS>
+hipError_t launch_t(const QuantizeLaunch &p, hipStream_t stream) {
+  const int32_t lanes_per_row = p.d / 8;
+  const int64_t total = p.B * p.H * p.N * lanes_per_row;
+  const int64_t blocks = (total + kThreads - 1) / kThreads;
+  const T *x = static_cast<const T *>(p.x);
+  const int32_t gpr = p.d / p.group;
+  switch (p.group) {
+    case 32:
+      quantize_pack<T, BITS, 4><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream>>>(
+          x, total, lanes_per_row, p.N, p.codes, p.scale, p.zero, p.cap, p.off, gpr);
+      break;
+    case 64:
+      quantize_pack<T, BITS, 8><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream>>>(
+          x, total, lanes_per_row, p.N, p.codes, p.scale, p.zero, p.cap, p.off, gpr);
+      break;
+    default:
+      quantize_pack<T, BITS, 16><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream>>>(
+          x, total, lanes_per_row, p.N, p.codes, p.scale, p.zero, p.cap, p.off, gpr);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const QuantizeLaunch &p, hipStream_t stream) {
+  if (p.B * p.H * p.N == 0) return hipSuccess;
+  if (p.xdt == KV_BF16) return p.bits == 2 ? launch_t<uint16_t, 2>(p, stream) : launch_t<uint16_t, 4>(p, stream);
+  return p.bits == 2 ? launch_t<float, 2>(p, stream) : launch_t<float, 4>(p, stream);
+}
+
+}  // namespace kvq

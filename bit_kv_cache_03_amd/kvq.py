@@ -1,0 +1,154 @@
+"""ctypes binding of libkvq.so (declared in include/kvq.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of the library.  torch is used for device memory (tensors) and
+streams.  Importing this module loads the library and raises ImportError if
+it has not been built (``python -m bit_kv_cache_03_amd.build``); there is no
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvq.so")
+
+KV_OK, KV_ERR_NULL, KV_ERR_SHAPE, KV_ERR_UNSUPPORTED, KV_ERR_WORKSPACE, KV_ERR_ALIGN, KV_ERR_ALIAS, KV_ERR_HIP = range(8)
+KV_BF16, KV_F32 = 0, 1
+CORR = {"off": 0, "taylor": 1, "exact": 2}
+PATH = {"auto": 0, "long": 1, "short": 2}
+
+EXPORTED = ("kv_quantize", "kv_attention_workspace_size", "kv_attention_corrected",
+            "kv_status_string", "kv_version")
+
+
+class QTensor(C.Structure):
+    """kv_qtensor."""
+    _fields_ = [("codes", C.c_void_p), ("scale", C.c_void_p), ("zero", C.c_void_p),
+                ("bits", C.c_int32), ("group", C.c_int32), ("cap", C.c_int64)]
+
+
+class AttnArgs(C.Structure):
+    """kv_attn_args."""
+    _fields_ = [("B", C.c_int64), ("Hq", C.c_int64), ("Hkv", C.c_int64), ("Nq", C.c_int64),
+                ("Ncur", C.c_int64), ("Nc", C.c_int64), ("d", C.c_int32),
+                ("q", C.c_void_p), ("k_cur", C.c_void_p), ("v_cur", C.c_void_p),
+                ("k_cache", C.POINTER(QTensor)), ("v_cache", C.POINTER(QTensor)),
+                ("out", C.c_void_p), ("softmax_scale", C.c_float), ("corr", C.c_int32),
+                ("path", C.c_int32), ("splits", C.c_int32),
+                ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m bit_kv_cache_03_amd.build`")
+    L = C.CDLL(LIB_PATH)
+    L.kv_quantize.argtypes = [C.c_void_p, C.c_int, C.c_int64, C.c_int64, C.c_int64, C.c_int32,
+                              C.POINTER(QTensor), C.c_int64, C.c_void_p]
+    L.kv_quantize.restype = C.c_int
+    L.kv_attention_workspace_size.argtypes = [C.POINTER(AttnArgs)]
+    L.kv_attention_workspace_size.restype = C.c_size_t
+    L.kv_attention_corrected.argtypes = [C.POINTER(AttnArgs), C.c_void_p]
+    L.kv_attention_corrected.restype = C.c_int
+    L.kv_status_string.argtypes = [C.c_int]
+    L.kv_status_string.restype = C.c_char_p
+    L.kv_version.restype = C.c_int32
+    return L
+
+
+lib = _load()
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {lib.kv_status_string(status).decode()} (status {status})")
+
+
+def _check(status: int, what: str):
+    if status != KV_OK:
+        raise KvqError(status, what)
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+class QCache:
+    """A quantized cache tensor (K or V): codes, step and zero-point on the GPU."""
+
+    def __init__(self, B: int, H: int, cap: int, d: int, bits: int, group: int = 64, device="cuda"):
+        import torch
+        self.B, self.H, self.cap, self.d, self.bits, self.group = B, H, cap, d, bits, group
+        self.codes = torch.zeros((B, H, cap, d * bits // 8), dtype=torch.uint8, device=device)
+        self.scale = torch.zeros((B, H, cap, d // group), dtype=torch.float32, device=device)
+        self.zero = torch.zeros((B, H, cap, d // group), dtype=torch.float32, device=device)
+
+    def descriptor(self) -> QTensor:
+        return QTensor(self.codes.data_ptr(), self.scale.data_ptr(), self.zero.data_ptr(),
+                       self.bits, self.group, self.cap)
+
+
+def quantize(x, cache: QCache, tok_offset: int = 0, stream=None) -> None:
+    """Quantize x [B][H][N][d] (bf16 or fp32, on the GPU) into cache rows
+    [tok_offset, tok_offset + N)."""
+    import torch
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    xdt = {torch.bfloat16: KV_BF16, torch.float32: KV_F32}.get(x.dtype)
+    if xdt is None:
+        raise TypeError("x must be bfloat16 or float32")
+    B, H, N, d = x.shape
+    desc = cache.descriptor()
+    _check(lib.kv_quantize(x.data_ptr(), xdt, B, H, N, d, C.byref(desc), tok_offset, _stream(stream)),
+           "kv_quantize")
+
+
+def make_args(q, k_cur, v_cur, k_cache: Optional[QCache], v_cache: Optional[QCache], nc: int, out,
+              corr: str = "taylor", scale: float = 0.0, path: str = "auto", splits: int = 0,
+              workspace=None):
+    """Fill kv_attn_args (keeps the descriptors alive on the returned object)."""
+    B, Hq, Nq, d = q.shape
+    Hkv = k_cur.shape[1] if k_cur is not None else k_cache.H
+    ncur = k_cur.shape[2] if k_cur is not None else 0
+    a = AttnArgs()
+    a.B, a.Hq, a.Hkv, a.Nq, a.Ncur, a.Nc, a.d = B, Hq, Hkv, Nq, ncur, nc, d
+    a.q, a.k_cur, a.v_cur, a.out = _ptr(q), _ptr(k_cur), _ptr(v_cur), _ptr(out)
+    a._kd = k_cache.descriptor() if k_cache is not None else None
+    a._vd = v_cache.descriptor() if v_cache is not None else None
+    a.k_cache = C.pointer(a._kd) if a._kd is not None else None
+    a.v_cache = C.pointer(a._vd) if a._vd is not None else None
+    a.softmax_scale, a.corr, a.path, a.splits = scale, CORR[corr], PATH[path], splits
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return a
+
+
+def workspace_size(args: AttnArgs) -> int:
+    return lib.kv_attention_workspace_size(C.byref(args))
+
+
+def attention(q, k_cur, v_cur, k_cache: Optional[QCache], v_cache: Optional[QCache], nc: int,
+              corr: str = "taylor", scale: float = 0.0, path: str = "auto", splits: int = 0,
+              out=None, workspace=None, stream=None):
+    """Corrected attention of q [B][Hq][Nq][d] (bf16) over the first nc tokens
+    of the quantized caches and the bf16 current chunk [B][Hkv][Ncur][d].
+    Returns out [B][Hq][Nq][d] bf16."""
+    import torch
+    if out is None:
+        out = torch.empty_like(q)
+    args = make_args(q, k_cur, v_cur, k_cache, v_cache, nc, out, corr, scale, path, splits, workspace)
+    need = workspace_size(args)
+    if need > 0 and (workspace is None or args.workspace_bytes < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        args.workspace, args.workspace_bytes = workspace.data_ptr(), need
+    _check(lib.kv_attention_corrected(C.byref(args), _stream(stream)), "kv_attention_corrected")
+    return out

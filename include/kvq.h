@@ -1,0 +1,163 @@
+/*
+ * kvq.h -- C ABI of libkvq.so: Jensen-bias-corrected attention over a
+ * group-wise INT2/INT4 KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * The method (sources cited by page title and section):
+ *  - "量化鍵值偷走注意力：針對 KV-Cache 的 Jensen 偏差校正還原影片擴散品質"
+ *    (agents-report.net), sections 問題 and 方法: keys and values of earlier
+ *    chunks are cached at INT4/INT2; the exponential in softmax turns the
+ *    zero-mean rounding noise of cached keys into an upward bias of their
+ *    weight; each cached-key score gets b_i = log E[exp(delta_i)] subtracted,
+ *    in practice its second-order form (1/(24 d)) sum_c q_c^2 D_{i,c}^2,
+ *    built from per-group query squared norms and the keys' step sizes.
+ *    Section 為何校正有效: b is subtracted from the quantised keys' scores
+ *    before the softmax; current-chunk scores are left alone.
+ *  - "Quantized Keys Steal Attention: Bias Correction for KV-Cache
+ *    Compression in Video Diffusion" (fugumt.com), Abstract: the correction is
+ *    computed on the fly from the cached keys' step sizes and the query norm,
+ *    with no memory beyond the cache.
+ *  - "QuantWM：保住时间一致性的两比特键值缓存量化" (pchao.org), section
+ *    方法概览: each cache block is quantised once after it is built;
+ *    section 研究缺口, Eq. (5): logits are Q K^T / sqrt(d).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *    library never allocates, frees or retains them and keeps no state
+ *    between calls; concurrent calls on different streams are safe.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Work is only enqueued there; calls return before it completes.
+ *  - Arguments are validated on the host before any HIP call; an invalid call
+ *    returns an error and touches no memory.  Launch failures return
+ *    KV_ERR_HIP.  A device fault surfaces at the caller's next
+ *    synchronisation.
+ *  - Tensors are dense and row-major in the shapes given; every pointer must
+ *    be 16-byte aligned.
+ *  - NaN or Inf inputs, and groups whose range max-min overflows fp32, are
+ *    outside the contract.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KV_OK = 0,
+  KV_ERR_NULL = 1,        /* a required pointer is NULL */
+  KV_ERR_SHAPE = 2,       /* sizes inconsistent or out of range */
+  KV_ERR_UNSUPPORTED = 3, /* valid but not implemented (bits, group, d, path) */
+  KV_ERR_WORKSPACE = 4,   /* workspace missing or too small */
+  KV_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned */
+  KV_ERR_ALIAS = 6,       /* the output overlaps an input */
+  KV_ERR_HIP = 7          /* a HIP runtime call or launch failed */
+} kv_status;
+
+typedef enum { KV_BF16 = 0, KV_F32 = 1 } kv_dtype;
+
+/* Correction applied to cached-key logits. */
+typedef enum {
+  KV_CORR_OFF = 0,    /* plain softmax over [dequantised cache ; current chunk] */
+  KV_CORR_TAYLOR = 1, /* b = (tau^2/24) sum_g D_g^2 ||q_g||^2  (page 方法 formula) */
+  KV_CORR_EXACT = 2   /* b = sum_c log(sinh x_c / x_c), x_c = tau q_c D_{g(c)} / 2:
+                         the uniform-noise closed form; slow path, no perf target */
+} kv_corr;
+
+/* Kernel path.  AUTO picks by rows per KV head; tests may force either. */
+typedef enum {
+  KV_PATH_AUTO = 0,
+  KV_PATH_LONG = 1,  /* MFMA tile kernel, query rows tiled, one pass over keys */
+  KV_PATH_SHORT = 2  /* split over cached tokens + log-sum-exp combine */
+} kv_path;
+
+/*
+ * One quantised cache tensor (K or V) of B x H heads and `cap` token slots.
+ * Group-wise asymmetric uniform quantisation along the head dimension:
+ * token row of d values, groups of `group` consecutive values, per group
+ *   step  D = fl32(fl32(max - min) / (2^bits - 1)),   zero z = min
+ *   code  c = clamp(round_half_even(fl32(fl32(x - min) / D)), 0, 2^bits - 1)
+ *         (c = 0 when D == 0; a zero min or max is taken as +0)
+ *   value x^ = z + D * c.
+ * Codes are packed LSB-first: element k of a row lives in byte
+ * floor(k*bits/8) at bit (k*bits) mod 8.
+ */
+typedef struct {
+  uint8_t *codes; /* [B][H][cap][d*bits/8] bytes */
+  float *scale;   /* [B][H][cap][d/group]  step D */
+  float *zero;    /* [B][H][cap][d/group]  zero-point z (the group minimum) */
+  int32_t bits;   /* 2 or 4 */
+  int32_t group;  /* 32, 64 or 128; divides d */
+  int64_t cap;    /* token capacity (row stride in tokens) */
+} kv_qtensor;
+
+/*
+ * kv_quantize -- quantise N new tokens of every (b, h) and store them in
+ * cache rows [tok_offset, tok_offset + N): how a finished chunk is appended
+ * (QuantWM page, 方法概览: each block is quantised once after it is built).
+ *
+ *   x    : [B][H][N][d], bf16 (xdt = KV_BF16) or fp32 (KV_F32), device.
+ *   dst  : host pointer to the descriptor of the destination cache.
+ * d must be 64 or 128.  N = 0 is a no-op.  Output is bit-exact with the
+ * definition above (IEEE fp32 division, round half to even).
+ * Errors: KV_ERR_NULL, KV_ERR_SHAPE (tok_offset + N > cap, ...),
+ * KV_ERR_UNSUPPORTED (bits, group, d), KV_ERR_ALIGN, KV_ERR_HIP.
+ */
+kv_status kv_quantize(const void *x, kv_dtype xdt, int64_t B, int64_t H, int64_t N, int32_t d,
+                      const kv_qtensor *dst, int64_t tok_offset, void *stream);
+
+/*
+ * Arguments of one corrected-attention call.  For query head h (KV head
+ * hk = h / (Hq/Hkv)) and query row j, with tau = softmax_scale (0 -> 1/sqrt(d)):
+ *   cached  logits  s_i = tau q.x^_i - b_i   for i <  Nc  (b per `corr`)
+ *   current logits  s_i = tau q.k_i          for i <  Ncur (never corrected)
+ *   out = softmax over both segments together, applied to [v^ ; v_cur]
+ * Values get no correction (they enter the output linearly).  No mask.
+ */
+typedef struct {
+  int64_t B, Hq, Hkv; /* Hq % Hkv == 0 */
+  int64_t Nq;         /* query rows per head, >= 1 */
+  int64_t Ncur;       /* current-chunk tokens, >= 0 */
+  int64_t Nc;         /* cached tokens in use (rows [0, Nc) of the caches), >= 0 */
+  int32_t d;          /* head dimension: 64 or 128 */
+  const void *q;      /* bf16 [B][Hq][Nq][d] */
+  const void *k_cur;  /* bf16 [B][Hkv][Ncur][d] (may be NULL if Ncur == 0) */
+  const void *v_cur;  /* bf16 [B][Hkv][Ncur][d] (may be NULL if Ncur == 0) */
+  const kv_qtensor *k_cache; /* host pointers to descriptors; may be NULL if Nc == 0 */
+  const kv_qtensor *v_cache; /* both with the same group */
+  void *out;          /* bf16 [B][Hq][Nq][d], overwritten; must not overlap inputs */
+  float softmax_scale; /* tau; 0 -> 1/sqrt(d); the correction uses tau^2/24 */
+  int32_t corr;       /* kv_corr */
+  int32_t path;       /* kv_path */
+  int32_t splits;     /* short path: key-range splits, 0 = automatic, at most 1024 */
+  void *workspace;    /* device scratch of kv_attention_workspace_size() bytes */
+  size_t workspace_bytes;
+} kv_attn_args;
+
+/* Bytes of device workspace the call needs (0 for the long path).  Returns
+ * 0 for invalid arguments as well; kv_attention_corrected reports those. */
+size_t kv_attention_workspace_size(const kv_attn_args *a);
+
+/*
+ * kv_attention_corrected -- the hot path: one call computes `out` for all
+ * B x Hq x Nq query rows in a single fused pass over the packed cache and the
+ * bf16 current chunk (dequantisation, scores, correction, softmax and the
+ * value product all inside the kernel).
+ * Errors: KV_ERR_NULL, KV_ERR_SHAPE, KV_ERR_UNSUPPORTED, KV_ERR_WORKSPACE,
+ * KV_ERR_ALIGN, KV_ERR_ALIAS, KV_ERR_HIP.
+ */
+kv_status kv_attention_corrected(const kv_attn_args *a, void *stream);
+
+/* Static English description of a status code. */
+const char *kv_status_string(kv_status s);
+
+/* ABI version (bumped on any change to these declarations). */
+int32_t kv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,185 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every
+function include/kvq.h declares, the ctypes structures match the header's
+layout, and every argument error is reported before any HIP call."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+
+@pytest.fixture(scope="module")
+def kvq():
+    from bit_kv_cache_03_amd import kvq
+    return kvq
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kv_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(kvq):
+    names = declared_functions()
+    assert set(names) == set(kvq.EXPORTED)
+    for n in names:
+        assert hasattr(kvq.lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", kvq.LIB_PATH], capture_output=True, text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}\b", out), n
+
+
+def test_version_and_status_strings(kvq):
+    assert kvq.lib.kv_version() == 1
+    for s in range(1, 8):
+        assert len(kvq.lib.kv_status_string(s)) > 10
+    assert kvq.lib.kv_status_string(0) == b"ok"
+    assert b"unknown" in kvq.lib.kv_status_string(99)
+
+
+def test_struct_layout_matches_header(kvq, tmp_path):
+    prog = tmp_path / "layout.c"
+    prog.write_text("""
+#include <stdio.h>
+#include <stddef.h>
+#include "kvq.h"
+#define F(T, f) printf(#T "." #f " %zu\\n", offsetof(T, f))
+int main(void) {
+  printf("kv_qtensor %zu\\n", sizeof(kv_qtensor));
+  printf("kv_attn_args %zu\\n", sizeof(kv_attn_args));
+  F(kv_qtensor, codes); F(kv_qtensor, scale); F(kv_qtensor, zero); F(kv_qtensor, bits);
+  F(kv_qtensor, group); F(kv_qtensor, cap);
+  F(kv_attn_args, B); F(kv_attn_args, Hq); F(kv_attn_args, Hkv); F(kv_attn_args, Nq);
+  F(kv_attn_args, Ncur); F(kv_attn_args, Nc); F(kv_attn_args, d); F(kv_attn_args, q);
+  F(kv_attn_args, k_cur); F(kv_attn_args, v_cur); F(kv_attn_args, k_cache); F(kv_attn_args, v_cache);
+  F(kv_attn_args, out); F(kv_attn_args, softmax_scale); F(kv_attn_args, corr); F(kv_attn_args, path);
+  F(kv_attn_args, splits); F(kv_attn_args, workspace); F(kv_attn_args, workspace_bytes);
+  return 0;
+}
+""")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(prog), "-o", str(exe)], check=True)
+    lines = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    got = dict(l.rsplit(" ", 1) for l in lines if l)
+    assert int(got["kv_qtensor"]) == C.sizeof(kvq.QTensor)
+    assert int(got["kv_attn_args"]) == C.sizeof(kvq.AttnArgs)
+    for key, val in got.items():
+        if "." in key:
+            T, f = key.split(".")
+            S = kvq.QTensor if T == "kv_qtensor" else kvq.AttnArgs
+            assert getattr(S, f).offset == int(val), key
+
+
+# ---------------------------------------------------------------------------
+# validation (fake, aligned device addresses: nothing is dereferenced)
+# ---------------------------------------------------------------------------
+
+A = 0x100000  # aligned fake device pointer base
+
+
+def _qt(kvq, base, bits=2, group=64, cap=100, d=128):
+    return kvq.QTensor(base, base + 0x100000, base + 0x200000, bits, group, cap)
+
+
+def _args(kvq, **kw):
+    a = kvq.AttnArgs()
+    a.B, a.Hq, a.Hkv, a.Nq, a.Ncur, a.Nc, a.d = 1, 4, 2, 8, 8, 50, 128
+    a.q, a.k_cur, a.v_cur, a.out = A, 2 * A, 3 * A, 4 * A
+    a._k = _qt(kvq, 0x10000000)
+    a._v = _qt(kvq, 0x20000000)
+    a.k_cache, a.v_cache = C.pointer(a._k), C.pointer(a._v)
+    a.softmax_scale, a.corr, a.path, a.splits = 0.0, 1, 0, 0
+    a.workspace, a.workspace_bytes = None, 0
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _attn(kvq, a):
+    return kvq.lib.kv_attention_corrected(C.byref(a), None)
+
+
+CASES = [
+    ("null q", dict(q=None), "KV_ERR_NULL"),
+    ("null out", dict(out=None), "KV_ERR_NULL"),
+    ("null k_cur with Ncur>0", dict(k_cur=None), "KV_ERR_NULL"),
+    ("null cache with Nc>0", dict(k_cache=None), "KV_ERR_NULL"),
+    ("B=0", dict(B=0), "KV_ERR_SHAPE"),
+    ("Hq % Hkv", dict(Hq=3), "KV_ERR_SHAPE"),
+    ("Nq=0", dict(Nq=0), "KV_ERR_SHAPE"),
+    ("empty key set", dict(Nc=0, Ncur=0), "KV_ERR_SHAPE"),
+    ("negative Nc", dict(Nc=-1), "KV_ERR_SHAPE"),
+    ("d=96", dict(d=96), "KV_ERR_UNSUPPORTED"),
+    ("corr=3", dict(corr=3), "KV_ERR_UNSUPPORTED"),
+    ("path=7", dict(path=7), "KV_ERR_UNSUPPORTED"),
+    ("splits>1024", dict(splits=1025), "KV_ERR_UNSUPPORTED"),
+    ("negative splits", dict(splits=-1), "KV_ERR_SHAPE"),
+    ("negative scale", dict(softmax_scale=-1.0), "KV_ERR_SHAPE"),
+    ("nan scale", dict(softmax_scale=float("nan")), "KV_ERR_SHAPE"),
+    ("misaligned q", dict(q=A + 2), "KV_ERR_ALIGN"),
+    ("out aliases q", dict(out=A + 64), "KV_ERR_ALIAS"),
+    ("out aliases k_cur", dict(out=2 * A), "KV_ERR_ALIAS"),
+]
+
+
+@pytest.mark.parametrize("name,kw,err", CASES, ids=[c[0] for c in CASES])
+def test_attention_argument_errors(kvq, name, kw, err):
+    assert _attn(kvq, _args(kvq, **kw)) == getattr(kvq, err)
+
+
+def test_attention_cache_errors(kvq):
+    for field, val, err in [("bits", 3, kvq.KV_ERR_UNSUPPORTED), ("group", 48, kvq.KV_ERR_UNSUPPORTED),
+                            ("group", 256, kvq.KV_ERR_UNSUPPORTED), ("cap", 49, kvq.KV_ERR_SHAPE),
+                            ("codes", None, kvq.KV_ERR_NULL), ("scale", 0x10000004, kvq.KV_ERR_ALIGN)]:
+        a = _args(kvq)
+        setattr(a._k, field, val)
+        assert _attn(kvq, a) == err, (field, val)
+    a = _args(kvq)
+    a._v.group = 32  # K and V groups differ
+    assert _attn(kvq, a) == kvq.KV_ERR_UNSUPPORTED
+
+
+def test_short_path_needs_workspace(kvq):
+    a = _args(kvq, path=2)
+    need = kvq.lib.kv_attention_workspace_size(C.byref(a))
+    assert need > 0
+    assert _attn(kvq, a) == kvq.KV_ERR_WORKSPACE
+    a = _args(kvq, path=2, workspace=0x40000000, workspace_bytes=need - 1)
+    assert _attn(kvq, a) == kvq.KV_ERR_WORKSPACE
+    a = _args(kvq, path=2, workspace=0x40000004, workspace_bytes=need)
+    assert _attn(kvq, a) == kvq.KV_ERR_ALIGN
+    # long path needs none; invalid arguments report 0
+    assert kvq.lib.kv_attention_workspace_size(C.byref(_args(kvq, path=1))) == 0
+    assert kvq.lib.kv_attention_workspace_size(C.byref(_args(kvq, B=0))) == 0
+    assert kvq.lib.kv_attention_workspace_size(None) == 0
+
+
+def test_short_path_workspace_grows_with_splits(kvq):
+    sizes = [kvq.lib.kv_attention_workspace_size(C.byref(_args(kvq, path=2, splits=s))) for s in (1, 2, 4, 8)]
+    assert sizes == sorted(sizes) and sizes[0] > 0 and sizes[3] == 8 * sizes[0]
+    assert sizes[0] == 1 * 4 * 8 * (128 + 2) * 4
+
+
+def test_quantize_argument_errors(kvq):
+    q = kvq.lib.kv_quantize
+    good = _qt(kvq, 0x30000000, bits=4, group=64, cap=64)
+    assert q(None, 0, 1, 2, 8, 128, C.byref(good), 0, None) == kvq.KV_ERR_NULL
+    assert q(A, 0, 1, 2, 8, 128, None, 0, None) == kvq.KV_ERR_NULL
+    assert q(A, 5, 1, 2, 8, 128, C.byref(good), 0, None) == kvq.KV_ERR_UNSUPPORTED
+    assert q(A, 0, 0, 2, 8, 128, C.byref(good), 0, None) == kvq.KV_ERR_SHAPE
+    assert q(A, 0, 1, 2, -1, 128, C.byref(good), 0, None) == kvq.KV_ERR_SHAPE
+    assert q(A, 0, 1, 2, 8, 80, C.byref(good), 0, None) == kvq.KV_ERR_UNSUPPORTED
+    assert q(A, 0, 1, 2, 8, 128, C.byref(good), 57, None) == kvq.KV_ERR_SHAPE  # 57 + 8 > 64
+    assert q(A, 0, 1, 2, 8, 128, C.byref(good), -1, None) == kvq.KV_ERR_SHAPE
+    assert q(A + 8, 0, 1, 2, 8, 128, C.byref(good), 0, None) == kvq.KV_ERR_ALIGN
+    bad = _qt(kvq, 0x30000000, bits=3, group=64, cap=64)
+    assert q(A, 0, 1, 2, 8, 128, C.byref(bad), 0, None) == kvq.KV_ERR_UNSUPPORTED
+    bad = _qt(kvq, 0x30000000, bits=2, group=24, cap=64)
+    assert q(A, 0, 1, 2, 8, 128, C.byref(bad), 0, None) == kvq.KV_ERR_UNSUPPORTED
+    # N = 0 is a valid no-op that launches nothing
+    assert q(A, 0, 1, 2, 0, 128, C.byref(good), 64, None) == kvq.KV_OK

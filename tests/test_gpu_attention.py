@@ -1,0 +1,102 @@
+"""kv_attention_corrected on the GPU against the oracle, element by element.
+
+Inputs are seeded and synthetic with each workload's structure, at sizes the
+oracle finishes in seconds that still span several row tiles and key tiles
+with ragged tails; both kernel paths, all three correction modes, and the
+degenerate cases (no cache, no current chunk, one query row, head dim 64,
+groups of 32/128, a non-default scale, GQA).  The oracle quantizes the
+cache itself from the raw inputs; the GPU builds its own with kv_quantize.
+Bar: max |out - ref| <= 2e-2 against the fp64 oracle and
+mean |out - bf16(ref)| <= 1e-3 in the bf16 output format (see _gpu.check)."""
+import numpy as np
+import pytest
+import torch
+
+from bit_kv_cache_03_amd import workloads as W
+from _problems import oracle_problem
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "tiny": W.WORKLOADS["tiny_d64_int2"],
+    "int4": W.WORKLOADS["h24_int4_cache16k"].scaled(Hq=2, Hkv=2, Nq=200, Ncur=200, Nc=333),
+    "outliers": W.WORKLOADS["h40_int2_outliers_cache25k"].scaled(Hq=2, Hkv=2, Nq=150, Ncur=150, Nc=300),
+    "gqa": W.WORKLOADS["gqa_prefill_b16_cache32k"].scaled(B=2, Hq=8, Hkv=2, Nq=50, Ncur=50, Nc=333),
+    "longvideo": W.WORKLOADS["long_video_cache61k"].scaled(Hq=2, Hkv=2, Nq=130, Ncur=130, Nc=400),
+}
+
+
+def _compare(orc, w, corr, path, scale=0.0, splits=0, data=None):
+    import _gpu
+    data = W.generate(w) if data is None else data
+    print(f"[attention] B={w.B} Hq={w.Hq} Hkv={w.Hkv} d={w.d} Nq={w.Nq} Ncur={w.Ncur} Nc={w.Nc} "
+          f"bits={w.kbits}/{w.vbits} group={w.group} corr={corr} path={path} splits={splits}", flush=True)
+    kc = _gpu.build_cache(w, data["kc"], w.kbits) if w.Nc > 0 else None
+    vc = _gpu.build_cache(w, data["vc"], w.vbits) if w.Nc > 0 else None
+    out = _gpu.run_attention(w, data, kc, vc, corr=corr, path=path, scale=scale, splits=splits)
+    got = _gpu.out_rows(out)
+    ref = oracle_problem(orc, w, corr, data=data, scale=scale).attention()
+    _gpu.check(got, ref)
+    return got, ref
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+@pytest.mark.parametrize("corr", ["off", "taylor", "exact"])
+@pytest.mark.parametrize("path", ["long", "short"])
+def test_parity(orc, case, corr, path):
+    _compare(orc, CASES[case], corr, path)
+
+
+EDGE = {
+    "no_cache": W.WORKLOADS["h24_int4_cache16k"].scaled(Hq=2, Hkv=2, Nq=70, Ncur=90, Nc=0),
+    "no_current": W.WORKLOADS["h24_int4_cache16k"].scaled(Hq=2, Hkv=2, Nq=70, Ncur=0, Nc=150),
+    "one_query": W.WORKLOADS["gqa_prefill_b16_cache32k"].scaled(B=1, Nq=1, Ncur=1, Nc=700),
+    "one_key": W.WORKLOADS["h40_int2_outliers_cache25k"].scaled(Hq=1, Hkv=1, Nq=33, Ncur=0, Nc=1),
+    "d64_group32": W.WORKLOADS["tiny_d64_int2"].scaled(Hq=4, Hkv=2, Nq=77, Ncur=40, Nc=130, group=32, kbits=4),
+    "group32": W.WORKLOADS["h40_int2_outliers_cache25k"].scaled(Hq=2, Hkv=2, Nq=64, Ncur=64, Nc=200, group=32),
+    "group128": W.WORKLOADS["long_video_cache61k"].scaled(Hq=2, Hkv=2, Nq=64, Ncur=64, Nc=200, group=128),
+    "nq_ne_ncur": W.WORKLOADS["h24_int4_cache16k"].scaled(Hq=3, Hkv=1, Nq=45, Ncur=111, Nc=129),
+    "exact_tiles": W.WORKLOADS["h24_int4_cache16k"].scaled(Hq=1, Hkv=1, Nq=128, Ncur=64, Nc=256),
+}
+
+
+@pytest.mark.parametrize("case", sorted(EDGE))
+@pytest.mark.parametrize("path", ["long", "short"])
+def test_edge_cases(orc, case, path):
+    w = EDGE[case]
+    if path == "short" and w.Nc == 0:
+        pytest.skip("the split path needs cached tokens")
+    for corr in ("off", "taylor", "exact"):
+        _compare(orc, w, corr, path)
+
+
+def test_explicit_scale(orc):
+    _compare(orc, CASES["outliers"], "taylor", "long", scale=0.05)
+    _compare(orc, CASES["gqa"], "exact", "short", scale=0.2)
+
+
+@pytest.mark.parametrize("splits", [1, 3, 7, 64])
+def test_split_counts(orc, splits):
+    _compare(orc, CASES["gqa"], "taylor", "short", splits=splits)
+
+
+def test_correction_matters_and_modes_differ(orc):
+    """The GPU output moves with the correction the way the oracle's does."""
+    w = CASES["outliers"]
+    data = W.generate(w)
+    outs = {c: _compare(orc, w, c, "long", data=data) for c in ("off", "taylor", "exact")}
+    d_gpu = np.abs(outs["taylor"][0] - outs["off"][0]).mean()
+    d_ref = np.abs(outs["taylor"][1] - outs["off"][1]).mean()
+    assert d_ref > 1e-3 and abs(d_gpu - d_ref) < 0.1 * d_ref
+
+
+def test_deterministic(orc):
+    import _gpu
+    w = CASES["gqa"]
+    data = W.generate(w)
+    kc = _gpu.build_cache(w, data["kc"], w.kbits)
+    vc = _gpu.build_cache(w, data["vc"], w.vbits)
+    for path in ("long", "short"):
+        a = _gpu.run_attention(w, data, kc, vc, path=path)
+        b = _gpu.run_attention(w, data, kc, vc, path=path)
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
