@@ -35,7 +35,7 @@ DEFAULT_WORKLOAD = "h24_int4_cache16k"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "cached-key tokens\u00b7queries/s (TFLOP/s eff.) and packed-KV HBM GB/s vs roofline"
-KERNEL_SOURCES = [os.path.join(ROOT, "bit_kv_cache_03_amd", "csrc", f) for f in ("attention.hip", "kvq_api.cpp", "kvq_internal.h")]
+KERNEL_SOURCES = [os.path.join(ROOT, "bit_kv_cache_03_amd", "csrc", f) for f in ("attention.hip", "attention_fast.hip", "kvq_api.cpp", "kvq_internal.h")]
 
 
 def kernel_sha() -> str:

@@ -150,7 +150,9 @@ __global__ __launch_bounds__(kThreads, EXACT ? 1 : 2) void attn_tile_kernel(Attn
       const float lo = __uint_as_float(u[i] << 16), hi = __uint_as_float(u[i] & 0xffff0000u);
       acc += lo * lo + hi * hi;
     }
-    nsum[(16 * s + 8 * h) >> group_shift] += acc;
+    const int gs = (16 * s + 8 * h) >> group_shift;  // group of these 8 values
+#pragma unroll
+    for (int g = 0; g < 4; ++g) nsum[g] += g == gs ? acc : 0.f;
   }
   // correction operand of the queries: slots 3g+{0,1,2} = N_hi, N_hi, N_lo with
   // N_g = tau/24 * ||q_g||^2; lane half h holds slots 8h..8h+7
@@ -436,10 +438,10 @@ __global__ __launch_bounds__(kThreads, EXACT ? 1 : 2) void attn_tile_kernel(Attn
   // ---------------- finalize ----------------
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (SPLIT) {
-    // partial: O (unnormalised) then (m, l), fp32, [split][qrow][D + 2]
+    // partial: O (unnormalised) then (m, l), fp32, [split][qrow][kPartialStride(D)]
     if (row_ok) {
       float *w = static_cast<float *>(p.workspace) +
-                 (static_cast<int64_t>(blockIdx.z) * (p.B * p.Hq * p.Nq) + qrow) * (D + 2);
+                 (static_cast<int64_t>(blockIdx.z) * (p.B * p.Hq * p.Nq) + qrow) * kPartialStride(D);
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -476,13 +478,14 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float *__restri
   const int lane = threadIdx.x & 63;
   if (row >= nrows) return;
   constexpr int PER = D / 64;  // values per lane
+  constexpr int64_t W = kPartialStride(D);
   float m = -INFINITY;
-  for (int s = 0; s < splits; ++s) m = fmaxf(m, ws[(s * nrows + row) * (D + 2) + D]);
+  for (int s = 0; s < splits; ++s) m = fmaxf(m, ws[(s * nrows + row) * W + D]);
   float l = 0.f, acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
   for (int s = 0; s < splits; ++s) {
-    const float *w = ws + (s * nrows + row) * (D + 2);
+    const float *w = ws + (s * nrows + row) * W;
     const float ms = w[D];
     if (ms == -INFINITY) continue;  // empty split
     const float f = exp2f(ms - m);
@@ -530,6 +533,7 @@ hipError_t launch_d(const AttnLaunch &p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_attention_long(const AttnLaunch &p, hipStream_t stream) {
+  if (fast_path_supported(p)) return launch_attention_fast(p, stream, false);
   return p.d == 64 ? launch_d<64, false>(p, stream) : launch_d<128, false>(p, stream);
 }
 
@@ -548,7 +552,8 @@ int short_path_splits(int64_t B, int64_t Hkv, int64_t rows_per_kvhead, int64_t N
 }
 
 size_t short_path_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int32_t d, int splits) {
-  return static_cast<size_t>(splits) * static_cast<size_t>(B * Hq * Nq) * static_cast<size_t>(d + 2) * sizeof(float);
+  return static_cast<size_t>(splits) * static_cast<size_t>(B * Hq * Nq) * static_cast<size_t>(kPartialStride(d)) *
+         sizeof(float);
 }
 
 }  // namespace kvq

@@ -13,6 +13,7 @@ using kvq::AttnLaunch;
 
 constexpr int32_t kAbiVersion = 1;
 constexpr int32_t kMaxSplits = 1024;  // grid z extent of the split path
+constexpr int64_t kMaxTokensPerHead = int64_t(1) << 23;  // 8M tokens: 32-bit in-head offsets
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -43,6 +44,7 @@ kv_status check_qtensor(const kv_qtensor *t, int32_t d, int64_t need_rows) {
   if (t->bits != 2 && t->bits != 4) return KV_ERR_UNSUPPORTED;
   if (!group_ok(t->group, d)) return KV_ERR_UNSUPPORTED;
   if (t->cap < need_rows || t->cap < 0) return KV_ERR_SHAPE;
+  if (t->cap > kMaxTokensPerHead) return KV_ERR_UNSUPPORTED;
   if (!aligned16(t->codes) || !aligned16(t->scale) || !aligned16(t->zero)) return KV_ERR_ALIGN;
   return KV_OK;
 }
@@ -87,6 +89,8 @@ kv_status validate_attention(const kv_attn_args *a) {
   if (!mul_ok(a->B, a->Hq, &t) || !mul_ok(t, a->Nq, &t) || !mul_ok(t, a->d, &nq_el)) return KV_ERR_SHAPE;
   if (!mul_ok(a->B, a->Hkv, &t) || !mul_ok(t, a->Ncur, &t) || !mul_ok(t, a->d, &ncur_el)) return KV_ERR_SHAPE;
   if (a->B * a->Hkv > 65535) return KV_ERR_UNSUPPORTED;
+  // per-head token counts: kernels index rows within a head in 32 bits
+  if (a->Ncur > kMaxTokensPerHead || a->Nc > kMaxTokensPerHead) return KV_ERR_UNSUPPORTED;
   if ((a->Nq * (a->Hq / a->Hkv)) > (int64_t(1) << 40)) return KV_ERR_SHAPE;
   if (!aligned16(a->q) || !aligned16(a->out)) return KV_ERR_ALIGN;
   if (a->Ncur > 0) {

@@ -39,9 +39,16 @@ struct AttnLaunch {
   void *workspace;
 };
 
+// Split path partials: per (split, query row) the unnormalised O[d] then the
+// running max (exp2 domain) and sum, padded to keep rows 16-byte aligned.
+constexpr __host__ __device__ int64_t kPartialStride(int32_t d) { return d + 4; }
+
 hipError_t launch_quantize(const QuantizeLaunch &p, hipStream_t stream);
 hipError_t launch_attention_long(const AttnLaunch &p, hipStream_t stream);
 hipError_t launch_attention_short(const AttnLaunch &p, hipStream_t stream);
+// Throughput kernel (attention_fast.hip): head dim 128, correction off or Taylor.
+bool fast_path_supported(const AttnLaunch &p);
+hipError_t launch_attention_fast(const AttnLaunch &p, hipStream_t stream, bool split);
 
 // Short path: cached-token split count chosen for a problem and the
 // workspace it needs (partials of every split for every query row).

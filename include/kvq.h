@@ -90,7 +90,7 @@ typedef struct {
   float *zero;    /* [B][H][cap][d/group]  zero-point z (the group minimum) */
   int32_t bits;   /* 2 or 4 */
   int32_t group;  /* 32, 64 or 128; divides d */
-  int64_t cap;    /* token capacity (row stride in tokens) */
+  int64_t cap;    /* token capacity (row stride in tokens), at most 2^23 */
 } kv_qtensor;
 
 /*
@@ -119,8 +119,8 @@ kv_status kv_quantize(const void *x, kv_dtype xdt, int64_t B, int64_t H, int64_t
 typedef struct {
   int64_t B, Hq, Hkv; /* Hq % Hkv == 0 */
   int64_t Nq;         /* query rows per head, >= 1 */
-  int64_t Ncur;       /* current-chunk tokens, >= 0 */
-  int64_t Nc;         /* cached tokens in use (rows [0, Nc) of the caches), >= 0 */
+  int64_t Ncur;       /* current-chunk tokens, 0 .. 2^23 */
+  int64_t Nc;         /* cached tokens in use (rows [0, Nc) of the caches), 0 .. 2^23 */
   int32_t d;          /* head dimension: 64 or 128 */
   const void *q;      /* bf16 [B][Hq][Nq][d] */
   const void *k_cur;  /* bf16 [B][Hkv][Ncur][d] (may be NULL if Ncur == 0) */

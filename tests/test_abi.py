@@ -162,7 +162,7 @@ def test_short_path_needs_workspace(kvq):
 def test_short_path_workspace_grows_with_splits(kvq):
     sizes = [kvq.lib.kv_attention_workspace_size(C.byref(_args(kvq, path=2, splits=s))) for s in (1, 2, 4, 8)]
     assert sizes == sorted(sizes) and sizes[0] > 0 and sizes[3] == 8 * sizes[0]
-    assert sizes[0] == 1 * 4 * 8 * (128 + 2) * 4
+    assert sizes[0] == 1 * 4 * 8 * (128 + 4) * 4
 
 
 def test_quantize_argument_errors(kvq):
