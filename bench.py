@@ -86,12 +86,19 @@ def cpu_baseline(w, data, corr: str, target_s: float = 12.0):
     oracle.quantize(data["k"], w.kbits, w.group)
     oracle.quantize(data["v"], w.vbits, w.group)
     t_quant = time.perf_counter() - t0
-    # calibrate, then size the sample for about target_s seconds
-    cal = np.linspace(0, total - 1, num=max(threads, 16)).astype(np.int64)
-    t0 = time.perf_counter()
-    prob.attention(rows=cal, threads=threads)
-    per_row = (time.perf_counter() - t0) / cal.size
-    n = int(min(total, max(cal.size, target_s / max(per_row, 1e-9))))
+    # grow a calibration sample until it runs for a second, then size the
+    # timed sample for about target_s seconds
+    n_cal = max(4 * threads, 16)
+    while True:
+        cal = np.linspace(0, total - 1, num=min(n_cal, total)).astype(np.int64)
+        t0 = time.perf_counter()
+        prob.attention(rows=cal, threads=threads)
+        t_cal = time.perf_counter() - t0
+        if t_cal >= 1.0 or cal.size >= total:
+            break
+        n_cal = int(n_cal * min(8.0, max(2.0, 1.2 / max(t_cal, 1e-3))))
+    per_row = t_cal / cal.size
+    n = int(min(total, max(cal.size, target_s / per_row)))
     rows = np.linspace(0, total - 1, num=n).astype(np.int64)
     t0 = time.perf_counter()
     prob.attention(rows=rows, threads=threads)
@@ -102,6 +109,48 @@ def cpu_baseline(w, data, corr: str, target_s: float = 12.0):
             "sample": f"{n} of {total} query rows (every {total / n:.1f}th, all heads) of {w.name}, "
                       f"fp64 oracle attention with {corr} correction over all {w.Nc}+{w.Ncur} keys, "
                       f"plus the chunk's quantize prorated; {t:.1f} s wall on {threads} threads"}
+
+
+def copy_probe(nbytes: int, reps: int = 3):
+    """A plain streaming kernel of known traffic (reads nbytes, writes
+    nbytes: an elementwise negation), profiled beside the attention to scale
+    the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
+
+
+def _counter_mean(csv_path: str, counter: str, kernel_substr: str) -> float:
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path))
+            if r["Counter_Name"] == counter and kernel_substr in r["Kernel_Name"]]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for kernels matching {kernel_substr!r} in {csv_path}")
+    return float(np.mean(vals))
+
+
+def write_traffic(w, pmc_dir: str, copy_bytes: int):
+    """HBM bytes per attention launch from four rocprofv3 --pmc runs under
+    pmc_dir (fetch/, write/: the bench; copy_fetch/, copy_write/: the copy
+    probe), each counter scaled by bytes/KiB-reading of the plain copy."""
+    f = lambda sub: os.path.join(pmc_dir, sub, "run_counter_collection.csv")
+    kname = "attn_"
+    fetch_kib = _counter_mean(f("fetch"), "FETCH_SIZE", kname)
+    write_kib = _counter_mean(f("write"), "WRITE_SIZE", kname)
+    cf = copy_bytes / (1024.0 * _counter_mean(f("copy_fetch"), "FETCH_SIZE", "neg"))
+    cw = copy_bytes / (1024.0 * _counter_mean(f("copy_write"), "WRITE_SIZE", "neg"))
+    t = {"workload": w.name, "kernel_sha": kernel_sha(), "fetch_kib": fetch_kib, "write_kib": write_kib,
+         "copy_bytes": copy_bytes, "fetch_factor": cf, "write_factor": cw,
+         "bytes_per_launch": 1024.0 * (fetch_kib * cf + write_kib * cw),
+         "algorithmic_packed_bytes": packed_bytes(w)}
+    out = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
+    with open(out, "w") as fh:
+        json.dump(t, fh, indent=1)
+    print(json.dumps(t))
 
 
 def main():
@@ -115,12 +164,24 @@ def main():
     ap.add_argument("--nq", type=int, default=0, help="override query rows (and current chunk) per head")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-overhead", action="store_true", help="skip the correction-off timing")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (counter calibration)")
+    ap.add_argument("--traffic", default=None, metavar="PMC_DIR",
+                    help="only turn rocprofv3 FETCH_SIZE/WRITE_SIZE runs into profiles/traffic_<workload>.json")
+    ap.add_argument("--copy-bytes", type=int, default=1 << 30)
     args = ap.parse_args()
+    if args.traffic:
+        write_traffic(W.WORKLOADS[args.workload], args.traffic, args.copy_bytes)
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
 
     import torch
     from bit_kv_cache_03_amd import kvq

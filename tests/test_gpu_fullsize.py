@@ -1,0 +1,62 @@
+"""The large workloads at their full sizes, in the launch configuration that
+bench.py times (path chosen by the library, the workload's correction, the
+cache built by kv_quantize one chunk at a time): the whole quantized cache
+bit-exact against the oracle's quantizer, and sampled attention rows (first
+and last rows of spread heads, the ragged last tile, random rows) against
+the oracle computed row by row.  Same bar as the small parity tests: max
+|out - ref| <= 2e-2 against the fp64 oracle, mean |out - bf16(ref)| <= 1e-3.
+
+Also the short-query regime on the GQA workload's cache (few query rows per
+KV head, the split-over-cache path)."""
+import numpy as np
+import pytest
+
+from bit_kv_cache_03_amd import workloads as W
+from _problems import as_bf16
+
+pytestmark = pytest.mark.gpu
+
+BIG = ["h24_int4_cache16k", "h40_int2_outliers_cache25k", "gqa_prefill_b16_cache32k", "long_video_cache61k"]
+
+
+def _bits_equal(a, b):
+    return np.array_equal(np.ascontiguousarray(a).view(np.uint8), np.ascontiguousarray(b).view(np.uint8))
+
+
+def _run(orc, w, corrs, nsample=48, check_cache=True):
+    import _gpu
+    print(f"[fullsize] {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Ncur={w.Ncur} Nc={w.Nc} "
+          f"bits={w.kbits}/{w.vbits}", flush=True)
+    data = W.generate(w)
+    kc = _gpu.build_cache(w, data["kc"], w.kbits, cap=w.Nc + w.Ncur)
+    vc = _gpu.build_cache(w, data["vc"], w.vbits, cap=w.Nc + w.Ncur)
+    okc = orc.quantize(data["kc"], w.kbits, w.group)
+    ovc = orc.quantize(data["vc"], w.vbits, w.group)
+    if check_cache:
+        for gc, ref, name in ((kc, okc, "K"), (vc, ovc, "V")):
+            got = _gpu.cache_to_host(gc, w.Nc)
+            for g, r, what in zip(got, ref, ("codes", "step", "zero")):
+                assert _bits_equal(g, r), (name, what)
+        print("    cache bit-exact", flush=True)
+    rows = W.sample_rows(w, nsample)
+    for corr in corrs:
+        out = _gpu.run_attention(w, data, kc, vc, corr=corr)
+        got = _gpu.out_rows(out, rows)
+        prob = orc.Problem(as_bf16(data["q"]), as_bf16(data["k"]), as_bf16(data["v"]), okc, ovc, w.Nc,
+                           w.kbits, w.vbits, w.group, corr=corr)
+        ref = prob.attention(rows=rows)
+        _gpu.check(got, ref, label=f"{corr:7s} rows={rows.size} ")
+
+
+@pytest.mark.parametrize("wname", BIG)
+def test_fullsize_sampled(orc, wname):
+    w = W.WORKLOADS[wname]
+    _run(orc, w, (w.corr, "off") if wname == "h24_int4_cache16k" else (w.corr,))
+
+
+@pytest.mark.parametrize("nq", [1, 16, 64])
+def test_short_query_on_gqa_cache(orc, nq):
+    """Nq = Ncur in {1, 16, 64} over the full 32k-token GQA cache (4 to 256
+    query rows per KV head)."""
+    w = W.WORKLOADS["gqa_prefill_b16_cache32k"].scaled(Nq=nq, Ncur=nq)
+    _run(orc, w, ("taylor", "exact"), nsample=64, check_cache=False)
