@@ -533,7 +533,7 @@ hipError_t launch_d(const AttnLaunch &p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_attention_long(const AttnLaunch &p, hipStream_t stream) {
-  if (fast_path_supported(p)) return launch_attention_fast(p, stream, false);
+  if (fast_path_supported(p)) return launch_attention_fast(p, stream);
   return p.d == 64 ? launch_d<64, false>(p, stream) : launch_d<128, false>(p, stream);
 }
 

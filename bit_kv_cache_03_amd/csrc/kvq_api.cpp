@@ -134,6 +134,8 @@ Plan plan_attention(const kv_attn_args *a, bool query_device) {
     const int cus = query_device ? device_cu_count() : 256;
     pl.splits = a->splits > 0 ? a->splits : kvq::short_path_splits(a->B, a->Hkv, rows, a->Nc, cus);
     pl.workspace = kvq::short_path_workspace_bytes(a->B, a->Hq, a->Nq, a->d, pl.splits);
+  } else if (a->d == 128 && a->corr != KV_CORR_EXACT) {  // the throughput kernel
+    pl.workspace = kvq::fast_path_workspace_bytes(a->B, a->Hkv);
   }
   return pl;
 }

@@ -46,9 +46,11 @@ constexpr __host__ __device__ int64_t kPartialStride(int32_t d) { return d + 4; 
 hipError_t launch_quantize(const QuantizeLaunch &p, hipStream_t stream);
 hipError_t launch_attention_long(const AttnLaunch &p, hipStream_t stream);
 hipError_t launch_attention_short(const AttnLaunch &p, hipStream_t stream);
-// Throughput kernel (attention_fast.hip): head dim 128, correction off or Taylor.
+// Throughput kernel (attention_fast.hip): head dim 128, correction off or
+// Taylor.  Its workspace holds one int32 key-scale exponent per (b, KV head).
 bool fast_path_supported(const AttnLaunch &p);
-hipError_t launch_attention_fast(const AttnLaunch &p, hipStream_t stream, bool split);
+size_t fast_path_workspace_bytes(int64_t B, int64_t Hkv);
+hipError_t launch_attention_fast(const AttnLaunch &p, hipStream_t stream);
 
 // Short path: cached-token split count chosen for a problem and the
 // workspace it needs (partials of every split for every query row).

@@ -153,10 +153,24 @@ def test_short_path_needs_workspace(kvq):
     assert _attn(kvq, a) == kvq.KV_ERR_WORKSPACE
     a = _args(kvq, path=2, workspace=0x40000004, workspace_bytes=need)
     assert _attn(kvq, a) == kvq.KV_ERR_ALIGN
-    # long path needs none; invalid arguments report 0
-    assert kvq.lib.kv_attention_workspace_size(C.byref(_args(kvq, path=1))) == 0
+    # invalid arguments report 0
     assert kvq.lib.kv_attention_workspace_size(C.byref(_args(kvq, B=0))) == 0
     assert kvq.lib.kv_attention_workspace_size(None) == 0
+
+
+def test_long_path_workspace(kvq):
+    """The head-dim-128 long path keeps one int32 key-scale exponent per
+    (batch, KV head), rounded up to 256 bytes; the general kernel (head dim
+    64, or the exact correction) needs none."""
+    size = lambda **kw: kvq.lib.kv_attention_workspace_size(C.byref(_args(kvq, path=1, **kw)))
+    assert size() == 256
+    assert size(B=3, Hq=80, Hkv=40) == 512          # 120 heads x 4 B -> 480 -> 512
+    assert size(corr=2) == 0
+    assert size(d=64) == 0
+    a = _args(kvq, path=1)
+    assert _attn(kvq, a) == kvq.KV_ERR_WORKSPACE
+    a = _args(kvq, path=1, workspace=0x40000000, workspace_bytes=255)
+    assert _attn(kvq, a) == kvq.KV_ERR_WORKSPACE
 
 
 def test_short_path_workspace_grows_with_splits(kvq):
