@@ -90,10 +90,48 @@ __device__ inline float sum8(bf16x8 v, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.w), one, acc, false);
 }
 
+// Codes as fp16 "magic" values 1024 + c (exact: the fp16 spacing at 1024 is
+// 1), built two at a time: m[j] holds codes j (low half) and j + 4 (high
+// half) of 8 codes of BITS bits stored LSB first in the low 8*BITS bits of
+// w.  A value z + D c is then fma(1024 + c, D, z - 1024 D) in fp32, which
+// v_fma_mix evaluates straight from the fp16 half and rounds to fp16.
+// The code mask is held in a vector register (`mask`, from opaque_u32) so
+// that each pair is one v_and_or_b32: gfx950's VOP3 encodings take no
+// literal, and with both constants literal the compiler emits and + or.
+__device__ inline uint32_t opaque_u32(uint32_t x) {
+  uint32_t r;
+  asm("v_mov_b32 %0, %1" : "=v"(r) : "s"(x));
+  return r;
+}
+template <int BITS>
+__device__ inline void magic8(uint32_t w, uint32_t mask, uint32_t (&m)[4]) {
+  if (BITS == 4) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m[j] = ((w >> (4 * j)) & mask) | 0x64006400u;
+  } else {
+    const uint32_t x = (w & 0xffffu) | ((w & 0xffffu) << 8);  // code j + 4 now also at bit 2j + 16
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m[j] = ((x >> (2 * j)) & mask) | 0x64006400u;
+  }
+}
+__device__ inline float magic_code(const uint32_t (&m)[4], int e) {  // 1024 + code e
+  const f16x2 h = __builtin_bit_cast(f16x2, m[e & 3]);
+  return static_cast<float>((e >> 2) ? h.y : h.x);
+}
+template <int BITS>
+constexpr uint32_t kCodeMask = BITS == 4 ? 0x000f000fu : 0x00030003u;
+
+// fma(1024 + code, s, z) rounded to fp16 (one v_fma_mix per value).
+__device__ inline _Float16 dequant_h(float magic, float s, float z) { return static_cast<_Float16>(fmaf(magic, s, z)); }
+__device__ inline uint32_t pair_h(_Float16 lo, _Float16 hi) {
+  const f16x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // V^T element (row = head-dim index, col = permuted key slot 0..63).  The
-// 16-byte chunks of a row are XOR-swizzled by (row / 16) % 8.  With 64 LDS
-// banks and a 144-byte row stride an operand read (16 lanes = 16
-// consecutive rows, one chunk) lands on disjoint bank quads.
+// 16-byte chunks of a row are XOR-swizzled by (row / 16) % 8, which spreads
+// the transposed 4-byte stores of unpack_v over the banks; operand reads
+// stay 16-byte aligned.
 __device__ inline int vt_index(int row, int col) {
   return row * VS + ((((col >> 3) ^ (row >> 4)) & 7) << 3) + (col & 7);
 }
@@ -187,6 +225,7 @@ struct Ctx {
   int ng, group_shift;
   int beg, end;     // key range of the segment
   float kscale;     // 2^-ek
+  uint32_t kmask;   // code mask of magic8, in a vector register
 };
 
 struct Soft {
@@ -197,6 +236,7 @@ struct Soft {
 // Thread roles in fetch / unpack:
 //  K: key tid / 8, values 16 * (tid % 8) .. +16
 //  V: keys 2*kq, 2*kq+1 with kq = tid / 16, values 8 * (tid % 16) .. +8
+//     (a wave reads 4 keys' rows whole: 16 lanes per row)
 // Rows past the end of the segment clamp to its last row (always in bounds).
 template <bool CACHED, int KBITS>
 __device__ inline void fetch_k(const Ctx &c, int k0, int tid, Fetch &f) {
@@ -268,11 +308,12 @@ __device__ inline void unpack_k_item(int p, const Ctx &c, int tid, const Fetch &
   if (p < 2) {
     uint32_t w[4];
     if (CACHED) {
-      float cv[8];
-      codes8<KBITS>(KBITS == 4 ? f.kw[p] : (f.kw[0] >> (16 * p)), cv);
-      const float s = f.kstep * c.kscale, z = f.kzero * c.kscale;
+      uint32_t m[4];
+      magic8<KBITS>(KBITS == 4 ? f.kw[p] : (f.kw[0] >> (16 * p)), c.kmask, m);
+      const float s = f.kstep * c.kscale, z = fmaf(-1024.0f, f.kstep, f.kzero) * c.kscale;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = pack2h(fmaf(s, cv[2 * e], z), fmaf(s, cv[2 * e + 1], z));
+      for (int e = 0; e < 4; ++e)
+        w[e] = pair_h(dequant_h(magic_code(m, 2 * e), s, z), dequant_h(magic_code(m, 2 * e + 1), s, z));
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -404,9 +445,9 @@ constexpr int kNqk = CACHED && TAYLOR ? 18 : 16;
 
 __device__ constexpr int qk_off(int j) { return (j & 1) * 32 * KS + (j < 16 ? 16 * (j >> 1) : KEXT); }
 
-// O^T += V^T P^T: MFMA j = (k-step j / 4, head-dim block j % 4).  With the
-// swizzle of vt_index the fragment of (row 32 db + qc, slot 16 ks + 8 h)
-// sits at the lane's base (qc * VS + 8 * (h ^ (qc / 16))) plus a constant.
+// O^T += V^T P^T: MFMA j = (k-step j / 4, head-dim block j % 4); the
+// fragment of (row 32 db + qc, slot 16 ks + 8 h) sits at the lane's base
+// (qc * VS + 8 h) plus a constant.
 __device__ constexpr int pv_off(int j) { return 32 * (j & 3) * VS + 16 * ((j >> 2) ^ (j & 3)); }
 
 __device__ inline uint4 lds16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
@@ -420,9 +461,9 @@ __device__ inline uint4 lds16(const uint16_t *p) { return *reinterpret_cast<cons
 //   NEXT: dequantise tile t+1 from f into K buffer Kn / V buffer Vn, and
 //         fetch tile t+2 (rows clamp into the segment).
 template <bool CACHED, bool TAYLOR, int KBITS, int VBITS, bool QK, bool PREV, bool NEXT, bool MASK>
-__device__ inline void tile_step(const Ctx &c, const QState &qs, Soft &st, Fetch &f, f32x16 (&s)[2],
-                                 const uint16_t *Kl, uint16_t *Kn, const uint16_t *Vp, uint16_t *Vn, int k0_next2,
-                                 int count, int tid) {
+__device__ inline void tile_step(const Ctx &c, const QState &qs, Soft &st, Fetch &f, const f32x16 (&s)[2],
+                                 f32x16 (&sn)[2], const uint16_t *Kl, uint16_t *Kn, const uint16_t *Vp, uint16_t *Vn,
+                                 int k0_next2, int count, int tid) {
   const int lane = tid & 63, qc = lane & 31, h = lane >> 5;
   const uint16_t *Kb = Kl + qc * KS + 8 * h;
   const uint16_t *Vb = Vp + qc * VS + 8 * (h ^ (qc >> 4));
@@ -431,7 +472,6 @@ __device__ inline void tile_step(const Ctx &c, const QState &qs, Soft &st, Fetch
   uint4 buf[4];
   float ev[8];
   bf16x8 pk[4];
-  f32x16 sn[2];
 
   // 1. S_t (fp16 keys, bf16 correction step), with the exponentials of t-1
   if (QK) {
@@ -481,11 +521,7 @@ __device__ inline void tile_step(const Ctx &c, const QState &qs, Soft &st, Fetch
       KVQ_FENCE();
     }
   }
-  if (QK) {
-    max_update(mt, st);
-    s[0] = sn[0];
-    s[1] = sn[1];
-  }
+  if (QK) max_update(mt, st);
 }
 
 #undef KVQ_FENCE
@@ -498,7 +534,6 @@ __device__ inline void segment(const Ctx &c, const QState &qs, Soft &st, uint16_
   if (nt == 0) return;
   const int tail = c.end - c.beg - (nt - 1) * BN;  // keys in the last tile
   Fetch f;
-  f32x16 s[2];
   {
     VWork u;
     fetch_k<CACHED, KBITS>(c, c.beg, tid, f);
@@ -513,36 +548,58 @@ __device__ inline void segment(const Ctx &c, const QState &qs, Soft &st, uint16_
     fetch_v<CACHED, VBITS>(c, c.beg + BN, tid, 1, f);
   }
   __syncthreads();
+  // Scores alternate between sa and sb: step t reads S_{t-1} from one and
+  // writes S_t to the other.
+  f32x16 sa[2], sb[2];
   // t = 0: S_0 only (and tile 1 into LDS when there is one)
   if (nt > 1)
-    tile_step<CACHED, TAYLOR, KBITS, VBITS, true, false, true, false>(c, qs, st, f, s, Kl, Kl + KBUF, Vl, Vl + VBUF,
-                                                                      c.beg + 2 * BN, BN, tid);
+    tile_step<CACHED, TAYLOR, KBITS, VBITS, true, false, true, false>(c, qs, st, f, sb, sa, Kl, Kl + KBUF, Vl,
+                                                                      Vl + VBUF, c.beg + 2 * BN, BN, tid);
   else
-    tile_step<CACHED, TAYLOR, KBITS, VBITS, true, false, false, false>(c, qs, st, f, s, Kl, Kl + KBUF, Vl,
+    tile_step<CACHED, TAYLOR, KBITS, VBITS, true, false, false, false>(c, qs, st, f, sb, sa, Kl, Kl + KBUF, Vl,
                                                                        Vl + VBUF, 0, BN, tid);
   __syncthreads();
-  // steady state: S_t, P_{t-1} V_{t-1}, tile t+1 into LDS
+  // steady state: S_t, P_{t-1} V_{t-1}, tile t+1 into LDS; two steps per trip
   int vb = 0;  // V buffer of tile t-1
-  for (int t = 1; t < nt - 1; ++t) {
-    const int vn = vb + 2 < NVBUF ? vb + 2 : vb + 2 - NVBUF;
-    tile_step<CACHED, TAYLOR, KBITS, VBITS, true, true, true, false>(
-        c, qs, st, f, s, Kl + (t & 1) * KBUF, Kl + ((t + 1) & 1) * KBUF, Vl + vb * VBUF, Vl + vn * VBUF,
-        c.beg + (t + 2) * BN, BN, tid);
-    vb = vb + 1 < NVBUF ? vb + 1 : 0;
+  int t = 1;
+  for (; t + 1 < nt - 1; t += 2) {
+    const int v1 = vb + 1 < NVBUF ? vb + 1 : 0, v2 = v1 + 1 < NVBUF ? v1 + 1 : 0, v3 = vb;
+    tile_step<CACHED, TAYLOR, KBITS, VBITS, true, true, true, false>(c, qs, st, f, sa, sb, Kl + KBUF, Kl,
+                                                                     Vl + vb * VBUF, Vl + v2 * VBUF,
+                                                                     c.beg + (t + 2) * BN, BN, tid);
     __syncthreads();
+    tile_step<CACHED, TAYLOR, KBITS, VBITS, true, true, true, false>(c, qs, st, f, sb, sa, Kl, Kl + KBUF,
+                                                                     Vl + v1 * VBUF, Vl + v3 * VBUF,
+                                                                     c.beg + (t + 3) * BN, BN, tid);
+    __syncthreads();
+    vb = v2;
   }
-  if (nt > 1) {  // t = nt - 1: S_{nt-1}, P_{nt-2} V_{nt-2}
-    tile_step<CACHED, TAYLOR, KBITS, VBITS, true, true, false, false>(c, qs, st, f, s, Kl + ((nt - 1) & 1) * KBUF,
+  if (t < nt - 1) {  // one more steady step (t odd: K buffer 1, S_t into sb)
+    const int vn = vb + 2 < NVBUF ? vb + 2 : vb + 2 - NVBUF;
+    tile_step<CACHED, TAYLOR, KBITS, VBITS, true, true, true, false>(c, qs, st, f, sa, sb, Kl + KBUF, Kl,
+                                                                     Vl + vb * VBUF, Vl + vn * VBUF,
+                                                                     c.beg + (t + 2) * BN, BN, tid);
+    __syncthreads();
+    vb = vb + 1 < NVBUF ? vb + 1 : 0;
+    ++t;
+    sa[0] = sb[0];
+    sa[1] = sb[1];
+  }
+  // here t = nt - 1 (nt > 1) with S_{t-1} in sa, or nt == 1 with S_0 in sa
+  if (nt > 1) {  // S_{nt-1}, P_{nt-2} V_{nt-2}
+    tile_step<CACHED, TAYLOR, KBITS, VBITS, true, true, false, false>(c, qs, st, f, sa, sb, Kl + ((nt - 1) & 1) * KBUF,
                                                                       Kl, Vl + vb * VBUF, Vl, 0, BN, tid);
     vb = vb + 1 < NVBUF ? vb + 1 : 0;
+    sa[0] = sb[0];
+    sa[1] = sb[1];
   }
   // drain: P_{nt-1} V_{nt-1}
   if (tail == BN)
-    tile_step<CACHED, TAYLOR, KBITS, VBITS, false, true, false, false>(c, qs, st, f, s, Kl, Kl, Vl + vb * VBUF, Vl,
-                                                                       0, BN, tid);
+    tile_step<CACHED, TAYLOR, KBITS, VBITS, false, true, false, false>(c, qs, st, f, sa, sb, Kl, Kl,
+                                                                       Vl + vb * VBUF, Vl, 0, BN, tid);
   else
-    tile_step<CACHED, TAYLOR, KBITS, VBITS, false, true, false, true>(c, qs, st, f, s, Kl, Kl, Vl + vb * VBUF, Vl,
-                                                                      0, tail, tid);
+    tile_step<CACHED, TAYLOR, KBITS, VBITS, false, true, false, true>(c, qs, st, f, sa, sb, Kl, Kl, Vl + vb * VBUF,
+                                                                      Vl, 0, tail, tid);
   __syncthreads();
 }
 
@@ -633,6 +690,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_fast_kernel(AttnLaunch p, int
   c.ng = ng;
   c.group_shift = group_shift;
   c.kscale = ldexpf(1.0f, -ek);
+  c.kmask = opaque_u32(kCodeMask<KBITS>);
   if (p.Nc > 0) {
     const int64_t hrow = bkv * p.cap;  // first cache row of this head
     c.kc_codes = p.kc_codes + hrow * (D * KBITS / 8);
