@@ -538,7 +538,17 @@ hipError_t launch_attention_long(const AttnLaunch &p, hipStream_t stream) {
 }
 
 hipError_t launch_attention_short(const AttnLaunch &p, hipStream_t stream) {
+  if (short_fast_supported(p.d, p.corr)) return launch_attention_short_fast(p, stream);
   return p.d == 64 ? launch_d<64, true>(p, stream) : launch_d<128, true>(p, stream);
+}
+
+hipError_t launch_combine(const float *ws, uint16_t *out, int64_t nrows, int splits, int32_t d, hipStream_t stream) {
+  const dim3 grid(static_cast<uint32_t>((nrows + 3) / 4));
+  if (d == 64)
+    attn_combine_kernel<64><<<grid, dim3(256), 0, stream>>>(ws, out, nrows, splits);
+  else
+    attn_combine_kernel<128><<<grid, dim3(256), 0, stream>>>(ws, out, nrows, splits);
+  return hipGetLastError();
 }
 
 int short_path_splits(int64_t B, int64_t Hkv, int64_t rows_per_kvhead, int64_t Nc, int cu_count) {

@@ -51,10 +51,21 @@ hipError_t launch_attention_short(const AttnLaunch &p, hipStream_t stream);
 bool fast_path_supported(const AttnLaunch &p);
 size_t fast_path_workspace_bytes(int64_t B, int64_t Hkv);
 hipError_t launch_attention_fast(const AttnLaunch &p, hipStream_t stream);
+// Pre-pass of the fp16 kernels: per (b, KV head) the exponent ek with the
+// largest |key| (dequantised cache and current chunk) times 2^-ek below 2^15.
+void launch_key_scale(const AttnLaunch &p, hipStream_t stream, int32_t *exps);
 
 // Short path: cached-token split count chosen for a problem and the
 // workspace it needs (partials of every split for every query row).
 int short_path_splits(int64_t B, int64_t Hkv, int64_t rows_per_kvhead, int64_t Nc, int cu_count);
 size_t short_path_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int32_t d, int splits);
+// Log-sum-exp merge of split partials into the bf16 output.
+hipError_t launch_combine(const float *ws, uint16_t *out, int64_t nrows, int splits, int32_t d, hipStream_t stream);
+// Short-query kernel (attention_short.hip): head dim 128, correction off or
+// Taylor; workspace = the split partials, then one int32 key-scale exponent
+// per (b, KV head) (fast_path_workspace_bytes).
+bool short_fast_supported(int32_t d, int corr);
+int short_fast_splits(int64_t B, int64_t Hkv, int64_t rows_per_kvhead, int64_t Nc, int64_t Ncur, int cu_count);
+hipError_t launch_attention_short_fast(const AttnLaunch &p, hipStream_t stream);
 
 }  // namespace kvq
