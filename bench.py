@@ -35,7 +35,7 @@ DEFAULT_WORKLOAD = "h24_int4_cache16k"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "cached-key tokens\u00b7queries/s (TFLOP/s eff.) and packed-KV HBM GB/s vs roofline"
-KERNEL_SOURCES = [os.path.join(ROOT, "bit_kv_cache_03_amd", "csrc", f) for f in ("attention.hip", "attention_fast.hip", "kvq_api.cpp", "kvq_internal.h")]
+KERNEL_SOURCES = [os.path.join(ROOT, "bit_kv_cache_03_amd", "csrc", f) for f in ("attention.hip", "attention_fast.hip", "attention_short.hip", "kvq_device.h", "kvq_api.cpp", "kvq_internal.h")]
 
 
 def kernel_sha() -> str:
@@ -197,7 +197,9 @@ def main():
     cap = w.Nc + w.Ncur
     kc = kvq.QCache(w.B, w.Hkv, cap, w.d, w.kbits, w.group)
     vc = kvq.QCache(w.B, w.Hkv, cap, w.d, w.vbits, w.group)
-    chunk = max(w.Ncur, 1)
+    # the cache content does not depend on how it is appended (quantisation
+    # is per token), so short chunks are appended in >= 4096-token calls
+    chunk = max(w.Ncur, 4096)
     for off in range(0, w.Nc, chunk):
         n = min(chunk, w.Nc - off)
         kvq.quantize(dev(np.ascontiguousarray(data["kc"][:, :, off:off + n])), kc, off)

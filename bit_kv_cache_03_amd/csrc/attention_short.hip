@@ -9,10 +9,12 @@
 // of the row group, with private LDS tiles (no barrier inside the loop).
 // The waves merge at the end (log-sum-exp), and the splits are merged by
 // attn_combine_kernel.  Numerics match the throughput kernel: keys in fp16
-// (magic-code dequantisation, per-head power-of-two scale from the
-// pre-pass), per-row query scale, probabilities and values in bf16, the
-// Taylor correction of the cached scores as one extra bf16 MFMA step
-// ("量化鍵值偷走注意力…" (agents-report.net), §方法 and §為何校正有效).
+// (magic-code dequantisation), per-row query scale, probabilities and values
+// in bf16, the Taylor correction of the cached scores as one extra bf16
+// MFMA step ("量化鍵值偷走注意力…" (agents-report.net), §方法 and §為何校正有效).
+// The keys' power-of-two fp16 scale is chosen per 32-key block from that
+// block's own steps and zero points (or values), and folded into the
+// softmax scale of the block, so no pass over the whole cache is needed.
 //
 // Per block (per wave): dequantise K (rows = keys) and V^T (rows = head
 // dimension, keys in the permuted order of the P operand) into LDS, fetch
@@ -64,9 +66,15 @@ struct Ctx {
   const uint16_t *k_cur, *v_cur;
   int ng, group_shift;
   int nc, ncur;     // segment lengths
-  float kscale;     // 2^-ek
   uint32_t kmask;   // code mask of magic8 (vector register)
 };
+
+// Largest of x over the wave.
+__device__ inline float wave_max(float x) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
 
 // Lane roles (per wave):
 //  K: key kr = lane % 32 of the block, head-dim half h = lane / 32
@@ -121,15 +129,23 @@ __device__ inline void fetch_cached(const Ctx &c, int k0, int lane, Fetch &f) {
 // and, for the Taylor correction, the slots 4g+{0,1,2,3} = (-D_g^2 split
 // hi, lo, hi; 0) in bf16 (zero for g >= d/group); lane h writes slots
 // 8h .. 8h+7 (groups 2h, 2h+1).
+// Returns the block's key exponent e (keys stored as k * 2^-e): the
+// dequantised values lie between z and z + (2^bits - 1) D of their group.
 template <bool TAYLOR, int KBITS>
-__device__ inline void unpack_k_cached(const Ctx &c, int lane, const Fetch &f, uint16_t *Kt) {
+__device__ inline int unpack_k_cached(const Ctx &c, int lane, const Fetch &f, uint16_t *Kt) {
   const int kr = lane & 31, h = lane >> 5;
   uint16_t *row = Kt + kr * KS;
+  float bound = 0.f;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    bound = fmaxf(bound, fmaxf(fabsf(f.kzero[j]), fabsf(fmaf(f.kstep[j], static_cast<float>((1 << KBITS) - 1), f.kzero[j]))));
+  const int e = scale_exponent(wave_max(bound));
+  const float kscale = ldexpf(1.0f, -e);
   float sj[2], zj[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    sj[j] = f.kstep[j] * c.kscale;
-    zj[j] = fmaf(-1024.0f, f.kstep[j], f.kzero[j]) * c.kscale;
+    sj[j] = f.kstep[j] * kscale;
+    zj[j] = fmaf(-1024.0f, f.kstep[j], f.kzero[j]) * kscale;
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {  // values d = 64h + 8i .. +7, in the group of d = 64h + 32 (i / 4)
@@ -147,13 +163,14 @@ __device__ inline void unpack_k_cached(const Ctx &c, int lane, const Fetch &f, u
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int g = 2 * h + j;
-      const float sq = g < c.ng ? f.gstep[j] * f.gstep[j] : 0.f;
+      const float sq = g < c.ng ? f.gstep[j] * f.gstep[j] * kscale : 0.f;
       const float hsq = lo_f(pack2(sq, 0.f));
       x[2 * j] = pack2(-hsq, -(sq - hsq));
       x[2 * j + 1] = pack2(-hsq, 0.f);
     }
     *reinterpret_cast<uint4 *>(row + KEXT + 8 * h) = make_uint4(x[0], x[1], x[2], x[3]);
   }
+  return e;
 }
 
 // V^T tile of a cached block: bf16 values of keys 4kq..4kq+3 (adjacent
@@ -181,20 +198,32 @@ __device__ inline void unpack_v_cached(int lane, const Fetch &f, uint16_t *Vt) {
   }
 }
 
-// Current-chunk block (bf16 keys and values, loaded and written directly).
-__device__ inline void unpack_current(const Ctx &c, int k0, int lane, uint16_t *Kt, uint16_t *Vt) {
+// Current-chunk block (bf16 keys and values, loaded and written directly);
+// returns the block's key exponent like unpack_k_cached.
+__device__ inline int unpack_current(const Ctx &c, int k0, int lane, uint16_t *Kt, uint16_t *Vt) {
   const int last = c.ncur - 1;
+  int ek;
   {
     const int kr = lane & 31, h = lane >> 5;
     const uint32_t row = static_cast<uint32_t>(k0 + kr <= last ? k0 + kr : last);
     const uint4 *ks = reinterpret_cast<const uint4 *>(c.k_cur + (row * D + 64u * h));
+    uint4 x[8];
+    float bound = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint4 x = ks[i];
-      const uint32_t u[4] = {x.x, x.y, x.z, x.w};
+      x[i] = ks[i];
+      const uint32_t u[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bound = fmaxf(bound, fmaxf(fabsf(lo_f(u[e])), fabsf(hi_f(u[e]))));
+    }
+    ek = scale_exponent(wave_max(bound));
+    const float kscale = ldexpf(1.0f, -ek);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t u[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
       uint32_t w[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = pack2h(lo_f(u[e]) * c.kscale, hi_f(u[e]) * c.kscale);
+      for (int e = 0; e < 4; ++e) w[e] = pack2h(lo_f(u[e]) * kscale, hi_f(u[e]) * kscale);
       *reinterpret_cast<uint4 *>(Kt + kr * KS + 64 * h + 8 * i) = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
@@ -227,6 +256,7 @@ __device__ inline void unpack_current(const Ctx &c, int k0, int lane, uint16_t *
             make_uint2(__builtin_amdgcn_perm(u[1], u[0], 0x07060302u), __builtin_amdgcn_perm(u[3], u[2], 0x07060302u));
       }
   }
+  return ek;
 }
 
 struct Soft {
@@ -238,7 +268,8 @@ struct Soft {
 // count < BK marks a ragged block; CORR adds the correction step.
 template <bool CORR>
 __device__ inline void block_compute(const uint16_t *Kt, const uint16_t *Vt, const f16x8 (&q)[8], bf16x8 qext,
-                                     int count, int lane, Soft &st) {
+                                     int count, int ek, int lane, Soft &st) {
+  const float alpha = ldexpf(st.alpha, ek);  // scores of this block are q.k * 2^-(eq+ek)
   const int qc = lane & 31, h = lane >> 5;
   f32x16 s = f32x16{};
   const uint16_t *kb = Kt + qc * KS + 8 * h;
@@ -255,7 +286,7 @@ __device__ inline void block_compute(const uint16_t *Kt, const uint16_t *Vt, con
   float mt = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[i]);
-  mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * st.alpha;
+  mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * alpha;
   const bool grow = mt > st.m + kLazy;
   if (__any(grow)) {
     const float m_new = grow ? mt : st.m;
@@ -270,7 +301,7 @@ __device__ inline void block_compute(const uint16_t *Kt, const uint16_t *Vt, con
   for (int hf = 0; hf < 2; ++hf) {
     float e[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) e[i] = __builtin_amdgcn_exp2f(fmaf(s[8 * hf + i], st.alpha, -st.m));
+    for (int i = 0; i < 8; ++i) e[i] = __builtin_amdgcn_exp2f(fmaf(s[8 * hf + i], alpha, -st.m));
     pk[hf] = __builtin_bit_cast(bf16x8, make_uint4(pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]),
                                                    pack2(e[6], e[7])));
     st.l = sum8(pk[hf], st.l);
@@ -289,7 +320,7 @@ __device__ inline void block_compute(const uint16_t *Kt, const uint16_t *Vt, con
 template <int KBITS, int VBITS, bool TAYLOR>
 __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, int32_t group_shift,
                                                                 int64_t rows_per_kvhead, int32_t row_groups,
-                                                                int32_t nsplit, const int32_t *kexp, float *ws) {
+                                                                int32_t nsplit, float *ws) {
   __shared__ __attribute__((aligned(16))) uint16_t L[WAVES * WLDS];
 
   const int tid = threadIdx.x;
@@ -308,7 +339,6 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
   const int64_t bkv = rest / row_groups;
   const int64_t b = bkv / p.Hkv, hk = bkv - b * p.Hkv;
   const int64_t gq = p.Hq / p.Hkv;
-  const int ek = kexp[bkv];
 
   // the lane's query row (all 4 waves hold the same 32 rows)
   const int64_t r = rg * 32 + qc;
@@ -318,7 +348,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
   f16x8 q[8];
   bf16x8 qext;
   Soft st;
-  load_query<TAYLOR>(p.q + qrow * D, h, group_shift, p.tau, ek, q, qext, st.alpha);
+  load_query<TAYLOR>(p.q + qrow * D, h, group_shift, p.tau, 0, q, qext, st.alpha);
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) st.o[db] = f32x16{};
   st.m = -INFINITY;
@@ -329,7 +359,6 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
   c.group_shift = group_shift;
   c.nc = static_cast<int>(p.Nc);
   c.ncur = static_cast<int>(p.Ncur);
-  c.kscale = ldexpf(1.0f, -ek);
   c.kmask = opaque_u32(kCodeMask<KBITS>);
   if (p.Nc > 0) {
     const int64_t hrow = bkv * p.cap;
@@ -362,16 +391,16 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
     if (blk < nbc) {
       const int k0 = blk * BK;
       count = c.nc - k0 < BK ? c.nc - k0 : BK;
-      unpack_k_cached<TAYLOR, KBITS>(c, lane, f, Kt);
+      const int ek = unpack_k_cached<TAYLOR, KBITS>(c, lane, f, Kt);
       unpack_v_cached<VBITS>(lane, f, Vt);
       const int nb = blk + WAVES;
       if (nb < bend && nb < nbc) fetch_cached<KBITS, VBITS>(c, nb * BK, lane, f);
-      block_compute<TAYLOR>(Kt, Vt, q, qext, count, lane, st);
+      block_compute<TAYLOR>(Kt, Vt, q, qext, count, ek, lane, st);
     } else {
       const int k0 = (blk - nbc) * BK;
       count = c.ncur - k0 < BK ? c.ncur - k0 : BK;
-      unpack_current(c, k0, lane, Kt, Vt);
-      block_compute<false>(Kt, Vt, q, qext, count, lane, st);
+      const int ek = unpack_current(c, k0, lane, Kt, Vt);
+      block_compute<false>(Kt, Vt, q, qext, count, ek, lane, st);
     }
   }
 
@@ -441,16 +470,12 @@ hipError_t launch_bits(const AttnLaunch &p, hipStream_t stream) {
   const int32_t gshift = __builtin_ctz(static_cast<unsigned>(p.group));
   const int64_t nrows = p.B * p.Hq * p.Nq;
   float *partials = static_cast<float *>(p.workspace);
-  int32_t *kexp = reinterpret_cast<int32_t *>(static_cast<char *>(p.workspace) +
-                                              short_path_workspace_bytes(p.B, p.Hq, p.Nq, p.d, p.splits));
-  launch_key_scale(p, stream, kexp);
   const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(p.splits) * row_groups * p.B * p.Hkv));
   if (p.corr == KV_CORR_TAYLOR)
-    attn_short_kernel<KB, VB, true><<<grid, dim3(THREADS), 0, stream>>>(p, gshift, rows, row_groups, p.splits, kexp,
-                                                                        partials);
+    attn_short_kernel<KB, VB, true><<<grid, dim3(THREADS), 0, stream>>>(p, gshift, rows, row_groups, p.splits, partials);
   else
     attn_short_kernel<KB, VB, false><<<grid, dim3(THREADS), 0, stream>>>(p, gshift, rows, row_groups, p.splits,
-                                                                         kexp, partials);
+                                                                         partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   return launch_combine(partials, p.out, nrows, p.splits, p.d, stream);

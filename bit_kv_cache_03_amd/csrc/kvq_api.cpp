@@ -134,8 +134,7 @@ Plan plan_attention(const kv_attn_args *a, bool query_device) {
     const int cus = query_device ? device_cu_count() : 256;
     if (kvq::short_fast_supported(a->d, a->corr)) {
       pl.splits = a->splits > 0 ? a->splits : kvq::short_fast_splits(a->B, a->Hkv, rows, a->Nc, a->Ncur, cus);
-      pl.workspace = kvq::short_path_workspace_bytes(a->B, a->Hq, a->Nq, a->d, pl.splits) +
-                     kvq::fast_path_workspace_bytes(a->B, a->Hkv);
+      pl.workspace = kvq::short_path_workspace_bytes(a->B, a->Hq, a->Nq, a->d, pl.splits);
     } else {
       pl.splits = a->splits > 0 ? a->splits : kvq::short_path_splits(a->B, a->Hkv, rows, a->Nc, cus);
       pl.workspace = kvq::short_path_workspace_bytes(a->B, a->Hq, a->Nq, a->d, pl.splits);

@@ -62,8 +62,7 @@ size_t short_path_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int32_t d, 
 // Log-sum-exp merge of split partials into the bf16 output.
 hipError_t launch_combine(const float *ws, uint16_t *out, int64_t nrows, int splits, int32_t d, hipStream_t stream);
 // Short-query kernel (attention_short.hip): head dim 128, correction off or
-// Taylor; workspace = the split partials, then one int32 key-scale exponent
-// per (b, KV head) (fast_path_workspace_bytes).
+// Taylor; workspace = the split partials.
 bool short_fast_supported(int32_t d, int corr);
 int short_fast_splits(int64_t B, int64_t Hkv, int64_t rows_per_kvhead, int64_t Nc, int64_t Ncur, int cu_count);
 hipError_t launch_attention_short_fast(const AttnLaunch &p, hipStream_t stream);

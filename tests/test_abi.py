@@ -174,12 +174,12 @@ def test_long_path_workspace(kvq):
 
 
 def test_short_path_workspace_grows_with_splits(kvq):
-    """Split partials (splits x B*Hq*Nq rows of d+4 floats); the head-dim-128
-    short kernel (correction off or Taylor) adds its 256-byte key-scale
-    block, the general kernel (head dim 64 or the exact correction) none."""
+    """Split partials: splits x B*Hq*Nq rows of d+4 floats, for both short
+    kernels (head dim 128 with correction off or Taylor, and the general
+    one)."""
     part = 1 * 4 * 8 * (128 + 4) * 4
     size = lambda **kw: kvq.lib.kv_attention_workspace_size(C.byref(_args(kvq, path=2, **kw)))
-    assert [size(splits=s) for s in (1, 2, 4, 8)] == [s * part + 256 for s in (1, 2, 4, 8)]
+    assert [size(splits=s) for s in (1, 2, 4, 8)] == [s * part for s in (1, 2, 4, 8)]
     assert [size(splits=s, corr=2) for s in (1, 2, 4, 8)] == [s * part for s in (1, 2, 4, 8)]
     assert size(splits=3, d=64) == 3 * 1 * 4 * 8 * (64 + 4) * 4
 
