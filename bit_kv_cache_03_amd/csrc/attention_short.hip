@@ -8,18 +8,26 @@
 // key range and keeps its own running max, sum and output for all 32 rows
 // of the row group, with private LDS tiles (no barrier inside the loop).
 // The waves merge at the end (log-sum-exp), and the splits are merged by
-// attn_combine_kernel.  Numerics match the throughput kernel: keys in fp16
-// (magic-code dequantisation), per-row query scale, probabilities and values
-// in bf16, the Taylor correction of the cached scores as one extra bf16
-// MFMA step ("量化鍵值偷走注意力…" (agents-report.net), §方法 and §為何校正有效).
-// The keys' power-of-two fp16 scale is chosen per 32-key block from that
-// block's own steps and zero points (or values), and folded into the
-// softmax scale of the block, so no pass over the whole cache is needed.
+// attn_combine_kernel.  Keys are fp16 (magic-code dequantisation) with a
+// per-row query scale as in the throughput kernel, and the Taylor correction
+// of the cached scores is one extra bf16 MFMA step ("量化鍵值偷走注意力…"
+// (agents-report.net), §方法 and §為何校正有效).  Values and probabilities
+// are fp16 here (values rounded once from an fp32 fma, as the keys): the
+// value dequantisation is the largest share of the work per key, and the
+// fp16 form needs no conversion after it.
+//
+// Power-of-two scales, chosen per 32-key block from that block's own steps
+// and zero points (or values), keep the fp16 operands in range; no pass over
+// the whole cache is needed.  Keys are stored as k 2^-ek, folded into the
+// softmax scale of the block.  Values are stored as v 2^-ev and their
+// probabilities as p 2^ev: the running max follows s alpha + ev, so every
+// probability stays at most 2^8 (the lazy threshold) and O = sum p v is
+// unchanged; l accumulates p 2^ev 2^-ev.
 //
 // Per block (per wave): dequantise K (rows = keys) and V^T (rows = head
 // dimension, keys in the permuted order of the P operand) into LDS, fetch
 // the next block, S^T = K Q^T (8 fp16 MFMA + 1 correction step), mask the
-// ragged block, lazy max, exponentials, O^T += V^T P^T (8 bf16 MFMA).
+// ragged block, lazy max, exponentials, O^T += V^T P^T (8 fp16 MFMA).
 #include <math.h>
 
 #include "kvq_device.h"
@@ -61,66 +69,136 @@ struct Fetch {
 };
 
 struct Ctx {
-  const uint8_t *kc_codes, *vc_codes;
+  const uint8_t *kc_codes, *vc_codes;  // the (b, KV head)'s cache rows
   const float *kc_scale, *kc_zero, *vc_scale, *vc_zero;
   const uint16_t *k_cur, *v_cur;
-  int ng, group_shift;
   int nc, ncur;     // segment lengths
   uint32_t kmask;   // code mask of magic8 (vector register)
+  uint32_t vmask0, vmask1;  // value code fields of unpack_v_cached (vector registers)
 };
 
-// Largest of x over the wave.
-__device__ inline float wave_max(float x) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return x;
+// Largest x over the wave, returned uniform: DPP steps (within quads,
+// half rows, rows, then across rows) leave the maximum in lane 63.
+template <int CTRL, int ROWS>
+__device__ inline float dpp_max(float x) {
+  const int v = __float_as_int(x);
+  return fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(v, v, CTRL, ROWS, 0xf, false)));
 }
+__device__ inline float wave_max(float x) {
+  x = dpp_max<0xb1, 0xf>(x);   // quad_perm [1,0,3,2]
+  x = dpp_max<0x4e, 0xf>(x);   // quad_perm [2,3,0,1]
+  x = dpp_max<0x141, 0xf>(x);  // row_half_mirror
+  x = dpp_max<0x140, 0xf>(x);  // row_mirror
+  x = dpp_max<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+  x = dpp_max<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
+// Raw buffer descriptor over `bytes` bytes at p (stride 0): loads at byte
+// offsets past `bytes` return zero instead of touching memory.
+typedef __amdgpu_buffer_rsrc_t Buf;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ inline Buf buffer_at(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, static_cast<int>(bytes), 0x00020000);
+}
+__device__ inline uint32_t ld32(Buf b, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b32(b, off, 0, 0); }
+__device__ inline u32x2 ld64(Buf b, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b64(b, off, 0, 0); }
+__device__ inline u32x4 ld128(Buf b, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b128(b, off, 0, 0); }
+
+// floor(log2 x) for x > 0 (one v_frexp_exp_i32_f32).
+__device__ inline int ilog2_pos(float x) { return __builtin_amdgcn_frexp_expf(x) - 1; }
+
+// Sum of the 8 fp16 values of v, added to acc.
+__device__ inline float sum8h(f16x8 v, float acc) {
+  const uint4 w = __builtin_bit_cast(uint4, v);
+  const f16x2 one = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w.x), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w.y), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w.z), one, acc, false);
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w.w), one, acc, false);
+}
+
+// Exponent ev of a block's values: |v| 2^-ev in [2^13, 2^14) for the largest
+// |v| of the block (0 for an all-zero block), the fp16 range with the most
+// precision.  Every block, cached or current, uses this rule, so the factor
+// 2^(ev - running max) that a probability carries only reflects real
+// differences of magnitude between blocks.
+__device__ inline int value_exponent(float vmax) { return vmax > 0.f ? ilog2_pos(vmax) - 13 : 0; }
 
 // Lane roles (per wave):
 //  K: key kr = lane % 32 of the block, head-dim half h = lane / 32
 //     (d in [64h, 64h+64), i.e. whole groups for group >= 64)
 //  V: keys 4kq..4kq+3 with kq = lane % 8, d in [16dq, 16dq+16), dq = lane / 8
-// Cached rows past the segment end clamp to its last row (in bounds; the
-// scores of those keys are masked).
-template <int KBITS, int VBITS>
-__device__ inline void fetch_cached(const Ctx &c, int k0, int lane, Fetch &f) {
-  const int last = c.nc - 1;
+// Byte offsets of the lane's data from the block's first cache row; NG is
+// the number of quantisation groups per row (128 / group).
+struct Lanes {
+  uint32_t kc, km, vc, vm;
+};
+template <int KBITS, int VBITS, int NG>
+__device__ inline Lanes lane_offsets(int lane) {
+  constexpr uint32_t KROW = D * KBITS / 8, VROW = D * VBITS / 8;
+  const uint32_t kr = lane & 31, h = lane >> 5, kq = lane & 7, dq = lane >> 3;
+  Lanes o;
+  o.kc = kr * KROW + h * (KROW / 2);
+  o.km = kr * NG * 4;
+  o.vc = 4 * kq * VROW + 16 * dq * VBITS / 8;
+  o.vm = (4 * kq * NG + (16 * dq * NG) / D) * 4;  // the group of d = 16dq
+  return o;
+}
+
+// Loads one cached block (rows [k0, k0 + 32)); rows at or past the segment
+// end read as zero (their scores are masked).
+template <int KBITS, int VBITS, int NG>
+__device__ inline void fetch_cached(const Ctx &c, int k0, const Lanes &o, int h, Fetch &f) {
+  constexpr uint32_t KROW = D * KBITS / 8, VROW = D * VBITS / 8;
+  const uint32_t rows = static_cast<uint32_t>(c.nc - k0);
   {
-    const int kr = lane & 31, h = lane >> 5;
-    const uint32_t row = static_cast<uint32_t>(k0 + kr <= last ? k0 + kr : last);
-    const uint4 *ks = reinterpret_cast<const uint4 *>(c.kc_codes + (row * (D * KBITS / 8) + 32u * KBITS / 4 * h));
-    const uint4 a = ks[0];
+    const Buf kc = buffer_at(c.kc_codes + static_cast<size_t>(k0) * KROW, rows * KROW);
+    const u32x4 a = ld128(kc, o.kc);
     f.kw[0] = a.x; f.kw[1] = a.y; f.kw[2] = a.z; f.kw[3] = a.w;
     if (KBITS == 4) {
-      const uint4 b = ks[1];
+      const u32x4 b = ld128(kc, o.kc + 16);
       f.kw[4] = b.x; f.kw[5] = b.y; f.kw[6] = b.z; f.kw[7] = b.w;
     }
-    const uint32_t km = row * static_cast<uint32_t>(c.ng);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t g = static_cast<uint32_t>((64 * h + 32 * j) >> c.group_shift);
-      f.kstep[j] = c.kc_scale[km + g];
-      f.kzero[j] = c.kc_zero[km + g];
-      const int gg = 2 * h + j < c.ng ? 2 * h + j : c.ng - 1;
-      f.gstep[j] = c.kc_scale[km + static_cast<uint32_t>(gg)];
+    const Buf ks = buffer_at(c.kc_scale + static_cast<size_t>(k0) * NG, rows * NG * 4);
+    const Buf kz = buffer_at(c.kc_zero + static_cast<size_t>(k0) * NG, rows * NG * 4);
+    // groups of d = 64h + 32j (kstep, kzero) and groups 2h + j (gstep; only
+    // those below NG are used)
+    if (NG == 1) {
+      const float st = __uint_as_float(ld32(ks, o.km)), z = __uint_as_float(ld32(kz, o.km));
+      f.kstep[0] = f.kstep[1] = f.gstep[0] = f.gstep[1] = st;
+      f.kzero[0] = f.kzero[1] = z;
+    } else if (NG == 2) {
+      const u32x2 st = ld64(ks, o.km);
+      const float z = __uint_as_float(ld32(kz, o.km + 4 * h));
+      f.kstep[0] = f.kstep[1] = __uint_as_float(h ? st.y : st.x);
+      f.kzero[0] = f.kzero[1] = z;
+      f.gstep[0] = __uint_as_float(st.x);
+      f.gstep[1] = __uint_as_float(st.y);
+    } else {
+      const u32x2 st = ld64(ks, o.km + 8 * h), z = ld64(kz, o.km + 8 * h);
+      f.kstep[0] = f.gstep[0] = __uint_as_float(st.x);
+      f.kstep[1] = f.gstep[1] = __uint_as_float(st.y);
+      f.kzero[0] = __uint_as_float(z.x);
+      f.kzero[1] = __uint_as_float(z.y);
     }
   }
   {
-    const int kq = lane & 7, dq = lane >> 3;
+    const Buf vc = buffer_at(c.vc_codes + static_cast<size_t>(k0) * VROW, rows * VROW);
+    const Buf vs = buffer_at(c.vc_scale + static_cast<size_t>(k0) * NG, rows * NG * 4);
+    const Buf vz = buffer_at(c.vc_zero + static_cast<size_t>(k0) * NG, rows * NG * 4);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t row = static_cast<uint32_t>(k0 + 4 * kq + j <= last ? k0 + 4 * kq + j : last);
-      const uint8_t *vs = c.vc_codes + (row * (D * VBITS / 8) + static_cast<uint32_t>(16 * dq * VBITS / 8));
       if (VBITS == 4) {
-        const uint2 w = *reinterpret_cast<const uint2 *>(vs);
+        const u32x2 w = ld64(vc, o.vc + j * VROW);
         f.vw[j] = w.x;
         f.vw2[j] = w.y;
       } else {
-        f.vw[j] = *reinterpret_cast<const uint32_t *>(vs);
+        f.vw[j] = ld32(vc, o.vc + j * VROW);
       }
-      const uint32_t vm = row * static_cast<uint32_t>(c.ng) + static_cast<uint32_t>((16 * dq) >> c.group_shift);
-      f.vstep[j] = c.vc_scale[vm];
-      f.vzero[j] = c.vc_zero[vm];
+      f.vstep[j] = __uint_as_float(ld32(vs, o.vm + j * NG * 4));
+      f.vzero[j] = __uint_as_float(ld32(vz, o.vm + j * NG * 4));
     }
   }
 }
@@ -131,7 +209,7 @@ __device__ inline void fetch_cached(const Ctx &c, int k0, int lane, Fetch &f) {
 // 8h .. 8h+7 (groups 2h, 2h+1).
 // Returns the block's key exponent e (keys stored as k * 2^-e): the
 // dequantised values lie between z and z + (2^bits - 1) D of their group.
-template <bool TAYLOR, int KBITS>
+template <bool TAYLOR, int KBITS, int NG>
 __device__ inline int unpack_k_cached(const Ctx &c, int lane, const Fetch &f, uint16_t *Kt) {
   const int kr = lane & 31, h = lane >> 5;
   uint16_t *row = Kt + kr * KS;
@@ -139,7 +217,8 @@ __device__ inline int unpack_k_cached(const Ctx &c, int lane, const Fetch &f, ui
 #pragma unroll
   for (int j = 0; j < 2; ++j)
     bound = fmaxf(bound, fmaxf(fabsf(f.kzero[j]), fabsf(fmaf(f.kstep[j], static_cast<float>((1 << KBITS) - 1), f.kzero[j]))));
-  const int e = scale_exponent(wave_max(bound));
+  const float kb = wave_max(bound);
+  const int e = kb > 0.f ? ilog2_pos(kb) - kFp16Exp : 0;
   const float kscale = ldexpf(1.0f, -e);
   float sj[2], zj[2];
 #pragma unroll
@@ -163,7 +242,7 @@ __device__ inline int unpack_k_cached(const Ctx &c, int lane, const Fetch &f, ui
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int g = 2 * h + j;
-      const float sq = g < c.ng ? f.gstep[j] * f.gstep[j] * kscale : 0.f;
+      const float sq = g < NG ? f.gstep[j] * f.gstep[j] * kscale : 0.f;
       const float hsq = lo_f(pack2(sq, 0.f));
       x[2 * j] = pack2(-hsq, -(sq - hsq));
       x[2 * j + 1] = pack2(-hsq, 0.f);
@@ -173,34 +252,76 @@ __device__ inline int unpack_k_cached(const Ctx &c, int lane, const Fetch &f, ui
   return e;
 }
 
-// V^T tile of a cached block: bf16 values of keys 4kq..4kq+3 (adjacent
-// permuted slots: key r of a 16-key step sits at slot (r&3) + 4*(r>>3) +
-// 8*((r>>2)&1)) at head-dim rows 16dq .. 16dq+15, one 8-byte store per row.
+// V^T tile of a cached block: fp16 values v 2^-ev of keys 4kq..4kq+3
+// (adjacent permuted slots: key r of a 16-key step sits at slot (r&3) +
+// 4*(r>>3) + 8*((r>>2)&1)) at head-dim rows 16dq .. 16dq+15, one 8-byte store
+// per row; returns ev.  One v_perm gathers the same code byte of two keys
+// (bits 0..7 and 16..23); one v_and_or turns a code field at bit p of both
+// into the fp16 magic numbers 1024 + c 2^p (exact: the fp16 spacing at 1024
+// is 1); then v 2^-ev = fma(1024 + c 2^p, D 2^-(p+ev), (z - 1024 D 2^-p) 2^-ev)
+// with fp32 operands, one v_fma_mix per value rounded once to fp16.
+// INT4 fields sit at p = 0 and 4; INT2 fields at p = 0 and 2 of the byte
+// and of the byte shifted right by 4.
 template <int VBITS>
-__device__ inline void unpack_v_cached(int lane, const Fetch &f, uint16_t *Vt) {
+__device__ inline int unpack_v_cached(const Ctx &c, int lane, const Fetch &f, uint16_t *Vt) {
+  constexpr int P1 = VBITS == 4 ? 4 : 2;
   const int kq = lane & 7, dq = lane >> 3;
   const int a = kq & 3;
   const int slot = 16 * (kq >> 2) + 4 * (a >> 1) + 8 * (a & 1);
+  float vmax = 0.f;
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {  // d = 16dq + 8half .. +7
-    float v[4][8];
+  for (int j = 0; j < 4; ++j)
+    vmax = fmaxf(vmax, fmaxf(fabsf(f.vzero[j]), fabsf(fmaf(f.vstep[j], static_cast<float>((1 << VBITS) - 1), f.vzero[j]))));
+  const int ev = value_exponent(wave_max(vmax));
+  const float vsc = ldexpf(1.0f, -ev);
+  float dd[4][2], zz[4][2];  // per key: operands of the fields at p = 0 and p = P1
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float cv[8];
-      codes8<VBITS>(VBITS == 4 ? (half ? f.vw2[j] : f.vw[j]) : (f.vw[j] >> (16 * half)), cv);
+  for (int j = 0; j < 4; ++j) {
+    const float d0 = f.vstep[j] * vsc, z0 = f.vzero[j] * vsc;
+    dd[j][0] = d0;
+    dd[j][1] = d0 * (1.0f / (1 << P1));
+    zz[j][0] = fmaf(-1024.0f, dd[j][0], z0);
+    zz[j][1] = fmaf(-1024.0f, dd[j][1], z0);
+  }
+  auto field = [&](uint32_t r, int k, uint32_t (&x)[2], int jp) {  // k: 0 (p = 0) or 1 (p = P1)
+    const uint32_t m = (r & (k ? c.vmask1 : c.vmask0)) | 0x64006400u;
+    const f16x2 h = __builtin_bit_cast(f16x2, m);
+    x[jp] = pair_h(dequant_h(static_cast<float>(h.x), dd[2 * jp][k], zz[2 * jp][k]),
+                   dequant_h(static_cast<float>(h.y), dd[2 * jp + 1][k], zz[2 * jp + 1][k]));
+  };
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[j][e] = fmaf(f.vstep[j], cv[e], f.vzero[j]);
+  for (int byte = 0; byte < (VBITS == 4 ? 8 : 4); ++byte) {
+    // INT4: d = 16dq + 2byte + {0, 1} (bytes 4.. from vw2); INT2: d = 16dq + 4byte + {0, 1, 2, 3}
+    const int bw = byte & 3;
+    const uint32_t sel = static_cast<uint32_t>(bw) | 0x0c00u | (static_cast<uint32_t>(4 + bw) << 16) | 0x0c000000u;
+    uint32_t r[2];
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) {
+      const uint32_t w0 = byte >= 4 ? f.vw2[2 * jp] : f.vw[2 * jp];
+      const uint32_t w1 = byte >= 4 ? f.vw2[2 * jp + 1] : f.vw[2 * jp + 1];
+      r[jp] = __builtin_amdgcn_perm(w1, w0, sel);
+    }
+    constexpr int NF = 8 / VBITS;
+    uint32_t x[NF][2];
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) {
+      field(r[jp], 0, x[0], jp);
+      field(r[jp], 1, x[1], jp);
+      if (VBITS == 2) {
+        field(r[jp] >> 4, 0, x[NF - 2], jp);
+        field(r[jp] >> 4, 1, x[NF - 1], jp);
+      }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      *reinterpret_cast<uint2 *>(Vt + vts(16 * dq + 8 * half + e, slot)) =
-          make_uint2(pack2(v[0][e], v[1][e]), pack2(v[2][e], v[3][e]));
+    for (int fl = 0; fl < NF; ++fl)
+      *reinterpret_cast<uint2 *>(Vt + vts(16 * dq + NF * byte + fl, slot)) = make_uint2(x[fl][0], x[fl][1]);
   }
+  return ev;
 }
 
-// Current-chunk block (bf16 keys and values, loaded and written directly);
-// returns the block's key exponent like unpack_k_cached.
-__device__ inline int unpack_current(const Ctx &c, int k0, int lane, uint16_t *Kt, uint16_t *Vt) {
+// Current-chunk block (bf16 keys and values, rescaled to fp16 like the
+// cached ones); returns the key exponent, ev the value exponent.
+__device__ inline int unpack_current(const Ctx &c, int k0, int lane, uint16_t *Kt, uint16_t *Vt, int &ev) {
   const int last = c.ncur - 1;
   int ek;
   {
@@ -216,7 +337,8 @@ __device__ inline int unpack_current(const Ctx &c, int k0, int lane, uint16_t *K
 #pragma unroll
       for (int e = 0; e < 4; ++e) bound = fmaxf(bound, fmaxf(fabsf(lo_f(u[e])), fabsf(hi_f(u[e]))));
     }
-    ek = scale_exponent(wave_max(bound));
+    const float kb = wave_max(bound);
+    ek = kb > 0.f ? ilog2_pos(kb) - kFp16Exp : 0;
     const float kscale = ldexpf(1.0f, -ek);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -231,30 +353,27 @@ __device__ inline int unpack_current(const Ctx &c, int k0, int lane, uint16_t *K
     const int kq = lane & 7, dq = lane >> 3;
     const int a = kq & 3;
     const int slot = 16 * (kq >> 2) + 4 * (a >> 1) + 8 * (a & 1);
-    uint4 x[4][2];
+    uint32_t x[4][8];  // key j, bf16 pairs of d = 16dq + 2i, +1
+    float bound = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t row = static_cast<uint32_t>(k0 + 4 * kq + j <= last ? k0 + 4 * kq + j : last);
       const uint4 *vs = reinterpret_cast<const uint4 *>(c.v_cur + (row * D + 16u * dq));
-      x[j][0] = vs[0];
-      x[j][1] = vs[1];
+      const uint4 y0 = vs[0], y1 = vs[1];
+      x[j][0] = y0.x; x[j][1] = y0.y; x[j][2] = y0.z; x[j][3] = y0.w;
+      x[j][4] = y1.x; x[j][5] = y1.y; x[j][6] = y1.z; x[j][7] = y1.w;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bound = fmaxf(bound, fmaxf(fabsf(lo_f(x[j][i])), fabsf(hi_f(x[j][i]))));
     }
+    ev = value_exponent(wave_max(bound));
+    const float vsc = ldexpf(1.0f, -ev);
 #pragma unroll
-    for (int half = 0; half < 2; ++half)
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {  // bf16 pair (8half + 2e2, +1) of each key
-        uint32_t u[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint4 y = x[j][half];
-          u[j] = e2 == 0 ? y.x : e2 == 1 ? y.y : e2 == 2 ? y.z : y.w;
-        }
-        // row d = 16dq + 8half + 2e2 (low halves) and +1 (high halves)
-        *reinterpret_cast<uint2 *>(Vt + vts(16 * dq + 8 * half + 2 * e2, slot)) =
-            make_uint2(__builtin_amdgcn_perm(u[1], u[0], 0x05040100u), __builtin_amdgcn_perm(u[3], u[2], 0x05040100u));
-        *reinterpret_cast<uint2 *>(Vt + vts(16 * dq + 8 * half + 2 * e2 + 1, slot)) =
-            make_uint2(__builtin_amdgcn_perm(u[1], u[0], 0x07060302u), __builtin_amdgcn_perm(u[3], u[2], 0x07060302u));
-      }
+    for (int i = 0; i < 8; ++i) {
+      *reinterpret_cast<uint2 *>(Vt + vts(16 * dq + 2 * i, slot)) =
+          make_uint2(pack2h(lo_f(x[0][i]) * vsc, lo_f(x[1][i]) * vsc), pack2h(lo_f(x[2][i]) * vsc, lo_f(x[3][i]) * vsc));
+      *reinterpret_cast<uint2 *>(Vt + vts(16 * dq + 2 * i + 1, slot)) =
+          make_uint2(pack2h(hi_f(x[0][i]) * vsc, hi_f(x[1][i]) * vsc), pack2h(hi_f(x[2][i]) * vsc, hi_f(x[3][i]) * vsc));
+    }
   }
   return ek;
 }
@@ -268,8 +387,9 @@ struct Soft {
 // count < BK marks a ragged block; CORR adds the correction step.
 template <bool CORR>
 __device__ inline void block_compute(const uint16_t *Kt, const uint16_t *Vt, const f16x8 (&q)[8], bf16x8 qext,
-                                     int count, int ek, int lane, Soft &st) {
+                                     int count, int ek, int ev, int lane, Soft &st) {
   const float alpha = ldexpf(st.alpha, ek);  // scores of this block are q.k * 2^-(eq+ek)
+  const float fev = static_cast<float>(ev);
   const int qc = lane & 31, h = lane >> 5;
   f32x16 s = f32x16{};
   const uint16_t *kb = Kt + qc * KS + 8 * h;
@@ -286,7 +406,7 @@ __device__ inline void block_compute(const uint16_t *Kt, const uint16_t *Vt, con
   float mt = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[i]);
-  mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * alpha;
+  mt = fmaf(fmaxf(mt, __shfl_xor(mt, 32, 64)), alpha, fev);
   const bool grow = mt > st.m + kLazy;
   if (__any(grow)) {
     const float m_new = grow ? mt : st.m;
@@ -296,37 +416,41 @@ __device__ inline void block_compute(const uint16_t *Kt, const uint16_t *Vt, con
     for (int db = 0; db < D / 32; ++db) st.o[db] *= sc;
     st.m = m_new;
   }
-  bf16x8 pk[2];
+  f16x8 pk[2];
+  const float shift = fev - st.m;
+  float lb = 0.f;
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
     float e[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) e[i] = __builtin_amdgcn_exp2f(fmaf(s[8 * hf + i], alpha, -st.m));
-    pk[hf] = __builtin_bit_cast(bf16x8, make_uint4(pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]),
-                                                   pack2(e[6], e[7])));
-    st.l = sum8(pk[hf], st.l);
+    for (int i = 0; i < 8; ++i) e[i] = __builtin_amdgcn_exp2f(fmaf(s[8 * hf + i], alpha, shift));
+    pk[hf] = __builtin_bit_cast(f16x8, make_uint4(pack2h(e[0], e[1]), pack2h(e[2], e[3]), pack2h(e[4], e[5]),
+                                                  pack2h(e[6], e[7])));
+    lb = sum8h(pk[hf], lb);
   }
+  st.l = fmaf(lb, ldexpf(1.0f, -ev), st.l);
   // O^T += V^T P^T: k-step ks (keys 16ks..16ks+15), head-dim block db
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       const int row = 32 * db + qc;
-      st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          *reinterpret_cast<const bf16x8 *>(Vt + vts(row, 16 * ks + 8 * h)), pk[ks], st.o[db], 0, 0, 0);
+      st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+          *reinterpret_cast<const f16x8 *>(Vt + vts(row, 16 * ks + 8 * h)), pk[ks], st.o[db], 0, 0, 0);
     }
 }
 
-template <int KBITS, int VBITS, bool TAYLOR>
-__global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, int32_t group_shift,
-                                                                int64_t rows_per_kvhead, int32_t row_groups,
-                                                                int32_t nsplit, float *ws) {
+template <int KBITS, int VBITS, bool TAYLOR, int NG>
+__global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, int64_t rows_per_kvhead,
+                                                                int32_t row_groups, int32_t nsplit, float *ws) {
   __shared__ __attribute__((aligned(16))) uint16_t L[WAVES * WLDS];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: block loop control stays scalar
   const int qc = lane & 31, h = lane >> 5;
-  const int ng = D >> group_shift;
+  constexpr int ng = NG;
+  constexpr int group_shift = NG == 1 ? 7 : NG == 2 ? 6 : 5;
 
   // Workgroups are dealt to the 8 XCDs round-robin by id; renumber so that
   // consecutive ids (the splits and row groups of one KV head) share an XCD.
@@ -355,11 +479,11 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
   st.l = 0.f;
 
   Ctx c{};
-  c.ng = ng;
-  c.group_shift = group_shift;
   c.nc = static_cast<int>(p.Nc);
   c.ncur = static_cast<int>(p.Ncur);
   c.kmask = opaque_u32(kCodeMask<KBITS>);
+  c.vmask0 = opaque_u32(VBITS == 4 ? 0x000f000fu : 0x00030003u);
+  c.vmask1 = opaque_u32(VBITS == 4 ? 0x00f000f0u : 0x000c000cu);
   if (p.Nc > 0) {
     const int64_t hrow = bkv * p.cap;
     c.kc_codes = p.kc_codes + hrow * (D * KBITS / 8);
@@ -384,24 +508,24 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
   uint16_t *Vt = Kt + KT;
 
   int blk = bbeg + wave;
+  const int cend = bend < nbc ? bend : nbc;
+  const Lanes lo = lane_offsets<KBITS, VBITS, NG>(lane);
   Fetch f;
-  if (blk < bend && blk < nbc) fetch_cached<KBITS, VBITS>(c, blk * BK, lane, f);
+  if (blk < cend) fetch_cached<KBITS, VBITS, NG>(c, blk * BK, lo, h, f);
+  for (; blk < cend; blk += WAVES) {
+    const int k0 = blk * BK;
+    const int count = c.nc - k0 < BK ? c.nc - k0 : BK;
+    const int ek = unpack_k_cached<TAYLOR, KBITS, NG>(c, lane, f, Kt);
+    const int ev = unpack_v_cached<VBITS>(c, lane, f, Vt);
+    if (blk + WAVES < cend) fetch_cached<KBITS, VBITS, NG>(c, (blk + WAVES) * BK, lo, h, f);
+    block_compute<TAYLOR>(Kt, Vt, q, qext, count, ek, ev, lane, st);
+  }
   for (; blk < bend; blk += WAVES) {
-    int count;
-    if (blk < nbc) {
-      const int k0 = blk * BK;
-      count = c.nc - k0 < BK ? c.nc - k0 : BK;
-      const int ek = unpack_k_cached<TAYLOR, KBITS>(c, lane, f, Kt);
-      unpack_v_cached<VBITS>(lane, f, Vt);
-      const int nb = blk + WAVES;
-      if (nb < bend && nb < nbc) fetch_cached<KBITS, VBITS>(c, nb * BK, lane, f);
-      block_compute<TAYLOR>(Kt, Vt, q, qext, count, ek, lane, st);
-    } else {
-      const int k0 = (blk - nbc) * BK;
-      count = c.ncur - k0 < BK ? c.ncur - k0 : BK;
-      const int ek = unpack_current(c, k0, lane, Kt, Vt);
-      block_compute<false>(Kt, Vt, q, qext, count, ek, lane, st);
-    }
+    const int k0 = (blk - nbc) * BK;
+    const int count = c.ncur - k0 < BK ? c.ncur - k0 : BK;
+    int ev;
+    const int ek = unpack_current(c, k0, lane, Kt, Vt, ev);
+    block_compute<false>(Kt, Vt, q, qext, count, ek, ev, lane, st);
   }
 
   // ---- merge the 4 waves (log-sum-exp), then the split partial or output ----
@@ -463,19 +587,28 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
   }
 }
 
+template <int KB, int VB, int NG>
+void launch_kernel(const AttnLaunch &p, hipStream_t stream, dim3 grid, int64_t rows, int32_t row_groups,
+                   float *partials) {
+  if (p.corr == KV_CORR_TAYLOR)
+    attn_short_kernel<KB, VB, true, NG><<<grid, dim3(THREADS), 0, stream>>>(p, rows, row_groups, p.splits, partials);
+  else
+    attn_short_kernel<KB, VB, false, NG><<<grid, dim3(THREADS), 0, stream>>>(p, rows, row_groups, p.splits, partials);
+}
+
 template <int KB, int VB>
 hipError_t launch_bits(const AttnLaunch &p, hipStream_t stream) {
   const int64_t rows = p.Nq * (p.Hq / p.Hkv);
   const int32_t row_groups = static_cast<int32_t>((rows + 31) / 32);
-  const int32_t gshift = __builtin_ctz(static_cast<unsigned>(p.group));
   const int64_t nrows = p.B * p.Hq * p.Nq;
   float *partials = static_cast<float *>(p.workspace);
   const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(p.splits) * row_groups * p.B * p.Hkv));
-  if (p.corr == KV_CORR_TAYLOR)
-    attn_short_kernel<KB, VB, true><<<grid, dim3(THREADS), 0, stream>>>(p, gshift, rows, row_groups, p.splits, partials);
+  if (p.group == 128)
+    launch_kernel<KB, VB, 1>(p, stream, grid, rows, row_groups, partials);
+  else if (p.group == 64)
+    launch_kernel<KB, VB, 2>(p, stream, grid, rows, row_groups, partials);
   else
-    attn_short_kernel<KB, VB, false><<<grid, dim3(THREADS), 0, stream>>>(p, gshift, rows, row_groups, p.splits,
-                                                                         partials);
+    launch_kernel<KB, VB, 4>(p, stream, grid, rows, row_groups, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   return launch_combine(partials, p.out, nrows, p.splits, p.d, stream);
