@@ -42,13 +42,11 @@ constexpr int D = 128;
 constexpr int BK = 32;          // keys per block
 constexpr int WAVES = 4;
 constexpr int THREADS = 64 * WAVES;
-constexpr int KS = D + 16 + 8;  // K row in LDS: fp16 values[128], bf16 corr[16], pad[8]
-constexpr int KEXT = D;
-constexpr int VS = BK + 8;      // V^T row in LDS: bf16 keys[32], pad[8] (80 bytes)
-constexpr int KT = BK * KS;     // 16-bit elements of a wave's K tile
+constexpr int VS = BK + 8;      // V^T row in LDS: fp16 keys[32], pad[8] (80 bytes)
 constexpr int VT = D * VS;      // 16-bit elements of a wave's V^T tile
-constexpr int WLDS = KT + VT;
 constexpr int OS = D + 4;       // fp32 row of the merge buffer
+constexpr int MERGE = 32 * OS + 64;  // floats of a wave's merge buffer (O rows, then m and l)
+constexpr int LDS_BYTES = WAVES * VT * 2 > WAVES * MERGE * 4 ? WAVES * VT * 2 : WAVES * MERGE * 4;
 
 // V^T element (row = head-dim index, col = permuted key slot 0..31); the
 // 16-byte chunks of a row are XOR-swizzled by (row / 16) % 4 so that the
@@ -203,23 +201,36 @@ __device__ inline void fetch_cached(const Ctx &c, int k0, const Lanes &o, int h,
   }
 }
 
-// K tile of a cached block: fp16 values (magic codes, one v_fma_mix each)
-// and, for the Taylor correction, the slots 4g+{0,1,2,3} = (-D_g^2 split
-// hi, lo, hi; 0) in bf16 (zero for g >= d/group); lane h writes slots
-// 8h .. 8h+7 (groups 2h, 2h+1).
-// Returns the block's key exponent e (keys stored as k * 2^-e): the
-// dequantised values lie between z and z + (2^bits - 1) D of their group.
-template <bool TAYLOR, int KBITS, int NG>
-__device__ inline int unpack_k_cached(const Ctx &c, int lane, const Fetch &f, uint16_t *Kt) {
-  const int kr = lane & 31, h = lane >> 5;
-  uint16_t *row = Kt + kr * KS;
-  float bound = 0.f;
+// Largest |k| (|v|) a lane's share of a cached block can dequantise to:
+// the values of a group lie between z and z + (2^bits - 1) D.
+template <int KBITS>
+__device__ inline float k_bound(const Fetch &f) {
+  float b = 0.f;
 #pragma unroll
   for (int j = 0; j < 2; ++j)
-    bound = fmaxf(bound, fmaxf(fabsf(f.kzero[j]), fabsf(fmaf(f.kstep[j], static_cast<float>((1 << KBITS) - 1), f.kzero[j]))));
-  const float kb = wave_max(bound);
-  const int e = kb > 0.f ? ilog2_pos(kb) - kFp16Exp : 0;
-  const float kscale = ldexpf(1.0f, -e);
+    b = fmaxf(b, fmaxf(fabsf(f.kzero[j]), fabsf(fmaf(f.kstep[j], static_cast<float>((1 << KBITS) - 1), f.kzero[j]))));
+  return b;
+}
+template <int VBITS>
+__device__ inline float v_bound(const Fetch &f) {
+  float b = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    b = fmaxf(b, fmaxf(fabsf(f.vzero[j]), fabsf(fmaf(f.vstep[j], static_cast<float>((1 << VBITS) - 1), f.vzero[j]))));
+  return b;
+}
+
+// K operand of a cached block, straight into the MFMA A-operand registers
+// of S^T = K Q^T: the lane (key kr = lane % 32, half h = lane / 32) holds
+// its key's values d = 64h + 8s .. +7 in k[s] (k-step s, slots 8h .. 8h+7;
+// the query uses the same order), as fp16 k 2^-ek (magic codes, one v_fma_mix
+// each), and for the Taylor correction the slots 4g+{0,1,2,3} = (-D_g^2
+// split hi, lo, hi; 0) in bf16 for its groups g = 2h, 2h+1 (zero for
+// g >= d/group), scaled like the keys.
+template <bool TAYLOR, int KBITS, int NG>
+__device__ inline void unpack_k_cached(const Ctx &c, int lane, const Fetch &f, float kscale, f16x8 (&k)[8],
+                                       bf16x8 &kext) {
+  const int h = lane >> 5;
   float sj[2], zj[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -235,7 +246,7 @@ __device__ inline int unpack_k_cached(const Ctx &c, int lane, const Fetch &f, ui
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       w[e] = pair_h(dequant_h(magic_code(m, 2 * e), st, z), dequant_h(magic_code(m, 2 * e + 1), st, z));
-    *reinterpret_cast<uint4 *>(row + 64 * h + 8 * i) = make_uint4(w[0], w[1], w[2], w[3]);
+    k[i] = __builtin_bit_cast(f16x8, make_uint4(w[0], w[1], w[2], w[3]));
   }
   if (TAYLOR) {
     uint32_t x[4];
@@ -247,15 +258,14 @@ __device__ inline int unpack_k_cached(const Ctx &c, int lane, const Fetch &f, ui
       x[2 * j] = pack2(-hsq, -(sq - hsq));
       x[2 * j + 1] = pack2(-hsq, 0.f);
     }
-    *reinterpret_cast<uint4 *>(row + KEXT + 8 * h) = make_uint4(x[0], x[1], x[2], x[3]);
+    kext = __builtin_bit_cast(bf16x8, make_uint4(x[0], x[1], x[2], x[3]));
   }
-  return e;
 }
 
 // V^T tile of a cached block: fp16 values v 2^-ev of keys 4kq..4kq+3
 // (adjacent permuted slots: key r of a 16-key step sits at slot (r&3) +
 // 4*(r>>3) + 8*((r>>2)&1)) at head-dim rows 16dq .. 16dq+15, one 8-byte store
-// per row; returns ev.  One v_perm gathers the same code byte of two keys
+// per row.  One v_perm gathers the same code byte of two keys
 // (bits 0..7 and 16..23); one v_and_or turns a code field at bit p of both
 // into the fp16 magic numbers 1024 + c 2^p (exact: the fp16 spacing at 1024
 // is 1); then v 2^-ev = fma(1024 + c 2^p, D 2^-(p+ev), (z - 1024 D 2^-p) 2^-ev)
@@ -263,17 +273,11 @@ __device__ inline int unpack_k_cached(const Ctx &c, int lane, const Fetch &f, ui
 // INT4 fields sit at p = 0 and 4; INT2 fields at p = 0 and 2 of the byte
 // and of the byte shifted right by 4.
 template <int VBITS>
-__device__ inline int unpack_v_cached(const Ctx &c, int lane, const Fetch &f, uint16_t *Vt) {
+__device__ inline void unpack_v_cached(const Ctx &c, int lane, const Fetch &f, float vsc, uint16_t *Vt) {
   constexpr int P1 = VBITS == 4 ? 4 : 2;
   const int kq = lane & 7, dq = lane >> 3;
   const int a = kq & 3;
   const int slot = 16 * (kq >> 2) + 4 * (a >> 1) + 8 * (a & 1);
-  float vmax = 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    vmax = fmaxf(vmax, fmaxf(fabsf(f.vzero[j]), fabsf(fmaf(f.vstep[j], static_cast<float>((1 << VBITS) - 1), f.vzero[j]))));
-  const int ev = value_exponent(wave_max(vmax));
-  const float vsc = ldexpf(1.0f, -ev);
   float dd[4][2], zz[4][2];  // per key: operands of the fields at p = 0 and p = P1
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -316,88 +320,113 @@ __device__ inline int unpack_v_cached(const Ctx &c, int lane, const Fetch &f, ui
     for (int fl = 0; fl < NF; ++fl)
       *reinterpret_cast<uint2 *>(Vt + vts(16 * dq + NF * byte + fl, slot)) = make_uint2(x[fl][0], x[fl][1]);
   }
-  return ev;
 }
 
-// Current-chunk block (bf16 keys and values, rescaled to fp16 like the
-// cached ones); returns the key exponent, ev the value exponent.
-__device__ inline int unpack_current(const Ctx &c, int k0, int lane, uint16_t *Kt, uint16_t *Vt, int &ev) {
+// Current-chunk block (bf16 keys and values): the lane's raw rows (same
+// lane roles as the cached blocks; rows past the end clamp to the last one,
+// their scores are masked) and the largest |k| and |v| among them.
+struct Cur {
+  uint4 k[8];      // key kr, d = 64h .. 64h+63
+  uint32_t v[4][8];  // keys 4kq+j, bf16 pairs of d = 16dq + 2i, +1
+};
+__device__ inline void load_current(const Ctx &c, int k0, int lane, Cur &x, float &kb, float &vb) {
   const int last = c.ncur - 1;
-  int ek;
+  kb = vb = 0.f;
   {
     const int kr = lane & 31, h = lane >> 5;
     const uint32_t row = static_cast<uint32_t>(k0 + kr <= last ? k0 + kr : last);
     const uint4 *ks = reinterpret_cast<const uint4 *>(c.k_cur + (row * D + 64u * h));
-    uint4 x[8];
-    float bound = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      x[i] = ks[i];
-      const uint32_t u[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
+      x.k[i] = ks[i];
+      const uint32_t u[4] = {x.k[i].x, x.k[i].y, x.k[i].z, x.k[i].w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) bound = fmaxf(bound, fmaxf(fabsf(lo_f(u[e])), fabsf(hi_f(u[e]))));
-    }
-    const float kb = wave_max(bound);
-    ek = kb > 0.f ? ilog2_pos(kb) - kFp16Exp : 0;
-    const float kscale = ldexpf(1.0f, -ek);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t u[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
-      uint32_t w[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = pack2h(lo_f(u[e]) * kscale, hi_f(u[e]) * kscale);
-      *reinterpret_cast<uint4 *>(Kt + kr * KS + 64 * h + 8 * i) = make_uint4(w[0], w[1], w[2], w[3]);
+      for (int e = 0; e < 4; ++e) kb = fmaxf(kb, fmaxf(fabsf(lo_f(u[e])), fabsf(hi_f(u[e]))));
     }
   }
   {
     const int kq = lane & 7, dq = lane >> 3;
-    const int a = kq & 3;
-    const int slot = 16 * (kq >> 2) + 4 * (a >> 1) + 8 * (a & 1);
-    uint32_t x[4][8];  // key j, bf16 pairs of d = 16dq + 2i, +1
-    float bound = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t row = static_cast<uint32_t>(k0 + 4 * kq + j <= last ? k0 + 4 * kq + j : last);
       const uint4 *vs = reinterpret_cast<const uint4 *>(c.v_cur + (row * D + 16u * dq));
       const uint4 y0 = vs[0], y1 = vs[1];
-      x[j][0] = y0.x; x[j][1] = y0.y; x[j][2] = y0.z; x[j][3] = y0.w;
-      x[j][4] = y1.x; x[j][5] = y1.y; x[j][6] = y1.z; x[j][7] = y1.w;
+      x.v[j][0] = y0.x; x.v[j][1] = y0.y; x.v[j][2] = y0.z; x.v[j][3] = y0.w;
+      x.v[j][4] = y1.x; x.v[j][5] = y1.y; x.v[j][6] = y1.z; x.v[j][7] = y1.w;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) bound = fmaxf(bound, fmaxf(fabsf(lo_f(x[j][i])), fabsf(hi_f(x[j][i]))));
-    }
-    ev = value_exponent(wave_max(bound));
-    const float vsc = ldexpf(1.0f, -ev);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      *reinterpret_cast<uint2 *>(Vt + vts(16 * dq + 2 * i, slot)) =
-          make_uint2(pack2h(lo_f(x[0][i]) * vsc, lo_f(x[1][i]) * vsc), pack2h(lo_f(x[2][i]) * vsc, lo_f(x[3][i]) * vsc));
-      *reinterpret_cast<uint2 *>(Vt + vts(16 * dq + 2 * i + 1, slot)) =
-          make_uint2(pack2h(hi_f(x[0][i]) * vsc, hi_f(x[1][i]) * vsc), pack2h(hi_f(x[2][i]) * vsc, hi_f(x[3][i]) * vsc));
+      for (int i = 0; i < 8; ++i) vb = fmaxf(vb, fmaxf(fabsf(lo_f(x.v[j][i])), fabsf(hi_f(x.v[j][i]))));
     }
   }
-  return ek;
 }
+
+// Keys to MFMA operand registers (as unpack_k_cached, no correction) and
+// values to the V^T tile (as unpack_v_cached), both rescaled to fp16.
+__device__ inline void unpack_current(int lane, const Cur &x, float kscale, float vsc, f16x8 (&k)[8], uint16_t *Vt) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t u[4] = {x.k[i].x, x.k[i].y, x.k[i].z, x.k[i].w};
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = pack2h(lo_f(u[e]) * kscale, hi_f(u[e]) * kscale);
+    k[i] = __builtin_bit_cast(f16x8, make_uint4(w[0], w[1], w[2], w[3]));
+  }
+  const int kq = lane & 7, dq = lane >> 3;
+  const int a = kq & 3;
+  const int slot = 16 * (kq >> 2) + 4 * (a >> 1) + 8 * (a & 1);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    *reinterpret_cast<uint2 *>(Vt + vts(16 * dq + 2 * i, slot)) =
+        make_uint2(pack2h(lo_f(x.v[0][i]) * vsc, lo_f(x.v[1][i]) * vsc), pack2h(lo_f(x.v[2][i]) * vsc, lo_f(x.v[3][i]) * vsc));
+    *reinterpret_cast<uint2 *>(Vt + vts(16 * dq + 2 * i + 1, slot)) =
+        make_uint2(pack2h(hi_f(x.v[0][i]) * vsc, hi_f(x.v[1][i]) * vsc), pack2h(hi_f(x.v[2][i]) * vsc, hi_f(x.v[3][i]) * vsc));
+  }
+}
+
+// Block exponents of a wave (uniform).  A block keeps the previous block's
+// exponent while all its values fit the fp16 headroom of it (|k| 2^-ek below
+// 2^15, |v| 2^-ev below 2^14): fp16 precision is relative, so an exponent
+// chosen for larger values costs nothing until values fall 2^28 below them.
+// Otherwise the exponent is recomputed from the block's largest magnitude
+// (one wave reduction): |k| 2^-ek in [2^14, 2^15), |v| 2^-ev in [2^13, 2^14).
+struct Scales {
+  int ek = 0, ev = 0;
+  float klim = 0.f, vlim = 0.f;    // 2^(15+ek), 2^(14+ev); 0 before the first block
+  float kscale = 1.f, vscale = 1.f;  // 2^-ek, 2^-ev
+  float alpha = 0.f;               // softmax scale of the block's scores (exp2 domain)
+  __device__ void update(float kb, float vb, float alpha_q) {
+    if (!__all(kb < klim)) {
+      const float m = wave_max(kb);
+      ek = m > 0.f ? ilog2_pos(m) - kFp16Exp : 0;
+      klim = ldexpf(32768.0f, ek);
+      kscale = ldexpf(1.0f, -ek);
+      alpha = ldexpf(alpha_q, ek);
+    }
+    if (!__all(vb < vlim)) {
+      ev = value_exponent(wave_max(vb));
+      vlim = ldexpf(16384.0f, ev);
+      vscale = ldexpf(1.0f, -ev);
+    }
+  }
+};
 
 struct Soft {
   f32x16 o[D / 32];
   float m, l, alpha;
 };
 
-// Scores, softmax and value product of one block from the wave's tiles.
-// count < BK marks a ragged block; CORR adds the correction step.
+// Scores, softmax and value product of one block: K operand registers,
+// the wave's V^T tile, the block's score scale alpha (scores are
+// q.k 2^-(eq+ek)) and value exponent ev.  count < BK marks a ragged block;
+// CORR adds the correction step.
 template <bool CORR>
-__device__ inline void block_compute(const uint16_t *Kt, const uint16_t *Vt, const f16x8 (&q)[8], bf16x8 qext,
-                                     int count, int ek, int ev, int lane, Soft &st) {
-  const float alpha = ldexpf(st.alpha, ek);  // scores of this block are q.k * 2^-(eq+ek)
+__device__ inline void block_compute(const f16x8 (&k)[8], bf16x8 kext, const uint16_t *Vt, const f16x8 (&q)[8],
+                                     bf16x8 qext, int count, float alpha, int ev, int lane, Soft &st) {
   const float fev = static_cast<float>(ev);
   const int qc = lane & 31, h = lane >> 5;
   f32x16 s = f32x16{};
-  const uint16_t *kb = Kt + qc * KS + 8 * h;
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    s = __builtin_amdgcn_mfma_f32_32x32x16_f16(*reinterpret_cast<const f16x8 *>(kb + 16 * j), q[j], s, 0, 0, 0);
-  if (CORR)
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8 *>(kb + KEXT), qext, s, 0, 0, 0);
+  for (int j = 0; j < 8; ++j) s = __builtin_amdgcn_mfma_f32_32x32x16_f16(k[j], q[j], s, 0, 0, 0);
+  if (CORR) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kext, qext, s, 0, 0, 0);
   if (count < BK) {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
@@ -443,7 +472,7 @@ __device__ inline void block_compute(const uint16_t *Kt, const uint16_t *Vt, con
 template <int KBITS, int VBITS, bool TAYLOR, int NG>
 __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, int64_t rows_per_kvhead,
                                                                 int32_t row_groups, int32_t nsplit, float *ws) {
-  __shared__ __attribute__((aligned(16))) uint16_t L[WAVES * WLDS];
+  __shared__ __attribute__((aligned(16))) uint16_t L[LDS_BYTES / 2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -472,7 +501,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
   f16x8 q[8];
   bf16x8 qext;
   Soft st;
-  load_query<TAYLOR>(p.q + qrow * D, h, group_shift, p.tau, 0, q, qext, st.alpha);
+  load_query<TAYLOR, true>(p.q + qrow * D, h, group_shift, p.tau, 0, q, qext, st.alpha);
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) st.o[db] = f32x16{};
   st.m = -INFINITY;
@@ -504,34 +533,40 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
   const int bps = (nbt + nsplit - 1) / nsplit;
   const int bbeg = static_cast<int>(split) * bps;
   const int bend = bbeg + bps < nbt ? bbeg + bps : nbt;
-  uint16_t *Kt = L + wave * WLDS;
-  uint16_t *Vt = Kt + KT;
+  uint16_t *Vt = L + wave * VT;
 
   int blk = bbeg + wave;
   const int cend = bend < nbc ? bend : nbc;
   const Lanes lo = lane_offsets<KBITS, VBITS, NG>(lane);
+  Scales sc;
+  f16x8 kreg[8];
+  bf16x8 kext = {};
   Fetch f;
   if (blk < cend) fetch_cached<KBITS, VBITS, NG>(c, blk * BK, lo, h, f);
   for (; blk < cend; blk += WAVES) {
     const int k0 = blk * BK;
     const int count = c.nc - k0 < BK ? c.nc - k0 : BK;
-    const int ek = unpack_k_cached<TAYLOR, KBITS, NG>(c, lane, f, Kt);
-    const int ev = unpack_v_cached<VBITS>(c, lane, f, Vt);
+    sc.update(k_bound<KBITS>(f), v_bound<VBITS>(f), st.alpha);
+    unpack_k_cached<TAYLOR, KBITS, NG>(c, lane, f, sc.kscale, kreg, kext);
+    unpack_v_cached<VBITS>(c, lane, f, sc.vscale, Vt);
     if (blk + WAVES < cend) fetch_cached<KBITS, VBITS, NG>(c, (blk + WAVES) * BK, lo, h, f);
-    block_compute<TAYLOR>(Kt, Vt, q, qext, count, ek, ev, lane, st);
+    block_compute<TAYLOR>(kreg, kext, Vt, q, qext, count, sc.alpha, sc.ev, lane, st);
   }
   for (; blk < bend; blk += WAVES) {
     const int k0 = (blk - nbc) * BK;
     const int count = c.ncur - k0 < BK ? c.ncur - k0 : BK;
-    int ev;
-    const int ek = unpack_current(c, k0, lane, Kt, Vt, ev);
-    block_compute<false>(Kt, Vt, q, qext, count, ek, ev, lane, st);
+    Cur x;
+    float kb, vb;
+    load_current(c, k0, lane, x, kb, vb);
+    sc.update(kb, vb, st.alpha);
+    unpack_current(lane, x, sc.kscale, sc.vscale, kreg, Vt);
+    block_compute<false>(kreg, kext, Vt, q, qext, count, sc.alpha, sc.ev, lane, st);
   }
 
   // ---- merge the 4 waves (log-sum-exp), then the split partial or output ----
   const float l_tot = st.l + __shfl_xor(st.l, 32, 64);
   __syncthreads();  // every wave is done with its tiles
-  float *Ob = reinterpret_cast<float *>(L) + wave * (32 * OS + 64);
+  float *Ob = reinterpret_cast<float *>(L) + wave * MERGE;
   float *ml = Ob + 32 * OS;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -551,7 +586,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
       float mw[WAVES], m = -INFINITY;
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) {
-        mw[w] = reinterpret_cast<const float *>(L)[w * (32 * OS + 64) + 32 * OS + 2 * row];
+        mw[w] = reinterpret_cast<const float *>(L)[w * MERGE + 32 * OS + 2 * row];
         m = fmaxf(m, mw[w]);
       }
       float acc[16], l = 0.f;
@@ -559,7 +594,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
       for (int e = 0; e < 16; ++e) acc[e] = 0.f;
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) {
-        const float *base = reinterpret_cast<const float *>(L) + w * (32 * OS + 64);
+        const float *base = reinterpret_cast<const float *>(L) + w * MERGE;
         const float fw = mw[w] == -INFINITY ? 0.f : exp2f(mw[w] - m);
         l += fw * base[32 * OS + 2 * row + 1];
 #pragma unroll

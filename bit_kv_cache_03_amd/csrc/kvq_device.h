@@ -117,14 +117,16 @@ __device__ inline void pin(T &x) {
 }
 
 // The lane's query row for the fp16 Q K^T product (lane half h holds
-// dimensions 16 s + 8 h .. +7 of k-step s): the row scaled by its own power
+// dimensions 16 s + 8 h .. +7 of k-step s, or with HALVES the contiguous
+// 64 h + 8 s .. +7, so that each lane half covers one half of the head
+// dimension): the row scaled by its own power
 // of two 2^-eq (largest |q| to [2^14, 2^15)), the softmax scale of the
 // resulting scores (alpha = tau log2(e) 2^(eq+ek) for keys scaled by 2^-ek),
 // and the Taylor correction operands N_g = tau/24 ||q_g||^2 2^-(eq+ek) in
 // slots 4g+{0,1,2,3} as (hi, hi, lo, 0) split into bf16 (the lane holds
 // slots 8h .. 8h+7, i.e. groups 2h and 2h+1; zero when not TAYLOR).  The
 // row's other half sits in lane l^32.
-template <bool TAYLOR>
+template <bool TAYLOR, bool HALVES = false>
 __device__ inline void load_query(const uint16_t *qptr, int h, int group_shift, float tau, int ek, f16x8 (&q)[8],
                                   bf16x8 &qext, float &alpha) {
   const int ng = 128 >> group_shift;
@@ -133,7 +135,8 @@ __device__ inline void load_query(const uint16_t *qptr, int h, int group_shift, 
   float qmax = 0.f;
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
-    qw[s] = *reinterpret_cast<const uint4 *>(qptr + 16 * s + 8 * h);
+    const int d0 = HALVES ? 64 * h + 8 * s : 16 * s + 8 * h;
+    qw[s] = *reinterpret_cast<const uint4 *>(qptr + d0);
     const uint32_t u[4] = {qw[s].x, qw[s].y, qw[s].z, qw[s].w};
     float acc = 0.f;
 #pragma unroll
@@ -141,7 +144,7 @@ __device__ inline void load_query(const uint16_t *qptr, int h, int group_shift, 
       acc += lo_f(u[i]) * lo_f(u[i]) + hi_f(u[i]) * hi_f(u[i]);
       qmax = fmaxf(qmax, fmaxf(fabsf(lo_f(u[i])), fabsf(hi_f(u[i]))));
     }
-    const int gs = (16 * s + 8 * h) >> group_shift;
+    const int gs = d0 >> group_shift;
 #pragma unroll
     for (int g = 0; g < 4; ++g) nsum[g] += g == gs ? acc : 0.f;
   }
