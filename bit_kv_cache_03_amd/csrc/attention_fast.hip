@@ -73,26 +73,31 @@ __device__ inline int vt_index(int row, int col) {
 // ---- pre-pass: fp16 scale of the keys of each KV head ----------------------
 // Dequantised cached keys lie between z and z + (2^bits - 1) D of their
 // group (the two ends of the code range), so the bound needs only the step
-// and zero arrays; current keys are scanned directly.
+// and zero arrays; current keys are scanned directly.  Each KV head's rows
+// are split over KCHUNKS workgroups, each writing the largest |key| of its
+// share; the attention kernel reduces the KCHUNKS partial bounds.
+constexpr int KCHUNKS = 32;
+
 template <int KBITS>
-__global__ __launch_bounds__(256) void key_scale_kernel(AttnLaunch p, int32_t ng, int32_t *exps) {
+__global__ __launch_bounds__(256) void key_scale_kernel(AttnLaunch p, int32_t ng, float *part) {
   __shared__ float red[4];
-  const int64_t bkv = blockIdx.x;
+  const int64_t bkv = blockIdx.x / KCHUNKS;
+  const int64_t ch = blockIdx.x % KCHUNKS;
   const int tid = threadIdx.x;
   float bound = 0.f;
   if (p.Nc > 0) {
     const float *s = p.kc_scale + bkv * p.cap * ng;
     const float *z = p.kc_zero + bkv * p.cap * ng;
-    const int64_t n = p.Nc * ng;
-    for (int64_t i = tid; i < n; i += 256) {
+    const int64_t n = p.Nc * ng, lo = n * ch / KCHUNKS, hi = n * (ch + 1) / KCHUNKS;
+    for (int64_t i = lo + tid; i < hi; i += 256) {
       const float zi = z[i];
       bound = fmaxf(bound, fmaxf(fabsf(zi), fabsf(fmaf(s[i], static_cast<float>((1 << KBITS) - 1), zi))));
     }
   }
   if (p.Ncur > 0) {
     const uint4 *k = reinterpret_cast<const uint4 *>(p.k_cur + bkv * p.Ncur * D);
-    const int64_t n = p.Ncur * D / 8;
-    for (int64_t i = tid; i < n; i += 256) {
+    const int64_t n = p.Ncur * D / 8, lo = n * ch / KCHUNKS, hi = n * (ch + 1) / KCHUNKS;
+    for (int64_t i = lo + tid; i < hi; i += 256) {
       const uint4 w = k[i];
       const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -103,7 +108,7 @@ __global__ __launch_bounds__(256) void key_scale_kernel(AttnLaunch p, int32_t ng
   for (int o = 32; o >= 1; o >>= 1) bound = fmaxf(bound, __shfl_xor(bound, o, 64));
   if ((tid & 63) == 0) red[tid >> 6] = bound;
   __syncthreads();
-  if (tid == 0) exps[bkv] = scale_exponent(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+  if (tid == 0) part[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
 // ---- per-wave state ---------------------------------------------------------
@@ -508,7 +513,7 @@ __device__ inline void segment(const Ctx &c, const QState &qs, Soft &st, uint16_
 template <int KBITS, int VBITS, bool TAYLOR>
 __global__ __launch_bounds__(THREADS, 1) void attn_fast_kernel(AttnLaunch p, int32_t group_shift,
                                                                 int64_t rows_per_kvhead, int32_t row_blocks,
-                                                                const int32_t *kexp) {
+                                                                const float *kpart) {
   __shared__ __attribute__((aligned(16))) uint16_t Kl[2 * KBUF];
   __shared__ __attribute__((aligned(16))) uint16_t Vl[NVBUF * VBUF];
 
@@ -526,7 +531,11 @@ __global__ __launch_bounds__(THREADS, 1) void attn_fast_kernel(AttnLaunch p, int
   const int64_t rb = lin - bkv * row_blocks;
   const int64_t b = bkv / p.Hkv, hk = bkv - b * p.Hkv;
   const int64_t gq = p.Hq / p.Hkv;
-  const int ek = kexp[bkv];
+  // key exponent of the KV head from the pre-pass's partial bounds
+  float kb = lane < KCHUNKS ? kpart[bkv * KCHUNKS + lane] : 0.f;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) kb = fmaxf(kb, __shfl_xor(kb, o, 64));
+  const int ek = scale_exponent(kb);
 
   // ---- the lane's query row: fp16 operands, scale, correction operands ----
   QState qs;
@@ -584,13 +593,13 @@ hipError_t launch_bits(const AttnLaunch &p, hipStream_t stream) {
   const int64_t rows = p.Nq * (p.Hq / p.Hkv);
   const int32_t row_blocks = static_cast<int32_t>((rows + BM - 1) / BM);
   const int32_t gshift = __builtin_ctz(static_cast<unsigned>(p.group));
-  int32_t *kexp = static_cast<int32_t *>(p.workspace);
-  launch_key_scale(p, stream, kexp);
+  float *kpart = static_cast<float *>(p.workspace);
+  launch_key_scale(p, stream, kpart);
   const dim3 grid(static_cast<uint32_t>(row_blocks * p.B * p.Hkv));
   if (p.corr == KV_CORR_TAYLOR)
-    attn_fast_kernel<KB, VB, true><<<grid, dim3(THREADS), 0, stream>>>(p, gshift, rows, row_blocks, kexp);
+    attn_fast_kernel<KB, VB, true><<<grid, dim3(THREADS), 0, stream>>>(p, gshift, rows, row_blocks, kpart);
   else
-    attn_fast_kernel<KB, VB, false><<<grid, dim3(THREADS), 0, stream>>>(p, gshift, rows, row_blocks, kexp);
+    attn_fast_kernel<KB, VB, false><<<grid, dim3(THREADS), 0, stream>>>(p, gshift, rows, row_blocks, kpart);
   return hipGetLastError();
 }
 
@@ -598,17 +607,17 @@ hipError_t launch_bits(const AttnLaunch &p, hipStream_t stream) {
 
 bool fast_path_supported(const AttnLaunch &p) { return p.d == D && p.corr != KV_CORR_EXACT; }
 
-void launch_key_scale(const AttnLaunch &p, hipStream_t stream, int32_t *exps) {
+void launch_key_scale(const AttnLaunch &p, hipStream_t stream, float *part) {
   const int32_t ng = D / p.group;
-  const dim3 grid(static_cast<uint32_t>(p.B * p.Hkv));
+  const dim3 grid(static_cast<uint32_t>(p.B * p.Hkv * KCHUNKS));
   if (p.Nc > 0 && p.kbits == 4)
-    key_scale_kernel<4><<<grid, dim3(256), 0, stream>>>(p, ng, exps);
+    key_scale_kernel<4><<<grid, dim3(256), 0, stream>>>(p, ng, part);
   else
-    key_scale_kernel<2><<<grid, dim3(256), 0, stream>>>(p, ng, exps);
+    key_scale_kernel<2><<<grid, dim3(256), 0, stream>>>(p, ng, part);
 }
 
 size_t fast_path_workspace_bytes(int64_t B, int64_t Hkv) {
-  return (static_cast<size_t>(B * Hkv) * sizeof(int32_t) + 255) / 256 * 256;
+  return (static_cast<size_t>(B * Hkv) * KCHUNKS * sizeof(float) + 255) / 256 * 256;
 }
 
 hipError_t launch_attention_fast(const AttnLaunch &p, hipStream_t stream) {

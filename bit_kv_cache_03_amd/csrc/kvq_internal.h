@@ -47,13 +47,14 @@ hipError_t launch_quantize(const QuantizeLaunch &p, hipStream_t stream);
 hipError_t launch_attention_long(const AttnLaunch &p, hipStream_t stream);
 hipError_t launch_attention_short(const AttnLaunch &p, hipStream_t stream);
 // Throughput kernel (attention_fast.hip): head dim 128, correction off or
-// Taylor.  Its workspace holds one int32 key-scale exponent per (b, KV head).
+// Taylor.  Its workspace holds 32 fp32 partial key bounds per (b, KV head).
 bool fast_path_supported(const AttnLaunch &p);
 size_t fast_path_workspace_bytes(int64_t B, int64_t Hkv);
 hipError_t launch_attention_fast(const AttnLaunch &p, hipStream_t stream);
-// Pre-pass of the fp16 kernels: per (b, KV head) the exponent ek with the
-// largest |key| (dequantised cache and current chunk) times 2^-ek below 2^15.
-void launch_key_scale(const AttnLaunch &p, hipStream_t stream, int32_t *exps);
+// Pre-pass of the throughput kernel: per (b, KV head), 32 partial bounds of
+// |key| (dequantised cache and current chunk), from which the kernel takes
+// the exponent ek with the largest |key| times 2^-ek below 2^15.
+void launch_key_scale(const AttnLaunch &p, hipStream_t stream, float *part);
 
 // Short path: cached-token split count chosen for a problem and the
 // workspace it needs (partials of every split for every query row).

@@ -159,12 +159,13 @@ def test_short_path_needs_workspace(kvq):
 
 
 def test_long_path_workspace(kvq):
-    """The head-dim-128 long path keeps one int32 key-scale exponent per
+    """The head-dim-128 long path keeps 32 fp32 partial key bounds per
     (batch, KV head), rounded up to 256 bytes; the general kernel (head dim
     64, or the exact correction) needs none."""
     size = lambda **kw: kvq.lib.kv_attention_workspace_size(C.byref(_args(kvq, path=1, **kw)))
-    assert size() == 256
-    assert size(B=3, Hq=80, Hkv=40) == 512          # 120 heads x 4 B -> 480 -> 512
+    assert size() == 256                            # 2 heads x 32 x 4 B
+    assert size(B=3, Hq=80, Hkv=40) == 15360        # 120 heads x 128 B
+    assert size(B=1, Hq=3, Hkv=3) == 512            # 384 B -> 512
     assert size(corr=2) == 0
     assert size(d=64) == 0
     a = _args(kvq, path=1)
