@@ -5,8 +5,12 @@
 // Work split: one workgroup = 8 waves = 256 query rows of one KV head (GQA
 // rows of all its query heads packed together), 32 rows per wave; two waves
 // per SIMD, so the vector ALU of a SIMD is fed by two instruction streams.
-// Workgroup ids are remapped so that all row blocks of one KV head run on
-// one XCD and share its L2.
+// When the row blocks alone would leave the last round of workgroups
+// partly empty, the key range is also split (split-K): each split takes a
+// contiguous share of the 64-key tiles of [cache ; current chunk] and writes
+// unnormalised partials that attn_combine_kernel merges.  Workgroup ids
+// are remapped so that all row blocks of one KV head and split run on one
+// XCD and share its L2.
 //
 // Keys enter the Q K^T product as fp16: cached keys are dequantised in fp32
 // and rounded once to fp16 (11-bit significand, ~8x finer than a bf16
@@ -22,7 +26,11 @@
 //   1. S_t = K_t Q^T (fp16 MFMA)  with  exponentials of tile t-1 (VALU)
 //   2. O += V_{t-1}^T P_{t-1}^T   with  dequantisation of tile t+1 into LDS,
 //                                       the max of S_t, the HBM fetch of t+2
-//   3. lazy rescale of O and l when the running max moves
+//   3. on a segment's first tile only: its max, which sets the running max
+// After that the running max moves only when a tile's probabilities would
+// grow past 2^40 (see fix_growth): bf16 probabilities and the fp32 O and l
+// keep their relative precision at any such magnitude, so the per-tile max
+// is not needed.
 // K tiles are double-buffered and V tiles triple-buffered in LDS; one
 // barrier per tile.  Keys past the end of a segment are fetched as copies
 // of its last key: their scores equal that key's, so the tile max is
@@ -344,6 +352,33 @@ __device__ inline void exp_item(int k, const f32x16 (&acc)[2], Soft &st, int cou
   }
 }
 
+// Guard of the running max after the exponentials of a tile: if some row's
+// sum passed kGrowth (or overflowed), raise that row's max to the tile max,
+// rescale O and the sum taken before the tile (l0), and redo the tile's
+// probabilities.  Rare: it needs scores 40 binary orders above the first
+// tile's max.
+constexpr float kGrowth = 1099511627776.0f;  // 2^40
+
+template <bool MASK>
+__device__ inline void fix_growth(const f32x16 (&s)[2], Soft &st, float l0, int count, int h, bf16x8 (&pk)[4]) {
+  if (!__any(!(st.l < kGrowth))) return;
+  float mt = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[kb][i]);
+  mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * st.alpha;
+  const float m_new = fmaxf(st.m, mt);
+  const float sc = exp2f(st.m - m_new);
+  st.l = l0 * sc;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) st.o[db] *= sc;
+  st.m = m_new;
+  float e[8];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) exp_item<MASK>(k, s, st, count, h, e, pk);
+}
+
 // ---- MFMA sequences ------------------------------------------------------------
 // S^T of the wave's block: MFMA j < 16 uses the K fragment of k-step j / 2 of
 // key block j % 2; j = 16, 17 are the correction steps of the two blocks.
@@ -362,7 +397,8 @@ __device__ inline uint4 lds16(const uint16_t *p) { return *reinterpret_cast<cons
 #define KVQ_FENCE() __builtin_amdgcn_sched_barrier(0)
 
 // One step of the cross-tile pipeline of a segment:
-//   QK:   S_t of tile t (LDS K buffer Kl), then its max and the lazy rescale;
+//   QK:   S_t of tile t (LDS K buffer Kl); on the segment's first tile
+//         (QK without PREV) also its max and the lazy rescale;
 //   PREV: P_{t-1} from the saved scores S_{t-1} and O += V_{t-1} P_{t-1}
 //         (LDS V buffer Vp), MASK for a ragged last tile of count keys;
 //   NEXT: dequantise tile t+1 from f into K buffer Kn / V buffer Vn, and
@@ -381,6 +417,7 @@ __device__ inline void tile_step(const Ctx &c, const QState &qs, Soft &st, Fetch
   bf16x8 pk[4];
 
   // 1. S_t (fp16 keys, bf16 correction step), with the exponentials of t-1
+  const float l0 = st.l;
   if (QK) {
     sn[0] = f32x16{};
     sn[1] = f32x16{};
@@ -401,6 +438,7 @@ __device__ inline void tile_step(const Ctx &c, const QState &qs, Soft &st, Fetch
     if (PREV && j < 16) exp_item<MASK>(j, s, st, count, h, ev, pk);
     KVQ_FENCE();
   }
+  if (PREV) fix_growth<MASK>(s, st, l0, count, h, pk);
 
   // 2. O += V_{t-1}^T P_{t-1}^T, with tile t+1 into LDS, the max of S_t and
   //    the fetch of tile t+2
@@ -424,11 +462,11 @@ __device__ inline void tile_step(const Ctx &c, const QState &qs, Soft &st, Fetch
         else if (j == 9) fetch_k<CACHED, KBITS>(c, k0_next2, tid, f);
         else if (j == 10 || j == 11) fetch_v<CACHED, VBITS>(c, k0_next2, tid, j - 10, f);
       }
-      if (QK && j >= 12) max_item(j - 12, sn, mt);
+      if (QK && !PREV && j >= 12) max_item(j - 12, sn, mt);
       KVQ_FENCE();
     }
   }
-  if (QK) max_update(mt, st);
+  if (QK && !PREV) max_update(mt, st);
 }
 
 #undef KVQ_FENCE
@@ -513,7 +551,8 @@ __device__ inline void segment(const Ctx &c, const QState &qs, Soft &st, uint16_
 template <int KBITS, int VBITS, bool TAYLOR>
 __global__ __launch_bounds__(THREADS, 1) void attn_fast_kernel(AttnLaunch p, int32_t group_shift,
                                                                 int64_t rows_per_kvhead, int32_t row_blocks,
-                                                                const float *kpart) {
+                                                                const float *kpart, int32_t nsplit,
+                                                                float *partials) {
   __shared__ __attribute__((aligned(16))) uint16_t Kl[2 * KBUF];
   __shared__ __attribute__((aligned(16))) uint16_t Vl[NVBUF * VBUF];
 
@@ -527,8 +566,11 @@ __global__ __launch_bounds__(THREADS, 1) void attn_fast_kernel(AttnLaunch p, int
   const uint32_t nwg = gridDim.x, wg = blockIdx.x;
   const uint32_t per = nwg >> 3, extra = nwg & 7, xcd = wg & 7, slot = wg >> 3;
   const uint32_t lin = (xcd < extra ? xcd * (per + 1) : extra * (per + 1) + (xcd - extra) * per) + slot;
-  const int64_t bkv = lin / static_cast<uint32_t>(row_blocks);
-  const int64_t rb = lin - bkv * row_blocks;
+  const uint32_t per_split = static_cast<uint32_t>(row_blocks * p.B * p.Hkv);
+  const int64_t split = lin / per_split;
+  const int64_t rem = lin - split * per_split;
+  const int64_t bkv = rem / static_cast<uint32_t>(row_blocks);
+  const int64_t rb = rem - bkv * row_blocks;
   const int64_t b = bkv / p.Hkv, hk = bkv - b * p.Hkv;
   const int64_t gq = p.Hq / p.Hkv;
   // key exponent of the KV head from the pre-pass's partial bounds
@@ -564,19 +606,36 @@ __global__ __launch_bounds__(THREADS, 1) void attn_fast_kernel(AttnLaunch p, int
     c.vc_scale = p.vc_scale + hrow * ng;
     c.vc_zero = p.vc_zero + hrow * ng;
   }
-  c.beg = 0;
-  c.end = static_cast<int>(p.Nc);
+  // this split's tiles [t0, t1) of the cached tiles followed by the current ones
+  const int tc = static_cast<int>((p.Nc + BN - 1) / BN), tu = static_cast<int>((p.Ncur + BN - 1) / BN);
+  const int t0 = static_cast<int>(split * (tc + tu) / nsplit), t1 = static_cast<int>((split + 1) * (tc + tu) / nsplit);
+  c.beg = min(t0, tc) * BN;
+  c.end = min(min(t1, tc) * BN, static_cast<int>(p.Nc));
   segment<true, TAYLOR, KBITS, VBITS>(c, qs, st, Kl, Vl, tid);
   if (p.Ncur > 0) {
     c.k_cur = p.k_cur + bkv * p.Ncur * D;
     c.v_cur = p.v_cur + bkv * p.Ncur * D;
   }
-  c.beg = 0;
-  c.end = static_cast<int>(p.Ncur);
+  c.beg = max(t0 - tc, 0) * BN;
+  c.end = min(max(t1 - tc, 0) * BN, static_cast<int>(p.Ncur));
   segment<false, TAYLOR, KBITS, VBITS>(c, qs, st, Kl, Vl, tid);
 
   const float l_tot = st.l + __shfl_xor(st.l, 32, 64);
   if (!row_ok) return;
+  if (nsplit > 1) {  // partial: O (unnormalised), then (m, l); [split][qrow][kPartialStride(D)]
+    float *w = partials + (split * (p.B * p.Hq * p.Nq) + qrow) * kPartialStride(D);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<float4 *>(w + 32 * db + 8 * g4 + 4 * h) =
+            make_float4(st.o[db][4 * g4], st.o[db][4 * g4 + 1], st.o[db][4 * g4 + 2], st.o[db][4 * g4 + 3]);
+    if (h == 0) {
+      w[D] = st.m;
+      w[D + 1] = l_tot;
+    }
+    return;
+  }
   const float inv = 1.0f / l_tot;
   uint16_t *optr = p.out + qrow * D;
 #pragma unroll
@@ -593,14 +652,21 @@ hipError_t launch_bits(const AttnLaunch &p, hipStream_t stream) {
   const int64_t rows = p.Nq * (p.Hq / p.Hkv);
   const int32_t row_blocks = static_cast<int32_t>((rows + BM - 1) / BM);
   const int32_t gshift = __builtin_ctz(static_cast<unsigned>(p.group));
-  float *kpart = static_cast<float *>(p.workspace);
+  const int nsplit = p.splits > 1 ? p.splits : 1;
+  float *partials = static_cast<float *>(p.workspace);
+  float *kpart = reinterpret_cast<float *>(static_cast<char *>(p.workspace) +
+                                           (nsplit > 1 ? short_path_workspace_bytes(p.B, p.Hq, p.Nq, p.d, nsplit) : 0));
   launch_key_scale(p, stream, kpart);
-  const dim3 grid(static_cast<uint32_t>(row_blocks * p.B * p.Hkv));
+  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(nsplit) * row_blocks * p.B * p.Hkv));
   if (p.corr == KV_CORR_TAYLOR)
-    attn_fast_kernel<KB, VB, true><<<grid, dim3(THREADS), 0, stream>>>(p, gshift, rows, row_blocks, kpart);
+    attn_fast_kernel<KB, VB, true><<<grid, dim3(THREADS), 0, stream>>>(p, gshift, rows, row_blocks, kpart, nsplit,
+                                                                       partials);
   else
-    attn_fast_kernel<KB, VB, false><<<grid, dim3(THREADS), 0, stream>>>(p, gshift, rows, row_blocks, kpart);
-  return hipGetLastError();
+    attn_fast_kernel<KB, VB, false><<<grid, dim3(THREADS), 0, stream>>>(p, gshift, rows, row_blocks, kpart, nsplit,
+                                                                        partials);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nsplit == 1) return e;
+  return launch_combine(partials, p.out, p.B * p.Hq * p.Nq, nsplit, p.d, stream);
 }
 
 }  // namespace
@@ -616,8 +682,32 @@ void launch_key_scale(const AttnLaunch &p, hipStream_t stream, float *part) {
     key_scale_kernel<2><<<grid, dim3(256), 0, stream>>>(p, ng, part);
 }
 
-size_t fast_path_workspace_bytes(int64_t B, int64_t Hkv) {
-  return (static_cast<size_t>(B * Hkv) * KCHUNKS * sizeof(float) + 255) / 256 * 256;
+size_t fast_path_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int splits) {
+  const size_t part = splits > 1 ? short_path_workspace_bytes(B, Hq, Nq, D, splits) : 0;
+  return part + (static_cast<size_t>(B * Hkv) * KCHUNKS * sizeof(float) + 255) / 256 * 256;
+}
+
+// Split count of the throughput kernel: rounds of one-per-CU workgroups
+// times the tiles each one runs, plus the HBM traffic of the partials.
+int fast_path_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nc, int64_t Ncur, int cu_count) {
+  const int64_t rows = Nq * (Hq / Hkv);
+  const int64_t wgs = (rows + BM - 1) / BM * B * Hkv;
+  const int64_t tiles = (Nc + BN - 1) / BN + (Ncur + BN - 1) / BN;
+  const double t_tile = 2.0e-6;     // one workgroup, one 64-key tile (measured order)
+  const double bytes_per_s = 4.0e12;  // partial write + combine read
+  const double part_bytes = static_cast<double>(B * Hq * Nq) * kPartialStride(D) * sizeof(float) * 2.0;
+  int best = 1;
+  double best_t = 0.0;
+  for (int64_t s = 1; s <= 64 && s * 2 <= tiles; ++s) {
+    const int64_t rounds = (wgs * s + cu_count - 1) / cu_count;
+    const double t = static_cast<double>(rounds) * static_cast<double>((tiles + s - 1) / s) * t_tile +
+                     (s > 1 ? s * part_bytes / bytes_per_s + 5.0e-6 : 0.0);
+    if (s == 1 || t < best_t * 0.98) {
+      best = static_cast<int>(s);
+      best_t = t;
+    }
+  }
+  return best;
 }
 
 hipError_t launch_attention_fast(const AttnLaunch &p, hipStream_t stream) {

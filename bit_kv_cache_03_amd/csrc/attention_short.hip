@@ -107,16 +107,6 @@ __device__ inline u32x4 ld128(Buf b, uint32_t off) { return __builtin_amdgcn_raw
 // floor(log2 x) for x > 0 (one v_frexp_exp_i32_f32).
 __device__ inline int ilog2_pos(float x) { return __builtin_amdgcn_frexp_expf(x) - 1; }
 
-// Sum of the 8 fp16 values of v, added to acc.
-__device__ inline float sum8h(f16x8 v, float acc) {
-  const uint4 w = __builtin_bit_cast(uint4, v);
-  const f16x2 one = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
-  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w.x), one, acc, false);
-  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w.y), one, acc, false);
-  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w.z), one, acc, false);
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w.w), one, acc, false);
-}
-
 // Exponent ev of a block's values: |v| 2^-ev in [2^13, 2^14) for the largest
 // |v| of the block (0 for an all-zero block), the fp16 range with the most
 // precision.  Every block, cached or current, uses this rule, so the factor

@@ -139,8 +139,12 @@ Plan plan_attention(const kv_attn_args *a, bool query_device) {
       pl.splits = a->splits > 0 ? a->splits : kvq::short_path_splits(a->B, a->Hkv, rows, a->Nc, cus);
       pl.workspace = kvq::short_path_workspace_bytes(a->B, a->Hq, a->Nq, a->d, pl.splits);
     }
-  } else if (a->d == 128 && a->corr != KV_CORR_EXACT) {  // the throughput kernel
-    pl.workspace = kvq::fast_path_workspace_bytes(a->B, a->Hkv);
+  } else if (a->d == 128 && a->corr != KV_CORR_EXACT) {  // the throughput kernel, split-K when it balances
+    const int cus = query_device ? device_cu_count() : 256;
+    const int64_t tiles = (a->Nc + 63) / 64 + (a->Ncur + 63) / 64;
+    pl.splits = a->splits > 0 ? static_cast<int>(a->splits < tiles ? a->splits : tiles)
+                              : kvq::fast_path_splits(a->B, a->Hq, a->Hkv, a->Nq, a->Nc, a->Ncur, cus);
+    pl.workspace = kvq::fast_path_workspace_bytes(a->B, a->Hq, a->Hkv, a->Nq, pl.splits);
   }
   return pl;
 }

@@ -43,6 +43,16 @@ __device__ inline float sum8(bf16x8 v, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.w), one, acc, false);
 }
 
+// Sum of the 8 fp16 values of v, added to acc (two per v_dot2_f32_f16).
+__device__ inline float sum8h(f16x8 v, float acc) {
+  const uint4 w = __builtin_bit_cast(uint4, v);
+  const f16x2 one = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w.x), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w.y), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w.z), one, acc, false);
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w.w), one, acc, false);
+}
+
 // Codes as fp16 "magic" values 1024 + c (exact: the fp16 spacing at 1024 is
 // 1), built two at a time: m[j] holds codes j (low half) and j + 4 (high
 // half) of 8 codes of BITS bits stored LSB first in the low 8*BITS bits of

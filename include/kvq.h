@@ -131,15 +131,18 @@ typedef struct {
   float softmax_scale; /* tau; 0 -> 1/sqrt(d); the correction uses tau^2/24 */
   int32_t corr;       /* kv_corr */
   int32_t path;       /* kv_path */
-  int32_t splits;     /* short path: key-range splits, 0 = automatic, at most 1024 */
+  int32_t splits;     /* key-range splits, 0 = automatic, at most 1024: the short path,
+                         and the long path for d = 128 with correction off or Taylor
+                         (clamped to the number of 64-key tiles) */
   void *workspace;    /* device scratch of kv_attention_workspace_size() bytes */
   size_t workspace_bytes;
 } kv_attn_args;
 
 /* Bytes of device workspace the call needs: on the short path the
  * per-split partial results (splits x B*Hq*Nq rows of d+4 floats); on the
- * long path with d = 128 and correction off or Taylor, 32 fp32 partial key
- * bounds per (b, KV head) rounded up to 256 bytes; otherwise 0.  The
+ * long path with d = 128 and correction off or Taylor, the same partials
+ * when it splits the key range (more than one split), then 32 fp32 partial
+ * key bounds per (b, KV head) rounded up to 256 bytes; otherwise 0.  The
  * contents need no initialisation and are meaningless after the call.
  * Returns 0 for invalid arguments as well; kv_attention_corrected reports
  * those. */

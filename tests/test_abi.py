@@ -166,6 +166,9 @@ def test_long_path_workspace(kvq):
     assert size() == 256                            # 2 heads x 32 x 4 B
     assert size(B=3, Hq=80, Hkv=40) == 15360        # 120 heads x 128 B
     assert size(B=1, Hq=3, Hkv=3) == 512            # 384 B -> 512
+    # forced key-range splits (2 tiles here): partials of 2 splits first
+    assert size(splits=2) == 2 * 1 * 4 * 8 * (128 + 4) * 4 + 256
+    assert size(splits=5) == size(splits=2)         # clamped to the 2 tiles
     assert size(corr=2) == 0
     assert size(d=64) == 0
     a = _args(kvq, path=1)

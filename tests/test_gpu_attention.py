@@ -80,6 +80,16 @@ def test_split_counts(orc, splits):
     _compare(orc, CASES["gqa"], "taylor", "short", splits=splits)
 
 
+@pytest.mark.parametrize("splits", [2, 3, 5, 100])
+def test_long_path_split_counts(orc, splits):
+    """Key-range splits of the throughput kernel, forced: 2 and 3 cut inside
+    the cached segment, 5 also puts a boundary inside the current chunk, 100
+    is clamped to one 64-key tile per split (ragged last tiles in both
+    segments)."""
+    _compare(orc, CASES["longvideo"], "taylor", "long", splits=splits)
+    _compare(orc, CASES["gqa"], "off", "long", splits=splits)
+
+
 def test_correction_matters_and_modes_differ(orc):
     """The GPU output moves with the correction the way the oracle's does."""
     w = CASES["outliers"]
