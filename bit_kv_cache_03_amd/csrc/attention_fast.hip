@@ -12,25 +12,27 @@
 // are remapped so that all row blocks of one KV head and split run on one
 // XCD and share its L2.
 //
-// Keys enter the Q K^T product as fp16: cached keys are dequantised in fp32
-// and rounded once to fp16 (11-bit significand, ~8x finer than a bf16
-// rounding, which moved the scores of large-step groups too much), current
-// keys are converted exactly.  To keep every finite input in fp16 range, a
-// pre-pass (key_scale_kernel) bounds |k| per KV head from the cached steps
-// and zero points and the current keys, and picks a power of two 2^-ek that
-// maps the bound below 2^15; each query row is scaled by its own 2^-eq the
-// same way.  Both scalings are exact and fold into the softmax scale.
-// Probabilities and values stay bf16.
+// Keys enter the Q K^T product as fp16 with the softmax scale folded in:
+// cached keys are dequantised in fp32 as (z + D c) tau log2(e) 2^-ek and
+// rounded once to fp16 (11-bit significand, ~8x finer than a bf16 rounding,
+// which moved the scores of large-step groups too much); queries enter as
+// q 2^ek, exact for bf16 input.  The scores then come out of the MFMA in the
+// exp2 domain.  A pre-pass (key_scale_kernel) bounds |k| and |q| per KV head,
+// and ek balances the two so both operands stay in fp16 range (keys below
+// 2^15 always; queries are clamped there, which only a product
+// |q| |k| tau log2(e) beyond ~2^29 can reach).  Probabilities and values
+// stay bf16.
 //
 // Per 64-key tile, software-pipelined across tiles inside each wave:
-//   1. S_t = K_t Q^T (fp16 MFMA)  with  exponentials of tile t-1 (VALU)
+//   1. S_t = K_t Q^T - m (fp16 MFMA, then one bf16 step)  with
+//      exponentials of tile t-1 (VALU)
 //   2. O += V_{t-1}^T P_{t-1}^T   with  dequantisation of tile t+1 into LDS,
-//                                       the max of S_t, the HBM fetch of t+2
-//   3. on a segment's first tile only: its max, which sets the running max
-// After that the running max moves only when a tile's probabilities would
-// grow past 2^40 (see fix_growth): bf16 probabilities and the fp32 O and l
-// keep their relative precision at any such magnitude, so the per-tile max
-// is not needed.
+//                                       the HBM fetch of t+2
+// The running max m of each row enters the score MFMAs through the extra
+// bf16 step (below), so an exponential is exp2 of the accumulator itself.
+// m starts at 0 and moves only when a row's sum would leave [2^-60, 2^40]
+// (see fix_growth): bf16 probabilities and the fp32 O and l keep their
+// relative precision over that whole range, so no per-tile max is needed.
 // K tiles are double-buffered and V tiles triple-buffered in LDS; one
 // barrier per tile.  Keys past the end of a segment are fetched as copies
 // of its last key: their scores equal that key's, so the tile max is
@@ -40,8 +42,10 @@
 // b = (1/(24 d)) sum_c q_c^2 D_{i,c}^2; §為何校正有效: subtracted from the
 // quantised keys' scores before softmax): one extra K=16 bf16 MFMA step per
 // 32x32 score block, accumulated into the same fp32 scores, with operands
-// [tau/24 * ||q_g||^2 (scaled like the scores)] per query and [-D_g^2] per
-// cached key, each split into bf16 hi and lo parts.
+// [tau^2/24 log2(e) ||q_g||^2] per query and [-D_g^2] per cached key, each
+// split into bf16 hi and lo parts, in slots 4g+{0,1,2}.  Slots 3 and 7 carry
+// the running max: 1.0 on every key, -m (hi, lo) on the query side.  The
+// step runs with the correction off too (then only the max slots are set).
 //
 // MFMA lane layouts (32x32x16, wave64): A operand lane l holds row l%32 and
 // k-slots 8*(l/32)..+7, B operand column l%32 and the same k-slots, the
@@ -78,13 +82,34 @@ __device__ inline int vt_index(int row, int col) {
   return row * VS + ((((col >> 3) ^ (row >> 4)) & 7) << 3) + (col & 7);
 }
 
-// ---- pre-pass: fp16 scale of the keys of each KV head ----------------------
+// ---- pre-pass: fp16 scales of the keys and queries of each KV head --------
 // Dequantised cached keys lie between z and z + (2^bits - 1) D of their
-// group (the two ends of the code range), so the bound needs only the step
-// and zero arrays; current keys are scanned directly.  Each KV head's rows
-// are split over KCHUNKS workgroups, each writing the largest |key| of its
-// share; the attention kernel reduces the KCHUNKS partial bounds.
+// group (the two ends of the code range), so their bound needs only the
+// step and zero arrays; current keys and the queries (the gq query heads of
+// the KV head) are scanned directly.  Each KV head's rows are split over
+// KCHUNKS workgroups, each writing the largest |key| and |query| of its
+// share (part[(2 bkv + 0|1) KCHUNKS + chunk]); the attention kernel reduces
+// the partial bounds.
 constexpr int KCHUNKS = 32;
+
+__device__ inline float bf16_bound(const uint16_t *x, int64_t lo, int64_t hi, int tid) {  // 8-value chunks
+  float b = 0.f;
+  for (int64_t i = lo + tid; i < hi; i += 256) {
+    const uint4 w = reinterpret_cast<const uint4 *>(x)[i];
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b = fmaxf(b, fmaxf(fabsf(lo_f(u[j])), fabsf(hi_f(u[j]))));
+  }
+  return b;
+}
+__device__ inline float block_max(float b, float *red, int tid) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) b = fmaxf(b, __shfl_xor(b, o, 64));
+  __syncthreads();
+  if ((tid & 63) == 0) red[tid >> 6] = b;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
 
 template <int KBITS>
 __global__ __launch_bounds__(256) void key_scale_kernel(AttnLaunch p, int32_t ng, float *part) {
@@ -92,31 +117,32 @@ __global__ __launch_bounds__(256) void key_scale_kernel(AttnLaunch p, int32_t ng
   const int64_t bkv = blockIdx.x / KCHUNKS;
   const int64_t ch = blockIdx.x % KCHUNKS;
   const int tid = threadIdx.x;
-  float bound = 0.f;
+  float kb = 0.f;
   if (p.Nc > 0) {
     const float *s = p.kc_scale + bkv * p.cap * ng;
     const float *z = p.kc_zero + bkv * p.cap * ng;
     const int64_t n = p.Nc * ng, lo = n * ch / KCHUNKS, hi = n * (ch + 1) / KCHUNKS;
     for (int64_t i = lo + tid; i < hi; i += 256) {
       const float zi = z[i];
-      bound = fmaxf(bound, fmaxf(fabsf(zi), fabsf(fmaf(s[i], static_cast<float>((1 << KBITS) - 1), zi))));
+      kb = fmaxf(kb, fmaxf(fabsf(zi), fabsf(fmaf(s[i], static_cast<float>((1 << KBITS) - 1), zi))));
     }
   }
   if (p.Ncur > 0) {
-    const uint4 *k = reinterpret_cast<const uint4 *>(p.k_cur + bkv * p.Ncur * D);
     const int64_t n = p.Ncur * D / 8, lo = n * ch / KCHUNKS, hi = n * (ch + 1) / KCHUNKS;
-    for (int64_t i = lo + tid; i < hi; i += 256) {
-      const uint4 w = k[i];
-      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bound = fmaxf(bound, fmaxf(fabsf(lo_f(u[j])), fabsf(hi_f(u[j]))));
-    }
+    kb = fmaxf(kb, bf16_bound(p.k_cur + bkv * p.Ncur * D, lo, hi, tid));
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) bound = fmaxf(bound, __shfl_xor(bound, o, 64));
-  if ((tid & 63) == 0) red[tid >> 6] = bound;
-  __syncthreads();
-  if (tid == 0) part[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float qb;
+  {
+    const int64_t gq = p.Hq / p.Hkv, b = bkv / p.Hkv, hk = bkv - b * p.Hkv;
+    const int64_t n = gq * p.Nq * D / 8, lo = n * ch / KCHUNKS, hi = n * (ch + 1) / KCHUNKS;
+    qb = bf16_bound(p.q + (b * p.Hq + hk * gq) * p.Nq * D, lo, hi, tid);
+  }
+  kb = block_max(kb, red, tid);
+  qb = block_max(qb, red, tid);
+  if (tid == 0) {
+    part[2 * bkv * KCHUNKS + ch] = kb;
+    part[(2 * bkv + 1) * KCHUNKS + ch] = qb;
+  }
 }
 
 // ---- per-wave state ---------------------------------------------------------
@@ -126,6 +152,46 @@ struct QState {
   f16x8 q[D / 16];
   bf16x8 qext;
 };
+
+// The lane's query operands (lane half h holds dimensions 16 s + 8 h .. +7 of
+// k-step s): q 2^ek in fp16 (exact for bf16 q; clamped to the fp16 range),
+// and the extra step's slots 4g+{0,1,2,3} = (N_hi, N_hi, N_lo, -m) with
+// N_g = tau^2/24 log2(e) ||q_g||^2 split into bf16 (zero without the
+// correction; the lane holds slots 8h .. 8h+7, groups 2h and 2h+1), m = 0.
+template <bool TAYLOR>
+__device__ inline void load_query_folded(const uint16_t *qptr, int h, int group_shift, float tau, int ek,
+                                         QState &qs) {
+  const int ng = 128 >> group_shift;
+  const float qsc = ldexpf(1.0f, ek);
+  float nsum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const uint4 qw = *reinterpret_cast<const uint4 *>(qptr + 16 * s + 8 * h);
+    const uint32_t u[4] = {qw.x, qw.y, qw.z, qw.w};
+    float acc = 0.f;
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc += lo_f(u[i]) * lo_f(u[i]) + hi_f(u[i]) * hi_f(u[i]);
+      w[i] = pack2h(fminf(fmaxf(lo_f(u[i]) * qsc, -65504.0f), 65504.0f),
+                    fminf(fmaxf(hi_f(u[i]) * qsc, -65504.0f), 65504.0f));
+    }
+    qs.q[s] = __builtin_bit_cast(f16x8, make_uint4(w[0], w[1], w[2], w[3]));
+    const int gs = (16 * s + 8 * h) >> group_shift;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) nsum[g] += g == gs ? acc : 0.f;
+  }
+  float nh[4], nl[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const float n = TAYLOR && g < ng ? (nsum[g] + __shfl_xor(nsum[g], 32, 64)) * (tau * tau / 24.0f * kLog2e) : 0.f;
+    nh[g] = lo_f(pack2(n, 0.f));
+    nl[g] = n - nh[g];
+  }
+  const float n0h = h ? nh[2] : nh[0], n0l = h ? nl[2] : nl[0];
+  const float n1h = h ? nh[3] : nh[1], n1l = h ? nl[3] : nl[1];
+  qs.qext = __builtin_bit_cast(bf16x8, make_uint4(pack2(n0h, n0h), pack2(n0l, 0.f), pack2(n1h, n1h), pack2(n1l, 0.f)));
+}
 
 // Packed data of one tile held in registers between the fetch and the unpack.
 struct Fetch {
@@ -145,13 +211,15 @@ struct Ctx {
   const uint16_t *k_cur, *v_cur;
   int ng, group_shift;
   int beg, end;     // key range of the segment
-  float kscale;     // 2^-ek
+  float kscale;     // tau log2(e) 2^-ek
   uint32_t kmask;   // code mask of magic8, in a vector register
 };
 
+// Per-lane softmax state of the lane's query row; m is the value the score
+// MFMAs subtract (bf16 hi + lo, exactly as carried in the query operand).
 struct Soft {
   f32x16 o[D / 32];
-  float m, l, alpha;
+  float m, l;
 };
 
 // Thread roles in fetch / unpack:
@@ -209,13 +277,13 @@ __device__ inline void fetch_v(const Ctx &c, int k0, int tid, int j, Fetch &f) {
 // the vector ALU stay busy together; each item's results are pinned (see
 // pin) so that it stays between its fences.
 
-// K tile row (fp16 values, then the Taylor correction slots 4g+{0,1,2,3} =
-// (-D_g^2 split hi, lo, hi; 0) in bf16, zero for g >= d/group).  Item p < 2
-// writes values 8p..8p+7 of the thread's 16; item 2 writes its two
-// correction slots 2*(tid%8), +1.  A 304-byte row stride keeps the 16-byte
+// K tile row (fp16 values, then the slots of the extra bf16 step: 4g+{0,1,2}
+// = -D_g^2 split (hi, lo, hi) for the Taylor correction (zero for
+// g >= d/group or without it), 1.0 in slots 3 and 7 (the running max), zero
+// elsewhere).  Item p < 2 writes values 8p..8p+7 of the thread's 16; item 2
+// writes its two slots 2*(tid%8), +1.  A 304-byte row stride keeps the 16-byte
 // writes (16 lanes = 2 keys x 8 chunks) on disjoint bank quads.
-template <bool CACHED, bool TAYLOR>
-constexpr int kItemsK = CACHED && TAYLOR ? 3 : 2;
+constexpr int kItemsK = 3;
 
 template <bool CACHED, bool TAYLOR, int KBITS>
 __device__ inline void unpack_k_item(int p, const Ctx &c, int tid, const Fetch &f, uint16_t *Kb) {
@@ -237,11 +305,15 @@ __device__ inline void unpack_k_item(int p, const Ctx &c, int tid, const Fetch &
       }
     }
     *reinterpret_cast<uint4 *>(Kb + kk * KS + d0 + 8 * p) = make_uint4(w[0], w[1], w[2], w[3]);
-  } else if (CACHED && TAYLOR) {
-    const float sq = (j >> 1) < c.ng ? f.gstep * f.gstep : 0.f;
-    const float hsq = lo_f(pack2(sq, 0.f));
-    *reinterpret_cast<uint32_t *>(Kb + kk * KS + KEXT + 2 * j) =
-        (j & 1) ? pack2(-hsq, 0.f) : pack2(-hsq, -(sq - hsq));
+  } else {  // slots 2j, 2j+1: correction terms of group j/2, and 1.0 in the max slots 3 and 7
+    const float one = j == 1 || j == 3 ? 1.0f : 0.f;
+    uint32_t w = pack2(0.f, one);
+    if (CACHED && TAYLOR) {
+      const float sq = (j >> 1) < c.ng ? f.gstep * f.gstep : 0.f;
+      const float hsq = lo_f(pack2(sq, 0.f));
+      w = (j & 1) ? pack2(-hsq, one) : pack2(-hsq, -(sq - hsq));
+    }
+    *reinterpret_cast<uint32_t *>(Kb + kk * KS + KEXT + 2 * j) = w;
   }
 }
 
@@ -304,40 +376,19 @@ __device__ inline void unpack_v_item(int p, int tid, const Fetch &f, uint16_t *V
   }
 }
 
-// Tile max of the score block in 4 items (8 scores each).
-__device__ inline void max_item(int r, const f32x16 (&acc)[2], float &mt) {
-  const int kb = r >> 1, i0 = 8 * (r & 1);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) mt = fmaxf(mt, acc[kb][i0 + i]);
-  pin(mt);
-}
-
-// Lazy rescale: the running max only moves when the tile max exceeds it by
-// more than kLazy, so p <= 2^kLazy.
-__device__ inline void max_update(float mt, Soft &st) {
-  mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * st.alpha;
-  const bool grow = mt > st.m + kLazy;
-  if (__any(grow)) {
-    const float m_new = grow ? mt : st.m;
-    const float sc = exp2f(st.m - m_new);
-    st.l *= sc;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) st.o[db] *= sc;
-    st.m = m_new;
-  }
-}
-
-// p = exp2(s * alpha - m) for scores 2k, 2k+1 of the block (k = 0..15); every
-// fourth item packs 8 of them into a bf16 P operand and adds the rounded p to
-// the row sum.  MASK zeroes keys at or past `count`.
-template <bool MASK>
+// p = exp2(s) for scores 2k, 2k+1 of the block (k = 0..15): the running max
+// is already subtracted by the score MFMAs (SHIFT subtracts a further
+// `shift`, in the rare redo of fix_growth); every fourth item packs 8 of
+// them into a bf16 P operand and adds the rounded p to the row sum.  MASK
+// zeroes keys at or past `count`.
+template <bool MASK, bool SHIFT = false>
 __device__ inline void exp_item(int k, const f32x16 (&acc)[2], Soft &st, int count, int h, float (&e)[8],
-                                bf16x8 (&pk)[4]) {
+                                bf16x8 (&pk)[4], float shift = 0.f) {
   const int kb = k >> 3;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int i = 2 * (k & 7) + u;
-    float x = __builtin_amdgcn_exp2f(fmaf(acc[kb][i], st.alpha, -st.m));
+    float x = __builtin_amdgcn_exp2f(SHIFT ? acc[kb][i] - shift : acc[kb][i]);
     if (MASK && kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3) >= count) x = 0.f;
     e[(2 * k + u) & 7] = x;
   }
@@ -352,38 +403,64 @@ __device__ inline void exp_item(int k, const f32x16 (&acc)[2], Soft &st, int cou
   }
 }
 
-// Guard of the running max after the exponentials of a tile: if some row's
-// sum passed kGrowth (or overflowed), raise that row's max to the tile max,
-// rescale O and the sum taken before the tile (l0), and redo the tile's
-// probabilities.  Rare: it needs scores 40 binary orders above the first
-// tile's max.
-constexpr float kGrowth = 1099511627776.0f;  // 2^40
+// The running max carried by the query operand: -m split into bf16 (hi, lo)
+// in slots 3 and 7 (lanes of half 0); returns the m those two carry.
+__device__ inline float set_max_slots(QState &qs, float m, int h) {
+  const float mh = lo_f(pack2(m, 0.f));
+  const float ml = lo_f(pack2(m - mh, 0.f));
+  if (h == 0) {
+    uint4 w = __builtin_bit_cast(uint4, qs.qext);
+    w.y = (w.y & 0xffffu) | (pack2(0.f, -mh) & 0xffff0000u);
+    w.w = (w.w & 0xffffu) | (pack2(0.f, -ml) & 0xffff0000u);
+    qs.qext = __builtin_bit_cast(bf16x8, w);
+  }
+  return mh + ml;
+}
 
-template <bool MASK>
-__device__ inline void fix_growth(const f32x16 (&s)[2], Soft &st, float l0, int count, int h, bf16x8 (&pk)[4]) {
-  if (!__any(!(st.l < kGrowth))) return;
+// Guard of the running max after the exponentials of a tile (sum l0 before
+// it): if some row's sum left [kShrink, kGrowth] (or is not finite), move
+// that row's m by the tile max (up or down), rescale O and l0, redo the
+// tile's probabilities, and shift the already computed next scores sn by the
+// same amount.  Rare: it takes scores 40 binary orders above m, or all of a
+// row's scores so far 60 below it (the first tile after m = 0 can be one).
+constexpr float kGrowth = 1099511627776.0f;        // 2^40
+constexpr float kShrink = 8.673617379884035e-19f;  // 2^-60
+
+template <bool MASK, bool QK>
+__device__ inline void fix_growth(const f32x16 (&s)[2], f32x16 (&sn)[2], QState &qs, Soft &st, float l0, int count,
+                                  int h, bf16x8 (&pk)[4]) {
+  const float lt = st.l + __shfl_xor(st.l, 32, 64);
+  const bool need = !(lt < kGrowth && lt > kShrink);
+  if (!__any(need)) return;
   float mt = -INFINITY;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[kb][i]);
-  mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * st.alpha;
-  const float m_new = fmaxf(st.m, mt);
-  const float sc = exp2f(st.m - m_new);
+    for (int i = 0; i < 16; ++i)
+      if (!MASK || kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3) < count) mt = fmaxf(mt, s[kb][i]);
+  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+  const float m_new = set_max_slots(qs, need && mt > -INFINITY ? st.m + mt : st.m, h);
+  const float shift = m_new - st.m;
+  const float sc = exp2f(-shift);
   st.l = l0 * sc;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) st.o[db] *= sc;
   st.m = m_new;
   float e[8];
 #pragma unroll
-  for (int k = 0; k < 16; ++k) exp_item<MASK>(k, s, st, count, h, e, pk);
+  for (int k = 0; k < 16; ++k) exp_item<MASK, true>(k, s, st, count, h, e, pk, shift);
+  if (QK) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sn[kb][i] -= shift;
+  }
 }
 
 // ---- MFMA sequences ------------------------------------------------------------
 // S^T of the wave's block: MFMA j < 16 uses the K fragment of k-step j / 2 of
 // key block j % 2; j = 16, 17 are the correction steps of the two blocks.
-template <bool CACHED, bool TAYLOR>
-constexpr int kNqk = CACHED && TAYLOR ? 18 : 16;
+constexpr int kNqk = 18;
 
 __device__ constexpr int qk_off(int j) { return (j & 1) * 32 * KS + (j < 16 ? 16 * (j >> 1) : KEXT); }
 
@@ -397,26 +474,26 @@ __device__ inline uint4 lds16(const uint16_t *p) { return *reinterpret_cast<cons
 #define KVQ_FENCE() __builtin_amdgcn_sched_barrier(0)
 
 // One step of the cross-tile pipeline of a segment:
-//   QK:   S_t of tile t (LDS K buffer Kl); on the segment's first tile
-//         (QK without PREV) also its max and the lazy rescale;
+//   QK:   S_t - m of tile t (LDS K buffer Kl);
 //   PREV: P_{t-1} from the saved scores S_{t-1} and O += V_{t-1} P_{t-1}
 //         (LDS V buffer Vp), MASK for a ragged last tile of count keys;
 //   NEXT: dequantise tile t+1 from f into K buffer Kn / V buffer Vn, and
 //         fetch tile t+2 (rows clamp into the segment).
 template <bool CACHED, bool TAYLOR, int KBITS, int VBITS, bool QK, bool PREV, bool NEXT, bool MASK>
-__device__ inline void tile_step(const Ctx &c, const QState &qs, Soft &st, Fetch &f, const f32x16 (&s)[2],
+__device__ inline void tile_step(const Ctx &c, QState &qs, Soft &st, Fetch &f, const f32x16 (&s)[2],
                                  f32x16 (&sn)[2], const uint16_t *Kl, uint16_t *Kn, const uint16_t *Vp, uint16_t *Vn,
                                  int k0_next2, int count, int tid) {
   const int lane = tid & 63, qc = lane & 31, h = lane >> 5;
   const uint16_t *Kb = Kl + qc * KS + 8 * h;
   const uint16_t *Vb = Vp + qc * VS + 8 * (h ^ (qc >> 4));
-  constexpr int NQK = kNqk<CACHED, TAYLOR>;
-  constexpr int NK = kItemsK<CACHED, TAYLOR>;
+  constexpr int NQK = kNqk;
+  constexpr int NK = kItemsK;
   uint4 buf[4];
   float ev[8];
   bf16x8 pk[4];
 
-  // 1. S_t (fp16 keys, bf16 correction step), with the exponentials of t-1
+  // 1. S_t - m (fp16 keys, bf16 correction and max step), with the
+  //    exponentials of t-1
   const float l0 = st.l;
   if (QK) {
     sn[0] = f32x16{};
@@ -438,11 +515,10 @@ __device__ inline void tile_step(const Ctx &c, const QState &qs, Soft &st, Fetch
     if (PREV && j < 16) exp_item<MASK>(j, s, st, count, h, ev, pk);
     KVQ_FENCE();
   }
-  if (PREV) fix_growth<MASK>(s, st, l0, count, h, pk);
+  if (PREV) fix_growth<MASK, QK>(s, sn, qs, st, l0, count, h, pk);
 
-  // 2. O += V_{t-1}^T P_{t-1}^T, with tile t+1 into LDS, the max of S_t and
-  //    the fetch of tile t+2
-  float mt = -INFINITY;
+  // 2. O += V_{t-1}^T P_{t-1}^T, with tile t+1 into LDS and the fetch of
+  //    tile t+2
   {
     VWork u;
     if (PREV) {
@@ -462,11 +538,9 @@ __device__ inline void tile_step(const Ctx &c, const QState &qs, Soft &st, Fetch
         else if (j == 9) fetch_k<CACHED, KBITS>(c, k0_next2, tid, f);
         else if (j == 10 || j == 11) fetch_v<CACHED, VBITS>(c, k0_next2, tid, j - 10, f);
       }
-      if (QK && !PREV && j >= 12) max_item(j - 12, sn, mt);
       KVQ_FENCE();
     }
   }
-  if (QK && !PREV) max_update(mt, st);
 }
 
 #undef KVQ_FENCE
@@ -474,7 +548,7 @@ __device__ inline void tile_step(const Ctx &c, const QState &qs, Soft &st, Fetch
 // One segment (cached or current keys) of the key range; ends with a barrier
 // so the next segment may reuse every LDS buffer.
 template <bool CACHED, bool TAYLOR, int KBITS, int VBITS>
-__device__ inline void segment(const Ctx &c, const QState &qs, Soft &st, uint16_t *Kl, uint16_t *Vl, int tid) {
+__device__ inline void segment(const Ctx &c, QState &qs, Soft &st, uint16_t *Kl, uint16_t *Vl, int tid) {
   const int nt = c.end > c.beg ? (c.end - c.beg + BN - 1) / BN : 0;
   if (nt == 0) return;
   const int tail = c.end - c.beg - (nt - 1) * BN;  // keys in the last tile
@@ -485,7 +559,7 @@ __device__ inline void segment(const Ctx &c, const QState &qs, Soft &st, uint16_
     fetch_v<CACHED, VBITS>(c, c.beg, tid, 0, f);
     fetch_v<CACHED, VBITS>(c, c.beg, tid, 1, f);
 #pragma unroll
-    for (int p = 0; p < kItemsK<CACHED, TAYLOR>; ++p) unpack_k_item<CACHED, TAYLOR, KBITS>(p, c, tid, f, Kl);
+    for (int p = 0; p < kItemsK; ++p) unpack_k_item<CACHED, TAYLOR, KBITS>(p, c, tid, f, Kl);
 #pragma unroll
     for (int p = 0; p < kItemsV; ++p) unpack_v_item<CACHED, VBITS>(p, tid, f, Vl, u);
     fetch_k<CACHED, KBITS>(c, c.beg + BN, tid, f);
@@ -573,11 +647,23 @@ __global__ __launch_bounds__(THREADS, 1) void attn_fast_kernel(AttnLaunch p, int
   const int64_t rb = rem - bkv * row_blocks;
   const int64_t b = bkv / p.Hkv, hk = bkv - b * p.Hkv;
   const int64_t gq = p.Hq / p.Hkv;
-  // key exponent of the KV head from the pre-pass's partial bounds
-  float kb = lane < KCHUNKS ? kpart[bkv * KCHUNKS + lane] : 0.f;
+  // exponent ek of the KV head from the pre-pass's partial bounds: keys
+  // k tau log2(e) 2^-ek and queries q 2^ek near the same magnitude, keys
+  // always below 2^15
+  float kb = lane < KCHUNKS ? kpart[2 * bkv * KCHUNKS + lane] : 0.f;
+  float qb = lane < KCHUNKS ? kpart[(2 * bkv + 1) * KCHUNKS + lane] : 0.f;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) kb = fmaxf(kb, __shfl_xor(kb, o, 64));
-  const int ek = scale_exponent(kb);
+  for (int o = 32; o >= 1; o >>= 1) {
+    kb = fmaxf(kb, __shfl_xor(kb, o, 64));
+    qb = fmaxf(qb, __shfl_xor(qb, o, 64));
+  }
+  const float kt = kb * (p.tau * kLog2e);
+  int ek = 0;
+  if (kt > 0.f) {
+    const int lk = ilogbf(kt);
+    if (qb > 0.f) ek = (lk - ilogbf(qb)) >> 1;
+    if (lk - ek > kFp16Exp) ek = lk - kFp16Exp;
+  }
 
   // ---- the lane's query row: fp16 operands, scale, correction operands ----
   QState qs;
@@ -586,16 +672,16 @@ __global__ __launch_bounds__(THREADS, 1) void attn_fast_kernel(AttnLaunch p, int
   const int64_t rr = row_ok ? r : rows_per_kvhead - 1;
   const int64_t qrow = (b * p.Hq + hk * gq + rr / p.Nq) * p.Nq + rr % p.Nq;
   Soft st;
-  load_query<TAYLOR>(p.q + qrow * D, h, group_shift, p.tau, ek, qs.q, qs.qext, st.alpha);
+  load_query_folded<TAYLOR>(p.q + qrow * D, h, group_shift, p.tau, ek, qs);
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) st.o[db] = f32x16{};
-  st.m = -INFINITY;
+  st.m = 0.f;
   st.l = 0.f;
 
   Ctx c{};
   c.ng = ng;
   c.group_shift = group_shift;
-  c.kscale = ldexpf(1.0f, -ek);
+  c.kscale = ldexpf(p.tau * kLog2e, -ek);
   c.kmask = opaque_u32(kCodeMask<KBITS>);
   if (p.Nc > 0) {
     const int64_t hrow = bkv * p.cap;  // first cache row of this head
@@ -684,7 +770,7 @@ void launch_key_scale(const AttnLaunch &p, hipStream_t stream, float *part) {
 
 size_t fast_path_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int splits) {
   const size_t part = splits > 1 ? short_path_workspace_bytes(B, Hq, Nq, D, splits) : 0;
-  return part + (static_cast<size_t>(B * Hkv) * KCHUNKS * sizeof(float) + 255) / 256 * 256;
+  return part + (static_cast<size_t>(B * Hkv) * 2 * KCHUNKS * sizeof(float) + 255) / 256 * 256;
 }
 
 // Split count of the throughput kernel: rounds of one-per-CU workgroups

@@ -48,14 +48,15 @@ hipError_t launch_attention_long(const AttnLaunch &p, hipStream_t stream);
 hipError_t launch_attention_short(const AttnLaunch &p, hipStream_t stream);
 // Throughput kernel (attention_fast.hip): head dim 128, correction off or
 // Taylor.  Its workspace holds the split partials (when splits > 1, laid out
-// as on the short path), then 32 fp32 partial key bounds per (b, KV head).
+// as on the short path), then 32 fp32 partial key bounds and 32 partial
+// query bounds per (b, KV head).
 bool fast_path_supported(const AttnLaunch &p);
 size_t fast_path_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int splits);
 int fast_path_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nc, int64_t Ncur, int cu_count);
 hipError_t launch_attention_fast(const AttnLaunch &p, hipStream_t stream);
 // Pre-pass of the throughput kernel: per (b, KV head), 32 partial bounds of
-// |key| (dequantised cache and current chunk), from which the kernel takes
-// the exponent ek with the largest |key| times 2^-ek below 2^15.
+// |key| (dequantised cache and current chunk) and of |query|, from which the
+// kernel takes the exponent that balances its fp16 key and query operands.
 void launch_key_scale(const AttnLaunch &p, hipStream_t stream, float *part);
 
 // Short path: cached-token split count chosen for a problem and the

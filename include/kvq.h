@@ -141,8 +141,9 @@ typedef struct {
 /* Bytes of device workspace the call needs: on the short path the
  * per-split partial results (splits x B*Hq*Nq rows of d+4 floats); on the
  * long path with d = 128 and correction off or Taylor, the same partials
- * when it splits the key range (more than one split), then 32 fp32 partial
- * key bounds per (b, KV head) rounded up to 256 bytes; otherwise 0.  The
+ * when it splits the key range (more than one split), then 64 fp32 partial
+ * key and query bounds per (b, KV head) rounded up to 256 bytes; otherwise
+ * 0.  The
  * contents need no initialisation and are meaningless after the call.
  * Returns 0 for invalid arguments as well; kv_attention_corrected reports
  * those. */

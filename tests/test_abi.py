@@ -159,15 +159,15 @@ def test_short_path_needs_workspace(kvq):
 
 
 def test_long_path_workspace(kvq):
-    """The head-dim-128 long path keeps 32 fp32 partial key bounds per
-    (batch, KV head), rounded up to 256 bytes; the general kernel (head dim
-    64, or the exact correction) needs none."""
+    """The head-dim-128 long path keeps 32 fp32 partial key bounds and 32
+    partial query bounds per (batch, KV head), rounded up to 256 bytes; the
+    general kernel (head dim 64, or the exact correction) needs none."""
     size = lambda **kw: kvq.lib.kv_attention_workspace_size(C.byref(_args(kvq, path=1, **kw)))
-    assert size() == 256                            # 2 heads x 32 x 4 B
-    assert size(B=3, Hq=80, Hkv=40) == 15360        # 120 heads x 128 B
-    assert size(B=1, Hq=3, Hkv=3) == 512            # 384 B -> 512
+    assert size() == 512                            # 2 heads x 64 x 4 B
+    assert size(B=3, Hq=80, Hkv=40) == 30720        # 120 heads x 256 B
+    assert size(B=1, Hq=3, Hkv=3) == 768            # 3 heads x 256 B
     # forced key-range splits (2 tiles here): partials of 2 splits first
-    assert size(splits=2) == 2 * 1 * 4 * 8 * (128 + 4) * 4 + 256
+    assert size(splits=2) == 2 * 1 * 4 * 8 * (128 + 4) * 4 + 512
     assert size(splits=5) == size(splits=2)         # clamped to the 2 tiles
     assert size(corr=2) == 0
     assert size(d=64) == 0
