@@ -69,11 +69,11 @@ MAX_ABS = 2e-2
 MEAN_ABS = 1e-3
 
 
-def check(got: np.ndarray, ref: np.ndarray, label: str = ""):
+def check(got: np.ndarray, ref: np.ndarray, label: str = "", max_abs: float = MAX_ABS, mean_abs: float = MEAN_ABS):
     mx, mean_raw = errors(got, ref)
     _, mean = errors(got, bf16_round(ref))
     print(f"    {label}max_abs={mx:.3e} mean_abs(bf16 ref)={mean:.3e} mean_abs(raw)={mean_raw:.3e} "
           f"|ref|max={np.abs(ref).max():.3f}", flush=True)
     assert np.all(np.isfinite(got))
-    assert mx <= MAX_ABS and mean <= MEAN_ABS, (mx, mean)
+    assert mx <= max_abs and mean <= mean_abs, (mx, mean)
     return mx, mean

@@ -110,3 +110,50 @@ def test_deterministic(orc):
         a = _gpu.run_attention(w, data, kc, vc, path=path)
         b = _gpu.run_attention(w, data, kc, vc, path=path)
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def _scaled(data, sq, sk, sv):
+    """The workload's inputs with q, keys and values multiplied by powers of
+    two (exact in bf16)."""
+    f = {"q": sq, "kc": sk, "k": sk, "vc": sv, "v": sv}
+    out = {}
+    for name, x in data.items():
+        x32 = (x.astype(np.uint32) << 16).view(np.float32) if x.dtype == np.uint16 else x
+        out[name] = W.bf16_bits(x32 * np.float32(f[name]))
+    return out
+
+
+SCALES = {
+    # tiny operands: logits x2^-14 (near-uniform attention), values x2^-10
+    "small": (2.0 ** -6, 2.0 ** -8, 2.0 ** -10),
+    # operands spread over ~20 binary orders with the logits unchanged: the
+    # key/query exponent balance and the value exponents at range extremes
+    "wide": (2.0 ** -6, 2.0 ** 6, 2.0 ** 10),
+    # logits x4: sharply peaked rows
+    "peaked": (2.0, 2.0, 1.0),
+}
+
+
+@pytest.mark.parametrize("scales", sorted(SCALES))
+@pytest.mark.parametrize("path", ["long", "short"])
+def test_scaled_inputs(orc, scales, path):
+    """Inputs far from unit size.  Outputs are linear in the values, so both
+    sides are divided by the value factor before the comparison.  The bar is
+    the usual one, except that for "peaked" it is multiplied by the logit
+    factor sq*sk: each key enters the scores rounded once to fp16 (relative
+    2^-12), so score errors, and through the softmax the output errors, grow
+    in proportion to the logits (a bf16 key would give 8x more)."""
+    import _gpu
+    sq, sk, sv = SCALES[scales]
+    widen = sq * sk if scales == "peaked" else 1.0
+    for case in ("gqa", "longvideo"):
+        w = CASES[case]
+        data = _scaled(W.generate(w), sq, sk, sv)
+        for corr in ("off", "taylor"):
+            print(f"[scaled] {scales} q x{sq} k x{sk} v x{sv} {case} corr={corr} path={path}", flush=True)
+            kc = _gpu.build_cache(w, data["kc"], w.kbits)
+            vc = _gpu.build_cache(w, data["vc"], w.vbits)
+            out = _gpu.run_attention(w, data, kc, vc, corr=corr, path=path)
+            got = _gpu.out_rows(out)
+            ref = oracle_problem(orc, w, corr, data=data).attention()
+            _gpu.check(got / sv, ref / sv, max_abs=_gpu.MAX_ABS * widen, mean_abs=_gpu.MEAN_ABS * widen)
