@@ -166,7 +166,7 @@ class _Attn(C.Structure):
         ("kc_codes", C.c_void_p), ("kc_step", C.c_void_p), ("kc_zero", C.c_void_p),
         ("vc_codes", C.c_void_p), ("vc_step", C.c_void_p), ("vc_zero", C.c_void_p),
         ("kbits", C.c_int32), ("vbits", C.c_int32), ("cap", C.c_int64),
-        ("scale", C.c_double), ("corr", C.c_int32),
+        ("scale", C.c_double), ("corr", C.c_int32), ("causal", C.c_int32),
     ]
 
 
@@ -178,7 +178,7 @@ class Problem:
     """
 
     def __init__(self, q, k_cur, v_cur, kcache, vcache, nc: int, kbits: int, vbits: int,
-                 group: int, scale: float = 0.0, corr: str = "taylor"):
+                 group: int, scale: float = 0.0, corr: str = "taylor", causal: bool = False):
         self.q = np.ascontiguousarray(q, dtype=np.uint16)
         B, Hq, Nq, d = self.q.shape
         self.k_cur = np.ascontiguousarray(k_cur, dtype=np.uint16)
@@ -191,7 +191,7 @@ class Problem:
                        _p(self.q).value, _p(self.k_cur).value, _p(self.v_cur).value,
                        _p(self.kc[0]).value, _p(self.kc[1]).value, _p(self.kc[2]).value,
                        _p(self.vc[0]).value, _p(self.vc[1]).value, _p(self.vc[2]).value,
-                       kbits, vbits, cap, float(scale), CORR[corr])
+                       kbits, vbits, cap, float(scale), CORR[corr], 1 if causal else 0)
         self.shape = (B, Hq, Nq, d)
 
     def with_corr(self, corr: str) -> "Problem":

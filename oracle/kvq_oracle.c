@@ -43,7 +43,10 @@
  *  - the exact bias is sum_c log(sinh x_c / x_c), x_c = tau q_c D_{g(c)} / 2,
  *    the log-MGF of independent U(-D/2, D/2) key noise;
  *  - GQA: query head h reads KV head h / (Hq / Hkv);
- *  - no mask: every query sees every cached and current key.
+ *  - by default no mask: every query sees every cached and current key
+ *    (chunk-wise video generation); optionally a causal mask within the
+ *    current chunk aligned to its end (query row j sees current keys
+ *    i <= j + Ncur - Nq and the whole cache), for chunked prefill.
  *
  * Build: gcc -O2 -std=c11 -fopenmp -ffp-contract=off -fPIC -shared
  * (no -ffast-math: the quantizer relies on IEEE fp32 division and rint).
@@ -280,12 +283,15 @@ typedef struct {
   int64_t cap;
   double scale; /* softmax scale tau; <= 0 means 1/sqrt(d) */
   int32_t corr; /* 0 off, 1 Taylor, 2 exact */
+  int32_t causal; /* 0 no mask; 1 end-aligned causal mask on the current chunk */
 } kvo_attn;
 
 static int attn_ok(const kvo_attn *a) {
   if (!a || a->B < 1 || a->Hq < 1 || a->Hkv < 1 || a->Hq % a->Hkv) return 0;
   if (a->Nq < 1 || a->Ncur < 0 || a->Nc < 0 || a->Nc + a->Ncur < 1) return 0;
   if (a->corr < 0 || a->corr > 2 || !a->q) return 0;
+  if (a->causal != 0 && a->causal != 1) return 0;
+  if (a->causal && a->Nc == 0 && a->Nq > a->Ncur) return 0; /* a row would see no key */
   if (a->Ncur > 0 && (!a->k_cur || !a->v_cur)) return 0;
   if (a->Nc > 0) {
     if (!a->kc_codes || !a->kc_step || !a->kc_zero || !a->vc_codes || !a->vc_step || !a->vc_zero) return 0;
@@ -312,6 +318,15 @@ static void row_setup(const kvo_attn *a, int64_t row, rowctx *rc, double *qbuf) 
   rc->q = qbuf;
   const uint16_t *qp = a->q + row * a->d;
   for (int32_t c = 0; c < a->d; ++c) rc->q[c] = (double)bf16_bits_to_f32(qp[c]);
+}
+
+/* Whether key t is visible to flat query row `row` (query j = row mod Nq):
+ * every cached key; current key i = t - Nc unless the causal mask hides it
+ * (i > j + Ncur - Nq). */
+static int visible(const kvo_attn *a, int64_t row, int64_t t) {
+  if (t < a->Nc || !a->causal) return 1;
+  const int64_t j = row % a->Nq;
+  return t - a->Nc <= j + a->Ncur - a->Nq;
 }
 
 /* Key index t in [0, Nc + Ncur): t < Nc is cached key t, else current key
@@ -369,7 +384,7 @@ int kvo_logits(const kvo_attn *a, int64_t row, double *logits) {
   row_setup(a, row, &rc, buf);
   for (int64_t t = 0; t < a->Nc + a->Ncur; ++t) {
     key_value(&rc, t, buf + d, buf + 2 * d);
-    logits[t] = logit_of(&rc, t, buf + d);
+    logits[t] = visible(a, row, t) ? logit_of(&rc, t, buf + d) : -INFINITY;
   }
   free(buf);
   return KVO_OK;
@@ -387,12 +402,13 @@ static int attention_row(const kvo_attn *a, int64_t row, double *out, double *wo
   double m = -INFINITY;
   for (int64_t t = 0; t < n; ++t) {
     key_value(&rc, t, k, v);
-    s[t] = logit_of(&rc, t, k);
+    s[t] = visible(a, row, t) ? logit_of(&rc, t, k) : -INFINITY;
     if (s[t] > m) m = s[t];
   }
   double l = 0.0;
   for (int32_t c = 0; c < d; ++c) out[c] = 0.0;
   for (int64_t t = 0; t < n; ++t) {
+    if (s[t] == -INFINITY) continue; /* masked */
     double p = exp(s[t] - m);
     l += p;
     key_value(&rc, t, k, v);
@@ -476,7 +492,7 @@ int kvo_attention_online(const kvo_attn *a, int64_t row, int64_t tile, const int
       for (int64_t p = p0; p < p1; ++p) {
         int64_t t = order_key(a, p, cur_first);
         key_value(&rc, t, k, v);
-        s[p - p0] = logit_of(&rc, t, k);
+        s[p - p0] = visible(a, row, t) ? logit_of(&rc, t, k) : -INFINITY;
         if (s[p - p0] > mt) mt = s[p - p0];
       }
       double mnew = mt > m ? mt : m;
@@ -485,6 +501,7 @@ int kvo_attention_online(const kvo_attn *a, int64_t row, int64_t tile, const int
       for (int32_t c = 0; c < d; ++c) po[c] *= alpha;
       for (int64_t p = p0; p < p1; ++p) {
         int64_t t = order_key(a, p, cur_first);
+        if (s[p - p0] == -INFINITY) continue; /* masked */
         key_value(&rc, t, k, v);
         double w = exp(s[p - p0] - mnew);
         l += w;
@@ -513,4 +530,4 @@ int kvo_attention_online(const kvo_attn *a, int64_t row, int64_t tile, const int
   return KVO_OK;
 }
 
-int kvo_version(void) { return 1; }
+int kvo_version(void) { return 2; }

@@ -18,8 +18,8 @@ def oracle_caches(orc, w, data):
     return kc, vc
 
 
-def oracle_problem(orc, w, corr="taylor", data=None, scale=0.0, caches=None):
+def oracle_problem(orc, w, corr="taylor", data=None, scale=0.0, caches=None, causal=False):
     data = W.generate(w) if data is None else data
     kc, vc = oracle_caches(orc, w, data) if caches is None else caches
     return orc.Problem(as_bf16(data["q"]), as_bf16(data["k"]), as_bf16(data["v"]), kc, vc,
-                       w.Nc, w.kbits, w.vbits, w.group, scale=scale, corr=corr)
+                       w.Nc, w.kbits, w.vbits, w.group, scale=scale, corr=corr, causal=causal)

@@ -53,6 +53,10 @@ MUTANTS = [
      [("test_oracle_attention", "test_matches_library_sdpa", {"corr": "off", "wi": 0})]),
     ("online_no_rescale", "      l *= alpha;\n", "",
      [("test_oracle_attention", "test_online_matches_brute_force", {"corr": "off"})]),
+    ("causal_top_left", "return t - a->Nc <= j + a->Ncur - a->Nq;", "return t - a->Nc <= j;",
+     [("test_oracle_causal", "test_matches_library_lower_right", {"corr": "off", "wi": 0})]),
+    ("causal_off_by_one", "return t - a->Nc <= j + a->Ncur - a->Nq;", "return t - a->Nc < j + a->Ncur - a->Nq;",
+     [("test_oracle_causal", "test_matches_library_lower_right", {"corr": "off", "wi": 1})]),
     ("value_not_dequantized_zero",
      "v[c] = (double)a->vc_zero[base * ng + g] + ", "v[c] = ",
      [("test_oracle_attention", "test_matches_library_sdpa", {"corr": "off", "wi": 2})]),
