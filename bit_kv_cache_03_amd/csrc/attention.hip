@@ -198,7 +198,18 @@ __global__ __launch_bounds__(kThreads, EXACT ? 1 : 2) void attn_tile_kernel(Attn
     kend = kbeg + split_keys < kend ? kbeg + split_keys : kend;
   }
   const int64_t c_beg = kbeg < p.Nc ? kbeg : p.Nc, c_end = kend < p.Nc ? kend : p.Nc;
-  const int64_t u_beg = (kbeg > p.Nc ? kbeg : p.Nc) - p.Nc, u_end = (kend > p.Nc ? kend : p.Nc) - p.Nc;
+  const int64_t u_beg = (kbeg > p.Nc ? kbeg : p.Nc) - p.Nc;
+  int64_t u_end = (kend > p.Nc ? kend : p.Nc) - p.Nc;
+  // causal mask: current keys below climit are visible to this lane's row;
+  // the workgroup stops at the largest limit of its rows
+  const int64_t climit = p.causal ? qj + p.Ncur - p.Nq + 1 : p.Ncur;
+  if (p.causal) {
+    const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kBM;
+    const int64_t r1 = (r0 + kBM < rows_per_kvhead ? r0 + kBM : rows_per_kvhead) - 1;
+    const int64_t jmax = r0 / p.Nq == r1 / p.Nq ? r1 % p.Nq : p.Nq - 1;
+    const int64_t wlim = jmax + p.Ncur - p.Nq + 1;
+    if (u_end > wlim) u_end = wlim;
+  }
   const int64_t nt_c = c_end > c_beg ? (c_end - c_beg + kBN - 1) / kBN : 0;
   const int64_t nt_u = u_end > u_beg ? (u_end - u_beg + kBN - 1) / kBN : 0;
   const int64_t kvbase_c = bkv * p.cap;             // first cache row of this (b, hk)
@@ -211,6 +222,9 @@ __global__ __launch_bounds__(kThreads, EXACT ? 1 : 2) void attn_tile_kernel(Attn
     const int64_t k0 = cached ? c_beg + t * kBN : u_beg + (t - nt_c) * kBN;
     const int64_t kn = cached ? c_end : u_end;
     const int count = static_cast<int>(kn - k0 < kBN ? kn - k0 : kBN);
+    // keys of this lane's row in the tile (fewer under the causal mask)
+    const int64_t vis = cached ? count : climit - k0;
+    const int rcount = vis < count ? static_cast<int>(vis) : count;
 
     __syncthreads();  // previous tile fully consumed
     // ---------------- K tile -> LDS (row-major, bf16) ----------------
@@ -393,12 +407,14 @@ __global__ __launch_bounds__(kThreads, EXACT ? 1 : 2) void attn_tile_kernel(Attn
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-        if (key >= count) z[kb][i] = -INFINITY;
+        if (key >= rcount) z[kb][i] = -INFINITY;
         mt = fmaxf(mt, z[kb][i]);
       }
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
     const float m_new = fmaxf(m_run, mt);
-    const float sc = exp2f(m_run - m_new);
+    // a row with no visible key yet keeps m = -inf; its terms are all zero
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float sc = exp2f(m_run - m_use);
     m_run = m_new;
     l_run *= sc;
     if (__any(sc != 1.0f)) {
@@ -411,7 +427,7 @@ __global__ __launch_bounds__(kThreads, EXACT ? 1 : 2) void attn_tile_kernel(Attn
       float e[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        e[i] = exp2f(z[kb][i] - m_new);
+        e[i] = exp2f(z[kb][i] - m_use);
         l_run += e[i];
       }
 #pragma unroll

@@ -211,6 +211,7 @@ struct Ctx {
   const uint16_t *k_cur, *v_cur;
   int ng, group_shift;
   int beg, end;     // key range of the segment
+  int climit;       // causal mask: current keys below climit are visible to the lane's row
   float kscale;     // tau log2(e) 2^-ek
   uint32_t kmask;   // code mask of magic8, in a vector register
 };
@@ -423,6 +424,8 @@ __device__ inline float set_max_slots(QState &qs, float m, int h) {
 // tile's probabilities, and shift the already computed next scores sn by the
 // same amount.  Rare: it takes scores 40 binary orders above m, or all of a
 // row's scores so far 60 below it (the first tile after m = 0 can be one).
+// A row with an empty sum and no visible key in the tile (causal mask) is
+// left alone.
 constexpr float kGrowth = 1099511627776.0f;        // 2^40
 constexpr float kShrink = 8.673617379884035e-19f;  // 2^-60
 
@@ -430,7 +433,7 @@ template <bool MASK, bool QK>
 __device__ inline void fix_growth(const f32x16 (&s)[2], f32x16 (&sn)[2], QState &qs, Soft &st, float l0, int count,
                                   int h, bf16x8 (&pk)[4]) {
   const float lt = st.l + __shfl_xor(st.l, 32, 64);
-  const bool need = !(lt < kGrowth && lt > kShrink);
+  const bool need = !(lt < kGrowth && (lt > kShrink || (MASK && lt == 0.f && count <= 0)));
   if (!__any(need)) return;
   float mt = -INFINITY;
 #pragma unroll
@@ -546,12 +549,15 @@ __device__ inline void tile_step(const Ctx &c, QState &qs, Soft &st, Fetch &f, c
 #undef KVQ_FENCE
 
 // One segment (cached or current keys) of the key range; ends with a barrier
-// so the next segment may reuse every LDS buffer.
-template <bool CACHED, bool TAYLOR, int KBITS, int VBITS>
+// so the next segment may reuse every LDS buffer.  CAUSAL (current keys
+// only) masks every tile with the lane's own count of visible keys.
+template <bool CACHED, bool TAYLOR, int KBITS, int VBITS, bool CAUSAL = false>
 __device__ inline void segment(const Ctx &c, QState &qs, Soft &st, uint16_t *Kl, uint16_t *Vl, int tid) {
   const int nt = c.end > c.beg ? (c.end - c.beg + BN - 1) / BN : 0;
   if (nt == 0) return;
   const int tail = c.end - c.beg - (nt - 1) * BN;  // keys in the last tile
+  // keys of tile t that the lane's row sees (n in the tile)
+  auto cnt = [&](int t, int n) { return CAUSAL ? min(n, c.climit - (c.beg + t * BN)) : n; };
   Fetch f;
   {
     VWork u;
@@ -583,21 +589,21 @@ __device__ inline void segment(const Ctx &c, QState &qs, Soft &st, uint16_t *Kl,
   int t = 1;
   for (; t + 1 < nt - 1; t += 2) {
     const int v1 = vb + 1 < NVBUF ? vb + 1 : 0, v2 = v1 + 1 < NVBUF ? v1 + 1 : 0, v3 = vb;
-    tile_step<CACHED, TAYLOR, KBITS, VBITS, true, true, true, false>(c, qs, st, f, sa, sb, Kl + KBUF, Kl,
-                                                                     Vl + vb * VBUF, Vl + v2 * VBUF,
-                                                                     c.beg + (t + 2) * BN, BN, tid);
+    tile_step<CACHED, TAYLOR, KBITS, VBITS, true, true, true, CAUSAL>(c, qs, st, f, sa, sb, Kl + KBUF, Kl,
+                                                                      Vl + vb * VBUF, Vl + v2 * VBUF,
+                                                                      c.beg + (t + 2) * BN, cnt(t - 1, BN), tid);
     __syncthreads();
-    tile_step<CACHED, TAYLOR, KBITS, VBITS, true, true, true, false>(c, qs, st, f, sb, sa, Kl, Kl + KBUF,
-                                                                     Vl + v1 * VBUF, Vl + v3 * VBUF,
-                                                                     c.beg + (t + 3) * BN, BN, tid);
+    tile_step<CACHED, TAYLOR, KBITS, VBITS, true, true, true, CAUSAL>(c, qs, st, f, sb, sa, Kl, Kl + KBUF,
+                                                                      Vl + v1 * VBUF, Vl + v3 * VBUF,
+                                                                      c.beg + (t + 3) * BN, cnt(t, BN), tid);
     __syncthreads();
     vb = v2;
   }
   if (t < nt - 1) {  // one more steady step (t odd: K buffer 1, S_t into sb)
     const int vn = vb + 2 < NVBUF ? vb + 2 : vb + 2 - NVBUF;
-    tile_step<CACHED, TAYLOR, KBITS, VBITS, true, true, true, false>(c, qs, st, f, sa, sb, Kl + KBUF, Kl,
-                                                                     Vl + vb * VBUF, Vl + vn * VBUF,
-                                                                     c.beg + (t + 2) * BN, BN, tid);
+    tile_step<CACHED, TAYLOR, KBITS, VBITS, true, true, true, CAUSAL>(c, qs, st, f, sa, sb, Kl + KBUF, Kl,
+                                                                      Vl + vb * VBUF, Vl + vn * VBUF,
+                                                                      c.beg + (t + 2) * BN, cnt(t - 1, BN), tid);
     __syncthreads();
     vb = vb + 1 < NVBUF ? vb + 1 : 0;
     ++t;
@@ -606,23 +612,24 @@ __device__ inline void segment(const Ctx &c, QState &qs, Soft &st, uint16_t *Kl,
   }
   // here t = nt - 1 (nt > 1) with S_{t-1} in sa, or nt == 1 with S_0 in sa
   if (nt > 1) {  // S_{nt-1}, P_{nt-2} V_{nt-2}
-    tile_step<CACHED, TAYLOR, KBITS, VBITS, true, true, false, false>(c, qs, st, f, sa, sb, Kl + ((nt - 1) & 1) * KBUF,
-                                                                      Kl, Vl + vb * VBUF, Vl, 0, BN, tid);
+    tile_step<CACHED, TAYLOR, KBITS, VBITS, true, true, false, CAUSAL>(c, qs, st, f, sa, sb,
+                                                                       Kl + ((nt - 1) & 1) * KBUF, Kl, Vl + vb * VBUF,
+                                                                       Vl, 0, cnt(nt - 2, BN), tid);
     vb = vb + 1 < NVBUF ? vb + 1 : 0;
     sa[0] = sb[0];
     sa[1] = sb[1];
   }
   // drain: P_{nt-1} V_{nt-1}
-  if (tail == BN)
+  if (tail == BN && !CAUSAL)
     tile_step<CACHED, TAYLOR, KBITS, VBITS, false, true, false, false>(c, qs, st, f, sa, sb, Kl, Kl,
                                                                        Vl + vb * VBUF, Vl, 0, BN, tid);
   else
     tile_step<CACHED, TAYLOR, KBITS, VBITS, false, true, false, true>(c, qs, st, f, sa, sb, Kl, Kl, Vl + vb * VBUF,
-                                                                      Vl, 0, tail, tid);
+                                                                      Vl, 0, cnt(nt - 1, tail), tid);
   __syncthreads();
 }
 
-template <int KBITS, int VBITS, bool TAYLOR>
+template <int KBITS, int VBITS, bool TAYLOR, bool CAUSAL>
 __global__ __launch_bounds__(THREADS, 1) void attn_fast_kernel(AttnLaunch p, int32_t group_shift,
                                                                 int64_t rows_per_kvhead, int32_t row_blocks,
                                                                 const float *kpart, int32_t nsplit,
@@ -704,7 +711,16 @@ __global__ __launch_bounds__(THREADS, 1) void attn_fast_kernel(AttnLaunch p, int
   }
   c.beg = max(t0 - tc, 0) * BN;
   c.end = min(max(t1 - tc, 0) * BN, static_cast<int>(p.Ncur));
-  segment<false, TAYLOR, KBITS, VBITS>(c, qs, st, Kl, Vl, tid);
+  if (CAUSAL) {
+    // current keys below climit are visible to the lane's row (query j of
+    // Nq, aligned to the chunk's end); the workgroup stops at the largest
+    // limit of its rows
+    c.climit = static_cast<int>(rr % p.Nq + p.Ncur - p.Nq + 1);
+    const int64_t r0 = rb * BM, r1 = min(r0 + BM, rows_per_kvhead) - 1;
+    const int64_t jmax = r0 / p.Nq == r1 / p.Nq ? r1 % p.Nq : p.Nq - 1;
+    c.end = static_cast<int>(min(static_cast<int64_t>(c.end), jmax + p.Ncur - p.Nq + 1));
+  }
+  segment<false, TAYLOR, KBITS, VBITS, CAUSAL>(c, qs, st, Kl, Vl, tid);
 
   const float l_tot = st.l + __shfl_xor(st.l, 32, 64);
   if (!row_ok) return;
@@ -717,7 +733,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_fast_kernel(AttnLaunch p, int
         *reinterpret_cast<float4 *>(w + 32 * db + 8 * g4 + 4 * h) =
             make_float4(st.o[db][4 * g4], st.o[db][4 * g4 + 1], st.o[db][4 * g4 + 2], st.o[db][4 * g4 + 3]);
     if (h == 0) {
-      w[D] = st.m;
+      w[D] = l_tot > 0.f ? st.m : -INFINITY;  // -inf: no key of this split is visible to the row
       w[D + 1] = l_tot;
     }
     return;
@@ -744,12 +760,11 @@ hipError_t launch_bits(const AttnLaunch &p, hipStream_t stream) {
                                            (nsplit > 1 ? short_path_workspace_bytes(p.B, p.Hq, p.Nq, p.d, nsplit) : 0));
   launch_key_scale(p, stream, kpart);
   const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(nsplit) * row_blocks * p.B * p.Hkv));
-  if (p.corr == KV_CORR_TAYLOR)
-    attn_fast_kernel<KB, VB, true><<<grid, dim3(THREADS), 0, stream>>>(p, gshift, rows, row_blocks, kpart, nsplit,
-                                                                       partials);
-  else
-    attn_fast_kernel<KB, VB, false><<<grid, dim3(THREADS), 0, stream>>>(p, gshift, rows, row_blocks, kpart, nsplit,
-                                                                        partials);
+  auto kernel = p.corr == KV_CORR_TAYLOR ? (p.causal ? attn_fast_kernel<KB, VB, true, true>
+                                                     : attn_fast_kernel<KB, VB, true, false>)
+                                         : (p.causal ? attn_fast_kernel<KB, VB, false, true>
+                                                     : attn_fast_kernel<KB, VB, false, false>);
+  kernel<<<grid, dim3(THREADS), 0, stream>>>(p, gshift, rows, row_blocks, kpart, nsplit, partials);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
   return launch_combine(partials, p.out, p.B * p.Hq * p.Nq, nsplit, p.d, stream);

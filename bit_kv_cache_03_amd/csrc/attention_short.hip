@@ -407,8 +407,9 @@ struct Soft {
 // Scores, softmax and value product of one block: K operand registers,
 // the wave's V^T tile, the block's score scale alpha (scores are
 // q.k 2^-(eq+ek)) and value exponent ev.  count < BK marks a ragged block;
-// CORR adds the correction step.
-template <bool CORR>
+// CORR adds the correction step.  CAUSAL: count is the lane's own (possibly
+// <= 0), and a row may have seen no key yet (m = -inf).
+template <bool CORR, bool CAUSAL = false>
 __device__ inline void block_compute(const f16x8 (&k)[8], bf16x8 kext, const uint16_t *Vt, const f16x8 (&q)[8],
                                      bf16x8 qext, int count, float alpha, int ev, int lane, Soft &st) {
   const float fev = static_cast<float>(ev);
@@ -417,7 +418,7 @@ __device__ inline void block_compute(const f16x8 (&k)[8], bf16x8 kext, const uin
 #pragma unroll
   for (int j = 0; j < 8; ++j) s = __builtin_amdgcn_mfma_f32_32x32x16_f16(k[j], q[j], s, 0, 0, 0);
   if (CORR) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kext, qext, s, 0, 0, 0);
-  if (count < BK) {
+  if (CAUSAL || count < BK) {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       if (8 * (i >> 2) + 4 * h + (i & 3) >= count) s[i] = -INFINITY;
@@ -429,7 +430,7 @@ __device__ inline void block_compute(const f16x8 (&k)[8], bf16x8 kext, const uin
   const bool grow = mt > st.m + kLazy;
   if (__any(grow)) {
     const float m_new = grow ? mt : st.m;
-    const float sc = exp2f(st.m - m_new);
+    const float sc = CAUSAL && !grow ? 1.f : exp2f(st.m - m_new);
     st.l *= sc;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) st.o[db] *= sc;
@@ -442,7 +443,10 @@ __device__ inline void block_compute(const f16x8 (&k)[8], bf16x8 kext, const uin
   for (int hf = 0; hf < 2; ++hf) {
     float e[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) e[i] = __builtin_amdgcn_exp2f(fmaf(s[8 * hf + i], alpha, shift));
+    for (int i = 0; i < 8; ++i) {
+      e[i] = __builtin_amdgcn_exp2f(fmaf(s[8 * hf + i], alpha, shift));
+      if (CAUSAL && s[8 * hf + i] == -INFINITY) e[i] = 0.f;  // shift is +inf while m = -inf
+    }
     pk[hf] = __builtin_bit_cast(f16x8, make_uint4(pack2h(e[0], e[1]), pack2h(e[2], e[3]), pack2h(e[4], e[5]),
                                                   pack2h(e[6], e[7])));
     lb = sum8h(pk[hf], lb);
@@ -459,7 +463,7 @@ __device__ inline void block_compute(const f16x8 (&k)[8], bf16x8 kext, const uin
     }
 }
 
-template <int KBITS, int VBITS, bool TAYLOR, int NG>
+template <int KBITS, int VBITS, bool TAYLOR, int NG, bool CAUSAL>
 __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, int64_t rows_per_kvhead,
                                                                 int32_t row_groups, int32_t nsplit, float *ws) {
   __shared__ __attribute__((aligned(16))) uint16_t L[LDS_BYTES / 2];
@@ -522,7 +526,17 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
   const int nbc = (c.nc + BK - 1) / BK, nbt = nbc + (c.ncur + BK - 1) / BK;
   const int bps = (nbt + nsplit - 1) / nsplit;
   const int bbeg = static_cast<int>(split) * bps;
-  const int bend = bbeg + bps < nbt ? bbeg + bps : nbt;
+  int bend = bbeg + bps < nbt ? bbeg + bps : nbt;
+  // causal mask: current keys below climit are visible to the lane's row
+  // (query j of Nq, aligned to the chunk's end); the workgroup stops at the
+  // largest limit of its 32 rows
+  const int climit = static_cast<int>(rr % p.Nq + p.Ncur - p.Nq + 1);
+  if (CAUSAL) {
+    const int64_t r0 = rg * 32, r1 = min(r0 + 32, rows_per_kvhead) - 1;
+    const int64_t wlim = (r0 / p.Nq == r1 / p.Nq ? r1 % p.Nq : p.Nq - 1) + p.Ncur - p.Nq + 1;
+    const int cb = nbc + static_cast<int>(wlim > 0 ? (wlim + BK - 1) / BK : 0);
+    if (bend > cb) bend = cb;
+  }
   uint16_t *Vt = L + wave * VT;
 
   int blk = bbeg + wave;
@@ -544,13 +558,14 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
   }
   for (; blk < bend; blk += WAVES) {
     const int k0 = (blk - nbc) * BK;
-    const int count = c.ncur - k0 < BK ? c.ncur - k0 : BK;
+    int count = c.ncur - k0 < BK ? c.ncur - k0 : BK;
+    if (CAUSAL) count = min(count, climit - k0);
     Cur x;
     float kb, vb;
     load_current(c, k0, lane, x, kb, vb);
     sc.update(kb, vb, st.alpha);
     unpack_current(lane, x, sc.kscale, sc.vscale, kreg, Vt);
-    block_compute<false>(kreg, kext, Vt, q, qext, count, sc.alpha, sc.ev, lane, st);
+    block_compute<false, CAUSAL>(kreg, kext, Vt, q, qext, count, sc.alpha, sc.ev, lane, st);
   }
 
   // ---- merge the 4 waves (log-sum-exp), then the split partial or output ----
@@ -615,10 +630,10 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
 template <int KB, int VB, int NG>
 void launch_kernel(const AttnLaunch &p, hipStream_t stream, dim3 grid, int64_t rows, int32_t row_groups,
                    float *partials) {
-  if (p.corr == KV_CORR_TAYLOR)
-    attn_short_kernel<KB, VB, true, NG><<<grid, dim3(THREADS), 0, stream>>>(p, rows, row_groups, p.splits, partials);
-  else
-    attn_short_kernel<KB, VB, false, NG><<<grid, dim3(THREADS), 0, stream>>>(p, rows, row_groups, p.splits, partials);
+  auto kernel = p.corr == KV_CORR_TAYLOR
+                    ? (p.causal ? attn_short_kernel<KB, VB, true, NG, true> : attn_short_kernel<KB, VB, true, NG, false>)
+                    : (p.causal ? attn_short_kernel<KB, VB, false, NG, true> : attn_short_kernel<KB, VB, false, NG, false>);
+  kernel<<<grid, dim3(THREADS), 0, stream>>>(p, rows, row_groups, p.splits, partials);
 }
 
 template <int KB, int VB>

@@ -11,7 +11,7 @@ namespace {
 
 using kvq::AttnLaunch;
 
-constexpr int32_t kAbiVersion = 1;
+constexpr int32_t kAbiVersion = 2;
 constexpr int32_t kMaxSplits = 1024;  // grid z extent of the split path
 constexpr int64_t kMaxTokensPerHead = int64_t(1) << 23;  // 8M tokens: 32-bit in-head offsets
 
@@ -83,6 +83,8 @@ kv_status validate_attention(const kv_attn_args *a) {
   if (a->path < KV_PATH_AUTO || a->path > KV_PATH_SHORT) return KV_ERR_UNSUPPORTED;
   if (a->splits < 0) return KV_ERR_SHAPE;
   if (a->splits > kMaxSplits) return KV_ERR_UNSUPPORTED;
+  if (a->causal != 0 && a->causal != 1) return KV_ERR_UNSUPPORTED;
+  if (a->causal && a->Nc == 0 && a->Nq > a->Ncur) return KV_ERR_SHAPE;  // a row would see no key
   if (!(a->softmax_scale >= 0.0f) || !isfinite(a->softmax_scale)) return KV_ERR_SHAPE;
   // sizes: every element count must fit comfortably in int64 and the grid
   int64_t nq_el = 0, ncur_el = 0, t = 0;
@@ -216,6 +218,7 @@ kv_status kv_attention_corrected(const kv_attn_args *a, void *stream) {
   }
   p.tau = a->softmax_scale > 0.0f ? a->softmax_scale : 1.0f / sqrtf(static_cast<float>(a->d));
   p.corr = a->corr;
+  p.causal = a->causal;
   p.splits = pl.splits;
   p.workspace = a->workspace;
   if (debug_log())

@@ -35,7 +35,8 @@ struct AttnLaunch {
   int64_t cap;
   float tau;   // resolved softmax scale
   int corr;    // kv_corr
-  int splits;  // short path: resolved split count
+  int causal;  // 1: current key i visible to query row j only if i <= j + Ncur - Nq
+  int splits;  // resolved key-range split count
   void *workspace;
 };
 

@@ -37,7 +37,7 @@ class AttnArgs(C.Structure):
                 ("q", C.c_void_p), ("k_cur", C.c_void_p), ("v_cur", C.c_void_p),
                 ("k_cache", C.POINTER(QTensor)), ("v_cache", C.POINTER(QTensor)),
                 ("out", C.c_void_p), ("softmax_scale", C.c_float), ("corr", C.c_int32),
-                ("path", C.c_int32), ("splits", C.c_int32),
+                ("path", C.c_int32), ("splits", C.c_int32), ("causal", C.c_int32),
                 ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t)]
 
 
@@ -114,7 +114,7 @@ def quantize(x, cache: QCache, tok_offset: int = 0, stream=None) -> None:
 
 def make_args(q, k_cur, v_cur, k_cache: Optional[QCache], v_cache: Optional[QCache], nc: int, out,
               corr: str = "taylor", scale: float = 0.0, path: str = "auto", splits: int = 0,
-              workspace=None):
+              workspace=None, causal: bool = False):
     """Fill kv_attn_args (keeps the descriptors alive on the returned object)."""
     B, Hq, Nq, d = q.shape
     Hkv = k_cur.shape[1] if k_cur is not None else k_cache.H
@@ -127,6 +127,7 @@ def make_args(q, k_cur, v_cur, k_cache: Optional[QCache], v_cache: Optional[QCac
     a.k_cache = C.pointer(a._kd) if a._kd is not None else None
     a.v_cache = C.pointer(a._vd) if a._vd is not None else None
     a.softmax_scale, a.corr, a.path, a.splits = scale, CORR[corr], PATH[path], splits
+    a.causal = 1 if causal else 0
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return a
@@ -138,14 +139,15 @@ def workspace_size(args: AttnArgs) -> int:
 
 def attention(q, k_cur, v_cur, k_cache: Optional[QCache], v_cache: Optional[QCache], nc: int,
               corr: str = "taylor", scale: float = 0.0, path: str = "auto", splits: int = 0,
-              out=None, workspace=None, stream=None):
+              out=None, workspace=None, stream=None, causal: bool = False):
     """Corrected attention of q [B][Hq][Nq][d] (bf16) over the first nc tokens
-    of the quantized caches and the bf16 current chunk [B][Hkv][Ncur][d].
+    of the quantized caches and the bf16 current chunk [B][Hkv][Ncur][d]
+    (causal: end-aligned causal mask within the current chunk).
     Returns out [B][Hq][Nq][d] bf16."""
     import torch
     if out is None:
         out = torch.empty_like(q)
-    args = make_args(q, k_cur, v_cur, k_cache, v_cache, nc, out, corr, scale, path, splits, workspace)
+    args = make_args(q, k_cur, v_cur, k_cache, v_cache, nc, out, corr, scale, path, splits, workspace, causal)
     need = workspace_size(args)
     if need > 0 and (workspace is None or args.workspace_bytes < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)

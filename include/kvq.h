@@ -114,7 +114,12 @@ kv_status kv_quantize(const void *x, kv_dtype xdt, int64_t B, int64_t H, int64_t
  *   cached  logits  s_i = tau q.x^_i - b_i   for i <  Nc  (b per `corr`)
  *   current logits  s_i = tau q.k_i          for i <  Ncur (never corrected)
  *   out = softmax over both segments together, applied to [v^ ; v_cur]
- * Values get no correction (they enter the output linearly).  No mask.
+ * Values get no correction (they enter the output linearly).  By default
+ * there is no mask (chunk-wise video generation: every query sees every
+ * key).  With `causal` = 1 the current chunk is masked causally, aligned to
+ * its end: query row j sees current keys i <= j + Ncur - Nq (and the whole
+ * cache), as in chunked prefill where the chunk's queries are its last Nq
+ * tokens.
  */
 typedef struct {
   int64_t B, Hq, Hkv; /* Hq % Hkv == 0 */
@@ -134,6 +139,8 @@ typedef struct {
   int32_t splits;     /* key-range splits, 0 = automatic, at most 1024: the short path,
                          and the long path for d = 128 with correction off or Taylor
                          (clamped to the number of 64-key tiles) */
+  int32_t causal;     /* 0: no mask; 1: causal within the current chunk, end-aligned
+                         (every query row must then see a key: Nc > 0 or Ncur >= Nq) */
   void *workspace;    /* device scratch of kv_attention_workspace_size() bytes */
   size_t workspace_bytes;
 } kv_attn_args;
@@ -154,7 +161,8 @@ size_t kv_attention_workspace_size(const kv_attn_args *a);
  * B x Hq x Nq query rows in a single fused pass over the packed cache and the
  * bf16 current chunk (dequantisation, scores, correction, softmax and the
  * value product all inside the kernel).
- * Errors: KV_ERR_NULL, KV_ERR_SHAPE, KV_ERR_UNSUPPORTED, KV_ERR_WORKSPACE,
+ * Errors: KV_ERR_NULL, KV_ERR_SHAPE (also: causal with Nc = 0 and
+ * Nq > Ncur), KV_ERR_UNSUPPORTED (also: causal not 0 or 1), KV_ERR_WORKSPACE,
  * KV_ERR_ALIGN, KV_ERR_ALIAS, KV_ERR_HIP.
  */
 kv_status kv_attention_corrected(const kv_attn_args *a, void *stream);

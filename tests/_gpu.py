@@ -35,12 +35,12 @@ def cache_to_host(c: kvq.QCache, nc: int):
     return tuple(t[:, :, :nc].cpu().numpy() for t in (c.codes, c.scale, c.zero))
 
 
-def run_attention(w, data, kc, vc, corr="taylor", path="auto", scale=0.0, splits=0):
+def run_attention(w, data, kc, vc, corr="taylor", path="auto", scale=0.0, splits=0, causal=False):
     q = as_bf16_dev(data["q"])
     k = as_bf16_dev(data["k"]) if w.Ncur > 0 else None
     v = as_bf16_dev(data["v"]) if w.Ncur > 0 else None
     out = kvq.attention(q, k, v, kc if w.Nc > 0 else None, vc if w.Nc > 0 else None, w.Nc,
-                        corr=corr, scale=scale, path=path, splits=splits)
+                        corr=corr, scale=scale, path=path, splits=splits, causal=causal)
     torch.cuda.synchronize()
     return out
 

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(kvq):
 
 
 def test_version_and_status_strings(kvq):
-    assert kvq.lib.kv_version() == 1
+    assert kvq.lib.kv_version() == 2
     for s in range(1, 8):
         assert len(kvq.lib.kv_status_string(s)) > 10
     assert kvq.lib.kv_status_string(0) == b"ok"
@@ -58,7 +58,7 @@ int main(void) {
   F(kv_attn_args, Ncur); F(kv_attn_args, Nc); F(kv_attn_args, d); F(kv_attn_args, q);
   F(kv_attn_args, k_cur); F(kv_attn_args, v_cur); F(kv_attn_args, k_cache); F(kv_attn_args, v_cache);
   F(kv_attn_args, out); F(kv_attn_args, softmax_scale); F(kv_attn_args, corr); F(kv_attn_args, path);
-  F(kv_attn_args, splits); F(kv_attn_args, workspace); F(kv_attn_args, workspace_bytes);
+  F(kv_attn_args, splits); F(kv_attn_args, causal); F(kv_attn_args, workspace); F(kv_attn_args, workspace_bytes);
   return 0;
 }
 """)
@@ -124,6 +124,8 @@ CASES = [
     ("misaligned q", dict(q=A + 2), "KV_ERR_ALIGN"),
     ("out aliases q", dict(out=A + 64), "KV_ERR_ALIAS"),
     ("out aliases k_cur", dict(out=2 * A), "KV_ERR_ALIAS"),
+    ("causal=2", dict(causal=2), "KV_ERR_UNSUPPORTED"),
+    ("causal rows without keys", dict(causal=1, Nc=0, Nq=9, Ncur=8), "KV_ERR_SHAPE"),
 ]
 
 

@@ -26,16 +26,17 @@ CASES = {
 }
 
 
-def _compare(orc, w, corr, path, scale=0.0, splits=0, data=None):
+def _compare(orc, w, corr, path, scale=0.0, splits=0, data=None, causal=False):
     import _gpu
     data = W.generate(w) if data is None else data
     print(f"[attention] B={w.B} Hq={w.Hq} Hkv={w.Hkv} d={w.d} Nq={w.Nq} Ncur={w.Ncur} Nc={w.Nc} "
-          f"bits={w.kbits}/{w.vbits} group={w.group} corr={corr} path={path} splits={splits}", flush=True)
+          f"bits={w.kbits}/{w.vbits} group={w.group} corr={corr} path={path} splits={splits} causal={causal}",
+          flush=True)
     kc = _gpu.build_cache(w, data["kc"], w.kbits) if w.Nc > 0 else None
     vc = _gpu.build_cache(w, data["vc"], w.vbits) if w.Nc > 0 else None
-    out = _gpu.run_attention(w, data, kc, vc, corr=corr, path=path, scale=scale, splits=splits)
+    out = _gpu.run_attention(w, data, kc, vc, corr=corr, path=path, scale=scale, splits=splits, causal=causal)
     got = _gpu.out_rows(out)
-    ref = oracle_problem(orc, w, corr, data=data, scale=scale).attention()
+    ref = oracle_problem(orc, w, corr, data=data, scale=scale, causal=causal).attention()
     _gpu.check(got, ref)
     return got, ref
 
@@ -157,3 +158,50 @@ def test_scaled_inputs(orc, scales, path):
             got = _gpu.out_rows(out)
             ref = oracle_problem(orc, w, corr, data=data).attention()
             _gpu.check(got / sv, ref / sv, max_abs=_gpu.MAX_ABS * widen, mean_abs=_gpu.MEAN_ABS * widen)
+
+
+# Causal mask within the current chunk, aligned to its end (query j of Nq
+# sees current keys i <= j + Ncur - Nq, and the whole cache).
+CAUSAL = {
+    "square": CASES["int4"],
+    "gqa": CASES["gqa"],  # 4 query heads per KV head: row blocks span several heads
+    "nq_lt_ncur": EDGE["nq_ne_ncur"],
+    "nq_gt_ncur": W.WORKLOADS["h40_int2_outliers_cache25k"].scaled(Hq=2, Hkv=2, Nq=150, Ncur=70, Nc=300),
+    "rows3": W.WORKLOADS["long_video_cache61k"].scaled(Hq=1, Hkv=1, Nq=600, Ncur=600, Nc=100),  # 3 row blocks
+    "no_cache": W.WORKLOADS["h24_int4_cache16k"].scaled(Hq=1, Hkv=1, Nq=300, Ncur=300, Nc=0),
+    "d64": W.WORKLOADS["tiny_d64_int2"].scaled(Hq=4, Hkv=2, Nq=40, Ncur=77, Nc=130, group=32, kbits=4),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CAUSAL))
+@pytest.mark.parametrize("path", ["long", "short"])
+def test_causal(orc, case, path):
+    w = CAUSAL[case]
+    if path == "short" and w.Nc == 0:
+        pytest.skip("the split path needs cached tokens")
+    data = W.generate(w)
+    for corr in ("off", "taylor", "exact"):
+        _compare(orc, w, corr, path, data=data, causal=True)
+
+
+@pytest.mark.parametrize("splits", [2, 3, 7, 40])
+@pytest.mark.parametrize("path", ["long", "short"])
+def test_causal_split_counts(orc, splits, path):
+    """Forced key-range splits under the mask: late splits hold only
+    current keys, some of them hidden from every row of a workgroup or
+    from some of its rows."""
+    for case in ("rows3", "gqa"):
+        _compare(orc, CAUSAL[case], "taylor", path, splits=splits, causal=True)
+
+
+def test_causal_one_query_is_unmasked(orc):
+    """With one query row (decode) the mask hides nothing."""
+    import _gpu
+    w = W.WORKLOADS["gqa_prefill_b16_cache32k"].scaled(B=2, Nq=1, Ncur=37, Nc=500)
+    data = W.generate(w)
+    kc = _gpu.build_cache(w, data["kc"], w.kbits)
+    vc = _gpu.build_cache(w, data["vc"], w.vbits)
+    for path in ("long", "short"):
+        a = _gpu.run_attention(w, data, kc, vc, path=path)
+        b = _gpu.run_attention(w, data, kc, vc, path=path, causal=True)
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
