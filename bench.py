@@ -35,7 +35,8 @@ DEFAULT_WORKLOAD = "h24_int4_cache16k"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "cached-key tokens\u00b7queries/s (TFLOP/s eff.) and packed-KV HBM GB/s vs roofline"
-KERNEL_SOURCES = [os.path.join(ROOT, "bit_kv_cache_03_amd", "csrc", f) for f in ("attention.hip", "attention_fast.hip", "attention_short.hip", "kvq_device.h", "kvq_api.cpp", "kvq_internal.h")]
+KERNEL_SOURCES = [os.path.join(ROOT, "bit_kv_cache_03_amd", "csrc", f) for f in ("attention.hip", "attention_fast.hip", "attention_fast_causal.hip", "attention_short.hip",
+                                                                            "kvq_device.h", "kvq_api.cpp", "kvq_internal.h")]
 
 
 def kernel_sha() -> str:
@@ -53,9 +54,19 @@ def packed_bytes(w) -> int:
     return w.B * w.Hkv * w.Nc * per_tok
 
 
-def attention_flops(w) -> float:
-    """Algorithmic flops: Q K^T and P V over both segments (4 d per pair)."""
-    return 4.0 * w.d * w.B * w.Hq * w.Nq * (w.Nc + w.Ncur)
+def visible_current_pairs(w, causal: bool) -> int:
+    """(query row, current key) pairs per head: all of them, or under the
+    end-aligned causal mask those with key i <= j + Ncur - Nq."""
+    if not causal:
+        return w.Nq * w.Ncur
+    j = np.arange(w.Nq)
+    return int(np.clip(j + w.Ncur - w.Nq + 1, 0, w.Ncur).sum())
+
+
+def attention_flops(w, causal: bool = False) -> float:
+    """Algorithmic flops: Q K^T and P V over the visible (query, key) pairs
+    of both segments (4 d per pair)."""
+    return 4.0 * w.d * w.B * w.Hq * (w.Nq * w.Nc + visible_current_pairs(w, causal))
 
 
 def traffic_from_profiles(w, sha: str):
@@ -71,7 +82,7 @@ def traffic_from_profiles(w, sha: str):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(w, data, corr: str, target_s: float = 12.0):
+def cpu_baseline(w, data, corr: str, target_s: float = 12.0, causal: bool = False):
     """The oracle as it stands, on a bounded sample of query rows (all heads,
     rows spread over the chunk), with the quantize of the chunk prorated."""
     import oracle
@@ -80,7 +91,7 @@ def cpu_baseline(w, data, corr: str, target_s: float = 12.0):
     vc = oracle.quantize(data["vc"], w.vbits, w.group)
     qb = lambda x: x if x.dtype == np.uint16 else W.bf16_bits(x)
     prob = oracle.Problem(qb(data["q"]), qb(data["k"]), qb(data["v"]), kc, vc, w.Nc, w.kbits, w.vbits,
-                          w.group, corr=corr)
+                          w.group, corr=corr, causal=causal)
     total = prob.rows_total()
     t0 = time.perf_counter()
     oracle.quantize(data["k"], w.kbits, w.group)
@@ -107,7 +118,8 @@ def cpu_baseline(w, data, corr: str, target_s: float = 12.0):
     return {"value": n * w.Nc / t, "unit": "cached-key tokens·queries/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{n} of {total} query rows (every {total / n:.1f}th, all heads) of {w.name}, "
-                      f"fp64 oracle attention with {corr} correction over all {w.Nc}+{w.Ncur} keys, "
+                      f"fp64 oracle attention with {corr} correction over all {w.Nc}+{w.Ncur} keys"
+                      f"{' (causal mask on the current chunk)' if causal else ''}, "
                       f"plus the chunk's quantize prorated; {t:.1f} s wall on {threads} threads"}
 
 
@@ -162,6 +174,7 @@ def main():
     ap.add_argument("--corr", default=None, choices=["off", "taylor", "exact"])
     ap.add_argument("--path", default="auto", choices=["auto", "long", "short"])
     ap.add_argument("--nq", type=int, default=0, help="override query rows (and current chunk) per head")
+    ap.add_argument("--causal", action="store_true", help="end-aligned causal mask within the current chunk")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-overhead", action="store_true", help="skip the correction-off timing")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -205,10 +218,11 @@ def main():
         kvq.quantize(dev(np.ascontiguousarray(data["kc"][:, :, off:off + n])), kc, off)
         kvq.quantize(dev(np.ascontiguousarray(data["vc"][:, :, off:off + n])), vc, off)
     out = torch.empty_like(q)
-    args_c = kvq.make_args(q, k, v, kc, vc, w.Nc, out, corr=corr, path=args.path)
+    args_c = kvq.make_args(q, k, v, kc, vc, w.Nc, out, corr=corr, path=args.path, causal=args.causal)
     ws_bytes = kvq.workspace_size(args_c)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
-    args_c = kvq.make_args(q, k, v, kc, vc, w.Nc, out, corr=corr, path=args.path, workspace=ws)
+    args_c = kvq.make_args(q, k, v, kc, vc, w.Nc, out, corr=corr, path=args.path, workspace=ws,
+                           causal=args.causal)
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     import ctypes as C
@@ -247,7 +261,8 @@ def main():
 
     overhead = None
     if not args.no_overhead and corr != "off":
-        a_off = kvq.make_args(q, k, v, kc, vc, w.Nc, out, corr="off", path=args.path, workspace=ws)
+        a_off = kvq.make_args(q, k, v, kc, vc, w.Nc, out, corr="off", path=args.path, workspace=ws,
+                              causal=args.causal)
         for _ in range(args.warmup):
             attention(a_off)
         e_off = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -260,7 +275,7 @@ def main():
         t_on = float(np.median([a.elapsed_time(b) for a, b in e_on]))
         overhead = t_on / t_off - 1.0
 
-    flops = attention_flops(w)
+    flops = attention_flops(w, args.causal)
     ckq = w.B * w.Hq * w.Nq * w.Nc
     achieved = flops / (attn_ms * 1e-3) / 1e12
     # few query rows per KV head: the packed cache read bounds the kernel
@@ -288,7 +303,7 @@ def main():
             w.kbits, w.vbits, w.group),
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "Nq": w.Nq,
                    "Ncur": w.Ncur, "Nc": w.Nc, "kbits": w.kbits, "vbits": w.vbits, "group": w.group,
-                   "corr": corr, "path": args.path},
+                   "corr": corr, "path": args.path, "causal": args.causal},
         "attention_ms": attn_ms,
         "quantize_ms": quant_ms,
         "tflops_eff": achieved,
@@ -300,7 +315,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, data, corr)
+        line["cpu_baseline"] = cpu_baseline(w, data, corr, causal=args.causal)
     print(json.dumps(line), flush=True)
 
 

@@ -53,10 +53,19 @@
 // (keys as rows) each lane owns one query: row max and sum are local plus
 // one exchange with lane l^32, and the P operand is the score accumulator
 // itself; V^T is stored in LDS in the matching permuted key order.
+//
+// The causal-mask instances are built from this file in a translation unit
+// of their own (attention_fast_causal.hip defines KVQ_FAST_CAUSAL to 1):
+// compiled next to the unmasked ones, they changed how those were
+// optimised (query operands spilled inside the tile loop).
 #include <math.h>
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
+
+#ifndef KVQ_FAST_CAUSAL
+#define KVQ_FAST_CAUSAL 0
+#endif
 
 namespace kvq {
 namespace {
@@ -760,10 +769,8 @@ hipError_t launch_bits(const AttnLaunch &p, hipStream_t stream) {
                                            (nsplit > 1 ? short_path_workspace_bytes(p.B, p.Hq, p.Nq, p.d, nsplit) : 0));
   launch_key_scale(p, stream, kpart);
   const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(nsplit) * row_blocks * p.B * p.Hkv));
-  auto kernel = p.corr == KV_CORR_TAYLOR ? (p.causal ? attn_fast_kernel<KB, VB, true, true>
-                                                     : attn_fast_kernel<KB, VB, true, false>)
-                                         : (p.causal ? attn_fast_kernel<KB, VB, false, true>
-                                                     : attn_fast_kernel<KB, VB, false, false>);
+  auto kernel = p.corr == KV_CORR_TAYLOR ? attn_fast_kernel<KB, VB, true, KVQ_FAST_CAUSAL != 0>
+                                         : attn_fast_kernel<KB, VB, false, KVQ_FAST_CAUSAL != 0>;
   kernel<<<grid, dim3(THREADS), 0, stream>>>(p, gshift, rows, row_blocks, kpart, nsplit, partials);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
@@ -772,6 +779,15 @@ hipError_t launch_bits(const AttnLaunch &p, hipStream_t stream) {
 
 }  // namespace
 
+#if KVQ_FAST_CAUSAL
+hipError_t launch_attention_fast_causal(const AttnLaunch &p, hipStream_t stream) {
+  const int kb = p.Nc > 0 ? p.kbits : 2, vb = p.Nc > 0 ? p.vbits : 2;
+  if (kb == 2 && vb == 2) return launch_bits<2, 2>(p, stream);
+  if (kb == 2 && vb == 4) return launch_bits<2, 4>(p, stream);
+  if (kb == 4 && vb == 2) return launch_bits<4, 2>(p, stream);
+  return launch_bits<4, 4>(p, stream);
+}
+#else
 bool fast_path_supported(const AttnLaunch &p) { return p.d == D && p.corr != KV_CORR_EXACT; }
 
 void launch_key_scale(const AttnLaunch &p, hipStream_t stream, float *part) {
@@ -812,11 +828,13 @@ int fast_path_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nc,
 }
 
 hipError_t launch_attention_fast(const AttnLaunch &p, hipStream_t stream) {
+  if (p.causal) return launch_attention_fast_causal(p, stream);
   const int kb = p.Nc > 0 ? p.kbits : 2, vb = p.Nc > 0 ? p.vbits : 2;
   if (kb == 2 && vb == 2) return launch_bits<2, 2>(p, stream);
   if (kb == 2 && vb == 4) return launch_bits<2, 4>(p, stream);
   if (kb == 4 && vb == 2) return launch_bits<4, 2>(p, stream);
   return launch_bits<4, 4>(p, stream);
 }
+#endif
 
 }  // namespace kvq

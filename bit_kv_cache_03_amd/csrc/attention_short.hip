@@ -661,7 +661,10 @@ bool short_fast_supported(int32_t d, int corr) { return d == D && corr != KV_COR
 int short_fast_splits(int64_t B, int64_t Hkv, int64_t rows_per_kvhead, int64_t Nc, int64_t Ncur, int cu_count) {
   const int64_t groups = B * Hkv * ((rows_per_kvhead + 31) / 32);
   const int64_t blocks = (Nc + BK - 1) / BK + (Ncur + BK - 1) / BK;
-  int64_t s = (4 * static_cast<int64_t>(cu_count) + groups - 1) / groups;  // ~4 workgroups per CU
+  // ~2 workgroups per CU: one round of resident workgroups (two fit a CU),
+  // each wave with as many blocks as possible to spread its fixed costs
+  // (query load, merge, partials) over
+  int64_t s = (2 * static_cast<int64_t>(cu_count) + groups - 1) / groups;
   const int64_t max_s = (blocks + 4 * WAVES - 1) / (4 * WAVES);              // >= 4 blocks per wave
   if (s > max_s) s = max_s;
   if (s < 1) s = 1;

@@ -55,6 +55,8 @@ bool fast_path_supported(const AttnLaunch &p);
 size_t fast_path_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int splits);
 int fast_path_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nc, int64_t Ncur, int cu_count);
 hipError_t launch_attention_fast(const AttnLaunch &p, hipStream_t stream);
+// The same with the causal mask (built in attention_fast_causal.hip).
+hipError_t launch_attention_fast_causal(const AttnLaunch &p, hipStream_t stream);
 // Pre-pass of the throughput kernel: per (b, KV head), 32 partial bounds of
 // |key| (dequantised cache and current chunk) and of |query|, from which the
 // kernel takes the exponent that balances its fp16 key and query operands.

@@ -1,0 +1,31 @@
+"""Host-side arithmetic of bench.py: the algorithmic work counts behind the
+roofline figures (no GPU)."""
+import importlib.util
+import os
+
+import pytest
+from torch.nn.attention.bias import causal_lower_right
+
+from bit_kv_cache_03_amd import workloads as W
+
+_spec = importlib.util.spec_from_file_location(
+    "bench", os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "bench.py"))
+bench = importlib.util.module_from_spec(_spec)
+_spec.loader.exec_module(bench)
+
+
+@pytest.mark.parametrize("nq,ncur", [(1, 37), (5, 9), (6, 6), (7, 4), (300, 300), (4096, 4096)])
+def test_visible_pairs_match_lower_right_mask(nq, ncur):
+    w = W.WORKLOADS["h24_int4_cache16k"].scaled(Nq=nq, Ncur=ncur)
+    assert bench.visible_current_pairs(w, False) == nq * ncur
+    assert bench.visible_current_pairs(w, True) == int(causal_lower_right(nq, ncur)._materialize().sum())
+
+
+def test_flops_and_bytes_of_the_default_workload():
+    w = W.WORKLOADS["h24_int4_cache16k"]
+    # 4 d flops per (query, key) pair over the cache and the chunk
+    assert bench.attention_flops(w) == 4.0 * 128 * 24 * 4096 * (16384 + 4096)
+    # square chunk under the mask: Nq (Nq + 1) / 2 current pairs per head
+    assert bench.attention_flops(w, causal=True) == 4.0 * 128 * 24 * (4096 * 16384 + 4096 * 4097 // 2)
+    # INT4 K and V codes (64 + 64 bytes) plus fp32 step and zero of 2 groups for K and V (32 bytes)
+    assert bench.packed_bytes(w) == 24 * 16384 * 160
