@@ -136,28 +136,41 @@ def copy_probe(nbytes: int, reps: int = 3):
     print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
-def _counter_mean(csv_path: str, counter: str, kernel_substr: str) -> float:
+def _counter_means(csv_path: str, counter: str, kernel_substrs) -> dict:
+    """Mean per dispatch of one counter for each kernel whose name holds one
+    of kernel_substrs (keyed by that substring)."""
     import csv
-    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path))
-            if r["Counter_Name"] == counter and kernel_substr in r["Kernel_Name"]]
+    vals = {}
+    for r in csv.DictReader(open(csv_path)):
+        hit = [k for k in kernel_substrs if k in r["Kernel_Name"]]
+        if r["Counter_Name"] == counter and hit:
+            vals.setdefault(hit[0], []).append(float(r["Counter_Value"]))
     if not vals:
-        raise SystemExit(f"no {counter} rows for kernels matching {kernel_substr!r} in {csv_path}")
-    return float(np.mean(vals))
+        raise SystemExit(f"no {counter} rows for kernels matching {kernel_substrs!r} in {csv_path}")
+    return {k: float(np.mean(v)) for k, v in vals.items()}
+
+
+# kernels one kv_attention_corrected call launches (pre-pass, attention, combine)
+ATTENTION_CALL_KERNELS = ("key_scale_kernel", "attn_fast_kernel", "attn_short_kernel", "attn_tile_kernel",
+                          "attn_combine_kernel")
 
 
 def write_traffic(w, pmc_dir: str, copy_bytes: int):
-    """HBM bytes per attention launch from four rocprofv3 --pmc runs under
+    """HBM bytes per attention call from four rocprofv3 --pmc runs under
     pmc_dir (fetch/, write/: the bench; copy_fetch/, copy_write/: the copy
-    probe), each counter scaled by bytes/KiB-reading of the plain copy."""
+    probe): each kernel's mean counter per dispatch, scaled by bytes per
+    KiB-reading of the plain copy, summed over the kernels of one call (the
+    span bench times)."""
     f = lambda sub: os.path.join(pmc_dir, sub, "run_counter_collection.csv")
-    kname = "attn_"
-    fetch_kib = _counter_mean(f("fetch"), "FETCH_SIZE", kname)
-    write_kib = _counter_mean(f("write"), "WRITE_SIZE", kname)
-    cf = copy_bytes / (1024.0 * _counter_mean(f("copy_fetch"), "FETCH_SIZE", "neg"))
-    cw = copy_bytes / (1024.0 * _counter_mean(f("copy_write"), "WRITE_SIZE", "neg"))
-    t = {"workload": w.name, "kernel_sha": kernel_sha(), "fetch_kib": fetch_kib, "write_kib": write_kib,
-         "copy_bytes": copy_bytes, "fetch_factor": cf, "write_factor": cw,
-         "bytes_per_launch": 1024.0 * (fetch_kib * cf + write_kib * cw),
+    fetch = _counter_means(f("fetch"), "FETCH_SIZE", ATTENTION_CALL_KERNELS)
+    write = _counter_means(f("write"), "WRITE_SIZE", ATTENTION_CALL_KERNELS)
+    cf = copy_bytes / (1024.0 * sum(_counter_means(f("copy_fetch"), "FETCH_SIZE", ("neg",)).values()))
+    cw = copy_bytes / (1024.0 * sum(_counter_means(f("copy_write"), "WRITE_SIZE", ("neg",)).values()))
+    per_kernel = {k: {"fetch_bytes": 1024.0 * fetch.get(k, 0.0) * cf, "write_bytes": 1024.0 * write.get(k, 0.0) * cw}
+                  for k in sorted(set(fetch) | set(write))}
+    t = {"workload": w.name, "kernel_sha": kernel_sha(), "copy_bytes": copy_bytes, "fetch_factor": cf,
+         "write_factor": cw, "per_kernel": per_kernel,
+         "bytes_per_launch": sum(v["fetch_bytes"] + v["write_bytes"] for v in per_kernel.values()),
          "algorithmic_packed_bytes": packed_bytes(w)}
     out = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
     with open(out, "w") as fh:
