@@ -63,6 +63,7 @@ def _load(path: str):
     L.kvo_logits.argtypes = [vp, i64, vp]
     L.kvo_attention.argtypes = [vp, vp, i64, vp, i32]
     L.kvo_attention_online.argtypes = [vp, i64, i64, vp, i64, i32, vp]
+    L.kvo_diagnostics.argtypes = [vp, vp, vp, i64, vp, vp, i32]
     return L
 
 
@@ -227,3 +228,23 @@ class Problem:
                                         bounds.size - 1, int(cur_first), _p(out))
         _check(rc, "attention_online")
         return out
+
+    def diagnostics(self, k_ref, rows=None, threads: int = 0):
+        """Attention-balance statistics per row (kvo_diagnostics in the C
+        source): ``stats`` [n][5] = lse_ref, lse_q, mass_ref, mass_q, kl and
+        ``top`` [n][2][5] = top-5 key indices of the reference and of the
+        quantised softmax (-1 past the visible keys).  ``k_ref``: uint16 bf16
+        bits [B][Hkv][Nc][d], the cached keys before quantisation."""
+        k_ref = np.ascontiguousarray(k_ref, dtype=np.uint16)
+        if rows is None:
+            n = self.rows_total()
+            rp = None
+        else:
+            rows = np.ascontiguousarray(rows, dtype=np.int64)
+            n = rows.size
+            rp = _p(rows)
+        stats = np.zeros((n, 5), np.float64)
+        top = np.zeros((n, 2, 5), np.int64)
+        _check(lib().kvo_diagnostics(C.byref(self.s), _p(k_ref), rp, n, _p(stats), _p(top), threads),
+               "diagnostics")
+        return stats, top

@@ -26,7 +26,10 @@
  *  - attention: one softmax over [cached keys ; current keys] with b
  *    subtracted from cached logits only, in fp64, brute force.
  *  - an online (tiled, split, LSE-merged) evaluation of the same softmax,
- *    used only to check the online formulation against brute force.
+ *    used only to check the online formulation against brute force;
+ *  - attention-balance statistics of a row: the softmax over unquantised
+ *    cached keys against the quantised one (log-sum-exps, current-chunk
+ *    mass, KL divergence, top-5 keys).
  *
  * Readings taken where the pages are silent (each also listed in the design
  * notes of the repository):
@@ -530,4 +533,127 @@ int kvo_attention_online(const kvo_attn *a, int64_t row, int64_t tile, const int
   return KVO_OK;
 }
 
-int kvo_version(void) { return 2; }
+/* ------------------------------------------------------------------ */
+/* Attention-balance diagnostics ([S1] 問題: quantisation noise on the */
+/* keys raises the cached logits' share of the softmax through the     */
+/* exponential's convexity, so attention moves from the current chunk  */
+/* to the cache; [S1] 為何校正有效: subtracting b restores the balance). */
+/* For one row, the softmax over the unquantised cached keys (given as */
+/* bf16 k_ref) is compared with the one over the quantised cache under */
+/* the problem's correction mode; current keys are the same in both.   */
+/* ------------------------------------------------------------------ */
+
+#define KVO_TOPK 5
+
+/* The k largest of s[0..n) in (value descending, index ascending) order,
+ * skipping -inf (masked) entries; unused slots are -1.  Repeated scans:
+ * slot r takes the best entry that is ordered after slot r-1's. */
+static void top_k(const double *s, int64_t n, int64_t *idx) {
+  int64_t prev = -1;
+  for (int32_t r = 0; r < KVO_TOPK; ++r) {
+    int64_t best = -1;
+    for (int64_t t = 0; t < n; ++t) {
+      if (s[t] == -INFINITY) continue;
+      if (prev >= 0 && (s[t] > s[prev] || (s[t] == s[prev] && t <= prev))) continue; /* already taken */
+      if (best < 0 || s[t] > s[best]) best = t; /* first index wins ties (t increases) */
+    }
+    idx[r] = best;
+    if (best < 0) {
+      for (int32_t q = r + 1; q < KVO_TOPK; ++q) idx[q] = -1;
+      return;
+    }
+    prev = best;
+  }
+}
+
+/* log sum exp of the visible entries. */
+static double lse_of(const double *s, int64_t n) {
+  double m = -INFINITY;
+  for (int64_t t = 0; t < n; ++t)
+    if (s[t] > m) m = s[t];
+  double l = 0.0;
+  for (int64_t t = 0; t < n; ++t)
+    if (s[t] != -INFINITY) l += exp(s[t] - m);
+  return m + log(l);
+}
+
+/* k_ref: bf16 bits [B][Hkv][Nc][d], the cached keys before quantisation.
+ * Per row (flat index, NULL rows = all rows in order):
+ *   stats[5]: lse_ref, lse_q   log sum_t exp(logit_t) over visible keys,
+ *             mass_ref, mass_q the softmax mass on current-chunk keys,
+ *             kl               KL(p_ref || p_q) = sum_t p_ref,t log(p_ref,t / p_q,t);
+ *   top[10]:  the 5 largest logits' key indices (descending, ties by lower
+ *             index; -1 past the visible count) of ref, then of q.
+ * ref logits: tau q.k_ref for cached keys, tau q.k for current keys;
+ * q logits: as kvo_logits (tau q.k^ - b for cached keys). */
+int kvo_diagnostics(const kvo_attn *a, const uint16_t *k_ref, const int64_t *rows, int64_t nrows,
+                    double *stats, int64_t *top, int32_t threads) {
+  if (!attn_ok(a) || !stats || !top || (a->Nc > 0 && !k_ref)) return KVO_ERR_ARG;
+  const int64_t total = a->B * a->Hq * a->Nq;
+  if (!rows) nrows = total;
+  for (int64_t i = 0; rows && i < nrows; ++i)
+    if (rows[i] < 0 || rows[i] >= total) return KVO_ERR_ARG;
+  const int32_t d = a->d;
+  const int64_t n = a->Nc + a->Ncur;
+  int err = KVO_OK;
+#ifdef _OPENMP
+  if (threads <= 0) threads = omp_get_max_threads();
+#else
+  (void)threads;
+#endif
+#pragma omp parallel num_threads(threads)
+  {
+    double *work = (double *)malloc(sizeof(double) * (size_t)(3 * d + 2 * n));
+    if (!work) {
+#pragma omp atomic write
+      err = KVO_ERR_MEM;
+    } else {
+      double *q = work, *k = work + d, *v = work + 2 * d, *sr = work + 3 * d, *sq = sr + n;
+#pragma omp for schedule(dynamic, 4)
+      for (int64_t i = 0; i < nrows; ++i) {
+        const int64_t row = rows ? rows[i] : i;
+        rowctx rc;
+        row_setup(a, row, &rc, q);
+        for (int64_t t = 0; t < n; ++t) {
+          if (!visible(a, row, t)) {
+            sr[t] = sq[t] = -INFINITY;
+            continue;
+          }
+          key_value(&rc, t, k, v);
+          sq[t] = logit_of(&rc, t, k);
+          if (t < a->Nc) {
+            const uint16_t *kr = k_ref + ((rc.b * a->Hkv + rc.hk) * a->Nc + t) * d;
+            double s = 0.0;
+            for (int32_t c = 0; c < d; ++c) s += q[c] * (double)bf16_bits_to_f32(kr[c]);
+            sr[t] = s * rc.tau;
+          } else {
+            sr[t] = sq[t]; /* current keys: the same logit in both */
+          }
+        }
+        const double lr = lse_of(sr, n), lq = lse_of(sq, n);
+        double mr = 0.0, mq = 0.0, kl = 0.0;
+        for (int64_t t = 0; t < n; ++t) {
+          if (sr[t] == -INFINITY) continue;
+          const double pr = exp(sr[t] - lr);
+          kl += pr * ((sr[t] - lr) - (sq[t] - lq));
+          if (t >= a->Nc) {
+            mr += pr;
+            mq += exp(sq[t] - lq);
+          }
+        }
+        double *st = stats + i * 5;
+        st[0] = lr;
+        st[1] = lq;
+        st[2] = mr;
+        st[3] = mq;
+        st[4] = kl;
+        top_k(sr, n, top + i * 2 * KVO_TOPK);
+        top_k(sq, n, top + i * 2 * KVO_TOPK + KVO_TOPK);
+      }
+      free(work);
+    }
+  }
+  return err;
+}
+
+int kvo_version(void) { return 3; }

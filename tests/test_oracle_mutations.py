@@ -57,6 +57,14 @@ MUTANTS = [
      [("test_oracle_causal", "test_matches_library_lower_right", {"corr": "off", "wi": 0})]),
     ("causal_off_by_one", "return t - a->Nc <= j + a->Ncur - a->Nq;", "return t - a->Nc < j + a->Ncur - a->Nq;",
      [("test_oracle_causal", "test_matches_library_lower_right", {"corr": "off", "wi": 1})]),
+    ("diag_mass_over_cache", "          if (t >= a->Nc) {\n            mr += pr;", "          if (t < a->Nc) {\n            mr += pr;",
+     [("test_oracle_diagnostics", "test_matches_library_statistics", {"case": "tiny", "corr": "off", "tied": False})]),
+    ("diag_kl_reversed", "kl += pr * ((sr[t] - lr) - (sq[t] - lq));", "kl += pr * ((sq[t] - lq) - (sr[t] - lr));",
+     [("test_oracle_diagnostics", "test_matches_library_statistics", {"case": "int4", "corr": "taylor", "tied": False})]),
+    ("diag_ties_to_last", "if (best < 0 || s[t] > s[best]) best = t;", "if (best < 0 || s[t] >= s[best]) best = t;",
+     [("test_oracle_diagnostics", "test_matches_library_statistics", {"case": "tiny", "corr": "off", "tied": True})]),
+    ("diag_ref_scale_dropped", "            sr[t] = s * rc.tau;", "            sr[t] = s;",
+     [("test_oracle_diagnostics", "test_matches_library_statistics", {"case": "gqa_causal", "corr": "off", "tied": False})]),
     ("value_not_dequantized_zero",
      "v[c] = (double)a->vc_zero[base * ng + g] + ", "v[c] = ",
      [("test_oracle_attention", "test_matches_library_sdpa", {"corr": "off", "wi": 2})]),
