@@ -11,7 +11,7 @@ namespace {
 
 using kvq::AttnLaunch;
 
-constexpr int32_t kAbiVersion = 2;
+constexpr int32_t kAbiVersion = 3;
 constexpr int32_t kMaxSplits = 1024;  // grid z extent of the split path
 constexpr int64_t kMaxTokensPerHead = int64_t(1) << 23;  // 8M tokens: 32-bit in-head offsets
 
@@ -126,6 +126,50 @@ kv_status validate_attention(const kv_attn_args *a) {
   return KV_OK;
 }
 
+kv_status validate_diagnostics(const kv_diag_args *a) {
+  if (!a) return KV_ERR_NULL;
+  if (!a->q || !a->out) return KV_ERR_NULL;
+  if (a->B < 1 || a->Hq < 1 || a->Hkv < 1 || a->Nq < 1 || a->Ncur < 0 || a->Nc < 0) return KV_ERR_SHAPE;
+  if (a->Hq % a->Hkv != 0 || a->Nc + a->Ncur < 1) return KV_ERR_SHAPE;
+  if (!head_dim_ok(a->d)) return KV_ERR_UNSUPPORTED;
+  if (a->corr < KV_CORR_OFF || a->corr > KV_CORR_EXACT) return KV_ERR_UNSUPPORTED;
+  if (a->causal != 0 && a->causal != 1) return KV_ERR_UNSUPPORTED;
+  if (a->causal && a->Nc == 0 && a->Nq > a->Ncur) return KV_ERR_SHAPE;  // a row would see no key
+  if (!(a->softmax_scale >= 0.0f) || !isfinite(a->softmax_scale)) return KV_ERR_SHAPE;
+  int64_t nq_el = 0, ncur_el = 0, nc_el = 0, t = 0;
+  if (!mul_ok(a->B, a->Hq, &t) || !mul_ok(t, a->Nq, &t) || !mul_ok(t, a->d, &nq_el)) return KV_ERR_SHAPE;
+  if (!mul_ok(a->B, a->Hkv, &t) || !mul_ok(t, a->Ncur, &t) || !mul_ok(t, a->d, &ncur_el)) return KV_ERR_SHAPE;
+  if (!mul_ok(a->B, a->Hkv, &t) || !mul_ok(t, a->Nc, &t) || !mul_ok(t, a->d, &nc_el)) return KV_ERR_SHAPE;
+  if (a->B * a->Hkv > 65535) return KV_ERR_UNSUPPORTED;
+  if (a->Ncur > kMaxTokensPerHead || a->Nc > kMaxTokensPerHead) return KV_ERR_UNSUPPORTED;
+  if ((a->Nq * (a->Hq / a->Hkv)) > (int64_t(1) << 36)) return KV_ERR_SHAPE;
+  if (!aligned16(a->q) || !aligned16(a->out)) return KV_ERR_ALIGN;
+  if (a->Ncur > 0) {
+    if (!a->k_cur) return KV_ERR_NULL;
+    if (!aligned16(a->k_cur)) return KV_ERR_ALIGN;
+  }
+  if (a->Nc > 0) {
+    if (!a->k_ref) return KV_ERR_NULL;
+    const kv_status s = check_qtensor(a->k_cache, a->d, a->Nc);
+    if (s != KV_OK) return s;
+    if (!aligned16(a->k_ref)) return KV_ERR_ALIGN;
+  }
+  // the records must not overlap any input
+  const size_t out_b = static_cast<size_t>(nq_el / a->d) * sizeof(kv_diag_row);
+  if (overlaps(a->out, out_b, a->q, static_cast<size_t>(nq_el) * 2)) return KV_ERR_ALIAS;
+  if (a->Ncur > 0 && overlaps(a->out, out_b, a->k_cur, static_cast<size_t>(ncur_el) * 2)) return KV_ERR_ALIAS;
+  if (a->Nc > 0) {
+    const kv_qtensor *c = a->k_cache;
+    const size_t rows = static_cast<size_t>(a->B * a->Hkv * c->cap);
+    const size_t ng = static_cast<size_t>(a->d / c->group);
+    if (overlaps(a->out, out_b, a->k_ref, static_cast<size_t>(nc_el) * 2) ||
+        overlaps(a->out, out_b, c->codes, rows * static_cast<size_t>(a->d * c->bits / 8)) ||
+        overlaps(a->out, out_b, c->scale, rows * ng * 4) || overlaps(a->out, out_b, c->zero, rows * ng * 4))
+      return KV_ERR_ALIAS;
+  }
+  return KV_OK;
+}
+
 Plan plan_attention(const kv_attn_args *a, bool query_device) {
   Plan pl{KV_PATH_LONG, 0, 0};
   const int64_t rows = a->Nq * (a->Hq / a->Hkv);
@@ -228,6 +272,27 @@ kv_status kv_attention_corrected(const kv_attn_args *a, void *stream) {
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = pl.path == KV_PATH_SHORT ? kvq::launch_attention_short(p, s) : kvq::launch_attention_long(p, s);
   return e == hipSuccess ? KV_OK : KV_ERR_HIP;
+}
+
+kv_status kv_attention_diagnostics(const kv_diag_args *a, void *stream) {
+  const kv_status v = validate_diagnostics(a);
+  if (v != KV_OK) return v;
+  kvq::DiagLaunch p{};
+  p.B = a->B; p.Hq = a->Hq; p.Hkv = a->Hkv; p.Nq = a->Nq; p.Ncur = a->Ncur; p.Nc = a->Nc; p.d = a->d;
+  p.q = static_cast<const uint16_t *>(a->q);
+  p.k_cur = static_cast<const uint16_t *>(a->k_cur);
+  p.k_ref = static_cast<const uint16_t *>(a->k_ref);
+  if (a->Nc > 0) {
+    p.kc_codes = a->k_cache->codes; p.kc_scale = a->k_cache->scale; p.kc_zero = a->k_cache->zero;
+    p.kbits = a->k_cache->bits; p.group = a->k_cache->group; p.cap = a->k_cache->cap;
+  } else {
+    p.kbits = 2; p.group = a->d; p.cap = 0;
+  }
+  p.tau = a->softmax_scale > 0.0f ? a->softmax_scale : 1.0f / sqrtf(static_cast<float>(a->d));
+  p.corr = a->corr;
+  p.causal = a->causal;
+  p.out = a->out;
+  return kvq::launch_diagnostics(p, static_cast<hipStream_t>(stream)) == hipSuccess ? KV_OK : KV_ERR_HIP;
 }
 
 }  // extern "C"

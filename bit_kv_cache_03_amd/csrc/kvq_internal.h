@@ -74,4 +74,21 @@ bool short_fast_supported(int32_t d, int corr);
 int short_fast_splits(int64_t B, int64_t Hkv, int64_t rows_per_kvhead, int64_t Nc, int64_t Ncur, int cu_count);
 hipError_t launch_attention_short_fast(const AttnLaunch &p, hipStream_t stream);
 
+// Everything a diagnostics launch needs, already validated by the host.
+struct DiagLaunch {
+  int64_t B, Hq, Hkv, Nq, Ncur, Nc;
+  int32_t d;
+  const uint16_t *q, *k_cur, *k_ref;
+  const uint8_t *kc_codes;
+  const float *kc_scale, *kc_zero;
+  int32_t kbits, group;
+  int64_t cap;
+  float tau;   // resolved softmax scale
+  int corr;    // kv_corr
+  int causal;
+  kv_diag_row *out;
+};
+// Attention-balance statistics (diagnostics.hip).
+hipError_t launch_diagnostics(const DiagLaunch &p, hipStream_t stream);
+
 }  // namespace kvq

@@ -21,7 +21,7 @@ CORR = {"off": 0, "taylor": 1, "exact": 2}
 PATH = {"auto": 0, "long": 1, "short": 2}
 
 EXPORTED = ("kv_quantize", "kv_attention_workspace_size", "kv_attention_corrected",
-            "kv_status_string", "kv_version")
+            "kv_attention_diagnostics", "kv_status_string", "kv_version")
 
 
 class QTensor(C.Structure):
@@ -41,6 +41,18 @@ class AttnArgs(C.Structure):
                 ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t)]
 
 
+class DiagArgs(C.Structure):
+    """kv_diag_args."""
+    _fields_ = [("B", C.c_int64), ("Hq", C.c_int64), ("Hkv", C.c_int64), ("Nq", C.c_int64),
+                ("Ncur", C.c_int64), ("Nc", C.c_int64), ("d", C.c_int32), ("corr", C.c_int32),
+                ("q", C.c_void_p), ("k_cur", C.c_void_p), ("k_ref", C.c_void_p),
+                ("k_cache", C.POINTER(QTensor)), ("softmax_scale", C.c_float), ("causal", C.c_int32),
+                ("out", C.c_void_p)]
+
+
+DIAG_ROW_WORDS = 16  # kv_diag_row: 5 floats, 2 x 5 int32 indices, 1 reserved int32
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python -m bit_kv_cache_03_amd.build`")
@@ -52,6 +64,8 @@ def _load():
     L.kv_attention_workspace_size.restype = C.c_size_t
     L.kv_attention_corrected.argtypes = [C.POINTER(AttnArgs), C.c_void_p]
     L.kv_attention_corrected.restype = C.c_int
+    L.kv_attention_diagnostics.argtypes = [C.POINTER(DiagArgs), C.c_void_p]
+    L.kv_attention_diagnostics.restype = C.c_int
     L.kv_status_string.argtypes = [C.c_int]
     L.kv_status_string.restype = C.c_char_p
     L.kv_version.restype = C.c_int32
@@ -153,4 +167,39 @@ def attention(q, k_cur, v_cur, k_cache: Optional[QCache], v_cache: Optional[QCac
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         args.workspace, args.workspace_bytes = workspace.data_ptr(), need
     _check(lib.kv_attention_corrected(C.byref(args), _stream(stream)), "kv_attention_corrected")
+    return out
+
+
+def make_diag_args(q, k_cur, k_ref, k_cache: Optional[QCache], nc: int, out, corr: str = "taylor",
+                   scale: float = 0.0, causal: bool = False):
+    """Fill kv_diag_args (keeps the descriptor alive on the returned object)."""
+    B, Hq, Nq, d = q.shape
+    Hkv = k_cur.shape[1] if k_cur is not None else k_cache.H
+    ncur = k_cur.shape[2] if k_cur is not None else 0
+    a = DiagArgs()
+    a.B, a.Hq, a.Hkv, a.Nq, a.Ncur, a.Nc, a.d = B, Hq, Hkv, Nq, ncur, nc, d
+    a.corr = CORR[corr]
+    a.q, a.k_cur, a.k_ref = _ptr(q), _ptr(k_cur), _ptr(k_ref)
+    a._kd = k_cache.descriptor() if k_cache is not None else None
+    a.k_cache = C.pointer(a._kd) if a._kd is not None else None
+    a.softmax_scale, a.causal = scale, 1 if causal else 0
+    a.out = _ptr(out)
+    return a
+
+
+def diagnostics(q, k_cur, k_ref, k_cache: Optional[QCache], nc: int, corr: str = "taylor",
+                scale: float = 0.0, causal: bool = False, out=None, stream=None):
+    """Attention-balance statistics of every query row (kv_attention_diagnostics):
+    the softmax over the unquantised cached keys k_ref [B][Hkv][nc][d] (bf16)
+    against the one over the first nc tokens of the quantised k_cache (with
+    `corr`), both with the bf16 current keys k_cur.  Returns an int32 tensor
+    [B*Hq*Nq][16] of kv_diag_row records: columns 0..4 are the fp32 lse_ref,
+    lse_q, mass_ref, mass_q, kl (``.view(torch.float32)``), 5..9 the
+    reference top-5 key indices, 10..14 the quantised ones."""
+    import torch
+    B, Hq, Nq, _ = q.shape
+    if out is None:
+        out = torch.empty((B * Hq * Nq, DIAG_ROW_WORDS), dtype=torch.int32, device=q.device)
+    args = make_diag_args(q, k_cur, k_ref, k_cache, nc, out, corr, scale, causal)
+    _check(lib.kv_attention_diagnostics(C.byref(args), _stream(stream)), "kv_attention_diagnostics")
     return out

@@ -167,6 +167,56 @@ size_t kv_attention_workspace_size(const kv_attn_args *a);
  */
 kv_status kv_attention_corrected(const kv_attn_args *a, void *stream);
 
+/*
+ * Attention-balance diagnostics ("量化鍵值偷走注意力…" (agents-report.net),
+ * section 問題: rounding noise on cached keys raises their share of the
+ * softmax through the exponential's convexity, so attention moves from the
+ * current chunk to the cache; section 為何校正有效: subtracting b restores
+ * the balance).  For every query row the softmax over the cached keys
+ * before quantisation (k_ref, bf16) is compared with the softmax the
+ * corrected attention uses (the quantised cache with `corr`); the current
+ * chunk's keys are the same in both.  With logits l (natural log units,
+ * tau as in kv_attn_args, the same mask):
+ *   lse   = log sum_i exp(l_i) over the visible keys,
+ *   mass  = sum over visible current keys of exp(l_i - lse),
+ *   kl    = KL(p_ref || p_q) = sum_i p_ref,i log(p_ref,i / p_q,i),
+ *   top   = the 5 largest logits' key indices, descending, ties to the lower
+ *           index; index i < Nc is cached key i, Nc + j is current key j;
+ *           -1 past the number of visible keys.
+ * One record per query row, rows in [B][Hq][Nq] order; 64 bytes.
+ */
+typedef struct {
+  float lse_ref, lse_q;
+  float mass_ref, mass_q;
+  float kl;
+  int32_t top_ref[5];
+  int32_t top_q[5];
+  int32_t reserved; /* written as 0 */
+} kv_diag_row;
+
+typedef struct {
+  int64_t B, Hq, Hkv, Nq, Ncur, Nc; /* as in kv_attn_args (Nc >= 1 or Ncur >= 1) */
+  int32_t d;          /* 64 or 128 */
+  int32_t corr;       /* kv_corr applied to the quantised cached logits */
+  const void *q;      /* bf16 [B][Hq][Nq][d] */
+  const void *k_cur;  /* bf16 [B][Hkv][Ncur][d] (may be NULL if Ncur == 0) */
+  const void *k_ref;  /* bf16 [B][Hkv][Nc][d]: the cached keys before quantisation
+                         (may be NULL if Nc == 0) */
+  const kv_qtensor *k_cache; /* host pointer to the quantised keys' descriptor */
+  float softmax_scale; /* tau; 0 -> 1/sqrt(d) */
+  int32_t causal;     /* as in kv_attn_args */
+  kv_diag_row *out;   /* [B*Hq*Nq] records, overwritten; must not overlap inputs */
+} kv_diag_args;
+
+/*
+ * kv_attention_diagnostics -- the statistics above for every query row, one
+ * pass over both key sets (scores only, no value product).  A measurement
+ * tool beside the hot path, not part of it.
+ * Errors: KV_ERR_NULL, KV_ERR_SHAPE, KV_ERR_UNSUPPORTED (d, bits, group,
+ * corr, causal), KV_ERR_ALIGN, KV_ERR_ALIAS, KV_ERR_HIP.
+ */
+kv_status kv_attention_diagnostics(const kv_diag_args *a, void *stream);
+
 /* Static English description of a status code. */
 const char *kv_status_string(kv_status s);
 

@@ -77,3 +77,18 @@ def check(got: np.ndarray, ref: np.ndarray, label: str = "", max_abs: float = MA
     assert np.all(np.isfinite(got))
     assert mx <= max_abs and mean <= mean_abs, (mx, mean)
     return mx, mean
+
+
+def run_diagnostics(w, data, kc, corr="taylor", causal=False):
+    """kv_attention_diagnostics on the workload's inputs: the unquantised
+    cached keys (bf16) against the GPU-built quantised cache.  Returns the
+    records as (stats [n][5] fp32 -> float64, tops [n][2][5] int)."""
+    q = as_bf16_dev(data["q"])
+    k = as_bf16_dev(data["k"]) if w.Ncur > 0 else None
+    kref = as_bf16_dev(data["kc"]) if w.Nc > 0 else None
+    rec = kvq.diagnostics(q, k, kref, kc if w.Nc > 0 else None, w.Nc, corr=corr, causal=causal)
+    torch.cuda.synchronize()
+    r = rec.cpu().numpy()
+    stats = r[:, :5].view(np.float32).astype(np.float64)
+    tops = r[:, 5:15].reshape(-1, 2, 5).astype(np.int64)
+    return stats, tops

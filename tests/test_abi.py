@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(kvq):
 
 
 def test_version_and_status_strings(kvq):
-    assert kvq.lib.kv_version() == 2
+    assert kvq.lib.kv_version() == 3
     for s in range(1, 8):
         assert len(kvq.lib.kv_status_string(s)) > 10
     assert kvq.lib.kv_status_string(0) == b"ok"
@@ -59,6 +59,14 @@ int main(void) {
   F(kv_attn_args, k_cur); F(kv_attn_args, v_cur); F(kv_attn_args, k_cache); F(kv_attn_args, v_cache);
   F(kv_attn_args, out); F(kv_attn_args, softmax_scale); F(kv_attn_args, corr); F(kv_attn_args, path);
   F(kv_attn_args, splits); F(kv_attn_args, causal); F(kv_attn_args, workspace); F(kv_attn_args, workspace_bytes);
+  printf("kv_diag_args %zu\\n", sizeof(kv_diag_args));
+  printf("kv_diag_row %zu\\n", sizeof(kv_diag_row));
+  F(kv_diag_args, B); F(kv_diag_args, Hq); F(kv_diag_args, Hkv); F(kv_diag_args, Nq); F(kv_diag_args, Ncur);
+  F(kv_diag_args, Nc); F(kv_diag_args, d); F(kv_diag_args, corr); F(kv_diag_args, q); F(kv_diag_args, k_cur);
+  F(kv_diag_args, k_ref); F(kv_diag_args, k_cache); F(kv_diag_args, softmax_scale); F(kv_diag_args, causal);
+  F(kv_diag_args, out);
+  F(kv_diag_row, lse_ref); F(kv_diag_row, lse_q); F(kv_diag_row, mass_ref); F(kv_diag_row, mass_q);
+  F(kv_diag_row, kl); F(kv_diag_row, top_ref); F(kv_diag_row, top_q); F(kv_diag_row, reserved);
   return 0;
 }
 """)
@@ -68,10 +76,17 @@ int main(void) {
     got = dict(l.rsplit(" ", 1) for l in lines if l)
     assert int(got["kv_qtensor"]) == C.sizeof(kvq.QTensor)
     assert int(got["kv_attn_args"]) == C.sizeof(kvq.AttnArgs)
+    assert int(got["kv_diag_args"]) == C.sizeof(kvq.DiagArgs)
+    assert int(got["kv_diag_row"]) == 4 * kvq.DIAG_ROW_WORDS
+    row = {"lse_ref": 0, "lse_q": 4, "mass_ref": 8, "mass_q": 12, "kl": 16, "top_ref": 20, "top_q": 40,
+           "reserved": 60}  # the binding's column split of a record
     for key, val in got.items():
         if "." in key:
             T, f = key.split(".")
-            S = kvq.QTensor if T == "kv_qtensor" else kvq.AttnArgs
+            if T == "kv_diag_row":
+                assert row[f] == int(val), key
+                continue
+            S = {"kv_qtensor": kvq.QTensor, "kv_attn_args": kvq.AttnArgs, "kv_diag_args": kvq.DiagArgs}[T]
             assert getattr(S, f).offset == int(val), key
 
 
@@ -208,3 +223,48 @@ def test_quantize_argument_errors(kvq):
     assert q(A, 0, 1, 2, 8, 128, C.byref(bad), 0, None) == kvq.KV_ERR_UNSUPPORTED
     # N = 0 is a valid no-op that launches nothing
     assert q(A, 0, 1, 2, 0, 128, C.byref(good), 64, None) == kvq.KV_OK
+
+
+def _dargs(kvq, **kw):
+    a = kvq.DiagArgs()
+    a.B, a.Hq, a.Hkv, a.Nq, a.Ncur, a.Nc, a.d, a.corr = 1, 4, 2, 8, 8, 50, 128, 1
+    a.q, a.k_cur, a.k_ref, a.out = A, 2 * A, 3 * A, 4 * A
+    a._k = _qt(kvq, 0x10000000)
+    a.k_cache = C.pointer(a._k)
+    a.softmax_scale, a.causal = 0.0, 0
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("name,kw,err", [
+    ("null_q", dict(q=None), "KV_ERR_NULL"),
+    ("null_out", dict(out=None), "KV_ERR_NULL"),
+    ("null_kref", dict(k_ref=None), "KV_ERR_NULL"),
+    ("null_kcur", dict(k_cur=None), "KV_ERR_NULL"),
+    ("gqa", dict(Hq=3), "KV_ERR_SHAPE"),
+    ("no_keys", dict(Nc=0, Ncur=0), "KV_ERR_SHAPE"),
+    ("d", dict(d=96), "KV_ERR_UNSUPPORTED"),
+    ("corr", dict(corr=3), "KV_ERR_UNSUPPORTED"),
+    ("causal", dict(causal=2), "KV_ERR_UNSUPPORTED"),
+    ("causal_empty_row", dict(causal=1, Nc=0, Nq=9), "KV_ERR_SHAPE"),
+    ("scale", dict(softmax_scale=-1.0), "KV_ERR_SHAPE"),
+    ("align", dict(k_ref=3 * A + 4), "KV_ERR_ALIGN"),
+    ("alias_q", dict(out=A + 16), "KV_ERR_ALIAS"),
+    ("alias_kref", dict(out=3 * A + 64), "KV_ERR_ALIAS"),
+])
+def test_diagnostics_argument_errors(kvq, name, kw, err):
+    a = _dargs(kvq, **kw)
+    assert kvq.lib.kv_attention_diagnostics(C.byref(a), None) == getattr(kvq, err), name
+
+
+def test_diagnostics_cache_errors(kvq):
+    a = _dargs(kvq)
+    a._k = _qt(kvq, 0x10000000, cap=49)  # smaller than Nc
+    a.k_cache = C.pointer(a._k)
+    assert kvq.lib.kv_attention_diagnostics(C.byref(a), None) == kvq.KV_ERR_SHAPE
+    a._k = _qt(kvq, 0x10000000, bits=3)
+    a.k_cache = C.pointer(a._k)
+    assert kvq.lib.kv_attention_diagnostics(C.byref(a), None) == kvq.KV_ERR_UNSUPPORTED
+    a.k_cache = None
+    assert kvq.lib.kv_attention_diagnostics(C.byref(a), None) == kvq.KV_ERR_NULL
