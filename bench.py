@@ -178,6 +178,55 @@ def write_traffic(w, pmc_dir: str, copy_bytes: int):
     print(json.dumps(t))
 
 
+def diag_bench(args, w, corr, data, dev, q, k, kc):
+    """Time kv_attention_diagnostics (correction off and the workload's mode)
+    on the full workload and summarise the statistics over all rows."""
+    import ctypes as C
+    import torch
+    from bit_kv_cache_03_amd import kvq
+    kref = dev(data["kc"])
+    stream = torch.cuda.current_stream()
+    rows = w.B * w.Hq * w.Nq
+    res = {}
+    for mode in dict.fromkeys(("off", corr)):
+        rec = torch.empty((rows, kvq.DIAG_ROW_WORDS), dtype=torch.int32, device="cuda")
+        a = kvq.make_diag_args(q, k, kref, kc, w.Nc, rec, corr=mode, causal=args.causal)
+        call = lambda: kvq._check(kvq.lib.kv_attention_diagnostics(C.byref(a), stream.cuda_stream),
+                                  "kv_attention_diagnostics")
+        for _ in range(args.warmup):
+            call()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            call()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+        r = rec.cpu().numpy()
+        st = r[:, :5].view(np.float32).astype(np.float64)
+        top = r[:, 5:15].reshape(-1, 2, 5)
+        recall = np.mean([len(set(a[a >= 0]) & set(b[b >= 0])) / max(1, int((a >= 0).sum())) for a, b in top])
+        res[mode] = {"ms": ms, "mass_q": float(st[:, 3].mean()), "kl": float(st[:, 4].mean()),
+                     "top1_drift": float((top[:, 0, 0] != top[:, 1, 0]).mean()), "top5_recall": float(recall),
+                     "mass_ref": float(st[:, 2].mean())}
+    # algorithmic work: 2d flops per visible (row, key) pair for each score
+    # set; the current chunk's scores are shared by both sets
+    pairs_c = w.B * w.Hq * w.Nq * w.Nc
+    pairs_u = w.B * w.Hq * visible_current_pairs(w, args.causal)
+    flops = 2.0 * w.d * (2 * pairs_c + pairs_u)
+    ms = res[corr]["ms"]
+    line = {
+        "metric": "attention-balance diagnostics (kv_attention_diagnostics)",
+        "workload": w.name, "corr": corr, "causal": args.causal, "rows": rows, "steps": args.steps,
+        "ms": ms, "roofline": {"bound": "mfma", "achieved": flops / (ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+                               "unit": "TFLOP/s", "frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+        "mass_ref": res[corr]["mass_ref"],
+        "modes": {m: {k: v for k, v in d.items() if k != "mass_ref"} for m, d in res.items()},
+        "data": "synthetic: seeded, the workload's key structure; reference = the cached keys before quantisation",
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -188,6 +237,8 @@ def main():
     ap.add_argument("--path", default="auto", choices=["auto", "long", "short"])
     ap.add_argument("--nq", type=int, default=0, help="override query rows (and current chunk) per head")
     ap.add_argument("--causal", action="store_true", help="end-aligned causal mask within the current chunk")
+    ap.add_argument("--diag", action="store_true",
+                    help="time kv_attention_diagnostics and report the attention-balance statistics instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-overhead", action="store_true", help="skip the correction-off timing")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -230,6 +281,9 @@ def main():
         n = min(chunk, w.Nc - off)
         kvq.quantize(dev(np.ascontiguousarray(data["kc"][:, :, off:off + n])), kc, off)
         kvq.quantize(dev(np.ascontiguousarray(data["vc"][:, :, off:off + n])), vc, off)
+    if args.diag:
+        diag_bench(args, w, corr, data, dev, q, k, kc)
+        return
     out = torch.empty_like(q)
     args_c = kvq.make_args(q, k, v, kc, vc, w.Nc, out, corr=corr, path=args.path, causal=args.causal)
     ws_bytes = kvq.workspace_size(args_c)
