@@ -35,8 +35,10 @@ DEFAULT_WORKLOAD = "h24_int4_cache16k"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "cached-key tokens\u00b7queries/s (TFLOP/s eff.) and packed-KV HBM GB/s vs roofline"
-KERNEL_SOURCES = [os.path.join(ROOT, "bit_kv_cache_03_amd", "csrc", f) for f in ("attention.hip", "attention_fast.hip", "attention_fast_causal.hip", "attention_short.hip",
-                                                                            "kvq_device.h", "kvq_api.cpp", "kvq_internal.h")]
+KERNEL_SOURCES = [os.path.join(ROOT, "bit_kv_cache_03_amd", "csrc", f) for f in ("attention.hip", "attention_fast.hip", "attention_fast_causal.hip", "attention_fast_paged.hip",
+                                                                            "attention_fast_paged_causal.hip", "attention_short.hip",
+                                                                            "attention_short_paged.hip", "kvq_device.h", "kvq_api.cpp",
+                                                                            "kvq_internal.h")]
 
 
 def kernel_sha() -> str:
@@ -237,6 +239,8 @@ def main():
     ap.add_argument("--path", default="auto", choices=["auto", "long", "short"])
     ap.add_argument("--nq", type=int, default=0, help="override query rows (and current chunk) per head")
     ap.add_argument("--causal", action="store_true", help="end-aligned causal mask within the current chunk")
+    ap.add_argument("--page-size", type=int, default=0,
+                    help="paged cache layout with pages of this many tokens (shuffled page table)")
     ap.add_argument("--diag", action="store_true",
                     help="time kv_attention_diagnostics and report the attention-balance statistics instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -272,8 +276,18 @@ def main():
                      else torch.from_numpy(W.bf16_bits(x).view(np.int16)).view(torch.bfloat16)).cuda()
     q, k, v = dev(data["q"]), dev(data["k"]), dev(data["v"])
     cap = w.Nc + w.Ncur
-    kc = kvq.QCache(w.B, w.Hkv, cap, w.d, w.kbits, w.group)
-    vc = kvq.QCache(w.B, w.Hkv, cap, w.d, w.vbits, w.group)
+    if args.page_size:
+        # pages of a shuffled pool: every (sequence, block) on a page drawn at random
+        ps = args.page_size
+        cap = (cap + ps - 1) // ps * ps
+        npages = w.B * (cap // ps)
+        perm = np.random.default_rng(11).permutation(npages).astype(np.int32).reshape(w.B, cap // ps)
+        table = torch.from_numpy(perm).cuda()
+        paged = dict(page_table=table, page_size=ps, num_pages=npages)
+    else:
+        paged = {}
+    kc = kvq.QCache(w.B, w.Hkv, cap, w.d, w.kbits, w.group, **paged)
+    vc = kvq.QCache(w.B, w.Hkv, cap, w.d, w.vbits, w.group, **paged)
     # the cache content does not depend on how it is appended (quantisation
     # is per token), so short chunks are appended in >= 4096-token calls
     chunk = max(w.Ncur, 4096)
@@ -370,7 +384,7 @@ def main():
             w.kbits, w.vbits, w.group),
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "Nq": w.Nq,
                    "Ncur": w.Ncur, "Nc": w.Nc, "kbits": w.kbits, "vbits": w.vbits, "group": w.group,
-                   "corr": corr, "path": args.path, "causal": args.causal},
+                   "corr": corr, "path": args.path, "causal": args.causal, "page_size": args.page_size},
         "attention_ms": attn_ms,
         "quantize_ms": quant_ms,
         "tflops_eff": achieved,

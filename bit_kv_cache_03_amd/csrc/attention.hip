@@ -212,7 +212,6 @@ __global__ __launch_bounds__(kThreads, EXACT ? 1 : 2) void attn_tile_kernel(Attn
   }
   const int64_t nt_c = c_end > c_beg ? (c_end - c_beg + kBN - 1) / kBN : 0;
   const int64_t nt_u = u_end > u_beg ? (u_end - u_beg + kBN - 1) / kBN : 0;
-  const int64_t kvbase_c = bkv * p.cap;             // first cache row of this (b, hk)
   const int64_t kvbase_u = bkv * p.Ncur;            // first current row of this (b, hk)
   constexpr int KROW = D * KBITS / 8;               // packed bytes per key row
   constexpr int VROW = D * VBITS / 8;
@@ -235,7 +234,7 @@ __global__ __launch_bounds__(kThreads, EXACT ? 1 : 2) void attn_tile_kernel(Attn
       const bool ok = key < count;
       uint32_t outw[DPT / 2];
       if (cached) {
-        const int64_t row = kvbase_c + k0 + (ok ? key : 0);
+        const int64_t row = p.layout.row(p.cap, p.Hkv, b, hk, k0 + (ok ? key : 0));  // cache row of the key
         const int g = d0 >> group_shift;
         const float stp = ok ? p.kc_scale[row * ng + g] : 0.f;
         const float zp = ok ? p.kc_zero[row * ng + g] : 0.f;
@@ -310,7 +309,7 @@ __global__ __launch_bounds__(kThreads, EXACT ? 1 : 2) void attn_tile_kernel(Attn
           for (int j = 0; j < 4; ++j) {
             const int key = 4 * kq + j;
             const bool ok = key < count;
-            const int64_t row = kvbase_c + k0 + (ok ? key : 0);
+            const int64_t row = p.layout.row(p.cap, p.Hkv, b, hk, k0 + (ok ? key : 0));
             const float stp = ok ? p.vc_scale[row * ng + g] : 0.f;
             const float zp = ok ? p.vc_zero[row * ng + g] : 0.f;
             const uint8_t *src = p.vc_codes + row * VROW + dq * VBITS;  // 8 codes = VBITS bytes

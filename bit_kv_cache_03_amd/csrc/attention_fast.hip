@@ -57,7 +57,9 @@
 // The causal-mask instances are built from this file in a translation unit
 // of their own (attention_fast_causal.hip defines KVQ_FAST_CAUSAL to 1):
 // compiled next to the unmasked ones, they changed how those were
-// optimised (query operands spilled inside the tile loop).
+// optimised (query operands spilled inside the tile loop).  The paged-cache
+// instances likewise (attention_fast_paged.hip and
+// attention_fast_paged_causal.hip: KVQ_FAST_PAGED): one variant per file.
 #include <math.h>
 
 #include "kvq_device.h"
@@ -65,6 +67,9 @@
 
 #ifndef KVQ_FAST_CAUSAL
 #define KVQ_FAST_CAUSAL 0
+#endif
+#ifndef KVQ_FAST_PAGED
+#define KVQ_FAST_PAGED 0
 #endif
 
 namespace kvq {
@@ -128,12 +133,21 @@ __global__ __launch_bounds__(256) void key_scale_kernel(AttnLaunch p, int32_t ng
   const int tid = threadIdx.x;
   float kb = 0.f;
   if (p.Nc > 0) {
-    const float *s = p.kc_scale + bkv * p.cap * ng;
-    const float *z = p.kc_zero + bkv * p.cap * ng;
     const int64_t n = p.Nc * ng, lo = n * ch / KCHUNKS, hi = n * (ch + 1) / KCHUNKS;
-    for (int64_t i = lo + tid; i < hi; i += 256) {
-      const float zi = z[i];
-      kb = fmaxf(kb, fmaxf(fabsf(zi), fabsf(fmaf(s[i], static_cast<float>((1 << KBITS) - 1), zi))));
+    if (p.layout.page_table) {  // element i = (token i / ng, group i % ng) through the page table
+      const int64_t b = bkv / p.Hkv, hk = bkv - b * p.Hkv;
+      for (int64_t i = lo + tid; i < hi; i += 256) {
+        const int64_t e = p.layout.row(p.cap, p.Hkv, b, hk, i / ng) * ng + i % ng;
+        const float zi = p.kc_zero[e];
+        kb = fmaxf(kb, fmaxf(fabsf(zi), fabsf(fmaf(p.kc_scale[e], static_cast<float>((1 << KBITS) - 1), zi))));
+      }
+    } else {
+      const float *s = p.kc_scale + bkv * p.cap * ng;
+      const float *z = p.kc_zero + bkv * p.cap * ng;
+      for (int64_t i = lo + tid; i < hi; i += 256) {
+        const float zi = z[i];
+        kb = fmaxf(kb, fmaxf(fabsf(zi), fabsf(fmaf(s[i], static_cast<float>((1 << KBITS) - 1), zi))));
+      }
     }
   }
   if (p.Ncur > 0) {
@@ -223,7 +237,23 @@ struct Ctx {
   int climit;       // causal mask: current keys below climit are visible to the lane's row
   float kscale;     // tau log2(e) 2^-ek
   uint32_t kmask;   // code mask of magic8, in a vector register
+  CacheLayout layout;         // paged caches: pointers at the pools, rows of (b, hk)
+  int64_t cap, H, b, hk;
 };
+
+// Paged caches: the pool row of the first row of the tile that holds rows
+// [k0, k0 + 64) after clamping to the segment's last row (a tile that starts
+// at or past the end holds only clamped rows: the tile of the last row).
+// Such a tile lies in one page.
+__device__ inline int tile_start(const Ctx &c, int k0) { return min(k0, (c.end - 1) & ~(BN - 1)); }
+__device__ inline size_t tile_pool_row(const Ctx &c, int ts) {
+  // wave-uniform page index (the host bounds B * pages per sequence to int32): one scalar load
+  const int idx = __builtin_amdgcn_readfirstlane(static_cast<int>(c.b) * c.layout.pages_per_seq +
+                                                 (ts >> c.layout.page_shift));
+  const int64_t page = c.layout.page_table[idx];
+  return static_cast<size_t>(((page * c.H + c.hk) << c.layout.page_shift) +
+                             (ts & ((1 << c.layout.page_shift) - 1)));
+}
 
 // Per-lane softmax state of the lane's query row; m is the value the score
 // MFMAs subtract (bf16 hi + lo, exactly as carried in the query operand).
@@ -237,13 +267,22 @@ struct Soft {
 //  V: keys 2*kq, 2*kq+1 with kq = tid / 16, values 8 * (tid % 16) .. +8
 //     (a wave reads 4 keys' rows whole: 16 lanes per row)
 // Rows past the end of the segment clamp to its last row (always in bounds).
-template <bool CACHED, int KBITS>
-__device__ inline void fetch_k(const Ctx &c, int k0, int tid, Fetch &f) {
+template <bool CACHED, int KBITS, bool PAGED = false>
+__device__ inline void fetch_k(const Ctx &c, int k0, int tid, Fetch &f, size_t pr = 0) {
   const int last = c.end - 1;
   const int kk = tid >> 3, d0 = (tid & 7) * 16;
-  const uint32_t krow = static_cast<uint32_t>(k0 + kk <= last ? k0 + kk : last);
+  uint32_t krow = static_cast<uint32_t>(k0 + kk <= last ? k0 + kk : last);
   if (CACHED) {
-    const uint8_t *ks = c.kc_codes + (krow * (D * KBITS / 8) + static_cast<uint32_t>(d0 * KBITS / 8));
+    const uint8_t *kc_codes = c.kc_codes;
+    const float *kc_scale = c.kc_scale, *kc_zero = c.kc_zero;
+    if (PAGED) {  // pool row pr of the tile (looked up a step earlier), then rows within it
+      const int ts = tile_start(c, k0);
+      kc_codes += pr * (D * KBITS / 8);
+      kc_scale += pr * c.ng;
+      kc_zero += pr * c.ng;
+      krow -= static_cast<uint32_t>(ts);
+    }
+    const uint8_t *ks = kc_codes + (krow * (D * KBITS / 8) + static_cast<uint32_t>(d0 * KBITS / 8));
     if (KBITS == 4) {
       const uint2 w = *reinterpret_cast<const uint2 *>(ks);
       f.kw[0] = w.x; f.kw[1] = w.y;
@@ -252,9 +291,9 @@ __device__ inline void fetch_k(const Ctx &c, int k0, int tid, Fetch &f) {
     }
     const uint32_t km = krow * static_cast<uint32_t>(c.ng);
     const int gj = ((tid & 7) >> 1) < c.ng ? ((tid & 7) >> 1) : c.ng - 1;
-    f.kstep = c.kc_scale[km + static_cast<uint32_t>(d0 >> c.group_shift)];
-    f.kzero = c.kc_zero[km + static_cast<uint32_t>(d0 >> c.group_shift)];
-    f.gstep = c.kc_scale[km + static_cast<uint32_t>(gj)];
+    f.kstep = kc_scale[km + static_cast<uint32_t>(d0 >> c.group_shift)];
+    f.kzero = kc_zero[km + static_cast<uint32_t>(d0 >> c.group_shift)];
+    f.gstep = kc_scale[km + static_cast<uint32_t>(gj)];
   } else {
     const uint4 *ks = reinterpret_cast<const uint4 *>(c.k_cur + (krow * D + static_cast<uint32_t>(d0)));
     const uint4 a = ks[0], b = ks[1];
@@ -263,18 +302,27 @@ __device__ inline void fetch_k(const Ctx &c, int k0, int tid, Fetch &f) {
   }
 }
 
-template <bool CACHED, int VBITS>
-__device__ inline void fetch_v(const Ctx &c, int k0, int tid, int j, Fetch &f) {
+template <bool CACHED, int VBITS, bool PAGED = false>
+__device__ inline void fetch_v(const Ctx &c, int k0, int tid, int j, Fetch &f, size_t pr = 0) {
   const int last = c.end - 1;
   const int dq = tid & 15, kq = tid >> 4;
-  const uint32_t vrow = static_cast<uint32_t>(k0 + 2 * kq + j <= last ? k0 + 2 * kq + j : last);
+  uint32_t vrow = static_cast<uint32_t>(k0 + 2 * kq + j <= last ? k0 + 2 * kq + j : last);
   if (CACHED) {
-    const uint8_t *vs = c.vc_codes + (vrow * (D * VBITS / 8) + static_cast<uint32_t>(dq * VBITS));
+    const uint8_t *vc_codes = c.vc_codes;
+    const float *vc_scale = c.vc_scale, *vc_zero = c.vc_zero;
+    if (PAGED) {
+      const int ts = tile_start(c, k0);
+      vc_codes += pr * (D * VBITS / 8);
+      vc_scale += pr * c.ng;
+      vc_zero += pr * c.ng;
+      vrow -= static_cast<uint32_t>(ts);
+    }
+    const uint8_t *vs = vc_codes + (vrow * (D * VBITS / 8) + static_cast<uint32_t>(dq * VBITS));
     f.vw[j] = VBITS == 4 ? *reinterpret_cast<const uint32_t *>(vs)
                          : static_cast<uint32_t>(*reinterpret_cast<const uint16_t *>(vs));
     const uint32_t vm = vrow * static_cast<uint32_t>(c.ng) + static_cast<uint32_t>((8 * dq) >> c.group_shift);
-    f.vstep[j] = c.vc_scale[vm];
-    f.vzero[j] = c.vc_zero[vm];
+    f.vstep[j] = vc_scale[vm];
+    f.vzero[j] = vc_zero[vm];
   } else {
     const uint4 v = *reinterpret_cast<const uint4 *>(c.v_cur + (vrow * D + static_cast<uint32_t>(8 * dq)));
     f.vw[4 * j] = v.x; f.vw[4 * j + 1] = v.y; f.vw[4 * j + 2] = v.z; f.vw[4 * j + 3] = v.w;
@@ -491,10 +539,10 @@ __device__ inline uint4 lds16(const uint16_t *p) { return *reinterpret_cast<cons
 //         (LDS V buffer Vp), MASK for a ragged last tile of count keys;
 //   NEXT: dequantise tile t+1 from f into K buffer Kn / V buffer Vn, and
 //         fetch tile t+2 (rows clamp into the segment).
-template <bool CACHED, bool TAYLOR, int KBITS, int VBITS, bool QK, bool PREV, bool NEXT, bool MASK>
+template <bool CACHED, bool TAYLOR, int KBITS, int VBITS, bool QK, bool PREV, bool NEXT, bool MASK, bool PAGED>
 __device__ inline void tile_step(const Ctx &c, QState &qs, Soft &st, Fetch &f, const f32x16 (&s)[2],
                                  f32x16 (&sn)[2], const uint16_t *Kl, uint16_t *Kn, const uint16_t *Vp, uint16_t *Vn,
-                                 int k0_next2, int count, int tid) {
+                                 int k0_next2, int count, int tid, size_t &prn) {
   const int lane = tid & 63, qc = lane & 31, h = lane >> 5;
   const uint16_t *Kb = Kl + qc * KS + 8 * h;
   const uint16_t *Vb = Vp + qc * VS + 8 * (h ^ (qc >> 4));
@@ -547,12 +595,15 @@ __device__ inline void tile_step(const Ctx &c, QState &qs, Soft &st, Fetch &f, c
       if (NEXT) {
         if (j < NK) unpack_k_item<CACHED, TAYLOR, KBITS>(j, c, tid, f, Kn);
         else if (j >= 4 && j - 4 < kItemsV) unpack_v_item<CACHED, VBITS>(j - 4, tid, f, Vn, u);
-        else if (j == 9) fetch_k<CACHED, KBITS>(c, k0_next2, tid, f);
-        else if (j == 10 || j == 11) fetch_v<CACHED, VBITS>(c, k0_next2, tid, j - 10, f);
+        else if (j == 9) fetch_k<CACHED, KBITS, PAGED>(c, k0_next2, tid, f, prn);
+        else if (j == 10 || j == 11) fetch_v<CACHED, VBITS, PAGED>(c, k0_next2, tid, j - 10, f, prn);
       }
       KVQ_FENCE();
     }
   }
+  // paged: the pool row of the tile the next step fetches, looked up now so
+  // that the scalar load has long completed when that fetch needs it
+  if (CACHED && PAGED && NEXT) prn = tile_pool_row(c, tile_start(c, k0_next2 + BN));
 }
 
 #undef KVQ_FENCE
@@ -560,7 +611,7 @@ __device__ inline void tile_step(const Ctx &c, QState &qs, Soft &st, Fetch &f, c
 // One segment (cached or current keys) of the key range; ends with a barrier
 // so the next segment may reuse every LDS buffer.  CAUSAL (current keys
 // only) masks every tile with the lane's own count of visible keys.
-template <bool CACHED, bool TAYLOR, int KBITS, int VBITS, bool CAUSAL = false>
+template <bool CACHED, bool TAYLOR, int KBITS, int VBITS, bool CAUSAL = false, bool PAGED = false>
 __device__ inline void segment(const Ctx &c, QState &qs, Soft &st, uint16_t *Kl, uint16_t *Vl, int tid) {
   const int nt = c.end > c.beg ? (c.end - c.beg + BN - 1) / BN : 0;
   if (nt == 0) return;
@@ -570,49 +621,53 @@ __device__ inline void segment(const Ctx &c, QState &qs, Soft &st, uint16_t *Kl,
   Fetch f;
   {
     VWork u;
-    fetch_k<CACHED, KBITS>(c, c.beg, tid, f);
-    fetch_v<CACHED, VBITS>(c, c.beg, tid, 0, f);
-    fetch_v<CACHED, VBITS>(c, c.beg, tid, 1, f);
+    const size_t pr0 = CACHED && PAGED ? tile_pool_row(c, tile_start(c, c.beg)) : 0;
+    fetch_k<CACHED, KBITS, PAGED>(c, c.beg, tid, f, pr0);
+    fetch_v<CACHED, VBITS, PAGED>(c, c.beg, tid, 0, f, pr0);
+    fetch_v<CACHED, VBITS, PAGED>(c, c.beg, tid, 1, f, pr0);
 #pragma unroll
     for (int p = 0; p < kItemsK; ++p) unpack_k_item<CACHED, TAYLOR, KBITS>(p, c, tid, f, Kl);
 #pragma unroll
     for (int p = 0; p < kItemsV; ++p) unpack_v_item<CACHED, VBITS>(p, tid, f, Vl, u);
-    fetch_k<CACHED, KBITS>(c, c.beg + BN, tid, f);
-    fetch_v<CACHED, VBITS>(c, c.beg + BN, tid, 0, f);
-    fetch_v<CACHED, VBITS>(c, c.beg + BN, tid, 1, f);
+    const size_t pr1 = CACHED && PAGED ? tile_pool_row(c, tile_start(c, c.beg + BN)) : 0;
+    fetch_k<CACHED, KBITS, PAGED>(c, c.beg + BN, tid, f, pr1);
+    fetch_v<CACHED, VBITS, PAGED>(c, c.beg + BN, tid, 0, f, pr1);
+    fetch_v<CACHED, VBITS, PAGED>(c, c.beg + BN, tid, 1, f, pr1);
   }
   __syncthreads();
+  // paged: pool row of the tile the next fetch loads (tile 2)
+  size_t prn = CACHED && PAGED ? tile_pool_row(c, tile_start(c, c.beg + 2 * BN)) : 0;
   // Scores alternate between sa and sb: step t reads S_{t-1} from one and
   // writes S_t to the other.
   f32x16 sa[2], sb[2];
   // t = 0: S_0 only (and tile 1 into LDS when there is one)
   if (nt > 1)
-    tile_step<CACHED, TAYLOR, KBITS, VBITS, true, false, true, false>(c, qs, st, f, sb, sa, Kl, Kl + KBUF, Vl,
-                                                                      Vl + VBUF, c.beg + 2 * BN, BN, tid);
+    tile_step<CACHED, TAYLOR, KBITS, VBITS, true, false, true, false, PAGED>(c, qs, st, f, sb, sa, Kl, Kl + KBUF, Vl,
+                                                                      Vl + VBUF, c.beg + 2 * BN, BN, tid, prn);
   else
-    tile_step<CACHED, TAYLOR, KBITS, VBITS, true, false, false, false>(c, qs, st, f, sb, sa, Kl, Kl + KBUF, Vl,
-                                                                       Vl + VBUF, 0, BN, tid);
+    tile_step<CACHED, TAYLOR, KBITS, VBITS, true, false, false, false, PAGED>(c, qs, st, f, sb, sa, Kl, Kl + KBUF, Vl,
+                                                                       Vl + VBUF, 0, BN, tid, prn);
   __syncthreads();
   // steady state: S_t, P_{t-1} V_{t-1}, tile t+1 into LDS; two steps per trip
   int vb = 0;  // V buffer of tile t-1
   int t = 1;
   for (; t + 1 < nt - 1; t += 2) {
     const int v1 = vb + 1 < NVBUF ? vb + 1 : 0, v2 = v1 + 1 < NVBUF ? v1 + 1 : 0, v3 = vb;
-    tile_step<CACHED, TAYLOR, KBITS, VBITS, true, true, true, CAUSAL>(c, qs, st, f, sa, sb, Kl + KBUF, Kl,
+    tile_step<CACHED, TAYLOR, KBITS, VBITS, true, true, true, CAUSAL, PAGED>(c, qs, st, f, sa, sb, Kl + KBUF, Kl,
                                                                       Vl + vb * VBUF, Vl + v2 * VBUF,
-                                                                      c.beg + (t + 2) * BN, cnt(t - 1, BN), tid);
+                                                                      c.beg + (t + 2) * BN, cnt(t - 1, BN), tid, prn);
     __syncthreads();
-    tile_step<CACHED, TAYLOR, KBITS, VBITS, true, true, true, CAUSAL>(c, qs, st, f, sb, sa, Kl, Kl + KBUF,
+    tile_step<CACHED, TAYLOR, KBITS, VBITS, true, true, true, CAUSAL, PAGED>(c, qs, st, f, sb, sa, Kl, Kl + KBUF,
                                                                       Vl + v1 * VBUF, Vl + v3 * VBUF,
-                                                                      c.beg + (t + 3) * BN, cnt(t, BN), tid);
+                                                                      c.beg + (t + 3) * BN, cnt(t, BN), tid, prn);
     __syncthreads();
     vb = v2;
   }
   if (t < nt - 1) {  // one more steady step (t odd: K buffer 1, S_t into sb)
     const int vn = vb + 2 < NVBUF ? vb + 2 : vb + 2 - NVBUF;
-    tile_step<CACHED, TAYLOR, KBITS, VBITS, true, true, true, CAUSAL>(c, qs, st, f, sa, sb, Kl + KBUF, Kl,
+    tile_step<CACHED, TAYLOR, KBITS, VBITS, true, true, true, CAUSAL, PAGED>(c, qs, st, f, sa, sb, Kl + KBUF, Kl,
                                                                       Vl + vb * VBUF, Vl + vn * VBUF,
-                                                                      c.beg + (t + 2) * BN, cnt(t - 1, BN), tid);
+                                                                      c.beg + (t + 2) * BN, cnt(t - 1, BN), tid, prn);
     __syncthreads();
     vb = vb + 1 < NVBUF ? vb + 1 : 0;
     ++t;
@@ -621,24 +676,24 @@ __device__ inline void segment(const Ctx &c, QState &qs, Soft &st, uint16_t *Kl,
   }
   // here t = nt - 1 (nt > 1) with S_{t-1} in sa, or nt == 1 with S_0 in sa
   if (nt > 1) {  // S_{nt-1}, P_{nt-2} V_{nt-2}
-    tile_step<CACHED, TAYLOR, KBITS, VBITS, true, true, false, CAUSAL>(c, qs, st, f, sa, sb,
+    tile_step<CACHED, TAYLOR, KBITS, VBITS, true, true, false, CAUSAL, PAGED>(c, qs, st, f, sa, sb,
                                                                        Kl + ((nt - 1) & 1) * KBUF, Kl, Vl + vb * VBUF,
-                                                                       Vl, 0, cnt(nt - 2, BN), tid);
+                                                                       Vl, 0, cnt(nt - 2, BN), tid, prn);
     vb = vb + 1 < NVBUF ? vb + 1 : 0;
     sa[0] = sb[0];
     sa[1] = sb[1];
   }
   // drain: P_{nt-1} V_{nt-1}
   if (tail == BN && !CAUSAL)
-    tile_step<CACHED, TAYLOR, KBITS, VBITS, false, true, false, false>(c, qs, st, f, sa, sb, Kl, Kl,
-                                                                       Vl + vb * VBUF, Vl, 0, BN, tid);
+    tile_step<CACHED, TAYLOR, KBITS, VBITS, false, true, false, false, PAGED>(c, qs, st, f, sa, sb, Kl, Kl,
+                                                                       Vl + vb * VBUF, Vl, 0, BN, tid, prn);
   else
-    tile_step<CACHED, TAYLOR, KBITS, VBITS, false, true, false, true>(c, qs, st, f, sa, sb, Kl, Kl, Vl + vb * VBUF,
-                                                                      Vl, 0, cnt(nt - 1, tail), tid);
+    tile_step<CACHED, TAYLOR, KBITS, VBITS, false, true, false, true, PAGED>(c, qs, st, f, sa, sb, Kl, Kl, Vl + vb * VBUF,
+                                                                      Vl, 0, cnt(nt - 1, tail), tid, prn);
   __syncthreads();
 }
 
-template <int KBITS, int VBITS, bool TAYLOR, bool CAUSAL>
+template <int KBITS, int VBITS, bool TAYLOR, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(THREADS, 1) void attn_fast_kernel(AttnLaunch p, int32_t group_shift,
                                                                 int64_t rows_per_kvhead, int32_t row_blocks,
                                                                 const float *kpart, int32_t nsplit,
@@ -699,8 +754,13 @@ __global__ __launch_bounds__(THREADS, 1) void attn_fast_kernel(AttnLaunch p, int
   c.group_shift = group_shift;
   c.kscale = ldexpf(p.tau * kLog2e, -ek);
   c.kmask = opaque_u32(kCodeMask<KBITS>);
+  c.layout = p.layout;
+  c.cap = p.cap;
+  c.H = p.Hkv;
+  c.b = b;
+  c.hk = hk;
   if (p.Nc > 0) {
-    const int64_t hrow = bkv * p.cap;  // first cache row of this head
+    const int64_t hrow = PAGED ? 0 : bkv * p.cap;  // first cache row of this head (paged: the pool)
     c.kc_codes = p.kc_codes + hrow * (D * KBITS / 8);
     c.vc_codes = p.vc_codes + hrow * (D * VBITS / 8);
     c.kc_scale = p.kc_scale + hrow * ng;
@@ -713,7 +773,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_fast_kernel(AttnLaunch p, int
   const int t0 = static_cast<int>(split * (tc + tu) / nsplit), t1 = static_cast<int>((split + 1) * (tc + tu) / nsplit);
   c.beg = min(t0, tc) * BN;
   c.end = min(min(t1, tc) * BN, static_cast<int>(p.Nc));
-  segment<true, TAYLOR, KBITS, VBITS>(c, qs, st, Kl, Vl, tid);
+  segment<true, TAYLOR, KBITS, VBITS, false, PAGED>(c, qs, st, Kl, Vl, tid);
   if (p.Ncur > 0) {
     c.k_cur = p.k_cur + bkv * p.Ncur * D;
     c.v_cur = p.v_cur + bkv * p.Ncur * D;
@@ -729,7 +789,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_fast_kernel(AttnLaunch p, int
     const int64_t jmax = r0 / p.Nq == r1 / p.Nq ? r1 % p.Nq : p.Nq - 1;
     c.end = static_cast<int>(min(static_cast<int64_t>(c.end), jmax + p.Ncur - p.Nq + 1));
   }
-  segment<false, TAYLOR, KBITS, VBITS, CAUSAL>(c, qs, st, Kl, Vl, tid);
+  segment<false, TAYLOR, KBITS, VBITS, CAUSAL, PAGED>(c, qs, st, Kl, Vl, tid);
 
   const float l_tot = st.l + __shfl_xor(st.l, 32, 64);
   if (!row_ok) return;
@@ -769,8 +829,9 @@ hipError_t launch_bits(const AttnLaunch &p, hipStream_t stream) {
                                            (nsplit > 1 ? short_path_workspace_bytes(p.B, p.Hq, p.Nq, p.d, nsplit) : 0));
   launch_key_scale(p, stream, kpart);
   const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(nsplit) * row_blocks * p.B * p.Hkv));
-  auto kernel = p.corr == KV_CORR_TAYLOR ? attn_fast_kernel<KB, VB, true, KVQ_FAST_CAUSAL != 0>
-                                         : attn_fast_kernel<KB, VB, false, KVQ_FAST_CAUSAL != 0>;
+  constexpr bool CAUSAL = KVQ_FAST_CAUSAL != 0, PAGED = KVQ_FAST_PAGED != 0;
+  auto kernel = p.corr == KV_CORR_TAYLOR ? attn_fast_kernel<KB, VB, true, CAUSAL, PAGED>
+                                         : attn_fast_kernel<KB, VB, false, CAUSAL, PAGED>;
   kernel<<<grid, dim3(THREADS), 0, stream>>>(p, gshift, rows, row_blocks, kpart, nsplit, partials);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
@@ -779,8 +840,14 @@ hipError_t launch_bits(const AttnLaunch &p, hipStream_t stream) {
 
 }  // namespace
 
-#if KVQ_FAST_CAUSAL
+#if KVQ_FAST_PAGED || KVQ_FAST_CAUSAL
+#if KVQ_FAST_PAGED && KVQ_FAST_CAUSAL
+hipError_t launch_attention_fast_paged_causal(const AttnLaunch &p, hipStream_t stream) {
+#elif KVQ_FAST_PAGED
+hipError_t launch_attention_fast_paged(const AttnLaunch &p, hipStream_t stream) {
+#else
 hipError_t launch_attention_fast_causal(const AttnLaunch &p, hipStream_t stream) {
+#endif
   const int kb = p.Nc > 0 ? p.kbits : 2, vb = p.Nc > 0 ? p.vbits : 2;
   if (kb == 2 && vb == 2) return launch_bits<2, 2>(p, stream);
   if (kb == 2 && vb == 4) return launch_bits<2, 4>(p, stream);
@@ -828,6 +895,8 @@ int fast_path_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nc,
 }
 
 hipError_t launch_attention_fast(const AttnLaunch &p, hipStream_t stream) {
+  if (p.layout.page_table)
+    return p.causal ? launch_attention_fast_paged_causal(p, stream) : launch_attention_fast_paged(p, stream);
   if (p.causal) return launch_attention_fast_causal(p, stream);
   const int kb = p.Nc > 0 ? p.kbits : 2, vb = p.Nc > 0 ? p.vbits : 2;
   if (kb == 2 && vb == 2) return launch_bits<2, 2>(p, stream);

@@ -1,0 +1,4 @@
+// Paged-cache instances of the throughput kernel (no mask), built in their
+// own translation unit; the kernel itself is in attention_fast.hip.
+#define KVQ_FAST_PAGED 1
+#include "attention_fast.hip"

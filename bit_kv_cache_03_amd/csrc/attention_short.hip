@@ -28,10 +28,19 @@
 // dimension, keys in the permuted order of the P operand) into LDS, fetch
 // the next block, S^T = K Q^T (8 fp16 MFMA + 1 correction step), mask the
 // ragged block, lazy max, exponentials, O^T += V^T P^T (8 fp16 MFMA).
+//
+// Paged caches: the instances for the paged layout are built from this file
+// in a translation unit of their own (attention_short_paged.hip defines
+// KVQ_SHORT_PAGED to 1), so that they cannot change how the contiguous ones
+// are compiled.
 #include <math.h>
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
+
+#ifndef KVQ_SHORT_PAGED
+#define KVQ_SHORT_PAGED 0
+#endif
 
 namespace kvq {
 namespace {
@@ -71,6 +80,8 @@ struct Ctx {
   const float *kc_scale, *kc_zero, *vc_scale, *vc_zero;
   const uint16_t *k_cur, *v_cur;
   int nc, ncur;     // segment lengths
+  CacheLayout layout;         // paged caches: the pool rows of (b, hk)
+  int64_t cap, H, b, hk;
   uint32_t kmask;   // code mask of magic8 (vector register)
   uint32_t vmask0, vmask1;  // value code fields of unpack_v_cached (vector registers)
 };
@@ -135,22 +146,34 @@ __device__ inline Lanes lane_offsets(int lane) {
   return o;
 }
 
+// First row of the cached block at token k0: relative to the head's first
+// row (contiguous: the context's pointers are at that row), or the pool row
+// (paged: the context's pointers are at the pool; a 32-key block never
+// crosses a page).
+template <bool PAGED>
+__device__ inline size_t block_row(const Ctx &c, int k0) {
+  if (!PAGED) return static_cast<size_t>(k0);
+  return static_cast<size_t>(c.layout.row(c.cap, c.H, c.b, c.hk, k0));
+}
+
 // Loads one cached block (rows [k0, k0 + 32)); rows at or past the segment
-// end read as zero (their scores are masked).
-template <int KBITS, int VBITS, int NG>
-__device__ inline void fetch_cached(const Ctx &c, int k0, const Lanes &o, int h, Fetch &f) {
+// end read as zero (their scores are masked).  Paged: the buffer range stops
+// at the block's end, inside its page.
+template <int KBITS, int VBITS, int NG, bool PAGED>
+__device__ inline void fetch_cached(const Ctx &c, int k0, const Lanes &o, int h, Fetch &f, size_t pool_row = 0) {
   constexpr uint32_t KROW = D * KBITS / 8, VROW = D * VBITS / 8;
-  const uint32_t rows = static_cast<uint32_t>(c.nc - k0);
+  const uint32_t rows = static_cast<uint32_t>(PAGED ? min(c.nc - k0, BK) : c.nc - k0);
+  const size_t r0 = PAGED ? pool_row : block_row<false>(c, k0);  // paged: looked up a block earlier
   {
-    const Buf kc = buffer_at(c.kc_codes + static_cast<size_t>(k0) * KROW, rows * KROW);
+    const Buf kc = buffer_at(c.kc_codes + r0 * KROW, rows * KROW);
     const u32x4 a = ld128(kc, o.kc);
     f.kw[0] = a.x; f.kw[1] = a.y; f.kw[2] = a.z; f.kw[3] = a.w;
     if (KBITS == 4) {
       const u32x4 b = ld128(kc, o.kc + 16);
       f.kw[4] = b.x; f.kw[5] = b.y; f.kw[6] = b.z; f.kw[7] = b.w;
     }
-    const Buf ks = buffer_at(c.kc_scale + static_cast<size_t>(k0) * NG, rows * NG * 4);
-    const Buf kz = buffer_at(c.kc_zero + static_cast<size_t>(k0) * NG, rows * NG * 4);
+    const Buf ks = buffer_at(c.kc_scale + r0 * NG, rows * NG * 4);
+    const Buf kz = buffer_at(c.kc_zero + r0 * NG, rows * NG * 4);
     // groups of d = 64h + 32j (kstep, kzero) and groups 2h + j (gstep; only
     // those below NG are used)
     if (NG == 1) {
@@ -173,9 +196,9 @@ __device__ inline void fetch_cached(const Ctx &c, int k0, const Lanes &o, int h,
     }
   }
   {
-    const Buf vc = buffer_at(c.vc_codes + static_cast<size_t>(k0) * VROW, rows * VROW);
-    const Buf vs = buffer_at(c.vc_scale + static_cast<size_t>(k0) * NG, rows * NG * 4);
-    const Buf vz = buffer_at(c.vc_zero + static_cast<size_t>(k0) * NG, rows * NG * 4);
+    const Buf vc = buffer_at(c.vc_codes + r0 * VROW, rows * VROW);
+    const Buf vs = buffer_at(c.vc_scale + r0 * NG, rows * NG * 4);
+    const Buf vz = buffer_at(c.vc_zero + r0 * NG, rows * NG * 4);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (VBITS == 4) {
@@ -463,7 +486,7 @@ __device__ inline void block_compute(const f16x8 (&k)[8], bf16x8 kext, const uin
     }
 }
 
-template <int KBITS, int VBITS, bool TAYLOR, int NG, bool CAUSAL>
+template <int KBITS, int VBITS, bool TAYLOR, int NG, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, int64_t rows_per_kvhead,
                                                                 int32_t row_groups, int32_t nsplit, float *ws) {
   __shared__ __attribute__((aligned(16))) uint16_t L[LDS_BYTES / 2];
@@ -507,8 +530,13 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
   c.kmask = opaque_u32(kCodeMask<KBITS>);
   c.vmask0 = opaque_u32(VBITS == 4 ? 0x000f000fu : 0x00030003u);
   c.vmask1 = opaque_u32(VBITS == 4 ? 0x00f000f0u : 0x000c000cu);
+  c.layout = p.layout;
+  c.cap = p.cap;
+  c.H = p.Hkv;
+  c.b = b;
+  c.hk = hk;
   if (p.Nc > 0) {
-    const int64_t hrow = bkv * p.cap;
+    const int64_t hrow = PAGED ? 0 : bkv * p.cap;  // paged: the pointers stay at the pool
     c.kc_codes = p.kc_codes + hrow * (D * KBITS / 8);
     c.vc_codes = p.vc_codes + hrow * (D * VBITS / 8);
     c.kc_scale = p.kc_scale + hrow * ng;
@@ -546,15 +574,19 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
   f16x8 kreg[8];
   bf16x8 kext = {};
   Fetch f;
-  if (blk < cend) fetch_cached<KBITS, VBITS, NG>(c, blk * BK, lo, h, f);
+  if (blk < cend) fetch_cached<KBITS, VBITS, NG, PAGED>(c, blk * BK, lo, h, f, block_row<PAGED>(c, blk * BK));
+  // paged: the pool row of the next block to fetch, looked up one block ahead
+  // so that its scalar load has completed when the fetch needs it
+  size_t prn = PAGED && blk + WAVES < cend ? block_row<PAGED>(c, (blk + WAVES) * BK) : 0;
   for (; blk < cend; blk += WAVES) {
     const int k0 = blk * BK;
     const int count = c.nc - k0 < BK ? c.nc - k0 : BK;
     sc.update(k_bound<KBITS>(f), v_bound<VBITS>(f), st.alpha);
     unpack_k_cached<TAYLOR, KBITS, NG>(c, lane, f, sc.kscale, kreg, kext);
     unpack_v_cached<VBITS>(c, lane, f, sc.vscale, Vt);
-    if (blk + WAVES < cend) fetch_cached<KBITS, VBITS, NG>(c, (blk + WAVES) * BK, lo, h, f);
+    if (blk + WAVES < cend) fetch_cached<KBITS, VBITS, NG, PAGED>(c, (blk + WAVES) * BK, lo, h, f, prn);
     block_compute<TAYLOR>(kreg, kext, Vt, q, qext, count, sc.alpha, sc.ev, lane, st);
+    if (PAGED && blk + 2 * WAVES < cend) prn = block_row<PAGED>(c, (blk + 2 * WAVES) * BK);
   }
   for (; blk < bend; blk += WAVES) {
     const int k0 = (blk - nbc) * BK;
@@ -630,9 +662,11 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
 template <int KB, int VB, int NG>
 void launch_kernel(const AttnLaunch &p, hipStream_t stream, dim3 grid, int64_t rows, int32_t row_groups,
                    float *partials) {
-  auto kernel = p.corr == KV_CORR_TAYLOR
-                    ? (p.causal ? attn_short_kernel<KB, VB, true, NG, true> : attn_short_kernel<KB, VB, true, NG, false>)
-                    : (p.causal ? attn_short_kernel<KB, VB, false, NG, true> : attn_short_kernel<KB, VB, false, NG, false>);
+  constexpr bool PG = KVQ_SHORT_PAGED != 0;
+  auto kernel = p.corr == KV_CORR_TAYLOR ? (p.causal ? attn_short_kernel<KB, VB, true, NG, true, PG>
+                                                     : attn_short_kernel<KB, VB, true, NG, false, PG>)
+                                         : (p.causal ? attn_short_kernel<KB, VB, false, NG, true, PG>
+                                                     : attn_short_kernel<KB, VB, false, NG, false, PG>);
   kernel<<<grid, dim3(THREADS), 0, stream>>>(p, rows, row_groups, p.splits, partials);
 }
 
@@ -656,6 +690,15 @@ hipError_t launch_bits(const AttnLaunch &p, hipStream_t stream) {
 
 }  // namespace
 
+#if KVQ_SHORT_PAGED
+hipError_t launch_attention_short_fast_paged(const AttnLaunch &p, hipStream_t stream) {
+  const int kb = p.Nc > 0 ? p.kbits : 2, vb = p.Nc > 0 ? p.vbits : 2;
+  if (kb == 2 && vb == 2) return launch_bits<2, 2>(p, stream);
+  if (kb == 2 && vb == 4) return launch_bits<2, 4>(p, stream);
+  if (kb == 4 && vb == 2) return launch_bits<4, 2>(p, stream);
+  return launch_bits<4, 4>(p, stream);
+}
+#else
 bool short_fast_supported(int32_t d, int corr) { return d == D && corr != KV_CORR_EXACT; }
 
 int short_fast_splits(int64_t B, int64_t Hkv, int64_t rows_per_kvhead, int64_t Nc, int64_t Ncur, int cu_count) {
@@ -673,11 +716,13 @@ int short_fast_splits(int64_t B, int64_t Hkv, int64_t rows_per_kvhead, int64_t N
 }
 
 hipError_t launch_attention_short_fast(const AttnLaunch &p, hipStream_t stream) {
+  if (p.layout.page_table) return launch_attention_short_fast_paged(p, stream);
   const int kb = p.Nc > 0 ? p.kbits : 2, vb = p.Nc > 0 ? p.vbits : 2;
   if (kb == 2 && vb == 2) return launch_bits<2, 2>(p, stream);
   if (kb == 2 && vb == 4) return launch_bits<2, 4>(p, stream);
   if (kb == 4 && vb == 2) return launch_bits<4, 2>(p, stream);
   return launch_bits<4, 4>(p, stream);
 }
+#endif
 
 }  // namespace kvq

@@ -194,7 +194,7 @@ __global__ __launch_bounds__(THREADS) void attn_diag_kernel(DiagLaunch p, int32_
       const bool ok = key < count;
       uint32_t hi[DPT / 2];
       if (cached) {
-        const int64_t row = bkv * p.cap + k0 + (ok ? key : 0);
+        const int64_t row = p.layout.row(p.cap, p.Hkv, b, hk, k0 + (ok ? key : 0));  // cache row of the key
         const int g = d0 >> group_shift;
         const float st = ok ? p.kc_scale[row * ng + g] : 0.f;
         const float zp = ok ? p.kc_zero[row * ng + g] : 0.f;

@@ -11,11 +11,15 @@ namespace {
 
 using kvq::AttnLaunch;
 
-constexpr int32_t kAbiVersion = 3;
+constexpr int32_t kAbiVersion = 4;
 constexpr int32_t kMaxSplits = 1024;  // grid z extent of the split path
 constexpr int64_t kMaxTokensPerHead = int64_t(1) << 23;  // 8M tokens: 32-bit in-head offsets
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Page sizes of the paged layout: powers of two from 64 tokens (every 64-key
+// tile in one page; shifts and masks in the kernels).
+bool page_size_ok(int32_t ps) { return ps >= 64 && ps <= (1 << 23) && (ps & (ps - 1)) == 0; }
 
 bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
 
@@ -38,7 +42,7 @@ bool mul_ok(int64_t a, int64_t b, int64_t *out) {
   return true;
 }
 
-kv_status check_qtensor(const kv_qtensor *t, int32_t d, int64_t need_rows) {
+kv_status check_qtensor(const kv_qtensor *t, int32_t d, int64_t need_rows, int64_t B) {
   if (!t) return KV_ERR_NULL;
   if (!t->codes || !t->scale || !t->zero) return KV_ERR_NULL;
   if (t->bits != 2 && t->bits != 4) return KV_ERR_UNSUPPORTED;
@@ -46,7 +50,30 @@ kv_status check_qtensor(const kv_qtensor *t, int32_t d, int64_t need_rows) {
   if (t->cap < need_rows || t->cap < 0) return KV_ERR_SHAPE;
   if (t->cap > kMaxTokensPerHead) return KV_ERR_UNSUPPORTED;
   if (!aligned16(t->codes) || !aligned16(t->scale) || !aligned16(t->zero)) return KV_ERR_ALIGN;
+  if (t->page_table) {
+    if (!page_size_ok(t->page_size) || t->cap % t->page_size != 0) return KV_ERR_SHAPE;
+    if (t->num_pages < 1) return KV_ERR_SHAPE;
+    if (B * (t->cap / t->page_size) > INT32_MAX) return KV_ERR_SHAPE;  // page-table indices are 32-bit
+    if ((reinterpret_cast<uintptr_t>(t->page_table) & 3u) != 0) return KV_ERR_ALIGN;
+  } else if (t->page_size != 0 || t->num_pages != 0) {
+    return KV_ERR_SHAPE;
+  }
   return KV_OK;
+}
+
+kvq::CacheLayout layout_of(const kv_qtensor *t) {
+  if (!t->page_table) return kvq::CacheLayout{nullptr, 0, 0};
+  return kvq::CacheLayout{t->page_table, __builtin_ctz(static_cast<unsigned>(t->page_size)),
+                          static_cast<int32_t>(t->cap / t->page_size)};
+}
+
+// Token rows a cache tensor of B x H heads spans in memory (its pool when paged).
+int64_t tensor_rows(const kv_qtensor *t, int64_t B, int64_t H) {
+  return t->page_table ? static_cast<int64_t>(t->num_pages) * H * t->page_size : B * H * t->cap;
+}
+
+bool same_layout(const kv_qtensor *a, const kv_qtensor *b) {
+  return a->page_table == b->page_table && a->page_size == b->page_size;
 }
 
 bool debug_log() {
@@ -100,12 +127,13 @@ kv_status validate_attention(const kv_attn_args *a) {
     if (!aligned16(a->k_cur) || !aligned16(a->v_cur)) return KV_ERR_ALIGN;
   }
   if (a->Nc > 0) {
-    kv_status s = check_qtensor(a->k_cache, a->d, a->Nc);
+    kv_status s = check_qtensor(a->k_cache, a->d, a->Nc, a->B);
     if (s != KV_OK) return s;
-    s = check_qtensor(a->v_cache, a->d, a->Nc);
+    s = check_qtensor(a->v_cache, a->d, a->Nc, a->B);
     if (s != KV_OK) return s;
     if (a->k_cache->group != a->v_cache->group) return KV_ERR_UNSUPPORTED;
     if (a->k_cache->cap != a->v_cache->cap) return KV_ERR_SHAPE;
+    if (!same_layout(a->k_cache, a->v_cache)) return KV_ERR_UNSUPPORTED;
   }
   // the output must not overlap any input
   const size_t out_b = static_cast<size_t>(nq_el) * 2;
@@ -116,7 +144,7 @@ kv_status validate_attention(const kv_attn_args *a) {
   if (a->Nc > 0) {
     const kv_qtensor *ts[2] = {a->k_cache, a->v_cache};
     for (const kv_qtensor *c : ts) {
-      const size_t rows = static_cast<size_t>(a->B * a->Hkv * c->cap);
+      const size_t rows = static_cast<size_t>(tensor_rows(c, a->B, a->Hkv));
       const size_t ng = static_cast<size_t>(a->d / c->group);
       if (overlaps(a->out, out_b, c->codes, rows * static_cast<size_t>(a->d * c->bits / 8)) ||
           overlaps(a->out, out_b, c->scale, rows * ng * 4) || overlaps(a->out, out_b, c->zero, rows * ng * 4))
@@ -150,7 +178,7 @@ kv_status validate_diagnostics(const kv_diag_args *a) {
   }
   if (a->Nc > 0) {
     if (!a->k_ref) return KV_ERR_NULL;
-    const kv_status s = check_qtensor(a->k_cache, a->d, a->Nc);
+    const kv_status s = check_qtensor(a->k_cache, a->d, a->Nc, a->B);
     if (s != KV_OK) return s;
     if (!aligned16(a->k_ref)) return KV_ERR_ALIGN;
   }
@@ -160,7 +188,7 @@ kv_status validate_diagnostics(const kv_diag_args *a) {
   if (a->Ncur > 0 && overlaps(a->out, out_b, a->k_cur, static_cast<size_t>(ncur_el) * 2)) return KV_ERR_ALIAS;
   if (a->Nc > 0) {
     const kv_qtensor *c = a->k_cache;
-    const size_t rows = static_cast<size_t>(a->B * a->Hkv * c->cap);
+    const size_t rows = static_cast<size_t>(tensor_rows(c, a->B, a->Hkv));
     const size_t ng = static_cast<size_t>(a->d / c->group);
     if (overlaps(a->out, out_b, a->k_ref, static_cast<size_t>(nc_el) * 2) ||
         overlaps(a->out, out_b, c->codes, rows * static_cast<size_t>(a->d * c->bits / 8)) ||
@@ -225,13 +253,22 @@ kv_status kv_quantize(const void *x, kv_dtype xdt, int64_t B, int64_t H, int64_t
   if (dst->bits != 2 && dst->bits != 4) return KV_ERR_UNSUPPORTED;
   if (!group_ok(dst->group, d)) return KV_ERR_UNSUPPORTED;
   if (dst->cap < 0 || tok_offset > dst->cap || N > dst->cap - tok_offset) return KV_ERR_SHAPE;
+  if (dst->page_table) {
+    if (!page_size_ok(dst->page_size) || dst->cap % dst->page_size != 0) return KV_ERR_SHAPE;
+    if (dst->num_pages < 1) return KV_ERR_SHAPE;
+    if (B * (dst->cap / dst->page_size) > INT32_MAX) return KV_ERR_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(dst->page_table) & 3u) != 0) return KV_ERR_ALIGN;
+  } else if (dst->page_size != 0 || dst->num_pages != 0) {
+    return KV_ERR_SHAPE;
+  }
   int64_t t = 0;
   if (!mul_ok(B, H, &t) || !mul_ok(t, N, &t) || !mul_ok(t, d, &t) || t > (int64_t(1) << 40)) return KV_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(dst->codes) || !aligned16(dst->scale) || !aligned16(dst->zero))
     return KV_ERR_ALIGN;
   if (N == 0) return KV_OK;
   kvq::QuantizeLaunch p{x, static_cast<int>(xdt), B, H, N, d, dst->codes, dst->scale, dst->zero,
-                        dst->bits, dst->group, dst->cap, tok_offset};
+                        dst->bits, dst->group, dst->cap, tok_offset,
+                        layout_of(dst)};
   return kvq::launch_quantize(p, static_cast<hipStream_t>(stream)) == hipSuccess ? KV_OK : KV_ERR_HIP;
 }
 
@@ -257,6 +294,7 @@ kv_status kv_attention_corrected(const kv_attn_args *a, void *stream) {
     p.kc_codes = a->k_cache->codes; p.kc_scale = a->k_cache->scale; p.kc_zero = a->k_cache->zero;
     p.vc_codes = a->v_cache->codes; p.vc_scale = a->v_cache->scale; p.vc_zero = a->v_cache->zero;
     p.kbits = a->k_cache->bits; p.vbits = a->v_cache->bits; p.group = a->k_cache->group; p.cap = a->k_cache->cap;
+    p.layout = layout_of(a->k_cache);
   } else {
     p.kbits = 2; p.vbits = 2; p.group = a->d; p.cap = 0;
   }
@@ -285,6 +323,7 @@ kv_status kv_attention_diagnostics(const kv_diag_args *a, void *stream) {
   if (a->Nc > 0) {
     p.kc_codes = a->k_cache->codes; p.kc_scale = a->k_cache->scale; p.kc_zero = a->k_cache->zero;
     p.kbits = a->k_cache->bits; p.group = a->k_cache->group; p.cap = a->k_cache->cap;
+    p.layout = layout_of(a->k_cache);
   } else {
     p.kbits = 2; p.group = a->d; p.cap = 0;
   }

@@ -10,6 +10,23 @@
 
 namespace kvq {
 
+// Cache layout shared by a launch's cache tensors: contiguous, or paged
+// (see kv_qtensor; the page size is a power of two).  Physical row of token
+// t of head h of sequence b in a tensor of H heads:
+//   contiguous: (b*H + h)*cap + t
+//   paged:      (table[b*(cap/P) + t/P]*H + h)*P + t%P
+// A tile of 64 tokens starting at a multiple of 64 lies in one page.
+struct CacheLayout {
+  const int32_t *page_table;  // nullptr: contiguous
+  int32_t page_shift;         // log2(page size)
+  int32_t pages_per_seq;      // cap / page size
+  __host__ __device__ int64_t row(int64_t cap, int64_t H, int64_t b, int64_t h, int64_t t) const {
+    if (!page_table) return (b * H + h) * cap + t;
+    const int64_t page = page_table[b * pages_per_seq + (t >> page_shift)];
+    return ((page * H + h) << page_shift) + (t & ((int64_t(1) << page_shift) - 1));
+  }
+};
+
 // Everything a quantize launch needs, already validated by the host.
 struct QuantizeLaunch {
   const void *x;
@@ -21,6 +38,7 @@ struct QuantizeLaunch {
   float *zero;
   int32_t bits, group;
   int64_t cap, off;
+  CacheLayout layout;
 };
 
 // Everything an attention launch needs, already validated by the host.
@@ -33,6 +51,7 @@ struct AttnLaunch {
   const float *kc_scale, *kc_zero, *vc_scale, *vc_zero;
   int32_t kbits, vbits, group;
   int64_t cap;
+  CacheLayout layout;  // of both caches
   float tau;   // resolved softmax scale
   int corr;    // kv_corr
   int causal;  // 1: current key i visible to query row j only if i <= j + Ncur - Nq
@@ -55,8 +74,12 @@ bool fast_path_supported(const AttnLaunch &p);
 size_t fast_path_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int splits);
 int fast_path_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nc, int64_t Ncur, int cu_count);
 hipError_t launch_attention_fast(const AttnLaunch &p, hipStream_t stream);
-// The same with the causal mask (built in attention_fast_causal.hip).
+// The same with the causal mask (built in attention_fast_causal.hip), over
+// a paged cache (attention_fast_paged.hip), and both
+// (attention_fast_paged_causal.hip).
 hipError_t launch_attention_fast_causal(const AttnLaunch &p, hipStream_t stream);
+hipError_t launch_attention_fast_paged(const AttnLaunch &p, hipStream_t stream);
+hipError_t launch_attention_fast_paged_causal(const AttnLaunch &p, hipStream_t stream);
 // Pre-pass of the throughput kernel: per (b, KV head), 32 partial bounds of
 // |key| (dequantised cache and current chunk) and of |query|, from which the
 // kernel takes the exponent that balances its fp16 key and query operands.
@@ -73,6 +96,8 @@ hipError_t launch_combine(const float *ws, uint16_t *out, int64_t nrows, int spl
 bool short_fast_supported(int32_t d, int corr);
 int short_fast_splits(int64_t B, int64_t Hkv, int64_t rows_per_kvhead, int64_t Nc, int64_t Ncur, int cu_count);
 hipError_t launch_attention_short_fast(const AttnLaunch &p, hipStream_t stream);
+// The same over a paged cache (built in attention_short_paged.hip).
+hipError_t launch_attention_short_fast_paged(const AttnLaunch &p, hipStream_t stream);
 
 // Everything a diagnostics launch needs, already validated by the host.
 struct DiagLaunch {
@@ -83,6 +108,7 @@ struct DiagLaunch {
   const float *kc_scale, *kc_zero;
   int32_t kbits, group;
   int64_t cap;
+  CacheLayout layout;
   float tau;   // resolved softmax scale
   int corr;    // kv_corr
   int causal;

@@ -61,7 +61,7 @@ template <typename T, int BITS, int LANES>
 __global__ __launch_bounds__(kThreads) void quantize_pack(
     const T *__restrict__ x, int64_t total_lanes, int32_t lanes_per_row, int64_t N,
     uint8_t *__restrict__ codes, float *__restrict__ scale, float *__restrict__ zero,
-    int64_t cap, int64_t off, int32_t groups_per_row) {
+    int64_t cap, int64_t off, int32_t groups_per_row, CacheLayout layout, int64_t H) {
 #pragma clang fp contract(off)
   constexpr int TOP = (1 << BITS) - 1;
   const int64_t gl = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void quantize_pack(
   if (!live) return;
   const int64_t bh = row / N;
   const int64_t n = row - bh * N;
-  const int64_t orow = bh * cap + off + n;
+  const int64_t orow = layout.row(cap, H, bh / H, bh % H, off + n);  // the cache row of token off + n
   const int64_t row_bytes = static_cast<int64_t>(lanes_per_row) * BITS;  // 8 codes * BITS / 8 per lane
   uint8_t *dst = codes + orow * row_bytes + static_cast<int64_t>(chunk) * BITS;
   if (BITS == 2) {
@@ -124,15 +124,15 @@ hipError_t launch_t(const QuantizeLaunch &p, hipStream_t stream) {
   switch (p.group) {
     case 32:
       quantize_pack<T, BITS, 4><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream>>>(
-          x, total, lanes_per_row, p.N, p.codes, p.scale, p.zero, p.cap, p.off, gpr);
+          x, total, lanes_per_row, p.N, p.codes, p.scale, p.zero, p.cap, p.off, gpr, p.layout, p.H);
       break;
     case 64:
       quantize_pack<T, BITS, 8><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream>>>(
-          x, total, lanes_per_row, p.N, p.codes, p.scale, p.zero, p.cap, p.off, gpr);
+          x, total, lanes_per_row, p.N, p.codes, p.scale, p.zero, p.cap, p.off, gpr, p.layout, p.H);
       break;
     default:
       quantize_pack<T, BITS, 16><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream>>>(
-          x, total, lanes_per_row, p.N, p.codes, p.scale, p.zero, p.cap, p.off, gpr);
+          x, total, lanes_per_row, p.N, p.codes, p.scale, p.zero, p.cap, p.off, gpr, p.layout, p.H);
       break;
   }
   return hipGetLastError();

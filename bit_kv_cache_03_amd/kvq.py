@@ -27,7 +27,8 @@ EXPORTED = ("kv_quantize", "kv_attention_workspace_size", "kv_attention_correcte
 class QTensor(C.Structure):
     """kv_qtensor."""
     _fields_ = [("codes", C.c_void_p), ("scale", C.c_void_p), ("zero", C.c_void_p),
-                ("bits", C.c_int32), ("group", C.c_int32), ("cap", C.c_int64)]
+                ("bits", C.c_int32), ("group", C.c_int32), ("cap", C.c_int64),
+                ("page_table", C.c_void_p), ("page_size", C.c_int32), ("num_pages", C.c_int32)]
 
 
 class AttnArgs(C.Structure):
@@ -97,18 +98,39 @@ def _ptr(t) -> Optional[int]:
 
 
 class QCache:
-    """A quantized cache tensor (K or V): codes, step and zero-point on the GPU."""
+    """A quantized cache tensor (K or V): codes, step and zero-point on the GPU.
 
-    def __init__(self, B: int, H: int, cap: int, d: int, bits: int, group: int = 64, device="cuda"):
+    Contiguous: [B][H][cap][...].  Paged (``page_table`` given: an int32 GPU
+    tensor [B][cap // page_size] of page indices): pools of ``num_pages``
+    pages [num_pages][H][page_size][...]; token t of (b, h) lives in page
+    page_table[b][t // page_size] at row t % page_size."""
+
+    def __init__(self, B: int, H: int, cap: int, d: int, bits: int, group: int = 64, device="cuda",
+                 page_table=None, page_size: int = 0, num_pages: int = 0):
         import torch
         self.B, self.H, self.cap, self.d, self.bits, self.group = B, H, cap, d, bits, group
-        self.codes = torch.zeros((B, H, cap, d * bits // 8), dtype=torch.uint8, device=device)
-        self.scale = torch.zeros((B, H, cap, d // group), dtype=torch.float32, device=device)
-        self.zero = torch.zeros((B, H, cap, d // group), dtype=torch.float32, device=device)
+        self.page_table, self.page_size, self.num_pages = page_table, page_size, num_pages
+        lead = (num_pages, H, page_size) if page_table is not None else (B, H, cap)
+        self.codes = torch.zeros(lead + (d * bits // 8,), dtype=torch.uint8, device=device)
+        self.scale = torch.zeros(lead + (d // group,), dtype=torch.float32, device=device)
+        self.zero = torch.zeros(lead + (d // group,), dtype=torch.float32, device=device)
 
     def descriptor(self) -> QTensor:
         return QTensor(self.codes.data_ptr(), self.scale.data_ptr(), self.zero.data_ptr(),
-                       self.bits, self.group, self.cap)
+                       self.bits, self.group, self.cap,
+                       self.page_table.data_ptr() if self.page_table is not None else None,
+                       self.page_size, self.num_pages)
+
+    def logical(self, nc: int):
+        """(codes, step, zero) of tokens [0, nc) in the contiguous [B][H][nc][...]
+        order (a gather through the page table when paged)."""
+        if self.page_table is None:
+            return tuple(t[:, :, :nc] for t in (self.codes, self.scale, self.zero))
+        import torch
+        t = torch.arange(nc, device=self.codes.device)
+        page = self.page_table.long()[:, t // self.page_size]  # [B][nc]
+        row = t % self.page_size
+        return tuple(x[page, :, row.expand_as(page)].permute(0, 2, 1, 3) for x in (self.codes, self.scale, self.zero))
 
 
 def quantize(x, cache: QCache, tok_offset: int = 0, stream=None) -> None:

@@ -85,12 +85,24 @@ typedef enum {
  * floor(k*bits/8) at bit (k*bits) mod 8.
  */
 typedef struct {
-  uint8_t *codes; /* [B][H][cap][d*bits/8] bytes */
+  uint8_t *codes; /* [B][H][cap][d*bits/8] bytes (paged: the pool, see below) */
   float *scale;   /* [B][H][cap][d/group]  step D */
   float *zero;    /* [B][H][cap][d/group]  zero-point z (the group minimum) */
   int32_t bits;   /* 2 or 4 */
   int32_t group;  /* 32, 64 or 128; divides d */
-  int64_t cap;    /* token capacity (row stride in tokens), at most 2^23 */
+  int64_t cap;    /* token capacity per head, at most 2^23 */
+  /* Paged layout (page_table != NULL): tokens live in pages of page_size
+   * tokens of all H heads of one sequence.  codes, scale and zero then point
+   * to pools of num_pages pages, [num_pages][H][page_size][row], and token t
+   * of (b, h) is pool row (page_table[b*(cap/page_size) + t/page_size]*H + h)
+   * *page_size + t % page_size.  page_table is a DEVICE int32 array
+   * [B][cap/page_size] whose entries must lie in [0, num_pages) (not
+   * checked: device data); pages of different blocks may not coincide where
+   * a call writes.  page_size is a power of two, at least 64, and divides
+   * cap.  NULL, with page_size and num_pages 0: the contiguous layout above. */
+  const int32_t *page_table;
+  int32_t page_size;
+  int32_t num_pages;
 } kv_qtensor;
 
 /*
@@ -131,7 +143,8 @@ typedef struct {
   const void *k_cur;  /* bf16 [B][Hkv][Ncur][d] (may be NULL if Ncur == 0) */
   const void *v_cur;  /* bf16 [B][Hkv][Ncur][d] (may be NULL if Ncur == 0) */
   const kv_qtensor *k_cache; /* host pointers to descriptors; may be NULL if Nc == 0 */
-  const kv_qtensor *v_cache; /* both with the same group */
+  const kv_qtensor *v_cache; /* both with the same group, cap and layout (the same page
+                                table and page size when paged) */
   void *out;          /* bf16 [B][Hq][Nq][d], overwritten; must not overlap inputs */
   float softmax_scale; /* tau; 0 -> 1/sqrt(d); the correction uses tau^2/24 */
   int32_t corr;       /* kv_corr */

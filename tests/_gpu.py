@@ -92,3 +92,22 @@ def run_diagnostics(w, data, kc, corr="taylor", causal=False):
     stats = r[:, :5].view(np.float32).astype(np.float64)
     tops = r[:, 5:15].reshape(-1, 2, 5).astype(np.int64)
     return stats, tops
+
+
+def paged_cache(w, src: np.ndarray, bits: int, page_size: int, cap=None, chunk=None, seed=0, spare=3):
+    """The cache of build_cache in the paged layout: pages of page_size
+    tokens, every (sequence, block) on a page drawn from a shuffled pool with
+    `spare` unused pages, filled by kv_quantize through the page table."""
+    cap = w.Nc if cap is None else cap
+    cap = (cap + page_size - 1) // page_size * page_size
+    pps = cap // page_size
+    num_pages = w.B * pps + spare
+    perm = np.random.default_rng(seed).permutation(num_pages)[: w.B * pps].astype(np.int32)
+    table = torch.from_numpy(perm.reshape(w.B, pps)).cuda()
+    c = kvq.QCache(w.B, w.Hkv, cap, w.d, bits, w.group, page_table=table, page_size=page_size,
+                   num_pages=num_pages)
+    chunk = max(1, w.Ncur) if chunk is None else chunk
+    for off in range(0, w.Nc, chunk):
+        n = min(chunk, w.Nc - off)
+        kvq.quantize(to_dev(np.ascontiguousarray(src[:, :, off:off + n])), c, off)
+    return c

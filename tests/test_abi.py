@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(kvq):
 
 
 def test_version_and_status_strings(kvq):
-    assert kvq.lib.kv_version() == 3
+    assert kvq.lib.kv_version() == 4
     for s in range(1, 8):
         assert len(kvq.lib.kv_status_string(s)) > 10
     assert kvq.lib.kv_status_string(0) == b"ok"
@@ -53,7 +53,8 @@ int main(void) {
   printf("kv_qtensor %zu\\n", sizeof(kv_qtensor));
   printf("kv_attn_args %zu\\n", sizeof(kv_attn_args));
   F(kv_qtensor, codes); F(kv_qtensor, scale); F(kv_qtensor, zero); F(kv_qtensor, bits);
-  F(kv_qtensor, group); F(kv_qtensor, cap);
+  F(kv_qtensor, group); F(kv_qtensor, cap); F(kv_qtensor, page_table); F(kv_qtensor, page_size);
+  F(kv_qtensor, num_pages);
   F(kv_attn_args, B); F(kv_attn_args, Hq); F(kv_attn_args, Hkv); F(kv_attn_args, Nq);
   F(kv_attn_args, Ncur); F(kv_attn_args, Nc); F(kv_attn_args, d); F(kv_attn_args, q);
   F(kv_attn_args, k_cur); F(kv_attn_args, v_cur); F(kv_attn_args, k_cache); F(kv_attn_args, v_cache);
@@ -268,3 +269,41 @@ def test_diagnostics_cache_errors(kvq):
     assert kvq.lib.kv_attention_diagnostics(C.byref(a), None) == kvq.KV_ERR_UNSUPPORTED
     a.k_cache = None
     assert kvq.lib.kv_attention_diagnostics(C.byref(a), None) == kvq.KV_ERR_NULL
+
+
+def _paged(kvq, base, table=0x7000000, page_size=128, num_pages=4, cap=256, bits=2):
+    return kvq.QTensor(base, base + 0x100000, base + 0x200000, bits, 64, cap, table, page_size, num_pages)
+
+
+@pytest.mark.parametrize("name,kw,err", [
+    ("ok", dict(), "KV_OK"),
+    ("page_size_not_64x", dict(page_size=96), "KV_ERR_SHAPE"),
+    ("page_size_not_pow2", dict(page_size=192, cap=384), "KV_ERR_SHAPE"),
+    ("page_size_small", dict(page_size=32, cap=256), "KV_ERR_SHAPE"),
+    ("cap_not_pages", dict(page_size=128, cap=320), "KV_ERR_SHAPE"),
+    ("no_pages", dict(num_pages=0), "KV_ERR_SHAPE"),
+    ("table_align", dict(table=0x7000002), "KV_ERR_ALIGN"),
+])
+def test_quantize_paged_descriptor(kvq, name, kw, err):
+    t = _paged(kvq, 0x30000000, **kw)
+    # N = 0: full validation, then a no-op that launches nothing (fake pointers)
+    assert kvq.lib.kv_quantize(A, 0, 1, 2, 0, 128, C.byref(t), 0, None) == getattr(kvq, err), name
+
+
+def test_contiguous_descriptor_with_page_fields(kvq):
+    t = kvq.QTensor(0x30000000, 0x30100000, 0x30200000, 2, 64, 256, None, 64, 0)
+    assert kvq.lib.kv_quantize(A, 0, 1, 2, 0, 128, C.byref(t), 0, None) == kvq.KV_ERR_SHAPE
+
+
+def test_attention_paged_layouts_must_match(kvq):
+    a = _args(kvq)
+    a._k = _paged(kvq, 0x10000000)
+    a._v = _paged(kvq, 0x20000000)
+    a.k_cache, a.v_cache = C.pointer(a._k), C.pointer(a._v)
+    assert kvq.lib.kv_attention_workspace_size(C.byref(a)) > 0  # valid
+    a._v = _paged(kvq, 0x20000000, table=0x7100000)  # another page table
+    a.v_cache = C.pointer(a._v)
+    assert _attn(kvq, a) == kvq.KV_ERR_UNSUPPORTED
+    a._v = _qt(kvq, 0x20000000, cap=256)  # contiguous V with paged K
+    a.v_cache = C.pointer(a._v)
+    assert _attn(kvq, a) == kvq.KV_ERR_UNSUPPORTED
