@@ -697,7 +697,7 @@ template <int KBITS, int VBITS, bool TAYLOR, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(THREADS, 1) void attn_fast_kernel(AttnLaunch p, int32_t group_shift,
                                                                 int64_t rows_per_kvhead, int32_t row_blocks,
                                                                 const float *kpart, int32_t nsplit,
-                                                                float *partials) {
+                                                                float *partials, int64_t nfull) {
   __shared__ __attribute__((aligned(16))) uint16_t Kl[2 * KBUF];
   __shared__ __attribute__((aligned(16))) uint16_t Vl[NVBUF * VBUF];
 
@@ -707,15 +707,32 @@ __global__ __launch_bounds__(THREADS, 1) void attn_fast_kernel(AttnLaunch p, int
   const int ng = D >> group_shift;
 
   // Workgroups are dealt to the 8 XCDs round-robin by id; renumber so that
-  // consecutive ids (the row blocks of one KV head) share an XCD.
+  // consecutive ids (the row blocks of one KV head) share an XCD.  The first
+  // nfull ids (the unsplit units, dispatched first; a multiple of the CU
+  // count) and the rest are renumbered separately, so that the unsplit units
+  // all start in the first rounds.
   const uint32_t nwg = gridDim.x, wg = blockIdx.x;
-  const uint32_t per = nwg >> 3, extra = nwg & 7, xcd = wg & 7, slot = wg >> 3;
-  const uint32_t lin = (xcd < extra ? xcd * (per + 1) : extra * (per + 1) + (xcd - extra) * per) + slot;
-  const uint32_t per_split = static_cast<uint32_t>(row_blocks * p.B * p.Hkv);
-  const int64_t split = lin / per_split;
-  const int64_t rem = lin - split * per_split;
-  const int64_t bkv = rem / static_cast<uint32_t>(row_blocks);
-  const int64_t rb = rem - bkv * row_blocks;
+  const bool tail = nsplit > 1 && wg >= static_cast<uint32_t>(nfull);
+  const uint32_t base = tail ? static_cast<uint32_t>(nfull) : 0u;
+  const uint32_t cnt = nsplit > 1 ? (tail ? nwg - base : static_cast<uint32_t>(nfull)) : nwg;
+  const uint32_t k = wg - base;
+  const uint32_t per = cnt >> 3, extra = cnt & 7, xcd = k & 7, slot = k >> 3;
+  const uint32_t lin = base + (xcd < extra ? xcd * (per + 1) : extra * (per + 1) + (xcd - extra) * per) + slot;
+  // work units = (b, KV head, row block); the first nfull run over all keys,
+  // each of the others is split into nsplit key ranges (split-major, so that
+  // adjacent workgroups read the same keys)
+  const int64_t units = static_cast<int64_t>(row_blocks) * p.B * p.Hkv;
+  int64_t unit, split = 0, ns = 1;
+  if (static_cast<int64_t>(lin) < nfull) {
+    unit = lin;
+  } else {
+    const int64_t t = lin - nfull, ntail = units - nfull;
+    split = t / ntail;
+    unit = nfull + (t - split * ntail);
+    ns = nsplit;
+  }
+  const int64_t bkv = unit / row_blocks;
+  const int64_t rb = unit - bkv * row_blocks;
   const int64_t b = bkv / p.Hkv, hk = bkv - b * p.Hkv;
   const int64_t gq = p.Hq / p.Hkv;
   // exponent ek of the KV head from the pre-pass's partial bounds: keys
@@ -770,7 +787,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_fast_kernel(AttnLaunch p, int
   }
   // this split's tiles [t0, t1) of the cached tiles followed by the current ones
   const int tc = static_cast<int>((p.Nc + BN - 1) / BN), tu = static_cast<int>((p.Ncur + BN - 1) / BN);
-  const int t0 = static_cast<int>(split * (tc + tu) / nsplit), t1 = static_cast<int>((split + 1) * (tc + tu) / nsplit);
+  const int t0 = static_cast<int>(split * (tc + tu) / ns), t1 = static_cast<int>((split + 1) * (tc + tu) / ns);
   c.beg = min(t0, tc) * BN;
   c.end = min(min(t1, tc) * BN, static_cast<int>(p.Nc));
   segment<true, TAYLOR, KBITS, VBITS, false, PAGED>(c, qs, st, Kl, Vl, tid);
@@ -793,7 +810,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_fast_kernel(AttnLaunch p, int
 
   const float l_tot = st.l + __shfl_xor(st.l, 32, 64);
   if (!row_ok) return;
-  if (nsplit > 1) {  // partial: O (unnormalised), then (m, l); [split][qrow][kPartialStride(D)]
+  if (ns > 1) {  // partial: O (unnormalised), then (m, l); [split][qrow][kPartialStride(D)]
     float *w = partials + (split * (p.B * p.Hq * p.Nq) + qrow) * kPartialStride(D);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -818,6 +835,38 @@ __global__ __launch_bounds__(THREADS, 1) void attn_fast_kernel(AttnLaunch p, int
                      pack2(st.o[db][4 * g4 + 2] * inv, st.o[db][4 * g4 + 3] * inv));
 }
 
+// Log-sum-exp merge of the split partials of the tail units only (the
+// others wrote their output directly): one wave per query row of a tail
+// unit, 2 values per lane.
+__global__ __launch_bounds__(256) void tail_combine_kernel(const float *__restrict__ ws, uint16_t *__restrict__ out,
+                                                           AttnLaunch p, int64_t rows_per_kvhead, int32_t row_blocks,
+                                                           int64_t nfull, int32_t nsplit) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);  // row of the tail units
+  const int lane = threadIdx.x & 63;
+  const int64_t unit = nfull + idx / BM;
+  const int64_t bkv = unit / row_blocks, rb = unit - bkv * row_blocks;
+  const int64_t rr = rb * BM + idx % BM;
+  if (bkv >= p.B * p.Hkv || rr >= rows_per_kvhead) return;
+  const int64_t b = bkv / p.Hkv, hk = bkv - b * p.Hkv, gq = p.Hq / p.Hkv;
+  const int64_t qrow = (b * p.Hq + hk * gq + rr / p.Nq) * p.Nq + rr % p.Nq;
+  const int64_t nrows = p.B * p.Hq * p.Nq;
+  constexpr int64_t W = kPartialStride(D);
+  float m = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, ws[(s * nrows + qrow) * W + D]);
+  float l = 0.f, a0 = 0.f, a1 = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float *w = ws + (s * nrows + qrow) * W;
+    if (w[D] == -INFINITY) continue;  // no key of this split is visible to the row
+    const float f = exp2f(w[D] - m);
+    l += f * w[D + 1];
+    const float2 o = *reinterpret_cast<const float2 *>(w + 2 * lane);
+    a0 += f * o.x;
+    a1 += f * o.y;
+  }
+  const float inv = 1.0f / l;
+  *reinterpret_cast<uint32_t *>(out + qrow * D + 2 * lane) = pack2(a0 * inv, a1 * inv);
+}
+
 template <int KB, int VB>
 hipError_t launch_bits(const AttnLaunch &p, hipStream_t stream) {
   const int64_t rows = p.Nq * (p.Hq / p.Hkv);
@@ -828,14 +877,20 @@ hipError_t launch_bits(const AttnLaunch &p, hipStream_t stream) {
   float *kpart = reinterpret_cast<float *>(static_cast<char *>(p.workspace) +
                                            (nsplit > 1 ? short_path_workspace_bytes(p.B, p.Hq, p.Nq, p.d, nsplit) : 0));
   launch_key_scale(p, stream, kpart);
-  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(nsplit) * row_blocks * p.B * p.Hkv));
+  const int64_t units = static_cast<int64_t>(row_blocks) * p.B * p.Hkv;
+  const int64_t nfull = nsplit > 1 ? p.fast_full_units : units;
+  const dim3 grid(static_cast<uint32_t>(nfull + (units - nfull) * nsplit));
   constexpr bool CAUSAL = KVQ_FAST_CAUSAL != 0, PAGED = KVQ_FAST_PAGED != 0;
   auto kernel = p.corr == KV_CORR_TAYLOR ? attn_fast_kernel<KB, VB, true, CAUSAL, PAGED>
                                          : attn_fast_kernel<KB, VB, false, CAUSAL, PAGED>;
-  kernel<<<grid, dim3(THREADS), 0, stream>>>(p, gshift, rows, row_blocks, kpart, nsplit, partials);
+  kernel<<<grid, dim3(THREADS), 0, stream>>>(p, gshift, rows, row_blocks, kpart, nsplit, partials, nfull);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
-  return launch_combine(partials, p.out, p.B * p.Hq * p.Nq, nsplit, p.d, stream);
+  if (nfull == 0) return launch_combine(partials, p.out, p.B * p.Hq * p.Nq, nsplit, p.d, stream);
+  const int64_t tail_rows = (units - nfull) * BM;
+  tail_combine_kernel<<<dim3(static_cast<uint32_t>((tail_rows + 3) / 4)), dim3(256), 0, stream>>>(
+      partials, p.out, p, rows, row_blocks, nfull, nsplit);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -871,8 +926,31 @@ size_t fast_path_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
   return part + (static_cast<size_t>(B * Hkv) * 2 * KCHUNKS * sizeof(float) + 255) / 256 * 256;
 }
 
-// Split count of the throughput kernel: rounds of one-per-CU workgroups
-// times the tiles each one runs, plus the HBM traffic of the partials.
+// Key-range split of the throughput kernel.  With at least one full round
+// of one-per-CU work units (R = units / CUs >= 1), the units of the last,
+// partly empty round (r = units mod CUs) are split floor(CUs / r) ways so
+// that they fill it, and the others run unsplit: R + 1/s rounds instead of
+// R + 1, with partials and their merge for the r tail units only.  With
+// fewer units than CUs, all of them split (fast_path_splits).  A forced
+// count splits every unit.
+FastPlan fast_path_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nc, int64_t Ncur, int cu_count,
+                        int forced) {
+  const int64_t rows = Nq * (Hq / Hkv);
+  const int64_t units = (rows + BM - 1) / BM * B * Hkv;
+  const int64_t tiles = (Nc + BN - 1) / BN + (Ncur + BN - 1) / BN;
+  if (forced > 0) return FastPlan{static_cast<int>(forced < tiles ? forced : tiles), 0};
+  const int64_t R = units / cu_count, r = units - R * cu_count;
+  if (R == 0) return FastPlan{fast_path_splits(B, Hq, Hkv, Nq, Nc, Ncur, cu_count), 0};
+  int64_t s = r > 0 ? cu_count / r : 1;
+  if (s > 64) s = 64;
+  if (s * 2 > tiles) s = tiles / 2;
+  if (s < 2) return FastPlan{1, units};
+  return FastPlan{static_cast<int>(s), units - r};
+}
+
+// Split count of the throughput kernel when every work unit splits: rounds
+// of one-per-CU workgroups times the tiles each one runs, plus the HBM
+// traffic of the partials.
 int fast_path_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nc, int64_t Ncur, int cu_count) {
   const int64_t rows = Nq * (Hq / Hkv);
   const int64_t wgs = (rows + BM - 1) / BM * B * Hkv;

@@ -85,6 +85,7 @@ struct Plan {
   int path;  // KV_PATH_LONG or KV_PATH_SHORT
   int splits;
   size_t workspace;
+  int64_t full_units;  // throughput kernel: units run unsplit
 };
 
 // Rows per KV head at or below which the split-over-cache path is used.
@@ -199,7 +200,7 @@ kv_status validate_diagnostics(const kv_diag_args *a) {
 }
 
 Plan plan_attention(const kv_attn_args *a, bool query_device) {
-  Plan pl{KV_PATH_LONG, 0, 0};
+  Plan pl{KV_PATH_LONG, 0, 0, 0};
   const int64_t rows = a->Nq * (a->Hq / a->Hkv);
   int path = a->path;
   if (path == KV_PATH_AUTO) path = (rows <= kShortRows && a->Nc > 0) ? KV_PATH_SHORT : KV_PATH_LONG;
@@ -215,9 +216,9 @@ Plan plan_attention(const kv_attn_args *a, bool query_device) {
     }
   } else if (a->d == 128 && a->corr != KV_CORR_EXACT) {  // the throughput kernel, split-K when it balances
     const int cus = query_device ? device_cu_count() : 256;
-    const int64_t tiles = (a->Nc + 63) / 64 + (a->Ncur + 63) / 64;
-    pl.splits = a->splits > 0 ? static_cast<int>(a->splits < tiles ? a->splits : tiles)
-                              : kvq::fast_path_splits(a->B, a->Hq, a->Hkv, a->Nq, a->Nc, a->Ncur, cus);
+    const kvq::FastPlan fp = kvq::fast_path_plan(a->B, a->Hq, a->Hkv, a->Nq, a->Nc, a->Ncur, cus, a->splits);
+    pl.splits = fp.splits;
+    pl.full_units = fp.full_units;
     pl.workspace = kvq::fast_path_workspace_bytes(a->B, a->Hq, a->Hkv, a->Nq, pl.splits);
   }
   return pl;
@@ -302,11 +303,12 @@ kv_status kv_attention_corrected(const kv_attn_args *a, void *stream) {
   p.corr = a->corr;
   p.causal = a->causal;
   p.splits = pl.splits;
+  p.fast_full_units = pl.full_units;
   p.workspace = a->workspace;
   if (debug_log())
-    fprintf(stderr, "kvq: attention path=%s rows/kvhead=%lld splits=%d workspace=%zu corr=%d\n",
+    fprintf(stderr, "kvq: attention path=%s rows/kvhead=%lld splits=%d full_units=%lld workspace=%zu corr=%d\n",
             pl.path == KV_PATH_SHORT ? "short" : "long", static_cast<long long>(a->Nq * (a->Hq / a->Hkv)),
-            pl.splits, pl.workspace, a->corr);
+            pl.splits, static_cast<long long>(pl.full_units), pl.workspace, a->corr);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = pl.path == KV_PATH_SHORT ? kvq::launch_attention_short(p, s) : kvq::launch_attention_long(p, s);
   return e == hipSuccess ? KV_OK : KV_ERR_HIP;

@@ -56,6 +56,7 @@ struct AttnLaunch {
   int corr;    // kv_corr
   int causal;  // 1: current key i visible to query row j only if i <= j + Ncur - Nq
   int splits;  // resolved key-range split count
+  int64_t fast_full_units;  // throughput kernel: work units run unsplit before the split ones
   void *workspace;
 };
 
@@ -73,6 +74,12 @@ hipError_t launch_attention_short(const AttnLaunch &p, hipStream_t stream);
 bool fast_path_supported(const AttnLaunch &p);
 size_t fast_path_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int splits);
 int fast_path_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nc, int64_t Ncur, int cu_count);
+struct FastPlan {
+  int splits;          // key ranges of each split work unit
+  int64_t full_units;  // leading (b, KV head, 256-row block) units that run unsplit
+};
+FastPlan fast_path_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nc, int64_t Ncur, int cu_count,
+                        int forced);
 hipError_t launch_attention_fast(const AttnLaunch &p, hipStream_t stream);
 // The same with the causal mask (built in attention_fast_causal.hip), over
 // a paged cache (attention_fast_paged.hip), and both

@@ -205,3 +205,28 @@ def test_causal_one_query_is_unmasked(orc):
         a = _gpu.run_attention(w, data, kc, vc, path=path)
         b = _gpu.run_attention(w, data, kc, vc, path=path, causal=True)
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_long_path_tail_split(orc):
+    """300 work units (one 100-row block per head) on 256 CUs: the library
+    runs 256 units over all keys and splits the 44 others into 5 key ranges
+    (the tail of the last round); rows of both kinds against the oracle."""
+    import _gpu
+    from bit_kv_cache_03_amd import kvq
+    w = W.WORKLOADS["h24_int4_cache16k"].scaled(Hq=300, Hkv=300, Nq=100, Ncur=100, Nc=500)
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the split plan under test assumes 256 CUs")
+    data = W.generate(w)
+    kc = _gpu.build_cache(w, data["kc"], w.kbits)
+    vc = _gpu.build_cache(w, data["vc"], w.vbits)
+    q = _gpu.as_bf16_dev(data["q"])
+    args = kvq.make_args(q, _gpu.as_bf16_dev(data["k"]), _gpu.as_bf16_dev(data["v"]), kc, vc, w.Nc,
+                         torch.empty_like(q), corr="taylor")
+    partials = 5 * w.B * w.Hq * w.Nq * (w.d + 4) * 4
+    assert kvq.workspace_size(args) == partials + 300 * 256  # 5 key ranges; bounds of 300 KV heads
+    out = _gpu.run_attention(w, data, kc, vc, corr="taylor")
+    heads = [0, 1, 128, 255, 256, 257, 280, 299]  # units 256.. are the split tail
+    rows = np.array([h * w.Nq + j for h in heads for j in (0, 37, 99)], dtype=np.int64)
+    got = _gpu.out_rows(out, rows)
+    ref = oracle_problem(orc, w, "taylor", data=data).attention(rows=rows)
+    _gpu.check(got, ref)
