@@ -51,6 +51,10 @@ def _load(path: str):
     i64, i32, dbl, vp = C.c_int64, C.c_int32, C.c_double, C.c_void_p
     L.kvo_quantize_f32.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp]
     L.kvo_quantize_bf16.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp]
+    L.kvo_quantize_f32_meta.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp]
+    L.kvo_quantize_bf16_meta.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp]
+    L.kvo_round_fp16.argtypes = [C.c_float]
+    L.kvo_round_fp16.restype = C.c_float
     L.kvo_unpack.argtypes = [vp, i64, i32, i32, vp]
     L.kvo_pack.argtypes = [vp, i64, i32, i32, vp]
     L.kvo_dequant.argtypes = [vp, vp, vp, i64, i32, i32, i32, vp]
@@ -89,14 +93,17 @@ def _check(rc: int, what: str):
 # quantizer
 # --------------------------------------------------------------------------
 
-def quantize(x: np.ndarray, bits: int, group: int):
+def quantize(x: np.ndarray, bits: int, group: int, meta: str = "f32"):
     """Group-wise asymmetric quantization of the last axis of ``x``.
 
     ``x`` is float32 values, or uint16 bf16 bit patterns.  Returns
     ``(codes, step, zero)`` with codes packed LSB-first: shape
     ``x.shape[:-1] + (d*bits//8,)`` uint8, and step/zero of shape
-    ``x.shape[:-1] + (d//group,)`` float32.
+    ``x.shape[:-1] + (d//group,)`` float32.  ``meta="f16"``: step and zero
+    are rounded to binary16 (still returned as float32 values) and the codes
+    are taken against the rounded grid.
     """
+    meta16 = {"f32": 0, "f16": 1}[meta]
     x = np.ascontiguousarray(x)
     d = x.shape[-1]
     rows = x.size // d if d else 0
@@ -104,13 +111,17 @@ def quantize(x: np.ndarray, bits: int, group: int):
     step = np.zeros(x.shape[:-1] + (d // group,), np.float32)
     zero = np.zeros_like(step)
     if x.dtype == np.float32:
-        rc = lib().kvo_quantize_f32(_p(x), rows, d, group, bits, _p(codes), _p(step), _p(zero))
+        rc = lib().kvo_quantize_f32_meta(_p(x), rows, d, group, bits, meta16, _p(codes), _p(step), _p(zero))
     elif x.dtype == np.uint16:
-        rc = lib().kvo_quantize_bf16(_p(x), rows, d, group, bits, _p(codes), _p(step), _p(zero))
+        rc = lib().kvo_quantize_bf16_meta(_p(x), rows, d, group, bits, meta16, _p(codes), _p(step), _p(zero))
     else:
         raise TypeError("x must be float32 or uint16 (bf16 bits)")
     _check(rc, "quantize")
     return codes, step, zero
+
+
+def round_fp16(x: float) -> float:
+    return lib().kvo_round_fp16(float(x))
 
 
 def unpack(codes: np.ndarray, d: int, bits: int) -> np.ndarray:

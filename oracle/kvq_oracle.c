@@ -34,6 +34,8 @@
  * Readings taken where the pages are silent (each also listed in the design
  * notes of the repository):
  *  - step  D = fl32(fl32(mx - mn) / (2^bits - 1)), zero-point z = mn (fp32);
+ *    with binary16 metadata, D and z are rounded to binary16 (nearest,
+ *    ties to even) and the codes below use the rounded D and z;
  *  - code  c = clamp(rne(fl32(fl32(x - mn) / D)), 0, 2^bits - 1), 0 if D == 0;
  *  - mn and mx are canonicalised with "+ 0.0f" so a zero extreme is +0;
  *  - packing is LSB-first: element k of a row sits in byte floor(k*bits/8)
@@ -103,9 +105,33 @@ static int qparams_ok(int32_t d, int32_t group, int32_t bits) {
   return 1;
 }
 
+/* The binary16 value nearest to a finite fp32 x (round half to even),
+ * returned as fp32 (exactly).  binary16: 10 fraction bits, normals from
+ * 2^-14, subnormals spaced 2^-24, largest finite 65504; larger magnitudes
+ * round to infinity (outside the quantizer's contract).  The spacing of
+ * binary16 numbers in x's binade is a power of two u, so x/u is exact and
+ * rint(x/u)*u is the rounded value. */
+static float round_fp16(float x) {
+  if (x == 0.0f || !isfinite(x)) return x;
+  const float a = fabsf(x);
+  int e;
+  frexpf(a, &e);              /* a in [2^(e-1), 2^e) */
+  int ue = (e - 1) - 10;      /* spacing in that binade */
+  if (ue < -24) ue = -24;     /* subnormal spacing */
+  const float u = ldexpf(1.0f, ue);
+  const float r = rintf(a / u) * u;
+  if (r > 65504.0f) return copysignf(INFINITY, x);
+  return copysignf(r, x);
+}
+
+float kvo_round_fp16(float x) { return round_fp16(x); }
+
 /* Quantize one group of `group` fp32 values.  codes_out gets one code per
- * element (unpacked).  The order of fp32 operations is the contract. */
-static void quantize_group(const float *x, int32_t group, int32_t bits,
+ * element (unpacked).  The order of fp32 operations is the contract.
+ * meta16: the step and zero point are stored as binary16; they are rounded
+ * first and the codes are taken against the rounded grid, so that the
+ * dequantised value z + D c uses exactly what is stored. */
+static void quantize_group(const float *x, int32_t group, int32_t bits, int32_t meta16,
                            uint8_t *codes_out, float *step_out, float *zero_out) {
   const int32_t top = (1 << bits) - 1;
   float mn = x[0], mx = x[0];
@@ -117,12 +143,17 @@ static void quantize_group(const float *x, int32_t group, int32_t bits,
   mx = mx + 0.0f;
   float range = mx - mn;             /* fl32 subtraction */
   float step = range / (float)top;   /* fl32 IEEE division */
+  float zero = mn;
+  if (meta16) {
+    step = round_fp16(step);
+    zero = round_fp16(mn);
+  }
   *step_out = step;
-  *zero_out = mn;
+  *zero_out = zero;
   for (int32_t k = 0; k < group; ++k) {
     int32_t c = 0;
     if (step > 0.0f) {
-      float num = x[k] - mn;           /* fl32 subtraction */
+      float num = x[k] - zero;         /* fl32 subtraction */
       float t = num / step;            /* fl32 IEEE division */
       float r = rintf(t);                      /* round half to even */
       if (r < 0.0f) r = 0.0f;
@@ -143,10 +174,10 @@ static void pack_row(const uint8_t *c, int32_t d, int32_t bits, uint8_t *out) {
 }
 
 /* Quantize `rows` rows of d fp32 values.  codes: rows x (d*bits/8) bytes;
- * step, zero: rows x (d/group) fp32. */
-int kvo_quantize_f32(const float *x, int64_t rows, int32_t d, int32_t group,
-                     int32_t bits, uint8_t *codes, float *step, float *zero) {
-  if (!x || !codes || !step || !zero || rows < 0) return KVO_ERR_ARG;
+ * step, zero: rows x (d/group) fp32 (holding binary16 values when meta16). */
+int kvo_quantize_f32_meta(const float *x, int64_t rows, int32_t d, int32_t group,
+                          int32_t bits, int32_t meta16, uint8_t *codes, float *step, float *zero) {
+  if (!x || !codes || !step || !zero || rows < 0 || (meta16 != 0 && meta16 != 1)) return KVO_ERR_ARG;
   if (!qparams_ok(d, group, bits)) return KVO_ERR_ARG;
   const int32_t ng = d / group;
   const int64_t row_bytes = d * bits / 8;
@@ -161,7 +192,7 @@ int kvo_quantize_f32(const float *x, int64_t rows, int32_t d, int32_t group,
 #pragma omp for schedule(static)
       for (int64_t r = 0; r < rows; ++r) {
         for (int32_t g = 0; g < ng; ++g)
-          quantize_group(x + r * d + (int64_t)g * group, group, bits, c + g * group,
+          quantize_group(x + r * d + (int64_t)g * group, group, bits, meta16, c + g * group,
                          step + r * ng + g, zero + r * ng + g);
         pack_row(c, d, bits, codes + r * row_bytes);
       }
@@ -171,16 +202,26 @@ int kvo_quantize_f32(const float *x, int64_t rows, int32_t d, int32_t group,
   return err;
 }
 
+int kvo_quantize_f32(const float *x, int64_t rows, int32_t d, int32_t group,
+                     int32_t bits, uint8_t *codes, float *step, float *zero) {
+  return kvo_quantize_f32_meta(x, rows, d, group, bits, 0, codes, step, zero);
+}
+
 /* Same, for bf16 input (widened exactly to fp32 first). */
-int kvo_quantize_bf16(const uint16_t *x, int64_t rows, int32_t d, int32_t group,
-                      int32_t bits, uint8_t *codes, float *step, float *zero) {
+int kvo_quantize_bf16_meta(const uint16_t *x, int64_t rows, int32_t d, int32_t group,
+                           int32_t bits, int32_t meta16, uint8_t *codes, float *step, float *zero) {
   if (!x || rows < 0 || d <= 0) return KVO_ERR_ARG;
   float *f = (float *)malloc((size_t)(rows * d) * sizeof(float) + 1);
   if (!f) return KVO_ERR_MEM;
   kvo_bf16_to_f32(x, rows * d, f);
-  int rc = kvo_quantize_f32(f, rows, d, group, bits, codes, step, zero);
+  int rc = kvo_quantize_f32_meta(f, rows, d, group, bits, meta16, codes, step, zero);
   free(f);
   return rc;
+}
+
+int kvo_quantize_bf16(const uint16_t *x, int64_t rows, int32_t d, int32_t group,
+                      int32_t bits, uint8_t *codes, float *step, float *zero) {
+  return kvo_quantize_bf16_meta(x, rows, d, group, bits, 0, codes, step, zero);
 }
 
 /* Read code k of a packed row (LSB-first). */
@@ -656,4 +697,4 @@ int kvo_diagnostics(const kvo_attn *a, const uint16_t *k_ref, const int64_t *row
   return err;
 }
 
-int kvo_version(void) { return 3; }
+int kvo_version(void) { return 4; }

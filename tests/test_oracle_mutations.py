@@ -65,6 +65,10 @@ MUTANTS = [
      [("test_oracle_diagnostics", "test_matches_library_statistics", {"case": "tiny", "corr": "off", "tied": True})]),
     ("diag_ref_scale_dropped", "            sr[t] = s * rc.tau;", "            sr[t] = s;",
      [("test_oracle_diagnostics", "test_matches_library_statistics", {"case": "gqa_causal", "corr": "off", "tied": False})]),
+    ("meta16_codes_against_raw_min", "      float num = x[k] - zero;", "      float num = x[k] - mn;",
+     [("test_oracle_meta16", "test_quantizer_with_binary16_metadata", {"bits": 4, "group": 64})]),
+    ("meta16_ties_away", "  const float r = rintf(a / u) * u;", "  const float r = roundf(a / u) * u;",
+     [("test_oracle_meta16", "test_rounding_ties_subnormals_overflow", {})]),
     ("value_not_dequantized_zero",
      "v[c] = (double)a->vc_zero[base * ng + g] + ", "v[c] = ",
      [("test_oracle_attention", "test_matches_library_sdpa", {"corr": "off", "wi": 2})]),
