@@ -49,10 +49,11 @@ def kernel_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def packed_bytes(w) -> int:
+def packed_bytes(w, meta_bytes: int = 4) -> int:
     """Algorithmic bytes of the packed cache read by one attention call:
-    codes of K and V plus fp32 step and zero of both, over Nc tokens."""
-    per_tok = w.d * (w.kbits + w.vbits) // 8 + 2 * 2 * (w.d // w.group) * 4
+    codes of K and V plus step and zero of both (fp32: 4 bytes each,
+    binary16: 2), over Nc tokens."""
+    per_tok = w.d * (w.kbits + w.vbits) // 8 + 2 * 2 * (w.d // w.group) * meta_bytes
     return w.B * w.Hkv * w.Nc * per_tok
 
 
@@ -71,33 +72,40 @@ def attention_flops(w, causal: bool = False) -> float:
     return 4.0 * w.d * w.B * w.Hq * (w.Nq * w.Nc + visible_current_pairs(w, causal))
 
 
-def traffic_from_profiles(w, sha: str):
+def call_options(args) -> dict:
+    """The options of the timed attention call besides the workload."""
+    return {"nq": args.nq, "corr": args.corr, "path": args.path, "causal": args.causal,
+            "page_size": args.page_size, "meta": args.meta}
+
+
+def traffic_from_profiles(w, sha: str, options: dict):
     """HBM bytes per attention launch from the committed rocprofv3 counter
-    runs, if they were taken on the current kernel source."""
+    runs, if they were taken on the current kernel source with the same call
+    options."""
     path = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_sha") != sha:
+    if t.get("kernel_sha") != sha or t.get("options") != options:
         return None
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(w, data, corr: str, target_s: float = 12.0, causal: bool = False):
+def cpu_baseline(w, data, corr: str, target_s: float = 12.0, causal: bool = False, meta: str = "f32"):
     """The oracle as it stands, on a bounded sample of query rows (all heads,
     rows spread over the chunk), with the quantize of the chunk prorated."""
     import oracle
     threads = len(os.sched_getaffinity(0))
-    kc = oracle.quantize(data["kc"], w.kbits, w.group)
-    vc = oracle.quantize(data["vc"], w.vbits, w.group)
+    kc = oracle.quantize(data["kc"], w.kbits, w.group, meta=meta)
+    vc = oracle.quantize(data["vc"], w.vbits, w.group, meta=meta)
     qb = lambda x: x if x.dtype == np.uint16 else W.bf16_bits(x)
     prob = oracle.Problem(qb(data["q"]), qb(data["k"]), qb(data["v"]), kc, vc, w.Nc, w.kbits, w.vbits,
                           w.group, corr=corr, causal=causal)
     total = prob.rows_total()
     t0 = time.perf_counter()
-    oracle.quantize(data["k"], w.kbits, w.group)
-    oracle.quantize(data["v"], w.vbits, w.group)
+    oracle.quantize(data["k"], w.kbits, w.group, meta=meta)
+    oracle.quantize(data["v"], w.vbits, w.group, meta=meta)
     t_quant = time.perf_counter() - t0
     # grow a calibration sample until it runs for a second, then size the
     # timed sample for about target_s seconds
@@ -157,7 +165,7 @@ ATTENTION_CALL_KERNELS = ("key_scale_kernel", "attn_fast_kernel", "attn_short_ke
                           "attn_combine_kernel")
 
 
-def write_traffic(w, pmc_dir: str, copy_bytes: int):
+def write_traffic(w, pmc_dir: str, copy_bytes: int, options: dict):
     """HBM bytes per attention call from four rocprofv3 --pmc runs under
     pmc_dir (fetch/, write/: the bench; copy_fetch/, copy_write/: the copy
     probe): each kernel's mean counter per dispatch, scaled by bytes per
@@ -170,10 +178,11 @@ def write_traffic(w, pmc_dir: str, copy_bytes: int):
     cw = copy_bytes / (1024.0 * sum(_counter_means(f("copy_write"), "WRITE_SIZE", ("neg",)).values()))
     per_kernel = {k: {"fetch_bytes": 1024.0 * fetch.get(k, 0.0) * cf, "write_bytes": 1024.0 * write.get(k, 0.0) * cw}
                   for k in sorted(set(fetch) | set(write))}
-    t = {"workload": w.name, "kernel_sha": kernel_sha(), "copy_bytes": copy_bytes, "fetch_factor": cf,
+    t = {"workload": w.name, "options": options, "kernel_sha": kernel_sha(), "copy_bytes": copy_bytes,
+         "fetch_factor": cf,
          "write_factor": cw, "per_kernel": per_kernel,
          "bytes_per_launch": sum(v["fetch_bytes"] + v["write_bytes"] for v in per_kernel.values()),
-         "algorithmic_packed_bytes": packed_bytes(w)}
+         "algorithmic_packed_bytes": packed_bytes(w, 2 if options["meta"] == "f16" else 4)}
     out = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
     with open(out, "w") as fh:
         json.dump(t, fh, indent=1)
@@ -241,6 +250,8 @@ def main():
     ap.add_argument("--causal", action="store_true", help="end-aligned causal mask within the current chunk")
     ap.add_argument("--page-size", type=int, default=0,
                     help="paged cache layout with pages of this many tokens (shuffled page table)")
+    ap.add_argument("--meta", default="f32", choices=["f32", "f16"],
+                    help="storage type of the caches' step and zero point")
     ap.add_argument("--diag", action="store_true",
                     help="time kv_attention_diagnostics and report the attention-balance statistics instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -252,7 +263,7 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
     args = ap.parse_args()
     if args.traffic:
-        write_traffic(W.WORKLOADS[args.workload], args.traffic, args.copy_bytes)
+        write_traffic(W.WORKLOADS[args.workload], args.traffic, args.copy_bytes, call_options(args))
         return
 
     if args.gpus != 1:
@@ -286,8 +297,8 @@ def main():
         paged = dict(page_table=table, page_size=ps, num_pages=npages)
     else:
         paged = {}
-    kc = kvq.QCache(w.B, w.Hkv, cap, w.d, w.kbits, w.group, **paged)
-    vc = kvq.QCache(w.B, w.Hkv, cap, w.d, w.vbits, w.group, **paged)
+    kc = kvq.QCache(w.B, w.Hkv, cap, w.d, w.kbits, w.group, meta=args.meta, **paged)
+    vc = kvq.QCache(w.B, w.Hkv, cap, w.d, w.vbits, w.group, meta=args.meta, **paged)
     # the cache content does not depend on how it is appended (quantisation
     # is per token), so short chunks are appended in >= 4096-token calls
     chunk = max(w.Ncur, 4096)
@@ -361,13 +372,14 @@ def main():
     achieved = flops / (attn_ms * 1e-3) / 1e12
     # few query rows per KV head: the packed cache read bounds the kernel
     hbm_bound = w.rows_per_kvhead <= 64
+    pbytes = packed_bytes(w, 2 if args.meta == "f16" else 4)
     if hbm_bound:
-        roof = {"bound": "hbm", "achieved": packed_bytes(w) / (attn_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+        roof = {"bound": "hbm", "achieved": pbytes / (attn_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
     else:
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
     sha = kernel_sha()
-    traffic = traffic_from_profiles(w, sha)
+    traffic = traffic_from_profiles(w, sha, call_options(args))
     line = {
         "metric": METRIC,
         "value": ckq / (ms_step * 1e-3),
@@ -380,15 +392,16 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic: seeded N(0,1) q/k/v with the workload's key structure, bf16; cache INT%d/INT%d group %d" % (
-            w.kbits, w.vbits, w.group),
+        "data": "synthetic: seeded N(0,1) q/k/v with the workload's key structure, bf16; cache INT%d/INT%d group %d%s" % (
+            w.kbits, w.vbits, w.group, ", binary16 step/zero" if args.meta == "f16" else ""),
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "Nq": w.Nq,
                    "Ncur": w.Ncur, "Nc": w.Nc, "kbits": w.kbits, "vbits": w.vbits, "group": w.group,
-                   "corr": corr, "path": args.path, "causal": args.causal, "page_size": args.page_size},
+                   "corr": corr, "path": args.path, "causal": args.causal, "page_size": args.page_size,
+                   "meta": args.meta},
         "attention_ms": attn_ms,
         "quantize_ms": quant_ms,
         "tflops_eff": achieved,
-        "packed_kv_gbs": packed_bytes(w) / (attn_ms * 1e-3) / 1e9,
+        "packed_kv_gbs": pbytes / (attn_ms * 1e-3) / 1e9,
         "correction_overhead": overhead,
         "wall_s": wall,
         "kernel_sha": sha,
@@ -396,7 +409,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, data, corr, causal=args.causal)
+        line["cpu_baseline"] = cpu_baseline(w, data, corr, causal=args.causal, meta=args.meta)
     print(json.dumps(line), flush=True)
 
 

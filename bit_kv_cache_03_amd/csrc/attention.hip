@@ -236,8 +236,8 @@ __global__ __launch_bounds__(kThreads, EXACT ? 1 : 2) void attn_tile_kernel(Attn
       if (cached) {
         const int64_t row = p.layout.row(p.cap, p.Hkv, b, hk, k0 + (ok ? key : 0));  // cache row of the key
         const int g = d0 >> group_shift;
-        const float stp = ok ? p.kc_scale[row * ng + g] : 0.f;
-        const float zp = ok ? p.kc_zero[row * ng + g] : 0.f;
+        const float stp = ok ? meta_at(p.kc_scale, row * ng + g, p.meta16) : 0.f;
+        const float zp = ok ? meta_at(p.kc_zero, row * ng + g, p.meta16) : 0.f;
         constexpr int WORDS = DPT * KBITS / 32;
         uint32_t w[WORDS];
         const uint8_t *src = p.kc_codes + row * KROW + d0 * KBITS / 8;
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(kThreads, EXACT ? 1 : 2) void attn_tile_kernel(Attn
           float e16[16];
           float dsh[4] = {0.f, 0.f, 0.f, 0.f}, dsl[4] = {0.f, 0.f, 0.f, 0.f};
           for (int gg = 0; gg < ng; ++gg) {
-            const float s = ok ? p.kc_scale[row * ng + gg] : 0.f;
+            const float s = ok ? meta_at(p.kc_scale, row * ng + gg, p.meta16) : 0.f;
             const float sq = s * s;
             dsh[gg] = bf16_bits_to_f32(f32_to_bf16_bits(sq));
             dsl[gg] = sq - dsh[gg];
@@ -310,8 +310,8 @@ __global__ __launch_bounds__(kThreads, EXACT ? 1 : 2) void attn_tile_kernel(Attn
             const int key = 4 * kq + j;
             const bool ok = key < count;
             const int64_t row = p.layout.row(p.cap, p.Hkv, b, hk, k0 + (ok ? key : 0));
-            const float stp = ok ? p.vc_scale[row * ng + g] : 0.f;
-            const float zp = ok ? p.vc_zero[row * ng + g] : 0.f;
+            const float stp = ok ? meta_at(p.vc_scale, row * ng + g, p.meta16) : 0.f;
+            const float zp = ok ? meta_at(p.vc_zero, row * ng + g, p.meta16) : 0.f;
             const uint8_t *src = p.vc_codes + row * VROW + dq * VBITS;  // 8 codes = VBITS bytes
             uint32_t w = 0;
             if (ok) w = VBITS == 2 ? *reinterpret_cast<const uint16_t *>(src) : *reinterpret_cast<const uint32_t *>(src);

@@ -59,7 +59,9 @@
 // compiled next to the unmasked ones, they changed how those were
 // optimised (query operands spilled inside the tile loop).  The paged-cache
 // instances likewise (attention_fast_paged.hip and
-// attention_fast_paged_causal.hip: KVQ_FAST_PAGED): one variant per file.
+// attention_fast_paged_causal.hip: KVQ_FAST_PAGED), and those reading
+// binary16 steps and zero points (attention_fast_m16*.hip: KVQ_FAST_META16):
+// one variant per file.
 #include <math.h>
 
 #include "kvq_device.h"
@@ -70,6 +72,9 @@
 #endif
 #ifndef KVQ_FAST_PAGED
 #define KVQ_FAST_PAGED 0
+#endif
+#ifndef KVQ_FAST_META16
+#define KVQ_FAST_META16 0
 #endif
 
 namespace kvq {
@@ -87,6 +92,19 @@ constexpr int VS = BN + 8;     // V^T row in LDS (bf16)
 constexpr int KBUF = BN * KS;  // 16-bit elements per K buffer
 constexpr int VBUF = D * VS;   // 16-bit elements per V buffer
 constexpr int NVBUF = 3;
+
+// Step / zero-point arrays: fp32, or binary16 in the KVQ_FAST_META16 units
+// (the float pointers then address binary16 elements).
+constexpr bool kMeta16 = KVQ_FAST_META16 != 0;
+template <bool M16, typename I>
+__device__ inline float meta_ld(const float *p, I i) {
+  if (M16) return static_cast<float>(reinterpret_cast<const _Float16 *>(p)[i]);
+  return p[i];
+}
+template <bool M16>
+__device__ inline const float *meta_adv(const float *p, int64_t n) {
+  return reinterpret_cast<const float *>(reinterpret_cast<const char *>(p) + n * (M16 ? 2 : 4));
+}
 
 // V^T element (row = head-dim index, col = permuted key slot 0..63).  The
 // 16-byte chunks of a row are XOR-swizzled by (row / 16) % 8, which spreads
@@ -125,7 +143,7 @@ __device__ inline float block_max(float b, float *red, int tid) {
   return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-template <int KBITS>
+template <int KBITS, bool M16>
 __global__ __launch_bounds__(256) void key_scale_kernel(AttnLaunch p, int32_t ng, float *part) {
   __shared__ float red[4];
   const int64_t bkv = blockIdx.x / KCHUNKS;
@@ -138,15 +156,17 @@ __global__ __launch_bounds__(256) void key_scale_kernel(AttnLaunch p, int32_t ng
       const int64_t b = bkv / p.Hkv, hk = bkv - b * p.Hkv;
       for (int64_t i = lo + tid; i < hi; i += 256) {
         const int64_t e = p.layout.row(p.cap, p.Hkv, b, hk, i / ng) * ng + i % ng;
-        const float zi = p.kc_zero[e];
-        kb = fmaxf(kb, fmaxf(fabsf(zi), fabsf(fmaf(p.kc_scale[e], static_cast<float>((1 << KBITS) - 1), zi))));
+        const float zi = meta_ld<M16>(p.kc_zero, e);
+        kb = fmaxf(kb, fmaxf(fabsf(zi), fabsf(fmaf(meta_ld<M16>(p.kc_scale, e),
+                                                   static_cast<float>((1 << KBITS) - 1), zi))));
       }
     } else {
-      const float *s = p.kc_scale + bkv * p.cap * ng;
-      const float *z = p.kc_zero + bkv * p.cap * ng;
+      const float *s = meta_adv<M16>(p.kc_scale, bkv * p.cap * ng);
+      const float *z = meta_adv<M16>(p.kc_zero, bkv * p.cap * ng);
       for (int64_t i = lo + tid; i < hi; i += 256) {
-        const float zi = z[i];
-        kb = fmaxf(kb, fmaxf(fabsf(zi), fabsf(fmaf(s[i], static_cast<float>((1 << KBITS) - 1), zi))));
+        const float zi = meta_ld<M16>(z, i);
+        kb = fmaxf(kb, fmaxf(fabsf(zi), fabsf(fmaf(meta_ld<M16>(s, i),
+                                                   static_cast<float>((1 << KBITS) - 1), zi))));
       }
     }
   }
@@ -278,8 +298,8 @@ __device__ inline void fetch_k(const Ctx &c, int k0, int tid, Fetch &f, size_t p
     if (PAGED) {  // pool row pr of the tile (looked up a step earlier), then rows within it
       const int ts = tile_start(c, k0);
       kc_codes += pr * (D * KBITS / 8);
-      kc_scale += pr * c.ng;
-      kc_zero += pr * c.ng;
+      kc_scale = meta_adv<kMeta16>(kc_scale, pr * c.ng);
+      kc_zero = meta_adv<kMeta16>(kc_zero, pr * c.ng);
       krow -= static_cast<uint32_t>(ts);
     }
     const uint8_t *ks = kc_codes + (krow * (D * KBITS / 8) + static_cast<uint32_t>(d0 * KBITS / 8));
@@ -291,9 +311,9 @@ __device__ inline void fetch_k(const Ctx &c, int k0, int tid, Fetch &f, size_t p
     }
     const uint32_t km = krow * static_cast<uint32_t>(c.ng);
     const int gj = ((tid & 7) >> 1) < c.ng ? ((tid & 7) >> 1) : c.ng - 1;
-    f.kstep = kc_scale[km + static_cast<uint32_t>(d0 >> c.group_shift)];
-    f.kzero = kc_zero[km + static_cast<uint32_t>(d0 >> c.group_shift)];
-    f.gstep = kc_scale[km + static_cast<uint32_t>(gj)];
+    f.kstep = meta_ld<kMeta16>(kc_scale, km + static_cast<uint32_t>(d0 >> c.group_shift));
+    f.kzero = meta_ld<kMeta16>(kc_zero, km + static_cast<uint32_t>(d0 >> c.group_shift));
+    f.gstep = meta_ld<kMeta16>(kc_scale, km + static_cast<uint32_t>(gj));
   } else {
     const uint4 *ks = reinterpret_cast<const uint4 *>(c.k_cur + (krow * D + static_cast<uint32_t>(d0)));
     const uint4 a = ks[0], b = ks[1];
@@ -313,16 +333,16 @@ __device__ inline void fetch_v(const Ctx &c, int k0, int tid, int j, Fetch &f, s
     if (PAGED) {
       const int ts = tile_start(c, k0);
       vc_codes += pr * (D * VBITS / 8);
-      vc_scale += pr * c.ng;
-      vc_zero += pr * c.ng;
+      vc_scale = meta_adv<kMeta16>(vc_scale, pr * c.ng);
+      vc_zero = meta_adv<kMeta16>(vc_zero, pr * c.ng);
       vrow -= static_cast<uint32_t>(ts);
     }
     const uint8_t *vs = vc_codes + (vrow * (D * VBITS / 8) + static_cast<uint32_t>(dq * VBITS));
     f.vw[j] = VBITS == 4 ? *reinterpret_cast<const uint32_t *>(vs)
                          : static_cast<uint32_t>(*reinterpret_cast<const uint16_t *>(vs));
     const uint32_t vm = vrow * static_cast<uint32_t>(c.ng) + static_cast<uint32_t>((8 * dq) >> c.group_shift);
-    f.vstep[j] = vc_scale[vm];
-    f.vzero[j] = vc_zero[vm];
+    f.vstep[j] = meta_ld<kMeta16>(vc_scale, vm);
+    f.vzero[j] = meta_ld<kMeta16>(vc_zero, vm);
   } else {
     const uint4 v = *reinterpret_cast<const uint4 *>(c.v_cur + (vrow * D + static_cast<uint32_t>(8 * dq)));
     f.vw[4 * j] = v.x; f.vw[4 * j + 1] = v.y; f.vw[4 * j + 2] = v.z; f.vw[4 * j + 3] = v.w;
@@ -693,7 +713,8 @@ __device__ inline void segment(const Ctx &c, QState &qs, Soft &st, uint16_t *Kl,
   __syncthreads();
 }
 
-template <int KBITS, int VBITS, bool TAYLOR, bool CAUSAL, bool PAGED>
+// (M16 names the metadata type in the kernel's symbol; it equals kMeta16.)
+template <int KBITS, int VBITS, bool TAYLOR, bool CAUSAL, bool PAGED, bool M16>
 __global__ __launch_bounds__(THREADS, 1) void attn_fast_kernel(AttnLaunch p, int32_t group_shift,
                                                                 int64_t rows_per_kvhead, int32_t row_blocks,
                                                                 const float *kpart, int32_t nsplit,
@@ -780,10 +801,10 @@ __global__ __launch_bounds__(THREADS, 1) void attn_fast_kernel(AttnLaunch p, int
     const int64_t hrow = PAGED ? 0 : bkv * p.cap;  // first cache row of this head (paged: the pool)
     c.kc_codes = p.kc_codes + hrow * (D * KBITS / 8);
     c.vc_codes = p.vc_codes + hrow * (D * VBITS / 8);
-    c.kc_scale = p.kc_scale + hrow * ng;
-    c.kc_zero = p.kc_zero + hrow * ng;
-    c.vc_scale = p.vc_scale + hrow * ng;
-    c.vc_zero = p.vc_zero + hrow * ng;
+    c.kc_scale = meta_adv<M16>(p.kc_scale, hrow * ng);
+    c.kc_zero = meta_adv<M16>(p.kc_zero, hrow * ng);
+    c.vc_scale = meta_adv<M16>(p.vc_scale, hrow * ng);
+    c.vc_zero = meta_adv<M16>(p.vc_zero, hrow * ng);
   }
   // this split's tiles [t0, t1) of the cached tiles followed by the current ones
   const int tc = static_cast<int>((p.Nc + BN - 1) / BN), tu = static_cast<int>((p.Ncur + BN - 1) / BN);
@@ -881,8 +902,8 @@ hipError_t launch_bits(const AttnLaunch &p, hipStream_t stream) {
   const int64_t nfull = nsplit > 1 ? p.fast_full_units : units;
   const dim3 grid(static_cast<uint32_t>(nfull + (units - nfull) * nsplit));
   constexpr bool CAUSAL = KVQ_FAST_CAUSAL != 0, PAGED = KVQ_FAST_PAGED != 0;
-  auto kernel = p.corr == KV_CORR_TAYLOR ? attn_fast_kernel<KB, VB, true, CAUSAL, PAGED>
-                                         : attn_fast_kernel<KB, VB, false, CAUSAL, PAGED>;
+  auto kernel = p.corr == KV_CORR_TAYLOR ? attn_fast_kernel<KB, VB, true, CAUSAL, PAGED, kMeta16>
+                                         : attn_fast_kernel<KB, VB, false, CAUSAL, PAGED, kMeta16>;
   kernel<<<grid, dim3(THREADS), 0, stream>>>(p, gshift, rows, row_blocks, kpart, nsplit, partials, nfull);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
@@ -895,8 +916,16 @@ hipError_t launch_bits(const AttnLaunch &p, hipStream_t stream) {
 
 }  // namespace
 
-#if KVQ_FAST_PAGED || KVQ_FAST_CAUSAL
-#if KVQ_FAST_PAGED && KVQ_FAST_CAUSAL
+#if KVQ_FAST_PAGED || KVQ_FAST_CAUSAL || KVQ_FAST_META16
+#if KVQ_FAST_META16 && KVQ_FAST_PAGED && KVQ_FAST_CAUSAL
+hipError_t launch_attention_fast_m16_paged_causal(const AttnLaunch &p, hipStream_t stream) {
+#elif KVQ_FAST_META16 && KVQ_FAST_PAGED
+hipError_t launch_attention_fast_m16_paged(const AttnLaunch &p, hipStream_t stream) {
+#elif KVQ_FAST_META16 && KVQ_FAST_CAUSAL
+hipError_t launch_attention_fast_m16_causal(const AttnLaunch &p, hipStream_t stream) {
+#elif KVQ_FAST_META16
+hipError_t launch_attention_fast_m16(const AttnLaunch &p, hipStream_t stream) {
+#elif KVQ_FAST_PAGED && KVQ_FAST_CAUSAL
 hipError_t launch_attention_fast_paged_causal(const AttnLaunch &p, hipStream_t stream) {
 #elif KVQ_FAST_PAGED
 hipError_t launch_attention_fast_paged(const AttnLaunch &p, hipStream_t stream) {
@@ -915,10 +944,10 @@ bool fast_path_supported(const AttnLaunch &p) { return p.d == D && p.corr != KV_
 void launch_key_scale(const AttnLaunch &p, hipStream_t stream, float *part) {
   const int32_t ng = D / p.group;
   const dim3 grid(static_cast<uint32_t>(p.B * p.Hkv * KCHUNKS));
-  if (p.Nc > 0 && p.kbits == 4)
-    key_scale_kernel<4><<<grid, dim3(256), 0, stream>>>(p, ng, part);
-  else
-    key_scale_kernel<2><<<grid, dim3(256), 0, stream>>>(p, ng, part);
+  const bool k4 = p.Nc > 0 && p.kbits == 4;
+  auto kernel = p.meta16 ? (k4 ? key_scale_kernel<4, true> : key_scale_kernel<2, true>)
+                         : (k4 ? key_scale_kernel<4, false> : key_scale_kernel<2, false>);
+  kernel<<<grid, dim3(256), 0, stream>>>(p, ng, part);
 }
 
 size_t fast_path_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int splits) {
@@ -973,6 +1002,11 @@ int fast_path_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nc,
 }
 
 hipError_t launch_attention_fast(const AttnLaunch &p, hipStream_t stream) {
+  if (p.meta16) {
+    if (p.layout.page_table)
+      return p.causal ? launch_attention_fast_m16_paged_causal(p, stream) : launch_attention_fast_m16_paged(p, stream);
+    return p.causal ? launch_attention_fast_m16_causal(p, stream) : launch_attention_fast_m16(p, stream);
+  }
   if (p.layout.page_table)
     return p.causal ? launch_attention_fast_paged_causal(p, stream) : launch_attention_fast_paged(p, stream);
   if (p.causal) return launch_attention_fast_causal(p, stream);

@@ -29,10 +29,11 @@
 // the next block, S^T = K Q^T (8 fp16 MFMA + 1 correction step), mask the
 // ragged block, lazy max, exponentials, O^T += V^T P^T (8 fp16 MFMA).
 //
-// Paged caches: the instances for the paged layout are built from this file
-// in a translation unit of their own (attention_short_paged.hip defines
-// KVQ_SHORT_PAGED to 1), so that they cannot change how the contiguous ones
-// are compiled.
+// Paged caches and binary16 metadata: the instances for them are built from
+// this file in translation units of their own (attention_short_paged.hip,
+// attention_short_m16.hip, attention_short_m16_paged.hip define
+// KVQ_SHORT_PAGED / KVQ_SHORT_META16), so that they cannot change how the
+// default ones are compiled.
 #include <math.h>
 
 #include "kvq_device.h"
@@ -40,6 +41,9 @@
 
 #ifndef KVQ_SHORT_PAGED
 #define KVQ_SHORT_PAGED 0
+#endif
+#ifndef KVQ_SHORT_META16
+#define KVQ_SHORT_META16 0
 #endif
 
 namespace kvq {
@@ -115,6 +119,29 @@ __device__ inline uint32_t ld32(Buf b, uint32_t off) { return __builtin_amdgcn_r
 __device__ inline u32x2 ld64(Buf b, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b64(b, off, 0, 0); }
 __device__ inline u32x4 ld128(Buf b, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b128(b, off, 0, 0); }
 
+// Step / zero-point elements (fp32, or binary16 when M16) at a byte offset:
+// one element, or two consecutive ones.
+template <bool M16>
+__device__ inline float ld_meta1(Buf b, uint32_t off) {
+  if (M16) return static_cast<float>(__builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(b, off, 0, 0)));
+  return __uint_as_float(ld32(b, off));
+}
+template <bool M16>
+__device__ inline float2 ld_meta2(Buf b, uint32_t off) {
+  if (M16) {
+    const uint32_t w = ld32(b, off);
+    return make_float2(static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w))),
+                       static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16))));
+  }
+  const u32x2 w = ld64(b, off);
+  return make_float2(__uint_as_float(w.x), __uint_as_float(w.y));
+}
+// A step or zero-point array advanced by n elements.
+template <bool M16>
+__device__ inline const float *meta_adv(const float *p, int64_t n) {
+  return reinterpret_cast<const float *>(reinterpret_cast<const char *>(p) + n * (M16 ? 2 : 4));
+}
+
 // floor(log2 x) for x > 0 (one v_frexp_exp_i32_f32).
 __device__ inline int ilog2_pos(float x) { return __builtin_amdgcn_frexp_expf(x) - 1; }
 
@@ -134,15 +161,15 @@ __device__ inline int value_exponent(float vmax) { return vmax > 0.f ? ilog2_pos
 struct Lanes {
   uint32_t kc, km, vc, vm;
 };
-template <int KBITS, int VBITS, int NG>
+template <int KBITS, int VBITS, int NG, bool M16>
 __device__ inline Lanes lane_offsets(int lane) {
-  constexpr uint32_t KROW = D * KBITS / 8, VROW = D * VBITS / 8;
+  constexpr uint32_t KROW = D * KBITS / 8, VROW = D * VBITS / 8, ES = M16 ? 2 : 4;
   const uint32_t kr = lane & 31, h = lane >> 5, kq = lane & 7, dq = lane >> 3;
   Lanes o;
   o.kc = kr * KROW + h * (KROW / 2);
-  o.km = kr * NG * 4;
+  o.km = kr * NG * ES;
   o.vc = 4 * kq * VROW + 16 * dq * VBITS / 8;
-  o.vm = (4 * kq * NG + (16 * dq * NG) / D) * 4;  // the group of d = 16dq
+  o.vm = (4 * kq * NG + (16 * dq * NG) / D) * ES;  // the group of d = 16dq
   return o;
 }
 
@@ -159,9 +186,9 @@ __device__ inline size_t block_row(const Ctx &c, int k0) {
 // Loads one cached block (rows [k0, k0 + 32)); rows at or past the segment
 // end read as zero (their scores are masked).  Paged: the buffer range stops
 // at the block's end, inside its page.
-template <int KBITS, int VBITS, int NG, bool PAGED>
+template <int KBITS, int VBITS, int NG, bool PAGED, bool M16>
 __device__ inline void fetch_cached(const Ctx &c, int k0, const Lanes &o, int h, Fetch &f, size_t pool_row = 0) {
-  constexpr uint32_t KROW = D * KBITS / 8, VROW = D * VBITS / 8;
+  constexpr uint32_t KROW = D * KBITS / 8, VROW = D * VBITS / 8, ES = M16 ? 2 : 4;
   const uint32_t rows = static_cast<uint32_t>(PAGED ? min(c.nc - k0, BK) : c.nc - k0);
   const size_t r0 = PAGED ? pool_row : block_row<false>(c, k0);  // paged: looked up a block earlier
   {
@@ -172,33 +199,33 @@ __device__ inline void fetch_cached(const Ctx &c, int k0, const Lanes &o, int h,
       const u32x4 b = ld128(kc, o.kc + 16);
       f.kw[4] = b.x; f.kw[5] = b.y; f.kw[6] = b.z; f.kw[7] = b.w;
     }
-    const Buf ks = buffer_at(c.kc_scale + r0 * NG, rows * NG * 4);
-    const Buf kz = buffer_at(c.kc_zero + r0 * NG, rows * NG * 4);
+    const Buf ks = buffer_at(meta_adv<M16>(c.kc_scale, r0 * NG), rows * NG * ES);
+    const Buf kz = buffer_at(meta_adv<M16>(c.kc_zero, r0 * NG), rows * NG * ES);
     // groups of d = 64h + 32j (kstep, kzero) and groups 2h + j (gstep; only
     // those below NG are used)
     if (NG == 1) {
-      const float st = __uint_as_float(ld32(ks, o.km)), z = __uint_as_float(ld32(kz, o.km));
+      const float st = ld_meta1<M16>(ks, o.km), z = ld_meta1<M16>(kz, o.km);
       f.kstep[0] = f.kstep[1] = f.gstep[0] = f.gstep[1] = st;
       f.kzero[0] = f.kzero[1] = z;
     } else if (NG == 2) {
-      const u32x2 st = ld64(ks, o.km);
-      const float z = __uint_as_float(ld32(kz, o.km + 4 * h));
-      f.kstep[0] = f.kstep[1] = __uint_as_float(h ? st.y : st.x);
+      const float2 st = ld_meta2<M16>(ks, o.km);
+      const float z = ld_meta1<M16>(kz, o.km + ES * h);
+      f.kstep[0] = f.kstep[1] = h ? st.y : st.x;
       f.kzero[0] = f.kzero[1] = z;
-      f.gstep[0] = __uint_as_float(st.x);
-      f.gstep[1] = __uint_as_float(st.y);
+      f.gstep[0] = st.x;
+      f.gstep[1] = st.y;
     } else {
-      const u32x2 st = ld64(ks, o.km + 8 * h), z = ld64(kz, o.km + 8 * h);
-      f.kstep[0] = f.gstep[0] = __uint_as_float(st.x);
-      f.kstep[1] = f.gstep[1] = __uint_as_float(st.y);
-      f.kzero[0] = __uint_as_float(z.x);
-      f.kzero[1] = __uint_as_float(z.y);
+      const float2 st = ld_meta2<M16>(ks, o.km + 2 * ES * h), z = ld_meta2<M16>(kz, o.km + 2 * ES * h);
+      f.kstep[0] = f.gstep[0] = st.x;
+      f.kstep[1] = f.gstep[1] = st.y;
+      f.kzero[0] = z.x;
+      f.kzero[1] = z.y;
     }
   }
   {
     const Buf vc = buffer_at(c.vc_codes + r0 * VROW, rows * VROW);
-    const Buf vs = buffer_at(c.vc_scale + r0 * NG, rows * NG * 4);
-    const Buf vz = buffer_at(c.vc_zero + r0 * NG, rows * NG * 4);
+    const Buf vs = buffer_at(meta_adv<M16>(c.vc_scale, r0 * NG), rows * NG * ES);
+    const Buf vz = buffer_at(meta_adv<M16>(c.vc_zero, r0 * NG), rows * NG * ES);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (VBITS == 4) {
@@ -208,8 +235,8 @@ __device__ inline void fetch_cached(const Ctx &c, int k0, const Lanes &o, int h,
       } else {
         f.vw[j] = ld32(vc, o.vc + j * VROW);
       }
-      f.vstep[j] = __uint_as_float(ld32(vs, o.vm + j * NG * 4));
-      f.vzero[j] = __uint_as_float(ld32(vz, o.vm + j * NG * 4));
+      f.vstep[j] = ld_meta1<M16>(vs, o.vm + j * NG * ES);
+      f.vzero[j] = ld_meta1<M16>(vz, o.vm + j * NG * ES);
     }
   }
 }
@@ -486,7 +513,7 @@ __device__ inline void block_compute(const f16x8 (&k)[8], bf16x8 kext, const uin
     }
 }
 
-template <int KBITS, int VBITS, bool TAYLOR, int NG, bool CAUSAL, bool PAGED>
+template <int KBITS, int VBITS, bool TAYLOR, int NG, bool CAUSAL, bool PAGED, bool M16>
 __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, int64_t rows_per_kvhead,
                                                                 int32_t row_groups, int32_t nsplit, float *ws) {
   __shared__ __attribute__((aligned(16))) uint16_t L[LDS_BYTES / 2];
@@ -539,10 +566,10 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
     const int64_t hrow = PAGED ? 0 : bkv * p.cap;  // paged: the pointers stay at the pool
     c.kc_codes = p.kc_codes + hrow * (D * KBITS / 8);
     c.vc_codes = p.vc_codes + hrow * (D * VBITS / 8);
-    c.kc_scale = p.kc_scale + hrow * ng;
-    c.kc_zero = p.kc_zero + hrow * ng;
-    c.vc_scale = p.vc_scale + hrow * ng;
-    c.vc_zero = p.vc_zero + hrow * ng;
+    c.kc_scale = meta_adv<M16>(p.kc_scale, hrow * ng);
+    c.kc_zero = meta_adv<M16>(p.kc_zero, hrow * ng);
+    c.vc_scale = meta_adv<M16>(p.vc_scale, hrow * ng);
+    c.vc_zero = meta_adv<M16>(p.vc_zero, hrow * ng);
   }
   if (p.Ncur > 0) {
     c.k_cur = p.k_cur + bkv * p.Ncur * D;
@@ -569,12 +596,12 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
 
   int blk = bbeg + wave;
   const int cend = bend < nbc ? bend : nbc;
-  const Lanes lo = lane_offsets<KBITS, VBITS, NG>(lane);
+  const Lanes lo = lane_offsets<KBITS, VBITS, NG, M16>(lane);
   Scales sc;
   f16x8 kreg[8];
   bf16x8 kext = {};
   Fetch f;
-  if (blk < cend) fetch_cached<KBITS, VBITS, NG, PAGED>(c, blk * BK, lo, h, f, block_row<PAGED>(c, blk * BK));
+  if (blk < cend) fetch_cached<KBITS, VBITS, NG, PAGED, M16>(c, blk * BK, lo, h, f, block_row<PAGED>(c, blk * BK));
   // paged: the pool row of the next block to fetch, looked up one block ahead
   // so that its scalar load has completed when the fetch needs it
   size_t prn = PAGED && blk + WAVES < cend ? block_row<PAGED>(c, (blk + WAVES) * BK) : 0;
@@ -584,7 +611,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
     sc.update(k_bound<KBITS>(f), v_bound<VBITS>(f), st.alpha);
     unpack_k_cached<TAYLOR, KBITS, NG>(c, lane, f, sc.kscale, kreg, kext);
     unpack_v_cached<VBITS>(c, lane, f, sc.vscale, Vt);
-    if (blk + WAVES < cend) fetch_cached<KBITS, VBITS, NG, PAGED>(c, (blk + WAVES) * BK, lo, h, f, prn);
+    if (blk + WAVES < cend) fetch_cached<KBITS, VBITS, NG, PAGED, M16>(c, (blk + WAVES) * BK, lo, h, f, prn);
     block_compute<TAYLOR>(kreg, kext, Vt, q, qext, count, sc.alpha, sc.ev, lane, st);
     if (PAGED && blk + 2 * WAVES < cend) prn = block_row<PAGED>(c, (blk + 2 * WAVES) * BK);
   }
@@ -662,11 +689,11 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
 template <int KB, int VB, int NG>
 void launch_kernel(const AttnLaunch &p, hipStream_t stream, dim3 grid, int64_t rows, int32_t row_groups,
                    float *partials) {
-  constexpr bool PG = KVQ_SHORT_PAGED != 0;
-  auto kernel = p.corr == KV_CORR_TAYLOR ? (p.causal ? attn_short_kernel<KB, VB, true, NG, true, PG>
-                                                     : attn_short_kernel<KB, VB, true, NG, false, PG>)
-                                         : (p.causal ? attn_short_kernel<KB, VB, false, NG, true, PG>
-                                                     : attn_short_kernel<KB, VB, false, NG, false, PG>);
+  constexpr bool PG = KVQ_SHORT_PAGED != 0, MH = KVQ_SHORT_META16 != 0;
+  auto kernel = p.corr == KV_CORR_TAYLOR ? (p.causal ? attn_short_kernel<KB, VB, true, NG, true, PG, MH>
+                                                     : attn_short_kernel<KB, VB, true, NG, false, PG, MH>)
+                                         : (p.causal ? attn_short_kernel<KB, VB, false, NG, true, PG, MH>
+                                                     : attn_short_kernel<KB, VB, false, NG, false, PG, MH>);
   kernel<<<grid, dim3(THREADS), 0, stream>>>(p, rows, row_groups, p.splits, partials);
 }
 
@@ -690,8 +717,14 @@ hipError_t launch_bits(const AttnLaunch &p, hipStream_t stream) {
 
 }  // namespace
 
-#if KVQ_SHORT_PAGED
+#if KVQ_SHORT_PAGED || KVQ_SHORT_META16
+#if KVQ_SHORT_PAGED && KVQ_SHORT_META16
+hipError_t launch_attention_short_fast_m16_paged(const AttnLaunch &p, hipStream_t stream) {
+#elif KVQ_SHORT_PAGED
 hipError_t launch_attention_short_fast_paged(const AttnLaunch &p, hipStream_t stream) {
+#else
+hipError_t launch_attention_short_fast_m16(const AttnLaunch &p, hipStream_t stream) {
+#endif
   const int kb = p.Nc > 0 ? p.kbits : 2, vb = p.Nc > 0 ? p.vbits : 2;
   if (kb == 2 && vb == 2) return launch_bits<2, 2>(p, stream);
   if (kb == 2 && vb == 4) return launch_bits<2, 4>(p, stream);
@@ -716,6 +749,8 @@ int short_fast_splits(int64_t B, int64_t Hkv, int64_t rows_per_kvhead, int64_t N
 }
 
 hipError_t launch_attention_short_fast(const AttnLaunch &p, hipStream_t stream) {
+  if (p.meta16)
+    return p.layout.page_table ? launch_attention_short_fast_m16_paged(p, stream) : launch_attention_short_fast_m16(p, stream);
   if (p.layout.page_table) return launch_attention_short_fast_paged(p, stream);
   const int kb = p.Nc > 0 ? p.kbits : 2, vb = p.Nc > 0 ? p.vbits : 2;
   if (kb == 2 && vb == 2) return launch_bits<2, 2>(p, stream);

@@ -1,0 +1,5 @@
+// Binary16-metadata, paged-cache instances of the short-query kernel, built in their own
+// translation unit; the kernel itself is in attention_short.hip.
+#define KVQ_SHORT_PAGED 1
+#define KVQ_SHORT_META16 1
+#include "attention_short.hip"

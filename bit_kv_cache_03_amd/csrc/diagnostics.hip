@@ -196,8 +196,8 @@ __global__ __launch_bounds__(THREADS) void attn_diag_kernel(DiagLaunch p, int32_
       if (cached) {
         const int64_t row = p.layout.row(p.cap, p.Hkv, b, hk, k0 + (ok ? key : 0));  // cache row of the key
         const int g = d0 >> group_shift;
-        const float st = ok ? p.kc_scale[row * ng + g] : 0.f;
-        const float zp = ok ? p.kc_zero[row * ng + g] : 0.f;
+        const float st = ok ? meta_at(p.kc_scale, row * ng + g, p.meta16) : 0.f;
+        const float zp = ok ? meta_at(p.kc_zero, row * ng + g, p.meta16) : 0.f;
         constexpr int WORDS = DPT * KBITS / 32;
         constexpr int PER = 32 / KBITS;
         uint32_t w[WORDS];
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(THREADS) void attn_diag_kernel(DiagLaunch p, int32_
           float e16[16];
           float dsh[4] = {0.f, 0.f, 0.f, 0.f}, dsl[4] = {0.f, 0.f, 0.f, 0.f};
           for (int gg = 0; gg < ng; ++gg) {
-            const float s = ok ? p.kc_scale[row * ng + gg] : 0.f;
+            const float s = ok ? meta_at(p.kc_scale, row * ng + gg, p.meta16) : 0.f;
             dsh[gg] = bf16_round(s * s);
             dsl[gg] = s * s - dsh[gg];
             if (EXACT) Dk[key * 4 + gg] = s;

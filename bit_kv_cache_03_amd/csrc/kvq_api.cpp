@@ -11,7 +11,7 @@ namespace {
 
 using kvq::AttnLaunch;
 
-constexpr int32_t kAbiVersion = 4;
+constexpr int32_t kAbiVersion = 5;
 constexpr int32_t kMaxSplits = 1024;  // grid z extent of the split path
 constexpr int64_t kMaxTokensPerHead = int64_t(1) << 23;  // 8M tokens: 32-bit in-head offsets
 
@@ -50,6 +50,7 @@ kv_status check_qtensor(const kv_qtensor *t, int32_t d, int64_t need_rows, int64
   if (t->cap < need_rows || t->cap < 0) return KV_ERR_SHAPE;
   if (t->cap > kMaxTokensPerHead) return KV_ERR_UNSUPPORTED;
   if (!aligned16(t->codes) || !aligned16(t->scale) || !aligned16(t->zero)) return KV_ERR_ALIGN;
+  if (t->meta != KV_META_F32 && t->meta != KV_META_F16) return KV_ERR_UNSUPPORTED;
   if (t->page_table) {
     if (!page_size_ok(t->page_size) || t->cap % t->page_size != 0) return KV_ERR_SHAPE;
     if (t->num_pages < 1) return KV_ERR_SHAPE;
@@ -73,8 +74,11 @@ int64_t tensor_rows(const kv_qtensor *t, int64_t B, int64_t H) {
 }
 
 bool same_layout(const kv_qtensor *a, const kv_qtensor *b) {
-  return a->page_table == b->page_table && a->page_size == b->page_size;
+  return a->page_table == b->page_table && a->page_size == b->page_size && a->meta == b->meta;
 }
+
+// Bytes of one step or zero-point element.
+size_t meta_bytes(const kv_qtensor *t) { return t->meta == KV_META_F16 ? 2 : 4; }
 
 bool debug_log() {
   const char *e = getenv("KVQ_LOG");
@@ -148,7 +152,8 @@ kv_status validate_attention(const kv_attn_args *a) {
       const size_t rows = static_cast<size_t>(tensor_rows(c, a->B, a->Hkv));
       const size_t ng = static_cast<size_t>(a->d / c->group);
       if (overlaps(a->out, out_b, c->codes, rows * static_cast<size_t>(a->d * c->bits / 8)) ||
-          overlaps(a->out, out_b, c->scale, rows * ng * 4) || overlaps(a->out, out_b, c->zero, rows * ng * 4))
+          overlaps(a->out, out_b, c->scale, rows * ng * meta_bytes(c)) ||
+          overlaps(a->out, out_b, c->zero, rows * ng * meta_bytes(c)))
         return KV_ERR_ALIAS;
     }
   }
@@ -193,7 +198,8 @@ kv_status validate_diagnostics(const kv_diag_args *a) {
     const size_t ng = static_cast<size_t>(a->d / c->group);
     if (overlaps(a->out, out_b, a->k_ref, static_cast<size_t>(nc_el) * 2) ||
         overlaps(a->out, out_b, c->codes, rows * static_cast<size_t>(a->d * c->bits / 8)) ||
-        overlaps(a->out, out_b, c->scale, rows * ng * 4) || overlaps(a->out, out_b, c->zero, rows * ng * 4))
+        overlaps(a->out, out_b, c->scale, rows * ng * meta_bytes(c)) ||
+          overlaps(a->out, out_b, c->zero, rows * ng * meta_bytes(c)))
       return KV_ERR_ALIAS;
   }
   return KV_OK;
@@ -266,10 +272,11 @@ kv_status kv_quantize(const void *x, kv_dtype xdt, int64_t B, int64_t H, int64_t
   if (!mul_ok(B, H, &t) || !mul_ok(t, N, &t) || !mul_ok(t, d, &t) || t > (int64_t(1) << 40)) return KV_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(dst->codes) || !aligned16(dst->scale) || !aligned16(dst->zero))
     return KV_ERR_ALIGN;
+  if (dst->meta != KV_META_F32 && dst->meta != KV_META_F16) return KV_ERR_UNSUPPORTED;
   if (N == 0) return KV_OK;
-  kvq::QuantizeLaunch p{x, static_cast<int>(xdt), B, H, N, d, dst->codes, dst->scale, dst->zero,
-                        dst->bits, dst->group, dst->cap, tok_offset,
-                        layout_of(dst)};
+  kvq::QuantizeLaunch p{x, static_cast<int>(xdt), B, H, N, d, dst->codes, static_cast<float *>(dst->scale),
+                        static_cast<float *>(dst->zero), dst->bits, dst->group, dst->cap, tok_offset,
+                        layout_of(dst), dst->meta == KV_META_F16};
   return kvq::launch_quantize(p, static_cast<hipStream_t>(stream)) == hipSuccess ? KV_OK : KV_ERR_HIP;
 }
 
@@ -292,8 +299,13 @@ kv_status kv_attention_corrected(const kv_attn_args *a, void *stream) {
   p.v_cur = static_cast<const uint16_t *>(a->v_cur);
   p.out = static_cast<uint16_t *>(a->out);
   if (a->Nc > 0) {
-    p.kc_codes = a->k_cache->codes; p.kc_scale = a->k_cache->scale; p.kc_zero = a->k_cache->zero;
-    p.vc_codes = a->v_cache->codes; p.vc_scale = a->v_cache->scale; p.vc_zero = a->v_cache->zero;
+    p.kc_codes = a->k_cache->codes;
+    p.kc_scale = static_cast<const float *>(a->k_cache->scale);
+    p.kc_zero = static_cast<const float *>(a->k_cache->zero);
+    p.vc_codes = a->v_cache->codes;
+    p.vc_scale = static_cast<const float *>(a->v_cache->scale);
+    p.vc_zero = static_cast<const float *>(a->v_cache->zero);
+    p.meta16 = a->k_cache->meta == KV_META_F16;
     p.kbits = a->k_cache->bits; p.vbits = a->v_cache->bits; p.group = a->k_cache->group; p.cap = a->k_cache->cap;
     p.layout = layout_of(a->k_cache);
   } else {
@@ -323,7 +335,10 @@ kv_status kv_attention_diagnostics(const kv_diag_args *a, void *stream) {
   p.k_cur = static_cast<const uint16_t *>(a->k_cur);
   p.k_ref = static_cast<const uint16_t *>(a->k_ref);
   if (a->Nc > 0) {
-    p.kc_codes = a->k_cache->codes; p.kc_scale = a->k_cache->scale; p.kc_zero = a->k_cache->zero;
+    p.kc_codes = a->k_cache->codes;
+    p.kc_scale = static_cast<const float *>(a->k_cache->scale);
+    p.kc_zero = static_cast<const float *>(a->k_cache->zero);
+    p.meta16 = a->k_cache->meta == KV_META_F16;
     p.kbits = a->k_cache->bits; p.group = a->k_cache->group; p.cap = a->k_cache->cap;
     p.layout = layout_of(a->k_cache);
   } else {

@@ -27,6 +27,12 @@ struct CacheLayout {
   }
 };
 
+// Metadata element i of a step or zero-point array stored as fp32, or as
+// binary16 when meta16 (the pointer then addresses binary16 elements).
+__host__ __device__ inline float meta_at(const float *p, int64_t i, bool meta16) {
+  return meta16 ? static_cast<float>(reinterpret_cast<const _Float16 *>(p)[i]) : p[i];
+}
+
 // Everything a quantize launch needs, already validated by the host.
 struct QuantizeLaunch {
   const void *x;
@@ -39,6 +45,7 @@ struct QuantizeLaunch {
   int32_t bits, group;
   int64_t cap, off;
   CacheLayout layout;
+  bool meta16;  // scale and zero are binary16 (the pointers are then read as such)
 };
 
 // Everything an attention launch needs, already validated by the host.
@@ -52,6 +59,7 @@ struct AttnLaunch {
   int32_t kbits, vbits, group;
   int64_t cap;
   CacheLayout layout;  // of both caches
+  bool meta16;         // the caches' scale and zero are binary16 (pointers read as such)
   float tau;   // resolved softmax scale
   int corr;    // kv_corr
   int causal;  // 1: current key i visible to query row j only if i <= j + Ncur - Nq
@@ -87,6 +95,12 @@ hipError_t launch_attention_fast(const AttnLaunch &p, hipStream_t stream);
 hipError_t launch_attention_fast_causal(const AttnLaunch &p, hipStream_t stream);
 hipError_t launch_attention_fast_paged(const AttnLaunch &p, hipStream_t stream);
 hipError_t launch_attention_fast_paged_causal(const AttnLaunch &p, hipStream_t stream);
+// Binary16 steps and zero points: the same four variants
+// (attention_fast_m16*.hip).
+hipError_t launch_attention_fast_m16(const AttnLaunch &p, hipStream_t stream);
+hipError_t launch_attention_fast_m16_causal(const AttnLaunch &p, hipStream_t stream);
+hipError_t launch_attention_fast_m16_paged(const AttnLaunch &p, hipStream_t stream);
+hipError_t launch_attention_fast_m16_paged_causal(const AttnLaunch &p, hipStream_t stream);
 // Pre-pass of the throughput kernel: per (b, KV head), 32 partial bounds of
 // |key| (dequantised cache and current chunk) and of |query|, from which the
 // kernel takes the exponent that balances its fp16 key and query operands.
@@ -103,8 +117,12 @@ hipError_t launch_combine(const float *ws, uint16_t *out, int64_t nrows, int spl
 bool short_fast_supported(int32_t d, int corr);
 int short_fast_splits(int64_t B, int64_t Hkv, int64_t rows_per_kvhead, int64_t Nc, int64_t Ncur, int cu_count);
 hipError_t launch_attention_short_fast(const AttnLaunch &p, hipStream_t stream);
-// The same over a paged cache (built in attention_short_paged.hip).
+// The same over a paged cache, with binary16 metadata, and both (built in
+// attention_short_paged.hip, attention_short_m16.hip,
+// attention_short_m16_paged.hip).
 hipError_t launch_attention_short_fast_paged(const AttnLaunch &p, hipStream_t stream);
+hipError_t launch_attention_short_fast_m16(const AttnLaunch &p, hipStream_t stream);
+hipError_t launch_attention_short_fast_m16_paged(const AttnLaunch &p, hipStream_t stream);
 
 // Everything a diagnostics launch needs, already validated by the host.
 struct DiagLaunch {
@@ -116,6 +134,7 @@ struct DiagLaunch {
   int32_t kbits, group;
   int64_t cap;
   CacheLayout layout;
+  bool meta16;
   float tau;   // resolved softmax scale
   int corr;    // kv_corr
   int causal;

@@ -56,8 +56,10 @@ __device__ inline void load8<float>(const float *p, float (&v)[8]) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
-// T: uint16_t (bf16 bits) or float.  LANES = group / 8.
-template <typename T, int BITS, int LANES>
+// T: uint16_t (bf16 bits) or float.  LANES = group / 8.  M16: the step and
+// zero point are stored as binary16, rounded (nearest, ties to even) before
+// the codes are taken so that z + D c uses exactly what is stored.
+template <typename T, int BITS, int LANES, bool M16>
 __global__ __launch_bounds__(kThreads) void quantize_pack(
     const T *__restrict__ x, int64_t total_lanes, int32_t lanes_per_row, int64_t N,
     uint8_t *__restrict__ codes, float *__restrict__ scale, float *__restrict__ zero,
@@ -82,14 +84,19 @@ __global__ __launch_bounds__(kThreads) void quantize_pack(
   mn = group_min<LANES>(mn) + 0.0f;  // + 0.0f: a zero extreme is +0
   mx = group_max<LANES>(mx) + 0.0f;
   const float range = mx - mn;
-  const float step = range / static_cast<float>(TOP);  // IEEE division
+  float step = range / static_cast<float>(TOP);  // IEEE division
+  float zp = mn;
+  if (M16) {
+    step = static_cast<float>(static_cast<_Float16>(step));
+    zp = static_cast<float>(static_cast<_Float16>(mn));
+  }
 
   uint32_t packed = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     uint32_t c = 0;
     if (step > 0.0f) {
-      const float t = (v[i] - mn) / step;  // IEEE division
+      const float t = (v[i] - zp) / step;  // IEEE division
       const float r = fminf(fmaxf(rintf(t), 0.0f), static_cast<float>(TOP));
       c = static_cast<uint32_t>(r);
     }
@@ -109,12 +116,17 @@ __global__ __launch_bounds__(kThreads) void quantize_pack(
   }
   if ((chunk % LANES) == 0) {
     const int64_t m = orow * groups_per_row + chunk / LANES;
-    scale[m] = step;
-    zero[m] = mn;
+    if (M16) {
+      reinterpret_cast<_Float16 *>(scale)[m] = static_cast<_Float16>(step);
+      reinterpret_cast<_Float16 *>(zero)[m] = static_cast<_Float16>(zp);
+    } else {
+      scale[m] = step;
+      zero[m] = mn;
+    }
   }
 }
 
-template <typename T, int BITS>
+template <typename T, int BITS, bool M16>
 hipError_t launch_t(const QuantizeLaunch &p, hipStream_t stream) {
   const int32_t lanes_per_row = p.d / 8;
   const int64_t total = p.B * p.H * p.N * lanes_per_row;
@@ -123,15 +135,15 @@ hipError_t launch_t(const QuantizeLaunch &p, hipStream_t stream) {
   const int32_t gpr = p.d / p.group;
   switch (p.group) {
     case 32:
-      quantize_pack<T, BITS, 4><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream>>>(
+      quantize_pack<T, BITS, 4, M16><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream>>>(
           x, total, lanes_per_row, p.N, p.codes, p.scale, p.zero, p.cap, p.off, gpr, p.layout, p.H);
       break;
     case 64:
-      quantize_pack<T, BITS, 8><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream>>>(
+      quantize_pack<T, BITS, 8, M16><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream>>>(
           x, total, lanes_per_row, p.N, p.codes, p.scale, p.zero, p.cap, p.off, gpr, p.layout, p.H);
       break;
     default:
-      quantize_pack<T, BITS, 16><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream>>>(
+      quantize_pack<T, BITS, 16, M16><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream>>>(
           x, total, lanes_per_row, p.N, p.codes, p.scale, p.zero, p.cap, p.off, gpr, p.layout, p.H);
       break;
   }
@@ -142,8 +154,14 @@ hipError_t launch_t(const QuantizeLaunch &p, hipStream_t stream) {
 
 hipError_t launch_quantize(const QuantizeLaunch &p, hipStream_t stream) {
   if (p.B * p.H * p.N == 0) return hipSuccess;
-  if (p.xdt == KV_BF16) return p.bits == 2 ? launch_t<uint16_t, 2>(p, stream) : launch_t<uint16_t, 4>(p, stream);
-  return p.bits == 2 ? launch_t<float, 2>(p, stream) : launch_t<float, 4>(p, stream);
+  if (p.meta16) {
+    if (p.xdt == KV_BF16)
+      return p.bits == 2 ? launch_t<uint16_t, 2, true>(p, stream) : launch_t<uint16_t, 4, true>(p, stream);
+    return p.bits == 2 ? launch_t<float, 2, true>(p, stream) : launch_t<float, 4, true>(p, stream);
+  }
+  if (p.xdt == KV_BF16)
+    return p.bits == 2 ? launch_t<uint16_t, 2, false>(p, stream) : launch_t<uint16_t, 4, false>(p, stream);
+  return p.bits == 2 ? launch_t<float, 2, false>(p, stream) : launch_t<float, 4, false>(p, stream);
 }
 
 }  // namespace kvq

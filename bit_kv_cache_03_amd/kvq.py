@@ -28,7 +28,11 @@ class QTensor(C.Structure):
     """kv_qtensor."""
     _fields_ = [("codes", C.c_void_p), ("scale", C.c_void_p), ("zero", C.c_void_p),
                 ("bits", C.c_int32), ("group", C.c_int32), ("cap", C.c_int64),
-                ("page_table", C.c_void_p), ("page_size", C.c_int32), ("num_pages", C.c_int32)]
+                ("page_table", C.c_void_p), ("page_size", C.c_int32), ("num_pages", C.c_int32),
+                ("meta", C.c_int32)]
+
+
+META = {"f32": 0, "f16": 1}  # kv_meta: storage type of a cache tensor's step and zero point
 
 
 class AttnArgs(C.Structure):
@@ -103,23 +107,28 @@ class QCache:
     Contiguous: [B][H][cap][...].  Paged (``page_table`` given: an int32 GPU
     tensor [B][cap // page_size] of page indices): pools of ``num_pages``
     pages [num_pages][H][page_size][...]; token t of (b, h) lives in page
-    page_table[b][t // page_size] at row t % page_size."""
+    page_table[b][t // page_size] at row t % page_size.  ``meta``: "f32" or
+    "f16" (binary16 step and zero point)."""
 
     def __init__(self, B: int, H: int, cap: int, d: int, bits: int, group: int = 64, device="cuda",
-                 page_table=None, page_size: int = 0, num_pages: int = 0):
+                 page_table=None, page_size: int = 0, num_pages: int = 0, meta: str = "f32"):
         import torch
+        if meta not in META:
+            raise ValueError(f"meta must be one of {sorted(META)}")
         self.B, self.H, self.cap, self.d, self.bits, self.group = B, H, cap, d, bits, group
         self.page_table, self.page_size, self.num_pages = page_table, page_size, num_pages
+        self.meta = meta
         lead = (num_pages, H, page_size) if page_table is not None else (B, H, cap)
+        mdt = torch.float16 if meta == "f16" else torch.float32
         self.codes = torch.zeros(lead + (d * bits // 8,), dtype=torch.uint8, device=device)
-        self.scale = torch.zeros(lead + (d // group,), dtype=torch.float32, device=device)
-        self.zero = torch.zeros(lead + (d // group,), dtype=torch.float32, device=device)
+        self.scale = torch.zeros(lead + (d // group,), dtype=mdt, device=device)
+        self.zero = torch.zeros(lead + (d // group,), dtype=mdt, device=device)
 
     def descriptor(self) -> QTensor:
         return QTensor(self.codes.data_ptr(), self.scale.data_ptr(), self.zero.data_ptr(),
                        self.bits, self.group, self.cap,
                        self.page_table.data_ptr() if self.page_table is not None else None,
-                       self.page_size, self.num_pages)
+                       self.page_size, self.num_pages, META[self.meta])
 
     def logical(self, nc: int):
         """(codes, step, zero) of tokens [0, nc) in the contiguous [B][H][nc][...]

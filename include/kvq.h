@@ -66,6 +66,15 @@ typedef enum {
                          the uniform-noise closed form; slow path, no perf target */
 } kv_corr;
 
+/* Storage type of a cache tensor's step D and zero point z. */
+typedef enum {
+  KV_META_F32 = 0, /* fp32 (default) */
+  KV_META_F16 = 1  /* IEEE binary16: D and z rounded (nearest, ties to even) before
+                      the codes are taken, so that z + D c uses what is stored; 2x less
+                      metadata (INT2/INT2 at group 64 and d = 128: 80 instead of 96 bytes
+                      per token per head); |values| must stay below 65504 */
+} kv_meta;
+
 /* Kernel path.  AUTO picks by rows per KV head; tests may force either. */
 typedef enum {
   KV_PATH_AUTO = 0,
@@ -86,8 +95,8 @@ typedef enum {
  */
 typedef struct {
   uint8_t *codes; /* [B][H][cap][d*bits/8] bytes (paged: the pool, see below) */
-  float *scale;   /* [B][H][cap][d/group]  step D */
-  float *zero;    /* [B][H][cap][d/group]  zero-point z (the group minimum) */
+  void *scale;    /* [B][H][cap][d/group]  step D (fp32 or binary16, see `meta`) */
+  void *zero;     /* [B][H][cap][d/group]  zero-point z (the group minimum, rounded like D) */
   int32_t bits;   /* 2 or 4 */
   int32_t group;  /* 32, 64 or 128; divides d */
   int64_t cap;    /* token capacity per head, at most 2^23 */
@@ -103,6 +112,7 @@ typedef struct {
   const int32_t *page_table;
   int32_t page_size;
   int32_t num_pages;
+  int32_t meta;   /* kv_meta of scale and zero; K and V caches of one call share it */
 } kv_qtensor;
 
 /*

@@ -12,14 +12,14 @@ def as_bf16(x):
     return x if x.dtype == np.uint16 else W.bf16_bits(x)
 
 
-def oracle_caches(orc, w, data):
-    kc = orc.quantize(data["kc"], w.kbits, w.group)
-    vc = orc.quantize(data["vc"], w.vbits, w.group)
+def oracle_caches(orc, w, data, meta="f32"):
+    kc = orc.quantize(data["kc"], w.kbits, w.group, meta=meta)
+    vc = orc.quantize(data["vc"], w.vbits, w.group, meta=meta)
     return kc, vc
 
 
-def oracle_problem(orc, w, corr="taylor", data=None, scale=0.0, caches=None, causal=False):
+def oracle_problem(orc, w, corr="taylor", data=None, scale=0.0, caches=None, causal=False, meta="f32"):
     data = W.generate(w) if data is None else data
-    kc, vc = oracle_caches(orc, w, data) if caches is None else caches
+    kc, vc = oracle_caches(orc, w, data, meta) if caches is None else caches
     return orc.Problem(as_bf16(data["q"]), as_bf16(data["k"]), as_bf16(data["v"]), kc, vc,
                        w.Nc, w.kbits, w.vbits, w.group, scale=scale, corr=corr, causal=causal)

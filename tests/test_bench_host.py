@@ -29,3 +29,5 @@ def test_flops_and_bytes_of_the_default_workload():
     assert bench.attention_flops(w, causal=True) == 4.0 * 128 * 24 * (4096 * 16384 + 4096 * 4097 // 2)
     # INT4 K and V codes (64 + 64 bytes) plus fp32 step and zero of 2 groups for K and V (32 bytes)
     assert bench.packed_bytes(w) == 24 * 16384 * 160
+    # binary16 step and zero: 16 bytes of metadata per token instead of 32
+    assert bench.packed_bytes(w, 2) == 24 * 16384 * 144

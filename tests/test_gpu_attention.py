@@ -26,17 +26,17 @@ CASES = {
 }
 
 
-def _compare(orc, w, corr, path, scale=0.0, splits=0, data=None, causal=False):
+def _compare(orc, w, corr, path, scale=0.0, splits=0, data=None, causal=False, meta="f32"):
     import _gpu
     data = W.generate(w) if data is None else data
     print(f"[attention] B={w.B} Hq={w.Hq} Hkv={w.Hkv} d={w.d} Nq={w.Nq} Ncur={w.Ncur} Nc={w.Nc} "
-          f"bits={w.kbits}/{w.vbits} group={w.group} corr={corr} path={path} splits={splits} causal={causal}",
-          flush=True)
-    kc = _gpu.build_cache(w, data["kc"], w.kbits) if w.Nc > 0 else None
-    vc = _gpu.build_cache(w, data["vc"], w.vbits) if w.Nc > 0 else None
+          f"bits={w.kbits}/{w.vbits} group={w.group} corr={corr} path={path} splits={splits} causal={causal} "
+          f"meta={meta}", flush=True)
+    kc = _gpu.build_cache(w, data["kc"], w.kbits, meta=meta) if w.Nc > 0 else None
+    vc = _gpu.build_cache(w, data["vc"], w.vbits, meta=meta) if w.Nc > 0 else None
     out = _gpu.run_attention(w, data, kc, vc, corr=corr, path=path, scale=scale, splits=splits, causal=causal)
     got = _gpu.out_rows(out)
-    ref = oracle_problem(orc, w, corr, data=data, scale=scale, causal=causal).attention()
+    ref = oracle_problem(orc, w, corr, data=data, scale=scale, causal=causal, meta=meta).attention()
     _gpu.check(got, ref)
     return got, ref
 
