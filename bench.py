@@ -18,6 +18,7 @@ sample of the same workload on this host's cores, is the `cpu_baseline`.
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import os
@@ -35,10 +36,11 @@ DEFAULT_WORKLOAD = "h24_int4_cache16k"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "cached-key tokens\u00b7queries/s (TFLOP/s eff.) and packed-KV HBM GB/s vs roofline"
-KERNEL_SOURCES = [os.path.join(ROOT, "bit_kv_cache_03_amd", "csrc", f) for f in ("attention.hip", "attention_fast.hip", "attention_fast_causal.hip", "attention_fast_paged.hip",
-                                                                            "attention_fast_paged_causal.hip", "attention_short.hip",
-                                                                            "attention_short_paged.hip", "kvq_device.h", "kvq_api.cpp",
-                                                                            "kvq_internal.h")]
+# every source the library is built from (the hash names the kernels a
+# stored counter run measured)
+KERNEL_SOURCES = sorted(glob.glob(os.path.join(ROOT, "bit_kv_cache_03_amd", "csrc", "*.hip")) +
+                        glob.glob(os.path.join(ROOT, "bit_kv_cache_03_amd", "csrc", "*.h")) +
+                        glob.glob(os.path.join(ROOT, "bit_kv_cache_03_amd", "csrc", "*.cpp")))
 
 
 def kernel_sha() -> str:
@@ -162,7 +164,7 @@ def _counter_means(csv_path: str, counter: str, kernel_substrs) -> dict:
 
 # kernels one kv_attention_corrected call launches (pre-pass, attention, combine)
 ATTENTION_CALL_KERNELS = ("key_scale_kernel", "attn_fast_kernel", "attn_short_kernel", "attn_tile_kernel",
-                          "attn_combine_kernel")
+                          "attn_combine_kernel", "tail_combine_kernel")
 
 
 def write_traffic(w, pmc_dir: str, copy_bytes: int, options: dict):
