@@ -53,6 +53,8 @@ def _load(path: str):
     L.kvo_quantize_bf16.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp]
     L.kvo_quantize_f32_meta.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp]
     L.kvo_quantize_bf16_meta.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp]
+    L.kvo_quantize_tokens_f32_meta.argtypes = [vp, i64, i64, i32, i32, i32, i32, vp, vp, vp]
+    L.kvo_quantize_tokens_bf16_meta.argtypes = [vp, i64, i64, i32, i32, i32, i32, vp, vp, vp]
     L.kvo_round_fp16.argtypes = [C.c_float]
     L.kvo_round_fp16.restype = C.c_float
     L.kvo_unpack.argtypes = [vp, i64, i32, i32, vp]
@@ -93,7 +95,7 @@ def _check(rc: int, what: str):
 # quantizer
 # --------------------------------------------------------------------------
 
-def quantize(x: np.ndarray, bits: int, group: int, meta: str = "f32"):
+def quantize(x: np.ndarray, bits: int, group: int, meta: str = "f32", axis: str = "dim"):
     """Group-wise asymmetric quantization of the last axis of ``x``.
 
     ``x`` is float32 values, or uint16 bf16 bit patterns.  Returns
@@ -101,9 +103,16 @@ def quantize(x: np.ndarray, bits: int, group: int, meta: str = "f32"):
     ``x.shape[:-1] + (d*bits//8,)`` uint8, and step/zero of shape
     ``x.shape[:-1] + (d//group,)`` float32.  ``meta="f16"``: step and zero
     are rounded to binary16 (still returned as float32 values) and the codes
-    are taken against the rounded grid.
+    are taken against the rounded grid.  ``axis="tokens"``: groups run
+    along the second-to-last axis instead (per channel, ``group``
+    consecutive tokens; the last group may be shorter): step/zero then have
+    shape ``x.shape[:-2] + (ceil(N/group), d)``.
     """
     meta16 = {"f32": 0, "f16": 1}[meta]
+    if axis == "tokens":
+        return _quantize_tokens(np.ascontiguousarray(x), bits, group, meta16)
+    if axis != "dim":
+        raise ValueError("axis must be 'dim' or 'tokens'")
     x = np.ascontiguousarray(x)
     d = x.shape[-1]
     rows = x.size // d if d else 0
@@ -117,6 +126,23 @@ def quantize(x: np.ndarray, bits: int, group: int, meta: str = "f32"):
     else:
         raise TypeError("x must be float32 or uint16 (bf16 bits)")
     _check(rc, "quantize")
+    return codes, step, zero
+
+
+def _quantize_tokens(x: np.ndarray, bits: int, group: int, meta16: int):
+    n, d = x.shape[-2], x.shape[-1]
+    outer = x.size // (n * d) if n * d else 0
+    ngr = (n + group - 1) // group
+    codes = np.zeros(x.shape[:-1] + (d * bits // 8,), np.uint8)
+    step = np.zeros(x.shape[:-2] + (ngr, d), np.float32)
+    zero = np.zeros_like(step)
+    if x.dtype == np.float32:
+        f = lib().kvo_quantize_tokens_f32_meta
+    elif x.dtype == np.uint16:
+        f = lib().kvo_quantize_tokens_bf16_meta
+    else:
+        raise TypeError("x must be float32 or uint16 (bf16 bits)")
+    _check(f(_p(x), outer, n, d, group, bits, meta16, _p(codes), _p(step), _p(zero)), "quantize_tokens")
     return codes, step, zero
 
 
@@ -179,18 +205,25 @@ class _Attn(C.Structure):
         ("vc_codes", C.c_void_p), ("vc_step", C.c_void_p), ("vc_zero", C.c_void_p),
         ("kbits", C.c_int32), ("vbits", C.c_int32), ("cap", C.c_int64),
         ("scale", C.c_double), ("corr", C.c_int32), ("causal", C.c_int32),
+        ("kaxis", C.c_int32), ("vaxis", C.c_int32),
     ]
+
+
+AXIS = {"dim": 0, "tokens": 1}
 
 
 class Problem:
     """One attention problem in the library's layouts (host numpy arrays).
 
     q: uint16 bf16 bits [B][Hq][Nq][d]; k_cur, v_cur: uint16 [B][Hkv][Ncur][d];
-    kcache/vcache: (codes, step, zero) with shapes [B][Hkv][cap][...].
+    kcache/vcache: (codes, step, zero) with shapes [B][Hkv][cap][...]; with
+    kaxis/vaxis "tokens" that cache's step and zero are
+    [B][Hkv][ceil(cap/group)][d] (groups along the tokens).
     """
 
     def __init__(self, q, k_cur, v_cur, kcache, vcache, nc: int, kbits: int, vbits: int,
-                 group: int, scale: float = 0.0, corr: str = "taylor", causal: bool = False):
+                 group: int, scale: float = 0.0, corr: str = "taylor", causal: bool = False,
+                 kaxis: str = "dim", vaxis: str = "dim"):
         self.q = np.ascontiguousarray(q, dtype=np.uint16)
         B, Hq, Nq, d = self.q.shape
         self.k_cur = np.ascontiguousarray(k_cur, dtype=np.uint16)
@@ -203,7 +236,8 @@ class Problem:
                        _p(self.q).value, _p(self.k_cur).value, _p(self.v_cur).value,
                        _p(self.kc[0]).value, _p(self.kc[1]).value, _p(self.kc[2]).value,
                        _p(self.vc[0]).value, _p(self.vc[1]).value, _p(self.vc[2]).value,
-                       kbits, vbits, cap, float(scale), CORR[corr], 1 if causal else 0)
+                       kbits, vbits, cap, float(scale), CORR[corr], 1 if causal else 0,
+                       AXIS[kaxis], AXIS[vaxis])
         self.shape = (B, Hq, Nq, d)
 
     def with_corr(self, corr: str) -> "Problem":

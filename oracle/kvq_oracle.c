@@ -41,6 +41,11 @@
  *  - packing is LSB-first: element k of a row sits in byte floor(k*bits/8)
  *    at bit (k*bits) mod 8; rows are contiguous along the head dimension and
  *    groups are consecutive runs of `group` elements of a row;
+ *  - groups along the tokens instead (per channel, the grouping the pages
+ *    name beside per-group steps): channel c of `group` consecutive tokens
+ *    of one head shares D and z; the last group of a quantised run may be
+ *    shorter; codes are packed per token row as above, and D, z are stored
+ *    [token group][channel]; the bias then uses D_{g(t),c} per channel;
  *  - dequantised value  x^ = z + D * c  (fp64 here);
  *  - tau = 1/sqrt(d) unless a scale is given; the Taylor bias is
  *    (tau^2/24) * sum_g D_g^2 * sum_{c in g} q_c^2, which equals the page's
@@ -219,6 +224,62 @@ int kvo_quantize_bf16_meta(const uint16_t *x, int64_t rows, int32_t d, int32_t g
   return rc;
 }
 
+/* Groups along the tokens: x is `outer` runs of n tokens of d fp32 values
+ * ([outer][n][d], one run per (b, h)); within a run, channel c of tokens
+ * [j*group, min(n, (j+1)*group)) is one group, quantised exactly like a
+ * group of the head-dimension layout.  codes: [outer][n][d*bits/8] (token
+ * rows, packed as above); step, zero: [outer][ceil(n/group)][d].  Any
+ * group >= 1 is accepted here. */
+int kvo_quantize_tokens_f32_meta(const float *x, int64_t outer, int64_t n, int32_t d, int32_t group,
+                                 int32_t bits, int32_t meta16, uint8_t *codes, float *step, float *zero) {
+  if (!x || !codes || !step || !zero || outer < 0 || n < 0 || d <= 0 || group < 1) return KVO_ERR_ARG;
+  if ((bits != 2 && bits != 4) || (d * bits) % 8 != 0 || (meta16 != 0 && meta16 != 1)) return KVO_ERR_ARG;
+  const int64_t ngr = (n + group - 1) / group;
+  const int64_t row_bytes = d * bits / 8;
+  int err = KVO_OK;
+#pragma omp parallel
+  {
+    float *vals = (float *)malloc(sizeof(float) * (size_t)group);
+    uint8_t *gc = (uint8_t *)malloc((size_t)group);
+    uint8_t *u = (uint8_t *)malloc((size_t)(n * d) + 1); /* unpacked codes of one run */
+    if (!vals || !gc || !u) {
+#pragma omp atomic write
+      err = KVO_ERR_MEM;
+    } else {
+#pragma omp for schedule(static)
+      for (int64_t o = 0; o < outer; ++o) {
+        const float *xo = x + o * n * d;
+        for (int64_t j = 0; j < ngr; ++j) {
+          const int64_t t0 = j * group;
+          const int32_t cnt = (int32_t)(n - t0 < group ? n - t0 : group);
+          for (int32_t c = 0; c < d; ++c) {
+            for (int32_t i = 0; i < cnt; ++i) vals[i] = xo[(t0 + i) * d + c];
+            quantize_group(vals, cnt, bits, meta16, gc, step + (o * ngr + j) * d + c,
+                           zero + (o * ngr + j) * d + c);
+            for (int32_t i = 0; i < cnt; ++i) u[(t0 + i) * d + c] = gc[i];
+          }
+        }
+        for (int64_t t = 0; t < n; ++t) pack_row(u + t * d, d, bits, codes + (o * n + t) * row_bytes);
+      }
+    }
+    free(vals);
+    free(gc);
+    free(u);
+  }
+  return err;
+}
+
+int kvo_quantize_tokens_bf16_meta(const uint16_t *x, int64_t outer, int64_t n, int32_t d, int32_t group,
+                                  int32_t bits, int32_t meta16, uint8_t *codes, float *step, float *zero) {
+  if (!x || outer < 0 || n < 0 || d <= 0) return KVO_ERR_ARG;
+  float *f = (float *)malloc((size_t)(outer * n * d) * sizeof(float) + 1);
+  if (!f) return KVO_ERR_MEM;
+  kvo_bf16_to_f32(x, outer * n * d, f);
+  int rc = kvo_quantize_tokens_f32_meta(f, outer, n, d, group, bits, meta16, codes, step, zero);
+  free(f);
+  return rc;
+}
+
 int kvo_quantize_bf16(const uint16_t *x, int64_t rows, int32_t d, int32_t group,
                       int32_t bits, uint8_t *codes, float *step, float *zero) {
   return kvo_quantize_bf16_meta(x, rows, d, group, bits, 0, codes, step, zero);
@@ -318,7 +379,7 @@ typedef struct {
   const uint16_t *k_cur; /* bf16 bits [B][Hkv][Ncur][d] */
   const uint16_t *v_cur; /* bf16 bits [B][Hkv][Ncur][d] */
   const uint8_t *kc_codes; /* [B][Hkv][cap][d*kbits/8] */
-  const float *kc_step;    /* [B][Hkv][cap][d/group] */
+  const float *kc_step;    /* [B][Hkv][cap][d/group], or [B][Hkv][ceil(cap/group)][d] (kaxis 1) */
   const float *kc_zero;
   const uint8_t *vc_codes;
   const float *vc_step;
@@ -328,6 +389,8 @@ typedef struct {
   double scale; /* softmax scale tau; <= 0 means 1/sqrt(d) */
   int32_t corr; /* 0 off, 1 Taylor, 2 exact */
   int32_t causal; /* 0 no mask; 1 end-aligned causal mask on the current chunk */
+  int32_t kaxis;  /* 0: K groups along the head dimension; 1: along the tokens (per channel) */
+  int32_t vaxis;  /* the same for V */
 } kvo_attn;
 
 static int attn_ok(const kvo_attn *a) {
@@ -339,7 +402,13 @@ static int attn_ok(const kvo_attn *a) {
   if (a->Ncur > 0 && (!a->k_cur || !a->v_cur)) return 0;
   if (a->Nc > 0) {
     if (!a->kc_codes || !a->kc_step || !a->kc_zero || !a->vc_codes || !a->vc_step || !a->vc_zero) return 0;
-    if (!qparams_ok(a->d, a->group, a->kbits) || !qparams_ok(a->d, a->group, a->vbits)) return 0;
+    if (a->kaxis < 0 || a->kaxis > 1 || a->vaxis < 0 || a->vaxis > 1) return 0;
+    if (a->kaxis == 0 ? !qparams_ok(a->d, a->group, a->kbits)
+                      : (a->group < 1 || (a->kbits != 2 && a->kbits != 4) || (a->d * a->kbits) % 8))
+      return 0;
+    if (a->vaxis == 0 ? !qparams_ok(a->d, a->group, a->vbits)
+                      : (a->group < 1 || (a->vbits != 2 && a->vbits != 4) || (a->d * a->vbits) % 8))
+      return 0;
     if (a->cap < a->Nc) return 0;
   }
   return a->d > 0;
@@ -373,20 +442,29 @@ static int visible(const kvo_attn *a, int64_t row, int64_t t) {
   return t - a->Nc <= j + a->Ncur - a->Nq;
 }
 
+/* Index of the step and zero point of channel c of cached token t of
+ * (b, hk) = bkv: groups along the head dimension (axis 0: [cap][d/group])
+ * or along the tokens (axis 1: [ceil(cap/group)][d]). */
+static int64_t meta_index(const kvo_attn *a, int32_t axis, int64_t bkv, int64_t t, int32_t c) {
+  if (axis == 0) return (bkv * a->cap + t) * (a->d / a->group) + c / a->group;
+  const int64_t capg = (a->cap + a->group - 1) / a->group;
+  return (bkv * capg + t / a->group) * a->d + c;
+}
+
 /* Key index t in [0, Nc + Ncur): t < Nc is cached key t, else current key
  * t - Nc. Writes the (fp64) key and value vectors. */
 static void key_value(const rowctx *rc, int64_t t, double *k, double *v) {
   const kvo_attn *a = rc->a;
   const int32_t d = a->d;
   if (t < a->Nc) {
-    const int32_t ng = d / a->group;
-    const int64_t base = (rc->b * a->Hkv + rc->hk) * a->cap + t;
+    const int64_t bkv = rc->b * a->Hkv + rc->hk;
+    const int64_t base = bkv * a->cap + t;
     const uint8_t *kr = a->kc_codes + base * (d * a->kbits / 8);
     const uint8_t *vr = a->vc_codes + base * (d * a->vbits / 8);
     for (int32_t c = 0; c < d; ++c) {
-      int32_t g = c / a->group;
-      k[c] = (double)a->kc_zero[base * ng + g] + (double)a->kc_step[base * ng + g] * code_at(kr, c, a->kbits);
-      v[c] = (double)a->vc_zero[base * ng + g] + (double)a->vc_step[base * ng + g] * code_at(vr, c, a->vbits);
+      const int64_t mk = meta_index(a, a->kaxis, bkv, t, c), mv = meta_index(a, a->vaxis, bkv, t, c);
+      k[c] = (double)a->kc_zero[mk] + (double)a->kc_step[mk] * code_at(kr, c, a->kbits);
+      v[c] = (double)a->vc_zero[mv] + (double)a->vc_step[mv] * code_at(vr, c, a->vbits);
     }
   } else {
     const int64_t base = ((rc->b * a->Hkv + rc->hk) * a->Ncur + (t - a->Nc)) * d;
@@ -409,11 +487,13 @@ static double logit_of(const rowctx *rc, int64_t t, const double *k) {
   for (int32_t c = 0; c < a->d; ++c) s += rc->q[c] * k[c];
   s *= rc->tau;
   if (t < a->Nc && a->corr != 0) {
-    const int32_t ng = a->d / a->group;
-    const int64_t base = (rc->b * a->Hkv + rc->hk) * a->cap + t;
-    const float *step = a->kc_step + base * ng;
-    s -= (a->corr == 1) ? kvo_bias_taylor(rc->q, step, a->d, a->group, rc->tau)
-                        : kvo_bias_exact(rc->q, step, a->d, a->group, rc->tau);
+    /* the key's steps: d/group of them, or one per channel (groups along
+     * the tokens: a group of one channel each) */
+    const int64_t bkv = rc->b * a->Hkv + rc->hk;
+    const float *step = a->kc_step + meta_index(a, a->kaxis, bkv, t, 0);
+    const int32_t gsz = a->kaxis == 0 ? a->group : 1;
+    s -= (a->corr == 1) ? kvo_bias_taylor(rc->q, step, a->d, gsz, rc->tau)
+                        : kvo_bias_exact(rc->q, step, a->d, gsz, rc->tau);
   }
   return s;
 }

@@ -12,14 +12,16 @@ def as_bf16(x):
     return x if x.dtype == np.uint16 else W.bf16_bits(x)
 
 
-def oracle_caches(orc, w, data, meta="f32"):
-    kc = orc.quantize(data["kc"], w.kbits, w.group, meta=meta)
-    vc = orc.quantize(data["vc"], w.vbits, w.group, meta=meta)
+def oracle_caches(orc, w, data, meta="f32", kaxis="dim", vaxis="dim"):
+    kc = orc.quantize(data["kc"], w.kbits, w.group, meta=meta, axis=kaxis)
+    vc = orc.quantize(data["vc"], w.vbits, w.group, meta=meta, axis=vaxis)
     return kc, vc
 
 
-def oracle_problem(orc, w, corr="taylor", data=None, scale=0.0, caches=None, causal=False, meta="f32"):
+def oracle_problem(orc, w, corr="taylor", data=None, scale=0.0, caches=None, causal=False, meta="f32",
+                   kaxis="dim", vaxis="dim"):
     data = W.generate(w) if data is None else data
-    kc, vc = oracle_caches(orc, w, data, meta) if caches is None else caches
+    kc, vc = oracle_caches(orc, w, data, meta, kaxis, vaxis) if caches is None else caches
     return orc.Problem(as_bf16(data["q"]), as_bf16(data["k"]), as_bf16(data["v"]), kc, vc,
-                       w.Nc, w.kbits, w.vbits, w.group, scale=scale, corr=corr, causal=causal)
+                       w.Nc, w.kbits, w.vbits, w.group, scale=scale, corr=corr, causal=causal,
+                       kaxis=kaxis, vaxis=vaxis)

@@ -69,8 +69,17 @@ MUTANTS = [
      [("test_oracle_meta16", "test_quantizer_with_binary16_metadata", {"bits": 4, "group": 64})]),
     ("meta16_ties_away", "  const float r = rintf(a / u) * u;", "  const float r = roundf(a / u) * u;",
      [("test_oracle_meta16", "test_rounding_ties_subnormals_overflow", {})]),
+    ("tokens_group_row_mod", "return (bkv * capg + t / a->group) * a->d + c;",
+     "return (bkv * capg + t % a->group) * a->d + c;",
+     [("test_oracle_tokens", "test_tokens_matches_library_sdpa", {"case": "int2_k_tokens", "corr": "off"})]),
+    ("tokens_bias_per_group", "const int32_t gsz = a->kaxis == 0 ? a->group : 1;", "const int32_t gsz = a->group;",
+     [("test_oracle_tokens", "test_tokens_matches_library_sdpa", {"case": "int4_both_tokens", "corr": "taylor"})]),
+    ("tokens_read_transposed", "for (int32_t i = 0; i < cnt; ++i) vals[i] = xo[(t0 + i) * d + c];",
+     "for (int32_t i = 0; i < cnt; ++i) vals[i] = xo[(t0 + i) + (int64_t)c * n];",
+     [("test_oracle_tokens", "test_quantizer_is_the_transposed_head_dim_quantizer",
+       {"bits": 2, "group": 32, "src": "f32", "meta": "f32"})]),
     ("value_not_dequantized_zero",
-     "v[c] = (double)a->vc_zero[base * ng + g] + ", "v[c] = ",
+     "v[c] = (double)a->vc_zero[mv] + ", "v[c] = ",
      [("test_oracle_attention", "test_matches_library_sdpa", {"corr": "off", "wi": 2})]),
 ]
 
