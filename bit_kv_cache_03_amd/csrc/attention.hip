@@ -31,6 +31,13 @@
 //   5. O^T += V^T P^T on bf16 MFMA.
 // Finally O / l is rounded to bf16 and stored.
 //
+// Caches whose groups run along the tokens (per channel: D_{t/G, c}) are
+// dequantised channel by channel; their bias is then the same for every key
+// of a token group, so with G >= 32 and tiles starting at multiples of 64
+// each 32-key half of a tile has one bias per query row:
+// tau^2/24 sum_c q_c^2 D_c^2 (or the exact sum_c log(sinh x_c / x_c)),
+// computed per row from the half's per-channel steps staged in LDS.
+//
 // MFMA lane layouts (32x32x16 bf16, wave64): A operand lane l holds row l%32,
 // k-slots 8*(l/32)..+7; B operand lane l holds column l%32, the same k-slots;
 // the 32x32 fp32 result gives lane l column l%32 and rows
@@ -41,9 +48,18 @@
 // lane's 8 keys are 16*(ks%2) + {4h..4h+3, 8+4h..8+4h+3}.  The V tile is
 // written to LDS transposed in that same key order, so both operands of
 // O^T = V^T P^T are single 16-byte LDS reads.
+//
+// The instances for caches grouped along the tokens are built from this file
+// in a translation unit of their own (attention_tokens.hip defines
+// KVQ_TILE_TOKENS to 1): the head-dimension instances compile exactly as
+// without them, and the token instances get their own register budget.
 #include <math.h>
 
 #include "kvq_internal.h"
+
+#ifndef KVQ_TILE_TOKENS
+#define KVQ_TILE_TOKENS 0
+#endif
 
 namespace kvq {
 namespace {
@@ -102,8 +118,10 @@ __device__ inline float code_f(uint32_t w, int j) {
 // SPLIT: blockIdx.z selects a contiguous range of the key sequence
 // [cache ; current]; the workgroup writes unnormalised partials (running max
 // in the log2 domain, running sum, O) to the workspace instead of `out`.
-template <int D, int KBITS, int VBITS, bool EXACT, bool SPLIT>
-__global__ __launch_bounds__(kThreads, EXACT ? 1 : 2) void attn_tile_kernel(AttnLaunch p, int32_t group_shift,
+// TOK: the caches may group along the tokens (p.ktok / p.vtok); false
+// compiles those paths out.
+template <int D, int KBITS, int VBITS, bool EXACT, bool SPLIT, bool TOK>
+__global__ __launch_bounds__(kThreads, EXACT || TOK ? 1 : 2) void attn_tile_kernel(AttnLaunch p, int32_t group_shift,
                                                                  int64_t rows_per_kvhead, int64_t split_keys) {
   constexpr int KS = Tile<D>::kStride;
   constexpr int VS = Tile<D>::vStride;
@@ -114,10 +132,14 @@ __global__ __launch_bounds__(kThreads, EXACT ? 1 : 2) void attn_tile_kernel(Attn
   // exact form only: per-key steps and the workgroup's query rows (bf16)
   __shared__ float Dk[EXACT ? kBN * 4 : 1];
   __shared__ __attribute__((aligned(16))) uint16_t Qs[EXACT ? kBM * (D + 8) : 1];
+  // groups along the tokens: per-channel steps of the token group of each
+  // 32-key half of the tile
+  __shared__ __attribute__((aligned(16))) float Dt[TOK ? 2 * D : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const bool ktok = TOK && p.ktok, vtok = TOK && p.vtok;
   const int qc = lane & 31;  // query column owned by this lane
   const int h = lane >> 5;   // lane half
   const int group = 1 << group_shift;
@@ -171,7 +193,7 @@ __global__ __launch_bounds__(kThreads, EXACT ? 1 : 2) void attn_tile_kernel(Attn
     for (int j = 0; j < 8; ++j) {
       const int slot = 8 * h + j, g = slot / 3, part = slot % 3;
       e[j] = 0.f;
-      if (g < ng && p.corr == KV_CORR_TAYLOR) e[j] = part == 2 ? nl[g] : nh[g];
+      if (g < ng && p.corr == KV_CORR_TAYLOR && !ktok) e[j] = part == 2 ? nl[g] : nh[g];
     }
     qext = __builtin_bit_cast(bf16x8, make_uint4(pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]),
                                                  pack_bf16x2(e[4], e[5]), pack_bf16x2(e[6], e[7])));
@@ -235,9 +257,6 @@ __global__ __launch_bounds__(kThreads, EXACT ? 1 : 2) void attn_tile_kernel(Attn
       uint32_t outw[DPT / 2];
       if (cached) {
         const int64_t row = p.layout.row(p.cap, p.Hkv, b, hk, k0 + (ok ? key : 0));  // cache row of the key
-        const int g = d0 >> group_shift;
-        const float stp = ok ? meta_at(p.kc_scale, row * ng + g, p.meta16) : 0.f;
-        const float zp = ok ? meta_at(p.kc_zero, row * ng + g, p.meta16) : 0.f;
         constexpr int WORDS = DPT * KBITS / 32;
         uint32_t w[WORDS];
         const uint8_t *src = p.kc_codes + row * KROW + d0 * KBITS / 8;
@@ -245,19 +264,37 @@ __global__ __launch_bounds__(kThreads, EXACT ? 1 : 2) void attn_tile_kernel(Attn
         for (int i = 0; i < WORDS; ++i) w[i] = ok ? reinterpret_cast<const uint32_t *>(src)[i] : 0u;
         constexpr int PER = 32 / KBITS;
         uint32_t low[DPT / 2];
-#pragma unroll
-        for (int e = 0; e < DPT; e += 2) {
-          const float a = fmaf(stp, code_f<KBITS>(w[e / PER], e % PER), zp);
-          const float c = fmaf(stp, code_f<KBITS>(w[(e + 1) / PER], (e + 1) % PER), zp);
+        // values e, e + 1 as a bf16 hi pair and the lo pair of the remainders
+        auto put = [&](int e, float a, float c) {
           const uint32_t hi = ok ? pack_bf16x2(a, c) : 0u;
           outw[e / 2] = hi;
           low[e / 2] = ok ? pack_bf16x2(a - __uint_as_float(hi << 16), c - __uint_as_float(hi & 0xffff0000u)) : 0u;
+        };
+        if (!ktok) {  // one step / zero point for the thread's values (one group of the row)
+          const int g = d0 >> group_shift;
+          const float stp = ok ? meta_at(p.kc_scale, row * ng + g, p.meta16) : 0.f;
+          const float zp = ok ? meta_at(p.kc_zero, row * ng + g, p.meta16) : 0.f;
+#pragma unroll
+          for (int e = 0; e < DPT; e += 2)
+            put(e, fmaf(stp, code_f<KBITS>(w[e / PER], e % PER), zp),
+                fmaf(stp, code_f<KBITS>(w[(e + 1) / PER], (e + 1) % PER), zp));
+        } else {  // groups along the tokens: one per channel of the key's token group
+          const int64_t m0 = (row >> group_shift) * D + d0;
+#pragma unroll
+          for (int e = 0; e < DPT; e += 2) {
+            const float sa = ok ? meta_at(p.kc_scale, m0 + e, p.meta16) : 0.f;
+            const float za = ok ? meta_at(p.kc_zero, m0 + e, p.meta16) : 0.f;
+            const float sc = ok ? meta_at(p.kc_scale, m0 + e + 1, p.meta16) : 0.f;
+            const float zc = ok ? meta_at(p.kc_zero, m0 + e + 1, p.meta16) : 0.f;
+            put(e, fmaf(sa, code_f<KBITS>(w[e / PER], e % PER), za),
+                fmaf(sc, code_f<KBITS>(w[(e + 1) / PER], (e + 1) % PER), zc));
+          }
         }
         uint4 *dlo = reinterpret_cast<uint4 *>(&Ks[key * KS + Tile<D>::kLo + d0]);
 #pragma unroll
         for (int i = 0; i < DPT / 8; ++i)
           dlo[i] = make_uint4(low[4 * i], low[4 * i + 1], low[4 * i + 2], low[4 * i + 3]);
-        if ((tid & 3) == 0) {
+        if ((tid & 3) == 0 && !ktok) {
           // correction slots: 3g+{0,1,2} = -Dsq_hi, -Dsq_lo, -Dsq_hi
           float e16[16];
           float dsh[4] = {0.f, 0.f, 0.f, 0.f}, dsl[4] = {0.f, 0.f, 0.f, 0.f};
@@ -292,6 +329,12 @@ __global__ __launch_bounds__(kThreads, EXACT ? 1 : 2) void attn_tile_kernel(Attn
 #pragma unroll
       for (int i = 0; i < DPT / 8; ++i)
         dst[i] = make_uint4(outw[4 * i], outw[4 * i + 1], outw[4 * i + 2], outw[4 * i + 3]);
+      if (cached && ktok && p.corr != KV_CORR_OFF && tid < 2 * D) {
+        const int hk0 = 32 * (tid / D);  // first key of the half
+        const bool okh = hk0 < count;
+        const int64_t hrow = p.layout.row(p.cap, p.Hkv, b, hk, k0 + (okh ? hk0 : 0));
+        Dt[tid] = okh ? meta_at(p.kc_scale, (hrow >> group_shift) * D + tid % D, p.meta16) : 0.f;
+      }
     }
     // ---------------- V tile -> LDS (transposed, permuted key order) ----------------
     {
@@ -304,19 +347,28 @@ __global__ __launch_bounds__(kThreads, EXACT ? 1 : 2) void attn_tile_kernel(Attn
         const int slot = 16 * ks + ((a >> 1) << 2) + ((a & 1) << 3);
         float v[4][8];
         if (cached) {
-          const int g = (8 * dq) >> group_shift;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int key = 4 * kq + j;
             const bool ok = key < count;
             const int64_t row = p.layout.row(p.cap, p.Hkv, b, hk, k0 + (ok ? key : 0));
-            const float stp = ok ? meta_at(p.vc_scale, row * ng + g, p.meta16) : 0.f;
-            const float zp = ok ? meta_at(p.vc_zero, row * ng + g, p.meta16) : 0.f;
             const uint8_t *src = p.vc_codes + row * VROW + dq * VBITS;  // 8 codes = VBITS bytes
             uint32_t w = 0;
             if (ok) w = VBITS == 2 ? *reinterpret_cast<const uint16_t *>(src) : *reinterpret_cast<const uint32_t *>(src);
+            if (!vtok) {  // one step per group of the row
+              const int64_t m = row * ng + ((8 * dq) >> group_shift);
+              const float stp = ok ? meta_at(p.vc_scale, m, p.meta16) : 0.f;
+              const float zp = ok ? meta_at(p.vc_zero, m, p.meta16) : 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[j][e] = ok ? fmaf(stp, code_f<VBITS>(w, e), zp) : 0.f;
+              for (int e = 0; e < 8; ++e) v[j][e] = ok ? fmaf(stp, code_f<VBITS>(w, e), zp) : 0.f;
+            } else {  // groups along the tokens: one per channel
+              const int64_t m0 = (row >> group_shift) * D + 8 * dq;
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                v[j][e] = ok ? fmaf(meta_at(p.vc_scale, m0 + e, p.meta16), code_f<VBITS>(w, e),
+                                    meta_at(p.vc_zero, m0 + e, p.meta16))
+                             : 0.f;
+            }
           }
         } else {
 #pragma unroll
@@ -342,6 +394,36 @@ __global__ __launch_bounds__(kThreads, EXACT ? 1 : 2) void attn_tile_kernel(Attn
     }
     __syncthreads();
 
+    // groups along the tokens: one bias per query row and 32-key half (one
+    // token group each), in logit units; the lane sums its half of the
+    // channels, then the two lane halves combine
+    float tokb[2] = {0.f, 0.f};
+    if (cached && ktok && p.corr != KV_CORR_OFF) {
+      constexpr bool taylor = !EXACT;  // this instance runs Taylor (EXACT: the exact form)
+      const float half_tau = 0.5f * p.tau;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const uint4 w = __builtin_bit_cast(uint4, qreg[s]);
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const float4 *dv = reinterpret_cast<const float4 *>(&Dt[kb * D + 16 * s + 8 * h]);
+          const float4 d0v = dv[0], d1v = dv[1];
+          const float st[8] = {d0v.x, d0v.y, d0v.z, d0v.w, d1v.x, d1v.y, d1v.z, d1v.w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float qv = (i & 1) ? __uint_as_float(u[i >> 1] & 0xffff0000u) : __uint_as_float(u[i >> 1] << 16);
+            tokb[kb] += taylor ? qv * qv * (st[i] * st[i]) : logsinhc(half_tau * qv * st[i]);
+          }
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const float tot = tokb[kb] + __shfl_xor(tokb[kb], 32, 64);
+        tokb[kb] = taylor ? tot * (p.tau * p.tau / 24.0f) : tot;  // tau^2/24 sum q^2 D^2, or sum L(x_c)
+      }
+    }
+
     // ---------------- S^T = K Q^T (+ correction step) ----------------
     f32x16 acc[2];
 #pragma unroll
@@ -360,7 +442,7 @@ __global__ __launch_bounds__(kThreads, EXACT ? 1 : 2) void attn_tile_kernel(Attn
           acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[s], acc[kb], 0, 0, 0);
         }
       }
-      if (!EXACT && cached && p.corr == KV_CORR_TAYLOR) {
+      if (!EXACT && cached && p.corr == KV_CORR_TAYLOR && !ktok) {
         const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(krow + Tile<D>::kExt);
         acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qext, acc[kb], 0, 0, 0);
       }
@@ -368,7 +450,12 @@ __global__ __launch_bounds__(kThreads, EXACT ? 1 : 2) void attn_tile_kernel(Attn
 
     // ---------------- logits (log2 domain) ----------------
     float z[2][16];
-    if (EXACT && cached && p.corr == KV_CORR_EXACT) {
+    if (cached && ktok && p.corr != KV_CORR_OFF) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) z[kb][i] = (acc[kb][i] * p.tau - tokb[kb]) * kLog2e;
+    } else if (EXACT && cached && p.corr == KV_CORR_EXACT) {
       float be[2][16];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -513,6 +600,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float *__restri
   for (int e = 0; e < PER; ++e) out[row * D + lane * PER + e] = f32_to_bf16_bits(acc[e] * inv);
 }
 
+constexpr bool kTok = KVQ_TILE_TOKENS != 0;
+
 template <int D, int KB, int VB, bool SPLIT>
 hipError_t launch_bits(const AttnLaunch &p, hipStream_t stream, bool exact) {
   const int64_t rows = p.Nq * (p.Hq / p.Hkv);
@@ -524,9 +613,9 @@ hipError_t launch_bits(const AttnLaunch &p, hipStream_t stream, bool exact) {
                   static_cast<uint32_t>(splits));
   const int32_t gshift = __builtin_ctz(static_cast<unsigned>(p.group));
   if (exact)
-    attn_tile_kernel<D, KB, VB, true, SPLIT><<<grid, dim3(kThreads), 0, stream>>>(p, gshift, rows, split_keys);
+    attn_tile_kernel<D, KB, VB, true, SPLIT, kTok><<<grid, dim3(kThreads), 0, stream>>>(p, gshift, rows, split_keys);
   else
-    attn_tile_kernel<D, KB, VB, false, SPLIT><<<grid, dim3(kThreads), 0, stream>>>(p, gshift, rows, split_keys);
+    attn_tile_kernel<D, KB, VB, false, SPLIT, kTok><<<grid, dim3(kThreads), 0, stream>>>(p, gshift, rows, split_keys);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !SPLIT) return e;
   const int64_t nrows = p.B * p.Hq * p.Nq;
@@ -547,13 +636,21 @@ hipError_t launch_d(const AttnLaunch &p, hipStream_t stream) {
 
 }  // namespace
 
+#if KVQ_TILE_TOKENS
+hipError_t launch_attention_tokens(const AttnLaunch &p, hipStream_t stream, bool split) {
+  if (split) return p.d == 64 ? launch_d<64, true>(p, stream) : launch_d<128, true>(p, stream);
+  return p.d == 64 ? launch_d<64, false>(p, stream) : launch_d<128, false>(p, stream);
+}
+#else
 hipError_t launch_attention_long(const AttnLaunch &p, hipStream_t stream) {
+  if (p.ktok || p.vtok) return launch_attention_tokens(p, stream, false);
   if (fast_path_supported(p)) return launch_attention_fast(p, stream);
   return p.d == 64 ? launch_d<64, false>(p, stream) : launch_d<128, false>(p, stream);
 }
 
 hipError_t launch_attention_short(const AttnLaunch &p, hipStream_t stream) {
-  if (short_fast_supported(p.d, p.corr)) return launch_attention_short_fast(p, stream);
+  if (p.ktok || p.vtok) return launch_attention_tokens(p, stream, true);
+  if (short_fast_supported(p.d, p.corr, false)) return launch_attention_short_fast(p, stream);
   return p.d == 64 ? launch_d<64, true>(p, stream) : launch_d<128, true>(p, stream);
 }
 
@@ -580,5 +677,6 @@ size_t short_path_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int32_t d, 
   return static_cast<size_t>(splits) * static_cast<size_t>(B * Hq * Nq) * static_cast<size_t>(kPartialStride(d)) *
          sizeof(float);
 }
+#endif
 
 }  // namespace kvq

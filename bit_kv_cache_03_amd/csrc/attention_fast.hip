@@ -939,7 +939,7 @@ hipError_t launch_attention_fast_causal(const AttnLaunch &p, hipStream_t stream)
   return launch_bits<4, 4>(p, stream);
 }
 #else
-bool fast_path_supported(const AttnLaunch &p) { return p.d == D && p.corr != KV_CORR_EXACT; }
+bool fast_path_supported(const AttnLaunch &p) { return p.d == D && p.corr != KV_CORR_EXACT && !p.ktok && !p.vtok; }
 
 void launch_key_scale(const AttnLaunch &p, hipStream_t stream, float *part) {
   const int32_t ng = D / p.group;

@@ -732,7 +732,9 @@ hipError_t launch_attention_short_fast_m16(const AttnLaunch &p, hipStream_t stre
   return launch_bits<4, 4>(p, stream);
 }
 #else
-bool short_fast_supported(int32_t d, int corr) { return d == D && corr != KV_CORR_EXACT; }
+bool short_fast_supported(int32_t d, int corr, bool tokens_axis) {
+  return d == D && corr != KV_CORR_EXACT && !tokens_axis;
+}
 
 int short_fast_splits(int64_t B, int64_t Hkv, int64_t rows_per_kvhead, int64_t Nc, int64_t Ncur, int cu_count) {
   const int64_t groups = B * Hkv * ((rows_per_kvhead + 31) / 32);

@@ -11,7 +11,7 @@ namespace {
 
 using kvq::AttnLaunch;
 
-constexpr int32_t kAbiVersion = 5;
+constexpr int32_t kAbiVersion = 6;
 constexpr int32_t kMaxSplits = 1024;  // grid z extent of the split path
 constexpr int64_t kMaxTokensPerHead = int64_t(1) << 23;  // 8M tokens: 32-bit in-head offsets
 
@@ -25,6 +25,13 @@ bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
 
 bool group_ok(int32_t group, int32_t d) {
   return (group == 32 || group == 64 || group == 128) && group <= d && d % group == 0;
+}
+
+// Group size of a cache tensor: along the head dimension it must divide d;
+// along the tokens any of 32, 64, 128.
+bool tensor_group_ok(const kv_qtensor *t, int32_t d) {
+  if (t->axis == KV_AXIS_TOKENS) return t->group == 32 || t->group == 64 || t->group == 128;
+  return group_ok(t->group, d);
 }
 
 // Byte ranges [a, a+na) and [b, b+nb) overlap.
@@ -46,8 +53,11 @@ kv_status check_qtensor(const kv_qtensor *t, int32_t d, int64_t need_rows, int64
   if (!t) return KV_ERR_NULL;
   if (!t->codes || !t->scale || !t->zero) return KV_ERR_NULL;
   if (t->bits != 2 && t->bits != 4) return KV_ERR_UNSUPPORTED;
-  if (!group_ok(t->group, d)) return KV_ERR_UNSUPPORTED;
+  if (t->axis != KV_AXIS_DIM && t->axis != KV_AXIS_TOKENS) return KV_ERR_UNSUPPORTED;
+  if (!tensor_group_ok(t, d)) return KV_ERR_UNSUPPORTED;
   if (t->cap < need_rows || t->cap < 0) return KV_ERR_SHAPE;
+  if (t->axis == KV_AXIS_TOKENS && (t->cap % t->group != 0 || (t->page_table && t->page_size % t->group != 0)))
+    return KV_ERR_SHAPE;
   if (t->cap > kMaxTokensPerHead) return KV_ERR_UNSUPPORTED;
   if (!aligned16(t->codes) || !aligned16(t->scale) || !aligned16(t->zero)) return KV_ERR_ALIGN;
   if (t->meta != KV_META_F32 && t->meta != KV_META_F16) return KV_ERR_UNSUPPORTED;
@@ -79,6 +89,18 @@ bool same_layout(const kv_qtensor *a, const kv_qtensor *b) {
 
 // Bytes of one step or zero-point element.
 size_t meta_bytes(const kv_qtensor *t) { return t->meta == KV_META_F16 ? 2 : 4; }
+
+// Bytes of a cache tensor's step (or zero-point) array over `rows` token rows.
+size_t meta_array_bytes(const kv_qtensor *t, size_t rows, int32_t d) {
+  const size_t elems = t->axis == KV_AXIS_TOKENS ? rows / static_cast<size_t>(t->group) * static_cast<size_t>(d)
+                                                 : rows * static_cast<size_t>(d / t->group);
+  return elems * meta_bytes(t);
+}
+
+// Either cache of a call groups along the tokens (general kernel only).
+bool tokens_axis(const kv_attn_args *a) {
+  return a->Nc > 0 && (a->k_cache->axis == KV_AXIS_TOKENS || a->v_cache->axis == KV_AXIS_TOKENS);
+}
 
 bool debug_log() {
   const char *e = getenv("KVQ_LOG");
@@ -150,10 +172,9 @@ kv_status validate_attention(const kv_attn_args *a) {
     const kv_qtensor *ts[2] = {a->k_cache, a->v_cache};
     for (const kv_qtensor *c : ts) {
       const size_t rows = static_cast<size_t>(tensor_rows(c, a->B, a->Hkv));
-      const size_t ng = static_cast<size_t>(a->d / c->group);
       if (overlaps(a->out, out_b, c->codes, rows * static_cast<size_t>(a->d * c->bits / 8)) ||
-          overlaps(a->out, out_b, c->scale, rows * ng * meta_bytes(c)) ||
-          overlaps(a->out, out_b, c->zero, rows * ng * meta_bytes(c)))
+          overlaps(a->out, out_b, c->scale, meta_array_bytes(c, rows, a->d)) ||
+          overlaps(a->out, out_b, c->zero, meta_array_bytes(c, rows, a->d)))
         return KV_ERR_ALIAS;
     }
   }
@@ -186,6 +207,7 @@ kv_status validate_diagnostics(const kv_diag_args *a) {
     if (!a->k_ref) return KV_ERR_NULL;
     const kv_status s = check_qtensor(a->k_cache, a->d, a->Nc, a->B);
     if (s != KV_OK) return s;
+    if (a->k_cache->axis != KV_AXIS_DIM) return KV_ERR_UNSUPPORTED;  // groups along the head dimension only
     if (!aligned16(a->k_ref)) return KV_ERR_ALIGN;
   }
   // the records must not overlap any input
@@ -195,11 +217,10 @@ kv_status validate_diagnostics(const kv_diag_args *a) {
   if (a->Nc > 0) {
     const kv_qtensor *c = a->k_cache;
     const size_t rows = static_cast<size_t>(tensor_rows(c, a->B, a->Hkv));
-    const size_t ng = static_cast<size_t>(a->d / c->group);
     if (overlaps(a->out, out_b, a->k_ref, static_cast<size_t>(nc_el) * 2) ||
         overlaps(a->out, out_b, c->codes, rows * static_cast<size_t>(a->d * c->bits / 8)) ||
-        overlaps(a->out, out_b, c->scale, rows * ng * meta_bytes(c)) ||
-          overlaps(a->out, out_b, c->zero, rows * ng * meta_bytes(c)))
+        overlaps(a->out, out_b, c->scale, meta_array_bytes(c, rows, a->d)) ||
+        overlaps(a->out, out_b, c->zero, meta_array_bytes(c, rows, a->d)))
       return KV_ERR_ALIAS;
   }
   return KV_OK;
@@ -213,14 +234,14 @@ Plan plan_attention(const kv_attn_args *a, bool query_device) {
   pl.path = path;
   if (path == KV_PATH_SHORT) {
     const int cus = query_device ? device_cu_count() : 256;
-    if (kvq::short_fast_supported(a->d, a->corr)) {
+    if (kvq::short_fast_supported(a->d, a->corr, tokens_axis(a))) {
       pl.splits = a->splits > 0 ? a->splits : kvq::short_fast_splits(a->B, a->Hkv, rows, a->Nc, a->Ncur, cus);
       pl.workspace = kvq::short_path_workspace_bytes(a->B, a->Hq, a->Nq, a->d, pl.splits);
     } else {
       pl.splits = a->splits > 0 ? a->splits : kvq::short_path_splits(a->B, a->Hkv, rows, a->Nc, cus);
       pl.workspace = kvq::short_path_workspace_bytes(a->B, a->Hq, a->Nq, a->d, pl.splits);
     }
-  } else if (a->d == 128 && a->corr != KV_CORR_EXACT) {  // the throughput kernel, split-K when it balances
+  } else if (a->d == 128 && a->corr != KV_CORR_EXACT && !tokens_axis(a)) {  // the throughput kernel, split-K when it balances
     const int cus = query_device ? device_cu_count() : 256;
     const kvq::FastPlan fp = kvq::fast_path_plan(a->B, a->Hq, a->Hkv, a->Nq, a->Nc, a->Ncur, cus, a->splits);
     pl.splits = fp.splits;
@@ -258,8 +279,13 @@ kv_status kv_quantize(const void *x, kv_dtype xdt, int64_t B, int64_t H, int64_t
   if (B < 1 || H < 1 || N < 0 || tok_offset < 0) return KV_ERR_SHAPE;
   if (!head_dim_ok(d)) return KV_ERR_UNSUPPORTED;
   if (dst->bits != 2 && dst->bits != 4) return KV_ERR_UNSUPPORTED;
-  if (!group_ok(dst->group, d)) return KV_ERR_UNSUPPORTED;
+  if (dst->axis != KV_AXIS_DIM && dst->axis != KV_AXIS_TOKENS) return KV_ERR_UNSUPPORTED;
+  if (!tensor_group_ok(dst, d)) return KV_ERR_UNSUPPORTED;
   if (dst->cap < 0 || tok_offset > dst->cap || N > dst->cap - tok_offset) return KV_ERR_SHAPE;
+  if (dst->axis == KV_AXIS_TOKENS &&
+      (tok_offset % dst->group != 0 || dst->cap % dst->group != 0 ||
+       (dst->page_table && dst->page_size % dst->group != 0)))
+    return KV_ERR_SHAPE;
   if (dst->page_table) {
     if (!page_size_ok(dst->page_size) || dst->cap % dst->page_size != 0) return KV_ERR_SHAPE;
     if (dst->num_pages < 1) return KV_ERR_SHAPE;
@@ -276,7 +302,7 @@ kv_status kv_quantize(const void *x, kv_dtype xdt, int64_t B, int64_t H, int64_t
   if (N == 0) return KV_OK;
   kvq::QuantizeLaunch p{x, static_cast<int>(xdt), B, H, N, d, dst->codes, static_cast<float *>(dst->scale),
                         static_cast<float *>(dst->zero), dst->bits, dst->group, dst->cap, tok_offset,
-                        layout_of(dst), dst->meta == KV_META_F16};
+                        layout_of(dst), dst->meta == KV_META_F16, dst->axis == KV_AXIS_TOKENS};
   return kvq::launch_quantize(p, static_cast<hipStream_t>(stream)) == hipSuccess ? KV_OK : KV_ERR_HIP;
 }
 
@@ -306,6 +332,8 @@ kv_status kv_attention_corrected(const kv_attn_args *a, void *stream) {
     p.vc_scale = static_cast<const float *>(a->v_cache->scale);
     p.vc_zero = static_cast<const float *>(a->v_cache->zero);
     p.meta16 = a->k_cache->meta == KV_META_F16;
+    p.ktok = a->k_cache->axis == KV_AXIS_TOKENS;
+    p.vtok = a->v_cache->axis == KV_AXIS_TOKENS;
     p.kbits = a->k_cache->bits; p.vbits = a->v_cache->bits; p.group = a->k_cache->group; p.cap = a->k_cache->cap;
     p.layout = layout_of(a->k_cache);
   } else {

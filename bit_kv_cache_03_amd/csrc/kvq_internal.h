@@ -46,6 +46,7 @@ struct QuantizeLaunch {
   int64_t cap, off;
   CacheLayout layout;
   bool meta16;  // scale and zero are binary16 (the pointers are then read as such)
+  bool tokens;  // groups along the tokens: scale/zero [row / group][d], row the cache row
 };
 
 // Everything an attention launch needs, already validated by the host.
@@ -60,6 +61,7 @@ struct AttnLaunch {
   int64_t cap;
   CacheLayout layout;  // of both caches
   bool meta16;         // the caches' scale and zero are binary16 (pointers read as such)
+  bool ktok, vtok;     // K / V groups along the tokens (per channel): scale/zero [row >> log2 group][d]
   float tau;   // resolved softmax scale
   int corr;    // kv_corr
   int causal;  // 1: current key i visible to query row j only if i <= j + Ncur - Nq
@@ -74,6 +76,9 @@ constexpr __host__ __device__ int64_t kPartialStride(int32_t d) { return d + 4; 
 
 hipError_t launch_quantize(const QuantizeLaunch &p, hipStream_t stream);
 hipError_t launch_attention_long(const AttnLaunch &p, hipStream_t stream);
+// The general kernel over caches grouped along the tokens (split: the
+// short-query path's key-range split), built in attention_tokens.hip.
+hipError_t launch_attention_tokens(const AttnLaunch &p, hipStream_t stream, bool split);
 hipError_t launch_attention_short(const AttnLaunch &p, hipStream_t stream);
 // Throughput kernel (attention_fast.hip): head dim 128, correction off or
 // Taylor.  Its workspace holds the split partials (when splits > 1, laid out
@@ -114,7 +119,7 @@ size_t short_path_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int32_t d, 
 hipError_t launch_combine(const float *ws, uint16_t *out, int64_t nrows, int splits, int32_t d, hipStream_t stream);
 // Short-query kernel (attention_short.hip): head dim 128, correction off or
 // Taylor; workspace = the split partials.
-bool short_fast_supported(int32_t d, int corr);
+bool short_fast_supported(int32_t d, int corr, bool tokens_axis);
 int short_fast_splits(int64_t B, int64_t Hkv, int64_t rows_per_kvhead, int64_t Nc, int64_t Ncur, int cu_count);
 hipError_t launch_attention_short_fast(const AttnLaunch &p, hipStream_t stream);
 // The same over a paged cache, with binary16 metadata, and both (built in

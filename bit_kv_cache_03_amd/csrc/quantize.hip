@@ -13,6 +13,12 @@
 // own one group and reduce min/max with cross-lane shuffles.  Each lane
 // writes its 8 codes as one 16-bit (INT2) or 32-bit (INT4) store, so a wave
 // writes a contiguous run of packed rows.  Pure streaming, HBM-bound.
+//
+// Groups along the tokens (per channel, the other grouping the method's
+// description names): one thread owns 8 consecutive channels of one token
+// group of one head.  It streams the group's rows once for the per-channel
+// minimum and maximum, then again (from cache) for the codes, which it
+// writes per token row in the same packed format.
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -150,10 +156,120 @@ hipError_t launch_t(const QuantizeLaunch &p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Groups along the tokens.  Thread = (b, h, token group j of the call,
+// channel octet); octets fastest, so a wave reads whole token rows.  The
+// call's tokens [off, off + N) start at a multiple of G; the last group may
+// be shorter.  Metadata row of a group = cache row of its first token >> log2 G.
+template <typename T, int BITS, bool M16>
+__global__ __launch_bounds__(kThreads) void quantize_tokens_pack(
+    const T *__restrict__ x, int64_t total, int32_t octets, int64_t groups, int64_t N, int32_t gshift,
+    uint8_t *__restrict__ codes, float *__restrict__ scale, float *__restrict__ zero, int64_t cap, int64_t off,
+    CacheLayout layout, int64_t H) {
+#pragma clang fp contract(off)
+  constexpr int TOP = (1 << BITS) - 1;
+  const int64_t id = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (id >= total) return;
+  const int32_t oc = static_cast<int32_t>(id % octets);
+  const int64_t rest = id / octets;
+  const int64_t j = rest % groups;
+  const int64_t bh = rest / groups;
+  const int64_t t0 = j << gshift;
+  const int64_t G = int64_t(1) << gshift;
+  const int cnt = static_cast<int>(N - t0 < G ? N - t0 : G);
+  const int32_t d = octets * 8;
+  const T *src = x + (bh * N + t0) * d + oc * 8;
+
+  float v[8], mn[8], mx[8];
+  load8<T>(src, v);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) mn[e] = mx[e] = v[e];
+  for (int i = 1; i < cnt; ++i) {
+    load8<T>(src + static_cast<int64_t>(i) * d, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      mn[e] = v[e] < mn[e] ? v[e] : mn[e];
+      mx[e] = v[e] > mx[e] ? v[e] : mx[e];
+    }
+  }
+  float step[8], zp[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    mn[e] = mn[e] + 0.0f;  // a zero extreme is +0
+    mx[e] = mx[e] + 0.0f;
+    step[e] = (mx[e] - mn[e]) / static_cast<float>(TOP);  // IEEE division
+    zp[e] = mn[e];
+    if (M16) {
+      step[e] = static_cast<float>(static_cast<_Float16>(step[e]));
+      zp[e] = static_cast<float>(static_cast<_Float16>(mn[e]));
+    }
+  }
+  const int64_t b = bh / H, h = bh - b * H;
+  const int64_t mrow = layout.row(cap, H, b, h, off + t0) >> gshift;
+  const int64_t m = mrow * d + oc * 8;
+  if (M16) {
+    _Float16 *ps = reinterpret_cast<_Float16 *>(scale) + m;
+    _Float16 *pz = reinterpret_cast<_Float16 *>(zero) + m;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ps[e] = static_cast<_Float16>(step[e]);
+      pz[e] = static_cast<_Float16>(zp[e]);
+    }
+  } else {
+    *reinterpret_cast<float4 *>(scale + m) = make_float4(step[0], step[1], step[2], step[3]);
+    *reinterpret_cast<float4 *>(scale + m + 4) = make_float4(step[4], step[5], step[6], step[7]);
+    *reinterpret_cast<float4 *>(zero + m) = make_float4(zp[0], zp[1], zp[2], zp[3]);
+    *reinterpret_cast<float4 *>(zero + m + 4) = make_float4(zp[4], zp[5], zp[6], zp[7]);
+  }
+
+  const int64_t row_bytes = static_cast<int64_t>(octets) * BITS;
+  for (int i = 0; i < cnt; ++i) {
+    load8<T>(src + static_cast<int64_t>(i) * d, v);
+    uint32_t packed = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint32_t c = 0;
+      if (step[e] > 0.0f) {
+        const float t = (v[e] - zp[e]) / step[e];  // IEEE division
+        c = static_cast<uint32_t>(fminf(fmaxf(rintf(t), 0.0f), static_cast<float>(TOP)));
+      }
+      packed |= c << (e * BITS);
+    }
+    const int64_t orow = layout.row(cap, H, b, h, off + t0 + i);
+    uint8_t *dst = codes + orow * row_bytes + static_cast<int64_t>(oc) * BITS;
+    if (BITS == 2)
+      *reinterpret_cast<uint16_t *>(dst) = static_cast<uint16_t>(packed);
+    else
+      *reinterpret_cast<uint32_t *>(dst) = packed;
+  }
+}
+
+template <typename T, int BITS, bool M16>
+hipError_t launch_tokens(const QuantizeLaunch &p, hipStream_t stream) {
+  const int32_t gshift = __builtin_ctz(static_cast<unsigned>(p.group));
+  const int64_t groups = (p.N + p.group - 1) / p.group;
+  const int32_t octets = p.d / 8;
+  const int64_t total = p.B * p.H * groups * octets;
+  const int64_t blocks = (total + kThreads - 1) / kThreads;
+  quantize_tokens_pack<T, BITS, M16><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream>>>(
+      static_cast<const T *>(p.x), total, octets, groups, p.N, gshift, p.codes, p.scale, p.zero, p.cap, p.off,
+      p.layout, p.H);
+  return hipGetLastError();
+}
+
+template <typename T, bool M16>
+hipError_t launch_tokens_bits(const QuantizeLaunch &p, hipStream_t stream) {
+  return p.bits == 2 ? launch_tokens<T, 2, M16>(p, stream) : launch_tokens<T, 4, M16>(p, stream);
+}
+
 }  // namespace
 
 hipError_t launch_quantize(const QuantizeLaunch &p, hipStream_t stream) {
   if (p.B * p.H * p.N == 0) return hipSuccess;
+  if (p.tokens) {
+    if (p.xdt == KV_BF16)
+      return p.meta16 ? launch_tokens_bits<uint16_t, true>(p, stream) : launch_tokens_bits<uint16_t, false>(p, stream);
+    return p.meta16 ? launch_tokens_bits<float, true>(p, stream) : launch_tokens_bits<float, false>(p, stream);
+  }
   if (p.meta16) {
     if (p.xdt == KV_BF16)
       return p.bits == 2 ? launch_t<uint16_t, 2, true>(p, stream) : launch_t<uint16_t, 4, true>(p, stream);

@@ -29,10 +29,11 @@ class QTensor(C.Structure):
     _fields_ = [("codes", C.c_void_p), ("scale", C.c_void_p), ("zero", C.c_void_p),
                 ("bits", C.c_int32), ("group", C.c_int32), ("cap", C.c_int64),
                 ("page_table", C.c_void_p), ("page_size", C.c_int32), ("num_pages", C.c_int32),
-                ("meta", C.c_int32)]
+                ("meta", C.c_int32), ("axis", C.c_int32)]
 
 
 META = {"f32": 0, "f16": 1}  # kv_meta: storage type of a cache tensor's step and zero point
+AXIS = {"dim": 0, "tokens": 1}  # kv_axis: groups along the head dimension or along the tokens
 
 
 class AttnArgs(C.Structure):
@@ -108,38 +109,50 @@ class QCache:
     tensor [B][cap // page_size] of page indices): pools of ``num_pages``
     pages [num_pages][H][page_size][...]; token t of (b, h) lives in page
     page_table[b][t // page_size] at row t % page_size.  ``meta``: "f32" or
-    "f16" (binary16 step and zero point)."""
+    "f16" (binary16 step and zero point).  ``axis``: "dim" (groups of
+    ``group`` channels per token) or "tokens" (per channel, groups of
+    ``group`` tokens: step and zero [B][H][cap // group][d], paged
+    [num_pages][H][page_size // group][d])."""
 
     def __init__(self, B: int, H: int, cap: int, d: int, bits: int, group: int = 64, device="cuda",
-                 page_table=None, page_size: int = 0, num_pages: int = 0, meta: str = "f32"):
+                 page_table=None, page_size: int = 0, num_pages: int = 0, meta: str = "f32", axis: str = "dim"):
         import torch
         if meta not in META:
             raise ValueError(f"meta must be one of {sorted(META)}")
+        if axis not in AXIS:
+            raise ValueError(f"axis must be one of {sorted(AXIS)}")
         self.B, self.H, self.cap, self.d, self.bits, self.group = B, H, cap, d, bits, group
         self.page_table, self.page_size, self.num_pages = page_table, page_size, num_pages
-        self.meta = meta
+        self.meta, self.axis = meta, axis
         lead = (num_pages, H, page_size) if page_table is not None else (B, H, cap)
         mdt = torch.float16 if meta == "f16" else torch.float32
         self.codes = torch.zeros(lead + (d * bits // 8,), dtype=torch.uint8, device=device)
-        self.scale = torch.zeros(lead + (d // group,), dtype=mdt, device=device)
-        self.zero = torch.zeros(lead + (d // group,), dtype=mdt, device=device)
+        mshape = lead[:2] + (lead[2] // group, d) if axis == "tokens" else lead + (d // group,)
+        self.scale = torch.zeros(mshape, dtype=mdt, device=device)
+        self.zero = torch.zeros(mshape, dtype=mdt, device=device)
 
     def descriptor(self) -> QTensor:
         return QTensor(self.codes.data_ptr(), self.scale.data_ptr(), self.zero.data_ptr(),
                        self.bits, self.group, self.cap,
                        self.page_table.data_ptr() if self.page_table is not None else None,
-                       self.page_size, self.num_pages, META[self.meta])
+                       self.page_size, self.num_pages, META[self.meta], AXIS[self.axis])
 
     def logical(self, nc: int):
         """(codes, step, zero) of tokens [0, nc) in the contiguous [B][H][nc][...]
-        order (a gather through the page table when paged)."""
+        order (a gather through the page table when paged); with axis
+        "tokens", step and zero of the ceil(nc / group) token groups."""
+        ng = -(-nc // self.group) if self.axis == "tokens" else nc
         if self.page_table is None:
-            return tuple(t[:, :, :nc] for t in (self.codes, self.scale, self.zero))
+            return self.codes[:, :, :nc], self.scale[:, :, :ng], self.zero[:, :, :ng]
         import torch
-        t = torch.arange(nc, device=self.codes.device)
-        page = self.page_table.long()[:, t // self.page_size]  # [B][nc]
-        row = t % self.page_size
-        return tuple(x[page, :, row.expand_as(page)].permute(0, 2, 1, 3) for x in (self.codes, self.scale, self.zero))
+
+        def gather(x, n, per_row):  # per_row: tokens per stored row (1, or group)
+            t = torch.arange(n, device=x.device) * per_row
+            page = self.page_table.long()[:, t // self.page_size]  # [B][n]
+            row = (t % self.page_size) // per_row
+            return x[page, :, row.expand_as(page)].permute(0, 2, 1, 3)
+        mper = self.group if self.axis == "tokens" else 1
+        return gather(self.codes, nc, 1), gather(self.scale, ng, mper), gather(self.zero, ng, mper)
 
 
 def quantize(x, cache: QCache, tok_offset: int = 0, stream=None) -> None:

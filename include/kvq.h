@@ -75,6 +75,19 @@ typedef enum {
                       per token per head); |values| must stay below 65504 */
 } kv_meta;
 
+/* Axis along which a cache tensor's groups run (agents-report.net page,
+ * §方法: the correction uses one step per group or per channel, D_{i,c}). */
+typedef enum {
+  KV_AXIS_DIM = 0,    /* along the head dimension (default): one D, z per token and
+                         group of `group` channels; scale/zero [..][cap][d/group] */
+  KV_AXIS_TOKENS = 1  /* along the tokens, per channel: one D, z per channel and group
+                         of `group` consecutive tokens (the first at a multiple of
+                         `group`); scale/zero [B][H][cap/group][d], paged
+                         [num_pages][H][page_size/group][d].  The bias of key i then
+                         uses D_{i/group, c} channel by channel.  Attention over such
+                         a cache runs on the general kernel */
+} kv_axis;
+
 /* Kernel path.  AUTO picks by rows per KV head; tests may force either. */
 typedef enum {
   KV_PATH_AUTO = 0,
@@ -113,6 +126,8 @@ typedef struct {
   int32_t page_size;
   int32_t num_pages;
   int32_t meta;   /* kv_meta of scale and zero; K and V caches of one call share it */
+  int32_t axis;   /* kv_axis; KV_AXIS_TOKENS needs cap (and page_size) to be multiples
+                     of group; K and V may differ */
 } kv_qtensor;
 
 /*
@@ -124,8 +139,13 @@ typedef struct {
  *   dst  : host pointer to the descriptor of the destination cache.
  * d must be 64 or 128.  N = 0 is a no-op.  Output is bit-exact with the
  * definition above (IEEE fp32 division, round half to even).
- * Errors: KV_ERR_NULL, KV_ERR_SHAPE (tok_offset + N > cap, ...),
- * KV_ERR_UNSUPPORTED (bits, group, d), KV_ERR_ALIGN, KV_ERR_HIP.
+ * KV_AXIS_TOKENS: tok_offset must be a multiple of group; the tokens of the
+ * call form groups [tok_offset + j*group, +group), the last one shorter when
+ * group does not divide N (quantised over the tokens it has; it cannot be
+ * extended later: the next call starts at the next multiple of group).
+ * Errors: KV_ERR_NULL, KV_ERR_SHAPE (tok_offset + N > cap, tok_offset not a
+ * multiple of a token group, ...), KV_ERR_UNSUPPORTED (bits, group, d, axis),
+ * KV_ERR_ALIGN, KV_ERR_HIP.
  */
 kv_status kv_quantize(const void *x, kv_dtype xdt, int64_t B, int64_t H, int64_t N, int32_t d,
                       const kv_qtensor *dst, int64_t tok_offset, void *stream);

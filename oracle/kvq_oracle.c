@@ -461,8 +461,12 @@ static void key_value(const rowctx *rc, int64_t t, double *k, double *v) {
     const int64_t base = bkv * a->cap + t;
     const uint8_t *kr = a->kc_codes + base * (d * a->kbits / 8);
     const uint8_t *vr = a->vc_codes + base * (d * a->vbits / 8);
+    /* channel c's step is at meta_index(.., 0) plus its group c / group, or
+     * plus c along the tokens */
+    const int64_t mk0 = meta_index(a, a->kaxis, bkv, t, 0), mv0 = meta_index(a, a->vaxis, bkv, t, 0);
     for (int32_t c = 0; c < d; ++c) {
-      const int64_t mk = meta_index(a, a->kaxis, bkv, t, c), mv = meta_index(a, a->vaxis, bkv, t, c);
+      const int32_t g = c / a->group;
+      const int64_t mk = mk0 + (a->kaxis == 0 ? g : c), mv = mv0 + (a->vaxis == 0 ? g : c);
       k[c] = (double)a->kc_zero[mk] + (double)a->kc_step[mk] * code_at(kr, c, a->kbits);
       v[c] = (double)a->vc_zero[mv] + (double)a->vc_step[mv] * code_at(vr, c, a->vbits);
     }

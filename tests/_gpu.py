@@ -19,13 +19,23 @@ def as_bf16_dev(x: np.ndarray) -> torch.Tensor:
     return to_dev(x if x.dtype == np.uint16 else W.bf16_bits(x))
 
 
-def build_cache(w, src: np.ndarray, bits: int, cap=None, chunk=None, meta="f32") -> kvq.QCache:
+def _chunk(w, chunk, axis):
+    chunk = max(1, w.Ncur) if chunk is None else chunk
+    if axis == "tokens":  # appends start at multiples of the token group
+        chunk = -(-chunk // w.group) * w.group
+    return chunk
+
+
+def build_cache(w, src: np.ndarray, bits: int, cap=None, chunk=None, meta="f32", axis="dim") -> kvq.QCache:
     """Quantize the cache source [B][H][Nc][d] on the GPU, appending chunks of
     `chunk` tokens (the last one partial) at increasing offsets (meta: the
-    storage type of step and zero point, "f32" or "f16")."""
+    storage type of step and zero point, "f32" or "f16"; axis: groups along
+    the head dimension or the tokens)."""
     cap = w.Nc if cap is None else cap
-    chunk = max(1, w.Ncur) if chunk is None else chunk
-    c = kvq.QCache(w.B, w.Hkv, cap, w.d, bits, w.group, meta=meta)
+    if axis == "tokens":
+        cap = -(-cap // w.group) * w.group
+    chunk = _chunk(w, chunk, axis)
+    c = kvq.QCache(w.B, w.Hkv, cap, w.d, bits, w.group, meta=meta, axis=axis)
     for off in range(0, w.Nc, chunk):
         n = min(chunk, w.Nc - off)
         kvq.quantize(to_dev(np.ascontiguousarray(src[:, :, off:off + n])), c, off)
@@ -33,7 +43,7 @@ def build_cache(w, src: np.ndarray, bits: int, cap=None, chunk=None, meta="f32")
 
 
 def cache_to_host(c: kvq.QCache, nc: int):
-    return tuple(t[:, :, :nc].cpu().numpy() for t in (c.codes, c.scale, c.zero))
+    return tuple(t.cpu().numpy() for t in c.logical(nc))
 
 
 def run_attention(w, data, kc, vc, corr="taylor", path="auto", scale=0.0, splits=0, causal=False):
@@ -95,7 +105,8 @@ def run_diagnostics(w, data, kc, corr="taylor", causal=False):
     return stats, tops
 
 
-def paged_cache(w, src: np.ndarray, bits: int, page_size: int, cap=None, chunk=None, seed=0, spare=3, meta="f32"):
+def paged_cache(w, src: np.ndarray, bits: int, page_size: int, cap=None, chunk=None, seed=0, spare=3, meta="f32",
+                axis="dim"):
     """The cache of build_cache in the paged layout: pages of page_size
     tokens, every (sequence, block) on a page drawn from a shuffled pool with
     `spare` unused pages, filled by kv_quantize through the page table."""
@@ -106,8 +117,8 @@ def paged_cache(w, src: np.ndarray, bits: int, page_size: int, cap=None, chunk=N
     perm = np.random.default_rng(seed).permutation(num_pages)[: w.B * pps].astype(np.int32)
     table = torch.from_numpy(perm.reshape(w.B, pps)).cuda()
     c = kvq.QCache(w.B, w.Hkv, cap, w.d, bits, w.group, page_table=table, page_size=page_size,
-                   num_pages=num_pages, meta=meta)
-    chunk = max(1, w.Ncur) if chunk is None else chunk
+                   num_pages=num_pages, meta=meta, axis=axis)
+    chunk = _chunk(w, chunk, axis)
     for off in range(0, w.Nc, chunk):
         n = min(chunk, w.Nc - off)
         kvq.quantize(to_dev(np.ascontiguousarray(src[:, :, off:off + n])), c, off)

@@ -6,6 +6,8 @@ the throughput kernel with its automatic key-range split, and the general
 kernel (exact correction) against the oracle.  Bar as in the other parity
 tests; values carry a per-channel offset so that outputs averaged over
 millions of keys stay of order one."""
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 
@@ -43,17 +45,28 @@ def test_largest_cache_per_head(orc):
     print("    cache bit-exact", flush=True)
     # Nq = 4 (16 rows per KV head): the short-query kernel (Taylor) and the
     # split general kernel (exact form); Nq = 20 (80 rows): the throughput
-    # kernel with its key-range split (Taylor, off)
+    # kernel with its key-range split (Taylor, off).  The GPU results come
+    # first; the oracle's four evaluations (each a full pass over 8M keys
+    # per row) then run side by side, four threads each.
+    runs = []
     for nq, corrs in ((4, ("taylor", "exact")), (20, ("taylor", "off"))):
         w = base.scaled(Nq=nq)
         d = dict(data, q=np.ascontiguousarray(data["q"][:, :, :nq]))
         for corr in corrs:
             # the oracle's exact form costs ~d log-sinh terms per key: fewer rows
-            n = 4 if corr == "exact" else 12
+            n = 2 if corr == "exact" else 4
             rows = np.unique(np.linspace(0, w.B * w.Hq * nq - 1, n).astype(np.int64))
             print(f"    Nq={nq} corr={corr} rows={rows.size}", flush=True)
             out = _gpu.run_attention(w, d, kc, vc, corr=corr)
-            got = _gpu.out_rows(out, rows)
-            prob = orc.Problem(as_bf16(d["q"]), as_bf16(d["k"]), as_bf16(d["v"]), okc, ovc, w.Nc, w.kbits, w.vbits,
-                               w.group, corr=corr)
-            _gpu.check(got, prob.attention(rows=rows), label=f"Nq={nq} {corr} ")
+            runs.append((w, d, corr, rows, _gpu.out_rows(out, rows)))
+
+    def oracle_rows(run):
+        w, d, corr, rows, _ = run
+        prob = orc.Problem(as_bf16(d["q"]), as_bf16(d["k"]), as_bf16(d["v"]), okc, ovc, w.Nc, w.kbits, w.vbits,
+                           w.group, corr=corr)
+        return prob.attention(rows=rows, threads=4)
+
+    with ThreadPoolExecutor(max_workers=len(runs)) as ex:
+        refs = list(ex.map(oracle_rows, runs))
+    for (w, _, corr, _, got), ref in zip(runs, refs):
+        _gpu.check(got, ref, label=f"Nq={w.Nq} {corr} ")
