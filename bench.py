@@ -51,12 +51,18 @@ def kernel_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def packed_bytes(w, meta_bytes: int = 4) -> int:
+def packed_bytes(w, meta_bytes: int = 4, kaxis: str = "dim", vaxis: str = "dim") -> int:
     """Algorithmic bytes of the packed cache read by one attention call:
     codes of K and V plus step and zero of both (fp32: 4 bytes each,
-    binary16: 2), over Nc tokens."""
-    per_tok = w.d * (w.kbits + w.vbits) // 8 + 2 * 2 * (w.d // w.group) * meta_bytes
-    return w.B * w.Hkv * w.Nc * per_tok
+    binary16: 2), over Nc tokens; a tensor grouped along the tokens holds
+    d steps and zero points per ceil(Nc / group) tokens instead of d / group
+    per token."""
+    codes = w.B * w.Hkv * w.Nc * (w.d * (w.kbits + w.vbits) // 8)
+    meta = 0
+    for axis in (kaxis, vaxis):
+        groups = -(-w.Nc // w.group) if axis == "tokens" else w.Nc * (w.d // w.group) // w.d
+        meta += w.B * w.Hkv * 2 * groups * w.d * meta_bytes
+    return codes + meta
 
 
 def visible_current_pairs(w, causal: bool) -> int:
@@ -77,7 +83,7 @@ def attention_flops(w, causal: bool = False) -> float:
 def call_options(args) -> dict:
     """The options of the timed attention call besides the workload."""
     return {"nq": args.nq, "corr": args.corr, "path": args.path, "causal": args.causal,
-            "page_size": args.page_size, "meta": args.meta}
+            "page_size": args.page_size, "meta": args.meta, "kaxis": args.kaxis, "vaxis": args.vaxis}
 
 
 def traffic_from_profiles(w, sha: str, options: dict):
@@ -94,20 +100,21 @@ def traffic_from_profiles(w, sha: str, options: dict):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(w, data, corr: str, target_s: float = 12.0, causal: bool = False, meta: str = "f32"):
+def cpu_baseline(w, data, corr: str, target_s: float = 12.0, causal: bool = False, meta: str = "f32",
+                 kaxis: str = "dim", vaxis: str = "dim"):
     """The oracle as it stands, on a bounded sample of query rows (all heads,
     rows spread over the chunk), with the quantize of the chunk prorated."""
     import oracle
     threads = len(os.sched_getaffinity(0))
-    kc = oracle.quantize(data["kc"], w.kbits, w.group, meta=meta)
-    vc = oracle.quantize(data["vc"], w.vbits, w.group, meta=meta)
+    kc = oracle.quantize(data["kc"], w.kbits, w.group, meta=meta, axis=kaxis)
+    vc = oracle.quantize(data["vc"], w.vbits, w.group, meta=meta, axis=vaxis)
     qb = lambda x: x if x.dtype == np.uint16 else W.bf16_bits(x)
     prob = oracle.Problem(qb(data["q"]), qb(data["k"]), qb(data["v"]), kc, vc, w.Nc, w.kbits, w.vbits,
-                          w.group, corr=corr, causal=causal)
+                          w.group, corr=corr, causal=causal, kaxis=kaxis, vaxis=vaxis)
     total = prob.rows_total()
     t0 = time.perf_counter()
-    oracle.quantize(data["k"], w.kbits, w.group, meta=meta)
-    oracle.quantize(data["v"], w.vbits, w.group, meta=meta)
+    oracle.quantize(data["k"], w.kbits, w.group, meta=meta, axis=kaxis)
+    oracle.quantize(data["v"], w.vbits, w.group, meta=meta, axis=vaxis)
     t_quant = time.perf_counter() - t0
     # grow a calibration sample until it runs for a second, then size the
     # timed sample for about target_s seconds
@@ -184,7 +191,8 @@ def write_traffic(w, pmc_dir: str, copy_bytes: int, options: dict):
          "fetch_factor": cf,
          "write_factor": cw, "per_kernel": per_kernel,
          "bytes_per_launch": sum(v["fetch_bytes"] + v["write_bytes"] for v in per_kernel.values()),
-         "algorithmic_packed_bytes": packed_bytes(w, 2 if options["meta"] == "f16" else 4)}
+         "algorithmic_packed_bytes": packed_bytes(w, 2 if options["meta"] == "f16" else 4, options["kaxis"],
+                                                  options["vaxis"])}
     out = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
     with open(out, "w") as fh:
         json.dump(t, fh, indent=1)
@@ -254,6 +262,9 @@ def main():
                     help="paged cache layout with pages of this many tokens (shuffled page table)")
     ap.add_argument("--meta", default="f32", choices=["f32", "f16"],
                     help="storage type of the caches' step and zero point")
+    ap.add_argument("--kaxis", default="dim", choices=["dim", "tokens"],
+                    help="K cache groups along the head dimension or along the tokens (per channel)")
+    ap.add_argument("--vaxis", default="dim", choices=["dim", "tokens"], help="the same for V")
     ap.add_argument("--diag", action="store_true",
                     help="time kv_attention_diagnostics and report the attention-balance statistics instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -289,6 +300,8 @@ def main():
                      else torch.from_numpy(W.bf16_bits(x).view(np.int16)).view(torch.bfloat16)).cuda()
     q, k, v = dev(data["q"]), dev(data["k"]), dev(data["v"])
     cap = w.Nc + w.Ncur
+    if "tokens" in (args.kaxis, args.vaxis):
+        cap = -(-cap // w.group) * w.group  # whole token groups
     if args.page_size:
         # pages of a shuffled pool: every (sequence, block) on a page drawn at random
         ps = args.page_size
@@ -299,8 +312,8 @@ def main():
         paged = dict(page_table=table, page_size=ps, num_pages=npages)
     else:
         paged = {}
-    kc = kvq.QCache(w.B, w.Hkv, cap, w.d, w.kbits, w.group, meta=args.meta, **paged)
-    vc = kvq.QCache(w.B, w.Hkv, cap, w.d, w.vbits, w.group, meta=args.meta, **paged)
+    kc = kvq.QCache(w.B, w.Hkv, cap, w.d, w.kbits, w.group, meta=args.meta, axis=args.kaxis, **paged)
+    vc = kvq.QCache(w.B, w.Hkv, cap, w.d, w.vbits, w.group, meta=args.meta, axis=args.vaxis, **paged)
     # the cache content does not depend on how it is appended (quantisation
     # is per token), so short chunks are appended in >= 4096-token calls
     chunk = max(w.Ncur, 4096)
@@ -312,8 +325,10 @@ def main():
         diag_bench(args, w, corr, data, dev, q, k, kc)
         return
     out = torch.empty_like(q)
-    args_c = kvq.make_args(q, k, v, kc, vc, w.Nc, out, corr=corr, path=args.path, causal=args.causal)
-    ws_bytes = kvq.workspace_size(args_c)
+    # one workspace for the timed mode and the correction-off comparison
+    # (which may take another kernel: the exact form runs on the general one)
+    ws_bytes = max(kvq.workspace_size(kvq.make_args(q, k, v, kc, vc, w.Nc, out, corr=c, path=args.path,
+                                                    causal=args.causal)) for c in (corr, "off"))
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
     args_c = kvq.make_args(q, k, v, kc, vc, w.Nc, out, corr=corr, path=args.path, workspace=ws,
                            causal=args.causal)
@@ -374,7 +389,7 @@ def main():
     achieved = flops / (attn_ms * 1e-3) / 1e12
     # few query rows per KV head: the packed cache read bounds the kernel
     hbm_bound = w.rows_per_kvhead <= 64
-    pbytes = packed_bytes(w, 2 if args.meta == "f16" else 4)
+    pbytes = packed_bytes(w, 2 if args.meta == "f16" else 4, args.kaxis, args.vaxis)
     if hbm_bound:
         roof = {"bound": "hbm", "achieved": pbytes / (attn_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
@@ -395,11 +410,12 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic: seeded N(0,1) q/k/v with the workload's key structure, bf16; cache INT%d/INT%d group %d%s" % (
-            w.kbits, w.vbits, w.group, ", binary16 step/zero" if args.meta == "f16" else ""),
+            w.kbits, w.vbits, w.group, (", binary16 step/zero" if args.meta == "f16" else "") +
+            (f", K/V groups along {args.kaxis}/{args.vaxis}" if "tokens" in (args.kaxis, args.vaxis) else "")),
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "Nq": w.Nq,
                    "Ncur": w.Ncur, "Nc": w.Nc, "kbits": w.kbits, "vbits": w.vbits, "group": w.group,
                    "corr": corr, "path": args.path, "causal": args.causal, "page_size": args.page_size,
-                   "meta": args.meta},
+                   "meta": args.meta, "kaxis": args.kaxis, "vaxis": args.vaxis},
         "attention_ms": attn_ms,
         "quantize_ms": quant_ms,
         "tflops_eff": achieved,
@@ -411,7 +427,8 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, data, corr, causal=args.causal, meta=args.meta)
+        line["cpu_baseline"] = cpu_baseline(w, data, corr, causal=args.causal, meta=args.meta, kaxis=args.kaxis,
+                                            vaxis=args.vaxis)
     print(json.dumps(line), flush=True)
 
 

@@ -31,3 +31,5 @@ def test_flops_and_bytes_of_the_default_workload():
     assert bench.packed_bytes(w) == 24 * 16384 * 160
     # binary16 step and zero: 16 bytes of metadata per token instead of 32
     assert bench.packed_bytes(w, 2) == 24 * 16384 * 144
+    # K grouped along the tokens (group 64): 2 x 128 fp32 values per 64 tokens (16 bytes per token)
+    assert bench.packed_bytes(w, 4, "tokens", "dim") == 24 * 16384 * 128 + 24 * 256 * 2 * 128 * 4 + 24 * 16384 * 16
