@@ -109,6 +109,17 @@ __device__ inline float logsinhc(float x) {
   return a - logf(2.0f * a) + log1pf(-expf(-2.0f * a));
 }
 
+// Metadata elements i .. i+3 (i a multiple of 4): fp32, or binary16 when
+// meta16; one 16-byte or 8-byte load.
+__device__ inline float4 meta4(const float *p, int64_t i, bool meta16) {
+  if (meta16) {
+    const uint2 w = *reinterpret_cast<const uint2 *>(reinterpret_cast<const _Float16 *>(p) + i);
+    const auto h = [](uint32_t x) { return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(x))); };
+    return make_float4(h(w.x), h(w.x >> 16), h(w.y), h(w.y >> 16));
+  }
+  return *reinterpret_cast<const float4 *>(p + i);
+}
+
 // code j of a packed word: BITS-wide fields, LSB first.
 template <int BITS>
 __device__ inline float code_f(uint32_t w, int j) {
@@ -279,15 +290,16 @@ __global__ __launch_bounds__(kThreads, EXACT || TOK ? 1 : 2) void attn_tile_kern
             put(e, fmaf(stp, code_f<KBITS>(w[e / PER], e % PER), zp),
                 fmaf(stp, code_f<KBITS>(w[(e + 1) / PER], (e + 1) % PER), zp));
         } else {  // groups along the tokens: one per channel of the key's token group
+          // (row is a valid cache row also for keys past the tile's end;
+          // put() zeroes their values)
           const int64_t m0 = (row >> group_shift) * D + d0;
 #pragma unroll
-          for (int e = 0; e < DPT; e += 2) {
-            const float sa = ok ? meta_at(p.kc_scale, m0 + e, p.meta16) : 0.f;
-            const float za = ok ? meta_at(p.kc_zero, m0 + e, p.meta16) : 0.f;
-            const float sc = ok ? meta_at(p.kc_scale, m0 + e + 1, p.meta16) : 0.f;
-            const float zc = ok ? meta_at(p.kc_zero, m0 + e + 1, p.meta16) : 0.f;
-            put(e, fmaf(sa, code_f<KBITS>(w[e / PER], e % PER), za),
-                fmaf(sc, code_f<KBITS>(w[(e + 1) / PER], (e + 1) % PER), zc));
+          for (int e = 0; e < DPT; e += 4) {
+            const float4 s4 = meta4(p.kc_scale, m0 + e, p.meta16), z4 = meta4(p.kc_zero, m0 + e, p.meta16);
+            put(e, fmaf(s4.x, code_f<KBITS>(w[e / PER], e % PER), z4.x),
+                fmaf(s4.y, code_f<KBITS>(w[(e + 1) / PER], (e + 1) % PER), z4.y));
+            put(e + 2, fmaf(s4.z, code_f<KBITS>(w[(e + 2) / PER], (e + 2) % PER), z4.z),
+                fmaf(s4.w, code_f<KBITS>(w[(e + 3) / PER], (e + 3) % PER), z4.w));
           }
         }
         uint4 *dlo = reinterpret_cast<uint4 *>(&Ks[key * KS + Tile<D>::kLo + d0]);
@@ -364,10 +376,12 @@ __global__ __launch_bounds__(kThreads, EXACT || TOK ? 1 : 2) void attn_tile_kern
             } else {  // groups along the tokens: one per channel
               const int64_t m0 = (row >> group_shift) * D + 8 * dq;
 #pragma unroll
-              for (int e = 0; e < 8; ++e)
-                v[j][e] = ok ? fmaf(meta_at(p.vc_scale, m0 + e, p.meta16), code_f<VBITS>(w, e),
-                                    meta_at(p.vc_zero, m0 + e, p.meta16))
-                             : 0.f;
+              for (int e4 = 0; e4 < 8; e4 += 4) {
+                const float4 s4 = meta4(p.vc_scale, m0 + e4, p.meta16), z4 = meta4(p.vc_zero, m0 + e4, p.meta16);
+                const float sv[4] = {s4.x, s4.y, s4.z, s4.w}, zv[4] = {z4.x, z4.y, z4.z, z4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[j][e4 + e] = ok ? fmaf(sv[e], code_f<VBITS>(w, e4 + e), zv[e]) : 0.f;
+              }
             }
           }
         } else {

@@ -17,6 +17,9 @@
 // both sets, a running max, sum, current-chunk sum and its 5 largest scores
 // (with indices), plus sum p_ref (s_ref - s_q) for the KL divergence.  The
 // two halves of a row merge at the end.  No value product: scores only.
+// Caches grouped along the tokens (per channel) are dequantised channel by
+// channel, and their bias is one value per row and 32-key half of a tile
+// (one token group), as in the general attention kernel.
 #include <math.h>
 
 #include "kvq_device.h"
@@ -113,6 +116,7 @@ __global__ __launch_bounds__(THREADS) void attn_diag_kernel(DiagLaunch p, int32_
   __shared__ __attribute__((aligned(16))) uint16_t Kr[BN * RS];
   __shared__ float Dk[EXACT ? BN * 4 : 1];
   __shared__ __attribute__((aligned(16))) uint16_t Qs[EXACT ? BM * (D + 8) : 1];
+  __shared__ __attribute__((aligned(16))) float Dt[2 * D];  // token groups: steps of each 32-key half
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -195,9 +199,10 @@ __global__ __launch_bounds__(THREADS) void attn_diag_kernel(DiagLaunch p, int32_
       uint32_t hi[DPT / 2];
       if (cached) {
         const int64_t row = p.layout.row(p.cap, p.Hkv, b, hk, k0 + (ok ? key : 0));  // cache row of the key
-        const int g = d0 >> group_shift;
-        const float st = ok ? meta_at(p.kc_scale, row * ng + g, p.meta16) : 0.f;
-        const float zp = ok ? meta_at(p.kc_zero, row * ng + g, p.meta16) : 0.f;
+        // one step / zero point for the thread's values (a group of the row),
+        // or one per channel (groups along the tokens)
+        const int64_t m0 = p.ktok ? (row >> group_shift) * D + d0 : row * ng + (d0 >> group_shift);
+        const int mstep = p.ktok ? 1 : 0;
         constexpr int WORDS = DPT * KBITS / 32;
         constexpr int PER = 32 / KBITS;
         uint32_t w[WORDS];
@@ -207,8 +212,12 @@ __global__ __launch_bounds__(THREADS) void attn_diag_kernel(DiagLaunch p, int32_
         uint32_t lo[DPT / 2];
 #pragma unroll
         for (int e = 0; e < DPT; e += 2) {
-          const float a = fmaf(st, code_at<KBITS>(w[e / PER], e % PER), zp);
-          const float c = fmaf(st, code_at<KBITS>(w[(e + 1) / PER], (e + 1) % PER), zp);
+          const float sa = meta_at(p.kc_scale, m0 + mstep * e, p.meta16);
+          const float za = meta_at(p.kc_zero, m0 + mstep * e, p.meta16);
+          const float sc = meta_at(p.kc_scale, m0 + mstep * (e + 1), p.meta16);
+          const float zc = meta_at(p.kc_zero, m0 + mstep * (e + 1), p.meta16);
+          const float a = fmaf(sa, code_at<KBITS>(w[e / PER], e % PER), za);
+          const float c = fmaf(sc, code_at<KBITS>(w[(e + 1) / PER], (e + 1) % PER), zc);
           hi[e / 2] = ok ? bf16_pair(a, c) : 0u;
           lo[e / 2] = ok ? bf16_pair(a - lo_f(hi[e / 2]), c - hi_f(hi[e / 2])) : 0u;
         }
@@ -222,7 +231,13 @@ __global__ __launch_bounds__(THREADS) void attn_diag_kernel(DiagLaunch p, int32_
 #pragma unroll
         for (int i = 0; i < DPT / 8; ++i)
           *reinterpret_cast<uint4 *>(&Kr[key * RS + d0 + 8 * i]) = ok ? rs[i] : make_uint4(0, 0, 0, 0);
-        if ((tid & 3) == 0) {
+        if (p.ktok && !(CORR == KV_CORR_OFF) && tid < 2 * D) {
+          const int hk0 = 32 * (tid / D);  // first key of the half
+          const bool okh = hk0 < count;
+          const int64_t hrow = p.layout.row(p.cap, p.Hkv, b, hk, k0 + (okh ? hk0 : 0));
+          Dt[tid] = okh ? meta_at(p.kc_scale, (hrow >> group_shift) * D + tid % D, p.meta16) : 0.f;
+        }
+        if ((tid & 3) == 0 && !p.ktok) {
           // correction slots 3g+{0,1,2} = -D^2 split (hi, lo, hi)
           float e16[16];
           float dsh[4] = {0.f, 0.f, 0.f, 0.f}, dsl[4] = {0.f, 0.f, 0.f, 0.f};
@@ -259,6 +274,32 @@ __global__ __launch_bounds__(THREADS) void attn_diag_kernel(DiagLaunch p, int32_
     }
     __syncthreads();
 
+    // groups along the tokens: the bias of each 32-key half (one token
+    // group) for the lane's row, in logit units
+    float tokb[2] = {0.f, 0.f};
+    if (cached && p.ktok && CORR != KV_CORR_OFF) {
+      const float half_tau = 0.5f * p.tau;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const uint4 w = __builtin_bit_cast(uint4, qreg[s]);
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float qv = (i & 1) ? hi_f(u[i >> 1]) : lo_f(u[i >> 1]);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            const float st = Dt[kb * D + 16 * s + 8 * h + i];
+            tokb[kb] += TAYLOR ? qv * qv * (st * st) : log_sinhc(half_tau * qv * st);
+          }
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const float tot = tokb[kb] + __shfl_xor(tokb[kb], 32, 64);
+        tokb[kb] = TAYLOR ? tot * (p.tau * p.tau / 24.0f) : tot;
+      }
+    }
+
     // S^T of both sets: lane (query qc) gets keys kb*32 + 8(i/4) + 4h + i%4
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -277,17 +318,17 @@ __global__ __launch_bounds__(THREADS) void attn_diag_kernel(DiagLaunch p, int32_
           ar = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8 *>(kr + 16 * s), qreg[s],
                                                        ar, 0, 0, 0);
         }
-        if (TAYLOR)
+        if (TAYLOR && !p.ktok)
           aq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8 *>(kq + DTile<D>::kExt),
                                                        qext, aq, 0, 0, 0);
       }
       float sq[16], sr[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        sq[i] = aq[i] * p.tau;
+        sq[i] = aq[i] * p.tau - tokb[kb];
         sr[i] = cached ? ar[i] * p.tau : sq[i];
       }
-      if (EXACT && cached) {
+      if (EXACT && cached && !p.ktok) {
         const uint16_t *qs = &Qs[(wave * 32 + qc) * (D + 8)];
         const float half_tau = 0.5f * p.tau;
         for (int g = 0; g < ng; ++g) {

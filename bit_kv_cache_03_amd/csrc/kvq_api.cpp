@@ -207,7 +207,6 @@ kv_status validate_diagnostics(const kv_diag_args *a) {
     if (!a->k_ref) return KV_ERR_NULL;
     const kv_status s = check_qtensor(a->k_cache, a->d, a->Nc, a->B);
     if (s != KV_OK) return s;
-    if (a->k_cache->axis != KV_AXIS_DIM) return KV_ERR_UNSUPPORTED;  // groups along the head dimension only
     if (!aligned16(a->k_ref)) return KV_ERR_ALIGN;
   }
   // the records must not overlap any input
@@ -367,6 +366,7 @@ kv_status kv_attention_diagnostics(const kv_diag_args *a, void *stream) {
     p.kc_scale = static_cast<const float *>(a->k_cache->scale);
     p.kc_zero = static_cast<const float *>(a->k_cache->zero);
     p.meta16 = a->k_cache->meta == KV_META_F16;
+    p.ktok = a->k_cache->axis == KV_AXIS_TOKENS;
     p.kbits = a->k_cache->bits; p.group = a->k_cache->group; p.cap = a->k_cache->cap;
     p.layout = layout_of(a->k_cache);
   } else {

@@ -140,6 +140,7 @@ struct DiagLaunch {
   int64_t cap;
   CacheLayout layout;
   bool meta16;
+  bool ktok;  // the K cache groups along the tokens (per channel)
   float tau;   // resolved softmax scale
   int corr;    // kv_corr
   int causal;

@@ -357,14 +357,13 @@ def test_attention_tokens_axis(kvq):
     a._k.axis = 1  # K per channel along the tokens, V along the head dimension
     a.k_cache, a.v_cache = C.pointer(a._k), C.pointer(a._v)
     assert kvq.lib.kv_attention_workspace_size(C.byref(a)) > 0  # valid (16 rows per KV head: split path)
-    # the diagnostics take head-dimension groups only
+    a._k.cap = 100  # cap must be a multiple of the token group
+    assert _attn(kvq, a) == kvq.KV_ERR_SHAPE
     d = kvq.DiagArgs()
     d.B, d.Hq, d.Hkv, d.Nq, d.Ncur, d.Nc, d.d, d.corr = 1, 4, 2, 8, 8, 50, 128, 1
     d.q, d.k_cur, d.k_ref, d.out = A, 2 * A, 3 * A, 4 * A
     d.k_cache = C.pointer(a._k)
-    assert kvq.lib.kv_attention_diagnostics(C.byref(d), None) == kvq.KV_ERR_UNSUPPORTED
-    a._k.cap = 100  # cap must be a multiple of the token group
-    assert _attn(kvq, a) == kvq.KV_ERR_SHAPE
+    assert kvq.lib.kv_attention_diagnostics(C.byref(d), None) == kvq.KV_ERR_SHAPE
 
 
 def test_binding_axis_shapes():

@@ -31,9 +31,9 @@ CASES = {
 }
 
 
-def _scores(orc, w, data, corr, causal, row, meta="f32"):
+def _scores(orc, w, data, corr, causal, row, meta="f32", kaxis="dim"):
     """Oracle scores of one row: quantised (kvo_logits) and reference."""
-    p = oracle_problem(orc, w, corr, data=data, causal=causal, meta=meta)
+    p = oracle_problem(orc, w, corr, data=data, causal=causal, meta=meta, kaxis=kaxis)
     sq = p.logits(row)
     rep = w.Hq // w.Hkv
     b, h, j = row // (w.Hq * w.Nq), (row // w.Nq) % w.Hq, row % w.Nq
@@ -55,16 +55,16 @@ def check_top(got, want, s, label):
     assert np.all(np.abs(s[g] - s[want[:nv]]) <= eps), (label, got, want, s[g], s[want[:nv]])
 
 
-def _compare(orc, w, causal, corr, data=None, max_rows=400, meta="f32"):
+def _compare(orc, w, causal, corr, data=None, max_rows=400, meta="f32", kaxis="dim"):
     import _gpu
     data = W.generate(w) if data is None else data
     print(f"[diagnostics] B={w.B} Hq={w.Hq} Hkv={w.Hkv} d={w.d} Nq={w.Nq} Ncur={w.Ncur} Nc={w.Nc} "
-          f"bits={w.kbits} group={w.group} corr={corr} causal={causal} meta={meta}", flush=True)
-    kc = _gpu.build_cache(w, data["kc"], w.kbits, meta=meta) if w.Nc > 0 else None
+          f"bits={w.kbits} group={w.group} corr={corr} causal={causal} meta={meta} kaxis={kaxis}", flush=True)
+    kc = _gpu.build_cache(w, data["kc"], w.kbits, meta=meta, axis=kaxis) if w.Nc > 0 else None
     stats, tops = _gpu.run_diagnostics(w, data, kc, corr=corr, causal=causal)
     n = stats.shape[0]
     rows = np.arange(n) if n <= max_rows else np.linspace(0, n - 1, max_rows).astype(np.int64)
-    ref, rtop = oracle_problem(orc, w, corr, data=data, causal=causal, meta=meta).diagnostics(
+    ref, rtop = oracle_problem(orc, w, corr, data=data, causal=causal, meta=meta, kaxis=kaxis).diagnostics(
         as_bf16(data["kc"]), rows=rows)
     got = stats[rows]
     lse_err = np.abs(got[:, :2] - ref[:, :2]) - 1e-5 * np.abs(ref[:, :2])
@@ -73,7 +73,7 @@ def _compare(orc, w, causal, corr, data=None, max_rows=400, meta="f32"):
     kl_err = np.abs(got[:, 4] - ref[:, 4]) - 1e-3 * np.abs(ref[:, 4])
     assert kl_err.max() <= 2e-4, kl_err.max()
     for i, row in enumerate(rows[:64]):
-        sr, sq = _scores(orc, w, data, corr, causal, int(row), meta)
+        sr, sq = _scores(orc, w, data, corr, causal, int(row), meta, kaxis)
         check_top(tops[row, 0], rtop[i, 0], sr, f"row {row} ref")
         check_top(tops[row, 1], rtop[i, 1], sq, f"row {row} q")
     return stats, ref

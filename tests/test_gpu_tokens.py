@@ -4,8 +4,9 @@ oracle run with the same grouping: kv_quantize's codes, steps and zero
 points bit-exact (appended in chunks of whole groups, a shorter last group,
 fp32 or binary16 metadata, contiguous or paged), and the attention within
 the output tolerance on the long and short paths, with every correction
-mode, the causal mask, d = 64 and 128, K or V or both grouped this way.  The
-paged results are also bit-identical to the contiguous ones."""
+mode, the causal mask, d = 64 and 128, K or V or both grouped this way, and
+the attention-balance diagnostics over such a K cache.  The paged results
+are also bit-identical to the contiguous ones."""
 import numpy as np
 import pytest
 import torch
@@ -128,6 +129,14 @@ def test_attention_tokens_short_queries(orc):
 
 
 @pytest.mark.parametrize("case", ["k_tokens_int4", "both_tokens_gqa", "k_tokens_d64"])
+@pytest.mark.parametrize("corr", ["off", "taylor", "exact"])
+def test_diagnostics_tokens(orc, case, corr):
+    from test_gpu_diagnostics import _compare as diag_compare
+    w, _, _ = ACASES[case]
+    diag_compare(orc, w, case == "both_tokens_gqa", corr, kaxis="tokens")
+
+
+@pytest.mark.parametrize("case", ["k_tokens_int4", "both_tokens_gqa", "k_tokens_d64"])
 def test_paged_tokens_matches_contiguous(case):
     import _gpu
     w, kaxis, vaxis = ACASES[case]
@@ -149,3 +158,7 @@ def test_paged_tokens_matches_contiguous(case):
         a = _gpu.run_attention(w, data, kc, vc, corr=corr, path=path, splits=splits, causal=causal)
         b = _gpu.run_attention(w, data, pk, pv, corr=corr, path=path, splits=splits, causal=causal)
         assert torch.equal(a.view(torch.int16), b.view(torch.int16)), (corr, path, splits, causal)
+    if kaxis == "tokens":
+        ra = _gpu.run_diagnostics(w, data, kc, corr="taylor")
+        rb = _gpu.run_diagnostics(w, data, pk, corr="taylor")
+        assert np.array_equal(ra[0], rb[0]) and np.array_equal(ra[1], rb[1])
