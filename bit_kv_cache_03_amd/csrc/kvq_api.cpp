@@ -276,6 +276,7 @@ kv_status kv_quantize(const void *x, kv_dtype xdt, int64_t B, int64_t H, int64_t
   if (!dst->codes || !dst->scale || !dst->zero) return KV_ERR_NULL;
   if (xdt != KV_BF16 && xdt != KV_F32) return KV_ERR_UNSUPPORTED;
   if (B < 1 || H < 1 || N < 0 || tok_offset < 0) return KV_ERR_SHAPE;
+  if (B > 65535 || H > 65535) return KV_ERR_UNSUPPORTED;  // grid y and z extents
   if (!head_dim_ok(d)) return KV_ERR_UNSUPPORTED;
   if (dst->bits != 2 && dst->bits != 4) return KV_ERR_UNSUPPORTED;
   if (dst->axis != KV_AXIS_DIM && dst->axis != KV_AXIS_TOKENS) return KV_ERR_UNSUPPORTED;

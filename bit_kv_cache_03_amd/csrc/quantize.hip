@@ -62,24 +62,49 @@ __device__ inline void load8<float>(const float *p, float (&v)[8]) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
+// Code of value v: rne((v - zp) / step) clamped to [0, TOP], with the IEEE
+// quotient of the definition.  The product with the reciprocal (v_rcp_f32,
+// 1 ulp; then one rounding) lies within 2^-21 |q| of that quotient, so when
+// it is farther than 2^-19 |q| + 2^-20 from every half-integer the two round
+// to the same integer; otherwise, or when step is outside [2^-120, 2^120]
+// (reciprocal not a normal number), the division itself is taken.
+template <int TOP>
+__device__ inline uint32_t code_of(float v, float zp, float step, float inv, bool fast) {
+#pragma clang fp contract(off)
+  const float num = v - zp;
+  float r;
+  const float q = num * inv;
+  const float frac = q - floorf(q);
+  if (fast && fabsf(frac - 0.5f) > fmaf(fabsf(q), 0x1p-19f, 0x1p-20f))
+    r = rintf(q);
+  else
+    r = rintf(num / step);  // IEEE division
+  return static_cast<uint32_t>(fminf(fmaxf(r, 0.0f), static_cast<float>(TOP)));
+}
+
+__device__ inline bool reciprocal_ok(float step) { return step >= 0x1p-120f && step <= 0x1p120f; }
+
 // T: uint16_t (bf16 bits) or float.  LANES = group / 8.  M16: the step and
 // zero point are stored as binary16, rounded (nearest, ties to even) before
 // the codes are taken so that z + D c uses exactly what is stored.
+// Grid: x over the N * d/8 lanes of one (b, h) = (blockIdx.z, blockIdx.y).
 template <typename T, int BITS, int LANES, bool M16>
 __global__ __launch_bounds__(kThreads) void quantize_pack(
-    const T *__restrict__ x, int64_t total_lanes, int32_t lanes_per_row, int64_t N,
+    const T *__restrict__ x, int32_t lane_shift, int64_t N,
     uint8_t *__restrict__ codes, float *__restrict__ scale, float *__restrict__ zero,
     int64_t cap, int64_t off, int32_t groups_per_row, CacheLayout layout, int64_t H) {
 #pragma clang fp contract(off)
   constexpr int TOP = (1 << BITS) - 1;
   const int64_t gl = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  const bool live = gl < total_lanes;
-  const int64_t lane_id = live ? gl : total_lanes - 1;  // dead lanes shadow a live row
-  const int64_t row = lane_id / lanes_per_row;          // (b*H + h)*N + n
-  const int32_t chunk = static_cast<int32_t>(lane_id % lanes_per_row);
+  const int64_t bh = static_cast<int64_t>(blockIdx.z) * H + blockIdx.y;
+  const int32_t lanes_per_row = 1 << lane_shift;
+  const bool live = gl < (N << lane_shift);
+  // dead lanes (whole groups past the last token) shadow the last token
+  const int64_t n = live ? (gl >> lane_shift) : N - 1;
+  const int32_t chunk = static_cast<int32_t>(gl & (lanes_per_row - 1));
 
   float v[8];
-  load8<T>(x + lane_id * 8, v);
+  load8<T>(x + ((bh * N + n) << (lane_shift + 3)) + chunk * 8, v);
 
   float mn = v[0], mx = v[0];
 #pragma unroll
@@ -98,21 +123,15 @@ __global__ __launch_bounds__(kThreads) void quantize_pack(
   }
 
   uint32_t packed = 0;
+  if (step > 0.0f) {
+    const bool fast = reciprocal_ok(step);
+    const float inv = fast ? __builtin_amdgcn_rcpf(step) : 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t c = 0;
-    if (step > 0.0f) {
-      const float t = (v[i] - zp) / step;  // IEEE division
-      const float r = fminf(fmaxf(rintf(t), 0.0f), static_cast<float>(TOP));
-      c = static_cast<uint32_t>(r);
-    }
-    packed |= c << (i * BITS);
+    for (int i = 0; i < 8; ++i) packed |= code_of<TOP>(v[i], zp, step, inv, fast) << (i * BITS);
   }
 
   if (!live) return;
-  const int64_t bh = row / N;
-  const int64_t n = row - bh * N;
-  const int64_t orow = layout.row(cap, H, bh / H, bh % H, off + n);  // the cache row of token off + n
+  const int64_t orow = layout.row(cap, H, blockIdx.z, blockIdx.y, off + n);  // the cache row of token off + n
   const int64_t row_bytes = static_cast<int64_t>(lanes_per_row) * BITS;  // 8 codes * BITS / 8 per lane
   uint8_t *dst = codes + orow * row_bytes + static_cast<int64_t>(chunk) * BITS;
   if (BITS == 2) {
@@ -134,23 +153,23 @@ __global__ __launch_bounds__(kThreads) void quantize_pack(
 
 template <typename T, int BITS, bool M16>
 hipError_t launch_t(const QuantizeLaunch &p, hipStream_t stream) {
-  const int32_t lanes_per_row = p.d / 8;
-  const int64_t total = p.B * p.H * p.N * lanes_per_row;
-  const int64_t blocks = (total + kThreads - 1) / kThreads;
+  const int32_t lane_shift = __builtin_ctz(static_cast<unsigned>(p.d / 8));  // d/8 lanes per token row
+  const int64_t blocks = ((p.N << lane_shift) + kThreads - 1) / kThreads;
+  const dim3 grid(static_cast<uint32_t>(blocks), static_cast<uint32_t>(p.H), static_cast<uint32_t>(p.B));
   const T *x = static_cast<const T *>(p.x);
   const int32_t gpr = p.d / p.group;
   switch (p.group) {
     case 32:
-      quantize_pack<T, BITS, 4, M16><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream>>>(
-          x, total, lanes_per_row, p.N, p.codes, p.scale, p.zero, p.cap, p.off, gpr, p.layout, p.H);
+      quantize_pack<T, BITS, 4, M16><<<grid, dim3(kThreads), 0, stream>>>(
+          x, lane_shift, p.N, p.codes, p.scale, p.zero, p.cap, p.off, gpr, p.layout, p.H);
       break;
     case 64:
-      quantize_pack<T, BITS, 8, M16><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream>>>(
-          x, total, lanes_per_row, p.N, p.codes, p.scale, p.zero, p.cap, p.off, gpr, p.layout, p.H);
+      quantize_pack<T, BITS, 8, M16><<<grid, dim3(kThreads), 0, stream>>>(
+          x, lane_shift, p.N, p.codes, p.scale, p.zero, p.cap, p.off, gpr, p.layout, p.H);
       break;
     default:
-      quantize_pack<T, BITS, 16, M16><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream>>>(
-          x, total, lanes_per_row, p.N, p.codes, p.scale, p.zero, p.cap, p.off, gpr, p.layout, p.H);
+      quantize_pack<T, BITS, 16, M16><<<grid, dim3(kThreads), 0, stream>>>(
+          x, lane_shift, p.N, p.codes, p.scale, p.zero, p.cap, p.off, gpr, p.layout, p.H);
       break;
   }
   return hipGetLastError();
@@ -221,19 +240,20 @@ __global__ __launch_bounds__(kThreads) void quantize_tokens_pack(
     *reinterpret_cast<float4 *>(zero + m + 4) = make_float4(zp[4], zp[5], zp[6], zp[7]);
   }
 
+  float inv[8];
+  bool fast[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    fast[e] = reciprocal_ok(step[e]);
+    inv[e] = fast[e] ? __builtin_amdgcn_rcpf(step[e]) : 0.f;
+  }
   const int64_t row_bytes = static_cast<int64_t>(octets) * BITS;
   for (int i = 0; i < cnt; ++i) {
     load8<T>(src + static_cast<int64_t>(i) * d, v);
     uint32_t packed = 0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint32_t c = 0;
-      if (step[e] > 0.0f) {
-        const float t = (v[e] - zp[e]) / step[e];  // IEEE division
-        c = static_cast<uint32_t>(fminf(fmaxf(rintf(t), 0.0f), static_cast<float>(TOP)));
-      }
-      packed |= c << (e * BITS);
-    }
+    for (int e = 0; e < 8; ++e)
+      if (step[e] > 0.0f) packed |= code_of<TOP>(v[e], zp[e], step[e], inv[e], fast[e]) << (e * BITS);
     const int64_t orow = layout.row(cap, H, b, h, off + t0 + i);
     uint8_t *dst = codes + orow * row_bytes + static_cast<int64_t>(oc) * BITS;
     if (BITS == 2)

@@ -137,7 +137,7 @@ typedef struct {
  *
  *   x    : [B][H][N][d], bf16 (xdt = KV_BF16) or fp32 (KV_F32), device.
  *   dst  : host pointer to the descriptor of the destination cache.
- * d must be 64 or 128.  N = 0 is a no-op.  Output is bit-exact with the
+ * d must be 64 or 128; B and H at most 65535.  N = 0 is a no-op.  Output is bit-exact with the
  * definition above (IEEE fp32 division, round half to even).
  * KV_AXIS_TOKENS: tok_offset must be a multiple of group; the tokens of the
  * call form groups [tok_offset + j*group, +group), the last one shorter when

@@ -80,3 +80,46 @@ def test_quantize_fp32_tiny_workload(orc):
         ref = orc.quantize(data[name], 2, w.group)
         for g, r in zip(got, ref):
             assert _bits_equal(g, r)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("meta", ["f32", "f16"])
+def test_quantize_near_ties(orc, bits, meta):
+    """Values whose quotient (x - z) / D lies 0..80 ulps from a half-integer,
+    across the band where the kernel turns from a reciprocal product to the
+    IEEE division: codes bit-exact against the oracle's division."""
+    import _gpu
+    from bit_kv_cache_03_amd import kvq
+    rng = np.random.default_rng(bits * 10 + (meta == "f16"))
+    top = (1 << bits) - 1
+    d, group, n = 128, 64, 512
+    x = np.empty((n, d), np.float32)
+    for r in range(n):
+        for g in range(d // group):
+            mn = np.float32(rng.standard_normal() * 10 ** rng.uniform(-3, 3))
+            rng_ = np.float32(abs(rng.standard_normal()) * 10 ** rng.uniform(-3, 3) + 1e-30)
+            mx = np.float32(mn + rng_)
+            step = np.float32((mx - mn) / np.float32(top))
+            k = rng.integers(0, top, size=group).astype(np.float32)
+            vals = np.float32(mn) + (k + np.float32(0.5)) * step
+            # move each value 0..80 ulps up or down from the tie: across the
+            # band where the kernel switches from the reciprocal to the division
+            steps = rng.integers(0, 81, size=group)
+            up = rng.random(group) < 0.5
+            for i in range(80):
+                move = steps > i
+                vals = np.where(move & up, np.nextafter(vals, np.float32(np.inf)),
+                                np.where(move & ~up, np.nextafter(vals, np.float32(-np.inf)), vals))
+            vals = vals.astype(np.float32)
+            vals[0], vals[1] = mn, mx  # the group's extremes
+            x[r, g * group:(g + 1) * group] = np.clip(vals, mn, mx)
+    x4 = np.ascontiguousarray(x.reshape(1, 1, n, d))
+    c = kvq.QCache(1, 1, n, d, bits, group, meta=meta)
+    kvq.quantize(_gpu.to_dev(x4), c, 0)
+    torch.cuda.synchronize()
+    got = _gpu.cache_to_host(c, n)
+    ref = orc.quantize(x4, bits, group, meta=meta)
+    assert np.array_equal(got[0], ref[0]), "codes"
+    for g_, r_ in zip(got[1:], ref[1:]):
+        g_ = g_.astype(np.float32) if g_.dtype == np.float16 else g_
+        assert np.array_equal(g_.view(np.uint32), r_.view(np.uint32))
