@@ -52,7 +52,8 @@
 // The instances for caches grouped along the tokens are built from this file
 // in a translation unit of their own (attention_tokens.hip defines
 // KVQ_TILE_TOKENS to 1): the head-dimension instances compile exactly as
-// without them, and the token instances get their own register budget.
+// without them.  At d = 128 the token instances spill ~30 registers at two
+// workgroups per CU and still run faster than at one.
 #include <math.h>
 
 #include "kvq_internal.h"
@@ -132,7 +133,7 @@ __device__ inline float code_f(uint32_t w, int j) {
 // TOK: the caches may group along the tokens (p.ktok / p.vtok); false
 // compiles those paths out.
 template <int D, int KBITS, int VBITS, bool EXACT, bool SPLIT, bool TOK>
-__global__ __launch_bounds__(kThreads, EXACT || TOK ? 1 : 2) void attn_tile_kernel(AttnLaunch p, int32_t group_shift,
+__global__ __launch_bounds__(kThreads, EXACT ? 1 : 2) void attn_tile_kernel(AttnLaunch p, int32_t group_shift,
                                                                  int64_t rows_per_kvhead, int64_t split_keys) {
   constexpr int KS = Tile<D>::kStride;
   constexpr int VS = Tile<D>::vStride;
