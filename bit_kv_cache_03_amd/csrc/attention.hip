@@ -52,8 +52,10 @@
 // The instances for caches grouped along the tokens are built from this file
 // in a translation unit of their own (attention_tokens.hip defines
 // KVQ_TILE_TOKENS to 1): the head-dimension instances compile exactly as
-// without them.  At d = 128 the token instances spill ~30 registers at two
-// workgroups per CU and still run faster than at one.
+// without them.  Every instance is built for two workgroups per CU: at
+// d = 128 the token instances then spill ~30 registers and still run faster
+// than at one; the exact-form instances at d = 128 need 88 KB of LDS, so
+// one workgroup per CU is all that fits there anyway.
 #include <math.h>
 
 #include "kvq_internal.h"
@@ -133,7 +135,7 @@ __device__ inline float code_f(uint32_t w, int j) {
 // TOK: the caches may group along the tokens (p.ktok / p.vtok); false
 // compiles those paths out.
 template <int D, int KBITS, int VBITS, bool EXACT, bool SPLIT, bool TOK>
-__global__ __launch_bounds__(kThreads, EXACT ? 1 : 2) void attn_tile_kernel(AttnLaunch p, int32_t group_shift,
+__global__ __launch_bounds__(kThreads, 2) void attn_tile_kernel(AttnLaunch p, int32_t group_shift,
                                                                  int64_t rows_per_kvhead, int64_t split_keys) {
   constexpr int KS = Tile<D>::kStride;
   constexpr int VS = Tile<D>::vStride;
