@@ -91,6 +91,27 @@ int main(void) {
             assert getattr(S, f).offset == int(val), key
 
 
+def test_enum_values_match_header(kvq, tmp_path):
+    """Every enum the binding mirrors has the header's values."""
+    prog = tmp_path / "enums.c"
+    names = ["KV_OK", "KV_ERR_NULL", "KV_ERR_SHAPE", "KV_ERR_UNSUPPORTED", "KV_ERR_WORKSPACE", "KV_ERR_ALIGN",
+             "KV_ERR_ALIAS", "KV_ERR_HIP", "KV_BF16", "KV_F32", "KV_CORR_OFF", "KV_CORR_TAYLOR", "KV_CORR_EXACT",
+             "KV_PATH_AUTO", "KV_PATH_LONG", "KV_PATH_SHORT", "KV_META_F32", "KV_META_F16", "KV_AXIS_DIM",
+             "KV_AXIS_TOKENS"]
+    prog.write_text('#include <stdio.h>\n#include "kvq.h"\nint main(void) {\n' +
+                    "".join(f'  printf("{n} %d\\n", (int){n});\n' for n in names) + "  return 0;\n}\n")
+    exe = tmp_path / "enums"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(prog), "-o", str(exe)], check=True)
+    got = dict(l.split(" ") for l in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                       check=True).stdout.split("\n") if l)
+    want = {n: getattr(kvq, n) for n in names[:10]}
+    want.update({f"KV_CORR_{k.upper()}": v for k, v in kvq.CORR.items()})
+    want.update({f"KV_PATH_{k.upper()}": v for k, v in kvq.PATH.items()})
+    want.update({f"KV_META_{k.upper()}": v for k, v in kvq.META.items()})
+    want.update({"KV_AXIS_DIM": kvq.AXIS["dim"], "KV_AXIS_TOKENS": kvq.AXIS["tokens"]})
+    assert {k: int(v) for k, v in got.items()} == want
+
+
 # ---------------------------------------------------------------------------
 # validation (fake, aligned device addresses: nothing is dereferenced)
 # ---------------------------------------------------------------------------
