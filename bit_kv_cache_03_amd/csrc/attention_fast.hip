@@ -118,10 +118,11 @@ __device__ inline int vt_index(int row, int col) {
 // Dequantised cached keys lie between z and z + (2^bits - 1) D of their
 // group (the two ends of the code range), so their bound needs only the
 // step and zero arrays; current keys and the queries (the gq query heads of
-// the KV head) are scanned directly.  Each KV head's rows are split over
-// KCHUNKS workgroups, each writing the largest |key| and |query| of its
-// share (part[(2 bkv + 0|1) KCHUNKS + chunk]); the attention kernel reduces
-// the partial bounds.
+// the KV head) are scanned directly, and values the same way as keys.  Each
+// KV head's rows are split over KCHUNKS workgroups, each writing the
+// largest |key|, |query| and |value| of its share
+// (part[(3 bkv + 0|1|2) KCHUNKS + chunk]); the attention kernel reduces the
+// partial bounds.
 constexpr int KCHUNKS = 32;
 
 __device__ inline float bf16_bound(const uint16_t *x, int64_t lo, int64_t hi, int tid) {  // 8-value chunks
@@ -143,36 +144,45 @@ __device__ inline float block_max(float b, float *red, int tid) {
   return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
+// Largest |z|, |z + top D| over this chunk's share of a cache tensor's groups.
+template <bool M16>
+__device__ inline float cache_bound(const AttnLaunch &p, const float *scale, const float *zero, float top,
+                                    int32_t ng, int64_t bkv, int64_t ch, int tid) {
+  float bd = 0.f;
+  const int64_t n = p.Nc * ng, lo = n * ch / KCHUNKS, hi = n * (ch + 1) / KCHUNKS;
+  if (p.layout.page_table) {  // element i = (token i / ng, group i % ng) through the page table
+    const int64_t b = bkv / p.Hkv, hk = bkv - b * p.Hkv;
+    for (int64_t i = lo + tid; i < hi; i += 256) {
+      const int64_t e = p.layout.row(p.cap, p.Hkv, b, hk, i / ng) * ng + i % ng;
+      const float zi = meta_ld<M16>(zero, e);
+      bd = fmaxf(bd, fmaxf(fabsf(zi), fabsf(fmaf(meta_ld<M16>(scale, e), top, zi))));
+    }
+  } else {
+    const float *s = meta_adv<M16>(scale, bkv * p.cap * ng);
+    const float *z = meta_adv<M16>(zero, bkv * p.cap * ng);
+    for (int64_t i = lo + tid; i < hi; i += 256) {
+      const float zi = meta_ld<M16>(z, i);
+      bd = fmaxf(bd, fmaxf(fabsf(zi), fabsf(fmaf(meta_ld<M16>(s, i), top, zi))));
+    }
+  }
+  return bd;
+}
+
 template <int KBITS, bool M16>
 __global__ __launch_bounds__(256) void key_scale_kernel(AttnLaunch p, int32_t ng, float *part) {
   __shared__ float red[4];
   const int64_t bkv = blockIdx.x / KCHUNKS;
   const int64_t ch = blockIdx.x % KCHUNKS;
   const int tid = threadIdx.x;
-  float kb = 0.f;
+  float kb = 0.f, vb = 0.f;
   if (p.Nc > 0) {
-    const int64_t n = p.Nc * ng, lo = n * ch / KCHUNKS, hi = n * (ch + 1) / KCHUNKS;
-    if (p.layout.page_table) {  // element i = (token i / ng, group i % ng) through the page table
-      const int64_t b = bkv / p.Hkv, hk = bkv - b * p.Hkv;
-      for (int64_t i = lo + tid; i < hi; i += 256) {
-        const int64_t e = p.layout.row(p.cap, p.Hkv, b, hk, i / ng) * ng + i % ng;
-        const float zi = meta_ld<M16>(p.kc_zero, e);
-        kb = fmaxf(kb, fmaxf(fabsf(zi), fabsf(fmaf(meta_ld<M16>(p.kc_scale, e),
-                                                   static_cast<float>((1 << KBITS) - 1), zi))));
-      }
-    } else {
-      const float *s = meta_adv<M16>(p.kc_scale, bkv * p.cap * ng);
-      const float *z = meta_adv<M16>(p.kc_zero, bkv * p.cap * ng);
-      for (int64_t i = lo + tid; i < hi; i += 256) {
-        const float zi = meta_ld<M16>(z, i);
-        kb = fmaxf(kb, fmaxf(fabsf(zi), fabsf(fmaf(meta_ld<M16>(s, i),
-                                                   static_cast<float>((1 << KBITS) - 1), zi))));
-      }
-    }
+    kb = cache_bound<M16>(p, p.kc_scale, p.kc_zero, static_cast<float>((1 << KBITS) - 1), ng, bkv, ch, tid);
+    vb = cache_bound<M16>(p, p.vc_scale, p.vc_zero, static_cast<float>((1 << p.vbits) - 1), ng, bkv, ch, tid);
   }
   if (p.Ncur > 0) {
     const int64_t n = p.Ncur * D / 8, lo = n * ch / KCHUNKS, hi = n * (ch + 1) / KCHUNKS;
     kb = fmaxf(kb, bf16_bound(p.k_cur + bkv * p.Ncur * D, lo, hi, tid));
+    vb = fmaxf(vb, bf16_bound(p.v_cur + bkv * p.Ncur * D, lo, hi, tid));
   }
   float qb;
   {
@@ -182,9 +192,11 @@ __global__ __launch_bounds__(256) void key_scale_kernel(AttnLaunch p, int32_t ng
   }
   kb = block_max(kb, red, tid);
   qb = block_max(qb, red, tid);
+  vb = block_max(vb, red, tid);
   if (tid == 0) {
-    part[2 * bkv * KCHUNKS + ch] = kb;
-    part[(2 * bkv + 1) * KCHUNKS + ch] = qb;
+    part[3 * bkv * KCHUNKS + ch] = kb;
+    part[(3 * bkv + 1) * KCHUNKS + ch] = qb;
+    part[(3 * bkv + 2) * KCHUNKS + ch] = vb;
   }
 }
 
@@ -256,6 +268,7 @@ struct Ctx {
   int beg, end;     // key range of the segment
   int climit;       // causal mask: current keys below climit are visible to the lane's row
   float kscale;     // tau log2(e) 2^-ek
+  float vscale;     // 2^-ev: values enter the PV product as fp16 v 2^-ev
   uint32_t kmask;   // code mask of magic8, in a vector register
   CacheLayout layout;         // paged caches: pointers at the pools, rows of (b, hk)
   int64_t cap, H, b, hk;
@@ -398,12 +411,15 @@ __device__ inline void unpack_k_item(int p, const Ctx &c, int tid, const Fetch &
 // V^T tile: the thread's 2 keys 2kq, 2kq+1 sit in adjacent permuted slots
 // (key r of a 16-key step sits at slot (r&3) + 4*(r>>3) + 8*((r>>2)&1)), so
 // each of its 8 head-dim rows gets one 4-byte store.  Item 0 splits the
-// codes of both keys into bytes (cached); items 1..4 dequantise and store
-// rows 2(p-1), 2(p-1)+1.
+// codes of both keys into bytes and scales their steps and zero points
+// (cached); items 1..4 dequantise and store rows 2(p-1), 2(p-1)+1.  Values
+// are stored as fp16 v 2^-ev (ev: the KV head's value exponent, so that
+// |v| 2^-ev < 2^15), rounded once from an fp32 fma.
 constexpr int kItemsV = 5;
 
 struct VWork {
   uint32_t c[2][2];  // per key: bytes holding codes (INT4: even / odd codes; INT2: codes j, j+4 pairs)
+  float s[2], z[2];  // per key: step and zero point times 2^-ev
 };
 
 // Code e (0..7) of a key from its VWork bytes.
@@ -419,10 +435,15 @@ __device__ inline float vcode(const uint32_t (&c)[2], int e) {
 }
 
 template <bool CACHED, int VBITS>
-__device__ inline void unpack_v_item(int p, int tid, const Fetch &f, uint16_t *Vb, VWork &u) {
+__device__ inline void unpack_v_item(int p, int tid, const Fetch &f, uint16_t *Vb, VWork &u, float vscale) {
   const int dq = tid & 15, kq = tid >> 4;
   if (p == 0) {
     if (CACHED) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        u.s[k] = f.vstep[k] * vscale;
+        u.z[k] = f.vzero[k] * vscale;
+      }
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const uint32_t w = f.vw[k];
@@ -443,11 +464,11 @@ __device__ inline void unpack_v_item(int p, int tid, const Fetch &f, uint16_t *V
       const int e = 2 * (p - 1) + i;
       uint32_t w;
       if (CACHED) {
-        w = pack2(fmaf(f.vstep[0], vcode<VBITS>(u.c[0], e), f.vzero[0]),
-                  fmaf(f.vstep[1], vcode<VBITS>(u.c[1], e), f.vzero[1]));
+        w = pack2h(fmaf(u.s[0], vcode<VBITS>(u.c[0], e), u.z[0]), fmaf(u.s[1], vcode<VBITS>(u.c[1], e), u.z[1]));
       } else {
-        // bf16 element e of key 0 (low half) and key 1 (high half)
-        w = __builtin_amdgcn_perm(f.vw[4 + (e >> 1)], f.vw[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+        // bf16 element e of key 0 (words 0..3) and key 1 (words 4..7), scaled (exact) and rounded to fp16
+        const uint32_t w0 = f.vw[e >> 1], w1 = f.vw[4 + (e >> 1)];
+        w = (e & 1) ? pack2h(hi_f(w0) * vscale, hi_f(w1) * vscale) : pack2h(lo_f(w0) * vscale, lo_f(w1) * vscale);
       }
       *reinterpret_cast<uint32_t *>(Vb + vt_index(8 * dq + e, slot)) = w;
     }
@@ -457,11 +478,12 @@ __device__ inline void unpack_v_item(int p, int tid, const Fetch &f, uint16_t *V
 // p = exp2(s) for scores 2k, 2k+1 of the block (k = 0..15): the running max
 // is already subtracted by the score MFMAs (SHIFT subtracts a further
 // `shift`, in the rare redo of fix_growth); every fourth item packs 8 of
-// them into a bf16 P operand and adds the rounded p to the row sum.  MASK
+// them into an fp16 P operand and adds the rounded p to the row sum (a p
+// above the fp16 range becomes inf, and fix_growth redoes the tile).  MASK
 // zeroes keys at or past `count`.
 template <bool MASK, bool SHIFT = false>
 __device__ inline void exp_item(int k, const f32x16 (&acc)[2], Soft &st, int count, int h, float (&e)[8],
-                                bf16x8 (&pk)[4], float shift = 0.f) {
+                                f16x8 (&pk)[4], float shift = 0.f) {
   const int kb = k >> 3;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -473,9 +495,9 @@ __device__ inline void exp_item(int k, const f32x16 (&acc)[2], Soft &st, int cou
   pin(e[(2 * k) & 7]);
   pin(e[(2 * k + 1) & 7]);
   if ((k & 3) == 3) {
-    pk[k >> 2] = __builtin_bit_cast(bf16x8, make_uint4(pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]),
-                                                       pack2(e[6], e[7])));
-    st.l = sum8(pk[k >> 2], st.l);
+    pk[k >> 2] = __builtin_bit_cast(f16x8, make_uint4(pack2h(e[0], e[1]), pack2h(e[2], e[3]), pack2h(e[4], e[5]),
+                                                      pack2h(e[6], e[7])));
+    st.l = sum8h(pk[k >> 2], st.l);
     pin(pk[k >> 2]);
     pin(st.l);
   }
@@ -503,12 +525,15 @@ __device__ inline float set_max_slots(QState &qs, float m, int h) {
 // row's scores so far 60 below it (the first tile after m = 0 can be one).
 // A row with an empty sum and no visible key in the tile (causal mask) is
 // left alone.
-constexpr float kGrowth = 1099511627776.0f;        // 2^40
-constexpr float kShrink = 8.673617379884035e-19f;  // 2^-60
+// (With fp16 probabilities a p above 65504 rounds to inf, which fails the
+// growth test; the shrink bound keeps a row's largest p away from the fp16
+// subnormals.)
+constexpr float kGrowth = 1099511627776.0f;  // 2^40
+constexpr float kShrink = 0.0009765625f;     // 2^-10
 
 template <bool MASK, bool QK>
 __device__ inline void fix_growth(const f32x16 (&s)[2], f32x16 (&sn)[2], QState &qs, Soft &st, float l0, int count,
-                                  int h, bf16x8 (&pk)[4]) {
+                                  int h, f16x8 (&pk)[4]) {
   const float lt = st.l + __shfl_xor(st.l, 32, 64);
   const bool need = !(lt < kGrowth && (lt > kShrink || (MASK && lt == 0.f && count <= 0)));
   if (!__any(need)) return;
@@ -570,7 +595,7 @@ __device__ inline void tile_step(const Ctx &c, QState &qs, Soft &st, Fetch &f, c
   constexpr int NK = kItemsK;
   uint4 buf[4];
   float ev[8];
-  bf16x8 pk[4];
+  f16x8 pk[4];
 
   // 1. S_t - m (fp16 keys, bf16 correction and max step), with the
   //    exponentials of t-1
@@ -608,13 +633,13 @@ __device__ inline void tile_step(const Ctx &c, QState &qs, Soft &st, Fetch &f, c
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       if (PREV) {
-        st.o[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, buf[j & 3]), pk[j >> 2],
-                                                              st.o[j & 3], 0, 0, 0);
+        st.o[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, buf[j & 3]), pk[j >> 2],
+                                                             st.o[j & 3], 0, 0, 0);
         if (j + 4 < 16) buf[j & 3] = lds16(Vb + pv_off(j + 4));
       }
       if (NEXT) {
         if (j < NK) unpack_k_item<CACHED, TAYLOR, KBITS>(j, c, tid, f, Kn);
-        else if (j >= 4 && j - 4 < kItemsV) unpack_v_item<CACHED, VBITS>(j - 4, tid, f, Vn, u);
+        else if (j >= 4 && j - 4 < kItemsV) unpack_v_item<CACHED, VBITS>(j - 4, tid, f, Vn, u, c.vscale);
         else if (j == 9) fetch_k<CACHED, KBITS, PAGED>(c, k0_next2, tid, f, prn);
         else if (j == 10 || j == 11) fetch_v<CACHED, VBITS, PAGED>(c, k0_next2, tid, j - 10, f, prn);
       }
@@ -648,7 +673,7 @@ __device__ inline void segment(const Ctx &c, QState &qs, Soft &st, uint16_t *Kl,
 #pragma unroll
     for (int p = 0; p < kItemsK; ++p) unpack_k_item<CACHED, TAYLOR, KBITS>(p, c, tid, f, Kl);
 #pragma unroll
-    for (int p = 0; p < kItemsV; ++p) unpack_v_item<CACHED, VBITS>(p, tid, f, Vl, u);
+    for (int p = 0; p < kItemsV; ++p) unpack_v_item<CACHED, VBITS>(p, tid, f, Vl, u, c.vscale);
     const size_t pr1 = CACHED && PAGED ? tile_pool_row(c, tile_start(c, c.beg + BN)) : 0;
     fetch_k<CACHED, KBITS, PAGED>(c, c.beg + BN, tid, f, pr1);
     fetch_v<CACHED, VBITS, PAGED>(c, c.beg + BN, tid, 0, f, pr1);
@@ -759,13 +784,17 @@ __global__ __launch_bounds__(THREADS, 1) void attn_fast_kernel(AttnLaunch p, int
   // exponent ek of the KV head from the pre-pass's partial bounds: keys
   // k tau log2(e) 2^-ek and queries q 2^ek near the same magnitude, keys
   // always below 2^15
-  float kb = lane < KCHUNKS ? kpart[2 * bkv * KCHUNKS + lane] : 0.f;
-  float qb = lane < KCHUNKS ? kpart[(2 * bkv + 1) * KCHUNKS + lane] : 0.f;
+  float kb = lane < KCHUNKS ? kpart[3 * bkv * KCHUNKS + lane] : 0.f;
+  float qb = lane < KCHUNKS ? kpart[(3 * bkv + 1) * KCHUNKS + lane] : 0.f;
+  float vb = lane < KCHUNKS ? kpart[(3 * bkv + 2) * KCHUNKS + lane] : 0.f;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     kb = fmaxf(kb, __shfl_xor(kb, o, 64));
     qb = fmaxf(qb, __shfl_xor(qb, o, 64));
+    vb = fmaxf(vb, __shfl_xor(vb, o, 64));
   }
+  // values enter the PV product as fp16 v 2^-ev, |v| 2^-ev below 2^15
+  const int ev = vb > 0.f ? ilogbf(vb) - 14 : 0;
   const float kt = kb * (p.tau * kLog2e);
   int ek = 0;
   if (kt > 0.f) {
@@ -791,6 +820,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_fast_kernel(AttnLaunch p, int
   c.ng = ng;
   c.group_shift = group_shift;
   c.kscale = ldexpf(p.tau * kLog2e, -ek);
+  c.vscale = ldexpf(1.0f, -ev);
   c.kmask = opaque_u32(kCodeMask<KBITS>);
   c.layout = p.layout;
   c.cap = p.cap;
@@ -831,6 +861,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_fast_kernel(AttnLaunch p, int
 
   const float l_tot = st.l + __shfl_xor(st.l, 32, 64);
   if (!row_ok) return;
+  const float vs = ldexpf(1.0f, ev);  // O accumulated values v 2^-ev
   if (ns > 1) {  // partial: O (unnormalised), then (m, l); [split][qrow][kPartialStride(D)]
     float *w = partials + (split * (p.B * p.Hq * p.Nq) + qrow) * kPartialStride(D);
 #pragma unroll
@@ -838,14 +869,15 @@ __global__ __launch_bounds__(THREADS, 1) void attn_fast_kernel(AttnLaunch p, int
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4)
         *reinterpret_cast<float4 *>(w + 32 * db + 8 * g4 + 4 * h) =
-            make_float4(st.o[db][4 * g4], st.o[db][4 * g4 + 1], st.o[db][4 * g4 + 2], st.o[db][4 * g4 + 3]);
+            make_float4(st.o[db][4 * g4] * vs, st.o[db][4 * g4 + 1] * vs, st.o[db][4 * g4 + 2] * vs,
+                        st.o[db][4 * g4 + 3] * vs);
     if (h == 0) {
       w[D] = l_tot > 0.f ? st.m : -INFINITY;  // -inf: no key of this split is visible to the row
       w[D + 1] = l_tot;
     }
     return;
   }
-  const float inv = 1.0f / l_tot;
+  const float inv = vs / l_tot;
   uint16_t *optr = p.out + qrow * D;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -939,7 +971,9 @@ hipError_t launch_attention_fast_causal(const AttnLaunch &p, hipStream_t stream)
   return launch_bits<4, 4>(p, stream);
 }
 #else
-bool fast_path_supported(const AttnLaunch &p) { return p.d == D && p.corr != KV_CORR_EXACT && !p.ktok && !p.vtok; }
+bool fast_path_supported(const AttnLaunch &p) {
+  return fast_kernel_ok(p.d, p.corr, p.ktok || p.vtok, layout_page_size(p.layout));
+}
 
 void launch_key_scale(const AttnLaunch &p, hipStream_t stream, float *part) {
   const int32_t ng = D / p.group;
@@ -952,7 +986,7 @@ void launch_key_scale(const AttnLaunch &p, hipStream_t stream, float *part) {
 
 size_t fast_path_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int splits) {
   const size_t part = splits > 1 ? short_path_workspace_bytes(B, Hq, Nq, D, splits) : 0;
-  return part + (static_cast<size_t>(B * Hkv) * 2 * KCHUNKS * sizeof(float) + 255) / 256 * 256;
+  return part + (static_cast<size_t>(B * Hkv) * 3 * KCHUNKS * sizeof(float) + 255) / 256 * 256;
 }
 
 // Key-range split of the throughput kernel.  With at least one full round

@@ -732,8 +732,10 @@ hipError_t launch_attention_short_fast_m16(const AttnLaunch &p, hipStream_t stre
   return launch_bits<4, 4>(p, stream);
 }
 #else
-bool short_fast_supported(int32_t d, int corr, bool tokens_axis) {
-  return d == D && corr != KV_CORR_EXACT && !tokens_axis;
+// d = 128, correction off or Taylor, groups along the head dimension, and
+// (paged) pages that hold whole 32-key blocks.
+bool short_fast_supported(int32_t d, int corr, bool tokens_axis, int32_t page_size) {
+  return d == D && corr != KV_CORR_EXACT && !tokens_axis && (page_size == 0 || page_size >= BK);
 }
 
 int short_fast_splits(int64_t B, int64_t Hkv, int64_t rows_per_kvhead, int64_t Nc, int64_t Ncur, int cu_count) {

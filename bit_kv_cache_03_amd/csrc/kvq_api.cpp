@@ -17,9 +17,11 @@ constexpr int64_t kMaxTokensPerHead = int64_t(1) << 23;  // 8M tokens: 32-bit in
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Page sizes of the paged layout: powers of two from 64 tokens (every 64-key
-// tile in one page; shifts and masks in the kernels).
-bool page_size_ok(int32_t ps) { return ps >= 64 && ps <= (1 << 23) && (ps & (ps - 1)) == 0; }
+// Page sizes of the paged layout: powers of two from 16 tokens (shifts and
+// masks in the kernels).  The throughput kernel needs pages of at least 64
+// tokens (whole tiles) and the short-query kernel of at least 32 (whole
+// blocks); smaller pages run on the general kernel, which looks every row up.
+bool page_size_ok(int32_t ps) { return ps >= 16 && ps <= (1 << 23) && (ps & (ps - 1)) == 0; }
 
 bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
 
@@ -95,6 +97,11 @@ size_t meta_array_bytes(const kv_qtensor *t, size_t rows, int32_t d) {
   const size_t elems = t->axis == KV_AXIS_TOKENS ? rows / static_cast<size_t>(t->group) * static_cast<size_t>(d)
                                                  : rows * static_cast<size_t>(d / t->group);
   return elems * meta_bytes(t);
+}
+
+// Page size of a call's caches (0: contiguous or no cache).
+int32_t cache_page_size(const kv_attn_args *a) {
+  return a->Nc > 0 && a->k_cache->page_table ? a->k_cache->page_size : 0;
 }
 
 // Either cache of a call groups along the tokens (general kernel only).
@@ -233,14 +240,14 @@ Plan plan_attention(const kv_attn_args *a, bool query_device) {
   pl.path = path;
   if (path == KV_PATH_SHORT) {
     const int cus = query_device ? device_cu_count() : 256;
-    if (kvq::short_fast_supported(a->d, a->corr, tokens_axis(a))) {
+    if (kvq::short_fast_supported(a->d, a->corr, tokens_axis(a), cache_page_size(a))) {
       pl.splits = a->splits > 0 ? a->splits : kvq::short_fast_splits(a->B, a->Hkv, rows, a->Nc, a->Ncur, cus);
       pl.workspace = kvq::short_path_workspace_bytes(a->B, a->Hq, a->Nq, a->d, pl.splits);
     } else {
       pl.splits = a->splits > 0 ? a->splits : kvq::short_path_splits(a->B, a->Hkv, rows, a->Nc, cus);
       pl.workspace = kvq::short_path_workspace_bytes(a->B, a->Hq, a->Nq, a->d, pl.splits);
     }
-  } else if (a->d == 128 && a->corr != KV_CORR_EXACT && !tokens_axis(a)) {  // the throughput kernel, split-K when it balances
+  } else if (kvq::fast_kernel_ok(a->d, a->corr, tokens_axis(a), cache_page_size(a))) {  // split-K when it balances
     const int cus = query_device ? device_cu_count() : 256;
     const kvq::FastPlan fp = kvq::fast_path_plan(a->B, a->Hq, a->Hkv, a->Nq, a->Nc, a->Ncur, cus, a->splits);
     pl.splits = fp.splits;

@@ -85,6 +85,14 @@ hipError_t launch_attention_short(const AttnLaunch &p, hipStream_t stream);
 // as on the short path), then 32 fp32 partial key bounds and 32 partial
 // query bounds per (b, KV head).
 bool fast_path_supported(const AttnLaunch &p);
+// The throughput kernel: d = 128, correction off or Taylor, groups along the
+// head dimension, and (paged) pages that hold whole 64-key tiles.  The
+// host's plan and the device dispatch both decide with this.
+inline bool fast_kernel_ok(int32_t d, int corr, bool tokens_axis, int32_t page_size) {
+  return d == 128 && corr != KV_CORR_EXACT && !tokens_axis && (page_size == 0 || page_size >= 64);
+}
+// Page size of a launch's layout (0: contiguous).
+inline int32_t layout_page_size(const CacheLayout &l) { return l.page_table ? (1 << l.page_shift) : 0; }
 size_t fast_path_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int splits);
 int fast_path_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nc, int64_t Ncur, int cu_count);
 struct FastPlan {
@@ -119,7 +127,7 @@ size_t short_path_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int32_t d, 
 hipError_t launch_combine(const float *ws, uint16_t *out, int64_t nrows, int splits, int32_t d, hipStream_t stream);
 // Short-query kernel (attention_short.hip): head dim 128, correction off or
 // Taylor; workspace = the split partials.
-bool short_fast_supported(int32_t d, int corr, bool tokens_axis);
+bool short_fast_supported(int32_t d, int corr, bool tokens_axis, int32_t page_size);
 int short_fast_splits(int64_t B, int64_t Hkv, int64_t rows_per_kvhead, int64_t Nc, int64_t Ncur, int cu_count);
 hipError_t launch_attention_short_fast(const AttnLaunch &p, hipStream_t stream);
 // The same over a paged cache, with binary16 metadata, and both (built in

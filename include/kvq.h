@@ -120,8 +120,9 @@ typedef struct {
    * *page_size + t % page_size.  page_table is a DEVICE int32 array
    * [B][cap/page_size] whose entries must lie in [0, num_pages) (not
    * checked: device data); pages of different blocks may not coincide where
-   * a call writes.  page_size is a power of two, at least 64, and divides
-   * cap.  NULL, with page_size and num_pages 0: the contiguous layout above. */
+   * a call writes.  page_size is a power of two, at least 16, and divides
+   * cap.  Attention over pages of fewer than 64 tokens (32 on the short-query
+   * path) runs on the general kernel, which looks up every row.  NULL, with page_size and num_pages 0: the contiguous layout above. */
   const int32_t *page_table;
   int32_t page_size;
   int32_t num_pages;
@@ -191,9 +192,9 @@ typedef struct {
 /* Bytes of device workspace the call needs: on the short path the
  * per-split partial results (splits x B*Hq*Nq rows of d+4 floats); on the
  * long path with d = 128 and correction off or Taylor, the same partials
- * when it splits the key range (more than one split), then 64 fp32 partial
- * key and query bounds per (b, KV head) rounded up to 256 bytes; otherwise
- * 0.  The
+ * when it splits the key range (more than one split), then 96 fp32 partial
+ * key, value and query bounds per (b, KV head) rounded up to 256 bytes;
+ * otherwise 0.  The
  * contents need no initialisation and are meaningless after the call.
  * Returns 0 for invalid arguments as well; kv_attention_corrected reports
  * those. */

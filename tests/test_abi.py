@@ -198,15 +198,16 @@ def test_short_path_needs_workspace(kvq):
 
 
 def test_long_path_workspace(kvq):
-    """The head-dim-128 long path keeps 32 fp32 partial key bounds and 32
-    partial query bounds per (batch, KV head), rounded up to 256 bytes; the
-    general kernel (head dim 64, or the exact correction) needs none."""
+    """The head-dim-128 long path keeps 32 fp32 partial key bounds, 32
+    partial value bounds and 32 partial query bounds per (batch, KV head),
+    rounded up to 256 bytes; the general kernel (head dim 64, or the exact
+    correction) needs none."""
     size = lambda **kw: kvq.lib.kv_attention_workspace_size(C.byref(_args(kvq, path=1, **kw)))
-    assert size() == 512                            # 2 heads x 64 x 4 B
-    assert size(B=3, Hq=80, Hkv=40) == 30720        # 120 heads x 256 B
-    assert size(B=1, Hq=3, Hkv=3) == 768            # 3 heads x 256 B
+    assert size() == 768                            # 2 heads x 96 x 4 B
+    assert size(B=3, Hq=80, Hkv=40) == 46080        # 120 heads x 384 B
+    assert size(B=1, Hq=3, Hkv=3) == 1280           # 3 heads x 384 B = 1152, rounded up
     # forced key-range splits (2 tiles here): partials of 2 splits first
-    assert size(splits=2) == 2 * 1 * 4 * 8 * (128 + 4) * 4 + 512
+    assert size(splits=2) == 2 * 1 * 4 * 8 * (128 + 4) * 4 + 768
     assert size(splits=5) == size(splits=2)         # clamped to the 2 tiles
     assert size(corr=2) == 0
     assert size(d=64) == 0
@@ -300,7 +301,10 @@ def _paged(kvq, base, table=0x7000000, page_size=128, num_pages=4, cap=256, bits
     ("ok", dict(), "KV_OK"),
     ("page_size_not_64x", dict(page_size=96), "KV_ERR_SHAPE"),
     ("page_size_not_pow2", dict(page_size=192, cap=384), "KV_ERR_SHAPE"),
-    ("page_size_small", dict(page_size=32, cap=256), "KV_ERR_SHAPE"),
+    ("page_size_16", dict(page_size=16, cap=256), "KV_OK"),
+    ("page_size_32", dict(page_size=32, cap=256), "KV_OK"),
+    ("page_size_small", dict(page_size=8, cap=256), "KV_ERR_SHAPE"),
+    ("page_size_48", dict(page_size=48, cap=240), "KV_ERR_SHAPE"),
     ("cap_not_pages", dict(page_size=128, cap=320), "KV_ERR_SHAPE"),
     ("no_pages", dict(num_pages=0), "KV_ERR_SHAPE"),
     ("table_align", dict(table=0x7000002), "KV_ERR_ALIGN"),

@@ -223,7 +223,7 @@ def test_long_path_tail_split(orc):
     args = kvq.make_args(q, _gpu.as_bf16_dev(data["k"]), _gpu.as_bf16_dev(data["v"]), kc, vc, w.Nc,
                          torch.empty_like(q), corr="taylor")
     partials = 5 * w.B * w.Hq * w.Nq * (w.d + 4) * 4
-    assert kvq.workspace_size(args) == partials + 300 * 256  # 5 key ranges; bounds of 300 KV heads
+    assert kvq.workspace_size(args) == partials + 300 * 384  # 5 key ranges; bounds of 300 KV heads
     out = _gpu.run_attention(w, data, kc, vc, corr="taylor")
     heads = [0, 1, 128, 255, 256, 257, 280, 299]  # units 256.. are the split tail
     rows = np.array([h * w.Nq + j for h in heads for j in (0, 37, 99)], dtype=np.int64)

@@ -61,3 +61,40 @@ def test_paged_matches_contiguous(case):
         rb = _gpu.run_diagnostics(w, data, pk, corr=corr)
         assert np.array_equal(ra[0], rb[0]) and np.array_equal(ra[1], rb[1]), corr
     print("    all paths identical", flush=True)
+
+
+SMALL_PAGE_CASES = {
+    # name: (workload, page size): pages that do not hold a whole 64-key tile
+    "int4_p16": (W.WORKLOADS["h24_int4_cache16k"].scaled(Hq=2, Hkv=2, Nq=150, Ncur=150, Nc=333), 16),
+    "gqa_p32": (W.WORKLOADS["gqa_prefill_b16_cache32k"].scaled(B=2, Hq=8, Hkv=2, Nq=40, Ncur=40, Nc=500), 32),
+    "gqa_p16": (W.WORKLOADS["gqa_prefill_b16_cache32k"].scaled(B=2, Hq=8, Hkv=2, Nq=3, Ncur=3, Nc=700), 16),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SMALL_PAGE_CASES))
+def test_small_pages(orc, case):
+    """Pages of 16 and 32 tokens: the cache bit-exact in logical order, the
+    attention (general kernel below 64 tokens per page, the short-query
+    kernel from 32) against the oracle on both paths and all modes, and
+    the diagnostics identical to the contiguous layout."""
+    import _gpu
+    from _problems import oracle_problem
+    w, ps = SMALL_PAGE_CASES[case]
+    print(f"[small pages] {case} page_size={ps} B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Nc={w.Nc}", flush=True)
+    data = W.generate(w)
+    cap = (w.Nc + ps - 1) // ps * ps
+    kc = _gpu.build_cache(w, data["kc"], w.kbits, cap=cap)
+    pk = _gpu.paged_cache(w, data["kc"], w.kbits, ps, cap=cap, seed=7)
+    pv = _gpu.paged_cache(w, data["vc"], w.vbits, ps, cap=cap, seed=7)
+    pv.page_table = pk.page_table
+    torch.cuda.synchronize()
+    for a, b in zip(kc.logical(w.Nc), pk.logical(w.Nc)):
+        assert torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
+    for corr in ("off", "taylor", "exact"):
+        ref = oracle_problem(orc, w, corr, data=data).attention()
+        for path in ("long", "short"):
+            got = _gpu.out_rows(_gpu.run_attention(w, data, pk, pv, corr=corr, path=path))
+            _gpu.check(got, ref, label=f"{path} {corr} ")
+    ra = _gpu.run_diagnostics(w, data, kc, corr="taylor")
+    rb = _gpu.run_diagnostics(w, data, pk, corr="taylor")
+    assert np.array_equal(ra[0], rb[0]) and np.array_equal(ra[1], rb[1])

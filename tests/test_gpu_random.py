@@ -41,10 +41,12 @@ def _cases(n=120, seed=20261203):
             path = "auto"
         splits = int(rng.choice([0, 0, 2, 5]))
         paged = bool(rng.random() < 0.3) and nc > 0
+        # pages of 16..128 tokens (token groups need whole groups per page)
+        ps = max(int(rng.choice([16, 32, 64, 128])), group if "tokens" in (axis_k, axis_v) else 16) if paged else 0
         meta = "f16" if rng.random() < 0.3 else "f32"
         w = base.scaled(B=int(rng.choice([1, 2])), Hq=hkv * gq, Hkv=hkv, Nq=nq, Ncur=ncur, Nc=nc, group=group,
                         kbits=int(rng.choice([2, 4])), vbits=int(rng.choice([2, 4])))
-        out.append((i, w, corr, path, splits, causal, paged, meta, axis_k, axis_v))
+        out.append((i, w, corr, path, splits, causal, ps, meta, axis_k, axis_v))
     return out
 
 
@@ -54,19 +56,19 @@ CASES = _cases()
 @pytest.mark.parametrize("case", CASES, ids=[f"r{c[0]}" for c in CASES])
 def test_random_configuration(orc, case):
     import _gpu
-    i, w, corr, path, splits, causal, paged, meta, axis_k, axis_v = case
+    i, w, corr, path, splits, causal, ps, meta, axis_k, axis_v = case
+    paged = ps > 0
     print(f"[random r{i}] {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} d={w.d} Nq={w.Nq} Ncur={w.Ncur} Nc={w.Nc} "
           f"bits={w.kbits}/{w.vbits} group={w.group} corr={corr} path={path} splits={splits} causal={causal} "
-          f"paged={paged} meta={meta} axes={axis_k}/{axis_v}", flush=True)
+          f"page_size={ps} meta={meta} axes={axis_k}/{axis_v}", flush=True)
     data = W.generate(w)
     kc = vc = None
     if w.Nc > 0:
-        mult = 64 if paged else 1
+        mult = 1
         if "tokens" in (axis_k, axis_v):
             mult = max(mult, w.group)
         cap = -(-w.Nc // mult) * mult
         if paged:
-            ps = 64 if w.group <= 64 else 128
             cap = -(-cap // ps) * ps
             kc = _gpu.paged_cache(w, data["kc"], w.kbits, ps, cap=cap, seed=i, meta=meta, axis=axis_k)
             vc = _gpu.paged_cache(w, data["vc"], w.vbits, ps, cap=cap, seed=i, meta=meta, axis=axis_v)
