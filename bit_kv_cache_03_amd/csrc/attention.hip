@@ -8,7 +8,8 @@
 // BN (64) keys.  Per tile:
 //   1. all 256 threads stream the packed INT2/INT4 codes and fp32 step/zero
 //      of the tile from HBM, dequantise x^ = z + D*c in fp32 and write bf16
-//      K (row-major) and V (transposed) tiles to LDS -- the dequantisation is
+//      K (row-major) and fp16 V (transposed, scaled by 2^-ev) tiles to LDS
+//      -- the dequantisation is
 //      fused into the attention kernel and no dequantised cache is ever
 //      written to memory ("量化后画面闪烁？…" (hotelren.com), §4.3: the unfused
 //      version cost +12% end to end, the fused one -3% vs FP16);
@@ -28,8 +29,18 @@
 //   4. one online softmax (running max and sum per query row, exp2 with
 //      log2(e) folded into the scale) spans both segments: cached logits are
 //      corrected, current logits are not;
-//   5. O^T += V^T P^T on bf16 MFMA.
-// Finally O / l is rounded to bf16 and stored.
+//   5. O^T += V^T P^T on fp16 MFMA (p <= 1 and v 2^-e in fp16: 11-bit
+//      significands; bf16 values move the outputs of short, large-step INT2
+//      caches by about the mean tolerance).
+// Finally O 2^ev / l is rounded to bf16 and stored.
+//
+// The value exponent ev is fixed per (b, KV head): a pre-pass
+// (value_bound_kernel) bounds |v| over the head's cached values (per group
+// max(|z|, |z + top D|): the dequantised values lie between the two) and
+// its current-chunk values, and ev = ilogb(bound) - 14 keeps |v| 2^-ev
+// below 2^15, inside the fp16 range.  Values far below the bound become
+// fp16 subnormals; their absolute error stays below 2^-24 of 2^ev, ~2^-39
+// of the largest value.
 //
 // Caches whose groups run along the tokens (per channel: D_{t/G, c}) are
 // dequantised channel by channel; their bias is then the same for every key
@@ -68,12 +79,16 @@ namespace kvq {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBM = 128;      // query rows per workgroup
 constexpr int kBN = 64;       // keys per tile
 constexpr int kThreads = 256;  // 4 waves
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMinVExp = -100;  // smallest value exponent (2^100 fits fp32)
+constexpr int kVChunks = 32;    // value pre-pass: workgroups and partial bounds per (b, KV head)
 
 // A cached key is dequantised in fp32 and kept as a pair of bf16 values
 // (hi = bf16(x^), lo = bf16(x^ - hi)) so that q.x^ carries ~16 significant
@@ -98,6 +113,12 @@ __device__ inline float bf16_bits_to_f32(uint16_t h) {
 
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
   return static_cast<uint32_t>(f32_to_bf16_bits(lo)) | (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
+}
+
+// Two floats -> two fp16 (round to nearest even) in one instruction.
+__device__ inline uint32_t pack_f16x2(float lo, float hi) {
+  const f16x2 v = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // log(sinh x / x) in fp32: series to x^10 below 0.5, else the identity
@@ -136,7 +157,8 @@ __device__ inline float code_f(uint32_t w, int j) {
 // compiles those paths out.
 template <int D, int KBITS, int VBITS, bool EXACT, bool SPLIT, bool TOK>
 __global__ __launch_bounds__(kThreads, 2) void attn_tile_kernel(AttnLaunch p, int32_t group_shift,
-                                                                 int64_t rows_per_kvhead, int64_t split_keys) {
+                                                                 int64_t rows_per_kvhead, int64_t split_keys,
+                                                                 const float *__restrict__ vbound) {
   constexpr int KS = Tile<D>::kStride;
   constexpr int VS = Tile<D>::vStride;
   constexpr int NS = D / 16;  // k-steps over the head dimension
@@ -225,6 +247,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_tile_kernel(AttnLaunch p, in
 #pragma unroll
   for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
+  // value exponent of the head from the pre-pass's partial bounds: O holds
+  // sum p v 2^-ev
+  float vb = lane < kVChunks ? vbound[bkv * kVChunks + lane] : 0.f;
+#pragma unroll
+  for (int o2 = 32; o2 >= 1; o2 >>= 1) vb = fmaxf(vb, __shfl_xor(vb, o2, 64));
+  const int ev = vb > 0.f ? max(min(ilogbf(vb), 127) - 14, kMinVExp) : kMinVExp;
+  const float vsc = ldexpf(1.0f, -ev);
   const float alpha = p.tau * kLog2e;
 
   // key range of this workgroup in the concatenated sequence [cache ; current]
@@ -355,9 +384,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_tile_kernel(AttnLaunch p, in
     {
       // unit = 4 consecutive keys x 8 consecutive head-dim values
       constexpr int UNITS = (kBN / 4) * (D / 8);
+      const int kq = tid & 15;  // key quad
+      const int dq = tid >> 4;  // head-dim octet
+      // dequantise v 2^-ev (exact scaling), round to fp16, store transposed
       if (tid < UNITS) {
-        const int kq = tid & 15;  // key quad
-        const int dq = tid >> 4;  // head-dim octet
         const int ks = kq >> 2, a = kq & 3;
         const int slot = 16 * ks + ((a >> 1) << 2) + ((a & 1) << 3);
         float v[4][8];
@@ -372,10 +402,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_tile_kernel(AttnLaunch p, in
             if (ok) w = VBITS == 2 ? *reinterpret_cast<const uint16_t *>(src) : *reinterpret_cast<const uint32_t *>(src);
             if (!vtok) {  // one step per group of the row
               const int64_t m = row * ng + ((8 * dq) >> group_shift);
-              const float stp = ok ? meta_at(p.vc_scale, m, p.meta16) : 0.f;
-              const float zp = ok ? meta_at(p.vc_zero, m, p.meta16) : 0.f;
+              const float stp = ok ? meta_at(p.vc_scale, m, p.meta16) * vsc : 0.f;
+              const float zp = ok ? meta_at(p.vc_zero, m, p.meta16) * vsc : 0.f;
 #pragma unroll
-              for (int e = 0; e < 8; ++e) v[j][e] = ok ? fmaf(stp, code_f<VBITS>(w, e), zp) : 0.f;
+              for (int e = 0; e < 8; ++e) v[j][e] = fmaf(stp, code_f<VBITS>(w, e), zp);
             } else {  // groups along the tokens: one per channel
               const int64_t m0 = (row >> group_shift) * D + 8 * dq;
 #pragma unroll
@@ -383,7 +413,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_tile_kernel(AttnLaunch p, in
                 const float4 s4 = meta4(p.vc_scale, m0 + e4, p.meta16), z4 = meta4(p.vc_zero, m0 + e4, p.meta16);
                 const float sv[4] = {s4.x, s4.y, s4.z, s4.w}, zv[4] = {z4.x, z4.y, z4.z, z4.w};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[j][e4 + e] = ok ? fmaf(sv[e], code_f<VBITS>(w, e4 + e), zv[e]) : 0.f;
+                for (int e = 0; e < 4; ++e)
+                  v[j][e4 + e] = ok ? fmaf(sv[e] * vsc, code_f<VBITS>(w, e4 + e), zv[e] * vsc) : 0.f;
               }
             }
           }
@@ -397,14 +428,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_tile_kernel(AttnLaunch p, in
             const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              v[j][2 * e] = __uint_as_float(u[e] << 16);
-              v[j][2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+              v[j][2 * e] = __uint_as_float(u[e] << 16) * vsc;
+              v[j][2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u) * vsc;
             }
           }
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          uint2 w2 = make_uint2(pack_bf16x2(v[0][e], v[1][e]), pack_bf16x2(v[2][e], v[3][e]));
+          uint2 w2 = make_uint2(pack_f16x2(v[0][e], v[1][e]), pack_f16x2(v[2][e], v[3][e]));
           *reinterpret_cast<uint2 *>(&Vt[(8 * dq + e) * VS + slot]) = w2;
         }
       }
@@ -524,7 +555,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_tile_kernel(AttnLaunch p, in
 #pragma unroll
       for (int db = 0; db < NDB; ++db) o[db] *= sc;
     }
-    bf16x8 pk[4];
+    f16x8 pk[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       float e[16];
@@ -537,8 +568,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_tile_kernel(AttnLaunch p, in
       for (int half = 0; half < 2; ++half) {
         const float *f = &e[8 * half];
         pk[2 * kb + half] = __builtin_bit_cast(
-            bf16x8, make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
-                               pack_bf16x2(f[6], f[7])));
+            f16x8, make_uint4(pack_f16x2(f[0], f[1]), pack_f16x2(f[2], f[3]), pack_f16x2(f[4], f[5]),
+                              pack_f16x2(f[6], f[7])));
       }
     }
 
@@ -548,14 +579,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_tile_kernel(AttnLaunch p, in
       const uint16_t *vrow = &Vt[(32 * db + qc) * VS + 8 * h];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 va = *reinterpret_cast<const bf16x8 *>(vrow + 16 * ks);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk[ks], o[db], 0, 0, 0);
+        const f16x8 va = *reinterpret_cast<const f16x8 *>(vrow + 16 * ks);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pk[ks], o[db], 0, 0, 0);
       }
     }
   }
 
   // ---------------- finalize ----------------
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float vs = ldexpf(1.0f, ev);
   if (SPLIT) {
     // partial: O (unnormalised) then (m, l), fp32, [split][qrow][kPartialStride(D)]
     if (row_ok) {
@@ -566,7 +598,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_tile_kernel(AttnLaunch p, in
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[32 * db + 8 * g4 + 4 * h + e] = o[db][4 * g4 + e];
+          for (int e = 0; e < 4; ++e) w[32 * db + 8 * g4 + 4 * h + e] = o[db][4 * g4 + e] * vs;
       if (h == 0) {
         w[D] = m_run;
         w[D + 1] = l_tot;
@@ -574,7 +606,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_tile_kernel(AttnLaunch p, in
     }
     return;
   }
-  const float inv = 1.0f / l_tot;
+  const float inv = vs / l_tot;
   if (row_ok) {
     uint16_t *optr = p.out + qrow * D;
 #pragma unroll
@@ -587,6 +619,47 @@ __global__ __launch_bounds__(kThreads, 2) void attn_tile_kernel(AttnLaunch p, in
         *reinterpret_cast<uint2 *>(optr + dd) = w;
       }
   }
+}
+
+// Value pre-pass: workgroup (chunk, b * Hkv + hk) bounds |v| over its
+// share of the head's cached value groups (max(|z|, |z + top D|) per group)
+// and of its current-chunk values, and writes the bound to
+// part[(b * Hkv + hk) * kVChunks + chunk].
+__global__ __launch_bounds__(256) void value_bound_kernel(AttnLaunch p, int32_t group_shift, float *part) {
+  const int tid = threadIdx.x;
+  const int64_t ch = blockIdx.x, bkv = blockIdx.y;
+  const int64_t b = bkv / p.Hkv, hk = bkv - b * p.Hkv;
+  float vm = 0.f;
+  if (p.Nc > 0) {
+    const float top = static_cast<float>((1 << p.vbits) - 1);
+    const bool tok = p.vtok;
+    // groups along the head dim: Nc rows of d/G groups; along the tokens:
+    // ceil(Nc/G) token groups of d channels
+    const int64_t per = tok ? p.d : (p.d >> group_shift);
+    const int64_t nrow = tok ? (p.Nc + (int64_t{1} << group_shift) - 1) >> group_shift : p.Nc;
+    const int64_t n = nrow * per, lo = n * ch / kVChunks, hi = n * (ch + 1) / kVChunks;
+    for (int64_t i = lo + tid; i < hi; i += 256) {
+      const int64_t r = i / per, c = i - r * per;
+      const int64_t e = tok ? (p.layout.row(p.cap, p.Hkv, b, hk, r << group_shift) >> group_shift) * per + c
+                            : p.layout.row(p.cap, p.Hkv, b, hk, r) * per + c;
+      const float stp = meta_at(p.vc_scale, e, p.meta16), zp = meta_at(p.vc_zero, e, p.meta16);
+      vm = fmaxf(vm, fmaxf(fabsf(zp), fabsf(fmaf(stp, top, zp))));
+    }
+  }
+  {  // current chunk: bf16 pairs
+    const uint32_t *w = reinterpret_cast<const uint32_t *>(p.v_cur + bkv * p.Ncur * p.d);
+    const int64_t n = p.Ncur * p.d / 2, lo = n * ch / kVChunks, hi = n * (ch + 1) / kVChunks;
+    for (int64_t i = lo + tid; i < hi; i += 256) {
+      const uint32_t u = w[i] & 0x7fff7fffu;  // |v| of both halves
+      vm = fmaxf(vm, fmaxf(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u)));
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) vm = fmaxf(vm, __shfl_xor(vm, o, 64));
+  __shared__ float red[4];
+  if ((tid & 63) == 0) red[tid >> 6] = vm;
+  __syncthreads();
+  if (tid == 0) part[bkv * kVChunks + ch] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
 // Log-sum-exp merge of the split partials: one wave per query row.
@@ -629,11 +702,19 @@ hipError_t launch_bits(const AttnLaunch &p, hipStream_t stream, bool exact) {
   const dim3 grid(static_cast<uint32_t>((rows + kBM - 1) / kBM), static_cast<uint32_t>(p.B * p.Hkv),
                   static_cast<uint32_t>(splits));
   const int32_t gshift = __builtin_ctz(static_cast<unsigned>(p.group));
-  if (exact)
-    attn_tile_kernel<D, KB, VB, true, SPLIT, kTok><<<grid, dim3(kThreads), 0, stream>>>(p, gshift, rows, split_keys);
-  else
-    attn_tile_kernel<D, KB, VB, false, SPLIT, kTok><<<grid, dim3(kThreads), 0, stream>>>(p, gshift, rows, split_keys);
+  // value bounds after the split partials
+  float *vpart = reinterpret_cast<float *>(static_cast<char *>(p.workspace) +
+                                           general_bound_offset(p.B, p.Hq, p.Nq, D, splits, SPLIT));
+  value_bound_kernel<<<dim3(kVChunks, static_cast<uint32_t>(p.B * p.Hkv)), dim3(256), 0, stream>>>(p, gshift, vpart);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (exact)
+    attn_tile_kernel<D, KB, VB, true, SPLIT, kTok>
+        <<<grid, dim3(kThreads), 0, stream>>>(p, gshift, rows, split_keys, vpart);
+  else
+    attn_tile_kernel<D, KB, VB, false, SPLIT, kTok>
+        <<<grid, dim3(kThreads), 0, stream>>>(p, gshift, rows, split_keys, vpart);
+  e = hipGetLastError();
   if (e != hipSuccess || !SPLIT) return e;
   const int64_t nrows = p.B * p.Hq * p.Nq;
   attn_combine_kernel<D><<<dim3(static_cast<uint32_t>((nrows + 3) / 4)), dim3(256), 0, stream>>>(
@@ -693,6 +774,16 @@ int short_path_splits(int64_t B, int64_t Hkv, int64_t rows_per_kvhead, int64_t N
 size_t short_path_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int32_t d, int splits) {
   return static_cast<size_t>(splits) * static_cast<size_t>(B * Hq * Nq) * static_cast<size_t>(kPartialStride(d)) *
          sizeof(float);
+}
+
+size_t general_bound_offset(int64_t B, int64_t Hq, int64_t Nq, int32_t d, int splits, bool split) {
+  return split ? (short_path_workspace_bytes(B, Hq, Nq, d, splits) + 255) / 256 * 256 : 0;
+}
+
+size_t general_path_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int32_t d, int splits,
+                                    bool split) {
+  return general_bound_offset(B, Hq, Nq, d, splits, split) +
+         (static_cast<size_t>(B * Hkv) * kVChunks * sizeof(float) + 255) / 256 * 256;
 }
 #endif
 

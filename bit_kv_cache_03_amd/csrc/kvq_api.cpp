@@ -245,7 +245,7 @@ Plan plan_attention(const kv_attn_args *a, bool query_device) {
       pl.workspace = kvq::short_path_workspace_bytes(a->B, a->Hq, a->Nq, a->d, pl.splits);
     } else {
       pl.splits = a->splits > 0 ? a->splits : kvq::short_path_splits(a->B, a->Hkv, rows, a->Nc, cus);
-      pl.workspace = kvq::short_path_workspace_bytes(a->B, a->Hq, a->Nq, a->d, pl.splits);
+      pl.workspace = kvq::general_path_workspace_bytes(a->B, a->Hq, a->Hkv, a->Nq, a->d, pl.splits, true);
     }
   } else if (kvq::fast_kernel_ok(a->d, a->corr, tokens_axis(a), cache_page_size(a))) {  // split-K when it balances
     const int cus = query_device ? device_cu_count() : 256;
@@ -253,6 +253,8 @@ Plan plan_attention(const kv_attn_args *a, bool query_device) {
     pl.splits = fp.splits;
     pl.full_units = fp.full_units;
     pl.workspace = kvq::fast_path_workspace_bytes(a->B, a->Hq, a->Hkv, a->Nq, pl.splits);
+  } else {
+    pl.workspace = kvq::general_path_workspace_bytes(a->B, a->Hq, a->Hkv, a->Nq, a->d, 1, false);
   }
   return pl;
 }

@@ -123,6 +123,13 @@ void launch_key_scale(const AttnLaunch &p, hipStream_t stream, float *part);
 // workspace it needs (partials of every split for every query row).
 int short_path_splits(int64_t B, int64_t Hkv, int64_t rows_per_kvhead, int64_t Nc, int cu_count);
 size_t short_path_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int32_t d, int splits);
+// General kernel (attention.hip; head dim 64, the exact form, groups along
+// the tokens, small pages): its workspace holds the split partials (split:
+// the short path's key-range split), then, from a 256-byte boundary, 32
+// fp32 partial bounds of |value| per (b, KV head) written by its pre-pass.
+size_t general_bound_offset(int64_t B, int64_t Hq, int64_t Nq, int32_t d, int splits, bool split);
+size_t general_path_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int32_t d, int splits,
+                                    bool split);
 // Log-sum-exp merge of split partials into the bf16 output.
 hipError_t launch_combine(const float *ws, uint16_t *out, int64_t nrows, int splits, int32_t d, hipStream_t stream);
 // Short-query kernel (attention_short.hip): head dim 128, correction off or

@@ -194,7 +194,9 @@ typedef struct {
  * long path with d = 128 and correction off or Taylor, the same partials
  * when it splits the key range (more than one split), then 96 fp32 partial
  * key, value and query bounds per (b, KV head) rounded up to 256 bytes;
- * otherwise 0.  The
+ * on the general kernel (d = 64, the exact form, groups along the tokens,
+ * pages smaller than a tile) 32 fp32 partial value bounds per (b, KV head),
+ * after the short path's partials rounded up to 256 bytes.  The
  * contents need no initialisation and are meaningless after the call.
  * Returns 0 for invalid arguments as well; kv_attention_corrected reports
  * those. */

@@ -201,7 +201,7 @@ def test_long_path_workspace(kvq):
     """The head-dim-128 long path keeps 32 fp32 partial key bounds, 32
     partial value bounds and 32 partial query bounds per (batch, KV head),
     rounded up to 256 bytes; the general kernel (head dim 64, or the exact
-    correction) needs none."""
+    correction) keeps 32 partial value bounds per (batch, KV head)."""
     size = lambda **kw: kvq.lib.kv_attention_workspace_size(C.byref(_args(kvq, path=1, **kw)))
     assert size() == 768                            # 2 heads x 96 x 4 B
     assert size(B=3, Hq=80, Hkv=40) == 46080        # 120 heads x 384 B
@@ -209,8 +209,9 @@ def test_long_path_workspace(kvq):
     # forced key-range splits (2 tiles here): partials of 2 splits first
     assert size(splits=2) == 2 * 1 * 4 * 8 * (128 + 4) * 4 + 768
     assert size(splits=5) == size(splits=2)         # clamped to the 2 tiles
-    assert size(corr=2) == 0
-    assert size(d=64) == 0
+    assert size(corr=2) == 256                      # 2 heads x 32 x 4 B
+    assert size(d=64) == 256
+    assert size(corr=2, B=3, Hq=80, Hkv=40) == 15360  # 120 heads x 128 B
     a = _args(kvq, path=1)
     assert _attn(kvq, a) == kvq.KV_ERR_WORKSPACE
     a = _args(kvq, path=1, workspace=0x40000000, workspace_bytes=255)
@@ -220,12 +221,13 @@ def test_long_path_workspace(kvq):
 def test_short_path_workspace_grows_with_splits(kvq):
     """Split partials: splits x B*Hq*Nq rows of d+4 floats, for both short
     kernels (head dim 128 with correction off or Taylor, and the general
-    one)."""
-    part = 1 * 4 * 8 * (128 + 4) * 4
+    one); the general one adds 32 partial value bounds per (batch, KV head)
+    from the next 256-byte boundary."""
+    part = 1 * 4 * 8 * (128 + 4) * 4                # a multiple of 256 here
     size = lambda **kw: kvq.lib.kv_attention_workspace_size(C.byref(_args(kvq, path=2, **kw)))
     assert [size(splits=s) for s in (1, 2, 4, 8)] == [s * part for s in (1, 2, 4, 8)]
-    assert [size(splits=s, corr=2) for s in (1, 2, 4, 8)] == [s * part for s in (1, 2, 4, 8)]
-    assert size(splits=3, d=64) == 3 * 1 * 4 * 8 * (64 + 4) * 4
+    assert [size(splits=s, corr=2) for s in (1, 2, 4, 8)] == [s * part + 256 for s in (1, 2, 4, 8)]
+    assert size(splits=3, d=64) == 3 * 1 * 4 * 8 * (64 + 4) * 4 + 256
 
 
 def test_quantize_argument_errors(kvq):
