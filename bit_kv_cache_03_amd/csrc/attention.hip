@@ -671,19 +671,24 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float *__restri
   if (row >= nrows) return;
   constexpr int PER = D / 64;  // values per lane
   constexpr int64_t W = kPartialStride(D);
-  float m = -INFINITY;
-  for (int s = 0; s < splits; ++s) m = fmaxf(m, ws[(s * nrows + row) * W + D]);
-  float l = 0.f, acc[PER];
+  // one pass, running max: a split's loads do not wait for the others' math
+  float m = -INFINITY, l = 0.f, acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+#pragma unroll 4
   for (int s = 0; s < splits; ++s) {
     const float *w = ws + (s * nrows + row) * W;
-    const float ms = w[D];
-    if (ms == -INFINITY) continue;  // empty split
-    const float f = exp2f(ms - m);
-    l += f * w[D + 1];
+    const float ms = w[D], ls = w[D + 1];
+    float o[PER];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] += f * w[lane * PER + e];
+    for (int e = 0; e < PER; ++e) o[e] = w[lane * PER + e];
+    if (ms == -INFINITY) continue;  // empty split
+    const float mn = fmaxf(m, ms);
+    const float c = exp2f(m - mn), f = exp2f(ms - mn);  // c = 0 for the first non-empty split
+    l = fmaf(l, c, f * ls);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] = fmaf(acc[e], c, f * o[e]);
+    m = mn;
   }
   const float inv = 1.0f / l;
 #pragma unroll

@@ -904,17 +904,20 @@ __global__ __launch_bounds__(256) void tail_combine_kernel(const float *__restri
   const int64_t qrow = (b * p.Hq + hk * gq + rr / p.Nq) * p.Nq + rr % p.Nq;
   const int64_t nrows = p.B * p.Hq * p.Nq;
   constexpr int64_t W = kPartialStride(D);
-  float m = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, ws[(s * nrows + qrow) * W + D]);
-  float l = 0.f, a0 = 0.f, a1 = 0.f;
+  // one pass, running max: a split's loads do not wait for the others' math
+  float m = -INFINITY, l = 0.f, a0 = 0.f, a1 = 0.f;
+#pragma unroll 4
   for (int s = 0; s < nsplit; ++s) {
     const float *w = ws + (s * nrows + qrow) * W;
-    if (w[D] == -INFINITY) continue;  // no key of this split is visible to the row
-    const float f = exp2f(w[D] - m);
-    l += f * w[D + 1];
+    const float ms = w[D], ls = w[D + 1];
     const float2 o = *reinterpret_cast<const float2 *>(w + 2 * lane);
-    a0 += f * o.x;
-    a1 += f * o.y;
+    if (ms == -INFINITY) continue;  // no key of this split is visible to the row
+    const float mn = fmaxf(m, ms);
+    const float c = exp2f(m - mn), f = exp2f(ms - mn);  // c = 0 for the first visible split
+    l = fmaf(l, c, f * ls);
+    a0 = fmaf(a0, c, f * o.x);
+    a1 = fmaf(a1, c, f * o.y);
+    m = mn;
   }
   const float inv = 1.0f / l;
   *reinterpret_cast<uint32_t *>(out + qrow * D + 2 * lane) = pack2(a0 * inv, a1 * inv);
