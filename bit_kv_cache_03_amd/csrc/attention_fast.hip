@@ -20,8 +20,11 @@
 // exp2 domain.  A pre-pass (key_scale_kernel) bounds |k| and |q| per KV head,
 // and ek balances the two so both operands stay in fp16 range (keys below
 // 2^15 always; queries are clamped there, which only a product
-// |q| |k| tau log2(e) beyond ~2^29 can reach).  Probabilities and values
-// stay bf16.
+// |q| |k| tau log2(e) beyond ~2^29 can reach).  Values and probabilities
+// are fp16 as well: the pre-pass also bounds |v| per KV head, values enter
+// as v 2^-ev with |v| 2^-ev below 2^15, and the epilogue multiplies O by
+// 2^ev (bf16 values moved the outputs of short INT2 caches with large steps
+// past the mean tolerance).
 //
 // Per 64-key tile, software-pipelined across tiles inside each wave:
 //   1. S_t = K_t Q^T - m (fp16 MFMA, then one bf16 step)  with
@@ -30,9 +33,10 @@
 //                                       the HBM fetch of t+2
 // The running max m of each row enters the score MFMAs through the extra
 // bf16 step (below), so an exponential is exp2 of the accumulator itself.
-// m starts at 0 and moves only when a row's sum would leave [2^-60, 2^40]
-// (see fix_growth): bf16 probabilities and the fp32 O and l keep their
-// relative precision over that whole range, so no per-tile max is needed.
+// m starts at 0 and moves only when a row's sum would leave [2^-10, 2^40]
+// or a probability overflows fp16 (see fix_growth): fp16 probabilities stay
+// out of the subnormals and fp32 O and l keep their relative precision over
+// that range, so no per-tile max is needed.
 // K tiles are double-buffered and V tiles triple-buffered in LDS; one
 // barrier per tile.  Keys past the end of a segment are fetched as copies
 // of its last key: their scores equal that key's, so the tile max is
@@ -521,13 +525,12 @@ __device__ inline float set_max_slots(QState &qs, float m, int h) {
 // it): if some row's sum left [kShrink, kGrowth] (or is not finite), move
 // that row's m by the tile max (up or down), rescale O and l0, redo the
 // tile's probabilities, and shift the already computed next scores sn by the
-// same amount.  Rare: it takes scores 40 binary orders above m, or all of a
-// row's scores so far 60 below it (the first tile after m = 0 can be one).
-// A row with an empty sum and no visible key in the tile (causal mask) is
-// left alone.
-// (With fp16 probabilities a p above 65504 rounds to inf, which fails the
-// growth test; the shrink bound keeps a row's largest p away from the fp16
-// subnormals.)
+// same amount.  Rare: it takes a score about 16 binary orders above m (a p
+// above 65504 rounds to inf in fp16, which fails the growth test), or all
+// of a row's scores so far about 10 below it (the first tile after m = 0
+// can be one); the shrink bound keeps a row's largest p away from the fp16
+// subnormals.  A row with an empty sum and no visible key in the tile
+// (causal mask) is left alone.
 constexpr float kGrowth = 1099511627776.0f;  // 2^40
 constexpr float kShrink = 0.0009765625f;     // 2^-10
 
