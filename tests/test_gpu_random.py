@@ -16,7 +16,7 @@ BASES = ["tiny_d64_int2", "h24_int4_cache16k", "h40_int2_outliers_cache25k", "gq
          "long_video_cache61k"]
 
 
-def _cases(n=120, seed=20261203):
+def _cases(n=600, seed=20261203):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
