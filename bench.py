@@ -32,7 +32,9 @@ sys.path.insert(0, ROOT)
 
 from bit_kv_cache_03_amd import workloads as W  # noqa: E402
 
-DEFAULT_WORKLOAD = "h24_int4_cache16k"
+# the largest workload that fits one GPU (4.47e12 flop, a 537 MB packed cache)
+DEFAULT_WORKLOAD = "gqa_prefill_b16_cache32k"
+MALL_EVICT_BYTES = 512 << 20  # > the 256 MB MALL: written between HBM-graded launches
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "cached-key tokens\u00b7queries/s (TFLOP/s eff.) and packed-KV HBM GB/s vs roofline"
@@ -140,6 +142,46 @@ def cpu_baseline(w, data, corr: str, target_s: float = 12.0, causal: bool = Fals
                       f"fp64 oracle attention with {corr} correction over all {w.Nc}+{w.Ncur} keys"
                       f"{' (causal mask on the current chunk)' if causal else ''}, "
                       f"plus the chunk's quantize prorated; {t:.1f} s wall on {threads} threads"}
+
+
+def arithmetic(w, corr: str, page_size: int, kaxis: str, vaxis: str) -> dict:
+    """The arithmetic the attention call computes in, by the kernel that
+    serves it: head dim 128 with correction off or Taylor, groups along the
+    head dimension and pages of at least one 32/64-key tile run the fp16
+    kernels; the rest runs the general kernel (bf16 hi + lo keys)."""
+    fp16 = (w.d == 128 and corr != "exact" and kaxis == "dim" and vaxis == "dim" and
+            (page_size == 0 or page_size >= 32))
+    if fp16:
+        return {"dtype": "fp16",
+                "dtype_detail": "Q K^T and P V on fp16 MFMA (v_mfma_f32_32x32x16_f16) with fp32 accumulation, "
+                                "keys and values scaled by powers of two into the fp16 range; the correction and "
+                                "running-max step on bf16 MFMA (hi + lo splits); softmax in fp32; bf16 inputs and "
+                                "outputs; INT%d keys / INT%d values dequantised in-kernel" % (w.kbits, w.vbits)}
+    return {"dtype": "bf16",
+            "dtype_detail": "Q K^T on bf16 MFMA with keys split into bf16 hi + lo parts, P V on fp16 MFMA, fp32 "
+                            "accumulation and softmax; bf16 inputs and outputs"}
+
+
+def gpu_clocks():
+    """Current shader (sclk) and memory (mclk) clocks of the GPU this process
+    uses (amdsmi, matched by PCI address), or None where unavailable."""
+    try:
+        import amdsmi
+        import torch
+        pr = torch.cuda.get_device_properties(torch.cuda.current_device())
+        bdf = "%04x:%02x:%02x.0" % (pr.pci_domain_id, pr.pci_bus_id, pr.pci_device_id)
+        amdsmi.amdsmi_init()
+        try:
+            h = amdsmi.amdsmi_get_processor_handle_from_bdf(bdf)
+            g = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.SYS)
+            m = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.MEM)
+            return {"sclk_mhz": g.get("clk"), "sclk_max_mhz": g.get("max_clk"), "mclk_mhz": m.get("clk"),
+                    "mclk_max_mhz": m.get("max_clk"), "bdf": bdf, "source": "amdsmi, sampled while the timed "
+                                                                            "steps ran"}
+        finally:
+            amdsmi.amdsmi_shut_down()
+    except Exception as e:  # the record is informative only
+        return {"error": f"{type(e).__name__}: {e}"}
 
 
 def copy_probe(nbytes: int, reps: int = 3):
@@ -274,6 +316,9 @@ def main():
     ap.add_argument("--traffic", default=None, metavar="PMC_DIR",
                     help="only turn rocprofv3 FETCH_SIZE/WRITE_SIZE runs into profiles/traffic_<workload>.json")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
+    ap.add_argument("--evict", default="auto", choices=["auto", "on", "off"],
+                    help="write a 512 MiB buffer between timed steps so that no launch finds the cache in the "
+                         "MALL (auto: on for HBM-graded runs, i.e. at most 64 query rows per KV head)")
     args = ap.parse_args()
     if args.traffic:
         write_traffic(W.WORKLOADS[args.workload], args.traffic, args.copy_bytes, call_options(args))
@@ -350,23 +395,36 @@ def main():
         kvq.quantize(k, kc, w.Nc, stream)
         kvq.quantize(v, vc, w.Nc, stream)
 
+    # few query rows per KV head: the packed cache read bounds the kernel
+    hbm_bound = w.rows_per_kvhead <= 64
+    evict = args.evict == "on" or (args.evict == "auto" and hbm_bound)
+    scratch = torch.empty(MALL_EVICT_BYTES // 4, dtype=torch.float32, device="cuda") if evict else None
     for _ in range(args.warmup):
         step(args_c)
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    s_end = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
     for i in range(args.steps):
+        if scratch is not None:
+            scratch.fill_(float(i))  # evicts the cache's lines from the MALL; outside the step's events
         step(args_c, evs[i])
+        s_end[i].record(stream)
     t_end.record(stream)
+    clocks = gpu_clocks()  # the steps above are still running: launches are asynchronous
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_step = t_start.elapsed_time(t_end) / args.steps
+    if scratch is None:
+        ms_step = t_start.elapsed_time(t_end) / args.steps
+    else:  # steps timed one by one, the eviction writes between them excluded
+        ms_step = float(np.mean([a.elapsed_time(e) for (a, _), e in zip(evs, s_end)]))
     attn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     quant_ms = ms_step - attn_ms
+    del scratch
 
     overhead = None
     if not args.no_overhead and corr != "off":
@@ -376,9 +434,15 @@ def main():
             attention(a_off)
         e_off = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
         e_on = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        scratch = torch.empty(MALL_EVICT_BYTES // 4, dtype=torch.float32, device="cuda") if evict else None
         for i in range(args.steps):   # interleave so drift hits both equally
+            if scratch is not None:
+                scratch.fill_(float(i))
             e_off[i][0].record(stream); attention(a_off); e_off[i][1].record(stream)
+            if scratch is not None:
+                scratch.fill_(float(i))
             e_on[i][0].record(stream); attention(args_c); e_on[i][1].record(stream)
+        del scratch
         torch.cuda.synchronize()
         t_off = float(np.median([a.elapsed_time(b) for a, b in e_off]))
         t_on = float(np.median([a.elapsed_time(b) for a, b in e_on]))
@@ -387,8 +451,6 @@ def main():
     flops = attention_flops(w, args.causal)
     ckq = w.B * w.Hq * w.Nq * w.Nc
     achieved = flops / (attn_ms * 1e-3) / 1e12
-    # few query rows per KV head: the packed cache read bounds the kernel
-    hbm_bound = w.rows_per_kvhead <= 64
     pbytes = packed_bytes(w, 2 if args.meta == "f16" else 4, args.kaxis, args.vaxis)
     if hbm_bound:
         roof = {"bound": "hbm", "achieved": pbytes / (attn_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
@@ -408,7 +470,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        **arithmetic(w, corr, args.page_size, args.kaxis, args.vaxis),
         "data": "synthetic: seeded N(0,1) q/k/v with the workload's key structure, bf16; cache INT%d/INT%d group %d%s" % (
             w.kbits, w.vbits, w.group, (", binary16 step/zero" if args.meta == "f16" else "") +
             (f", K/V groups along {args.kaxis}/{args.vaxis}" if "tokens" in (args.kaxis, args.vaxis) else "")),
@@ -423,6 +485,8 @@ def main():
         "correction_overhead": overhead,
         "wall_s": wall,
         "kernel_sha": sha,
+        "mall_evict_between_steps": evict,
+        "clocks": clocks,
         "roofline": dict(roof, frac=roof["achieved"] / roof["peak"], traffic=traffic),
         "cpu_baseline": None,
     }

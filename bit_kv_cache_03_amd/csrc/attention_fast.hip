@@ -212,33 +212,53 @@ struct QState {
   bf16x8 qext;
 };
 
-// The lane's query operands (lane half h holds dimensions 16 s + 8 h .. +7 of
-// k-step s): q 2^ek in fp16 (exact for bf16 q; clamped to the fp16 range),
-// and the extra step's slots 4g+{0,1,2,3} = (N_hi, N_hi, N_lo, -m) with
-// N_g = tau^2/24 log2(e) ||q_g||^2 split into bf16 (zero without the
-// correction; the lane holds slots 8h .. 8h+7, groups 2h and 2h+1), m = 0.
-template <bool TAYLOR>
-__device__ inline void load_query_folded(const uint16_t *qptr, int h, int group_shift, float tau, int ek,
-                                         QState &qs) {
-  const int ng = 128 >> group_shift;
-  const float qsc = ldexpf(1.0f, ek);
-  float nsum[4] = {0.f, 0.f, 0.f, 0.f};
+// The lane's fp16 query operands (lane half h holds dimensions 16 s + 8 h ..
+// +7 of k-step s): q times `scale`, clamped to the fp16 range.  Cached keys
+// carry tau log2(e) 2^-ek, so their queries take scale = 2^ek (exact for bf16
+// q); current keys are stored as k 2^-ek, so theirs take tau log2(e) 2^ek.
+__device__ inline void query_operands(const uint16_t *qptr, int h, float scale, QState &qs) {
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     const uint4 qw = *reinterpret_cast<const uint4 *>(qptr + 16 * s + 8 * h);
     const uint32_t u[4] = {qw.x, qw.y, qw.z, qw.w};
-    float acc = 0.f;
     uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = pack2h(fminf(fmaxf(lo_f(u[i]) * scale, -65504.0f), 65504.0f),
+                    fminf(fmaxf(hi_f(u[i]) * scale, -65504.0f), 65504.0f));
+    qs.q[s] = __builtin_bit_cast(f16x8, make_uint4(w[0], w[1], w[2], w[3]));
+  }
+}
+
+// The lane's query operands for the cached keys (query_operands with 2^ek)
+// and the extra step's query slots: in lane half 0, slots 4g+{0,1,2,3} =
+// (N_hi, N_hi, N_lo, -m) with N_g = tau^2/24 log2(e) ||q_g||^2 split into bf16
+// (zero without the correction; groups 0 and 1, m = 0 at the start); in lane
+// half 1, with 4 groups the same for groups 2 and 3, else the centre slots
+// 8 + 4g, 9 + 4g = (S_hi, S_lo) with S_g = tau log2(e) sum_{c in g} q_c, which
+// the cached keys' group centres multiply.
+template <bool TAYLOR>
+__device__ inline void load_query_folded(const uint16_t *qptr, int h, int group_shift, float tau, int ek,
+                                         QState &qs) {
+  const int ng = 128 >> group_shift;
+  query_operands(qptr, h, ldexpf(1.0f, ek), qs);
+  float nsum[4] = {0.f, 0.f, 0.f, 0.f}, qsum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const uint4 qw = *reinterpret_cast<const uint4 *>(qptr + 16 * s + 8 * h);
+    const uint32_t u[4] = {qw.x, qw.y, qw.z, qw.w};
+    float acc = 0.f, sum = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       acc += lo_f(u[i]) * lo_f(u[i]) + hi_f(u[i]) * hi_f(u[i]);
-      w[i] = pack2h(fminf(fmaxf(lo_f(u[i]) * qsc, -65504.0f), 65504.0f),
-                    fminf(fmaxf(hi_f(u[i]) * qsc, -65504.0f), 65504.0f));
+      sum += lo_f(u[i]) + hi_f(u[i]);
     }
-    qs.q[s] = __builtin_bit_cast(f16x8, make_uint4(w[0], w[1], w[2], w[3]));
     const int gs = (16 * s + 8 * h) >> group_shift;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) nsum[g] += g == gs ? acc : 0.f;
+    for (int g = 0; g < 4; ++g) {
+      nsum[g] += g == gs ? acc : 0.f;
+      qsum[g] += g == gs ? sum : 0.f;
+    }
   }
   float nh[4], nl[4];
 #pragma unroll
@@ -246,6 +266,17 @@ __device__ inline void load_query_folded(const uint16_t *qptr, int h, int group_
     const float n = TAYLOR && g < ng ? (nsum[g] + __shfl_xor(nsum[g], 32, 64)) * (tau * tau / 24.0f * kLog2e) : 0.f;
     nh[g] = lo_f(pack2(n, 0.f));
     nl[g] = n - nh[g];
+  }
+  float sh[2], sl[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const float t = (qsum[g] + __shfl_xor(qsum[g], 32, 64)) * (tau * kLog2e);
+    sh[g] = g < ng ? lo_f(pack2(t, 0.f)) : 0.f;
+    sl[g] = g < ng ? t - sh[g] : 0.f;
+  }
+  if (h == 1 && ng <= 2) {
+    qs.qext = __builtin_bit_cast(bf16x8, make_uint4(pack2(sh[0], sl[0]), 0u, pack2(sh[1], sl[1]), 0u));
+    return;
   }
   const float n0h = h ? nh[2] : nh[0], n0l = h ? nl[2] : nl[0];
   const float n1h = h ? nh[3] : nh[1], n1l = h ? nl[3] : nl[1];
@@ -257,7 +288,7 @@ struct Fetch {
   uint32_t kw[8];   // K: codes of 16 values (cached) or 16 bf16 values (current)
   uint32_t vw[8];   // V: codes of 2 keys x 8 values (cached) or 2 x 8 bf16 (current)
   float kstep, kzero;
-  float gstep;      // step of correction group (tid % 8) / 2 of the key
+  float gstep, gzero;  // step and zero of the key's extra-step group of the thread (see fetch_k)
   float vstep[2], vzero[2];
 };
 
@@ -271,7 +302,9 @@ struct Ctx {
   int ng, group_shift;
   int beg, end;     // key range of the segment
   int climit;       // causal mask: current keys below climit are visible to the lane's row
-  float kscale;     // tau log2(e) 2^-ek
+  float kscale;     // cached keys: tau log2(e) 2^-ek
+  float cscale;     // current keys: 2^-ek (exact for bf16 keys; tau log2(e) goes to the query)
+  bool centre;      // cached keys centred per group (at most 2 groups per row)
   float vscale;     // 2^-ev: values enter the PV product as fp16 v 2^-ev
   uint32_t kmask;   // code mask of magic8, in a vector register
   CacheLayout layout;         // paged caches: pointers at the pools, rows of (b, hk)
@@ -327,10 +360,16 @@ __device__ inline void fetch_k(const Ctx &c, int k0, int tid, Fetch &f, size_t p
       f.kw[0] = *reinterpret_cast<const uint32_t *>(ks);
     }
     const uint32_t km = krow * static_cast<uint32_t>(c.ng);
-    const int gj = ((tid & 7) >> 1) < c.ng ? ((tid & 7) >> 1) : c.ng - 1;
+    // the group of the thread's extra-step slots 2j, 2j+1 (j = tid % 8): the
+    // Taylor group j / 2 for j < 4 (and for every j with 4 groups), else the
+    // group (j - 4) / 2 whose centre it writes; clamped to the last group
+    const int j = tid & 7;
+    const int gx0 = c.ng == 4 ? (j >> 1) : ((j & 3) >> 1);
+    const int gj = gx0 < c.ng ? gx0 : c.ng - 1;
     f.kstep = meta_ld<kMeta16>(kc_scale, km + static_cast<uint32_t>(d0 >> c.group_shift));
     f.kzero = meta_ld<kMeta16>(kc_zero, km + static_cast<uint32_t>(d0 >> c.group_shift));
     f.gstep = meta_ld<kMeta16>(kc_scale, km + static_cast<uint32_t>(gj));
+    f.gzero = meta_ld<kMeta16>(kc_zero, km + static_cast<uint32_t>(gj));
   } else {
     const uint4 *ks = reinterpret_cast<const uint4 *>(c.k_cur + (krow * D + static_cast<uint32_t>(d0)));
     const uint4 a = ks[0], b = ks[1];
@@ -374,10 +413,14 @@ __device__ inline void fetch_v(const Ctx &c, int k0, int tid, int j, Fetch &f, s
 
 // K tile row (fp16 values, then the slots of the extra bf16 step: 4g+{0,1,2}
 // = -D_g^2 split (hi, lo, hi) for the Taylor correction (zero for
-// g >= d/group or without it), 1.0 in slots 3 and 7 (the running max), zero
-// elsewhere).  Item p < 2 writes values 8p..8p+7 of the thread's 16; item 2
-// writes its two slots 2*(tid%8), +1.  A 304-byte row stride keeps the 16-byte
-// writes (16 lanes = 2 keys x 8 chunks) on disjoint bank quads.
+// g >= d/group or without it), 1.0 in slots 3 and 7 (the running max), and
+// with at most two groups the centres c_g of a cached key's groups in slots
+// 8 + 4g and 9 + 4g; zero elsewhere).  Cached values are stored centred,
+// (z - c_g + D code) tau log2(e) 2^-ek, and the step adds c_g times the
+// query's group sums back; current keys are stored as k 2^-ek, exact.
+// Item p < 2 writes values 8p..8p+7 of the thread's 16; item 2 writes its two
+// slots 2*(tid%8), +1.  A 304-byte row stride keeps the 16-byte writes
+// (16 lanes = 2 keys x 8 chunks) on disjoint bank quads.
 constexpr int kItemsK = 3;
 
 template <bool CACHED, bool TAYLOR, int KBITS>
@@ -388,7 +431,8 @@ __device__ inline void unpack_k_item(int p, const Ctx &c, int tid, const Fetch &
     if (CACHED) {
       uint32_t m[4];
       magic8<KBITS>(KBITS == 4 ? f.kw[p] : (f.kw[0] >> (16 * p)), c.kmask, m);
-      const float s = f.kstep * c.kscale, z = fmaf(-1024.0f, f.kstep, f.kzero) * c.kscale;
+      const float zc = c.centre ? f.kzero - group_centre<KBITS>(f.kzero, f.kstep) : f.kzero;
+      const float s = f.kstep * c.kscale, z = fmaf(-1024.0f, f.kstep, zc) * c.kscale;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         w[e] = pair_h(dequant_h(magic_code(m, 2 * e), s, z), dequant_h(magic_code(m, 2 * e + 1), s, z));
@@ -396,14 +440,18 @@ __device__ inline void unpack_k_item(int p, const Ctx &c, int tid, const Fetch &
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t x = f.kw[4 * p + e];
-        w[e] = pack2h(lo_f(x) * c.kscale, hi_f(x) * c.kscale);
+        w[e] = pack2h(lo_f(x) * c.cscale, hi_f(x) * c.cscale);
       }
     }
     *reinterpret_cast<uint4 *>(Kb + kk * KS + d0 + 8 * p) = make_uint4(w[0], w[1], w[2], w[3]);
-  } else {  // slots 2j, 2j+1: correction terms of group j/2, and 1.0 in the max slots 3 and 7
+  } else {  // slots 2j, 2j+1: correction terms of group j/2, 1.0 in the max slots 3 and 7, centres
     const float one = j == 1 || j == 3 ? 1.0f : 0.f;
     uint32_t w = pack2(0.f, one);
-    if (CACHED && TAYLOR) {
+    if (CACHED && j >= 4 && c.centre) {  // slots 8 + 2(j-4), +1: centre of group (j-4)/2 in both of 8+4g, 9+4g
+      const int g = (j - 4) >> 1;
+      const float cg = (j & 1) == 0 && g < c.ng ? group_centre<KBITS>(f.gzero, f.gstep) : 0.f;
+      w = pack2(cg, cg);
+    } else if (CACHED && TAYLOR) {
       const float sq = (j >> 1) < c.ng ? f.gstep * f.gstep : 0.f;
       const float hsq = lo_f(pack2(sq, 0.f));
       w = (j & 1) ? pack2(-hsq, one) : pack2(-hsq, -(sq - hsq));
@@ -549,7 +597,11 @@ __device__ inline void fix_growth(const f32x16 (&s)[2], f32x16 (&sn)[2], QState 
   mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
   const float m_new = set_max_slots(qs, need && mt > -INFINITY ? st.m + mt : st.m, h);
   const float shift = m_new - st.m;
-  const float sc = exp2f(-shift);
+  // A shrink (shift < 0) only happens to a row whose sum was still empty, so
+  // O and l are zero; a shift below -128 would make exp2(-shift) infinite
+  // and 0 * inf a NaN, hence the clamp to the largest finite float (growth
+  // gives sc <= 1).
+  const float sc = fminf(exp2f(-shift), 3.4e38f);
   st.l = l0 * sc;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) st.o[db] *= sc;
@@ -784,9 +836,10 @@ __global__ __launch_bounds__(THREADS, 1) void attn_fast_kernel(AttnLaunch p, int
   const int64_t rb = unit - bkv * row_blocks;
   const int64_t b = bkv / p.Hkv, hk = bkv - b * p.Hkv;
   const int64_t gq = p.Hq / p.Hkv;
-  // exponent ek of the KV head from the pre-pass's partial bounds: keys
-  // k tau log2(e) 2^-ek and queries q 2^ek near the same magnitude, keys
-  // always below 2^15
+  // exponent ek of the KV head from the pre-pass's partial bounds: key
+  // operands (cached: centred, |k - c| <= 2 max|k|, times tau log2(e) 2^-ek;
+  // current: k 2^-ek) and query operands (q 2^ek, q tau log2(e) 2^ek) near
+  // the same magnitude, keys always below 2^15
   float kb = lane < KCHUNKS ? kpart[3 * bkv * KCHUNKS + lane] : 0.f;
   float qb = lane < KCHUNKS ? kpart[(3 * bkv + 1) * KCHUNKS + lane] : 0.f;
   float vb = lane < KCHUNKS ? kpart[(3 * bkv + 2) * KCHUNKS + lane] : 0.f;
@@ -798,11 +851,11 @@ __global__ __launch_bounds__(THREADS, 1) void attn_fast_kernel(AttnLaunch p, int
   }
   // values enter the PV product as fp16 v 2^-ev, |v| 2^-ev below 2^15
   const int ev = vb > 0.f ? ilogbf(vb) - 14 : 0;
-  const float kt = kb * (p.tau * kLog2e);
+  const float kt = kb * fmaxf(2.0f * p.tau * kLog2e, 1.0f), qt = qb * fmaxf(p.tau * kLog2e, 1.0f);
   int ek = 0;
   if (kt > 0.f) {
     const int lk = ilogbf(kt);
-    if (qb > 0.f) ek = (lk - ilogbf(qb)) >> 1;
+    if (qt > 0.f) ek = (lk - ilogbf(qt)) >> 1;
     if (lk - ek > kFp16Exp) ek = lk - kFp16Exp;
   }
 
@@ -823,6 +876,8 @@ __global__ __launch_bounds__(THREADS, 1) void attn_fast_kernel(AttnLaunch p, int
   c.ng = ng;
   c.group_shift = group_shift;
   c.kscale = ldexpf(p.tau * kLog2e, -ek);
+  c.cscale = ldexpf(1.0f, -ek);
+  c.centre = ng <= 2;
   c.vscale = ldexpf(1.0f, -ev);
   c.kmask = opaque_u32(kCodeMask<KBITS>);
   c.layout = p.layout;
@@ -851,6 +906,8 @@ __global__ __launch_bounds__(THREADS, 1) void attn_fast_kernel(AttnLaunch p, int
   }
   c.beg = max(t0 - tc, 0) * BN;
   c.end = min(max(t1 - tc, 0) * BN, static_cast<int>(p.Ncur));
+  // current keys are exact fp16 k 2^-ek: the softmax scale moves to the query
+  if (c.end > c.beg) query_operands(p.q + qrow * D, h, ldexpf(p.tau * kLog2e, ek), qs);
   if (CAUSAL) {
     // current keys below climit are visible to the lane's row (query j of
     // Nq, aligned to the chunk's end); the workgroup stops at the largest

@@ -74,6 +74,7 @@ struct Fetch {
   float kstep[2];      // step and zero point of the groups of d = 64h + 32j, j = 0, 1
   float kzero[2];
   float gstep[2];      // steps of groups 2h, 2h+1 (correction slots; clamped index)
+  float gzero[2];      // with at most 2 groups: zero points of groups 0 and 1 (centre slots)
   uint32_t vw[4];      // V codes of keys 4kq+j at d in [16dq, 16dq+16): INT4 words
   uint32_t vw2[4];     //   d 16dq..+7 in vw, +8..+15 in vw2; INT2 all 16 in vw
   float vstep[4], vzero[4];
@@ -206,14 +207,16 @@ __device__ inline void fetch_cached(const Ctx &c, int k0, const Lanes &o, int h,
     if (NG == 1) {
       const float st = ld_meta1<M16>(ks, o.km), z = ld_meta1<M16>(kz, o.km);
       f.kstep[0] = f.kstep[1] = f.gstep[0] = f.gstep[1] = st;
-      f.kzero[0] = f.kzero[1] = z;
+      f.kzero[0] = f.kzero[1] = f.gzero[0] = f.gzero[1] = z;
     } else if (NG == 2) {
       const float2 st = ld_meta2<M16>(ks, o.km);
-      const float z = ld_meta1<M16>(kz, o.km + ES * h);
+      const float2 z = ld_meta2<M16>(kz, o.km);
       f.kstep[0] = f.kstep[1] = h ? st.y : st.x;
-      f.kzero[0] = f.kzero[1] = z;
+      f.kzero[0] = f.kzero[1] = h ? z.y : z.x;
       f.gstep[0] = st.x;
       f.gstep[1] = st.y;
+      f.gzero[0] = z.x;
+      f.gzero[1] = z.y;
     } else {
       const float2 st = ld_meta2<M16>(ks, o.km + 2 * ES * h), z = ld_meta2<M16>(kz, o.km + 2 * ES * h);
       f.kstep[0] = f.gstep[0] = st.x;
@@ -243,12 +246,16 @@ __device__ inline void fetch_cached(const Ctx &c, int k0, const Lanes &o, int h,
 
 // Largest |k| (|v|) a lane's share of a cached block can dequantise to:
 // the values of a group lie between z and z + (2^bits - 1) D.
-template <int KBITS>
+// With at most two groups per row the cached keys are centred (see
+// group_centre), and the bound is that of k - centre.
+template <int KBITS, int NG>
 __device__ inline float k_bound(const Fetch &f) {
   float b = 0.f;
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
-    b = fmaxf(b, fmaxf(fabsf(f.kzero[j]), fabsf(fmaf(f.kstep[j], static_cast<float>((1 << KBITS) - 1), f.kzero[j]))));
+  for (int j = 0; j < 2; ++j) {
+    const float z = NG <= 2 ? f.kzero[j] - group_centre<KBITS>(f.kzero[j], f.kstep[j]) : f.kzero[j];
+    b = fmaxf(b, fmaxf(fabsf(z), fabsf(fmaf(f.kstep[j], static_cast<float>((1 << KBITS) - 1), z))));
+  }
   return b;
 }
 template <int VBITS>
@@ -260,13 +267,21 @@ __device__ inline float v_bound(const Fetch &f) {
   return b;
 }
 
+// The cached keys are centred per group (group_centre) when a row has at
+// most two groups: the extra bf16 step then has free slots 8 + 4g, 9 + 4g
+// (lane half 1) for centre x query group sum.
+template <int NG>
+constexpr bool kCentre = NG <= 2;
+
 // K operand of a cached block, straight into the MFMA A-operand registers
 // of S^T = K Q^T: the lane (key kr = lane % 32, half h = lane / 32) holds
 // its key's values d = 64h + 8s .. +7 in k[s] (k-step s, slots 8h .. 8h+7;
-// the query uses the same order), as fp16 k 2^-ek (magic codes, one v_fma_mix
-// each), and for the Taylor correction the slots 4g+{0,1,2,3} = (-D_g^2
-// split hi, lo, hi; 0) in bf16 for its groups g = 2h, 2h+1 (zero for
-// g >= d/group), scaled like the keys.
+// the query uses the same order), as fp16 (k - c_g) 2^-ek (magic codes, one
+// v_fma_mix each; c_g the group's centre, 0 with 4 groups), and in the extra
+// step's slots: for the Taylor correction 4g+{0,1,2,3} = (-D_g^2 split hi,
+// lo, hi; 0) in bf16 for its groups g = 2h, 2h+1 (zero for g >= d/group),
+// scaled like the keys; with centring, lane half 1 holds (c_0, c_0, 0, 0,
+// c_1, c_1, 0, 0) 2^-ek instead (the query side holds its group sums there).
 template <bool TAYLOR, int KBITS, int NG>
 __device__ inline void unpack_k_cached(const Ctx &c, int lane, const Fetch &f, float kscale, f16x8 (&k)[8],
                                        bf16x8 &kext) {
@@ -274,8 +289,9 @@ __device__ inline void unpack_k_cached(const Ctx &c, int lane, const Fetch &f, f
   float sj[2], zj[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
+    const float zc = kCentre<NG> ? f.kzero[j] - group_centre<KBITS>(f.kzero[j], f.kstep[j]) : f.kzero[j];
     sj[j] = f.kstep[j] * kscale;
-    zj[j] = fmaf(-1024.0f, f.kstep[j], f.kzero[j]) * kscale;
+    zj[j] = fmaf(-1024.0f, f.kstep[j], zc) * kscale;
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {  // values d = 64h + 8i .. +7, in the group of d = 64h + 32 (i / 4)
@@ -288,7 +304,11 @@ __device__ inline void unpack_k_cached(const Ctx &c, int lane, const Fetch &f, f
       w[e] = pair_h(dequant_h(magic_code(m, 2 * e), st, z), dequant_h(magic_code(m, 2 * e + 1), st, z));
     k[i] = __builtin_bit_cast(f16x8, make_uint4(w[0], w[1], w[2], w[3]));
   }
-  if (TAYLOR) {
+  if (kCentre<NG> && h == 1) {
+    const float c0 = group_centre<KBITS>(f.gzero[0], f.gstep[0]) * kscale;
+    const float c1 = NG == 2 ? group_centre<KBITS>(f.gzero[1], f.gstep[1]) * kscale : 0.f;
+    kext = __builtin_bit_cast(bf16x8, make_uint4(pack2(c0, c0), 0u, pack2(c1, c1), 0u));
+  } else if (TAYLOR) {
     uint32_t x[4];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -299,6 +319,8 @@ __device__ inline void unpack_k_cached(const Ctx &c, int lane, const Fetch &f, f
       x[2 * j + 1] = pack2(-hsq, 0.f);
     }
     kext = __builtin_bit_cast(bf16x8, make_uint4(x[0], x[1], x[2], x[3]));
+  } else {
+    kext = bf16x8{};
   }
 }
 
@@ -608,11 +630,11 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
   for (; blk < cend; blk += WAVES) {
     const int k0 = blk * BK;
     const int count = c.nc - k0 < BK ? c.nc - k0 : BK;
-    sc.update(k_bound<KBITS>(f), v_bound<VBITS>(f), st.alpha);
+    sc.update(k_bound<KBITS, NG>(f), v_bound<VBITS>(f), st.alpha);
     unpack_k_cached<TAYLOR, KBITS, NG>(c, lane, f, sc.kscale, kreg, kext);
     unpack_v_cached<VBITS>(c, lane, f, sc.vscale, Vt);
     if (blk + WAVES < cend) fetch_cached<KBITS, VBITS, NG, PAGED, M16>(c, (blk + WAVES) * BK, lo, h, f, prn);
-    block_compute<TAYLOR>(kreg, kext, Vt, q, qext, count, sc.alpha, sc.ev, lane, st);
+    block_compute<TAYLOR || kCentre<NG>>(kreg, kext, Vt, q, qext, count, sc.alpha, sc.ev, lane, st);
     if (PAGED && blk + 2 * WAVES < cend) prn = block_row<PAGED>(c, (blk + 2 * WAVES) * BK);
   }
   for (; blk < bend; blk += WAVES) {

@@ -188,6 +188,29 @@ kv_status validate_attention(const kv_attn_args *a) {
   return KV_OK;
 }
 
+// The byte range [p, p + n) overlaps the output or an input of the call
+// (used for the workspace).
+bool overlaps_call(const kv_attn_args *a, const void *p, size_t n) {
+  const size_t q_b = static_cast<size_t>(a->B * a->Hq * a->Nq * a->d) * 2;
+  const size_t cur_b = static_cast<size_t>(a->B * a->Hkv * a->Ncur * a->d) * 2;
+  if (overlaps(p, n, a->out, q_b) || overlaps(p, n, a->q, q_b)) return true;
+  if (a->Ncur > 0 && (overlaps(p, n, a->k_cur, cur_b) || overlaps(p, n, a->v_cur, cur_b))) return true;
+  if (a->Nc > 0) {
+    const kv_qtensor *ts[2] = {a->k_cache, a->v_cache};
+    for (const kv_qtensor *c : ts) {
+      const size_t rows = static_cast<size_t>(tensor_rows(c, a->B, a->Hkv));
+      if (overlaps(p, n, c->codes, rows * static_cast<size_t>(a->d * c->bits / 8)) ||
+          overlaps(p, n, c->scale, meta_array_bytes(c, rows, a->d)) ||
+          overlaps(p, n, c->zero, meta_array_bytes(c, rows, a->d)))
+        return true;
+      if (c->page_table &&
+          overlaps(p, n, c->page_table, static_cast<size_t>(a->B * (c->cap / c->page_size)) * sizeof(int32_t)))
+        return true;
+    }
+  }
+  return false;
+}
+
 kv_status validate_diagnostics(const kv_diag_args *a) {
   if (!a) return KV_ERR_NULL;
   if (!a->q || !a->out) return KV_ERR_NULL;
@@ -271,7 +294,7 @@ const char *kv_status_string(kv_status s) {
     case KV_ERR_UNSUPPORTED: return "unsupported bits, group, head dimension, correction or path";
     case KV_ERR_WORKSPACE: return "workspace missing or too small";
     case KV_ERR_ALIGN: return "a pointer is not 16-byte aligned";
-    case KV_ERR_ALIAS: return "the output overlaps an input";
+    case KV_ERR_ALIAS: return "an output or the workspace overlaps an input";
     case KV_ERR_HIP: return "a HIP runtime call or kernel launch failed";
   }
   return "unknown status";
@@ -291,6 +314,7 @@ kv_status kv_quantize(const void *x, kv_dtype xdt, int64_t B, int64_t H, int64_t
   if (dst->axis != KV_AXIS_DIM && dst->axis != KV_AXIS_TOKENS) return KV_ERR_UNSUPPORTED;
   if (!tensor_group_ok(dst, d)) return KV_ERR_UNSUPPORTED;
   if (dst->cap < 0 || tok_offset > dst->cap || N > dst->cap - tok_offset) return KV_ERR_SHAPE;
+  if (dst->cap > kMaxTokensPerHead) return KV_ERR_UNSUPPORTED;  // the attention would refuse the cache
   if (dst->axis == KV_AXIS_TOKENS &&
       (tok_offset % dst->group != 0 || dst->cap % dst->group != 0 ||
        (dst->page_table && dst->page_size % dst->group != 0)))
@@ -308,6 +332,14 @@ kv_status kv_quantize(const void *x, kv_dtype xdt, int64_t B, int64_t H, int64_t
   if (!aligned16(x) || !aligned16(dst->codes) || !aligned16(dst->scale) || !aligned16(dst->zero))
     return KV_ERR_ALIGN;
   if (dst->meta != KV_META_F32 && dst->meta != KV_META_F16) return KV_ERR_UNSUPPORTED;
+  {  // the input must not overlap the cache it is written into
+    const size_t xb = static_cast<size_t>(t) * (xdt == KV_BF16 ? 2 : 4);
+    const size_t rows = static_cast<size_t>(tensor_rows(dst, B, H));
+    if (overlaps(x, xb, dst->codes, rows * static_cast<size_t>(d * dst->bits / 8)) ||
+        overlaps(x, xb, dst->scale, meta_array_bytes(dst, rows, d)) ||
+        overlaps(x, xb, dst->zero, meta_array_bytes(dst, rows, d)))
+      return KV_ERR_ALIAS;
+  }
   if (N == 0) return KV_OK;
   kvq::QuantizeLaunch p{x, static_cast<int>(xdt), B, H, N, d, dst->codes, static_cast<float *>(dst->scale),
                         static_cast<float *>(dst->zero), dst->bits, dst->group, dst->cap, tok_offset,
@@ -326,6 +358,7 @@ kv_status kv_attention_corrected(const kv_attn_args *a, void *stream) {
   const Plan pl = plan_attention(a, true);
   if (pl.workspace > 0 && (!a->workspace || a->workspace_bytes < pl.workspace)) return KV_ERR_WORKSPACE;
   if (pl.workspace > 0 && !aligned16(a->workspace)) return KV_ERR_ALIGN;
+  if (pl.workspace > 0 && overlaps_call(a, a->workspace, pl.workspace)) return KV_ERR_ALIAS;
 
   AttnLaunch p{};
   p.B = a->B; p.Hq = a->Hq; p.Hkv = a->Hkv; p.Nq = a->Nq; p.Ncur = a->Ncur; p.Nc = a->Nc; p.d = a->d;

@@ -53,6 +53,24 @@ __device__ inline float sum8h(f16x8 v, float acc) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w.w), one, acc, false);
 }
 
+// Centre of a cached key group for the fp16 key operand.  When the group's
+// code range [z, z + (2^bits - 1) D] lies on one side of zero (its values
+// share an offset), the centre is the range's midpoint rounded to bf16,
+// else 0.  The kernels round z - centre + D c (not z + D c) to fp16, so that
+// the rounding error of offset groups scales with their half range rather
+// than with |k|, and add the centre back through the extra bf16 MFMA step as
+// centre x (sum of the query over the group): a bf16 centre times the bf16
+// (hi, lo) parts of the query sum is exact in the fp32 accumulator.  Keys
+// far from zero (a large shared mean, logits far from zero) would otherwise
+// lose the scores' low bits to fp16 rounding.  A range around zero keeps
+// centre 0: a group mixing small channels with large ones would have its
+// small values moved away from zero by a midpoint.
+template <int BITS>
+__device__ inline float group_centre(float z, float step) {
+  const float top = fmaf(static_cast<float>((1 << BITS) - 1), step, z);
+  return z > 0.f || top < 0.f ? lo_f(pack2(fmaf(static_cast<float>((1 << BITS) - 1) * 0.5f, step, z), 0.f)) : 0.f;
+}
+
 // Codes as fp16 "magic" values 1024 + c (exact: the fp16 spacing at 1024 is
 // 1), built two at a time: m[j] holds codes j (low half) and j + 4 (high
 // half) of 8 codes of BITS bits stored LSB first in the low 8*BITS bits of
@@ -134,29 +152,35 @@ __device__ inline void pin(T &x) {
 // resulting scores (alpha = tau log2(e) 2^(eq+ek) for keys scaled by 2^-ek),
 // and the Taylor correction operands N_g = tau/24 ||q_g||^2 2^-(eq+ek) in
 // slots 4g+{0,1,2,3} as (hi, hi, lo, 0) split into bf16 (the lane holds
-// slots 8h .. 8h+7, i.e. groups 2h and 2h+1; zero when not TAYLOR).  The
+// slots 8h .. 8h+7, i.e. groups 2h and 2h+1; zero when not TAYLOR).  With
+// at most two groups, lane half 1 holds instead the group sums
+// S_g = sum_{c in g} q_c 2^-eq as (S_hi, S_lo) in slots 8 + 4g, 9 + 4g, which
+// the centres of centred cached keys multiply (see group_centre).  The
 // row's other half sits in lane l^32.
 template <bool TAYLOR, bool HALVES = false>
 __device__ inline void load_query(const uint16_t *qptr, int h, int group_shift, float tau, int ek, f16x8 (&q)[8],
                                   bf16x8 &qext, float &alpha) {
   const int ng = 128 >> group_shift;
   uint4 qw[8];
-  float nsum[4] = {0.f, 0.f, 0.f, 0.f};
+  float nsum[4] = {0.f, 0.f, 0.f, 0.f}, qsum[2] = {0.f, 0.f};
   float qmax = 0.f;
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     const int d0 = HALVES ? 64 * h + 8 * s : 16 * s + 8 * h;
     qw[s] = *reinterpret_cast<const uint4 *>(qptr + d0);
     const uint32_t u[4] = {qw[s].x, qw[s].y, qw[s].z, qw[s].w};
-    float acc = 0.f;
+    float acc = 0.f, sum = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       acc += lo_f(u[i]) * lo_f(u[i]) + hi_f(u[i]) * hi_f(u[i]);
+      sum += lo_f(u[i]) + hi_f(u[i]);
       qmax = fmaxf(qmax, fmaxf(fabsf(lo_f(u[i])), fabsf(hi_f(u[i]))));
     }
     const int gs = d0 >> group_shift;
 #pragma unroll
     for (int g = 0; g < 4; ++g) nsum[g] += g == gs ? acc : 0.f;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) qsum[g] += g == gs ? sum : 0.f;
   }
   qmax = fmaxf(qmax, __shfl_xor(qmax, 32, 64));
   const int eq = scale_exponent(qmax);
@@ -177,6 +201,17 @@ __device__ inline void load_query(const uint16_t *qptr, int h, int group_shift, 
     const float n = TAYLOR && g < ng ? (nsum[g] + __shfl_xor(nsum[g], 32, 64)) * (tau / 24.0f) / unscale : 0.f;
     nh[g] = lo_f(pack2(n, 0.f));
     nl[g] = n - nh[g];
+  }
+  float sh[2], sl[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const float t = (qsum[g] + __shfl_xor(qsum[g], 32, 64)) * qs_scale;
+    sh[g] = g < ng ? lo_f(pack2(t, 0.f)) : 0.f;
+    sl[g] = g < ng ? t - sh[g] : 0.f;
+  }
+  if (h == 1 && ng <= 2) {
+    qext = __builtin_bit_cast(bf16x8, make_uint4(pack2(sh[0], sl[0]), 0u, pack2(sh[1], sl[1]), 0u));
+    return;
   }
   const float n0h = h ? nh[2] : nh[0], n0l = h ? nl[2] : nl[0];
   const float n1h = h ? nh[3] : nh[1], n1l = h ? nl[3] : nl[1];

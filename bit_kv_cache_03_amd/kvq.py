@@ -102,6 +102,15 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _keep_for(t, stream) -> None:
+    """A tensor allocated here from the current stream's pool but used by work
+    enqueued on another `stream`: tell the caching allocator, so that its
+    memory is not handed out again before that work has finished."""
+    import torch
+    if stream is not None and stream != torch.cuda.current_stream(t.device):
+        t.record_stream(stream)
+
+
 class QCache:
     """A quantized cache tensor (K or V): codes, step and zero-point on the GPU.
 
@@ -205,10 +214,12 @@ def attention(q, k_cur, v_cur, k_cache: Optional[QCache], v_cache: Optional[QCac
     import torch
     if out is None:
         out = torch.empty_like(q)
+        _keep_for(out, stream)
     args = make_args(q, k_cur, v_cur, k_cache, v_cache, nc, out, corr, scale, path, splits, workspace, causal)
     need = workspace_size(args)
     if need > 0 and (workspace is None or args.workspace_bytes < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        _keep_for(workspace, stream)
         args.workspace, args.workspace_bytes = workspace.data_ptr(), need
     _check(lib.kv_attention_corrected(C.byref(args), _stream(stream)), "kv_attention_corrected")
     return out
@@ -244,6 +255,7 @@ def diagnostics(q, k_cur, k_ref, k_cache: Optional[QCache], nc: int, corr: str =
     B, Hq, Nq, _ = q.shape
     if out is None:
         out = torch.empty((B * Hq * Nq, DIAG_ROW_WORDS), dtype=torch.int32, device=q.device)
+        _keep_for(out, stream)
     args = make_diag_args(q, k_cur, k_ref, k_cache, nc, out, corr, scale, causal)
     _check(lib.kv_attention_diagnostics(C.byref(args), _stream(stream)), "kv_attention_diagnostics")
     return out

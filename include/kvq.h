@@ -52,7 +52,7 @@ typedef enum {
   KV_ERR_UNSUPPORTED = 3, /* valid but not implemented (bits, group, d, path) */
   KV_ERR_WORKSPACE = 4,   /* workspace missing or too small */
   KV_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned */
-  KV_ERR_ALIAS = 6,       /* the output overlaps an input */
+  KV_ERR_ALIAS = 6,       /* an output or the workspace overlaps an input (or each other) */
   KV_ERR_HIP = 7          /* a HIP runtime call or launch failed */
 } kv_status;
 
@@ -145,8 +145,10 @@ typedef struct {
  * group does not divide N (quantised over the tokens it has; it cannot be
  * extended later: the next call starts at the next multiple of group).
  * Errors: KV_ERR_NULL, KV_ERR_SHAPE (tok_offset + N > cap, tok_offset not a
- * multiple of a token group, ...), KV_ERR_UNSUPPORTED (bits, group, d, axis),
- * KV_ERR_ALIGN, KV_ERR_HIP.
+ * multiple of a token group, ...), KV_ERR_UNSUPPORTED (bits, group, d, axis,
+ * cap above 2^23 tokens: no attention call would accept the cache),
+ * KV_ERR_ALIGN, KV_ERR_ALIAS (x overlaps the cache's codes, steps or zero
+ * points), KV_ERR_HIP.
  */
 kv_status kv_quantize(const void *x, kv_dtype xdt, int64_t B, int64_t H, int64_t N, int32_t d,
                       const kv_qtensor *dst, int64_t tok_offset, void *stream);
@@ -209,7 +211,8 @@ size_t kv_attention_workspace_size(const kv_attn_args *a);
  * value product all inside the kernel).
  * Errors: KV_ERR_NULL, KV_ERR_SHAPE (also: causal with Nc = 0 and
  * Nq > Ncur), KV_ERR_UNSUPPORTED (also: causal not 0 or 1), KV_ERR_WORKSPACE,
- * KV_ERR_ALIGN, KV_ERR_ALIAS, KV_ERR_HIP.
+ * KV_ERR_ALIGN, KV_ERR_ALIAS (out overlaps an input, or the bytes of the
+ * workspace the call uses overlap out, an input or a page table), KV_ERR_HIP.
  */
 kv_status kv_attention_corrected(const kv_attn_args *a, void *stream);
 

@@ -250,6 +250,36 @@ def test_quantize_argument_errors(kvq):
     assert q(A, 0, 1, 2, 0, 128, C.byref(good), 64, None) == kvq.KV_OK
 
 
+def test_quantize_cap_and_overlap(kvq):
+    """A cache larger than any attention call accepts (2^23 tokens per head)
+    is refused at append time too, and the input may not overlap the codes,
+    steps or zero points it is written into (x is 1*2*8*128 bf16 = 4 KiB)."""
+    q = kvq.lib.kv_quantize
+    big = _qt(kvq, 0x30000000, bits=4, group=64, cap=(1 << 23) + 64)
+    assert q(A, 0, 1, 2, 8, 128, C.byref(big), 0, None) == kvq.KV_ERR_UNSUPPORTED
+    c = _qt(kvq, 0x30000000, bits=4, group=64, cap=64)  # codes 8 KiB, steps / zeros 1 KiB each
+    for x in (0x30000000 + 4096, 0x30000000 - 2048, 0x30100000 + 512, 0x30200000 - 4080):
+        assert q(x, 0, 1, 2, 8, 128, C.byref(c), 0, None) == kvq.KV_ERR_ALIAS, hex(x)
+    assert q(0x30000000 - 4096 - 16, 1, 1, 2, 8, 128, C.byref(c), 0, None) == kvq.KV_ERR_ALIAS  # fp32: 8 KiB
+
+
+@pytest.mark.parametrize("where", ["out", "q", "k_cur", "v_cur", "k_codes", "v_scale", "page_table"])
+def test_workspace_overlap(kvq, where):
+    """The bytes of the workspace a call uses may not overlap its output,
+    an input or a page table."""
+    a = _args(kvq, path=2)
+    if where == "page_table":
+        a._k = _paged(kvq, 0x10000000)
+        a._v = _paged(kvq, 0x20000000)
+        a.k_cache, a.v_cache = C.pointer(a._k), C.pointer(a._v)
+    need = kvq.lib.kv_attention_workspace_size(C.byref(a))
+    assert need > 0
+    at = {"out": 4 * A, "q": A - need + 16, "k_cur": 2 * A + 256, "v_cur": 3 * A, "k_codes": 0x10000000 + 4096,
+          "v_scale": 0x20100000 - need + 16, "page_table": 0x7000000 - 16}[where]
+    a.workspace, a.workspace_bytes = at, need
+    assert _attn(kvq, a) == kvq.KV_ERR_ALIAS
+
+
 def _dargs(kvq, **kw):
     a = kvq.DiagArgs()
     a.B, a.Hq, a.Hkv, a.Nq, a.Ncur, a.Nc, a.d, a.corr = 1, 4, 2, 8, 8, 50, 128, 1

@@ -33,3 +33,18 @@ def test_flops_and_bytes_of_the_default_workload():
     assert bench.packed_bytes(w, 2) == 24 * 16384 * 144
     # K grouped along the tokens (group 64): 2 x 128 fp32 values per 64 tokens (16 bytes per token)
     assert bench.packed_bytes(w, 4, "tokens", "dim") == 24 * 16384 * 128 + 24 * 256 * 2 * 128 * 4 + 24 * 16384 * 16
+
+
+def test_default_workload_is_the_largest_single_gpu_one():
+    """The timed default is the workload with the most algorithmic flops."""
+    flops = {n: bench.attention_flops(w) for n, w in W.WORKLOADS.items()}
+    assert bench.DEFAULT_WORKLOAD == max(flops, key=flops.get) == "gqa_prefill_b16_cache32k"
+    assert bench.MALL_EVICT_BYTES >= 512 << 20
+
+
+def test_dtype_names_the_arithmetic_of_the_kernel():
+    w = W.WORKLOADS["gqa_prefill_b16_cache32k"]
+    assert bench.arithmetic(w, "taylor", 0, "dim", "dim")["dtype"] == "fp16"
+    assert bench.arithmetic(w, "exact", 0, "dim", "dim")["dtype"] == "bf16"
+    assert bench.arithmetic(w, "taylor", 0, "tokens", "dim")["dtype"] == "bf16"
+    assert bench.arithmetic(W.WORKLOADS["tiny_d64_int2"], "off", 0, "dim", "dim")["dtype"] == "bf16"
