@@ -162,26 +162,55 @@ def arithmetic(w, corr: str, page_size: int, kaxis: str, vaxis: str) -> dict:
                             "accumulation and softmax; bf16 inputs and outputs"}
 
 
-def gpu_clocks():
-    """Current shader (sclk) and memory (mclk) clocks of the GPU this process
-    uses (amdsmi, matched by PCI address), or None where unavailable."""
-    try:
-        import amdsmi
-        import torch
-        pr = torch.cuda.get_device_properties(torch.cuda.current_device())
-        bdf = "%04x:%02x:%02x.0" % (pr.pci_domain_id, pr.pci_bus_id, pr.pci_device_id)
-        amdsmi.amdsmi_init()
+class ClockProbe:
+    """Shader (sclk) and memory (mclk) clocks of the GPU this process uses
+    (amdsmi, matched by PCI address).  Opened before the timed steps, so that
+    sample() costs little and lands while the enqueued steps still run; the
+    record is informative only (None fields where amdsmi is unavailable)."""
+
+    def __init__(self):
+        self.h, self.err = None, None
         try:
-            h = amdsmi.amdsmi_get_processor_handle_from_bdf(bdf)
-            g = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.SYS)
-            m = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.MEM)
-            return {"sclk_mhz": g.get("clk"), "sclk_max_mhz": g.get("max_clk"), "mclk_mhz": m.get("clk"),
-                    "mclk_max_mhz": m.get("max_clk"), "bdf": bdf, "source": "amdsmi, sampled while the timed "
-                                                                            "steps ran"}
-        finally:
-            amdsmi.amdsmi_shut_down()
-    except Exception as e:  # the record is informative only
-        return {"error": f"{type(e).__name__}: {e}"}
+            import amdsmi
+            import torch
+            pr = torch.cuda.get_device_properties(torch.cuda.current_device())
+            self.bdf = "%04x:%02x:%02x.0" % (pr.pci_domain_id, pr.pci_bus_id, pr.pci_device_id)
+            amdsmi.amdsmi_init()
+            self.amdsmi = amdsmi
+            self.h = amdsmi.amdsmi_get_processor_handle_from_bdf(self.bdf)
+        except Exception as e:
+            self.err = f"{type(e).__name__}: {e}"
+
+    def sample(self, done):
+        """Poll the clocks every ~2 ms until done() (the timed steps have
+        finished); the median and the largest reading of each."""
+        if self.h is None:
+            return {"error": self.err}
+        try:
+            a = self.amdsmi
+            gs, ms = [], []
+            while True:
+                finished = done()
+                gs.append(a.amdsmi_get_clock_info(self.h, a.AmdSmiClkType.SYS))
+                ms.append(a.amdsmi_get_clock_info(self.h, a.AmdSmiClkType.MEM))
+                if finished or len(gs) >= 2000:
+                    break
+                time.sleep(0.002)
+            g = [x.get("clk") for x in gs if isinstance(x.get("clk"), (int, float))]
+            m = [x.get("clk") for x in ms if isinstance(x.get("clk"), (int, float))]
+            return {"sclk_mhz_median": float(np.median(g)) if g else None, "sclk_mhz_max": max(g) if g else None,
+                    "sclk_max_mhz": gs[0].get("max_clk"), "mclk_mhz_median": float(np.median(m)) if m else None,
+                    "mclk_max_mhz": ms[0].get("max_clk"), "samples": len(gs), "bdf": self.bdf,
+                    "source": "amdsmi, polled every ~2 ms from the enqueue of the timed steps to their end"}
+        except Exception as e:
+            return {"error": f"{type(e).__name__}: {e}"}
+
+    def close(self):
+        if self.h is not None:
+            try:
+                self.amdsmi.amdsmi_shut_down()
+            except Exception:
+                pass
 
 
 def copy_probe(nbytes: int, reps: int = 3):
@@ -406,6 +435,7 @@ def main():
     s_end = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    probe = ClockProbe()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
@@ -415,8 +445,9 @@ def main():
         step(args_c, evs[i])
         s_end[i].record(stream)
     t_end.record(stream)
-    clocks = gpu_clocks()  # the steps above are still running: launches are asynchronous
+    clocks = probe.sample(t_end.query)  # the steps above are still running: launches are asynchronous
     torch.cuda.synchronize()
+    probe.close()
     wall = time.perf_counter() - wall0
     if scratch is None:
         ms_step = t_start.elapsed_time(t_end) / args.steps
