@@ -5,13 +5,15 @@
 #include <stdlib.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "kvq_internal.h"
 
 namespace {
 
 using kvq::AttnLaunch;
 
-constexpr int32_t kAbiVersion = 6;
+constexpr int32_t kAbiVersion = 7;
 constexpr int32_t kMaxSplits = 1024;  // grid z extent of the split path
 constexpr int64_t kMaxTokensPerHead = int64_t(1) << 23;  // 8M tokens: 32-bit in-head offsets
 
@@ -255,7 +257,31 @@ kv_status validate_diagnostics(const kv_diag_args *a) {
   return KV_OK;
 }
 
-Plan plan_attention(const kv_attn_args *a, bool query_device) {
+// Scratch of kv_attention_corrected_static: one copy per device, addressed
+// only through the pointer hipGetSymbolAddress returns for that device.
+constexpr size_t kScratchBytes = KV_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+
+// Device address of the current device's scratch array (nullptr on failure),
+// looked up on the first call per device and kept.
+void *scratch_ptr() {
+  static std::mutex mu;
+  static void *ptrs[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    ptrs[dev] = p;
+  }
+  return ptrs[dev];
+}
+
+// `limit`: most workspace bytes the caller can give; an automatic split
+// count is lowered to fit it where possible (a forced one is kept).
+Plan plan_attention(const kv_attn_args *a, bool query_device, size_t limit = SIZE_MAX) {
   Plan pl{KV_PATH_LONG, 0, 0, 0};
   const int64_t rows = a->Nq * (a->Hq / a->Hkv);
   int path = a->path;
@@ -263,16 +289,31 @@ Plan plan_attention(const kv_attn_args *a, bool query_device) {
   pl.path = path;
   if (path == KV_PATH_SHORT) {
     const int cus = query_device ? device_cu_count() : 256;
-    if (kvq::short_fast_supported(a->d, a->corr, tokens_axis(a), cache_page_size(a))) {
-      pl.splits = a->splits > 0 ? a->splits : kvq::short_fast_splits(a->B, a->Hkv, rows, a->Nc, a->Ncur, cus);
-      pl.workspace = kvq::short_path_workspace_bytes(a->B, a->Hq, a->Nq, a->d, pl.splits);
-    } else {
-      pl.splits = a->splits > 0 ? a->splits : kvq::short_path_splits(a->B, a->Hkv, rows, a->Nc, cus);
-      pl.workspace = kvq::general_path_workspace_bytes(a->B, a->Hq, a->Hkv, a->Nq, a->d, pl.splits, true);
+    const bool fast = kvq::short_fast_supported(a->d, a->corr, tokens_axis(a), cache_page_size(a));
+    auto bytes = [&](int s) {
+      return fast ? kvq::short_path_workspace_bytes(a->B, a->Hq, a->Nq, a->d, s)
+                  : kvq::general_path_workspace_bytes(a->B, a->Hq, a->Hkv, a->Nq, a->d, s, true);
+    };
+    pl.splits = a->splits > 0 ? a->splits
+                : fast        ? kvq::short_fast_splits(a->B, a->Hkv, rows, a->Nc, a->Ncur, cus)
+                              : kvq::short_path_splits(a->B, a->Hkv, rows, a->Nc, cus);
+    pl.workspace = bytes(pl.splits);
+    if (pl.workspace > limit && a->splits == 0) {  // the partials grow linearly with the split count
+      const size_t fixed = bytes(1) - kvq::short_path_workspace_bytes(a->B, a->Hq, a->Nq, a->d, 1);
+      const size_t per = kvq::short_path_workspace_bytes(a->B, a->Hq, a->Nq, a->d, 1);
+      const size_t fit = limit > fixed && per > 0 ? (limit - fixed) / per : 0;
+      pl.splits = static_cast<int>(fit < 1 ? 1 : fit < static_cast<size_t>(pl.splits) ? fit : pl.splits);
+      while (pl.splits > 1 && bytes(pl.splits) > limit) --pl.splits;  // rounding of the general layout
+      pl.workspace = bytes(pl.splits);
     }
   } else if (kvq::fast_kernel_ok(a->d, a->corr, tokens_axis(a), cache_page_size(a))) {  // split-K when it balances
     const int cus = query_device ? device_cu_count() : 256;
-    const kvq::FastPlan fp = kvq::fast_path_plan(a->B, a->Hq, a->Hkv, a->Nq, a->Nc, a->Ncur, cus, a->splits);
+    kvq::FastPlan fp = kvq::fast_path_plan(a->B, a->Hq, a->Hkv, a->Nq, a->Nc, a->Ncur, cus, a->splits);
+    if (a->splits == 0 && fp.splits > 1 &&
+        kvq::fast_path_workspace_bytes(a->B, a->Hq, a->Hkv, a->Nq, fp.splits) > limit) {
+      const int64_t units = (a->Nq * (a->Hq / a->Hkv) + 255) / 256 * a->B * a->Hkv;
+      fp = kvq::FastPlan{1, units};  // no key-range split: no partials
+    }
     pl.splits = fp.splits;
     pl.full_units = fp.full_units;
     pl.workspace = kvq::fast_path_workspace_bytes(a->B, a->Hq, a->Hkv, a->Nq, pl.splits);
@@ -296,6 +337,7 @@ const char *kv_status_string(kv_status s) {
     case KV_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case KV_ERR_ALIAS: return "an output or the workspace overlaps an input";
     case KV_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+    case KV_ERR_SCRATCH: return "the call needs more scratch than the library's static array holds";
   }
   return "unknown status";
 }
@@ -352,14 +394,12 @@ size_t kv_attention_workspace_size(const kv_attn_args *a) {
   return plan_attention(a, true).workspace;
 }
 
-kv_status kv_attention_corrected(const kv_attn_args *a, void *stream) {
-  const kv_status v = validate_attention(a);
-  if (v != KV_OK) return v;
-  const Plan pl = plan_attention(a, true);
-  if (pl.workspace > 0 && (!a->workspace || a->workspace_bytes < pl.workspace)) return KV_ERR_WORKSPACE;
-  if (pl.workspace > 0 && !aligned16(a->workspace)) return KV_ERR_ALIGN;
-  if (pl.workspace > 0 && overlaps_call(a, a->workspace, pl.workspace)) return KV_ERR_ALIAS;
+}  // extern "C"
 
+namespace {
+
+// Launches a validated call with its plan and workspace.
+kv_status launch_attention(const kv_attn_args *a, const Plan &pl, void *workspace, void *stream) {
   AttnLaunch p{};
   p.B = a->B; p.Hq = a->Hq; p.Hkv = a->Hkv; p.Nq = a->Nq; p.Ncur = a->Ncur; p.Nc = a->Nc; p.d = a->d;
   p.q = static_cast<const uint16_t *>(a->q);
@@ -386,7 +426,7 @@ kv_status kv_attention_corrected(const kv_attn_args *a, void *stream) {
   p.causal = a->causal;
   p.splits = pl.splits;
   p.fast_full_units = pl.full_units;
-  p.workspace = a->workspace;
+  p.workspace = workspace;
   if (debug_log())
     fprintf(stderr, "kvq: attention path=%s rows/kvhead=%lld splits=%d full_units=%lld workspace=%zu corr=%d\n",
             pl.path == KV_PATH_SHORT ? "short" : "long", static_cast<long long>(a->Nq * (a->Hq / a->Hkv)),
@@ -394,6 +434,30 @@ kv_status kv_attention_corrected(const kv_attn_args *a, void *stream) {
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = pl.path == KV_PATH_SHORT ? kvq::launch_attention_short(p, s) : kvq::launch_attention_long(p, s);
   return e == hipSuccess ? KV_OK : KV_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+kv_status kv_attention_corrected(const kv_attn_args *a, void *stream) {
+  const kv_status v = validate_attention(a);
+  if (v != KV_OK) return v;
+  const Plan pl = plan_attention(a, true);
+  if (pl.workspace > 0 && (!a->workspace || a->workspace_bytes < pl.workspace)) return KV_ERR_WORKSPACE;
+  if (pl.workspace > 0 && !aligned16(a->workspace)) return KV_ERR_ALIGN;
+  if (pl.workspace > 0 && overlaps_call(a, a->workspace, pl.workspace)) return KV_ERR_ALIAS;
+  return launch_attention(a, pl, a->workspace, stream);
+}
+
+kv_status kv_attention_corrected_static(const kv_attn_args *a, void *stream) {
+  const kv_status v = validate_attention(a);
+  if (v != KV_OK) return v;
+  const Plan pl = plan_attention(a, true, kScratchBytes);
+  if (pl.workspace > kScratchBytes) return KV_ERR_SCRATCH;
+  void *ws = nullptr;
+  if (pl.workspace > 0 && !(ws = scratch_ptr())) return KV_ERR_HIP;
+  return launch_attention(a, pl, ws, stream);
 }
 
 kv_status kv_attention_diagnostics(const kv_diag_args *a, void *stream) {

@@ -15,13 +15,15 @@ from typing import Optional
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvq.so")
 
-KV_OK, KV_ERR_NULL, KV_ERR_SHAPE, KV_ERR_UNSUPPORTED, KV_ERR_WORKSPACE, KV_ERR_ALIGN, KV_ERR_ALIAS, KV_ERR_HIP = range(8)
+(KV_OK, KV_ERR_NULL, KV_ERR_SHAPE, KV_ERR_UNSUPPORTED, KV_ERR_WORKSPACE, KV_ERR_ALIGN, KV_ERR_ALIAS, KV_ERR_HIP,
+ KV_ERR_SCRATCH) = range(9)
+STATIC_SCRATCH_BYTES = 64 << 20  # KV_STATIC_SCRATCH_BYTES
 KV_BF16, KV_F32 = 0, 1
 CORR = {"off": 0, "taylor": 1, "exact": 2}
 PATH = {"auto": 0, "long": 1, "short": 2}
 
 EXPORTED = ("kv_quantize", "kv_attention_workspace_size", "kv_attention_corrected",
-            "kv_attention_diagnostics", "kv_status_string", "kv_version")
+            "kv_attention_corrected_static", "kv_attention_diagnostics", "kv_status_string", "kv_version")
 
 
 class QTensor(C.Structure):
@@ -70,6 +72,8 @@ def _load():
     L.kv_attention_workspace_size.restype = C.c_size_t
     L.kv_attention_corrected.argtypes = [C.POINTER(AttnArgs), C.c_void_p]
     L.kv_attention_corrected.restype = C.c_int
+    L.kv_attention_corrected_static.argtypes = [C.POINTER(AttnArgs), C.c_void_p]
+    L.kv_attention_corrected_static.restype = C.c_int
     L.kv_attention_diagnostics.argtypes = [C.POINTER(DiagArgs), C.c_void_p]
     L.kv_attention_diagnostics.restype = C.c_int
     L.kv_status_string.argtypes = [C.c_int]

@@ -53,7 +53,9 @@ typedef enum {
   KV_ERR_WORKSPACE = 4,   /* workspace missing or too small */
   KV_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned */
   KV_ERR_ALIAS = 6,       /* an output or the workspace overlaps an input (or each other) */
-  KV_ERR_HIP = 7          /* a HIP runtime call or launch failed */
+  KV_ERR_HIP = 7,         /* a HIP runtime call or launch failed */
+  KV_ERR_SCRATCH = 8      /* kv_attention_corrected_static: the call needs more scratch
+                             than KV_STATIC_SCRATCH_BYTES */
 } kv_status;
 
 typedef enum { KV_BF16 = 0, KV_F32 = 1 } kv_dtype;
@@ -215,6 +217,31 @@ size_t kv_attention_workspace_size(const kv_attn_args *a);
  * workspace the call uses overlap out, an input or a page table), KV_ERR_HIP.
  */
 kv_status kv_attention_corrected(const kv_attn_args *a, void *stream);
+
+/* Bytes of the static device scratch array of kv_attention_corrected_static
+ * (one copy per GPU the library runs on, held until the process ends). */
+#define KV_STATIC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * kv_attention_corrected_static -- kv_attention_corrected for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  The same computation and kernels;
+ * a->workspace and a->workspace_bytes are ignored and the scratch is a
+ * file-scope device array of KV_STATIC_SCRATCH_BYTES in the library.  The
+ * call allocates and frees nothing (its device address is looked up once
+ * per GPU, on the first call with that GPU current).
+ *  - Splits chosen automatically (a->splits = 0) are lowered where the
+ *    partials of the usual choice would not fit the array; a forced split
+ *    count, or a call whose scratch does not fit even unsplit, returns
+ *    KV_ERR_SCRATCH (kv_attention_workspace_size() reports what
+ *    kv_attention_corrected would use).
+ *  - Every call on one GPU uses that GPU's one array, and the scratch needs
+ *    no initialisation: calls on one stream are safe, calls that may overlap
+ *    in time on one GPU (other streams, other host threads) race.
+ * Errors: those of kv_attention_corrected except KV_ERR_WORKSPACE, and
+ * KV_ERR_SCRATCH; KV_ERR_HIP also when the array's address cannot be found.
+ */
+kv_status kv_attention_corrected_static(const kv_attn_args *a, void *stream);
 
 /*
  * Attention-balance diagnostics ("量化鍵值偷走注意力…" (agents-report.net),

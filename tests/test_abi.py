@@ -35,8 +35,8 @@ def test_exports_every_declared_symbol(kvq):
 
 
 def test_version_and_status_strings(kvq):
-    assert kvq.lib.kv_version() == 6
-    for s in range(1, 8):
+    assert kvq.lib.kv_version() == 7
+    for s in range(1, 9):
         assert len(kvq.lib.kv_status_string(s)) > 10
     assert kvq.lib.kv_status_string(0) == b"ok"
     assert b"unknown" in kvq.lib.kv_status_string(99)
@@ -95,7 +95,7 @@ def test_enum_values_match_header(kvq, tmp_path):
     """Every enum the binding mirrors has the header's values."""
     prog = tmp_path / "enums.c"
     names = ["KV_OK", "KV_ERR_NULL", "KV_ERR_SHAPE", "KV_ERR_UNSUPPORTED", "KV_ERR_WORKSPACE", "KV_ERR_ALIGN",
-             "KV_ERR_ALIAS", "KV_ERR_HIP", "KV_BF16", "KV_F32", "KV_CORR_OFF", "KV_CORR_TAYLOR", "KV_CORR_EXACT",
+             "KV_ERR_ALIAS", "KV_ERR_HIP", "KV_ERR_SCRATCH", "KV_BF16", "KV_F32", "KV_CORR_OFF", "KV_CORR_TAYLOR", "KV_CORR_EXACT",
              "KV_PATH_AUTO", "KV_PATH_LONG", "KV_PATH_SHORT", "KV_META_F32", "KV_META_F16", "KV_AXIS_DIM",
              "KV_AXIS_TOKENS"]
     prog.write_text('#include <stdio.h>\n#include "kvq.h"\nint main(void) {\n' +
@@ -104,7 +104,7 @@ def test_enum_values_match_header(kvq, tmp_path):
     subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(prog), "-o", str(exe)], check=True)
     got = dict(l.split(" ") for l in subprocess.run([str(exe)], capture_output=True, text=True,
                                                        check=True).stdout.split("\n") if l)
-    want = {n: getattr(kvq, n) for n in names[:10]}
+    want = {n: getattr(kvq, n) for n in names[:11]}
     want.update({f"KV_CORR_{k.upper()}": v for k, v in kvq.CORR.items()})
     want.update({f"KV_PATH_{k.upper()}": v for k, v in kvq.PATH.items()})
     want.update({f"KV_META_{k.upper()}": v for k, v in kvq.META.items()})
@@ -451,3 +451,24 @@ def test_attention_paged_layouts_must_match(kvq):
     a._v = _qt(kvq, 0x20000000, cap=256)  # contiguous V with paged K
     a.v_cache = C.pointer(a._v)
     assert _attn(kvq, a) == kvq.KV_ERR_UNSUPPORTED
+
+
+def test_static_entry_scratch_limit(kvq):
+    """kv_attention_corrected_static: the same argument errors as the
+    workspace entry point, and KV_ERR_SCRATCH (before any HIP call) when a
+    forced split count needs more scratch than the static array; the
+    header's size and the binding's agree."""
+    assert kvq.STATIC_SCRATCH_BYTES == 64 << 20
+    src = open(HEADER).read()
+    assert re.search(r"#define KV_STATIC_SCRATCH_BYTES \(64u << 20\)", src)
+    st = kvq.lib.kv_attention_corrected_static
+    for name, kw, err in CASES:
+        assert st(C.byref(_args(kvq, **kw)), None) == getattr(kvq, err), name
+    # 64 x 64 heads x 64 rows: 128 MiB of partials per split on the short path
+    G = 1 << 40
+    a = _args(kvq, B=64, Hq=64, Hkv=64, Nq=64, Ncur=64, path=2, splits=2, q=G, k_cur=2 * G, v_cur=3 * G, out=4 * G)
+    a._k = _qt(kvq, 5 * G)
+    a._v = _qt(kvq, 6 * G)
+    a.k_cache, a.v_cache = C.pointer(a._k), C.pointer(a._v)
+    assert kvq.lib.kv_attention_workspace_size(C.byref(a)) > kvq.STATIC_SCRATCH_BYTES
+    assert st(C.byref(a), None) == kvq.KV_ERR_SCRATCH
