@@ -231,12 +231,14 @@ __device__ inline void query_operands(const uint16_t *qptr, int h, float scale, 
 }
 
 // The lane's query operands for the cached keys (query_operands with 2^ek)
-// and the extra step's query slots: in lane half 0, slots 4g+{0,1,2,3} =
-// (N_hi, N_hi, N_lo, -m) with N_g = tau^2/24 log2(e) ||q_g||^2 split into bf16
-// (zero without the correction; groups 0 and 1, m = 0 at the start); in lane
-// half 1, with 4 groups the same for groups 2 and 3, else the centre slots
-// 8 + 4g, 9 + 4g = (S_hi, S_lo) with S_g = tau log2(e) sum_{c in g} q_c, which
-// the cached keys' group centres multiply.
+// and the extra step's query slots, matching the key slots of unpack_k_item:
+// N_g = tau^2/24 log2(e) ||q_g||^2 split into bf16 (N_hi, N_hi, N_lo) against
+// (-D_hi, -D_lo, -D_hi), zero without the correction; -m split (hi, lo) in
+// slots 3 and 7 (lane half 0; m = 0 at the start); S_g = tau log2(e)
+// sum_{c in g} q_c split (S_hi, S_lo) against the centre c_g twice.  Lane
+// half h holds slots 8h .. 8h+7: with two groups group h, (N, N, N, max,
+// S, S, 0, max); with four groups 2h and 2h+1, (N, N, N, max, N, N, N, max);
+// with one group (half 0) (N, N, N, max, S, S, 0, max).
 template <bool TAYLOR>
 __device__ inline void load_query_folded(const uint16_t *qptr, int h, int group_shift, float tau, int ek,
                                          QState &qs) {
@@ -274,13 +276,16 @@ __device__ inline void load_query_folded(const uint16_t *qptr, int h, int group_
     sh[g] = g < ng ? lo_f(pack2(t, 0.f)) : 0.f;
     sl[g] = g < ng ? t - sh[g] : 0.f;
   }
-  if (h == 1 && ng <= 2) {
-    qs.qext = __builtin_bit_cast(bf16x8, make_uint4(pack2(sh[0], sl[0]), 0u, pack2(sh[1], sl[1]), 0u));
-    return;
+  if (ng == 4) {
+    const float n0h = h ? nh[2] : nh[0], n0l = h ? nl[2] : nl[0];
+    const float n1h = h ? nh[3] : nh[1], n1l = h ? nl[3] : nl[1];
+    qs.qext = __builtin_bit_cast(bf16x8, make_uint4(pack2(n0h, n0h), pack2(n0l, 0.f), pack2(n1h, n1h), pack2(n1l, 0.f)));
+  } else {  // group h (one group: half 1 empty)
+    const bool on = h < ng;
+    const float gh = on ? (h ? nh[1] : nh[0]) : 0.f, gl = on ? (h ? nl[1] : nl[0]) : 0.f;
+    const float th = on ? (h ? sh[1] : sh[0]) : 0.f, tl = on ? (h ? sl[1] : sl[0]) : 0.f;
+    qs.qext = __builtin_bit_cast(bf16x8, make_uint4(pack2(gh, gh), pack2(gl, 0.f), pack2(th, tl), 0u));
   }
-  const float n0h = h ? nh[2] : nh[0], n0l = h ? nl[2] : nl[0];
-  const float n1h = h ? nh[3] : nh[1], n1l = h ? nl[3] : nl[1];
-  qs.qext = __builtin_bit_cast(bf16x8, make_uint4(pack2(n0h, n0h), pack2(n0l, 0.f), pack2(n1h, n1h), pack2(n1l, 0.f)));
 }
 
 // Packed data of one tile held in registers between the fetch and the unpack.
@@ -288,7 +293,6 @@ struct Fetch {
   uint32_t kw[8];   // K: codes of 16 values (cached) or 16 bf16 values (current)
   uint32_t vw[8];   // V: codes of 2 keys x 8 values (cached) or 2 x 8 bf16 (current)
   float kstep, kzero;
-  float gstep, gzero;  // step and zero of the key's extra-step group of the thread (see fetch_k)
   float vstep[2], vzero[2];
 };
 
@@ -360,16 +364,8 @@ __device__ inline void fetch_k(const Ctx &c, int k0, int tid, Fetch &f, size_t p
       f.kw[0] = *reinterpret_cast<const uint32_t *>(ks);
     }
     const uint32_t km = krow * static_cast<uint32_t>(c.ng);
-    // the group of the thread's extra-step slots 2j, 2j+1 (j = tid % 8): the
-    // Taylor group j / 2 for j < 4 (and for every j with 4 groups), else the
-    // group (j - 4) / 2 whose centre it writes; clamped to the last group
-    const int j = tid & 7;
-    const int gx0 = c.ng == 4 ? (j >> 1) : ((j & 3) >> 1);
-    const int gj = gx0 < c.ng ? gx0 : c.ng - 1;
     f.kstep = meta_ld<kMeta16>(kc_scale, km + static_cast<uint32_t>(d0 >> c.group_shift));
     f.kzero = meta_ld<kMeta16>(kc_zero, km + static_cast<uint32_t>(d0 >> c.group_shift));
-    f.gstep = meta_ld<kMeta16>(kc_scale, km + static_cast<uint32_t>(gj));
-    f.gzero = meta_ld<kMeta16>(kc_zero, km + static_cast<uint32_t>(gj));
   } else {
     const uint4 *ks = reinterpret_cast<const uint4 *>(c.k_cur + (krow * D + static_cast<uint32_t>(d0)));
     const uint4 a = ks[0], b = ks[1];
@@ -411,31 +407,43 @@ __device__ inline void fetch_v(const Ctx &c, int k0, int tid, int j, Fetch &f, s
 // the vector ALU stay busy together; each item's results are pinned (see
 // pin) so that it stays between its fences.
 
-// K tile row (fp16 values, then the slots of the extra bf16 step: 4g+{0,1,2}
-// = -D_g^2 split (hi, lo, hi) for the Taylor correction (zero for
-// g >= d/group or without it), 1.0 in slots 3 and 7 (the running max), and
-// with at most two groups the centres c_g of a cached key's groups in slots
-// 8 + 4g and 9 + 4g; zero elsewhere).  Cached values are stored centred,
-// (z - c_g + D code) tau log2(e) 2^-ek, and the step adds c_g times the
-// query's group sums back; current keys are stored as k 2^-ek, exact.
-// Item p < 2 writes values 8p..8p+7 of the thread's 16; item 2 writes its two
-// slots 2*(tid%8), +1.  A 304-byte row stride keeps the 16-byte writes
-// (16 lanes = 2 keys x 8 chunks) on disjoint bank quads.
+// K tile row: fp16 values, then the 16 slots of the extra bf16 step, laid
+// out so that each thread writes slots of its own group (that of its 16
+// values) and loads no other step or zero point.  With g the thread's group:
+//   -D_g^2 split (hi, lo, hi) for the Taylor correction (zero without it):
+//     two groups: slots 8g + {0, 1, 2}; four groups: 4g + {0, 1, 2}; one: 0..2;
+//   1.0 in slots 3 and 7 (the running max carried by the query side);
+//   the centre c_g of a cached key's group (see group_centre) in slots
+//     8g + 4, 8g + 5 (one or two groups; none with four);
+//   zero elsewhere.  Cached values are stored centred, (z - c_g + D code)
+// tau log2(e) 2^-ek, and the step adds c_g times the query's group sums
+// back; current keys are stored as k 2^-ek, exact.  Item 0 computes the
+// scaled step, centred zero point and centre (kept in KWork), items 0 and 1
+// write values 8p .. 8p+7 of the thread's 16, item 2 its two slots 2j, 2j+1
+// (j = tid % 8).  A 304-byte row stride keeps the 16-byte writes (16 lanes =
+// 2 keys x 8 chunks) on disjoint bank quads.
 constexpr int kItemsK = 3;
 
+struct KWork {
+  float s, z, centre;
+};
+
 template <bool CACHED, bool TAYLOR, int KBITS>
-__device__ inline void unpack_k_item(int p, const Ctx &c, int tid, const Fetch &f, uint16_t *Kb) {
+__device__ inline void unpack_k_item(int p, const Ctx &c, int tid, const Fetch &f, uint16_t *Kb, KWork &u) {
   const int kk = tid >> 3, j = tid & 7, d0 = j * 16;
+  if (CACHED && p == 0) {
+    u.centre = c.centre ? group_centre<KBITS>(f.kzero, f.kstep) : 0.f;
+    u.s = f.kstep * c.kscale;
+    u.z = fmaf(-1024.0f, f.kstep, f.kzero - u.centre) * c.kscale;
+  }
   if (p < 2) {
     uint32_t w[4];
     if (CACHED) {
       uint32_t m[4];
       magic8<KBITS>(KBITS == 4 ? f.kw[p] : (f.kw[0] >> (16 * p)), c.kmask, m);
-      const float zc = c.centre ? f.kzero - group_centre<KBITS>(f.kzero, f.kstep) : f.kzero;
-      const float s = f.kstep * c.kscale, z = fmaf(-1024.0f, f.kstep, zc) * c.kscale;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        w[e] = pair_h(dequant_h(magic_code(m, 2 * e), s, z), dequant_h(magic_code(m, 2 * e + 1), s, z));
+        w[e] = pair_h(dequant_h(magic_code(m, 2 * e), u.s, u.z), dequant_h(magic_code(m, 2 * e + 1), u.s, u.z));
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -444,19 +452,23 @@ __device__ inline void unpack_k_item(int p, const Ctx &c, int tid, const Fetch &
       }
     }
     *reinterpret_cast<uint4 *>(Kb + kk * KS + d0 + 8 * p) = make_uint4(w[0], w[1], w[2], w[3]);
-  } else {  // slots 2j, 2j+1: correction terms of group j/2, 1.0 in the max slots 3 and 7, centres
+  } else {  // slots 2j, 2j+1 (layout above); j's slot pair within its group: r
+    const int r = c.ng == 4 ? (j & 1) : c.ng == 2 ? (j & 3) : j;
     const float one = j == 1 || j == 3 ? 1.0f : 0.f;
-    uint32_t w = pack2(0.f, one);
-    if (CACHED && j >= 4 && c.centre) {  // slots 8 + 2(j-4), +1: centre of group (j-4)/2 in both of 8+4g, 9+4g
-      const int g = (j - 4) >> 1;
-      const float cg = (j & 1) == 0 && g < c.ng ? group_centre<KBITS>(f.gzero, f.gstep) : 0.f;
-      w = pack2(cg, cg);
-    } else if (CACHED && TAYLOR) {
-      const float sq = (j >> 1) < c.ng ? f.gstep * f.gstep : 0.f;
+    float a = 0.f, b = one;
+    if (CACHED) {
+      const float sq = TAYLOR ? f.kstep * f.kstep : 0.f;
       const float hsq = lo_f(pack2(sq, 0.f));
-      w = (j & 1) ? pack2(-hsq, one) : pack2(-hsq, -(sq - hsq));
+      if (r == 0) {
+        a = -hsq;
+        b = -(sq - hsq);
+      } else if (r == 1) {
+        a = -hsq;
+      } else if (r == 2) {  // (one or two groups) the centre, twice
+        a = b = u.centre;
+      }
     }
-    *reinterpret_cast<uint32_t *>(Kb + kk * KS + KEXT + 2 * j) = w;
+    *reinterpret_cast<uint32_t *>(Kb + kk * KS + KEXT + 2 * j) = pack2(a, b);
   }
 }
 
@@ -681,6 +693,7 @@ __device__ inline void tile_step(const Ctx &c, QState &qs, Soft &st, Fetch &f, c
   //    tile t+2
   {
     VWork u;
+    KWork ku;
     if (PREV) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) buf[j] = lds16(Vb + pv_off(j));
@@ -693,7 +706,7 @@ __device__ inline void tile_step(const Ctx &c, QState &qs, Soft &st, Fetch &f, c
         if (j + 4 < 16) buf[j & 3] = lds16(Vb + pv_off(j + 4));
       }
       if (NEXT) {
-        if (j < NK) unpack_k_item<CACHED, TAYLOR, KBITS>(j, c, tid, f, Kn);
+        if (j < NK) unpack_k_item<CACHED, TAYLOR, KBITS>(j, c, tid, f, Kn, ku);
         else if (j >= 4 && j - 4 < kItemsV) unpack_v_item<CACHED, VBITS>(j - 4, tid, f, Vn, u, c.vscale);
         else if (j == 9) fetch_k<CACHED, KBITS, PAGED>(c, k0_next2, tid, f, prn);
         else if (j == 10 || j == 11) fetch_v<CACHED, VBITS, PAGED>(c, k0_next2, tid, j - 10, f, prn);
@@ -721,12 +734,13 @@ __device__ inline void segment(const Ctx &c, QState &qs, Soft &st, uint16_t *Kl,
   Fetch f;
   {
     VWork u;
+    KWork ku;
     const size_t pr0 = CACHED && PAGED ? tile_pool_row(c, tile_start(c, c.beg)) : 0;
     fetch_k<CACHED, KBITS, PAGED>(c, c.beg, tid, f, pr0);
     fetch_v<CACHED, VBITS, PAGED>(c, c.beg, tid, 0, f, pr0);
     fetch_v<CACHED, VBITS, PAGED>(c, c.beg, tid, 1, f, pr0);
 #pragma unroll
-    for (int p = 0; p < kItemsK; ++p) unpack_k_item<CACHED, TAYLOR, KBITS>(p, c, tid, f, Kl);
+    for (int p = 0; p < kItemsK; ++p) unpack_k_item<CACHED, TAYLOR, KBITS>(p, c, tid, f, Kl, ku);
 #pragma unroll
     for (int p = 0; p < kItemsV; ++p) unpack_v_item<CACHED, VBITS>(p, tid, f, Vl, u, c.vscale);
     const size_t pr1 = CACHED && PAGED ? tile_pool_row(c, tile_start(c, c.beg + BN)) : 0;

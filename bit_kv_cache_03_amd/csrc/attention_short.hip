@@ -73,8 +73,6 @@ struct Fetch {
   uint32_t kw[8];      // K codes of d in [64h, 64h+64): INT4 8 words, INT2 4
   float kstep[2];      // step and zero point of the groups of d = 64h + 32j, j = 0, 1
   float kzero[2];
-  float gstep[2];      // steps of groups 2h, 2h+1 (correction slots; clamped index)
-  float gzero[2];      // with at most 2 groups: zero points of groups 0 and 1 (centre slots)
   uint32_t vw[4];      // V codes of keys 4kq+j at d in [16dq, 16dq+16): INT4 words
   uint32_t vw2[4];     //   d 16dq..+7 in vw, +8..+15 in vw2; INT2 all 16 in vw
   float vstep[4], vzero[4];
@@ -202,25 +200,19 @@ __device__ inline void fetch_cached(const Ctx &c, int k0, const Lanes &o, int h,
     }
     const Buf ks = buffer_at(meta_adv<M16>(c.kc_scale, r0 * NG), rows * NG * ES);
     const Buf kz = buffer_at(meta_adv<M16>(c.kc_zero, r0 * NG), rows * NG * ES);
-    // groups of d = 64h + 32j (kstep, kzero) and groups 2h + j (gstep; only
-    // those below NG are used)
+    // the groups of d = 64h + 32j, j = 0, 1 (the lane's own values)
     if (NG == 1) {
       const float st = ld_meta1<M16>(ks, o.km), z = ld_meta1<M16>(kz, o.km);
-      f.kstep[0] = f.kstep[1] = f.gstep[0] = f.gstep[1] = st;
-      f.kzero[0] = f.kzero[1] = f.gzero[0] = f.gzero[1] = z;
+      f.kstep[0] = f.kstep[1] = st;
+      f.kzero[0] = f.kzero[1] = z;
     } else if (NG == 2) {
-      const float2 st = ld_meta2<M16>(ks, o.km);
-      const float2 z = ld_meta2<M16>(kz, o.km);
-      f.kstep[0] = f.kstep[1] = h ? st.y : st.x;
-      f.kzero[0] = f.kzero[1] = h ? z.y : z.x;
-      f.gstep[0] = st.x;
-      f.gstep[1] = st.y;
-      f.gzero[0] = z.x;
-      f.gzero[1] = z.y;
+      const float st = ld_meta1<M16>(ks, o.km + ES * h), z = ld_meta1<M16>(kz, o.km + ES * h);
+      f.kstep[0] = f.kstep[1] = st;
+      f.kzero[0] = f.kzero[1] = z;
     } else {
       const float2 st = ld_meta2<M16>(ks, o.km + 2 * ES * h), z = ld_meta2<M16>(kz, o.km + 2 * ES * h);
-      f.kstep[0] = f.gstep[0] = st.x;
-      f.kstep[1] = f.gstep[1] = st.y;
+      f.kstep[0] = st.x;
+      f.kstep[1] = st.y;
       f.kzero[0] = z.x;
       f.kzero[1] = z.y;
     }
@@ -277,21 +269,22 @@ constexpr bool kCentre = NG <= 2;
 // of S^T = K Q^T: the lane (key kr = lane % 32, half h = lane / 32) holds
 // its key's values d = 64h + 8s .. +7 in k[s] (k-step s, slots 8h .. 8h+7;
 // the query uses the same order), as fp16 (k - c_g) 2^-ek (magic codes, one
-// v_fma_mix each; c_g the group's centre, 0 with 4 groups), and in the extra
-// step's slots: for the Taylor correction 4g+{0,1,2,3} = (-D_g^2 split hi,
-// lo, hi; 0) in bf16 for its groups g = 2h, 2h+1 (zero for g >= d/group),
-// scaled like the keys; with centring, lane half 1 holds (c_0, c_0, 0, 0,
-// c_1, c_1, 0, 0) 2^-ek instead (the query side holds its group sums there).
+// v_fma_mix each; c_g the group's centre, 0 with 4 groups), and in its
+// extra-step slots 8h .. 8h+7, scaled like the keys, terms of its own
+// groups only: with four groups (2h, 2h+1) the Taylor terms (-D_g^2 split
+// hi, lo, hi; 0) of each; with two groups (group h), or one (half 0), the
+// Taylor terms of the group, then (c_g, c_g, 0, 0) (the query side holds the
+// group sums against the centres); zero Taylor terms without the correction.
 template <bool TAYLOR, int KBITS, int NG>
 __device__ inline void unpack_k_cached(const Ctx &c, int lane, const Fetch &f, float kscale, f16x8 (&k)[8],
                                        bf16x8 &kext) {
   const int h = lane >> 5;
-  float sj[2], zj[2];
+  float sj[2], zj[2], cj[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const float zc = kCentre<NG> ? f.kzero[j] - group_centre<KBITS>(f.kzero[j], f.kstep[j]) : f.kzero[j];
+    cj[j] = kCentre<NG> ? group_centre<KBITS>(f.kzero[j], f.kstep[j]) : 0.f;
     sj[j] = f.kstep[j] * kscale;
-    zj[j] = fmaf(-1024.0f, f.kstep[j], zc) * kscale;
+    zj[j] = fmaf(-1024.0f, f.kstep[j], f.kzero[j] - cj[j]) * kscale;
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {  // values d = 64h + 8i .. +7, in the group of d = 64h + 32 (i / 4)
@@ -304,24 +297,21 @@ __device__ inline void unpack_k_cached(const Ctx &c, int lane, const Fetch &f, f
       w[e] = pair_h(dequant_h(magic_code(m, 2 * e), st, z), dequant_h(magic_code(m, 2 * e + 1), st, z));
     k[i] = __builtin_bit_cast(f16x8, make_uint4(w[0], w[1], w[2], w[3]));
   }
-  if (kCentre<NG> && h == 1) {
-    const float c0 = group_centre<KBITS>(f.gzero[0], f.gstep[0]) * kscale;
-    const float c1 = NG == 2 ? group_centre<KBITS>(f.gzero[1], f.gstep[1]) * kscale : 0.f;
-    kext = __builtin_bit_cast(bf16x8, make_uint4(pack2(c0, c0), 0u, pack2(c1, c1), 0u));
-  } else if (TAYLOR) {
-    uint32_t x[4];
+  uint32_t x[4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int g = 2 * h + j;
-      const float sq = g < NG ? f.gstep[j] * f.gstep[j] * kscale : 0.f;
-      const float hsq = lo_f(pack2(sq, 0.f));
-      x[2 * j] = pack2(-hsq, -(sq - hsq));
-      x[2 * j + 1] = pack2(-hsq, 0.f);
-    }
-    kext = __builtin_bit_cast(bf16x8, make_uint4(x[0], x[1], x[2], x[3]));
-  } else {
-    kext = bf16x8{};
+  for (int j = 0; j < 2; ++j) {  // Taylor terms of group j (four groups) or of the lane's group (j = 0)
+    const float sq = TAYLOR ? f.kstep[j] * f.kstep[j] * kscale : 0.f;
+    const float hsq = lo_f(pack2(sq, 0.f));
+    x[2 * j] = pack2(-hsq, -(sq - hsq));
+    x[2 * j + 1] = pack2(-hsq, 0.f);
   }
+  if (kCentre<NG>) {
+    const float cs = cj[0] * kscale;
+    x[2] = pack2(cs, cs);
+    x[3] = 0u;
+    if (NG == 1 && h == 1) x[0] = x[1] = x[2] = 0u;  // one group: its terms sit in half 0
+  }
+  kext = __builtin_bit_cast(bf16x8, make_uint4(x[0], x[1], x[2], x[3]));
 }
 
 // V^T tile of a cached block: fp16 values v 2^-ev of keys 4kq..4kq+3

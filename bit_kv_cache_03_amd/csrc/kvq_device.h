@@ -55,7 +55,7 @@ __device__ inline float sum8h(f16x8 v, float acc) {
 
 // Centre of a cached key group for the fp16 key operand.  When the group's
 // code range [z, z + (2^bits - 1) D] lies on one side of zero (its values
-// share an offset), the centre is the range's midpoint rounded to bf16,
+// share an offset), the centre is the range's midpoint truncated to bf16,
 // else 0.  The kernels round z - centre + D c (not z + D c) to fp16, so that
 // the rounding error of offset groups scales with their half range rather
 // than with |k|, and add the centre back through the extra bf16 MFMA step as
@@ -67,8 +67,11 @@ __device__ inline float sum8h(f16x8 v, float acc) {
 // small values moved away from zero by a midpoint.
 template <int BITS>
 __device__ inline float group_centre(float z, float step) {
-  const float top = fmaf(static_cast<float>((1 << BITS) - 1), step, z);
-  return z > 0.f || top < 0.f ? lo_f(pack2(fmaf(static_cast<float>((1 << BITS) - 1) * 0.5f, step, z), 0.f)) : 0.f;
+  const float half = static_cast<float>((1 << BITS) - 1) * 0.5f;
+  const float mid = fmaf(half, step, z);
+  // the range lies on one side of zero iff |mid| > half range; the centre is
+  // mid truncated to bf16 (any bf16 value near mid serves)
+  return fabsf(mid) > half * step ? __uint_as_float(__float_as_uint(mid) & 0xffff0000u) : 0.f;
 }
 
 // Codes as fp16 "magic" values 1024 + c (exact: the fp16 spacing at 1024 is
@@ -153,10 +156,11 @@ __device__ inline void pin(T &x) {
 // and the Taylor correction operands N_g = tau/24 ||q_g||^2 2^-(eq+ek) in
 // slots 4g+{0,1,2,3} as (hi, hi, lo, 0) split into bf16 (the lane holds
 // slots 8h .. 8h+7, i.e. groups 2h and 2h+1; zero when not TAYLOR).  With
-// at most two groups, lane half 1 holds instead the group sums
-// S_g = sum_{c in g} q_c 2^-eq as (S_hi, S_lo) in slots 8 + 4g, 9 + 4g, which
-// the centres of centred cached keys multiply (see group_centre).  The
-// row's other half sits in lane l^32.
+// at most two groups (and HALVES), lane half h holds group h only:
+// (N_hi, N_hi, N_lo, 0, S_hi, S_lo, 0, 0) with the group sum
+// S_g = sum_{c in g} q_c 2^-eq, which the centres of centred cached keys
+// multiply (see group_centre); half 1 is zero with one group.  The row's
+// other half sits in lane l^32.
 template <bool TAYLOR, bool HALVES = false>
 __device__ inline void load_query(const uint16_t *qptr, int h, int group_shift, float tau, int ek, f16x8 (&q)[8],
                                   bf16x8 &qext, float &alpha) {
@@ -209,8 +213,11 @@ __device__ inline void load_query(const uint16_t *qptr, int h, int group_shift, 
     sh[g] = g < ng ? lo_f(pack2(t, 0.f)) : 0.f;
     sl[g] = g < ng ? t - sh[g] : 0.f;
   }
-  if (h == 1 && ng <= 2) {
-    qext = __builtin_bit_cast(bf16x8, make_uint4(pack2(sh[0], sl[0]), 0u, pack2(sh[1], sl[1]), 0u));
+  if (ng <= 2) {
+    const bool on = h < ng;
+    const float gh = on ? (h ? nh[1] : nh[0]) : 0.f, gl = on ? (h ? nl[1] : nl[0]) : 0.f;
+    const float th = on ? (h ? sh[1] : sh[0]) : 0.f, tl = on ? (h ? sl[1] : sl[0]) : 0.f;
+    qext = __builtin_bit_cast(bf16x8, make_uint4(pack2(gh, gh), pack2(gl, 0.f), pack2(th, tl), 0u));
     return;
   }
   const float n0h = h ? nh[2] : nh[0], n0l = h ? nl[2] : nl[0];
