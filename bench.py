@@ -7,9 +7,10 @@ already resident in HBM:
   - kv_attention_corrected: the current chunk's queries against the Nc
     cached (INT2/INT4, dequantised in-kernel) tokens and the bf16 current
     chunk, Jensen-bias correction on cached scores, one online softmax;
-  - kv_quantize of the finished chunk's K and V, appended to the cache at
+  - the finished chunk's K and V quantised and appended to the cache at
     rows [Nc, Nc + Ncur) (rows the attention of this step does not read,
-    so every step does identical work).
+    so every step does identical work): by default inside the same call
+    (append = 1), with --append separate by two kv_quantize calls.
 Prints ONE JSON line.  `value` is cached-key tokens x queries per second of
 whole steps; the attention kernel's own duration (HIP events on the stream
 it runs on) gives the roofline figure.  The CPU oracle, timed on a bounded
@@ -85,7 +86,8 @@ def attention_flops(w, causal: bool = False) -> float:
 def call_options(args) -> dict:
     """The options of the timed attention call besides the workload."""
     return {"nq": args.nq, "corr": args.corr, "path": args.path, "causal": args.causal,
-            "page_size": args.page_size, "meta": args.meta, "kaxis": args.kaxis, "vaxis": args.vaxis}
+            "page_size": args.page_size, "meta": args.meta, "kaxis": args.kaxis, "vaxis": args.vaxis,
+            "append": args.append}
 
 
 def traffic_from_profiles(w, sha: str, options: dict):
@@ -345,10 +347,14 @@ def main():
     ap.add_argument("--traffic", default=None, metavar="PMC_DIR",
                     help="only turn rocprofv3 FETCH_SIZE/WRITE_SIZE runs into profiles/traffic_<workload>.json")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
+    ap.add_argument("--append", default="fused", choices=["fused", "separate"],
+                    help="append the chunk to the cache inside the attention call, or by kv_quantize after it")
     ap.add_argument("--evict", default="auto", choices=["auto", "on", "off"],
                     help="write a 512 MiB buffer between timed steps so that no launch finds the cache in the "
                          "MALL (auto: on for HBM-graded runs, i.e. at most 64 query rows per KV head)")
     args = ap.parse_args()
+    if "tokens" in (args.kaxis, args.vaxis):
+        args.append = "separate"  # the fused append takes caches grouped along the head dimension
     if args.traffic:
         write_traffic(W.WORKLOADS[args.workload], args.traffic, args.copy_bytes, call_options(args))
         return
@@ -404,8 +410,9 @@ def main():
     ws_bytes = max(kvq.workspace_size(kvq.make_args(q, k, v, kc, vc, w.Nc, out, corr=c, path=args.path,
                                                     causal=args.causal)) for c in (corr, "off"))
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    fused = args.append == "fused"
     args_c = kvq.make_args(q, k, v, kc, vc, w.Nc, out, corr=corr, path=args.path, workspace=ws,
-                           causal=args.causal)
+                           causal=args.causal, append=fused)
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     import ctypes as C
@@ -421,8 +428,9 @@ def main():
         attention(a)
         if ev is not None:
             ev[1].record(stream)
-        kvq.quantize(k, kc, w.Nc, stream)
-        kvq.quantize(v, vc, w.Nc, stream)
+        if not fused:
+            kvq.quantize(k, kc, w.Nc, stream)
+            kvq.quantize(v, vc, w.Nc, stream)
 
     # few query rows per KV head: the packed cache read bounds the kernel
     hbm_bound = w.rows_per_kvhead <= 64
@@ -457,27 +465,35 @@ def main():
     quant_ms = ms_step - attn_ms
     del scratch
 
-    overhead = None
-    if not args.no_overhead and corr != "off":
-        a_off = kvq.make_args(q, k, v, kc, vc, w.Nc, out, corr="off", path=args.path, workspace=ws,
-                              causal=args.causal)
-        for _ in range(args.warmup):
-            attention(a_off)
-        e_off = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-        e_on = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    overhead = append_overhead = None
+    if not args.no_overhead:
+        # interleaved so that drift hits all equally: the timed call, the
+        # same with the correction off, and (fused) the same without append
+        runs = {"on": args_c}
+        if corr != "off":
+            runs["off"] = kvq.make_args(q, k, v, kc, vc, w.Nc, out, corr="off", path=args.path, workspace=ws,
+                                        causal=args.causal, append=fused)
+        if fused:
+            runs["plain"] = kvq.make_args(q, k, v, kc, vc, w.Nc, out, corr=corr, path=args.path, workspace=ws,
+                                          causal=args.causal)
+        for a in runs.values():
+            for _ in range(args.warmup):
+                attention(a)
+        ev_runs = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(args.steps)] for n in runs}
         scratch = torch.empty(MALL_EVICT_BYTES // 4, dtype=torch.float32, device="cuda") if evict else None
-        for i in range(args.steps):   # interleave so drift hits both equally
-            if scratch is not None:
-                scratch.fill_(float(i))
-            e_off[i][0].record(stream); attention(a_off); e_off[i][1].record(stream)
-            if scratch is not None:
-                scratch.fill_(float(i))
-            e_on[i][0].record(stream); attention(args_c); e_on[i][1].record(stream)
+        for i in range(args.steps):
+            for n, a in runs.items():
+                if scratch is not None:
+                    scratch.fill_(float(i))
+                ev_runs[n][i][0].record(stream); attention(a); ev_runs[n][i][1].record(stream)
         del scratch
         torch.cuda.synchronize()
-        t_off = float(np.median([a.elapsed_time(b) for a, b in e_off]))
-        t_on = float(np.median([a.elapsed_time(b) for a, b in e_on]))
-        overhead = t_on / t_off - 1.0
+        t = {n: float(np.median([a.elapsed_time(b) for a, b in e])) for n, e in ev_runs.items()}
+        if "off" in t:
+            overhead = t["on"] / t["off"] - 1.0
+        if "plain" in t:
+            append_overhead = t["on"] / t["plain"] - 1.0
 
     flops = attention_flops(w, args.causal)
     ckq = w.B * w.Hq * w.Nq * w.Nc
@@ -514,6 +530,8 @@ def main():
         "tflops_eff": achieved,
         "packed_kv_gbs": pbytes / (attn_ms * 1e-3) / 1e9,
         "correction_overhead": overhead,
+        "append": args.append,
+        "append_overhead": append_overhead,
         "wall_s": wall,
         "kernel_sha": sha,
         "mall_evict_between_steps": evict,

@@ -70,6 +70,7 @@
 #include <math.h>
 
 #include "kvq_internal.h"
+#include "quant_device.h"
 
 #ifndef KVQ_TILE_TOKENS
 #define KVQ_TILE_TOKENS 0
@@ -624,7 +625,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_tile_kernel(AttnLaunch p, in
 // Value pre-pass: workgroup (chunk, b * Hkv + hk) bounds |v| over its
 // share of the head's cached value groups (max(|z|, |z + top D|) per group)
 // and of its current-chunk values, and writes the bound to
-// part[(b * Hkv + hk) * kVChunks + chunk].
+// part[(b * Hkv + hk) * kVChunks + chunk].  APPEND: the call's chunk append
+// rides along -- the workgroup also quantises its share of the chunk's K and
+// V rows into the caches, from the values it loads for the bound.
+template <bool APPEND>
 __global__ __launch_bounds__(256) void value_bound_kernel(AttnLaunch p, int32_t group_shift, float *part) {
   const int tid = threadIdx.x;
   const int64_t ch = blockIdx.x, bkv = blockIdx.y;
@@ -646,7 +650,11 @@ __global__ __launch_bounds__(256) void value_bound_kernel(AttnLaunch p, int32_t 
       vm = fmaxf(vm, fmaxf(fabsf(zp), fabsf(fmaf(stp, top, zp))));
     }
   }
-  {  // current chunk: bf16 pairs
+  if (APPEND) {  // the chunk's rows in this share: the value bound, and the codes of both tensors
+    const int64_t r0 = bkv * p.Ncur + p.Ncur * ch / kVChunks, r1 = bkv * p.Ncur + p.Ncur * (ch + 1) / kVChunks;
+    float kb = 0.f;
+    qdev::append_rows(p, r0, r1, true, tid, 256, kb, vm);
+  } else {  // current chunk: bf16 pairs
     const uint32_t *w = reinterpret_cast<const uint32_t *>(p.v_cur + bkv * p.Ncur * p.d);
     const int64_t n = p.Ncur * p.d / 2, lo = n * ch / kVChunks, hi = n * (ch + 1) / kVChunks;
     for (int64_t i = lo + tid; i < hi; i += 256) {
@@ -710,7 +718,11 @@ hipError_t launch_bits(const AttnLaunch &p, hipStream_t stream, bool exact) {
   // value bounds after the split partials
   float *vpart = reinterpret_cast<float *>(static_cast<char *>(p.workspace) +
                                            general_bound_offset(p.B, p.Hq, p.Nq, D, splits, SPLIT));
-  value_bound_kernel<<<dim3(kVChunks, static_cast<uint32_t>(p.B * p.Hkv)), dim3(256), 0, stream>>>(p, gshift, vpart);
+  const dim3 vgrid(kVChunks, static_cast<uint32_t>(p.B * p.Hkv));
+  if (p.app.on)  // the instance with the chunk append holds its registers
+    value_bound_kernel<true><<<vgrid, dim3(256), 0, stream>>>(p, gshift, vpart);
+  else
+    value_bound_kernel<false><<<vgrid, dim3(256), 0, stream>>>(p, gshift, vpart);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (exact)

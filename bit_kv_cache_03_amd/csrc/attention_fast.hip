@@ -70,6 +70,7 @@
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
+#include "quant_device.h"
 
 #ifndef KVQ_FAST_CAUSAL
 #define KVQ_FAST_CAUSAL 0
@@ -129,9 +130,10 @@ __device__ inline int vt_index(int row, int col) {
 // partial bounds.
 constexpr int KCHUNKS = 32;
 
+template <int NT>
 __device__ inline float bf16_bound(const uint16_t *x, int64_t lo, int64_t hi, int tid) {  // 8-value chunks
   float b = 0.f;
-  for (int64_t i = lo + tid; i < hi; i += 256) {
+  for (int64_t i = lo + tid; i < hi; i += NT) {
     const uint4 w = reinterpret_cast<const uint4 *>(x)[i];
     const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -139,24 +141,28 @@ __device__ inline float bf16_bound(const uint16_t *x, int64_t lo, int64_t hi, in
   }
   return b;
 }
+template <int NT>
 __device__ inline float block_max(float b, float *red, int tid) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) b = fmaxf(b, __shfl_xor(b, o, 64));
   __syncthreads();
   if ((tid & 63) == 0) red[tid >> 6] = b;
   __syncthreads();
-  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float m = red[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) m = fmaxf(m, red[w]);
+  return m;
 }
 
 // Largest |z|, |z + top D| over this chunk's share of a cache tensor's groups.
-template <bool M16>
+template <bool M16, int NT>
 __device__ inline float cache_bound(const AttnLaunch &p, const float *scale, const float *zero, float top,
                                     int32_t ng, int64_t bkv, int64_t ch, int tid) {
   float bd = 0.f;
   const int64_t n = p.Nc * ng, lo = n * ch / KCHUNKS, hi = n * (ch + 1) / KCHUNKS;
   if (p.layout.page_table) {  // element i = (token i / ng, group i % ng) through the page table
     const int64_t b = bkv / p.Hkv, hk = bkv - b * p.Hkv;
-    for (int64_t i = lo + tid; i < hi; i += 256) {
+    for (int64_t i = lo + tid; i < hi; i += NT) {
       const int64_t e = p.layout.row(p.cap, p.Hkv, b, hk, i / ng) * ng + i % ng;
       const float zi = meta_ld<M16>(zero, e);
       bd = fmaxf(bd, fmaxf(fabsf(zi), fabsf(fmaf(meta_ld<M16>(scale, e), top, zi))));
@@ -164,7 +170,7 @@ __device__ inline float cache_bound(const AttnLaunch &p, const float *scale, con
   } else {
     const float *s = meta_adv<M16>(scale, bkv * p.cap * ng);
     const float *z = meta_adv<M16>(zero, bkv * p.cap * ng);
-    for (int64_t i = lo + tid; i < hi; i += 256) {
+    for (int64_t i = lo + tid; i < hi; i += NT) {
       const float zi = meta_ld<M16>(z, i);
       bd = fmaxf(bd, fmaxf(fabsf(zi), fabsf(fmaf(meta_ld<M16>(s, i), top, zi))));
     }
@@ -172,31 +178,40 @@ __device__ inline float cache_bound(const AttnLaunch &p, const float *scale, con
   return bd;
 }
 
-template <int KBITS, bool M16>
+// Pre-pass: workgroup (b * Hkv + hk) * KCHUNKS + chunk bounds |key|, |query|
+// and |value| over its share of the head's cache groups, current chunk and
+// query rows.  APPEND: the call's chunk append rides along -- the workgroup
+// also quantises its share of the chunk's K and V rows into the caches, from
+// the values it loads for the bounds.
+template <int KBITS, bool M16, bool APPEND>
 __global__ __launch_bounds__(256) void key_scale_kernel(AttnLaunch p, int32_t ng, float *part) {
-  __shared__ float red[4];
+  constexpr int NT = 256;
+  __shared__ float red[NT / 64];
   const int64_t bkv = blockIdx.x / KCHUNKS;
   const int64_t ch = blockIdx.x % KCHUNKS;
   const int tid = threadIdx.x;
   float kb = 0.f, vb = 0.f;
   if (p.Nc > 0) {
-    kb = cache_bound<M16>(p, p.kc_scale, p.kc_zero, static_cast<float>((1 << KBITS) - 1), ng, bkv, ch, tid);
-    vb = cache_bound<M16>(p, p.vc_scale, p.vc_zero, static_cast<float>((1 << p.vbits) - 1), ng, bkv, ch, tid);
+    kb = cache_bound<M16, NT>(p, p.kc_scale, p.kc_zero, static_cast<float>((1 << KBITS) - 1), ng, bkv, ch, tid);
+    vb = cache_bound<M16, NT>(p, p.vc_scale, p.vc_zero, static_cast<float>((1 << p.vbits) - 1), ng, bkv, ch, tid);
   }
-  if (p.Ncur > 0) {
+  if (APPEND && p.Ncur > 0) {  // the chunk's rows in this share: their bounds, and their codes
+    const int64_t r0 = bkv * p.Ncur + p.Ncur * ch / KCHUNKS, r1 = bkv * p.Ncur + p.Ncur * (ch + 1) / KCHUNKS;
+    qdev::append_rows(p, r0, r1, true, tid, NT, kb, vb);
+  } else if (p.Ncur > 0) {
     const int64_t n = p.Ncur * D / 8, lo = n * ch / KCHUNKS, hi = n * (ch + 1) / KCHUNKS;
-    kb = fmaxf(kb, bf16_bound(p.k_cur + bkv * p.Ncur * D, lo, hi, tid));
-    vb = fmaxf(vb, bf16_bound(p.v_cur + bkv * p.Ncur * D, lo, hi, tid));
+    kb = fmaxf(kb, bf16_bound<NT>(p.k_cur + bkv * p.Ncur * D, lo, hi, tid));
+    vb = fmaxf(vb, bf16_bound<NT>(p.v_cur + bkv * p.Ncur * D, lo, hi, tid));
   }
   float qb;
   {
     const int64_t gq = p.Hq / p.Hkv, b = bkv / p.Hkv, hk = bkv - b * p.Hkv;
     const int64_t n = gq * p.Nq * D / 8, lo = n * ch / KCHUNKS, hi = n * (ch + 1) / KCHUNKS;
-    qb = bf16_bound(p.q + (b * p.Hq + hk * gq) * p.Nq * D, lo, hi, tid);
+    qb = bf16_bound<NT>(p.q + (b * p.Hq + hk * gq) * p.Nq * D, lo, hi, tid);
   }
-  kb = block_max(kb, red, tid);
-  qb = block_max(qb, red, tid);
-  vb = block_max(vb, red, tid);
+  kb = block_max<NT>(kb, red, tid);
+  qb = block_max<NT>(qb, red, tid);
+  vb = block_max<NT>(vb, red, tid);
   if (tid == 0) {
     part[3 * bkv * KCHUNKS + ch] = kb;
     part[(3 * bkv + 1) * KCHUNKS + ch] = qb;
@@ -1056,8 +1071,11 @@ void launch_key_scale(const AttnLaunch &p, hipStream_t stream, float *part) {
   const int32_t ng = D / p.group;
   const dim3 grid(static_cast<uint32_t>(p.B * p.Hkv * KCHUNKS));
   const bool k4 = p.Nc > 0 && p.kbits == 4;
-  auto kernel = p.meta16 ? (k4 ? key_scale_kernel<4, true> : key_scale_kernel<2, true>)
-                         : (k4 ? key_scale_kernel<4, false> : key_scale_kernel<2, false>);
+  // the instances with the chunk append hold its registers; those without stay lean
+  auto kernel = p.app.on ? (p.meta16 ? (k4 ? key_scale_kernel<4, true, true> : key_scale_kernel<2, true, true>)
+                                     : (k4 ? key_scale_kernel<4, false, true> : key_scale_kernel<2, false, true>))
+                         : (p.meta16 ? (k4 ? key_scale_kernel<4, true, false> : key_scale_kernel<2, true, false>)
+                                     : (k4 ? key_scale_kernel<4, false, false> : key_scale_kernel<2, false, false>));
   kernel<<<grid, dim3(256), 0, stream>>>(p, ng, part);
 }
 

@@ -38,6 +38,7 @@
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
+#include "quant_device.h"
 
 #ifndef KVQ_SHORT_PAGED
 #define KVQ_SHORT_PAGED 0
@@ -531,6 +532,10 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
   __shared__ __attribute__((aligned(16))) uint16_t L[LDS_BYTES / 2];
 
   const int tid = threadIdx.x;
+  if (blockIdx.x >= p.app.wg0) {  // the chunk append's workgroups
+    qdev::append_workgroup(p, blockIdx.x - p.app.wg0, tid, THREADS);
+    return;
+  }
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: block loop control stays scalar
   const int qc = lane & 31, h = lane >> 5;
@@ -539,7 +544,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
 
   // Workgroups are dealt to the 8 XCDs round-robin by id; renumber so that
   // consecutive ids (the splits and row groups of one KV head) share an XCD.
-  const uint32_t nwg = gridDim.x, wg = blockIdx.x;
+  const uint32_t nwg = static_cast<uint32_t>(p.app.wg0), wg = blockIdx.x;
   const uint32_t per = nwg >> 3, extra = nwg & 7, xcd = wg & 7, slotw = wg >> 3;
   const uint32_t lin = (xcd < extra ? xcd * (per + 1) : extra * (per + 1) + (xcd - extra) * per) + slotw;
   const int64_t split = lin % static_cast<uint32_t>(nsplit);
@@ -715,13 +720,19 @@ hipError_t launch_bits(const AttnLaunch &p, hipStream_t stream) {
   const int32_t row_groups = static_cast<int32_t>((rows + 31) / 32);
   const int64_t nrows = p.B * p.Hq * p.Nq;
   float *partials = static_cast<float *>(p.workspace);
-  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(p.splits) * row_groups * p.B * p.Hkv));
+  // attention workgroups, then those of the chunk append (about 64 rows of
+  // K and of V each)
+  AttnLaunch pa = p;
+  pa.app.wg0 = static_cast<int64_t>(p.splits) * row_groups * p.B * p.Hkv;
+  const int64_t append_wgs = (p.B * p.Hkv * p.Ncur + 63) / 64;
+  pa.app.wgs = p.app.on ? static_cast<int32_t>(append_wgs < 4096 ? append_wgs : 4096) : 0;
+  const dim3 grid(static_cast<uint32_t>(pa.app.wg0 + pa.app.wgs));
   if (p.group == 128)
-    launch_kernel<KB, VB, 1>(p, stream, grid, rows, row_groups, partials);
+    launch_kernel<KB, VB, 1>(pa, stream, grid, rows, row_groups, partials);
   else if (p.group == 64)
-    launch_kernel<KB, VB, 2>(p, stream, grid, rows, row_groups, partials);
+    launch_kernel<KB, VB, 2>(pa, stream, grid, rows, row_groups, partials);
   else
-    launch_kernel<KB, VB, 4>(p, stream, grid, rows, row_groups, partials);
+    launch_kernel<KB, VB, 4>(pa, stream, grid, rows, row_groups, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   return launch_combine(partials, p.out, nrows, p.splits, p.d, stream);

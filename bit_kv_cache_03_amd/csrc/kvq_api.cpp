@@ -13,7 +13,7 @@ namespace {
 
 using kvq::AttnLaunch;
 
-constexpr int32_t kAbiVersion = 7;
+constexpr int32_t kAbiVersion = 8;
 constexpr int32_t kMaxSplits = 1024;  // grid z extent of the split path
 constexpr int64_t kMaxTokensPerHead = int64_t(1) << 23;  // 8M tokens: 32-bit in-head offsets
 
@@ -135,6 +135,17 @@ int device_cu_count() {
   return cus;
 }
 
+// The call reads its caches (Nc > 0) or writes the chunk into them (append).
+bool uses_caches(const kv_attn_args *a) { return a->Nc > 0 || (a->append == 1 && a->Ncur > 0); }
+
+// [p, p + n) overlaps the codes, steps or zero points of cache tensor c.
+bool overlaps_cache(const kv_attn_args *a, const kv_qtensor *c, const void *p, size_t n) {
+  const size_t rows = static_cast<size_t>(tensor_rows(c, a->B, a->Hkv));
+  return overlaps(p, n, c->codes, rows * static_cast<size_t>(a->d * c->bits / 8)) ||
+         overlaps(p, n, c->scale, meta_array_bytes(c, rows, a->d)) ||
+         overlaps(p, n, c->zero, meta_array_bytes(c, rows, a->d));
+}
+
 kv_status validate_attention(const kv_attn_args *a) {
   if (!a) return KV_ERR_NULL;
   if (!a->q || !a->out) return KV_ERR_NULL;
@@ -162,14 +173,20 @@ kv_status validate_attention(const kv_attn_args *a) {
     if (!a->k_cur || !a->v_cur) return KV_ERR_NULL;
     if (!aligned16(a->k_cur) || !aligned16(a->v_cur)) return KV_ERR_ALIGN;
   }
-  if (a->Nc > 0) {
-    kv_status s = check_qtensor(a->k_cache, a->d, a->Nc, a->B);
+  if (a->append != 0 && a->append != 1) return KV_ERR_UNSUPPORTED;
+  if (a->reserved != 0) return KV_ERR_UNSUPPORTED;
+  if (uses_caches(a)) {
+    // appending needs room for the chunk after the cached rows
+    const int64_t need = a->Nc + (a->append ? a->Ncur : 0);
+    kv_status s = check_qtensor(a->k_cache, a->d, need, a->B);
     if (s != KV_OK) return s;
-    s = check_qtensor(a->v_cache, a->d, a->Nc, a->B);
+    s = check_qtensor(a->v_cache, a->d, need, a->B);
     if (s != KV_OK) return s;
     if (a->k_cache->group != a->v_cache->group) return KV_ERR_UNSUPPORTED;
     if (a->k_cache->cap != a->v_cache->cap) return KV_ERR_SHAPE;
     if (!same_layout(a->k_cache, a->v_cache)) return KV_ERR_UNSUPPORTED;
+    if (a->append && (a->k_cache->axis != KV_AXIS_DIM || a->v_cache->axis != KV_AXIS_DIM))
+      return KV_ERR_UNSUPPORTED;
   }
   // the output must not overlap any input
   const size_t out_b = static_cast<size_t>(nq_el) * 2;
@@ -177,15 +194,30 @@ kv_status validate_attention(const kv_attn_args *a) {
   if (a->Ncur > 0 && (overlaps(a->out, out_b, a->k_cur, static_cast<size_t>(ncur_el) * 2) ||
                       overlaps(a->out, out_b, a->v_cur, static_cast<size_t>(ncur_el) * 2)))
     return KV_ERR_ALIAS;
-  if (a->Nc > 0) {
+  if (uses_caches(a)) {
     const kv_qtensor *ts[2] = {a->k_cache, a->v_cache};
-    for (const kv_qtensor *c : ts) {
-      const size_t rows = static_cast<size_t>(tensor_rows(c, a->B, a->Hkv));
-      if (overlaps(a->out, out_b, c->codes, rows * static_cast<size_t>(a->d * c->bits / 8)) ||
-          overlaps(a->out, out_b, c->scale, meta_array_bytes(c, rows, a->d)) ||
-          overlaps(a->out, out_b, c->zero, meta_array_bytes(c, rows, a->d)))
+    for (const kv_qtensor *c : ts)
+      if (overlaps_cache(a, c, a->out, out_b)) return KV_ERR_ALIAS;
+  }
+  if (a->append && a->Ncur > 0) {  // the caches are written: nothing else the call touches may share their bytes
+    const size_t cur_b = static_cast<size_t>(ncur_el) * 2;
+    const kv_qtensor *ts[2] = {a->k_cache, a->v_cache};
+    for (const kv_qtensor *c : ts)
+      if (overlaps_cache(a, c, a->q, out_b) || overlaps_cache(a, c, a->k_cur, cur_b) ||
+          overlaps_cache(a, c, a->v_cur, cur_b))
         return KV_ERR_ALIAS;
-    }
+    const kv_qtensor *k = a->k_cache, *v = a->v_cache;
+    const size_t rows = static_cast<size_t>(tensor_rows(k, a->B, a->Hkv));
+    const size_t kc = rows * static_cast<size_t>(a->d * k->bits / 8), km = meta_array_bytes(k, rows, a->d);
+    if (overlaps_cache(a, v, k->codes, kc) || overlaps_cache(a, v, k->scale, km) || overlaps_cache(a, v, k->zero, km) ||
+        overlaps(k->codes, kc, k->scale, km) || overlaps(k->codes, kc, k->zero, km) ||
+        overlaps(k->scale, km, k->zero, km))
+      return KV_ERR_ALIAS;
+    const size_t vrows = static_cast<size_t>(tensor_rows(v, a->B, a->Hkv));
+    const size_t vcb = vrows * static_cast<size_t>(a->d * v->bits / 8), vm = meta_array_bytes(v, vrows, a->d);
+    if (overlaps(v->codes, vcb, v->scale, vm) || overlaps(v->codes, vcb, v->zero, vm) ||
+        overlaps(v->scale, vm, v->zero, vm))
+      return KV_ERR_ALIAS;
   }
   return KV_OK;
 }
@@ -197,14 +229,10 @@ bool overlaps_call(const kv_attn_args *a, const void *p, size_t n) {
   const size_t cur_b = static_cast<size_t>(a->B * a->Hkv * a->Ncur * a->d) * 2;
   if (overlaps(p, n, a->out, q_b) || overlaps(p, n, a->q, q_b)) return true;
   if (a->Ncur > 0 && (overlaps(p, n, a->k_cur, cur_b) || overlaps(p, n, a->v_cur, cur_b))) return true;
-  if (a->Nc > 0) {
+  if (uses_caches(a)) {
     const kv_qtensor *ts[2] = {a->k_cache, a->v_cache};
     for (const kv_qtensor *c : ts) {
-      const size_t rows = static_cast<size_t>(tensor_rows(c, a->B, a->Hkv));
-      if (overlaps(p, n, c->codes, rows * static_cast<size_t>(a->d * c->bits / 8)) ||
-          overlaps(p, n, c->scale, meta_array_bytes(c, rows, a->d)) ||
-          overlaps(p, n, c->zero, meta_array_bytes(c, rows, a->d)))
-        return true;
+      if (overlaps_cache(a, c, p, n)) return true;
       if (c->page_table &&
           overlaps(p, n, c->page_table, static_cast<size_t>(a->B * (c->cap / c->page_size)) * sizeof(int32_t)))
         return true;
@@ -427,10 +455,27 @@ kv_status launch_attention(const kv_attn_args *a, const Plan &pl, void *workspac
   p.splits = pl.splits;
   p.fast_full_units = pl.full_units;
   p.workspace = workspace;
+  if (a->append && a->Ncur > 0) {
+    const kv_qtensor *k = a->k_cache, *v = a->v_cache;
+    p.app.on = true;
+    p.app.codes[0] = k->codes;
+    p.app.codes[1] = v->codes;
+    p.app.scale[0] = static_cast<float *>(k->scale);
+    p.app.scale[1] = static_cast<float *>(v->scale);
+    p.app.zero[0] = static_cast<float *>(k->zero);
+    p.app.zero[1] = static_cast<float *>(v->zero);
+    p.app.bits[0] = k->bits;
+    p.app.bits[1] = v->bits;
+    p.app.group = k->group;
+    p.app.meta16 = k->meta == KV_META_F16;
+    p.app.cap = k->cap;
+    p.app.layout = layout_of(k);
+  }
   if (debug_log())
-    fprintf(stderr, "kvq: attention path=%s rows/kvhead=%lld splits=%d full_units=%lld workspace=%zu corr=%d\n",
+    fprintf(stderr,
+            "kvq: attention path=%s rows/kvhead=%lld splits=%d full_units=%lld workspace=%zu corr=%d append=%d\n",
             pl.path == KV_PATH_SHORT ? "short" : "long", static_cast<long long>(a->Nq * (a->Hq / a->Hkv)),
-            pl.splits, static_cast<long long>(pl.full_units), pl.workspace, a->corr);
+            pl.splits, static_cast<long long>(pl.full_units), pl.workspace, a->corr, p.app.on ? 1 : 0);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = pl.path == KV_PATH_SHORT ? kvq::launch_attention_short(p, s) : kvq::launch_attention_long(p, s);
   return e == hipSuccess ? KV_OK : KV_ERR_HIP;

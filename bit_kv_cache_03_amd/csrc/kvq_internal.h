@@ -49,6 +49,23 @@ struct QuantizeLaunch {
   bool tokens;  // groups along the tokens: scale/zero [row / group][d], row the cache row
 };
 
+// The chunk append an attention call may carry: K_cur and V_cur quantised
+// into rows [Nc, Nc + Ncur) of the caches (index 0: K, 1: V), groups along
+// the head dimension, in the workgroups of a pre-pass or in extra
+// workgroups of the attention launch (ids wg0 .. wg0 + wgs - 1).
+struct AppendLaunch {
+  bool on;
+  uint8_t *codes[2];
+  float *scale[2], *zero[2];  // binary16 arrays when meta16
+  int32_t bits[2];
+  int32_t group;
+  bool meta16;
+  int64_t cap;
+  CacheLayout layout;
+  int64_t wg0;  // set by the launcher that adds append workgroups
+  int32_t wgs;
+};
+
 // Everything an attention launch needs, already validated by the host.
 struct AttnLaunch {
   int64_t B, Hq, Hkv, Nq, Ncur, Nc;
@@ -68,6 +85,7 @@ struct AttnLaunch {
   int splits;  // resolved key-range split count
   int64_t fast_full_units;  // throughput kernel: work units run unsplit before the split ones
   void *workspace;
+  AppendLaunch app;
 };
 
 // Split path partials: per (split, query row) the unnormalised O[d] then the

@@ -19,70 +19,14 @@
 // group of one head.  It streams the group's rows once for the per-channel
 // minimum and maximum, then again (from cache) for the codes, which it
 // writes per token row in the same packed format.
-#include "kvq_internal.h"
+#include "quant_device.h"
 
 namespace kvq {
 namespace {
 
+using namespace qdev;
+
 constexpr int kThreads = 256;
-
-template <int LANES>
-__device__ inline float group_min(float v) {
-#pragma unroll
-  for (int o = 1; o < LANES; o <<= 1) v = fminf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-
-template <int LANES>
-__device__ inline float group_max(float v) {
-#pragma unroll
-  for (int o = 1; o < LANES; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-
-template <typename T>
-__device__ inline void load8(const T *p, float (&v)[8]);
-
-template <>
-__device__ inline void load8<uint16_t>(const uint16_t *p, float (&v)[8]) {
-  const uint4 w = *reinterpret_cast<const uint4 *>(p);
-  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = __uint_as_float(u[i] << 16);
-    v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
-  }
-}
-
-template <>
-__device__ inline void load8<float>(const float *p, float (&v)[8]) {
-  const float4 a = *reinterpret_cast<const float4 *>(p);
-  const float4 b = *reinterpret_cast<const float4 *>(p + 4);
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
-
-// Code of value v: rne((v - zp) / step) clamped to [0, TOP], with the IEEE
-// quotient of the definition.  The product with the reciprocal (v_rcp_f32,
-// 1 ulp; then one rounding) lies within 2^-21 |q| of that quotient, so when
-// it is farther than 2^-19 |q| + 2^-20 from every half-integer the two round
-// to the same integer; otherwise, or when step is outside [2^-120, 2^120]
-// (reciprocal not a normal number), the division itself is taken.
-template <int TOP>
-__device__ inline uint32_t code_of(float v, float zp, float step, float inv, bool fast) {
-#pragma clang fp contract(off)
-  const float num = v - zp;
-  float r;
-  const float q = num * inv;
-  const float frac = q - floorf(q);
-  if (fast && fabsf(frac - 0.5f) > fmaf(fabsf(q), 0x1p-19f, 0x1p-20f))
-    r = rintf(q);
-  else
-    r = rintf(num / step);  // IEEE division
-  return static_cast<uint32_t>(fminf(fmaxf(r, 0.0f), static_cast<float>(TOP)));
-}
-
-__device__ inline bool reciprocal_ok(float step) { return step >= 0x1p-120f && step <= 0x1p120f; }
 
 // T: uint16_t (bf16 bits) or float.  LANES = group / 8.  M16: the step and
 // zero point are stored as binary16, rounded (nearest, ties to even) before
@@ -92,9 +36,7 @@ template <typename T, int BITS, int LANES, bool M16>
 __global__ __launch_bounds__(kThreads) void quantize_pack(
     const T *__restrict__ x, int32_t lane_shift, int64_t N,
     uint8_t *__restrict__ codes, float *__restrict__ scale, float *__restrict__ zero,
-    int64_t cap, int64_t off, int32_t groups_per_row, CacheLayout layout, int64_t H) {
-#pragma clang fp contract(off)
-  constexpr int TOP = (1 << BITS) - 1;
+    int64_t cap, int64_t off, CacheLayout layout, int64_t H) {
   const int64_t gl = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   const int64_t bh = static_cast<int64_t>(blockIdx.z) * H + blockIdx.y;
   const int32_t lanes_per_row = 1 << lane_shift;
@@ -106,49 +48,12 @@ __global__ __launch_bounds__(kThreads) void quantize_pack(
   float v[8];
   load8<T>(x + ((bh * N + n) << (lane_shift + 3)) + chunk * 8, v);
 
-  float mn = v[0], mx = v[0];
-#pragma unroll
-  for (int i = 1; i < 8; ++i) {
-    mn = v[i] < mn ? v[i] : mn;
-    mx = v[i] > mx ? v[i] : mx;
-  }
-  mn = group_min<LANES>(mn) + 0.0f;  // + 0.0f: a zero extreme is +0
-  mx = group_max<LANES>(mx) + 0.0f;
-  const float range = mx - mn;
-  float step = range / static_cast<float>(TOP);  // IEEE division
-  float zp = mn;
-  if (M16) {
-    step = static_cast<float>(static_cast<_Float16>(step));
-    zp = static_cast<float>(static_cast<_Float16>(mn));
-  }
-
-  uint32_t packed = 0;
-  if (step > 0.0f) {
-    const bool fast = reciprocal_ok(step);
-    const float inv = fast ? __builtin_amdgcn_rcpf(step) : 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) packed |= code_of<TOP>(v[i], zp, step, inv, fast) << (i * BITS);
-  }
+  float step, zp;
+  const uint32_t packed = quantize8<BITS, LANES, M16>(v, step, zp);
 
   if (!live) return;
   const int64_t orow = layout.row(cap, H, blockIdx.z, blockIdx.y, off + n);  // the cache row of token off + n
-  const int64_t row_bytes = static_cast<int64_t>(lanes_per_row) * BITS;  // 8 codes * BITS / 8 per lane
-  uint8_t *dst = codes + orow * row_bytes + static_cast<int64_t>(chunk) * BITS;
-  if (BITS == 2) {
-    *reinterpret_cast<uint16_t *>(dst) = static_cast<uint16_t>(packed);
-  } else {
-    *reinterpret_cast<uint32_t *>(dst) = packed;
-  }
-  if ((chunk % LANES) == 0) {
-    const int64_t m = orow * groups_per_row + chunk / LANES;
-    if (M16) {
-      reinterpret_cast<_Float16 *>(scale)[m] = static_cast<_Float16>(step);
-      reinterpret_cast<_Float16 *>(zero)[m] = static_cast<_Float16>(zp);
-    } else {
-      scale[m] = step;
-      zero[m] = mn;
-    }
-  }
+  store8<BITS, LANES, M16>(codes, scale, zero, orow, lanes_per_row, chunk, packed, step, zp);
 }
 
 template <typename T, int BITS, bool M16>
@@ -157,19 +62,18 @@ hipError_t launch_t(const QuantizeLaunch &p, hipStream_t stream) {
   const int64_t blocks = ((p.N << lane_shift) + kThreads - 1) / kThreads;
   const dim3 grid(static_cast<uint32_t>(blocks), static_cast<uint32_t>(p.H), static_cast<uint32_t>(p.B));
   const T *x = static_cast<const T *>(p.x);
-  const int32_t gpr = p.d / p.group;
   switch (p.group) {
     case 32:
       quantize_pack<T, BITS, 4, M16><<<grid, dim3(kThreads), 0, stream>>>(
-          x, lane_shift, p.N, p.codes, p.scale, p.zero, p.cap, p.off, gpr, p.layout, p.H);
+          x, lane_shift, p.N, p.codes, p.scale, p.zero, p.cap, p.off, p.layout, p.H);
       break;
     case 64:
       quantize_pack<T, BITS, 8, M16><<<grid, dim3(kThreads), 0, stream>>>(
-          x, lane_shift, p.N, p.codes, p.scale, p.zero, p.cap, p.off, gpr, p.layout, p.H);
+          x, lane_shift, p.N, p.codes, p.scale, p.zero, p.cap, p.off, p.layout, p.H);
       break;
     default:
       quantize_pack<T, BITS, 16, M16><<<grid, dim3(kThreads), 0, stream>>>(
-          x, lane_shift, p.N, p.codes, p.scale, p.zero, p.cap, p.off, gpr, p.layout, p.H);
+          x, lane_shift, p.N, p.codes, p.scale, p.zero, p.cap, p.off, p.layout, p.H);
       break;
   }
   return hipGetLastError();

@@ -46,7 +46,8 @@ class AttnArgs(C.Structure):
                 ("k_cache", C.POINTER(QTensor)), ("v_cache", C.POINTER(QTensor)),
                 ("out", C.c_void_p), ("softmax_scale", C.c_float), ("corr", C.c_int32),
                 ("path", C.c_int32), ("splits", C.c_int32), ("causal", C.c_int32),
-                ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t)]
+                ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
+                ("append", C.c_int32), ("reserved", C.c_int32)]
 
 
 class DiagArgs(C.Structure):
@@ -185,7 +186,7 @@ def quantize(x, cache: QCache, tok_offset: int = 0, stream=None) -> None:
 
 def make_args(q, k_cur, v_cur, k_cache: Optional[QCache], v_cache: Optional[QCache], nc: int, out,
               corr: str = "taylor", scale: float = 0.0, path: str = "auto", splits: int = 0,
-              workspace=None, causal: bool = False):
+              workspace=None, causal: bool = False, append: bool = False):
     """Fill kv_attn_args (keeps the descriptors alive on the returned object)."""
     B, Hq, Nq, d = q.shape
     Hkv = k_cur.shape[1] if k_cur is not None else k_cache.H
@@ -199,6 +200,7 @@ def make_args(q, k_cur, v_cur, k_cache: Optional[QCache], v_cache: Optional[QCac
     a.v_cache = C.pointer(a._vd) if a._vd is not None else None
     a.softmax_scale, a.corr, a.path, a.splits = scale, CORR[corr], PATH[path], splits
     a.causal = 1 if causal else 0
+    a.append = 1 if append else 0
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return a
@@ -210,16 +212,18 @@ def workspace_size(args: AttnArgs) -> int:
 
 def attention(q, k_cur, v_cur, k_cache: Optional[QCache], v_cache: Optional[QCache], nc: int,
               corr: str = "taylor", scale: float = 0.0, path: str = "auto", splits: int = 0,
-              out=None, workspace=None, stream=None, causal: bool = False):
+              out=None, workspace=None, stream=None, causal: bool = False, append: bool = False):
     """Corrected attention of q [B][Hq][Nq][d] (bf16) over the first nc tokens
     of the quantized caches and the bf16 current chunk [B][Hkv][Ncur][d]
-    (causal: end-aligned causal mask within the current chunk).
+    (causal: end-aligned causal mask within the current chunk; append: the
+    same call also quantises the chunk into cache rows [nc, nc + Ncur)).
     Returns out [B][Hq][Nq][d] bf16."""
     import torch
     if out is None:
         out = torch.empty_like(q)
         _keep_for(out, stream)
-    args = make_args(q, k_cur, v_cur, k_cache, v_cache, nc, out, corr, scale, path, splits, workspace, causal)
+    args = make_args(q, k_cur, v_cur, k_cache, v_cache, nc, out, corr, scale, path, splits, workspace, causal,
+                     append)
     need = workspace_size(args)
     if need > 0 and (workspace is None or args.workspace_bytes < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)

@@ -191,6 +191,17 @@ typedef struct {
                          (every query row must then see a key: Nc > 0 or Ncur >= Nq) */
   void *workspace;    /* device scratch of kv_attention_workspace_size() bytes */
   size_t workspace_bytes;
+  int32_t append;     /* 0: the caches are only read.  1: the call also quantises the
+                         chunk into rows [Nc, Nc + Ncur) of the caches, exactly as
+                         kv_quantize(k_cur, KV_BF16, B, Hkv, Ncur, d, k_cache, Nc) and
+                         the same for v_cur and v_cache write them (each block is
+                         quantised once, after it is built: "QuantWM：…" (pchao.org),
+                         section 方法概览).  Needs both caches (also when Nc = 0),
+                         grouped along the head dimension, with cap >= Nc + Ncur.  The
+                         attention itself reads rows [0, Nc) only, so its result is
+                         the same with or without the append; on a paged cache no
+                         page that rows [0, Nc) use may also hold rows being written. */
+  int32_t reserved;   /* must be 0 */
 } kv_attn_args;
 
 /* Bytes of device workspace the call needs: on the short path the
@@ -212,9 +223,12 @@ size_t kv_attention_workspace_size(const kv_attn_args *a);
  * bf16 current chunk (dequantisation, scores, correction, softmax and the
  * value product all inside the kernel).
  * Errors: KV_ERR_NULL, KV_ERR_SHAPE (also: causal with Nc = 0 and
- * Nq > Ncur), KV_ERR_UNSUPPORTED (also: causal not 0 or 1), KV_ERR_WORKSPACE,
- * KV_ERR_ALIGN, KV_ERR_ALIAS (out overlaps an input, or the bytes of the
- * workspace the call uses overlap out, an input or a page table), KV_ERR_HIP.
+ * Nq > Ncur; with append, cap < Nc + Ncur), KV_ERR_UNSUPPORTED (also: causal
+ * or append not 0 or 1, reserved not 0, append to a cache grouped along the
+ * tokens), KV_ERR_WORKSPACE, KV_ERR_ALIGN, KV_ERR_ALIAS (out overlaps an
+ * input, or the bytes of the workspace the call uses overlap out, an input
+ * or a page table; with append, q, k_cur, v_cur, out or the workspace
+ * overlaps a cache array, or the K and V caches' arrays overlap), KV_ERR_HIP.
  */
 kv_status kv_attention_corrected(const kv_attn_args *a, void *stream);
 

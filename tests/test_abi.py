@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(kvq):
 
 
 def test_version_and_status_strings(kvq):
-    assert kvq.lib.kv_version() == 7
+    assert kvq.lib.kv_version() == 8
     for s in range(1, 9):
         assert len(kvq.lib.kv_status_string(s)) > 10
     assert kvq.lib.kv_status_string(0) == b"ok"
@@ -162,6 +162,13 @@ CASES = [
     ("out aliases q", dict(out=A + 64), "KV_ERR_ALIAS"),
     ("out aliases k_cur", dict(out=2 * A), "KV_ERR_ALIAS"),
     ("causal=2", dict(causal=2), "KV_ERR_UNSUPPORTED"),
+    ("append=2", dict(append=2), "KV_ERR_UNSUPPORTED"),
+    ("reserved set", dict(reserved=1), "KV_ERR_UNSUPPORTED"),
+    ("append past cap", dict(append=1, Nc=93), "KV_ERR_SHAPE"),  # cap 100 < 93 + 8
+    ("append without caches", dict(append=1, Nc=0, k_cache=None), "KV_ERR_NULL"),
+    ("append: k_cur in the K codes", dict(append=1, k_cur=0x10000000 + 4096), "KV_ERR_ALIAS"),
+    ("append: v_cur in the V zero points", dict(append=1, v_cur=0x20000000 + 0x200000), "KV_ERR_ALIAS"),
+    ("append: q in the K steps", dict(append=1, q=0x10000000 + 0x100000 + 64), "KV_ERR_ALIAS"),
     ("causal rows without keys", dict(causal=1, Nc=0, Nq=9, Ncur=8), "KV_ERR_SHAPE"),
 ]
 
@@ -472,3 +479,22 @@ def test_static_entry_scratch_limit(kvq):
     a.k_cache, a.v_cache = C.pointer(a._k), C.pointer(a._v)
     assert kvq.lib.kv_attention_workspace_size(C.byref(a)) > kvq.STATIC_SCRATCH_BYTES
     assert st(C.byref(a), None) == kvq.KV_ERR_SCRATCH
+
+
+def test_append_cache_errors(kvq):
+    """append = 1 writes the caches: they must group along the head dimension
+    and not share bytes with each other."""
+    a = _args(kvq, append=1)
+    a._k = kvq.QTensor(0x10000000, 0x10100000, 0x10200000, 2, 64, 128, None, 0, 0, kvq.META["f32"],
+                       kvq.AXIS["tokens"])
+    a._v = kvq.QTensor(0x20000000, 0x20100000, 0x20200000, 2, 64, 128, None, 0, 0, kvq.META["f32"],
+                       kvq.AXIS["tokens"])
+    a.k_cache, a.v_cache = C.pointer(a._k), C.pointer(a._v)
+    assert _attn(kvq, a) == kvq.KV_ERR_UNSUPPORTED
+    a = _args(kvq, append=1)
+    a._v = _qt(kvq, 0x10000000 + 256)  # V arrays inside K's
+    a.v_cache = C.pointer(a._v)
+    assert _attn(kvq, a) == kvq.KV_ERR_ALIAS
+    # the same layout without append only reads the caches: no alias error
+    a.append = 0
+    assert kvq.lib.kv_attention_workspace_size(C.byref(a)) > 0

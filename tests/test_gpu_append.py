@@ -1,0 +1,143 @@
+"""The chunk append fused into kv_attention_corrected (append = 1), on the GPU.
+
+One call both attends and quantises the chunk's K and V into cache rows
+[Nc, Nc + Ncur).  Against the oracle's quantizer, those rows are bit-exact
+(codes, steps, zero points) and rows past them stay untouched.  Against two
+kv_quantize calls followed by the same attention without append, the bytes
+of every cache array and the attention output are identical.  Every kernel
+path carries the append in its own place: the throughput kernel's pre-pass,
+extra workgroups of the short-query kernel, the general kernel's pre-pass.
+The cases cover first chunks (Nc = 0), paged pools, binary16 metadata,
+groups of 32/64/128, INT2 and INT4, the causal mask, forced splits, and two
+successive chunks.  The pages ("QuantWM：…" (pchao.org), section 方法概览)
+quantise each cache block once, after it is built."""
+import numpy as np
+import pytest
+import torch
+
+from bit_kv_cache_03_amd import kvq
+from bit_kv_cache_03_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+H24, GQA = W.WORKLOADS["h24_int4_cache16k"], W.WORKLOADS["gqa_prefill_b16_cache32k"]
+OUT, TINY = W.WORKLOADS["h40_int2_outliers_cache25k"], W.WORKLOADS["tiny_d64_int2"]
+
+CASES = {
+    # name: (workload, corr, path, splits, causal, meta, page size)
+    "fast_int4": (H24.scaled(Hq=2, Hkv=2, Nq=300, Ncur=300, Nc=200), "taylor", "long", 0, False, "f32", 0),
+    "fast_first_chunk": (H24.scaled(Hq=2, Hkv=2, Nq=130, Ncur=130, Nc=0), "taylor", "long", 0, False, "f32", 0),
+    "fast_causal_split": (GQA.scaled(B=2, Hq=8, Hkv=2, Nq=70, Ncur=70, Nc=333), "off", "long", 3, True, "f32", 0),
+    "fast_g32_m16": (OUT.scaled(Hq=2, Hkv=2, Nq=100, Ncur=100, Nc=257, group=32), "taylor", "long", 0, False, "f16", 0),
+    "fast_g128_paged": (H24.scaled(Hq=2, Hkv=2, Nq=90, Ncur=90, Nc=300, group=128, vbits=2), "taylor", "long", 0,
+                        False, "f32", 64),
+    "short_gqa": (GQA.scaled(B=3, Hq=8, Hkv=2, Nq=5, Ncur=5, Nc=1000), "taylor", "short", 0, False, "f32", 0),
+    "short_decode": (GQA.scaled(B=4, Hq=8, Hkv=2, Nq=1, Ncur=1, Nc=700), "taylor", "auto", 0, False, "f32", 0),
+    "short_long_chunk": (GQA.scaled(B=2, Hq=8, Hkv=2, Nq=4, Ncur=333, Nc=500), "off", "short", 4, True, "f32", 0),
+    "short_m16_paged": (GQA.scaled(B=2, Hq=8, Hkv=2, Nq=8, Ncur=8, Nc=640, group=32), "taylor", "short", 0, False,
+                        "f16", 64),
+    "general_exact": (H24.scaled(Hq=2, Hkv=2, Nq=100, Ncur=100, Nc=150), "exact", "long", 0, False, "f32", 0),
+    "general_exact_short": (GQA.scaled(B=2, Hq=8, Hkv=2, Nq=3, Ncur=3, Nc=400), "exact", "short", 0, False, "f16", 0),
+    "general_d64": (TINY.scaled(B=2, Hq=4, Hkv=2, Nq=77, Ncur=61, Nc=300, group=32, kbits=4), "taylor", "long", 0,
+                    False, "f32", 0),
+    "general_d64_first": (TINY.scaled(B=1, Hq=2, Hkv=1, Nq=16, Ncur=16, Nc=0), "taylor", "long", 0, False, "f32", 0),
+    "general_small_pages": (GQA.scaled(B=2, Hq=8, Hkv=2, Nq=40, Ncur=40, Nc=500), "taylor", "long", 0, False, "f32",
+                            16),
+}
+
+
+def _caches(w, data, meta, ps, cap):
+    import _gpu
+    if ps:
+        kc = _gpu.paged_cache(w, data["kc"], w.kbits, ps, cap=cap, seed=5, meta=meta)
+        vc = _gpu.paged_cache(w, data["vc"], w.vbits, ps, cap=cap, seed=5, meta=meta)
+        vc.page_table = kc.page_table  # one table, as the attention call requires
+    else:
+        kc = _gpu.build_cache(w, data["kc"], w.kbits, cap=cap, meta=meta)
+        vc = _gpu.build_cache(w, data["vc"], w.vbits, cap=cap, meta=meta)
+    return kc, vc
+
+
+def _clone(c):
+    d = kvq.QCache.__new__(kvq.QCache)
+    d.__dict__.update(c.__dict__)
+    d.codes, d.scale, d.zero = c.codes.clone(), c.scale.clone(), c.zero.clone()
+    return d
+
+
+def _bytes_equal(a, b):
+    return torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
+
+
+def _check_rows(orc, c, src, bits, w, meta, label):
+    """Rows [Nc, Nc + Ncur) of cache c against the oracle's quantizer of the chunk."""
+    codes, step, zero = (t.cpu().numpy() for t in c.logical(w.Nc + w.Ncur))
+    src = src if src.dtype == np.uint16 else W.bf16_bits(src)  # the call takes the chunk in bf16
+    ref = orc.quantize(src, bits, w.group, meta=meta)
+    assert np.array_equal(codes[:, :, w.Nc:], ref[0]), (label, "codes")
+    for got, want, what in ((step, ref[1], "step"), (zero, ref[2], "zero")):
+        got = got[:, :, w.Nc:].astype(np.float32)
+        assert np.array_equal(got.view(np.uint32), want.astype(np.float32).view(np.uint32)), (label, what)
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_fused_append(orc, case):
+    import _gpu
+    w, corr, path, splits, causal, meta, ps = CASES[case]
+    print(f"[append] {case}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Ncur={w.Ncur} Nc={w.Nc} d={w.d} "
+          f"K{w.kbits}/V{w.vbits} g{w.group} {corr} {path} splits={splits} causal={causal} meta={meta} page={ps}",
+          flush=True)
+    data = W.generate(w)
+    cap = w.Nc + w.Ncur + 37
+    kc, vc = _caches(w, data, meta, ps, cap)
+    kc2, vc2 = _clone(kc), _clone(vc)
+    q = _gpu.as_bf16_dev(data["q"])
+    k = _gpu.as_bf16_dev(data["k"])
+    v = _gpu.as_bf16_dev(data["v"])
+    # fused: one call attends over rows [0, Nc) and appends the chunk
+    out_a = kvq.attention(q, k, v, kc, vc, w.Nc, corr=corr, path=path, splits=splits, causal=causal, append=True)
+    # separate: the same attention, then kv_quantize of K and V
+    out_b = kvq.attention(q, k, v, kc2 if w.Nc else None, vc2 if w.Nc else None, w.Nc, corr=corr, path=path,
+                          splits=splits, causal=causal)
+    kvq.quantize(k, kc2, w.Nc)
+    kvq.quantize(v, vc2, w.Nc)
+    torch.cuda.synchronize()
+    assert _bytes_equal(out_a, out_b), "attention output differs with the append"
+    for a, b, label in ((kc, kc2, "K"), (vc, vc2, "V")):
+        for x, y, what in ((a.codes, b.codes, "codes"), (a.scale, b.scale, "step"), (a.zero, b.zero, "zero")):
+            assert _bytes_equal(x, y), (label, what)
+    _check_rows(orc, kc, data["k"], w.kbits, w, meta, "K")
+    _check_rows(orc, vc, data["v"], w.vbits, w, meta, "V")
+    if not ps:  # rows past the chunk are untouched (zero since allocation)
+        for c in (kc, vc):
+            assert torch.count_nonzero(c.codes[:, :, w.Nc + w.Ncur:]).item() == 0
+            assert torch.count_nonzero(c.scale[:, :, w.Nc + w.Ncur:]).item() == 0
+    print("    cache bytes and output identical to kv_quantize + attention; appended rows match the oracle",
+          flush=True)
+
+
+def test_append_two_chunks(orc):
+    """Chunk-wise generation: the second call attends over the rows the
+    first call appended (and appends its own)."""
+    import _gpu
+    w = GQA.scaled(B=2, Hq=8, Hkv=2, Nq=64, Ncur=64, Nc=256)
+    print(f"[append] two chunks: B={w.B} Hq={w.Hq} Hkv={w.Hkv} Ncur={w.Ncur} Nc={w.Nc}", flush=True)
+    d1 = W.generate(w, seed=21)
+    d2 = W.generate(w, seed=22)
+    cap = w.Nc + 2 * w.Ncur
+    kc, vc = _caches(w, d1, "f32", 0, cap)
+    kc2, vc2 = _clone(kc), _clone(vc)
+    for i, d in enumerate((d1, d2)):
+        nc = w.Nc + i * w.Ncur
+        q, k, v = (_gpu.as_bf16_dev(d[x]) for x in ("q", "k", "v"))
+        oa = kvq.attention(q, k, v, kc, vc, nc, append=True)
+        ob = kvq.attention(q, k, v, kc2, vc2, nc)
+        kvq.quantize(k, kc2, nc)
+        kvq.quantize(v, vc2, nc)
+        torch.cuda.synchronize()
+        assert _bytes_equal(oa, ob), i
+    for a, b in ((kc, kc2), (vc, vc2)):
+        assert _bytes_equal(a.codes, b.codes) and _bytes_equal(a.scale, b.scale) and _bytes_equal(a.zero, b.zero)
+    k2 = orc.quantize(d2["k"], w.kbits, w.group)
+    codes = kc.codes[:, :, w.Nc + w.Ncur:].cpu().numpy()
+    assert np.array_equal(codes, k2[0])
