@@ -1,0 +1,672 @@
+// Short-query kernel for at most 16 query rows per KV head (decode and
+// small chunks of GQA heads) on gfx950: head dim 128, correction off or
+// Taylor, groups along the head dimension.
+//
+// The same split of the cache as attention_short.hip (many workgroups per
+// KV head; inside one, 4 waves that stream their own 32-key blocks with
+// private LDS tiles and merge at the end), but on 16 x 16 x 32 MFMA tiles:
+// one 16-row query tile instead of a 32-row one, so a block's scores are 8
+// per lane instead of 16 (half the exponentials, maxima and packing) and
+// the accumulators take half the registers.  The dequantisation per block is
+// the same (64 key and 64 value codes per lane).  The scores of the cached
+// keys carry the Taylor correction in extra bf16 MFMA steps ("量化鍵值偷走注意力…"
+// (agents-report.net), §方法 and §為何校正有效), with the current chunk's
+// keys left alone; everything goes through one online softmax.
+//
+// Lane roles (r = lane % 16, j = lane / 16):
+//  K (A operand of S^T = K Q^T): keys 16t + r of the block (t = 0, 1), head
+//    dims 32j .. 32j+31 (k-step s: 32j + 8s .. +7) -- one group per lane;
+//  Q (B operand): query row r of the tile, the same dims;
+//  S^T (16 x 16 per key tile): query r, keys 16t + 4j + i (i = 0..3);
+//  P^T (B operand of O^T = V^T P^T, 32 keys in one k-step): query r, k-slots
+//    8j .. 8j+7 = keys 4j .. 4j+3, then 16+4j .. 16+4j+3 -- the lane's own
+//    probabilities, so the V^T tile in LDS takes its keys in that order;
+//  V (dequantisation): keys 4kq .. 4kq+3 (kq = lane % 8), dims 16dq .. 16dq+15
+//    (dq = lane / 8), written transposed into the V^T tile;
+//  O^T (16 x 16 per head-dim tile dt): query r, dims 16dt + 4j + i.
+#include <math.h>
+
+#include "kvq_device.h"
+#include "kvq_internal.h"
+#include "quant_device.h"
+#include "short_common.h"
+
+#ifndef KVQ_SHORT16_PAGED
+#define KVQ_SHORT16_PAGED 0
+#endif
+#ifndef KVQ_SHORT16_META16
+#define KVQ_SHORT16_META16 0
+#endif
+
+namespace kvq {
+namespace {
+
+using namespace dev;
+using namespace sk;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int WAVES = 4;
+constexpr int THREADS = 64 * WAVES;
+constexpr int ROWS = 16;             // query rows of the tile
+constexpr int VS = BK + 8;           // V^T row in LDS: fp16 key slots[32], pad[8] (80 bytes)
+constexpr int VT = D * VS;           // 16-bit elements of a wave's V^T tile
+constexpr int OS = D + 4;            // fp32 row of the merge buffer
+constexpr int MERGE = ROWS * OS + 2 * ROWS;  // floats of a wave's merge buffer (O rows, then m and l)
+constexpr int LDS_BYTES = WAVES * VT * 2 > WAVES * MERGE * 4 ? WAVES * VT * 2 : WAVES * MERGE * 4;
+
+// V^T element (row = head-dim index, col = key slot 0..31); the 16-byte
+// chunks of a row are XOR-swizzled by (row / 16) % 4 so that the transposed
+// 8-byte stores of 16 consecutive rows spread over the banks.
+__device__ inline int vts(int row, int col) {
+  return row * VS + ((((col >> 3) ^ (row >> 4)) & 3) << 3) + (col & 7);
+}
+
+// Key slot of the four keys 4kq .. 4kq+3 (consecutive slots): keys below 16
+// sit at 8 (k / 4) + k % 4, keys 16 + k at 8 (k / 4) + 4 + k % 4.
+__device__ inline int vslot4(int kq) { return kq < 4 ? 8 * kq : 8 * (kq - 4) + 4; }
+
+// Registers of one prefetched cached block.
+struct Fetch {
+  uint32_t kw[2][4];  // K codes of keys 16t + r, dims [32j, 32j+32): INT4 4 words, INT2 2
+  float kstep[2];     // their group's step and zero point
+  float kzero[2];
+  uint32_t vw[4];     // V codes of keys 4kq+i at d in [16dq, 16dq+16): INT4 words
+  uint32_t vw2[4];    //   d 16dq..+7 in vw, +8..+15 in vw2; INT2 all 16 in vw
+  float vstep[4], vzero[4];
+};
+
+// Byte offsets of the lane's data from the block's first cache row; NG is
+// the number of quantisation groups per row (128 / group).
+struct Lanes {
+  uint32_t kc, km, vc, vm;
+};
+template <int KBITS, int VBITS, int NG, bool M16>
+__device__ inline Lanes lane_offsets(int lane) {
+  constexpr uint32_t KROW = D * KBITS / 8, VROW = D * VBITS / 8, ES = M16 ? 2 : 4;
+  const uint32_t r = lane & 15, j = lane >> 4, kq = lane & 7, dq = lane >> 3;
+  Lanes o;
+  o.kc = r * KROW + j * (32 * KBITS / 8);
+  o.km = (r * NG + (32 * j * NG) / D) * ES;  // the group of d = 32j
+  o.vc = 4 * kq * VROW + 16 * dq * VBITS / 8;
+  o.vm = (4 * kq * NG + (16 * dq * NG) / D) * ES;  // the group of d = 16dq
+  return o;
+}
+
+// Loads one cached block (rows [k0, k0 + 32)); rows at or past the segment
+// end read as zero (their scores are masked).  Paged: the buffer range stops
+// at the block's end, inside its page.
+template <int KBITS, int VBITS, int NG, bool PAGED, bool M16>
+__device__ inline void fetch_cached(const Ctx &c, int k0, const Lanes &o, Fetch &f, size_t pool_row = 0) {
+  constexpr uint32_t KROW = D * KBITS / 8, VROW = D * VBITS / 8, ES = M16 ? 2 : 4;
+  const uint32_t rows = static_cast<uint32_t>(PAGED ? min(c.nc - k0, BK) : c.nc - k0);
+  const size_t r0 = PAGED ? pool_row : block_row<false>(c, k0);  // paged: looked up a block earlier
+  {
+    const Buf kc = buffer_at(c.kc_codes + r0 * KROW, rows * KROW);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if (KBITS == 4) {
+        const u32x4 a = ld128(kc, o.kc + t * 16 * KROW);
+        f.kw[t][0] = a.x; f.kw[t][1] = a.y; f.kw[t][2] = a.z; f.kw[t][3] = a.w;
+      } else {
+        const u32x2 a = ld64(kc, o.kc + t * 16 * KROW);
+        f.kw[t][0] = a.x; f.kw[t][1] = a.y;
+      }
+    }
+    const Buf ks = buffer_at(meta_adv<M16>(c.kc_scale, r0 * NG), rows * NG * ES);
+    const Buf kz = buffer_at(meta_adv<M16>(c.kc_zero, r0 * NG), rows * NG * ES);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f.kstep[t] = ld_meta1<M16>(ks, o.km + t * 16 * NG * ES);
+      f.kzero[t] = ld_meta1<M16>(kz, o.km + t * 16 * NG * ES);
+    }
+  }
+  {
+    const Buf vc = buffer_at(c.vc_codes + r0 * VROW, rows * VROW);
+    const Buf vs = buffer_at(meta_adv<M16>(c.vc_scale, r0 * NG), rows * NG * ES);
+    const Buf vz = buffer_at(meta_adv<M16>(c.vc_zero, r0 * NG), rows * NG * ES);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (VBITS == 4) {
+        const u32x2 w = ld64(vc, o.vc + i * VROW);
+        f.vw[i] = w.x;
+        f.vw2[i] = w.y;
+      } else {
+        f.vw[i] = ld32(vc, o.vc + i * VROW);
+      }
+      f.vstep[i] = ld_meta1<M16>(vs, o.vm + i * NG * ES);
+      f.vzero[i] = ld_meta1<M16>(vz, o.vm + i * NG * ES);
+    }
+  }
+}
+
+// The cached keys are centred per group (group_centre) when a row has at
+// most two groups; the extra bf16 steps carry centre x query group sum.
+template <int NG>
+constexpr bool kCentre = NG <= 2;
+
+// Largest |k - centre| (|v|) a lane's share of a cached block can
+// dequantise to: the values of a group lie between z and z + (2^bits - 1) D.
+template <int KBITS, int NG>
+__device__ inline float k_bound(const Fetch &f) {
+  float b = 0.f;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const float z = kCentre<NG> ? f.kzero[t] - group_centre<KBITS>(f.kzero[t], f.kstep[t]) : f.kzero[t];
+    b = fmaxf(b, fmaxf(fabsf(z), fabsf(fmaf(f.kstep[t], static_cast<float>((1 << KBITS) - 1), z))));
+  }
+  return b;
+}
+template <int VBITS>
+__device__ inline float v_bound(const Fetch &f) {
+  float b = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    b = fmaxf(b, fmaxf(fabsf(f.vzero[i]), fabsf(fmaf(f.vstep[i], static_cast<float>((1 << VBITS) - 1), f.vzero[i]))));
+  return b;
+}
+
+// Is the lane's quarter j the first of its group (the one that carries the
+// group's terms in the extra step)?
+template <int NG>
+__device__ inline bool group_owner(int j) {
+  return NG == 4 ? true : NG == 2 ? (j & 1) == 0 : j == 0;
+}
+
+// K operands of a cached block: k[t][s] = fp16 (k - c_g) 2^-ek of key 16t + r
+// at dims 32j + 8s .. +7 (magic codes, one v_fma_mix each; c_g the group's
+// centre, 0 with 4 groups), and the extra step's slots 8j .. 8j+7, scaled
+// like the keys, on the first quarter of each group only: the Taylor terms
+// (-D^2 split hi, lo, hi; 0), then (c_g, c_g, 0, 0) with centring (the query
+// side holds N_g and the group sum against them); zero elsewhere.
+template <bool TAYLOR, int KBITS, int NG>
+__device__ inline void unpack_k_cached(const Ctx &c, int lane, const Fetch &f, float kscale, f16x8 (&k)[2][4],
+                                       bf16x8 (&kext)[2]) {
+  const bool owner = group_owner<NG>(lane >> 4);
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const float cg = kCentre<NG> ? group_centre<KBITS>(f.kzero[t], f.kstep[t]) : 0.f;
+    const float st = f.kstep[t] * kscale;
+    const float z = fmaf(-1024.0f, f.kstep[t], f.kzero[t] - cg) * kscale;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      uint32_t m[4];
+      magic8<KBITS>(KBITS == 4 ? f.kw[t][s] : (f.kw[t][s >> 1] >> (16 * (s & 1))), c.kmask, m);
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = pair_h(dequant_h(magic_code(m, 2 * e), st, z), dequant_h(magic_code(m, 2 * e + 1), st, z));
+      k[t][s] = __builtin_bit_cast(f16x8, make_uint4(w[0], w[1], w[2], w[3]));
+    }
+    const float sq = TAYLOR ? f.kstep[t] * f.kstep[t] * kscale : 0.f;
+    const float hsq = lo_f(pack2(sq, 0.f));
+    const float cs = cg * kscale;
+    uint4 x = make_uint4(pack2(-hsq, -(sq - hsq)), pack2(-hsq, 0.f), kCentre<NG> ? pack2(cs, cs) : 0u, 0u);
+    if (!owner) x = make_uint4(0u, 0u, 0u, 0u);
+    kext[t] = __builtin_bit_cast(bf16x8, x);
+  }
+}
+
+// V^T tile of a cached block: fp16 values v 2^-ev of keys 4kq..4kq+3 (slots
+// vslot4(kq) .. +3) at head-dim rows 16dq .. 16dq+15, one 8-byte store per
+// row.  One v_perm gathers the same code byte of two keys (bits 0..7 and
+// 16..23); one v_and_or turns a code field at bit p of both into the fp16
+// magic numbers 1024 + c 2^p (exact: the fp16 spacing at 1024 is 1); then
+// v 2^-ev = fma(1024 + c 2^p, D 2^-(p+ev), (z - 1024 D 2^-p) 2^-ev) with fp32
+// operands, one v_fma_mix per value rounded once to fp16.  INT4 fields sit
+// at p = 0 and 4; INT2 fields at p = 0 and 2 of the byte and of the byte
+// shifted right by 4.
+template <int VBITS>
+__device__ inline void unpack_v_cached(const Ctx &c, int lane, const Fetch &f, float vsc, uint16_t *Vt) {
+  constexpr int P1 = VBITS == 4 ? 4 : 2;
+  const int kq = lane & 7, dq = lane >> 3;
+  const int slot = vslot4(kq);
+  float dd[4][2], zz[4][2];  // per key: operands of the fields at p = 0 and p = P1
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float d0 = f.vstep[i] * vsc, z0 = f.vzero[i] * vsc;
+    dd[i][0] = d0;
+    dd[i][1] = d0 * (1.0f / (1 << P1));
+    zz[i][0] = fmaf(-1024.0f, dd[i][0], z0);
+    zz[i][1] = fmaf(-1024.0f, dd[i][1], z0);
+  }
+  auto field = [&](uint32_t r, int k, uint32_t (&x)[2], int jp) {  // k: 0 (p = 0) or 1 (p = P1)
+    const uint32_t m = (r & (k ? c.vmask1 : c.vmask0)) | 0x64006400u;
+    const f16x2 h = __builtin_bit_cast(f16x2, m);
+    x[jp] = pair_h(dequant_h(static_cast<float>(h.x), dd[2 * jp][k], zz[2 * jp][k]),
+                   dequant_h(static_cast<float>(h.y), dd[2 * jp + 1][k], zz[2 * jp + 1][k]));
+  };
+#pragma unroll
+  for (int byte = 0; byte < (VBITS == 4 ? 8 : 4); ++byte) {
+    // INT4: d = 16dq + 2byte + {0, 1} (bytes 4.. from vw2); INT2: d = 16dq + 4byte + {0, 1, 2, 3}
+    const int bw = byte & 3;
+    const uint32_t sel = static_cast<uint32_t>(bw) | 0x0c00u | (static_cast<uint32_t>(4 + bw) << 16) | 0x0c000000u;
+    uint32_t r[2];
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) {
+      const uint32_t w0 = byte >= 4 ? f.vw2[2 * jp] : f.vw[2 * jp];
+      const uint32_t w1 = byte >= 4 ? f.vw2[2 * jp + 1] : f.vw[2 * jp + 1];
+      r[jp] = __builtin_amdgcn_perm(w1, w0, sel);
+    }
+    constexpr int NF = 8 / VBITS;
+    uint32_t x[NF][2];
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) {
+      field(r[jp], 0, x[0], jp);
+      field(r[jp], 1, x[1], jp);
+      if (VBITS == 2) {
+        field(r[jp] >> 4, 0, x[NF - 2], jp);
+        field(r[jp] >> 4, 1, x[NF - 1], jp);
+      }
+    }
+#pragma unroll
+    for (int fl = 0; fl < NF; ++fl)
+      *reinterpret_cast<uint2 *>(Vt + vts(16 * dq + NF * byte + fl, slot)) = make_uint2(x[fl][0], x[fl][1]);
+  }
+}
+
+// Current-chunk block (bf16 keys and values): the lane's raw rows (same
+// lane roles as the cached blocks; rows past the end clamp to the last one,
+// their scores are masked) and the largest |k| and |v| among them.
+struct Cur {
+  uint4 k[2][4];     // keys 16t + r, d = 32j + 8s .. +7
+  uint32_t v[4][8];  // keys 4kq+i, bf16 pairs of d = 16dq + 2e, +1
+};
+__device__ inline void load_current(const Ctx &c, int k0, int lane, Cur &x, float &kb, float &vb) {
+  const int last = c.ncur - 1;
+  kb = vb = 0.f;
+  {
+    const int r = lane & 15, j = lane >> 4;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint32_t row = static_cast<uint32_t>(k0 + 16 * t + r <= last ? k0 + 16 * t + r : last);
+      const uint4 *ks = reinterpret_cast<const uint4 *>(c.k_cur + (row * D + 32u * j));
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        x.k[t][s] = ks[s];
+        const uint32_t u[4] = {x.k[t][s].x, x.k[t][s].y, x.k[t][s].z, x.k[t][s].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kb = fmaxf(kb, fmaxf(fabsf(lo_f(u[e])), fabsf(hi_f(u[e]))));
+      }
+    }
+  }
+  {
+    const int kq = lane & 7, dq = lane >> 3;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t row = static_cast<uint32_t>(k0 + 4 * kq + i <= last ? k0 + 4 * kq + i : last);
+      const uint4 *vs = reinterpret_cast<const uint4 *>(c.v_cur + (row * D + 16u * dq));
+      const uint4 y0 = vs[0], y1 = vs[1];
+      x.v[i][0] = y0.x; x.v[i][1] = y0.y; x.v[i][2] = y0.z; x.v[i][3] = y0.w;
+      x.v[i][4] = y1.x; x.v[i][5] = y1.y; x.v[i][6] = y1.z; x.v[i][7] = y1.w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vb = fmaxf(vb, fmaxf(fabsf(lo_f(x.v[i][e])), fabsf(hi_f(x.v[i][e]))));
+    }
+  }
+}
+
+// Keys to MFMA operand registers (no correction) and values to the V^T
+// tile, both rescaled to fp16.
+__device__ inline void unpack_current(int lane, const Cur &x, float kscale, float vsc, f16x8 (&k)[2][4],
+                                      uint16_t *Vt) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t u[4] = {x.k[t][s].x, x.k[t][s].y, x.k[t][s].z, x.k[t][s].w};
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = pack2h(lo_f(u[e]) * kscale, hi_f(u[e]) * kscale);
+      k[t][s] = __builtin_bit_cast(f16x8, make_uint4(w[0], w[1], w[2], w[3]));
+    }
+  const int kq = lane & 7, dq = lane >> 3;
+  const int slot = vslot4(kq);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    *reinterpret_cast<uint2 *>(Vt + vts(16 * dq + 2 * e, slot)) =
+        make_uint2(pack2h(lo_f(x.v[0][e]) * vsc, lo_f(x.v[1][e]) * vsc), pack2h(lo_f(x.v[2][e]) * vsc, lo_f(x.v[3][e]) * vsc));
+    *reinterpret_cast<uint2 *>(Vt + vts(16 * dq + 2 * e + 1, slot)) =
+        make_uint2(pack2h(hi_f(x.v[0][e]) * vsc, hi_f(x.v[1][e]) * vsc), pack2h(hi_f(x.v[2][e]) * vsc, hi_f(x.v[3][e]) * vsc));
+  }
+}
+
+// The lane's query operands (query row r of the tile, dims 32j + 8s .. +7 in
+// q[s]): the row scaled by its own power of two 2^-eq (largest |q| to
+// [2^14, 2^15)), the softmax scale of the resulting scores (alpha = tau
+// log2(e) 2^eq for keys not yet scaled), and the extra step's slots 8j ..
+// 8j+7 on the first quarter of each group: N_g = tau/24 ||q_g||^2 2^-eq as
+// (hi, hi, lo, 0) split into bf16 (zero without the correction), then the
+// group sum S_g = sum_{c in g} q_c 2^-eq as (hi, lo, 0, 0) with centring.
+template <bool TAYLOR, int NG>
+__device__ inline void load_query(const uint16_t *qptr, int lane, float tau, f16x8 (&q)[4], bf16x8 &qext,
+                                  float &alpha) {
+  const int j = lane >> 4;
+  uint4 qw[4];
+  float nsum = 0.f, qsum = 0.f, qmax = 0.f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    qw[s] = *reinterpret_cast<const uint4 *>(qptr + 32 * j + 8 * s);
+    const uint32_t u[4] = {qw[s].x, qw[s].y, qw[s].z, qw[s].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      nsum += lo_f(u[e]) * lo_f(u[e]) + hi_f(u[e]) * hi_f(u[e]);
+      qsum += lo_f(u[e]) + hi_f(u[e]);
+      qmax = fmaxf(qmax, fmaxf(fabsf(lo_f(u[e])), fabsf(hi_f(u[e]))));
+    }
+  }
+  qmax = fmaxf(qmax, __shfl_xor(qmax, 16, 64));
+  qmax = fmaxf(qmax, __shfl_xor(qmax, 32, 64));
+  // group sums: one quarter per group (4 groups), two (2), four (1)
+  if (NG <= 2) {
+    nsum += __shfl_xor(nsum, 16, 64);
+    qsum += __shfl_xor(qsum, 16, 64);
+  }
+  if (NG == 1) {
+    nsum += __shfl_xor(nsum, 32, 64);
+    qsum += __shfl_xor(qsum, 32, 64);
+  }
+  const int eq = scale_exponent(qmax);
+  const float qs_scale = ldexpf(1.0f, -eq);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const uint32_t u[4] = {qw[s].x, qw[s].y, qw[s].z, qw[s].w};
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = pack2h(lo_f(u[e]) * qs_scale, hi_f(u[e]) * qs_scale);
+    q[s] = __builtin_bit_cast(f16x8, make_uint4(w[0], w[1], w[2], w[3]));
+  }
+  alpha = tau * kLog2e * ldexpf(1.0f, eq);
+  const float n = TAYLOR ? nsum * (tau / 24.0f) * qs_scale : 0.f;
+  const float nh = lo_f(pack2(n, 0.f)), nl = n - nh;
+  const float t = qsum * qs_scale;
+  const float th = lo_f(pack2(t, 0.f)), tl = t - th;
+  uint4 x = make_uint4(pack2(nh, nh), pack2(nl, 0.f), kCentre<NG> ? pack2(th, tl) : 0u, 0u);
+  if (!group_owner<NG>(j)) x = make_uint4(0u, 0u, 0u, 0u);
+  qext = __builtin_bit_cast(bf16x8, x);
+}
+
+struct Soft {
+  f32x4 o[D / 16];
+  float m, l, alpha;
+};
+
+// Scores, softmax and value product of one block: K operand registers, the
+// wave's V^T tile, the block's score scale alpha (scores are q.k 2^-(eq+ek))
+// and value exponent ev.  count < BK marks a ragged block; CORR adds the
+// correction steps.  CAUSAL: count is the lane's own (possibly <= 0), and a
+// row may have seen no key yet (m = -inf).
+template <bool CORR, bool CAUSAL = false>
+__device__ inline void block_compute(const f16x8 (&k)[2][4], const bf16x8 (&kext)[2], const uint16_t *Vt,
+                                     const f16x8 (&q)[4], bf16x8 qext, int count, float alpha, int ev, int lane,
+                                     Soft &st) {
+  const float fev = static_cast<float>(ev);
+  const int r = lane & 15, j = lane >> 4;
+  f32x4 s[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k[t][i], q[i], s[t], 0, 0, 0);
+    if (CORR) s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kext[t], qext, s[t], 0, 0, 0);
+  }
+  if (CAUSAL || count < BK) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (16 * t + 4 * j + i >= count) s[t][i] = -INFINITY;
+  }
+  float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                   fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+  mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+  mt = fmaf(fmaxf(mt, __shfl_xor(mt, 32, 64)), alpha, fev);
+  const bool grow = mt > st.m + kLazy;
+  if (__any(grow)) {
+    const float m_new = grow ? mt : st.m;
+    const float sc = CAUSAL && !grow ? 1.f : exp2f(st.m - m_new);
+    st.l *= sc;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) st.o[dt] *= sc;
+    st.m = m_new;
+  }
+  const float shift = fev - st.m;
+  float e[2][4];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      e[t][i] = __builtin_amdgcn_exp2f(fmaf(s[t][i], alpha, shift));
+      if (CAUSAL && s[t][i] == -INFINITY) e[t][i] = 0.f;  // shift is +inf while m = -inf
+    }
+  const f16x8 pk = __builtin_bit_cast(
+      f16x8, make_uint4(pack2h(e[0][0], e[0][1]), pack2h(e[0][2], e[0][3]), pack2h(e[1][0], e[1][1]),
+                        pack2h(e[1][2], e[1][3])));
+  st.l = fmaf(sum8h(pk, 0.f), ldexpf(1.0f, -ev), st.l);
+  // O^T += V^T P^T: head-dim tile dt, the block's 32 keys in one k-step
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt)
+    st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const f16x8 *>(Vt + vts(16 * dt + r, 8 * j)),
+                                                      pk, st.o[dt], 0, 0, 0);
+}
+
+template <int KBITS, int VBITS, bool TAYLOR, int NG, bool CAUSAL, bool PAGED, bool M16>
+__global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, int64_t rows_per_kvhead,
+                                                                  int32_t nsplit, float *ws) {
+  __shared__ __attribute__((aligned(16))) uint16_t L[LDS_BYTES / 2];
+
+  const int tid = threadIdx.x;
+  if (blockIdx.x >= p.app.wg0) {  // the chunk append's workgroups
+    qdev::append_workgroup(p, blockIdx.x - p.app.wg0, tid, THREADS);
+    return;
+  }
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: block loop control stays scalar
+  const int r = lane & 15;
+
+  // Workgroups are dealt to the 8 XCDs round-robin by id; renumber so that
+  // consecutive ids (the splits of one KV head) share an XCD.
+  const uint32_t nwg = static_cast<uint32_t>(p.app.wg0), wg = blockIdx.x;
+  const uint32_t per = nwg >> 3, extra = nwg & 7, xcd = wg & 7, slotw = wg >> 3;
+  const uint32_t lin = (xcd < extra ? xcd * (per + 1) : extra * (per + 1) + (xcd - extra) * per) + slotw;
+  const int64_t split = lin % static_cast<uint32_t>(nsplit);
+  const int64_t bkv = lin / static_cast<uint32_t>(nsplit);
+  const int64_t b = bkv / p.Hkv, hk = bkv - b * p.Hkv;
+  const int64_t gq = p.Hq / p.Hkv;
+
+  // the lane's query row (every quarter and every wave holds the 16 rows)
+  const bool row_ok = r < rows_per_kvhead;
+  const int64_t rr = row_ok ? r : rows_per_kvhead - 1;
+  const int64_t qrow = (b * p.Hq + hk * gq + rr / p.Nq) * p.Nq + rr % p.Nq;
+  f16x8 q[4];
+  bf16x8 qext;
+  Soft st;
+  load_query<TAYLOR, NG>(p.q + qrow * D, lane, p.tau, q, qext, st.alpha);
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.l = 0.f;
+
+  Ctx c{};
+  c.nc = static_cast<int>(p.Nc);
+  c.ncur = static_cast<int>(p.Ncur);
+  c.kmask = opaque_u32(kCodeMask<KBITS>);
+  c.vmask0 = opaque_u32(VBITS == 4 ? 0x000f000fu : 0x00030003u);
+  c.vmask1 = opaque_u32(VBITS == 4 ? 0x00f000f0u : 0x000c000cu);
+  c.layout = p.layout;
+  c.cap = p.cap;
+  c.H = p.Hkv;
+  c.b = b;
+  c.hk = hk;
+  if (p.Nc > 0) {
+    const int64_t hrow = PAGED ? 0 : bkv * p.cap;  // paged: the pointers stay at the pool
+    c.kc_codes = p.kc_codes + hrow * (D * KBITS / 8);
+    c.vc_codes = p.vc_codes + hrow * (D * VBITS / 8);
+    c.kc_scale = meta_adv<M16>(p.kc_scale, hrow * NG);
+    c.kc_zero = meta_adv<M16>(p.kc_zero, hrow * NG);
+    c.vc_scale = meta_adv<M16>(p.vc_scale, hrow * NG);
+    c.vc_zero = meta_adv<M16>(p.vc_zero, hrow * NG);
+  }
+  if (p.Ncur > 0) {
+    c.k_cur = p.k_cur + bkv * p.Ncur * D;
+    c.v_cur = p.v_cur + bkv * p.Ncur * D;
+  }
+
+  // key blocks: cached [0, nbc), current [nbc, nbt); this split's range,
+  // dealt to the waves round-robin
+  const int nbc = (c.nc + BK - 1) / BK, nbt = nbc + (c.ncur + BK - 1) / BK;
+  const int bps = (nbt + nsplit - 1) / nsplit;
+  const int bbeg = static_cast<int>(split) * bps;
+  int bend = bbeg + bps < nbt ? bbeg + bps : nbt;
+  // causal mask: current keys below climit are visible to the lane's row
+  // (query j of Nq, aligned to the chunk's end); the workgroup stops at the
+  // largest limit of its rows
+  const int climit = static_cast<int>(rr % p.Nq + p.Ncur - p.Nq + 1);
+  if (CAUSAL) {
+    const int64_t r1 = rows_per_kvhead - 1;
+    const int64_t wlim = (r1 / p.Nq == 0 ? r1 % p.Nq : p.Nq - 1) + p.Ncur - p.Nq + 1;
+    const int cb = nbc + static_cast<int>(wlim > 0 ? (wlim + BK - 1) / BK : 0);
+    if (bend > cb) bend = cb;
+  }
+  uint16_t *Vt = L + wave * VT;
+
+  int blk = bbeg + wave;
+  const int cend = bend < nbc ? bend : nbc;
+  const Lanes lo = lane_offsets<KBITS, VBITS, NG, M16>(lane);
+  Scales sc;
+  f16x8 kreg[2][4];
+  bf16x8 kext[2] = {};
+  Fetch f;
+  if (blk < cend) fetch_cached<KBITS, VBITS, NG, PAGED, M16>(c, blk * BK, lo, f, block_row<PAGED>(c, blk * BK));
+  // paged: the pool row of the next block to fetch, looked up one block ahead
+  // so that its scalar load has completed when the fetch needs it
+  size_t prn = PAGED && blk + WAVES < cend ? block_row<PAGED>(c, (blk + WAVES) * BK) : 0;
+  for (; blk < cend; blk += WAVES) {
+    const int k0 = blk * BK;
+    const int count = c.nc - k0 < BK ? c.nc - k0 : BK;
+    sc.update(k_bound<KBITS, NG>(f), v_bound<VBITS>(f), st.alpha);
+    unpack_k_cached<TAYLOR, KBITS, NG>(c, lane, f, sc.kscale, kreg, kext);
+    unpack_v_cached<VBITS>(c, lane, f, sc.vscale, Vt);
+    if (blk + WAVES < cend) fetch_cached<KBITS, VBITS, NG, PAGED, M16>(c, (blk + WAVES) * BK, lo, f, prn);
+    block_compute<TAYLOR || kCentre<NG>>(kreg, kext, Vt, q, qext, count, sc.alpha, sc.ev, lane, st);
+    if (PAGED && blk + 2 * WAVES < cend) prn = block_row<PAGED>(c, (blk + 2 * WAVES) * BK);
+  }
+  for (; blk < bend; blk += WAVES) {
+    const int k0 = (blk - nbc) * BK;
+    int count = c.ncur - k0 < BK ? c.ncur - k0 : BK;
+    if (CAUSAL) count = min(count, climit - k0);
+    Cur x;
+    float kb, vb;
+    load_current(c, k0, lane, x, kb, vb);
+    sc.update(kb, vb, st.alpha);
+    unpack_current(lane, x, sc.kscale, sc.vscale, kreg, Vt);
+    block_compute<false, CAUSAL>(kreg, kext, Vt, q, qext, count, sc.alpha, sc.ev, lane, st);
+  }
+
+  // ---- merge the 4 waves (log-sum-exp), then the split partial or output ----
+  float l_tot = st.l + __shfl_xor(st.l, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  __syncthreads();  // every wave is done with its tiles
+  float *Ob = reinterpret_cast<float *>(L) + wave * MERGE;
+  float *ml = Ob + ROWS * OS;
+  const int j = lane >> 4;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt)
+    *reinterpret_cast<float4 *>(Ob + r * OS + 16 * dt + 4 * j) =
+        make_float4(st.o[dt][0], st.o[dt][1], st.o[dt][2], st.o[dt][3]);
+  if (j == 0) {
+    ml[2 * r] = st.m;
+    ml[2 * r + 1] = l_tot;
+  }
+  __syncthreads();
+  {
+    const int row = tid >> 4, d0 = (tid & 15) * 8;  // 16 rows x 16 chunks of 8
+    if (row < rows_per_kvhead) {
+      float mw[WAVES], m = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) {
+        mw[w] = reinterpret_cast<const float *>(L)[w * MERGE + ROWS * OS + 2 * row];
+        m = fmaxf(m, mw[w]);
+      }
+      float acc[8], l = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) {
+        const float *base = reinterpret_cast<const float *>(L) + w * MERGE;
+        const float fw = mw[w] == -INFINITY ? 0.f : exp2f(mw[w] - m);
+        l += fw * base[ROWS * OS + 2 * row + 1];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += fw * base[row * OS + d0 + e];
+      }
+      const int64_t orow = (b * p.Hq + hk * gq + row / p.Nq) * p.Nq + row % p.Nq;
+      if (nsplit > 1) {
+        float *w = ws + (split * (p.B * p.Hq * p.Nq) + orow) * kPartialStride(D);
+#pragma unroll
+        for (int e = 0; e < 8; e += 4)
+          *reinterpret_cast<float4 *>(w + d0 + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+        if ((tid & 15) == 0) {
+          w[D] = m;
+          w[D + 1] = l;
+        }
+      } else {
+        const float inv = 1.0f / l;
+        uint16_t *o = p.out + orow * D + d0;
+        *reinterpret_cast<uint4 *>(o) = make_uint4(pack2(acc[0] * inv, acc[1] * inv), pack2(acc[2] * inv, acc[3] * inv),
+                                                   pack2(acc[4] * inv, acc[5] * inv), pack2(acc[6] * inv, acc[7] * inv));
+      }
+    }
+  }
+}
+
+template <int KB, int VB, int NG>
+void launch_kernel(const AttnLaunch &p, hipStream_t stream, dim3 grid, int64_t rows, float *partials) {
+  constexpr bool PG = KVQ_SHORT16_PAGED != 0, MH = KVQ_SHORT16_META16 != 0;
+  auto kernel = p.corr == KV_CORR_TAYLOR ? (p.causal ? attn_short16_kernel<KB, VB, true, NG, true, PG, MH>
+                                                     : attn_short16_kernel<KB, VB, true, NG, false, PG, MH>)
+                                         : (p.causal ? attn_short16_kernel<KB, VB, false, NG, true, PG, MH>
+                                                     : attn_short16_kernel<KB, VB, false, NG, false, PG, MH>);
+  kernel<<<grid, dim3(THREADS), 0, stream>>>(p, rows, p.splits, partials);
+}
+
+template <int KB, int VB>
+hipError_t launch_bits(const AttnLaunch &p, hipStream_t stream) {
+  const int64_t rows = p.Nq * (p.Hq / p.Hkv);
+  const int64_t nrows = p.B * p.Hq * p.Nq;
+  float *partials = static_cast<float *>(p.workspace);
+  // attention workgroups, then those of the chunk append (about 64 rows of
+  // K and of V each)
+  AttnLaunch pa = p;
+  pa.app.wg0 = static_cast<int64_t>(p.splits) * p.B * p.Hkv;
+  const int64_t append_wgs = (p.B * p.Hkv * p.Ncur + 63) / 64;
+  pa.app.wgs = p.app.on ? static_cast<int32_t>(append_wgs < 4096 ? append_wgs : 4096) : 0;
+  const dim3 grid(static_cast<uint32_t>(pa.app.wg0 + pa.app.wgs));
+  if (p.group == 128)
+    launch_kernel<KB, VB, 1>(pa, stream, grid, rows, partials);
+  else if (p.group == 64)
+    launch_kernel<KB, VB, 2>(pa, stream, grid, rows, partials);
+  else
+    launch_kernel<KB, VB, 4>(pa, stream, grid, rows, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.splits == 1) return e;
+  return launch_combine(partials, p.out, nrows, p.splits, p.d, stream);
+}
+
+}  // namespace
+
+#if KVQ_SHORT16_PAGED && KVQ_SHORT16_META16
+hipError_t launch_attention_short16_m16_paged(const AttnLaunch &p, hipStream_t stream) {
+#elif KVQ_SHORT16_PAGED
+hipError_t launch_attention_short16_paged(const AttnLaunch &p, hipStream_t stream) {
+#elif KVQ_SHORT16_META16
+hipError_t launch_attention_short16_m16(const AttnLaunch &p, hipStream_t stream) {
+#else
+hipError_t launch_attention_short16(const AttnLaunch &p, hipStream_t stream) {
+#endif
+  const int kb = p.Nc > 0 ? p.kbits : 2, vb = p.Nc > 0 ? p.vbits : 2;
+  if (kb == 2 && vb == 2) return launch_bits<2, 2>(p, stream);
+  if (kb == 2 && vb == 4) return launch_bits<2, 4>(p, stream);
+  if (kb == 4 && vb == 2) return launch_bits<4, 2>(p, stream);
+  return launch_bits<4, 4>(p, stream);
+}
+
+}  // namespace kvq

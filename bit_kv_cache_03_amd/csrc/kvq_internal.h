@@ -161,6 +161,14 @@ hipError_t launch_attention_short_fast(const AttnLaunch &p, hipStream_t stream);
 hipError_t launch_attention_short_fast_paged(const AttnLaunch &p, hipStream_t stream);
 hipError_t launch_attention_short_fast_m16(const AttnLaunch &p, hipStream_t stream);
 hipError_t launch_attention_short_fast_m16_paged(const AttnLaunch &p, hipStream_t stream);
+// The short-query kernel on 16-row query tiles (attention_short16.hip), for
+// at most 16 query rows per KV head; its paged, binary16 and paged binary16
+// instances in attention_short16_paged.hip, attention_short16_m16.hip,
+// attention_short16_m16_paged.hip.  Same workspace and split count.
+hipError_t launch_attention_short16(const AttnLaunch &p, hipStream_t stream);
+hipError_t launch_attention_short16_paged(const AttnLaunch &p, hipStream_t stream);
+hipError_t launch_attention_short16_m16(const AttnLaunch &p, hipStream_t stream);
+hipError_t launch_attention_short16_m16_paged(const AttnLaunch &p, hipStream_t stream);
 
 // Everything a diagnostics launch needs, already validated by the host.
 struct DiagLaunch {
