@@ -45,7 +45,16 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* The enumerations are 32-bit integers.  C++ sees them with that fixed
+ * underlying type, so any int32 value a caller passes (including the
+ * values that the entry points refuse) is a valid value of the type. */
+#ifdef __cplusplus
+#define KV_ENUM_TYPE : int32_t
+#else
+#define KV_ENUM_TYPE
+#endif
+
+typedef enum KV_ENUM_TYPE {
   KV_OK = 0,
   KV_ERR_NULL = 1,        /* a required pointer is NULL */
   KV_ERR_SHAPE = 2,       /* sizes inconsistent or out of range */
@@ -58,10 +67,10 @@ typedef enum {
                              than KV_STATIC_SCRATCH_BYTES */
 } kv_status;
 
-typedef enum { KV_BF16 = 0, KV_F32 = 1 } kv_dtype;
+typedef enum KV_ENUM_TYPE { KV_BF16 = 0, KV_F32 = 1 } kv_dtype;
 
 /* Correction applied to cached-key logits. */
-typedef enum {
+typedef enum KV_ENUM_TYPE {
   KV_CORR_OFF = 0,    /* plain softmax over [dequantised cache ; current chunk] */
   KV_CORR_TAYLOR = 1, /* b = (tau^2/24) sum_g D_g^2 ||q_g||^2  (page 方法 formula) */
   KV_CORR_EXACT = 2   /* b = sum_c log(sinh x_c / x_c), x_c = tau q_c D_{g(c)} / 2:
@@ -69,7 +78,7 @@ typedef enum {
 } kv_corr;
 
 /* Storage type of a cache tensor's step D and zero point z. */
-typedef enum {
+typedef enum KV_ENUM_TYPE {
   KV_META_F32 = 0, /* fp32 (default) */
   KV_META_F16 = 1  /* IEEE binary16: D and z rounded (nearest, ties to even) before
                       the codes are taken, so that z + D c uses what is stored; 2x less
@@ -79,7 +88,7 @@ typedef enum {
 
 /* Axis along which a cache tensor's groups run (agents-report.net page,
  * §方法: the correction uses one step per group or per channel, D_{i,c}). */
-typedef enum {
+typedef enum KV_ENUM_TYPE {
   KV_AXIS_DIM = 0,    /* along the head dimension (default): one D, z per token and
                          group of `group` channels; scale/zero [..][cap][d/group] */
   KV_AXIS_TOKENS = 1  /* along the tokens, per channel: one D, z per channel and group
@@ -91,7 +100,7 @@ typedef enum {
 } kv_axis;
 
 /* Kernel path.  AUTO picks by rows per KV head; tests may force either. */
-typedef enum {
+typedef enum KV_ENUM_TYPE {
   KV_PATH_AUTO = 0,
   KV_PATH_LONG = 1,  /* MFMA tile kernel, query rows tiled, one pass over keys */
   KV_PATH_SHORT = 2  /* split over cached tokens + log-sum-exp combine */
