@@ -75,7 +75,11 @@ __device__ inline float group_centre(float z, float step) {
 }
 
 // Codes as fp16 "magic" values 1024 + c (exact: the fp16 spacing at 1024 is
-// 1), built two at a time: m[j] holds codes j (low half) and j + 4 (high
+// 1): the integer-to-fp16 conversion by OR-ing the integer into the mantissa
+// of 1024 (0x6400) and folding the 1024 offset into the following affine
+// step, as published for INT4/INT8 weight dequantisation by Kim et al.,
+// "Who Says Elephants Can't Run: Bringing Large Scale MoE Models into Cloud
+// Scale Production" (2022).  Built here two at a time: m[j] holds codes j (low half) and j + 4 (high
 // half) of 8 codes of BITS bits stored LSB first in the low 8*BITS bits of
 // w.  A value z + D c is then fma(1024 + c, D, z - 1024 D) in fp32, which
 // v_fma_mix evaluates straight from the fp16 half and rounds to fp16.
