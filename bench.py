@@ -203,7 +203,10 @@ class ClockProbe:
             return {"sclk_mhz_median": float(np.median(g)) if g else None, "sclk_mhz_max": max(g) if g else None,
                     "sclk_max_mhz": gs[0].get("max_clk"), "mclk_mhz_median": float(np.median(m)) if m else None,
                     "mclk_max_mhz": ms[0].get("max_clk"), "samples": len(gs), "bdf": self.bdf,
-                    "source": "amdsmi, polled every ~2 ms from the enqueue of the timed steps to their end"}
+                    "source": "amdsmi, polled every ~2 ms from the enqueue of the timed steps to their end",
+                    "note": "as amdsmi reports them: on the MI355X systems measured here the readings stay near "
+                            "the idle level under load (a bf16 GEMM read 224 MHz on every XCD), so they are a "
+                            "record, not the clock the kernels ran at"}
         except Exception as e:
             return {"error": f"{type(e).__name__}: {e}"}
 

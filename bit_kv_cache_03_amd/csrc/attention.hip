@@ -623,8 +623,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_tile_kernel(AttnLaunch p, in
 }
 
 // Value pre-pass: workgroup (chunk, b * Hkv + hk) bounds |v| over its
-// share of the head's cached value groups (max(|z|, |z + top D|) per group)
-// and of its current-chunk values, and writes the bound to
+// share of the head's cached value groups (max(|z|, |z + top D|) per group;
+// chunk 0 takes the cache's running bound instead when it keeps one) and of
+// its current-chunk values, and writes the bound to
 // part[(b * Hkv + hk) * kVChunks + chunk].  APPEND: the call's chunk append
 // rides along -- the workgroup also quantises its share of the chunk's K and
 // V rows into the caches, from the values it loads for the bound.
@@ -634,7 +635,9 @@ __global__ __launch_bounds__(256) void value_bound_kernel(AttnLaunch p, int32_t 
   const int64_t ch = blockIdx.x, bkv = blockIdx.y;
   const int64_t b = bkv / p.Hkv, hk = bkv - b * p.Hkv;
   float vm = 0.f;
-  if (p.Nc > 0) {
+  if (p.Nc > 0 && p.vc_bound) {  // the value cache's running bound
+    vm = ch == 0 ? p.vc_bound[bkv] : 0.f;
+  } else if (p.Nc > 0) {
     const float top = static_cast<float>((1 << p.vbits) - 1);
     const bool tok = p.vtok;
     // groups along the head dim: Nc rows of d/G groups; along the tokens:
@@ -653,7 +656,10 @@ __global__ __launch_bounds__(256) void value_bound_kernel(AttnLaunch p, int32_t 
   if (APPEND) {  // the chunk's rows in this share: the value bound, and the codes of both tensors
     const int64_t r0 = bkv * p.Ncur + p.Ncur * ch / kVChunks, r1 = bkv * p.Ncur + p.Ncur * (ch + 1) / kVChunks;
     float kb = 0.f;
-    qdev::append_rows(p, r0, r1, true, tid, 256, kb, vm);
+    qdev::RowBounds rb;
+    qdev::append_rows(p, r0, r1, true, tid, 256, kb, vm, rb);
+    qdev::raise_bound(p.app.bound[0], bkv, rb.k);  // the rows are all of (b, KV head) bkv
+    qdev::raise_bound(p.app.bound[1], bkv, rb.v);
   } else {  // current chunk: bf16 pairs
     const uint32_t *w = reinterpret_cast<const uint32_t *>(p.v_cur + bkv * p.Ncur * p.d);
     const int64_t n = p.Ncur * p.d / 2, lo = n * ch / kVChunks, hi = n * (ch + 1) / kVChunks;

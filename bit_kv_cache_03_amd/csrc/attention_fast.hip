@@ -179,8 +179,8 @@ __device__ inline float cache_bound(const AttnLaunch &p, const float *scale, con
 }
 
 // Pre-pass: workgroup (b * Hkv + hk) * KCHUNKS + chunk bounds |key|, |query|
-// and |value| over its share of the head's cache groups, current chunk and
-// query rows.  APPEND: the call's chunk append rides along -- the workgroup
+// and |value| over its share of the head's cache groups (or takes the
+// caches' running bounds, chunk 0), current chunk and query rows.  APPEND: the call's chunk append rides along -- the workgroup
 // also quantises its share of the chunk's K and V rows into the caches, from
 // the values it loads for the bounds.
 template <int KBITS, bool M16, bool APPEND>
@@ -191,13 +191,24 @@ __global__ __launch_bounds__(256) void key_scale_kernel(AttnLaunch p, int32_t ng
   const int64_t ch = blockIdx.x % KCHUNKS;
   const int tid = threadIdx.x;
   float kb = 0.f, vb = 0.f;
-  if (p.Nc > 0) {
-    kb = cache_bound<M16, NT>(p, p.kc_scale, p.kc_zero, static_cast<float>((1 << KBITS) - 1), ng, bkv, ch, tid);
-    vb = cache_bound<M16, NT>(p, p.vc_scale, p.vc_zero, static_cast<float>((1 << p.vbits) - 1), ng, bkv, ch, tid);
+  if (p.Nc > 0) {  // the caches' running bounds when they keep them, else a scan of the metadata
+    kb = p.kc_bound ? (ch == 0 ? p.kc_bound[bkv] : 0.f)
+                    : cache_bound<M16, NT>(p, p.kc_scale, p.kc_zero, static_cast<float>((1 << KBITS) - 1), ng, bkv,
+                                           ch, tid);
+    vb = p.vc_bound ? (ch == 0 ? p.vc_bound[bkv] : 0.f)
+                    : cache_bound<M16, NT>(p, p.vc_scale, p.vc_zero, static_cast<float>((1 << p.vbits) - 1), ng, bkv,
+                                           ch, tid);
   }
   if (APPEND && p.Ncur > 0) {  // the chunk's rows in this share: their bounds, and their codes
     const int64_t r0 = bkv * p.Ncur + p.Ncur * ch / KCHUNKS, r1 = bkv * p.Ncur + p.Ncur * (ch + 1) / KCHUNKS;
-    qdev::append_rows(p, r0, r1, true, tid, NT, kb, vb);
+    qdev::RowBounds rb;
+    qdev::append_rows(p, r0, r1, true, tid, NT, kb, vb, rb);
+    // the rows are all of (b, KV head) bkv: one atomic per cache for the workgroup
+    const float rk = block_max<NT>(rb.k, red, tid), rv = block_max<NT>(rb.v, red, tid);
+    if (tid == 0) {
+      if (p.app.bound[0] && rk > 0.f) atomicMax(reinterpret_cast<int *>(p.app.bound[0]) + bkv, __float_as_int(rk));
+      if (p.app.bound[1] && rv > 0.f) atomicMax(reinterpret_cast<int *>(p.app.bound[1]) + bkv, __float_as_int(rv));
+    }
   } else if (p.Ncur > 0) {
     const int64_t n = p.Ncur * D / 8, lo = n * ch / KCHUNKS, hi = n * (ch + 1) / KCHUNKS;
     kb = fmaxf(kb, bf16_bound<NT>(p.k_cur + bkv * p.Ncur * D, lo, hi, tid));

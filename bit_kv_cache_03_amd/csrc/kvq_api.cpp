@@ -13,7 +13,7 @@ namespace {
 
 using kvq::AttnLaunch;
 
-constexpr int32_t kAbiVersion = 8;
+constexpr int32_t kAbiVersion = 9;
 constexpr int32_t kMaxSplits = 1024;  // grid z extent of the split path
 constexpr int64_t kMaxTokensPerHead = int64_t(1) << 23;  // 8M tokens: 32-bit in-head offsets
 
@@ -64,6 +64,7 @@ kv_status check_qtensor(const kv_qtensor *t, int32_t d, int64_t need_rows, int64
     return KV_ERR_SHAPE;
   if (t->cap > kMaxTokensPerHead) return KV_ERR_UNSUPPORTED;
   if (!aligned16(t->codes) || !aligned16(t->scale) || !aligned16(t->zero)) return KV_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(t->bound) & 3u) != 0) return KV_ERR_ALIGN;
   if (t->meta != KV_META_F32 && t->meta != KV_META_F16) return KV_ERR_UNSUPPORTED;
   if (t->page_table) {
     if (!page_size_ok(t->page_size) || t->cap % t->page_size != 0) return KV_ERR_SHAPE;
@@ -143,7 +144,8 @@ bool overlaps_cache(const kv_attn_args *a, const kv_qtensor *c, const void *p, s
   const size_t rows = static_cast<size_t>(tensor_rows(c, a->B, a->Hkv));
   return overlaps(p, n, c->codes, rows * static_cast<size_t>(a->d * c->bits / 8)) ||
          overlaps(p, n, c->scale, meta_array_bytes(c, rows, a->d)) ||
-         overlaps(p, n, c->zero, meta_array_bytes(c, rows, a->d));
+         overlaps(p, n, c->zero, meta_array_bytes(c, rows, a->d)) ||
+         overlaps(p, n, c->bound, static_cast<size_t>(a->B * a->Hkv) * sizeof(float));
 }
 
 kv_status validate_attention(const kv_attn_args *a) {
@@ -401,19 +403,21 @@ kv_status kv_quantize(const void *x, kv_dtype xdt, int64_t B, int64_t H, int64_t
   if (!mul_ok(B, H, &t) || !mul_ok(t, N, &t) || !mul_ok(t, d, &t) || t > (int64_t(1) << 40)) return KV_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(dst->codes) || !aligned16(dst->scale) || !aligned16(dst->zero))
     return KV_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(dst->bound) & 3u) != 0) return KV_ERR_ALIGN;
   if (dst->meta != KV_META_F32 && dst->meta != KV_META_F16) return KV_ERR_UNSUPPORTED;
   {  // the input must not overlap the cache it is written into
     const size_t xb = static_cast<size_t>(t) * (xdt == KV_BF16 ? 2 : 4);
     const size_t rows = static_cast<size_t>(tensor_rows(dst, B, H));
     if (overlaps(x, xb, dst->codes, rows * static_cast<size_t>(d * dst->bits / 8)) ||
         overlaps(x, xb, dst->scale, meta_array_bytes(dst, rows, d)) ||
-        overlaps(x, xb, dst->zero, meta_array_bytes(dst, rows, d)))
+        overlaps(x, xb, dst->zero, meta_array_bytes(dst, rows, d)) ||
+        overlaps(x, xb, dst->bound, static_cast<size_t>(B * H) * sizeof(float)))
       return KV_ERR_ALIAS;
   }
   if (N == 0) return KV_OK;
   kvq::QuantizeLaunch p{x, static_cast<int>(xdt), B, H, N, d, dst->codes, static_cast<float *>(dst->scale),
                         static_cast<float *>(dst->zero), dst->bits, dst->group, dst->cap, tok_offset,
-                        layout_of(dst), dst->meta == KV_META_F16, dst->axis == KV_AXIS_TOKENS};
+                        layout_of(dst), dst->meta == KV_META_F16, dst->axis == KV_AXIS_TOKENS, dst->bound};
   return kvq::launch_quantize(p, static_cast<hipStream_t>(stream)) == hipSuccess ? KV_OK : KV_ERR_HIP;
 }
 
@@ -446,6 +450,8 @@ kv_status launch_attention(const kv_attn_args *a, const Plan &pl, void *workspac
     p.vtok = a->v_cache->axis == KV_AXIS_TOKENS;
     p.kbits = a->k_cache->bits; p.vbits = a->v_cache->bits; p.group = a->k_cache->group; p.cap = a->k_cache->cap;
     p.layout = layout_of(a->k_cache);
+    p.kc_bound = a->k_cache->bound;
+    p.vc_bound = a->v_cache->bound;
   } else {
     p.kbits = 2; p.vbits = 2; p.group = a->d; p.cap = 0;
   }
@@ -470,6 +476,8 @@ kv_status launch_attention(const kv_attn_args *a, const Plan &pl, void *workspac
     p.app.meta16 = k->meta == KV_META_F16;
     p.app.cap = k->cap;
     p.app.layout = layout_of(k);
+    p.app.bound[0] = k->bound;
+    p.app.bound[1] = v->bound;
   }
   if (debug_log())
     fprintf(stderr,

@@ -47,6 +47,7 @@ struct QuantizeLaunch {
   CacheLayout layout;
   bool meta16;  // scale and zero are binary16 (the pointers are then read as such)
   bool tokens;  // groups along the tokens: scale/zero [row / group][d], row the cache row
+  float *bound;  // [B][H] running bound of |z|, |z + top D| (atomic max), or nullptr
 };
 
 // The chunk append an attention call may carry: K_cur and V_cur quantised
@@ -62,6 +63,7 @@ struct AppendLaunch {
   bool meta16;
   int64_t cap;
   CacheLayout layout;
+  float *bound[2];  // the caches' running bounds [B][Hkv], or nullptr
   int64_t wg0;  // set by the launcher that adds append workgroups
   int32_t wgs;
 };
@@ -74,6 +76,7 @@ struct AttnLaunch {
   uint16_t *out;
   const uint8_t *kc_codes, *vc_codes;
   const float *kc_scale, *kc_zero, *vc_scale, *vc_zero;
+  const float *kc_bound, *vc_bound;  // running bounds [B][Hkv] of the caches, or nullptr (scan the metadata)
   int32_t kbits, vbits, group;
   int64_t cap;
   CacheLayout layout;  // of both caches

@@ -107,6 +107,32 @@ __device__ inline uint32_t quantize8(const float (&v)[8], float &step, float &zp
   return packed;
 }
 
+// Bound of a group's dequantised values from its stored step and zero
+// point: the values lie between z and z + (2^bits - 1) D.  The attention
+// pre-passes use the same rule when they scan the metadata themselves.
+template <int BITS>
+__device__ inline float group_bound(float step, float zp) {
+  return fmaxf(fabsf(zp), fabsf(fmaf(step, static_cast<float>((1 << BITS) - 1), zp)));
+}
+
+// Raise the running bound of (b, h) = entry i to b (b >= 0, so the order of
+// the float bits is that of the integers: one atomic max).  Every lane of
+// the wave must call this together: when all lanes name the same entry the
+// wave maximum goes in with one atomic, otherwise each lane adds its own.
+__device__ inline void raise_bound(float *bound, int64_t i, float b) {
+  if (!bound) return;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(i));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(i) >> 32));
+  const int64_t i0 = static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+  if (__all(i == i0)) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) b = fmaxf(b, __shfl_xor(b, o, 64));
+    if (__lane_id() == 0 && b > 0.f) atomicMax(reinterpret_cast<int *>(bound) + i0, __float_as_int(b));
+  } else if (b > 0.f) {
+    atomicMax(reinterpret_cast<int *>(bound) + i, __float_as_int(b));
+  }
+}
+
 // Stores one lane's packed codes of token row `orow` (lane `chunk` of the
 // row's d/8) and, from the first lane of each group, the group's step and
 // zero point.
@@ -155,9 +181,17 @@ __device__ inline void store8_bits(int bits, uint8_t *codes, float *scale, float
 // row r0 + tid / (d/8) first, then every nthr / (d/8) rows, K and V of a row
 // loaded together.  kb, vb: raised to the largest |k| and |v| over the
 // lane's values (the pre-passes' bounds).
+// The running bounds the rows raise: on a row's first lane, those of its
+// rows in (b, KV head) entry `cur` (earlier entries already raised); zero on
+// the other lanes.
+struct RowBounds {
+  float k = 0.f, v = 0.f;
+  int64_t cur = 0;
+};
+
 template <int LANES, bool M16>
 __device__ void append_rows_t(const AttnLaunch &p, int64_t r0, int64_t r1, bool write, int tid, int nthr, float &kb,
-                              float &vb) {
+                              float &vb, RowBounds &rb) {
   const AppendLaunch &a = p.app;
   const int32_t lanes_per_row = p.d >> 3;
   const int32_t chunk = tid & (lanes_per_row - 1);
@@ -168,6 +202,10 @@ __device__ void append_rows_t(const AttnLaunch &p, int64_t r0, int64_t r1, bool 
   const int64_t bkv0 = r0 / p.Ncur;
   const uint32_t tok0 = static_cast<uint32_t>(r0 - bkv0 * p.Ncur), ncur = static_cast<uint32_t>(p.Ncur);
   const uint32_t hkv = static_cast<uint32_t>(p.Hkv);
+  // running bounds of the rows' groups, per (b, KV head) entry; a lane whose
+  // rows move to the next entry hands the finished one over first
+  float kbnd = 0.f, vbnd = 0.f;
+  int64_t cur = bkv0;
   auto load = [&](int64_t base, float (&k)[8], float (&v)[8]) {
     const int64_t r = base + lane_row;
     const int64_t rr = (r < r1 ? r : r1 - 1) * p.d + chunk * 8;  // dead rows (whole groups) repeat the last one
@@ -198,34 +236,60 @@ __device__ void append_rows_t(const AttnLaunch &p, int64_t r0, int64_t r1, bool 
         const int64_t orow = a.layout.row(a.cap, p.Hkv, b, h, p.Nc + tok);
         store8_bits<LANES, M16>(a.bits[0], a.codes[0], a.scale[0], a.zero[0], orow, lanes_per_row, chunk, kp, ks, kz);
         store8_bits<LANES, M16>(a.bits[1], a.codes[1], a.scale[1], a.zero[1], orow, lanes_per_row, chunk, vp, vs, vz);
+        // the row's bound over its lanes (a row's lanes are live together),
+        // kept by its first lane
+        float kr = a.bits[0] == 2 ? group_bound<2>(ks, kz) : group_bound<4>(ks, kz);
+        float vr = a.bits[1] == 2 ? group_bound<2>(vs, vz) : group_bound<4>(vs, vz);
+        for (int o = LANES; o < lanes_per_row; o <<= 1) {
+          kr = fmaxf(kr, __shfl_xor(kr, o, 64));
+          vr = fmaxf(vr, __shfl_xor(vr, o, 64));
+        }
+        if (chunk == 0) {
+          if (bkv != cur) {  // the lane's rows crossed into the next (b, KV head): hand the last one over
+            if (a.bound[0] && kbnd > 0.f) atomicMax(reinterpret_cast<int *>(a.bound[0]) + cur, __float_as_int(kbnd));
+            if (a.bound[1] && vbnd > 0.f) atomicMax(reinterpret_cast<int *>(a.bound[1]) + cur, __float_as_int(vbnd));
+            cur = bkv;
+            kbnd = vbnd = 0.f;
+          }
+          kbnd = fmaxf(kbnd, kr);
+          vbnd = fmaxf(vbnd, vr);
+        }
       }
     }
   }
+  rb.k = kbnd;
+  rb.v = vbnd;
+  rb.cur = cur;
 }
 
 // append_rows_t with the caches' group and metadata format (bounds only,
 // no group reduction and nothing stored, without `write`).  kb, vb are
-// raised to the bounds of the rows.
+// raised to the bounds of the rows; rb receives the rows' running bounds
+// for the caller to raise (its workgroup's rows may share one entry).
 __device__ inline void append_rows(const AttnLaunch &p, int64_t r0, int64_t r1, bool write, int tid, int nthr,
-                                   float &kb, float &vb) {
-  if (!write) return append_rows_t<4, false>(p, r0, r1, false, tid, nthr, kb, vb);
+                                   float &kb, float &vb, RowBounds &rb) {
+  if (!write) return append_rows_t<4, false>(p, r0, r1, false, tid, nthr, kb, vb, rb);
   const int g = p.app.group;
   if (p.app.meta16) {
-    if (g == 32) return append_rows_t<4, true>(p, r0, r1, true, tid, nthr, kb, vb);
-    if (g == 64) return append_rows_t<8, true>(p, r0, r1, true, tid, nthr, kb, vb);
-    return append_rows_t<16, true>(p, r0, r1, true, tid, nthr, kb, vb);
+    if (g == 32) return append_rows_t<4, true>(p, r0, r1, true, tid, nthr, kb, vb, rb);
+    if (g == 64) return append_rows_t<8, true>(p, r0, r1, true, tid, nthr, kb, vb, rb);
+    return append_rows_t<16, true>(p, r0, r1, true, tid, nthr, kb, vb, rb);
   }
-  if (g == 32) return append_rows_t<4, false>(p, r0, r1, true, tid, nthr, kb, vb);
-  if (g == 64) return append_rows_t<8, false>(p, r0, r1, true, tid, nthr, kb, vb);
-  return append_rows_t<16, false>(p, r0, r1, true, tid, nthr, kb, vb);
+  if (g == 32) return append_rows_t<4, false>(p, r0, r1, true, tid, nthr, kb, vb, rb);
+  if (g == 64) return append_rows_t<8, false>(p, r0, r1, true, tid, nthr, kb, vb, rb);
+  return append_rows_t<16, false>(p, r0, r1, true, tid, nthr, kb, vb, rb);
 }
 
 // Body of the append workgroups of a launch (ids p.app.wg0 .. + p.app.wgs):
-// workgroup a takes an equal share of the B*Hkv*Ncur rows of K and V.
+// workgroup a takes an equal share of the B*Hkv*Ncur rows of K and V (its
+// rows may span two entries of the running bounds: raised per wave).
 __device__ inline void append_workgroup(const AttnLaunch &p, int64_t a, int tid, int nthr) {
   const int64_t n = p.B * p.Hkv * p.Ncur, w = p.app.wgs;
   float kb = 0.f, vb = 0.f;
-  append_rows(p, n * a / w, n * (a + 1) / w, true, tid, nthr, kb, vb);
+  RowBounds rb;
+  append_rows(p, n * a / w, n * (a + 1) / w, true, tid, nthr, kb, vb, rb);
+  raise_bound(p.app.bound[0], rb.cur, rb.k);
+  raise_bound(p.app.bound[1], rb.cur, rb.v);
 }
 
 }  // namespace qdev

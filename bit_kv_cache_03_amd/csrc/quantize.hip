@@ -36,7 +36,7 @@ template <typename T, int BITS, int LANES, bool M16>
 __global__ __launch_bounds__(kThreads) void quantize_pack(
     const T *__restrict__ x, int32_t lane_shift, int64_t N,
     uint8_t *__restrict__ codes, float *__restrict__ scale, float *__restrict__ zero,
-    int64_t cap, int64_t off, CacheLayout layout, int64_t H) {
+    int64_t cap, int64_t off, CacheLayout layout, int64_t H, float *__restrict__ bound) {
   const int64_t gl = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   const int64_t bh = static_cast<int64_t>(blockIdx.z) * H + blockIdx.y;
   const int32_t lanes_per_row = 1 << lane_shift;
@@ -50,6 +50,7 @@ __global__ __launch_bounds__(kThreads) void quantize_pack(
 
   float step, zp;
   const uint32_t packed = quantize8<BITS, LANES, M16>(v, step, zp);
+  raise_bound(bound, bh, live ? group_bound<BITS>(step, zp) : 0.f);  // the block's (b, h)
 
   if (!live) return;
   const int64_t orow = layout.row(cap, H, blockIdx.z, blockIdx.y, off + n);  // the cache row of token off + n
@@ -65,15 +66,15 @@ hipError_t launch_t(const QuantizeLaunch &p, hipStream_t stream) {
   switch (p.group) {
     case 32:
       quantize_pack<T, BITS, 4, M16><<<grid, dim3(kThreads), 0, stream>>>(
-          x, lane_shift, p.N, p.codes, p.scale, p.zero, p.cap, p.off, p.layout, p.H);
+          x, lane_shift, p.N, p.codes, p.scale, p.zero, p.cap, p.off, p.layout, p.H, p.bound);
       break;
     case 64:
       quantize_pack<T, BITS, 8, M16><<<grid, dim3(kThreads), 0, stream>>>(
-          x, lane_shift, p.N, p.codes, p.scale, p.zero, p.cap, p.off, p.layout, p.H);
+          x, lane_shift, p.N, p.codes, p.scale, p.zero, p.cap, p.off, p.layout, p.H, p.bound);
       break;
     default:
       quantize_pack<T, BITS, 16, M16><<<grid, dim3(kThreads), 0, stream>>>(
-          x, lane_shift, p.N, p.codes, p.scale, p.zero, p.cap, p.off, p.layout, p.H);
+          x, lane_shift, p.N, p.codes, p.scale, p.zero, p.cap, p.off, p.layout, p.H, p.bound);
       break;
   }
   return hipGetLastError();
@@ -83,15 +84,14 @@ hipError_t launch_t(const QuantizeLaunch &p, hipStream_t stream) {
 // channel octet); octets fastest, so a wave reads whole token rows.  The
 // call's tokens [off, off + N) start at a multiple of G; the last group may
 // be shorter.  Metadata row of a group = cache row of its first token >> log2 G.
+// The body for one live thread; returns the bound of its channels' groups.
 template <typename T, int BITS, bool M16>
-__global__ __launch_bounds__(kThreads) void quantize_tokens_pack(
-    const T *__restrict__ x, int64_t total, int32_t octets, int64_t groups, int64_t N, int32_t gshift,
-    uint8_t *__restrict__ codes, float *__restrict__ scale, float *__restrict__ zero, int64_t cap, int64_t off,
-    CacheLayout layout, int64_t H) {
+__device__ inline float quantize_token_group(const T *__restrict__ x, int64_t id, int32_t octets, int64_t groups,
+                                             int64_t N, int32_t gshift, uint8_t *__restrict__ codes,
+                                             float *__restrict__ scale, float *__restrict__ zero, int64_t cap,
+                                             int64_t off, CacheLayout layout, int64_t H) {
 #pragma clang fp contract(off)
   constexpr int TOP = (1 << BITS) - 1;
-  const int64_t id = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (id >= total) return;
   const int32_t oc = static_cast<int32_t>(id % octets);
   const int64_t rest = id / octets;
   const int64_t j = rest % groups;
@@ -165,7 +165,28 @@ __global__ __launch_bounds__(kThreads) void quantize_tokens_pack(
     else
       *reinterpret_cast<uint32_t *>(dst) = packed;
   }
+  float bnd = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) bnd = fmaxf(bnd, group_bound<BITS>(step[e], zp[e]));
+  return bnd;
 }
+
+// The kernel: every lane of a wave, dead ones too, takes part in raising
+// the running bound.
+template <typename T, int BITS, bool M16>
+__global__ __launch_bounds__(kThreads) void quantize_tokens_pack(
+    const T *__restrict__ x, int64_t total, int32_t octets, int64_t groups, int64_t N, int32_t gshift,
+    uint8_t *__restrict__ codes, float *__restrict__ scale, float *__restrict__ zero, int64_t cap, int64_t off,
+    CacheLayout layout, int64_t H, float *__restrict__ bound) {
+  const int64_t id = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const bool live = id < total;
+  float bnd = 0.f;
+  if (live) bnd = quantize_token_group<T, BITS, M16>(x, id, octets, groups, N, gshift, codes, scale, zero, cap, off,
+                                                     layout, H);
+  // every lane of the wave takes part (dead lanes with 0): the group's (b, h)
+  raise_bound(bound, live ? id / octets / groups : total / octets / groups - 1, bnd);
+}
+
 
 template <typename T, int BITS, bool M16>
 hipError_t launch_tokens(const QuantizeLaunch &p, hipStream_t stream) {
@@ -176,7 +197,7 @@ hipError_t launch_tokens(const QuantizeLaunch &p, hipStream_t stream) {
   const int64_t blocks = (total + kThreads - 1) / kThreads;
   quantize_tokens_pack<T, BITS, M16><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream>>>(
       static_cast<const T *>(p.x), total, octets, groups, p.N, gshift, p.codes, p.scale, p.zero, p.cap, p.off,
-      p.layout, p.H);
+      p.layout, p.H, p.bound);
   return hipGetLastError();
 }
 

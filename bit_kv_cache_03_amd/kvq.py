@@ -31,7 +31,7 @@ class QTensor(C.Structure):
     _fields_ = [("codes", C.c_void_p), ("scale", C.c_void_p), ("zero", C.c_void_p),
                 ("bits", C.c_int32), ("group", C.c_int32), ("cap", C.c_int64),
                 ("page_table", C.c_void_p), ("page_size", C.c_int32), ("num_pages", C.c_int32),
-                ("meta", C.c_int32), ("axis", C.c_int32)]
+                ("meta", C.c_int32), ("axis", C.c_int32), ("bound", C.c_void_p)]
 
 
 META = {"f32": 0, "f16": 1}  # kv_meta: storage type of a cache tensor's step and zero point
@@ -126,10 +126,14 @@ class QCache:
     "f16" (binary16 step and zero point).  ``axis``: "dim" (groups of
     ``group`` channels per token) or "tokens" (per channel, groups of
     ``group`` tokens: step and zero [B][H][cap // group][d], paged
-    [num_pages][H][page_size // group][d])."""
+    [num_pages][H][page_size // group][d]).  ``bound``: keep the running
+    bound of |dequantised value| per (b, h) that the quantiser raises and
+    the attention reads instead of scanning the metadata (call
+    ``reset_bound`` before refilling the cache from scratch)."""
 
     def __init__(self, B: int, H: int, cap: int, d: int, bits: int, group: int = 64, device="cuda",
-                 page_table=None, page_size: int = 0, num_pages: int = 0, meta: str = "f32", axis: str = "dim"):
+                 page_table=None, page_size: int = 0, num_pages: int = 0, meta: str = "f32", axis: str = "dim",
+                 bound: bool = True):
         import torch
         if meta not in META:
             raise ValueError(f"meta must be one of {sorted(META)}")
@@ -144,12 +148,19 @@ class QCache:
         mshape = lead[:2] + (lead[2] // group, d) if axis == "tokens" else lead + (d // group,)
         self.scale = torch.zeros(mshape, dtype=mdt, device=device)
         self.zero = torch.zeros(mshape, dtype=mdt, device=device)
+        # running bound of |dequantised value| per (b, h), raised by every quantise
+        self.bound = torch.zeros((B, H), dtype=torch.float32, device=device) if bound else None
+
+    def reset_bound(self) -> None:
+        if self.bound is not None:
+            self.bound.zero_()
 
     def descriptor(self) -> QTensor:
         return QTensor(self.codes.data_ptr(), self.scale.data_ptr(), self.zero.data_ptr(),
                        self.bits, self.group, self.cap,
                        self.page_table.data_ptr() if self.page_table is not None else None,
-                       self.page_size, self.num_pages, META[self.meta], AXIS[self.axis])
+                       self.page_size, self.num_pages, META[self.meta], AXIS[self.axis],
+                       self.bound.data_ptr() if self.bound is not None else None)
 
     def logical(self, nc: int):
         """(codes, step, zero) of tokens [0, nc) in the contiguous [B][H][nc][...]

@@ -140,6 +140,17 @@ typedef struct {
   int32_t meta;   /* kv_meta of scale and zero; K and V caches of one call share it */
   int32_t axis;   /* kv_axis; KV_AXIS_TOKENS needs cap (and page_size) to be multiples
                      of group; K and V may differ */
+  /* Optional running bound, NULL or a DEVICE fp32 array [B][H] (4-byte
+   * aligned): for every (b, h), at least max(|z|, |z + (2^bits - 1) D|) over
+   * the groups of every row written so far, i.e. a bound on |x^|.
+   * kv_quantize and the fused append raise it (atomic max, never lower it);
+   * the attention calls read it to pick their fp16 scales instead of
+   * scanning every step and zero point of rows [0, Nc).  It must start at 0
+   * (or any value at least the bound of the rows already present), and be
+   * reset to 0 when the cache is refilled from scratch; a value below the
+   * true bound is outside the contract (fp16 overflow of the scaled keys or
+   * values).  With NULL the attention scans the metadata. */
+  float *bound;
 } kv_qtensor;
 
 /*

@@ -98,6 +98,12 @@ int main() {
         {[](Call &c) { c.a.causal = 2; }, KV_ERR_UNSUPPORTED},
         {[](Call &c) { c.a.causal = 1; c.a.Nc = 0; c.a.Nq = 9; }, KV_ERR_SHAPE},
         {[](Call &c) { c.k.bits = 3; }, KV_ERR_UNSUPPORTED},
+        {[](Call &c) { c.k.bound = static_cast<float *>(P(0x50000002)); }, KV_ERR_ALIGN},
+        {[](Call &c) {  // appending writes the running bound: it may not lie inside q
+           c.a.append = 1;
+           c.v.bound = static_cast<float *>(P(A));
+         },
+         KV_ERR_ALIAS},
         {[](Call &c) { c.k.cap = 10; }, KV_ERR_SHAPE},
         {[](Call &c) { c.v.group = 32; }, KV_ERR_UNSUPPORTED},
         {[](Call &c) { c.a.append = 2; }, KV_ERR_UNSUPPORTED},

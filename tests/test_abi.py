@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(kvq):
 
 
 def test_version_and_status_strings(kvq):
-    assert kvq.lib.kv_version() == 8
+    assert kvq.lib.kv_version() == 9
     for s in range(1, 9):
         assert len(kvq.lib.kv_status_string(s)) > 10
     assert kvq.lib.kv_status_string(0) == b"ok"
@@ -498,3 +498,15 @@ def test_append_cache_errors(kvq):
     # the same layout without append only reads the caches: no alias error
     a.append = 0
     assert kvq.lib.kv_attention_workspace_size(C.byref(a)) > 0
+
+
+def test_running_bound_alignment(kvq):
+    """The caches' running bound is an optional 4-byte aligned fp32 array."""
+    a = _args(kvq)
+    a._k.bound = 0x50000002
+    assert _attn(kvq, a) == kvq.KV_ERR_ALIGN
+    c = _qt(kvq, 0x30000000, 4, 64, 64)
+    c.bound = 0x50000006
+    assert kvq.lib.kv_quantize(A, 0, 1, 2, 0, 128, C.byref(c), 0, None) == kvq.KV_ERR_ALIGN
+    c.bound = A + 16  # inside the input
+    assert kvq.lib.kv_quantize(A, 0, 1, 2, 8, 128, C.byref(c), 0, None) == kvq.KV_ERR_ALIAS

@@ -62,6 +62,7 @@ def _clone(c):
     d = kvq.QCache.__new__(kvq.QCache)
     d.__dict__.update(c.__dict__)
     d.codes, d.scale, d.zero = c.codes.clone(), c.scale.clone(), c.zero.clone()
+    d.bound = None if c.bound is None else c.bound.clone()
     return d
 
 
@@ -104,7 +105,8 @@ def test_fused_append(orc, case):
     torch.cuda.synchronize()
     assert _bytes_equal(out_a, out_b), "attention output differs with the append"
     for a, b, label in ((kc, kc2, "K"), (vc, vc2, "V")):
-        for x, y, what in ((a.codes, b.codes, "codes"), (a.scale, b.scale, "step"), (a.zero, b.zero, "zero")):
+        for x, y, what in ((a.codes, b.codes, "codes"), (a.scale, b.scale, "step"), (a.zero, b.zero, "zero"),
+                           (a.bound, b.bound, "running bound")):
             assert _bytes_equal(x, y), (label, what)
     _check_rows(orc, kc, data["k"], w.kbits, w, meta, "K")
     _check_rows(orc, vc, data["v"], w.vbits, w, meta, "V")
