@@ -505,6 +505,11 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
   const int cend = bend < nbc ? bend : nbc;
   const Lanes lo = lane_offsets<KBITS, VBITS, NG, M16>(lane);
   Scales sc;
+  // with the caches' running bounds the exponents of the cached blocks are
+  // fixed once, from bounds that cover every cached block (a block's own
+  // check is then skipped); the current chunk's blocks still check theirs
+  const bool cache_bounds = p.Nc > 0 && p.kc_bound != nullptr && p.vc_bound != nullptr;
+  if (cache_bounds) sc.update(p.kc_bound[bkv], p.vc_bound[bkv], st.alpha);
   f16x8 kreg[8];
   bf16x8 kext = {};
   Fetch f;
@@ -515,7 +520,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
   for (; blk < cend; blk += WAVES) {
     const int k0 = blk * BK;
     const int count = c.nc - k0 < BK ? c.nc - k0 : BK;
-    sc.update(k_bound<KBITS, NG>(f), v_bound<VBITS>(f), st.alpha);
+    if (!cache_bounds) sc.update(k_bound<KBITS, NG>(f), v_bound<VBITS>(f), st.alpha);
     unpack_k_cached<TAYLOR, KBITS, NG>(c, lane, f, sc.kscale, kreg, kext);
     unpack_v_cached<VBITS>(c, lane, f, sc.vscale, Vt);
     if (blk + WAVES < cend) fetch_cached<KBITS, VBITS, NG, PAGED, M16>(c, (blk + WAVES) * BK, lo, h, f, prn);
