@@ -22,6 +22,7 @@ _SRC = os.path.join(_HERE, "kvq_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 CORR = {"off": 0, "taylor": 1, "exact": 2}
+META = {"f32": 0, "f16": 1, "bf16": 2}  # storage of the step and zero point
 
 
 GCC_FLAGS = ["-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
@@ -57,6 +58,8 @@ def _load(path: str):
     L.kvo_quantize_tokens_bf16_meta.argtypes = [vp, i64, i64, i32, i32, i32, i32, vp, vp, vp]
     L.kvo_round_fp16.argtypes = [C.c_float]
     L.kvo_round_fp16.restype = C.c_float
+    L.kvo_round_bf16.argtypes = [C.c_float]
+    L.kvo_round_bf16.restype = C.c_float
     L.kvo_unpack.argtypes = [vp, i64, i32, i32, vp]
     L.kvo_pack.argtypes = [vp, i64, i32, i32, vp]
     L.kvo_dequant.argtypes = [vp, vp, vp, i64, i32, i32, i32, vp]
@@ -101,16 +104,16 @@ def quantize(x: np.ndarray, bits: int, group: int, meta: str = "f32", axis: str 
     ``x`` is float32 values, or uint16 bf16 bit patterns.  Returns
     ``(codes, step, zero)`` with codes packed LSB-first: shape
     ``x.shape[:-1] + (d*bits//8,)`` uint8, and step/zero of shape
-    ``x.shape[:-1] + (d//group,)`` float32.  ``meta="f16"``: step and zero
-    are rounded to binary16 (still returned as float32 values) and the codes
-    are taken against the rounded grid.  ``axis="tokens"``: groups run
+    ``x.shape[:-1] + (d//group,)`` float32.  ``meta="f16"`` / ``"bf16"``: step
+    and zero are rounded to binary16 / bfloat16 (still returned as float32
+    values) and the codes are taken against the rounded grid.  ``axis="tokens"``: groups run
     along the second-to-last axis instead (per channel, ``group``
     consecutive tokens; the last group may be shorter): step/zero then have
     shape ``x.shape[:-2] + (ceil(N/group), d)``.
     """
-    meta16 = {"f32": 0, "f16": 1}[meta]
+    mk = META[meta]
     if axis == "tokens":
-        return _quantize_tokens(np.ascontiguousarray(x), bits, group, meta16)
+        return _quantize_tokens(np.ascontiguousarray(x), bits, group, mk)
     if axis != "dim":
         raise ValueError("axis must be 'dim' or 'tokens'")
     x = np.ascontiguousarray(x)
@@ -120,16 +123,16 @@ def quantize(x: np.ndarray, bits: int, group: int, meta: str = "f32", axis: str 
     step = np.zeros(x.shape[:-1] + (d // group,), np.float32)
     zero = np.zeros_like(step)
     if x.dtype == np.float32:
-        rc = lib().kvo_quantize_f32_meta(_p(x), rows, d, group, bits, meta16, _p(codes), _p(step), _p(zero))
+        rc = lib().kvo_quantize_f32_meta(_p(x), rows, d, group, bits, mk, _p(codes), _p(step), _p(zero))
     elif x.dtype == np.uint16:
-        rc = lib().kvo_quantize_bf16_meta(_p(x), rows, d, group, bits, meta16, _p(codes), _p(step), _p(zero))
+        rc = lib().kvo_quantize_bf16_meta(_p(x), rows, d, group, bits, mk, _p(codes), _p(step), _p(zero))
     else:
         raise TypeError("x must be float32 or uint16 (bf16 bits)")
     _check(rc, "quantize")
     return codes, step, zero
 
 
-def _quantize_tokens(x: np.ndarray, bits: int, group: int, meta16: int):
+def _quantize_tokens(x: np.ndarray, bits: int, group: int, mk: int):
     n, d = x.shape[-2], x.shape[-1]
     outer = x.size // (n * d) if n * d else 0
     ngr = (n + group - 1) // group
@@ -142,12 +145,16 @@ def _quantize_tokens(x: np.ndarray, bits: int, group: int, meta16: int):
         f = lib().kvo_quantize_tokens_bf16_meta
     else:
         raise TypeError("x must be float32 or uint16 (bf16 bits)")
-    _check(f(_p(x), outer, n, d, group, bits, meta16, _p(codes), _p(step), _p(zero)), "quantize_tokens")
+    _check(f(_p(x), outer, n, d, group, bits, mk, _p(codes), _p(step), _p(zero)), "quantize_tokens")
     return codes, step, zero
 
 
 def round_fp16(x: float) -> float:
     return lib().kvo_round_fp16(float(x))
+
+
+def round_bf16(x: float) -> float:
+    return lib().kvo_round_bf16(float(x))
 
 
 def unpack(codes: np.ndarray, d: int, bits: int) -> np.ndarray:

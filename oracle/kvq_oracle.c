@@ -34,8 +34,9 @@
  * Readings taken where the pages are silent (each also listed in the design
  * notes of the repository):
  *  - step  D = fl32(fl32(mx - mn) / (2^bits - 1)), zero-point z = mn (fp32);
- *    with binary16 metadata, D and z are rounded to binary16 (nearest,
- *    ties to even) and the codes below use the rounded D and z;
+ *    with 16-bit metadata (IEEE binary16 or bfloat16), D and z are rounded
+ *    to that format (nearest, ties to even) and the codes below use the
+ *    rounded D and z;
  *  - code  c = clamp(rne(fl32(fl32(x - mn) / D)), 0, 2^bits - 1), 0 if D == 0;
  *  - mn and mx are canonicalised with "+ 0.0f" so a zero extreme is +0;
  *  - packing is LSB-first: element k of a row sits in byte floor(k*bits/8)
@@ -131,12 +132,39 @@ static float round_fp16(float x) {
 
 float kvo_round_fp16(float x) { return round_fp16(x); }
 
+/* The bfloat16 value nearest to a finite fp32 x (round half to even),
+ * returned as fp32 (exactly).  bfloat16 keeps fp32's exponent range with 7
+ * fraction bits: normals from 2^-126 spaced 2^(e-8) in [2^(e-1), 2^e),
+ * subnormals spaced 2^-133, largest finite (2 - 2^-7) 2^127; magnitudes
+ * that round past it become infinity.  As for binary16, x/u is exact for
+ * the spacing u of x's binade and rint(x/u) u is the rounded value (the
+ * product overflows to infinity exactly when the rounded value does). */
+static float round_bf16(float x) {
+  if (x == 0.0f || !isfinite(x)) return x;
+  const float a = fabsf(x);
+  int e;
+  frexpf(a, &e);              /* a in [2^(e-1), 2^e) */
+  int ue = (e - 1) - 7;       /* spacing in that binade */
+  if (ue < -133) ue = -133;   /* subnormal spacing */
+  const float r = rintf(ldexpf(a, -ue));
+  return copysignf(ldexpf(r, ue), x);
+}
+
+float kvo_round_bf16(float x) { return round_bf16(x); }
+
+/* The stored value of a step or zero point: meta 0 fp32 (unchanged),
+ * 1 binary16, 2 bfloat16. */
+static float round_meta(float x, int32_t meta) {
+  return meta == 1 ? round_fp16(x) : meta == 2 ? round_bf16(x) : x;
+}
+
 /* Quantize one group of `group` fp32 values.  codes_out gets one code per
  * element (unpacked).  The order of fp32 operations is the contract.
- * meta16: the step and zero point are stored as binary16; they are rounded
- * first and the codes are taken against the rounded grid, so that the
- * dequantised value z + D c uses exactly what is stored. */
-static void quantize_group(const float *x, int32_t group, int32_t bits, int32_t meta16,
+ * meta: the storage of the step and zero point (0 fp32, 1 binary16,
+ * 2 bfloat16); with 16 bits they are rounded first and the codes are taken
+ * against the rounded grid, so that the dequantised value z + D c uses
+ * exactly what is stored. */
+static void quantize_group(const float *x, int32_t group, int32_t bits, int32_t meta,
                            uint8_t *codes_out, float *step_out, float *zero_out) {
   const int32_t top = (1 << bits) - 1;
   float mn = x[0], mx = x[0];
@@ -149,10 +177,8 @@ static void quantize_group(const float *x, int32_t group, int32_t bits, int32_t 
   float range = mx - mn;             /* fl32 subtraction */
   float step = range / (float)top;   /* fl32 IEEE division */
   float zero = mn;
-  if (meta16) {
-    step = round_fp16(step);
-    zero = round_fp16(mn);
-  }
+  step = round_meta(step, meta);
+  zero = round_meta(mn, meta);
   *step_out = step;
   *zero_out = zero;
   for (int32_t k = 0; k < group; ++k) {
@@ -179,10 +205,10 @@ static void pack_row(const uint8_t *c, int32_t d, int32_t bits, uint8_t *out) {
 }
 
 /* Quantize `rows` rows of d fp32 values.  codes: rows x (d*bits/8) bytes;
- * step, zero: rows x (d/group) fp32 (holding binary16 values when meta16). */
+ * step, zero: rows x (d/group) fp32 (holding the 16-bit values when meta is 1 or 2). */
 int kvo_quantize_f32_meta(const float *x, int64_t rows, int32_t d, int32_t group,
-                          int32_t bits, int32_t meta16, uint8_t *codes, float *step, float *zero) {
-  if (!x || !codes || !step || !zero || rows < 0 || (meta16 != 0 && meta16 != 1)) return KVO_ERR_ARG;
+                          int32_t bits, int32_t meta, uint8_t *codes, float *step, float *zero) {
+  if (!x || !codes || !step || !zero || rows < 0 || (meta < 0 || meta > 2)) return KVO_ERR_ARG;
   if (!qparams_ok(d, group, bits)) return KVO_ERR_ARG;
   const int32_t ng = d / group;
   const int64_t row_bytes = d * bits / 8;
@@ -197,7 +223,7 @@ int kvo_quantize_f32_meta(const float *x, int64_t rows, int32_t d, int32_t group
 #pragma omp for schedule(static)
       for (int64_t r = 0; r < rows; ++r) {
         for (int32_t g = 0; g < ng; ++g)
-          quantize_group(x + r * d + (int64_t)g * group, group, bits, meta16, c + g * group,
+          quantize_group(x + r * d + (int64_t)g * group, group, bits, meta, c + g * group,
                          step + r * ng + g, zero + r * ng + g);
         pack_row(c, d, bits, codes + r * row_bytes);
       }
@@ -214,12 +240,12 @@ int kvo_quantize_f32(const float *x, int64_t rows, int32_t d, int32_t group,
 
 /* Same, for bf16 input (widened exactly to fp32 first). */
 int kvo_quantize_bf16_meta(const uint16_t *x, int64_t rows, int32_t d, int32_t group,
-                           int32_t bits, int32_t meta16, uint8_t *codes, float *step, float *zero) {
+                           int32_t bits, int32_t meta, uint8_t *codes, float *step, float *zero) {
   if (!x || rows < 0 || d <= 0) return KVO_ERR_ARG;
   float *f = (float *)malloc((size_t)(rows * d) * sizeof(float) + 1);
   if (!f) return KVO_ERR_MEM;
   kvo_bf16_to_f32(x, rows * d, f);
-  int rc = kvo_quantize_f32_meta(f, rows, d, group, bits, meta16, codes, step, zero);
+  int rc = kvo_quantize_f32_meta(f, rows, d, group, bits, meta, codes, step, zero);
   free(f);
   return rc;
 }
@@ -231,9 +257,9 @@ int kvo_quantize_bf16_meta(const uint16_t *x, int64_t rows, int32_t d, int32_t g
  * rows, packed as above); step, zero: [outer][ceil(n/group)][d].  Any
  * group >= 1 is accepted here. */
 int kvo_quantize_tokens_f32_meta(const float *x, int64_t outer, int64_t n, int32_t d, int32_t group,
-                                 int32_t bits, int32_t meta16, uint8_t *codes, float *step, float *zero) {
+                                 int32_t bits, int32_t meta, uint8_t *codes, float *step, float *zero) {
   if (!x || !codes || !step || !zero || outer < 0 || n < 0 || d <= 0 || group < 1) return KVO_ERR_ARG;
-  if ((bits != 2 && bits != 4) || (d * bits) % 8 != 0 || (meta16 != 0 && meta16 != 1)) return KVO_ERR_ARG;
+  if ((bits != 2 && bits != 4) || (d * bits) % 8 != 0 || (meta < 0 || meta > 2)) return KVO_ERR_ARG;
   const int64_t ngr = (n + group - 1) / group;
   const int64_t row_bytes = d * bits / 8;
   int err = KVO_OK;
@@ -254,7 +280,7 @@ int kvo_quantize_tokens_f32_meta(const float *x, int64_t outer, int64_t n, int32
           const int32_t cnt = (int32_t)(n - t0 < group ? n - t0 : group);
           for (int32_t c = 0; c < d; ++c) {
             for (int32_t i = 0; i < cnt; ++i) vals[i] = xo[(t0 + i) * d + c];
-            quantize_group(vals, cnt, bits, meta16, gc, step + (o * ngr + j) * d + c,
+            quantize_group(vals, cnt, bits, meta, gc, step + (o * ngr + j) * d + c,
                            zero + (o * ngr + j) * d + c);
             for (int32_t i = 0; i < cnt; ++i) u[(t0 + i) * d + c] = gc[i];
           }
@@ -270,12 +296,12 @@ int kvo_quantize_tokens_f32_meta(const float *x, int64_t outer, int64_t n, int32
 }
 
 int kvo_quantize_tokens_bf16_meta(const uint16_t *x, int64_t outer, int64_t n, int32_t d, int32_t group,
-                                  int32_t bits, int32_t meta16, uint8_t *codes, float *step, float *zero) {
+                                  int32_t bits, int32_t meta, uint8_t *codes, float *step, float *zero) {
   if (!x || outer < 0 || n < 0 || d <= 0) return KVO_ERR_ARG;
   float *f = (float *)malloc((size_t)(outer * n * d) * sizeof(float) + 1);
   if (!f) return KVO_ERR_MEM;
   kvo_bf16_to_f32(x, outer * n * d, f);
-  int rc = kvo_quantize_tokens_f32_meta(f, outer, n, d, group, bits, meta16, codes, step, zero);
+  int rc = kvo_quantize_tokens_f32_meta(f, outer, n, d, group, bits, meta, codes, step, zero);
   free(f);
   return rc;
 }

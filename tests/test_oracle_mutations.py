@@ -69,6 +69,15 @@ MUTANTS = [
      [("test_oracle_meta16", "test_quantizer_with_binary16_metadata", {"bits": 4, "group": 64})]),
     ("meta16_ties_away", "  const float r = rintf(a / u) * u;", "  const float r = roundf(a / u) * u;",
      [("test_oracle_meta16", "test_rounding_ties_subnormals_overflow", {})]),
+    ("bf16_ties_away", "  const float r = rintf(ldexpf(a, -ue));", "  const float r = roundf(ldexpf(a, -ue));",
+     [("test_oracle_metabf16", "test_rounding_ties_subnormals_overflow", {})]),
+    ("bf16_fp16_spacing", "  int ue = (e - 1) - 7;       /* spacing in that binade */",
+     "  int ue = (e - 1) - 10;       /* spacing in that binade */",
+     [("test_oracle_metabf16", "test_rounding_matches_torch", {})]),
+    ("bf16_no_subnormal_clamp", "  if (ue < -133) ue = -133;   /* subnormal spacing */", "",
+     [("test_oracle_metabf16", "test_rounding_ties_subnormals_overflow", {})]),
+    ("bf16_zero_not_rounded", "  zero = round_meta(mn, meta);", "  zero = mn;",
+     [("test_oracle_metabf16", "test_quantizer_with_bfloat16_metadata", {"bits": 2, "group": 64})]),
     ("tokens_group_row_mod", "return (bkv * capg + t / a->group) * a->d + c;",
      "return (bkv * capg + t % a->group) * a->d + c;",
      [("test_oracle_tokens", "test_tokens_matches_library_sdpa", {"case": "int2_k_tokens", "corr": "off"})]),
