@@ -267,7 +267,7 @@ def write_traffic(w, pmc_dir: str, copy_bytes: int, options: dict):
          "fetch_factor": cf,
          "write_factor": cw, "per_kernel": per_kernel,
          "bytes_per_launch": sum(v["fetch_bytes"] + v["write_bytes"] for v in per_kernel.values()),
-         "algorithmic_packed_bytes": packed_bytes(w, 2 if options["meta"] == "f16" else 4, options["kaxis"],
+         "algorithmic_packed_bytes": packed_bytes(w, 4 if options["meta"] == "f32" else 2, options["kaxis"],
                                                   options["vaxis"])}
     out = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
     with open(out, "w") as fh:
@@ -336,7 +336,7 @@ def main():
     ap.add_argument("--causal", action="store_true", help="end-aligned causal mask within the current chunk")
     ap.add_argument("--page-size", type=int, default=0,
                     help="paged cache layout with pages of this many tokens (shuffled page table)")
-    ap.add_argument("--meta", default="f32", choices=["f32", "f16"],
+    ap.add_argument("--meta", default="f32", choices=["f32", "f16", "bf16"],
                     help="storage type of the caches' step and zero point")
     ap.add_argument("--kaxis", default="dim", choices=["dim", "tokens"],
                     help="K cache groups along the head dimension or along the tokens (per channel)")
@@ -501,7 +501,7 @@ def main():
     flops = attention_flops(w, args.causal)
     ckq = w.B * w.Hq * w.Nq * w.Nc
     achieved = flops / (attn_ms * 1e-3) / 1e12
-    pbytes = packed_bytes(w, 2 if args.meta == "f16" else 4, args.kaxis, args.vaxis)
+    pbytes = packed_bytes(w, 4 if args.meta == "f32" else 2, args.kaxis, args.vaxis)
     if hbm_bound:
         roof = {"bound": "hbm", "achieved": pbytes / (attn_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
@@ -522,7 +522,7 @@ def main():
         "vs_baseline": None,
         **arithmetic(w, corr, args.page_size, args.kaxis, args.vaxis),
         "data": "synthetic: seeded N(0,1) q/k/v with the workload's key structure, bf16; cache INT%d/INT%d group %d%s" % (
-            w.kbits, w.vbits, w.group, (", binary16 step/zero" if args.meta == "f16" else "") +
+            w.kbits, w.vbits, w.group, ({"f16": ", binary16 step/zero", "bf16": ", bfloat16 step/zero"}.get(args.meta, "")) +
             (f", K/V groups along {args.kaxis}/{args.vaxis}" if "tokens" in (args.kaxis, args.vaxis) else "")),
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "Nq": w.Nq,
                    "Ncur": w.Ncur, "Nc": w.Nc, "kbits": w.kbits, "vbits": w.vbits, "group": w.group,

@@ -134,11 +134,16 @@ __device__ inline float logsinhc(float x) {
   return a - logf(2.0f * a) + log1pf(-expf(-2.0f * a));
 }
 
-// Metadata elements i .. i+3 (i a multiple of 4): fp32, or binary16 when
-// meta16; one 16-byte or 8-byte load.
-__device__ inline float4 meta4(const float *p, int64_t i, bool meta16) {
-  if (meta16) {
-    const uint2 w = *reinterpret_cast<const uint2 *>(reinterpret_cast<const _Float16 *>(p) + i);
+// Metadata elements i .. i+3 (i a multiple of 4) of kind mk: fp32, or 16-bit
+// (binary16 or bfloat16); one 16-byte or 8-byte load.
+__device__ inline float4 meta4(const float *p, int64_t i, int mk) {
+  if (mk == kMetaBF16) {  // bfloat16 patterns are the upper halves of fp32 ones
+    const uint2 w = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(p) + i);
+    return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+                       __uint_as_float(w.y & 0xffff0000u));
+  }
+  if (mk == kMetaF16) {
+    const uint2 w = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(p) + i);
     const auto h = [](uint32_t x) { return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(x))); };
     return make_float4(h(w.x), h(w.x >> 16), h(w.y), h(w.y >> 16));
   }
@@ -316,8 +321,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_tile_kernel(AttnLaunch p, in
         };
         if (!ktok) {  // one step / zero point for the thread's values (one group of the row)
           const int g = d0 >> group_shift;
-          const float stp = ok ? meta_at(p.kc_scale, row * ng + g, p.meta16) : 0.f;
-          const float zp = ok ? meta_at(p.kc_zero, row * ng + g, p.meta16) : 0.f;
+          const float stp = ok ? meta_at(p.kc_scale, row * ng + g, p.meta) : 0.f;
+          const float zp = ok ? meta_at(p.kc_zero, row * ng + g, p.meta) : 0.f;
 #pragma unroll
           for (int e = 0; e < DPT; e += 2)
             put(e, fmaf(stp, code_f<KBITS>(w[e / PER], e % PER), zp),
@@ -328,7 +333,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_tile_kernel(AttnLaunch p, in
           const int64_t m0 = (row >> group_shift) * D + d0;
 #pragma unroll
           for (int e = 0; e < DPT; e += 4) {
-            const float4 s4 = meta4(p.kc_scale, m0 + e, p.meta16), z4 = meta4(p.kc_zero, m0 + e, p.meta16);
+            const float4 s4 = meta4(p.kc_scale, m0 + e, p.meta), z4 = meta4(p.kc_zero, m0 + e, p.meta);
             put(e, fmaf(s4.x, code_f<KBITS>(w[e / PER], e % PER), z4.x),
                 fmaf(s4.y, code_f<KBITS>(w[(e + 1) / PER], (e + 1) % PER), z4.y));
             put(e + 2, fmaf(s4.z, code_f<KBITS>(w[(e + 2) / PER], (e + 2) % PER), z4.z),
@@ -344,7 +349,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_tile_kernel(AttnLaunch p, in
           float e16[16];
           float dsh[4] = {0.f, 0.f, 0.f, 0.f}, dsl[4] = {0.f, 0.f, 0.f, 0.f};
           for (int gg = 0; gg < ng; ++gg) {
-            const float s = ok ? meta_at(p.kc_scale, row * ng + gg, p.meta16) : 0.f;
+            const float s = ok ? meta_at(p.kc_scale, row * ng + gg, p.meta) : 0.f;
             const float sq = s * s;
             dsh[gg] = bf16_bits_to_f32(f32_to_bf16_bits(sq));
             dsl[gg] = sq - dsh[gg];
@@ -378,7 +383,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_tile_kernel(AttnLaunch p, in
         const int hk0 = 32 * (tid / D);  // first key of the half
         const bool okh = hk0 < count;
         const int64_t hrow = p.layout.row(p.cap, p.Hkv, b, hk, k0 + (okh ? hk0 : 0));
-        Dt[tid] = okh ? meta_at(p.kc_scale, (hrow >> group_shift) * D + tid % D, p.meta16) : 0.f;
+        Dt[tid] = okh ? meta_at(p.kc_scale, (hrow >> group_shift) * D + tid % D, p.meta) : 0.f;
       }
     }
     // ---------------- V tile -> LDS (transposed, permuted key order) ----------------
@@ -403,15 +408,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_tile_kernel(AttnLaunch p, in
             if (ok) w = VBITS == 2 ? *reinterpret_cast<const uint16_t *>(src) : *reinterpret_cast<const uint32_t *>(src);
             if (!vtok) {  // one step per group of the row
               const int64_t m = row * ng + ((8 * dq) >> group_shift);
-              const float stp = ok ? meta_at(p.vc_scale, m, p.meta16) * vsc : 0.f;
-              const float zp = ok ? meta_at(p.vc_zero, m, p.meta16) * vsc : 0.f;
+              const float stp = ok ? meta_at(p.vc_scale, m, p.meta) * vsc : 0.f;
+              const float zp = ok ? meta_at(p.vc_zero, m, p.meta) * vsc : 0.f;
 #pragma unroll
               for (int e = 0; e < 8; ++e) v[j][e] = fmaf(stp, code_f<VBITS>(w, e), zp);
             } else {  // groups along the tokens: one per channel
               const int64_t m0 = (row >> group_shift) * D + 8 * dq;
 #pragma unroll
               for (int e4 = 0; e4 < 8; e4 += 4) {
-                const float4 s4 = meta4(p.vc_scale, m0 + e4, p.meta16), z4 = meta4(p.vc_zero, m0 + e4, p.meta16);
+                const float4 s4 = meta4(p.vc_scale, m0 + e4, p.meta), z4 = meta4(p.vc_zero, m0 + e4, p.meta);
                 const float sv[4] = {s4.x, s4.y, s4.z, s4.w}, zv[4] = {z4.x, z4.y, z4.z, z4.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
@@ -649,7 +654,7 @@ __global__ __launch_bounds__(256) void value_bound_kernel(AttnLaunch p, int32_t 
       const int64_t r = i / per, c = i - r * per;
       const int64_t e = tok ? (p.layout.row(p.cap, p.Hkv, b, hk, r << group_shift) >> group_shift) * per + c
                             : p.layout.row(p.cap, p.Hkv, b, hk, r) * per + c;
-      const float stp = meta_at(p.vc_scale, e, p.meta16), zp = meta_at(p.vc_zero, e, p.meta16);
+      const float stp = meta_at(p.vc_scale, e, p.meta), zp = meta_at(p.vc_zero, e, p.meta);
       vm = fmaxf(vm, fmaxf(fabsf(zp), fabsf(fmaf(stp, top, zp))));
     }
   }
@@ -657,7 +662,7 @@ __global__ __launch_bounds__(256) void value_bound_kernel(AttnLaunch p, int32_t 
     const int64_t r0 = bkv * p.Ncur + p.Ncur * ch / kVChunks, r1 = bkv * p.Ncur + p.Ncur * (ch + 1) / kVChunks;
     float kb = 0.f;
     qdev::RowBounds rb;
-    qdev::append_rows(p, r0, r1, true, tid, 256, kb, vm, rb);
+    qdev::append_rows_any(p, r0, r1, true, tid, 256, kb, vm, rb);
     qdev::raise_bound(p.app.bound[0], bkv, rb.k);  // the rows are all of (b, KV head) bkv
     qdev::raise_bound(p.app.bound[1], bkv, rb.v);
   } else {  // current chunk: bf16 pairs

@@ -98,17 +98,18 @@ constexpr int KBUF = BN * KS;  // 16-bit elements per K buffer
 constexpr int VBUF = D * VS;   // 16-bit elements per V buffer
 constexpr int NVBUF = 3;
 
-// Step / zero-point arrays: fp32, or binary16 in the KVQ_FAST_META16 units
-// (the float pointers then address binary16 elements).
-constexpr bool kMeta16 = KVQ_FAST_META16 != 0;
-template <bool M16, typename I>
+// Step / zero-point arrays: fp32, or the 16-bit kind KVQ_FAST_META16 names in
+// its units (1 binary16, 2 bfloat16; the float pointers then address 16-bit
+// elements).
+constexpr int kMeta = KVQ_FAST_META16;
+template <int MT, typename I>
 __device__ inline float meta_ld(const float *p, I i) {
-  if (M16) return static_cast<float>(reinterpret_cast<const _Float16 *>(p)[i]);
+  if (MT != kMetaF32) return meta16_value(reinterpret_cast<const uint16_t *>(p)[i], MT);
   return p[i];
 }
-template <bool M16>
+template <int MT>
 __device__ inline const float *meta_adv(const float *p, int64_t n) {
-  return reinterpret_cast<const float *>(reinterpret_cast<const char *>(p) + n * (M16 ? 2 : 4));
+  return reinterpret_cast<const float *>(reinterpret_cast<const char *>(p) + n * (MT ? 2 : 4));
 }
 
 // V^T element (row = head-dim index, col = permuted key slot 0..63).  The
@@ -155,7 +156,7 @@ __device__ inline float block_max(float b, float *red, int tid) {
 }
 
 // Largest |z|, |z + top D| over this chunk's share of a cache tensor's groups.
-template <bool M16, int NT>
+template <int MT, int NT>
 __device__ inline float cache_bound(const AttnLaunch &p, const float *scale, const float *zero, float top,
                                     int32_t ng, int64_t bkv, int64_t ch, int tid) {
   float bd = 0.f;
@@ -164,15 +165,15 @@ __device__ inline float cache_bound(const AttnLaunch &p, const float *scale, con
     const int64_t b = bkv / p.Hkv, hk = bkv - b * p.Hkv;
     for (int64_t i = lo + tid; i < hi; i += NT) {
       const int64_t e = p.layout.row(p.cap, p.Hkv, b, hk, i / ng) * ng + i % ng;
-      const float zi = meta_ld<M16>(zero, e);
-      bd = fmaxf(bd, fmaxf(fabsf(zi), fabsf(fmaf(meta_ld<M16>(scale, e), top, zi))));
+      const float zi = meta_ld<MT>(zero, e);
+      bd = fmaxf(bd, fmaxf(fabsf(zi), fabsf(fmaf(meta_ld<MT>(scale, e), top, zi))));
     }
   } else {
-    const float *s = meta_adv<M16>(scale, bkv * p.cap * ng);
-    const float *z = meta_adv<M16>(zero, bkv * p.cap * ng);
+    const float *s = meta_adv<MT>(scale, bkv * p.cap * ng);
+    const float *z = meta_adv<MT>(zero, bkv * p.cap * ng);
     for (int64_t i = lo + tid; i < hi; i += NT) {
-      const float zi = meta_ld<M16>(z, i);
-      bd = fmaxf(bd, fmaxf(fabsf(zi), fabsf(fmaf(meta_ld<M16>(s, i), top, zi))));
+      const float zi = meta_ld<MT>(z, i);
+      bd = fmaxf(bd, fmaxf(fabsf(zi), fabsf(fmaf(meta_ld<MT>(s, i), top, zi))));
     }
   }
   return bd;
@@ -183,7 +184,7 @@ __device__ inline float cache_bound(const AttnLaunch &p, const float *scale, con
 // caches' running bounds, chunk 0), current chunk and query rows.  APPEND: the call's chunk append rides along -- the workgroup
 // also quantises its share of the chunk's K and V rows into the caches, from
 // the values it loads for the bounds.
-template <int KBITS, bool M16, bool APPEND>
+template <int KBITS, int MT, bool APPEND>
 __global__ __launch_bounds__(256) void key_scale_kernel(AttnLaunch p, int32_t ng, float *part) {
   constexpr int NT = 256;
   __shared__ float red[NT / 64];
@@ -193,16 +194,16 @@ __global__ __launch_bounds__(256) void key_scale_kernel(AttnLaunch p, int32_t ng
   float kb = 0.f, vb = 0.f;
   if (p.Nc > 0) {  // the caches' running bounds when they keep them, else a scan of the metadata
     kb = p.kc_bound ? (ch == 0 ? p.kc_bound[bkv] : 0.f)
-                    : cache_bound<M16, NT>(p, p.kc_scale, p.kc_zero, static_cast<float>((1 << KBITS) - 1), ng, bkv,
+                    : cache_bound<MT, NT>(p, p.kc_scale, p.kc_zero, static_cast<float>((1 << KBITS) - 1), ng, bkv,
                                            ch, tid);
     vb = p.vc_bound ? (ch == 0 ? p.vc_bound[bkv] : 0.f)
-                    : cache_bound<M16, NT>(p, p.vc_scale, p.vc_zero, static_cast<float>((1 << p.vbits) - 1), ng, bkv,
+                    : cache_bound<MT, NT>(p, p.vc_scale, p.vc_zero, static_cast<float>((1 << p.vbits) - 1), ng, bkv,
                                            ch, tid);
   }
   if (APPEND && p.Ncur > 0) {  // the chunk's rows in this share: their bounds, and their codes
     const int64_t r0 = bkv * p.Ncur + p.Ncur * ch / KCHUNKS, r1 = bkv * p.Ncur + p.Ncur * (ch + 1) / KCHUNKS;
     qdev::RowBounds rb;
-    qdev::append_rows(p, r0, r1, true, tid, NT, kb, vb, rb);
+    qdev::append_rows<MT>(p, r0, r1, true, tid, NT, kb, vb, rb);
     // the rows are all of (b, KV head) bkv: one atomic per cache for the workgroup
     const float rk = block_max<NT>(rb.k, red, tid), rv = block_max<NT>(rb.v, red, tid);
     if (tid == 0) {
@@ -378,8 +379,8 @@ __device__ inline void fetch_k(const Ctx &c, int k0, int tid, Fetch &f, size_t p
     if (PAGED) {  // pool row pr of the tile (looked up a step earlier), then rows within it
       const int ts = tile_start(c, k0);
       kc_codes += pr * (D * KBITS / 8);
-      kc_scale = meta_adv<kMeta16>(kc_scale, pr * c.ng);
-      kc_zero = meta_adv<kMeta16>(kc_zero, pr * c.ng);
+      kc_scale = meta_adv<kMeta>(kc_scale, pr * c.ng);
+      kc_zero = meta_adv<kMeta>(kc_zero, pr * c.ng);
       krow -= static_cast<uint32_t>(ts);
     }
     const uint8_t *ks = kc_codes + (krow * (D * KBITS / 8) + static_cast<uint32_t>(d0 * KBITS / 8));
@@ -390,8 +391,8 @@ __device__ inline void fetch_k(const Ctx &c, int k0, int tid, Fetch &f, size_t p
       f.kw[0] = *reinterpret_cast<const uint32_t *>(ks);
     }
     const uint32_t km = krow * static_cast<uint32_t>(c.ng);
-    f.kstep = meta_ld<kMeta16>(kc_scale, km + static_cast<uint32_t>(d0 >> c.group_shift));
-    f.kzero = meta_ld<kMeta16>(kc_zero, km + static_cast<uint32_t>(d0 >> c.group_shift));
+    f.kstep = meta_ld<kMeta>(kc_scale, km + static_cast<uint32_t>(d0 >> c.group_shift));
+    f.kzero = meta_ld<kMeta>(kc_zero, km + static_cast<uint32_t>(d0 >> c.group_shift));
   } else {
     const uint4 *ks = reinterpret_cast<const uint4 *>(c.k_cur + (krow * D + static_cast<uint32_t>(d0)));
     const uint4 a = ks[0], b = ks[1];
@@ -411,16 +412,16 @@ __device__ inline void fetch_v(const Ctx &c, int k0, int tid, int j, Fetch &f, s
     if (PAGED) {
       const int ts = tile_start(c, k0);
       vc_codes += pr * (D * VBITS / 8);
-      vc_scale = meta_adv<kMeta16>(vc_scale, pr * c.ng);
-      vc_zero = meta_adv<kMeta16>(vc_zero, pr * c.ng);
+      vc_scale = meta_adv<kMeta>(vc_scale, pr * c.ng);
+      vc_zero = meta_adv<kMeta>(vc_zero, pr * c.ng);
       vrow -= static_cast<uint32_t>(ts);
     }
     const uint8_t *vs = vc_codes + (vrow * (D * VBITS / 8) + static_cast<uint32_t>(dq * VBITS));
     f.vw[j] = VBITS == 4 ? *reinterpret_cast<const uint32_t *>(vs)
                          : static_cast<uint32_t>(*reinterpret_cast<const uint16_t *>(vs));
     const uint32_t vm = vrow * static_cast<uint32_t>(c.ng) + static_cast<uint32_t>((8 * dq) >> c.group_shift);
-    f.vstep[j] = meta_ld<kMeta16>(vc_scale, vm);
-    f.vzero[j] = meta_ld<kMeta16>(vc_zero, vm);
+    f.vstep[j] = meta_ld<kMeta>(vc_scale, vm);
+    f.vzero[j] = meta_ld<kMeta>(vc_zero, vm);
   } else {
     const uint4 v = *reinterpret_cast<const uint4 *>(c.v_cur + (vrow * D + static_cast<uint32_t>(8 * dq)));
     f.vw[4 * j] = v.x; f.vw[4 * j + 1] = v.y; f.vw[4 * j + 2] = v.z; f.vw[4 * j + 3] = v.w;
@@ -833,8 +834,8 @@ __device__ inline void segment(const Ctx &c, QState &qs, Soft &st, uint16_t *Kl,
   __syncthreads();
 }
 
-// (M16 names the metadata type in the kernel's symbol; it equals kMeta16.)
-template <int KBITS, int VBITS, bool TAYLOR, bool CAUSAL, bool PAGED, bool M16>
+// (MT names the metadata type in the kernel's symbol; it equals kMeta.)
+template <int KBITS, int VBITS, bool TAYLOR, bool CAUSAL, bool PAGED, int MT>
 __global__ __launch_bounds__(THREADS, 1) void attn_fast_kernel(AttnLaunch p, int32_t group_shift,
                                                                 int64_t rows_per_kvhead, int32_t row_blocks,
                                                                 const float *kpart, int32_t nsplit,
@@ -929,10 +930,10 @@ __global__ __launch_bounds__(THREADS, 1) void attn_fast_kernel(AttnLaunch p, int
     const int64_t hrow = PAGED ? 0 : bkv * p.cap;  // first cache row of this head (paged: the pool)
     c.kc_codes = p.kc_codes + hrow * (D * KBITS / 8);
     c.vc_codes = p.vc_codes + hrow * (D * VBITS / 8);
-    c.kc_scale = meta_adv<M16>(p.kc_scale, hrow * ng);
-    c.kc_zero = meta_adv<M16>(p.kc_zero, hrow * ng);
-    c.vc_scale = meta_adv<M16>(p.vc_scale, hrow * ng);
-    c.vc_zero = meta_adv<M16>(p.vc_zero, hrow * ng);
+    c.kc_scale = meta_adv<MT>(p.kc_scale, hrow * ng);
+    c.kc_zero = meta_adv<MT>(p.kc_zero, hrow * ng);
+    c.vc_scale = meta_adv<MT>(p.vc_scale, hrow * ng);
+    c.vc_zero = meta_adv<MT>(p.vc_zero, hrow * ng);
   }
   // this split's tiles [t0, t1) of the cached tiles followed by the current ones
   const int tc = static_cast<int>((p.Nc + BN - 1) / BN), tu = static_cast<int>((p.Ncur + BN - 1) / BN);
@@ -1037,8 +1038,8 @@ hipError_t launch_bits(const AttnLaunch &p, hipStream_t stream) {
   const int64_t nfull = nsplit > 1 ? p.fast_full_units : units;
   const dim3 grid(static_cast<uint32_t>(nfull + (units - nfull) * nsplit));
   constexpr bool CAUSAL = KVQ_FAST_CAUSAL != 0, PAGED = KVQ_FAST_PAGED != 0;
-  auto kernel = p.corr == KV_CORR_TAYLOR ? attn_fast_kernel<KB, VB, true, CAUSAL, PAGED, kMeta16>
-                                         : attn_fast_kernel<KB, VB, false, CAUSAL, PAGED, kMeta16>;
+  auto kernel = p.corr == KV_CORR_TAYLOR ? attn_fast_kernel<KB, VB, true, CAUSAL, PAGED, kMeta>
+                                         : attn_fast_kernel<KB, VB, false, CAUSAL, PAGED, kMeta>;
   kernel<<<grid, dim3(THREADS), 0, stream>>>(p, gshift, rows, row_blocks, kpart, nsplit, partials, nfull);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
@@ -1052,7 +1053,15 @@ hipError_t launch_bits(const AttnLaunch &p, hipStream_t stream) {
 }  // namespace
 
 #if KVQ_FAST_PAGED || KVQ_FAST_CAUSAL || KVQ_FAST_META16
-#if KVQ_FAST_META16 && KVQ_FAST_PAGED && KVQ_FAST_CAUSAL
+#if KVQ_FAST_META16 == 2 && KVQ_FAST_PAGED && KVQ_FAST_CAUSAL
+hipError_t launch_attention_fast_mb16_paged_causal(const AttnLaunch &p, hipStream_t stream) {
+#elif KVQ_FAST_META16 == 2 && KVQ_FAST_PAGED
+hipError_t launch_attention_fast_mb16_paged(const AttnLaunch &p, hipStream_t stream) {
+#elif KVQ_FAST_META16 == 2 && KVQ_FAST_CAUSAL
+hipError_t launch_attention_fast_mb16_causal(const AttnLaunch &p, hipStream_t stream) {
+#elif KVQ_FAST_META16 == 2
+hipError_t launch_attention_fast_mb16(const AttnLaunch &p, hipStream_t stream) {
+#elif KVQ_FAST_META16 && KVQ_FAST_PAGED && KVQ_FAST_CAUSAL
 hipError_t launch_attention_fast_m16_paged_causal(const AttnLaunch &p, hipStream_t stream) {
 #elif KVQ_FAST_META16 && KVQ_FAST_PAGED
 hipError_t launch_attention_fast_m16_paged(const AttnLaunch &p, hipStream_t stream) {
@@ -1078,16 +1087,22 @@ bool fast_path_supported(const AttnLaunch &p) {
   return fast_kernel_ok(p.d, p.corr, p.ktok || p.vtok, layout_page_size(p.layout));
 }
 
+template <int MT>
+void key_scale_launch(const AttnLaunch &p, hipStream_t stream, float *part, dim3 grid, int32_t ng, bool k4) {
+  // the instances with the chunk append hold its registers; those without stay lean
+  auto kernel = p.app.on ? (k4 ? key_scale_kernel<4, MT, true> : key_scale_kernel<2, MT, true>)
+                         : (k4 ? key_scale_kernel<4, MT, false> : key_scale_kernel<2, MT, false>);
+  kernel<<<grid, dim3(256), 0, stream>>>(p, ng, part);
+}
+
 void launch_key_scale(const AttnLaunch &p, hipStream_t stream, float *part) {
   const int32_t ng = D / p.group;
   const dim3 grid(static_cast<uint32_t>(p.B * p.Hkv * KCHUNKS));
   const bool k4 = p.Nc > 0 && p.kbits == 4;
-  // the instances with the chunk append hold its registers; those without stay lean
-  auto kernel = p.app.on ? (p.meta16 ? (k4 ? key_scale_kernel<4, true, true> : key_scale_kernel<2, true, true>)
-                                     : (k4 ? key_scale_kernel<4, false, true> : key_scale_kernel<2, false, true>))
-                         : (p.meta16 ? (k4 ? key_scale_kernel<4, true, false> : key_scale_kernel<2, true, false>)
-                                     : (k4 ? key_scale_kernel<4, false, false> : key_scale_kernel<2, false, false>));
-  kernel<<<grid, dim3(256), 0, stream>>>(p, ng, part);
+  if (p.meta == kMetaBF16)
+    return key_scale_launch<kMetaBF16>(p, stream, part, grid, ng, k4);
+  if (p.meta == kMetaF16) return key_scale_launch<kMetaF16>(p, stream, part, grid, ng, k4);
+  key_scale_launch<kMetaF32>(p, stream, part, grid, ng, k4);
 }
 
 size_t fast_path_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int splits) {
@@ -1142,7 +1157,12 @@ int fast_path_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nc,
 }
 
 hipError_t launch_attention_fast(const AttnLaunch &p, hipStream_t stream) {
-  if (p.meta16) {
+  if (p.meta == kMetaBF16) {
+    if (p.layout.page_table)
+      return p.causal ? launch_attention_fast_mb16_paged_causal(p, stream) : launch_attention_fast_mb16_paged(p, stream);
+    return p.causal ? launch_attention_fast_mb16_causal(p, stream) : launch_attention_fast_mb16(p, stream);
+  }
+  if (p.meta == kMetaF16) {
     if (p.layout.page_table)
       return p.causal ? launch_attention_fast_m16_paged_causal(p, stream) : launch_attention_fast_m16_paged(p, stream);
     return p.causal ? launch_attention_fast_m16_causal(p, stream) : launch_attention_fast_m16(p, stream);

@@ -1,0 +1,6 @@
+// Bfloat16-metadata instances of the throughput kernel with the causal mask,
+// built in their own translation unit; the kernel itself is in
+// attention_fast.hip.
+#define KVQ_FAST_META16 2
+#define KVQ_FAST_CAUSAL 1
+#include "attention_fast.hip"

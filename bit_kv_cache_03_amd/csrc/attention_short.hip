@@ -29,11 +29,11 @@
 // the next block, S^T = K Q^T (8 fp16 MFMA + 1 correction step), mask the
 // ragged block, lazy max, exponentials, O^T += V^T P^T (8 fp16 MFMA).
 //
-// Paged caches and binary16 metadata: the instances for them are built from
+// Paged caches and 16-bit metadata: the instances for them are built from
 // this file in translation units of their own (attention_short_paged.hip,
-// attention_short_m16.hip, attention_short_m16_paged.hip define
-// KVQ_SHORT_PAGED / KVQ_SHORT_META16), so that they cannot change how the
-// default ones are compiled.
+// attention_short_m16*.hip and attention_short_mb16*.hip define
+// KVQ_SHORT_PAGED and KVQ_SHORT_META16 = 1 binary16 / 2 bfloat16), so that
+// they cannot change how the default ones are compiled.
 #include <math.h>
 
 #include "kvq_device.h"
@@ -88,9 +88,9 @@ struct Fetch {
 struct Lanes {
   uint32_t kc, km, vc, vm;
 };
-template <int KBITS, int VBITS, int NG, bool M16>
+template <int KBITS, int VBITS, int NG, int MT>
 __device__ inline Lanes lane_offsets(int lane) {
-  constexpr uint32_t KROW = D * KBITS / 8, VROW = D * VBITS / 8, ES = M16 ? 2 : 4;
+  constexpr uint32_t KROW = D * KBITS / 8, VROW = D * VBITS / 8, ES = MT ? 2 : 4;
   const uint32_t kr = lane & 31, h = lane >> 5, kq = lane & 7, dq = lane >> 3;
   Lanes o;
   o.kc = kr * KROW + h * (KROW / 2);
@@ -103,9 +103,9 @@ __device__ inline Lanes lane_offsets(int lane) {
 // Loads one cached block (rows [k0, k0 + 32)); rows at or past the segment
 // end read as zero (their scores are masked).  Paged: the buffer range stops
 // at the block's end, inside its page.
-template <int KBITS, int VBITS, int NG, bool PAGED, bool M16>
+template <int KBITS, int VBITS, int NG, bool PAGED, int MT>
 __device__ inline void fetch_cached(const Ctx &c, int k0, const Lanes &o, int h, Fetch &f, size_t pool_row = 0) {
-  constexpr uint32_t KROW = D * KBITS / 8, VROW = D * VBITS / 8, ES = M16 ? 2 : 4;
+  constexpr uint32_t KROW = D * KBITS / 8, VROW = D * VBITS / 8, ES = MT ? 2 : 4;
   const uint32_t rows = static_cast<uint32_t>(PAGED ? min(c.nc - k0, BK) : c.nc - k0);
   const size_t r0 = PAGED ? pool_row : block_row<false>(c, k0);  // paged: looked up a block earlier
   {
@@ -116,19 +116,19 @@ __device__ inline void fetch_cached(const Ctx &c, int k0, const Lanes &o, int h,
       const u32x4 b = ld128(kc, o.kc + 16);
       f.kw[4] = b.x; f.kw[5] = b.y; f.kw[6] = b.z; f.kw[7] = b.w;
     }
-    const Buf ks = buffer_at(meta_adv<M16>(c.kc_scale, r0 * NG), rows * NG * ES);
-    const Buf kz = buffer_at(meta_adv<M16>(c.kc_zero, r0 * NG), rows * NG * ES);
+    const Buf ks = buffer_at(meta_adv<MT>(c.kc_scale, r0 * NG), rows * NG * ES);
+    const Buf kz = buffer_at(meta_adv<MT>(c.kc_zero, r0 * NG), rows * NG * ES);
     // the groups of d = 64h + 32j, j = 0, 1 (the lane's own values)
     if (NG == 1) {
-      const float st = ld_meta1<M16>(ks, o.km), z = ld_meta1<M16>(kz, o.km);
+      const float st = ld_meta1<MT>(ks, o.km), z = ld_meta1<MT>(kz, o.km);
       f.kstep[0] = f.kstep[1] = st;
       f.kzero[0] = f.kzero[1] = z;
     } else if (NG == 2) {
-      const float st = ld_meta1<M16>(ks, o.km + ES * h), z = ld_meta1<M16>(kz, o.km + ES * h);
+      const float st = ld_meta1<MT>(ks, o.km + ES * h), z = ld_meta1<MT>(kz, o.km + ES * h);
       f.kstep[0] = f.kstep[1] = st;
       f.kzero[0] = f.kzero[1] = z;
     } else {
-      const float2 st = ld_meta2<M16>(ks, o.km + 2 * ES * h), z = ld_meta2<M16>(kz, o.km + 2 * ES * h);
+      const float2 st = ld_meta2<MT>(ks, o.km + 2 * ES * h), z = ld_meta2<MT>(kz, o.km + 2 * ES * h);
       f.kstep[0] = st.x;
       f.kstep[1] = st.y;
       f.kzero[0] = z.x;
@@ -137,8 +137,8 @@ __device__ inline void fetch_cached(const Ctx &c, int k0, const Lanes &o, int h,
   }
   {
     const Buf vc = buffer_at(c.vc_codes + r0 * VROW, rows * VROW);
-    const Buf vs = buffer_at(meta_adv<M16>(c.vc_scale, r0 * NG), rows * NG * ES);
-    const Buf vz = buffer_at(meta_adv<M16>(c.vc_zero, r0 * NG), rows * NG * ES);
+    const Buf vs = buffer_at(meta_adv<MT>(c.vc_scale, r0 * NG), rows * NG * ES);
+    const Buf vz = buffer_at(meta_adv<MT>(c.vc_zero, r0 * NG), rows * NG * ES);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (VBITS == 4) {
@@ -148,8 +148,8 @@ __device__ inline void fetch_cached(const Ctx &c, int k0, const Lanes &o, int h,
       } else {
         f.vw[j] = ld32(vc, o.vc + j * VROW);
       }
-      f.vstep[j] = ld_meta1<M16>(vs, o.vm + j * NG * ES);
-      f.vzero[j] = ld_meta1<M16>(vz, o.vm + j * NG * ES);
+      f.vstep[j] = ld_meta1<MT>(vs, o.vm + j * NG * ES);
+      f.vzero[j] = ld_meta1<MT>(vz, o.vm + j * NG * ES);
     }
   }
 }
@@ -416,14 +416,14 @@ __device__ inline void block_compute(const f16x8 (&k)[8], bf16x8 kext, const uin
     }
 }
 
-template <int KBITS, int VBITS, bool TAYLOR, int NG, bool CAUSAL, bool PAGED, bool M16>
+template <int KBITS, int VBITS, bool TAYLOR, int NG, bool CAUSAL, bool PAGED, int MT>
 __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, int64_t rows_per_kvhead,
                                                                 int32_t row_groups, int32_t nsplit, float *ws) {
   __shared__ __attribute__((aligned(16))) uint16_t L[LDS_BYTES / 2];
 
   const int tid = threadIdx.x;
   if (blockIdx.x >= p.app.wg0) {  // the chunk append's workgroups
-    qdev::append_workgroup(p, blockIdx.x - p.app.wg0, tid, THREADS);
+    qdev::append_workgroup<MT>(p, blockIdx.x - p.app.wg0, tid, THREADS);
     return;
   }
   const int lane = tid & 63;
@@ -473,10 +473,10 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
     const int64_t hrow = PAGED ? 0 : bkv * p.cap;  // paged: the pointers stay at the pool
     c.kc_codes = p.kc_codes + hrow * (D * KBITS / 8);
     c.vc_codes = p.vc_codes + hrow * (D * VBITS / 8);
-    c.kc_scale = meta_adv<M16>(p.kc_scale, hrow * ng);
-    c.kc_zero = meta_adv<M16>(p.kc_zero, hrow * ng);
-    c.vc_scale = meta_adv<M16>(p.vc_scale, hrow * ng);
-    c.vc_zero = meta_adv<M16>(p.vc_zero, hrow * ng);
+    c.kc_scale = meta_adv<MT>(p.kc_scale, hrow * ng);
+    c.kc_zero = meta_adv<MT>(p.kc_zero, hrow * ng);
+    c.vc_scale = meta_adv<MT>(p.vc_scale, hrow * ng);
+    c.vc_zero = meta_adv<MT>(p.vc_zero, hrow * ng);
   }
   if (p.Ncur > 0) {
     c.k_cur = p.k_cur + bkv * p.Ncur * D;
@@ -503,7 +503,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
 
   int blk = bbeg + wave;
   const int cend = bend < nbc ? bend : nbc;
-  const Lanes lo = lane_offsets<KBITS, VBITS, NG, M16>(lane);
+  const Lanes lo = lane_offsets<KBITS, VBITS, NG, MT>(lane);
   Scales sc;
   // with the caches' running bounds the exponents of the cached blocks are
   // fixed once, from bounds that cover every cached block (a block's own
@@ -513,7 +513,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
   f16x8 kreg[8];
   bf16x8 kext = {};
   Fetch f;
-  if (blk < cend) fetch_cached<KBITS, VBITS, NG, PAGED, M16>(c, blk * BK, lo, h, f, block_row<PAGED>(c, blk * BK));
+  if (blk < cend) fetch_cached<KBITS, VBITS, NG, PAGED, MT>(c, blk * BK, lo, h, f, block_row<PAGED>(c, blk * BK));
   // paged: the pool row of the next block to fetch, looked up one block ahead
   // so that its scalar load has completed when the fetch needs it
   size_t prn = PAGED && blk + WAVES < cend ? block_row<PAGED>(c, (blk + WAVES) * BK) : 0;
@@ -523,7 +523,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
     if (!cache_bounds) sc.update(k_bound<KBITS, NG>(f), v_bound<VBITS>(f), st.alpha);
     unpack_k_cached<TAYLOR, KBITS, NG>(c, lane, f, sc.kscale, kreg, kext);
     unpack_v_cached<VBITS>(c, lane, f, sc.vscale, Vt);
-    if (blk + WAVES < cend) fetch_cached<KBITS, VBITS, NG, PAGED, M16>(c, (blk + WAVES) * BK, lo, h, f, prn);
+    if (blk + WAVES < cend) fetch_cached<KBITS, VBITS, NG, PAGED, MT>(c, (blk + WAVES) * BK, lo, h, f, prn);
     block_compute<TAYLOR || kCentre<NG>>(kreg, kext, Vt, q, qext, count, sc.alpha, sc.ev, lane, st);
     if (PAGED && blk + 2 * WAVES < cend) prn = block_row<PAGED>(c, (blk + 2 * WAVES) * BK);
   }
@@ -601,7 +601,8 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
 template <int KB, int VB, int NG>
 void launch_kernel(const AttnLaunch &p, hipStream_t stream, dim3 grid, int64_t rows, int32_t row_groups,
                    float *partials) {
-  constexpr bool PG = KVQ_SHORT_PAGED != 0, MH = KVQ_SHORT_META16 != 0;
+  constexpr bool PG = KVQ_SHORT_PAGED != 0;
+  constexpr int MH = KVQ_SHORT_META16;
   auto kernel = p.corr == KV_CORR_TAYLOR ? (p.causal ? attn_short_kernel<KB, VB, true, NG, true, PG, MH>
                                                      : attn_short_kernel<KB, VB, true, NG, false, PG, MH>)
                                          : (p.causal ? attn_short_kernel<KB, VB, false, NG, true, PG, MH>
@@ -636,7 +637,11 @@ hipError_t launch_bits(const AttnLaunch &p, hipStream_t stream) {
 }  // namespace
 
 #if KVQ_SHORT_PAGED || KVQ_SHORT_META16
-#if KVQ_SHORT_PAGED && KVQ_SHORT_META16
+#if KVQ_SHORT_PAGED && KVQ_SHORT_META16 == 2
+hipError_t launch_attention_short_fast_mb16_paged(const AttnLaunch &p, hipStream_t stream) {
+#elif KVQ_SHORT_META16 == 2
+hipError_t launch_attention_short_fast_mb16(const AttnLaunch &p, hipStream_t stream) {
+#elif KVQ_SHORT_PAGED && KVQ_SHORT_META16
 hipError_t launch_attention_short_fast_m16_paged(const AttnLaunch &p, hipStream_t stream) {
 #elif KVQ_SHORT_PAGED
 hipError_t launch_attention_short_fast_paged(const AttnLaunch &p, hipStream_t stream) {
@@ -674,11 +679,16 @@ int short_fast_splits(int64_t B, int64_t Hkv, int64_t rows_per_kvhead, int64_t N
 
 hipError_t launch_attention_short_fast(const AttnLaunch &p, hipStream_t stream) {
   if (p.Nq * (p.Hq / p.Hkv) <= 16) {  // one 16-row query tile per KV head (attention_short16.hip)
-    if (p.meta16)
+    if (p.meta == kMetaBF16)
+      return p.layout.page_table ? launch_attention_short16_mb16_paged(p, stream) : launch_attention_short16_mb16(p, stream);
+    if (p.meta == kMetaF16)
       return p.layout.page_table ? launch_attention_short16_m16_paged(p, stream) : launch_attention_short16_m16(p, stream);
     return p.layout.page_table ? launch_attention_short16_paged(p, stream) : launch_attention_short16(p, stream);
   }
-  if (p.meta16)
+  if (p.meta == kMetaBF16)
+    return p.layout.page_table ? launch_attention_short_fast_mb16_paged(p, stream)
+                               : launch_attention_short_fast_mb16(p, stream);
+  if (p.meta == kMetaF16)
     return p.layout.page_table ? launch_attention_short_fast_m16_paged(p, stream) : launch_attention_short_fast_m16(p, stream);
   if (p.layout.page_table) return launch_attention_short_fast_paged(p, stream);
   const int kb = p.Nc > 0 ? p.kbits : 2, vb = p.Nc > 0 ? p.vbits : 2;

@@ -81,9 +81,9 @@ struct Fetch {
 struct Lanes {
   uint32_t kc, km, vc, vm;
 };
-template <int KBITS, int VBITS, int NG, bool M16>
+template <int KBITS, int VBITS, int NG, int MT>
 __device__ inline Lanes lane_offsets(int lane) {
-  constexpr uint32_t KROW = D * KBITS / 8, VROW = D * VBITS / 8, ES = M16 ? 2 : 4;
+  constexpr uint32_t KROW = D * KBITS / 8, VROW = D * VBITS / 8, ES = MT ? 2 : 4;
   const uint32_t r = lane & 15, j = lane >> 4, kq = lane & 7, dq = lane >> 3;
   Lanes o;
   o.kc = r * KROW + j * (32 * KBITS / 8);
@@ -96,9 +96,9 @@ __device__ inline Lanes lane_offsets(int lane) {
 // Loads one cached block (rows [k0, k0 + 32)); rows at or past the segment
 // end read as zero (their scores are masked).  Paged: the buffer range stops
 // at the block's end, inside its page.
-template <int KBITS, int VBITS, int NG, bool PAGED, bool M16>
+template <int KBITS, int VBITS, int NG, bool PAGED, int MT>
 __device__ inline void fetch_cached(const Ctx &c, int k0, const Lanes &o, Fetch &f, size_t pool_row = 0) {
-  constexpr uint32_t KROW = D * KBITS / 8, VROW = D * VBITS / 8, ES = M16 ? 2 : 4;
+  constexpr uint32_t KROW = D * KBITS / 8, VROW = D * VBITS / 8, ES = MT ? 2 : 4;
   const uint32_t rows = static_cast<uint32_t>(PAGED ? min(c.nc - k0, BK) : c.nc - k0);
   const size_t r0 = PAGED ? pool_row : block_row<false>(c, k0);  // paged: looked up a block earlier
   {
@@ -113,18 +113,18 @@ __device__ inline void fetch_cached(const Ctx &c, int k0, const Lanes &o, Fetch 
         f.kw[t][0] = a.x; f.kw[t][1] = a.y;
       }
     }
-    const Buf ks = buffer_at(meta_adv<M16>(c.kc_scale, r0 * NG), rows * NG * ES);
-    const Buf kz = buffer_at(meta_adv<M16>(c.kc_zero, r0 * NG), rows * NG * ES);
+    const Buf ks = buffer_at(meta_adv<MT>(c.kc_scale, r0 * NG), rows * NG * ES);
+    const Buf kz = buffer_at(meta_adv<MT>(c.kc_zero, r0 * NG), rows * NG * ES);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      f.kstep[t] = ld_meta1<M16>(ks, o.km + t * 16 * NG * ES);
-      f.kzero[t] = ld_meta1<M16>(kz, o.km + t * 16 * NG * ES);
+      f.kstep[t] = ld_meta1<MT>(ks, o.km + t * 16 * NG * ES);
+      f.kzero[t] = ld_meta1<MT>(kz, o.km + t * 16 * NG * ES);
     }
   }
   {
     const Buf vc = buffer_at(c.vc_codes + r0 * VROW, rows * VROW);
-    const Buf vs = buffer_at(meta_adv<M16>(c.vc_scale, r0 * NG), rows * NG * ES);
-    const Buf vz = buffer_at(meta_adv<M16>(c.vc_zero, r0 * NG), rows * NG * ES);
+    const Buf vs = buffer_at(meta_adv<MT>(c.vc_scale, r0 * NG), rows * NG * ES);
+    const Buf vz = buffer_at(meta_adv<MT>(c.vc_zero, r0 * NG), rows * NG * ES);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (VBITS == 4) {
@@ -134,8 +134,8 @@ __device__ inline void fetch_cached(const Ctx &c, int k0, const Lanes &o, Fetch 
       } else {
         f.vw[i] = ld32(vc, o.vc + i * VROW);
       }
-      f.vstep[i] = ld_meta1<M16>(vs, o.vm + i * NG * ES);
-      f.vzero[i] = ld_meta1<M16>(vz, o.vm + i * NG * ES);
+      f.vstep[i] = ld_meta1<MT>(vs, o.vm + i * NG * ES);
+      f.vzero[i] = ld_meta1<MT>(vz, o.vm + i * NG * ES);
     }
   }
 }
@@ -449,14 +449,14 @@ __device__ inline void block_compute(const f16x8 (&k)[2][4], const bf16x8 (&kext
                                                       pk, st.o[dt], 0, 0, 0);
 }
 
-template <int KBITS, int VBITS, bool TAYLOR, int NG, bool CAUSAL, bool PAGED, bool M16>
+template <int KBITS, int VBITS, bool TAYLOR, int NG, bool CAUSAL, bool PAGED, int MT>
 __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, int64_t rows_per_kvhead,
                                                                   int32_t nsplit, float *ws) {
   __shared__ __attribute__((aligned(16))) uint16_t L[LDS_BYTES / 2];
 
   const int tid = threadIdx.x;
   if (blockIdx.x >= p.app.wg0) {  // the chunk append's workgroups
-    qdev::append_workgroup(p, blockIdx.x - p.app.wg0, tid, THREADS);
+    qdev::append_workgroup<MT>(p, blockIdx.x - p.app.wg0, tid, THREADS);
     return;
   }
   const int lane = tid & 63;
@@ -501,10 +501,10 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
     const int64_t hrow = PAGED ? 0 : bkv * p.cap;  // paged: the pointers stay at the pool
     c.kc_codes = p.kc_codes + hrow * (D * KBITS / 8);
     c.vc_codes = p.vc_codes + hrow * (D * VBITS / 8);
-    c.kc_scale = meta_adv<M16>(p.kc_scale, hrow * NG);
-    c.kc_zero = meta_adv<M16>(p.kc_zero, hrow * NG);
-    c.vc_scale = meta_adv<M16>(p.vc_scale, hrow * NG);
-    c.vc_zero = meta_adv<M16>(p.vc_zero, hrow * NG);
+    c.kc_scale = meta_adv<MT>(p.kc_scale, hrow * NG);
+    c.kc_zero = meta_adv<MT>(p.kc_zero, hrow * NG);
+    c.vc_scale = meta_adv<MT>(p.vc_scale, hrow * NG);
+    c.vc_zero = meta_adv<MT>(p.vc_zero, hrow * NG);
   }
   if (p.Ncur > 0) {
     c.k_cur = p.k_cur + bkv * p.Ncur * D;
@@ -531,7 +531,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
 
   int blk = bbeg + wave;
   const int cend = bend < nbc ? bend : nbc;
-  const Lanes lo = lane_offsets<KBITS, VBITS, NG, M16>(lane);
+  const Lanes lo = lane_offsets<KBITS, VBITS, NG, MT>(lane);
   Scales sc;
   // with the caches' running bounds the exponents of the cached blocks are
   // fixed once, from bounds that cover every cached block (a block's own
@@ -541,7 +541,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
   f16x8 kreg[2][4];
   bf16x8 kext[2] = {};
   Fetch f;
-  if (blk < cend) fetch_cached<KBITS, VBITS, NG, PAGED, M16>(c, blk * BK, lo, f, block_row<PAGED>(c, blk * BK));
+  if (blk < cend) fetch_cached<KBITS, VBITS, NG, PAGED, MT>(c, blk * BK, lo, f, block_row<PAGED>(c, blk * BK));
   // paged: the pool row of the next block to fetch, looked up one block ahead
   // so that its scalar load has completed when the fetch needs it
   size_t prn = PAGED && blk + WAVES < cend ? block_row<PAGED>(c, (blk + WAVES) * BK) : 0;
@@ -551,7 +551,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
     if (!cache_bounds) sc.update(k_bound<KBITS, NG>(f), v_bound<VBITS>(f), st.alpha);
     unpack_k_cached<TAYLOR, KBITS, NG>(c, lane, f, sc.kscale, kreg, kext);
     unpack_v_cached<VBITS>(c, lane, f, sc.vscale, Vt);
-    if (blk + WAVES < cend) fetch_cached<KBITS, VBITS, NG, PAGED, M16>(c, (blk + WAVES) * BK, lo, f, prn);
+    if (blk + WAVES < cend) fetch_cached<KBITS, VBITS, NG, PAGED, MT>(c, (blk + WAVES) * BK, lo, f, prn);
     block_compute<TAYLOR || kCentre<NG>>(kreg, kext, Vt, q, qext, count, sc.alpha, sc.ev, lane, st);
     if (PAGED && blk + 2 * WAVES < cend) prn = block_row<PAGED>(c, (blk + 2 * WAVES) * BK);
   }
@@ -625,7 +625,8 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
 
 template <int KB, int VB, int NG>
 void launch_kernel(const AttnLaunch &p, hipStream_t stream, dim3 grid, int64_t rows, float *partials) {
-  constexpr bool PG = KVQ_SHORT16_PAGED != 0, MH = KVQ_SHORT16_META16 != 0;
+  constexpr bool PG = KVQ_SHORT16_PAGED != 0;
+  constexpr int MH = KVQ_SHORT16_META16;
   auto kernel = p.corr == KV_CORR_TAYLOR ? (p.causal ? attn_short16_kernel<KB, VB, true, NG, true, PG, MH>
                                                      : attn_short16_kernel<KB, VB, true, NG, false, PG, MH>)
                                          : (p.causal ? attn_short16_kernel<KB, VB, false, NG, true, PG, MH>
@@ -658,7 +659,11 @@ hipError_t launch_bits(const AttnLaunch &p, hipStream_t stream) {
 
 }  // namespace
 
-#if KVQ_SHORT16_PAGED && KVQ_SHORT16_META16
+#if KVQ_SHORT16_PAGED && KVQ_SHORT16_META16 == 2
+hipError_t launch_attention_short16_mb16_paged(const AttnLaunch &p, hipStream_t stream) {
+#elif KVQ_SHORT16_META16 == 2
+hipError_t launch_attention_short16_mb16(const AttnLaunch &p, hipStream_t stream) {
+#elif KVQ_SHORT16_PAGED && KVQ_SHORT16_META16
 hipError_t launch_attention_short16_m16_paged(const AttnLaunch &p, hipStream_t stream) {
 #elif KVQ_SHORT16_PAGED
 hipError_t launch_attention_short16_paged(const AttnLaunch &p, hipStream_t stream) {

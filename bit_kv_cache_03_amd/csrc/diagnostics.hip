@@ -212,10 +212,10 @@ __global__ __launch_bounds__(THREADS) void attn_diag_kernel(DiagLaunch p, int32_
         uint32_t lo[DPT / 2];
 #pragma unroll
         for (int e = 0; e < DPT; e += 2) {
-          const float sa = meta_at(p.kc_scale, m0 + mstep * e, p.meta16);
-          const float za = meta_at(p.kc_zero, m0 + mstep * e, p.meta16);
-          const float sc = meta_at(p.kc_scale, m0 + mstep * (e + 1), p.meta16);
-          const float zc = meta_at(p.kc_zero, m0 + mstep * (e + 1), p.meta16);
+          const float sa = meta_at(p.kc_scale, m0 + mstep * e, p.meta);
+          const float za = meta_at(p.kc_zero, m0 + mstep * e, p.meta);
+          const float sc = meta_at(p.kc_scale, m0 + mstep * (e + 1), p.meta);
+          const float zc = meta_at(p.kc_zero, m0 + mstep * (e + 1), p.meta);
           const float a = fmaf(sa, code_at<KBITS>(w[e / PER], e % PER), za);
           const float c = fmaf(sc, code_at<KBITS>(w[(e + 1) / PER], (e + 1) % PER), zc);
           hi[e / 2] = ok ? bf16_pair(a, c) : 0u;
@@ -235,14 +235,14 @@ __global__ __launch_bounds__(THREADS) void attn_diag_kernel(DiagLaunch p, int32_
           const int hk0 = 32 * (tid / D);  // first key of the half
           const bool okh = hk0 < count;
           const int64_t hrow = p.layout.row(p.cap, p.Hkv, b, hk, k0 + (okh ? hk0 : 0));
-          Dt[tid] = okh ? meta_at(p.kc_scale, (hrow >> group_shift) * D + tid % D, p.meta16) : 0.f;
+          Dt[tid] = okh ? meta_at(p.kc_scale, (hrow >> group_shift) * D + tid % D, p.meta) : 0.f;
         }
         if ((tid & 3) == 0 && !p.ktok) {
           // correction slots 3g+{0,1,2} = -D^2 split (hi, lo, hi)
           float e16[16];
           float dsh[4] = {0.f, 0.f, 0.f, 0.f}, dsl[4] = {0.f, 0.f, 0.f, 0.f};
           for (int gg = 0; gg < ng; ++gg) {
-            const float s = ok ? meta_at(p.kc_scale, row * ng + gg, p.meta16) : 0.f;
+            const float s = ok ? meta_at(p.kc_scale, row * ng + gg, p.meta) : 0.f;
             dsh[gg] = bf16_round(s * s);
             dsl[gg] = s * s - dsh[gg];
             if (EXACT) Dk[key * 4 + gg] = s;

@@ -13,7 +13,7 @@ namespace {
 
 using kvq::AttnLaunch;
 
-constexpr int32_t kAbiVersion = 9;
+constexpr int32_t kAbiVersion = 10;
 constexpr int32_t kMaxSplits = 1024;  // grid z extent of the split path
 constexpr int64_t kMaxTokensPerHead = int64_t(1) << 23;  // 8M tokens: 32-bit in-head offsets
 
@@ -26,6 +26,10 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool page_size_ok(int32_t ps) { return ps >= 16 && ps <= (1 << 23) && (ps & (ps - 1)) == 0; }
 
 bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
+
+static_assert(KV_META_F32 == kvq::kMetaF32 && KV_META_F16 == kvq::kMetaF16 && KV_META_BF16 == kvq::kMetaBF16,
+              "the kernels take kv_meta values as their metadata kinds");
+bool meta_ok(int32_t m) { return m == KV_META_F32 || m == KV_META_F16 || m == KV_META_BF16; }
 
 bool group_ok(int32_t group, int32_t d) {
   return (group == 32 || group == 64 || group == 128) && group <= d && d % group == 0;
@@ -65,7 +69,7 @@ kv_status check_qtensor(const kv_qtensor *t, int32_t d, int64_t need_rows, int64
   if (t->cap > kMaxTokensPerHead) return KV_ERR_UNSUPPORTED;
   if (!aligned16(t->codes) || !aligned16(t->scale) || !aligned16(t->zero)) return KV_ERR_ALIGN;
   if ((reinterpret_cast<uintptr_t>(t->bound) & 3u) != 0) return KV_ERR_ALIGN;
-  if (t->meta != KV_META_F32 && t->meta != KV_META_F16) return KV_ERR_UNSUPPORTED;
+  if (!meta_ok(t->meta)) return KV_ERR_UNSUPPORTED;
   if (t->page_table) {
     if (!page_size_ok(t->page_size) || t->cap % t->page_size != 0) return KV_ERR_SHAPE;
     if (t->num_pages < 1) return KV_ERR_SHAPE;
@@ -93,7 +97,7 @@ bool same_layout(const kv_qtensor *a, const kv_qtensor *b) {
 }
 
 // Bytes of one step or zero-point element.
-size_t meta_bytes(const kv_qtensor *t) { return t->meta == KV_META_F16 ? 2 : 4; }
+size_t meta_bytes(const kv_qtensor *t) { return t->meta == KV_META_F32 ? 4 : 2; }
 
 // Bytes of a cache tensor's step (or zero-point) array over `rows` token rows.
 size_t meta_array_bytes(const kv_qtensor *t, size_t rows, int32_t d) {
@@ -404,7 +408,7 @@ kv_status kv_quantize(const void *x, kv_dtype xdt, int64_t B, int64_t H, int64_t
   if (!aligned16(x) || !aligned16(dst->codes) || !aligned16(dst->scale) || !aligned16(dst->zero))
     return KV_ERR_ALIGN;
   if ((reinterpret_cast<uintptr_t>(dst->bound) & 3u) != 0) return KV_ERR_ALIGN;
-  if (dst->meta != KV_META_F32 && dst->meta != KV_META_F16) return KV_ERR_UNSUPPORTED;
+  if (!meta_ok(dst->meta)) return KV_ERR_UNSUPPORTED;
   {  // the input must not overlap the cache it is written into
     const size_t xb = static_cast<size_t>(t) * (xdt == KV_BF16 ? 2 : 4);
     const size_t rows = static_cast<size_t>(tensor_rows(dst, B, H));
@@ -417,7 +421,7 @@ kv_status kv_quantize(const void *x, kv_dtype xdt, int64_t B, int64_t H, int64_t
   if (N == 0) return KV_OK;
   kvq::QuantizeLaunch p{x, static_cast<int>(xdt), B, H, N, d, dst->codes, static_cast<float *>(dst->scale),
                         static_cast<float *>(dst->zero), dst->bits, dst->group, dst->cap, tok_offset,
-                        layout_of(dst), dst->meta == KV_META_F16, dst->axis == KV_AXIS_TOKENS, dst->bound};
+                        layout_of(dst), static_cast<int>(dst->meta), dst->axis == KV_AXIS_TOKENS, dst->bound};
   return kvq::launch_quantize(p, static_cast<hipStream_t>(stream)) == hipSuccess ? KV_OK : KV_ERR_HIP;
 }
 
@@ -445,7 +449,7 @@ kv_status launch_attention(const kv_attn_args *a, const Plan &pl, void *workspac
     p.vc_codes = a->v_cache->codes;
     p.vc_scale = static_cast<const float *>(a->v_cache->scale);
     p.vc_zero = static_cast<const float *>(a->v_cache->zero);
-    p.meta16 = a->k_cache->meta == KV_META_F16;
+    p.meta = static_cast<int>(a->k_cache->meta);
     p.ktok = a->k_cache->axis == KV_AXIS_TOKENS;
     p.vtok = a->v_cache->axis == KV_AXIS_TOKENS;
     p.kbits = a->k_cache->bits; p.vbits = a->v_cache->bits; p.group = a->k_cache->group; p.cap = a->k_cache->cap;
@@ -473,7 +477,7 @@ kv_status launch_attention(const kv_attn_args *a, const Plan &pl, void *workspac
     p.app.bits[0] = k->bits;
     p.app.bits[1] = v->bits;
     p.app.group = k->group;
-    p.app.meta16 = k->meta == KV_META_F16;
+    p.app.meta = static_cast<int>(k->meta);
     p.app.cap = k->cap;
     p.app.layout = layout_of(k);
     p.app.bound[0] = k->bound;
@@ -525,7 +529,7 @@ kv_status kv_attention_diagnostics(const kv_diag_args *a, void *stream) {
     p.kc_codes = a->k_cache->codes;
     p.kc_scale = static_cast<const float *>(a->k_cache->scale);
     p.kc_zero = static_cast<const float *>(a->k_cache->zero);
-    p.meta16 = a->k_cache->meta == KV_META_F16;
+    p.meta = static_cast<int>(a->k_cache->meta);
     p.ktok = a->k_cache->axis == KV_AXIS_TOKENS;
     p.kbits = a->k_cache->bits; p.group = a->k_cache->group; p.cap = a->k_cache->cap;
     p.layout = layout_of(a->k_cache);

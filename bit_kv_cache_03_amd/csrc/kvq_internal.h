@@ -27,10 +27,39 @@ struct CacheLayout {
   }
 };
 
-// Metadata element i of a step or zero-point array stored as fp32, or as
-// binary16 when meta16 (the pointer then addresses binary16 elements).
-__host__ __device__ inline float meta_at(const float *p, int64_t i, bool meta16) {
-  return meta16 ? static_cast<float>(reinterpret_cast<const _Float16 *>(p)[i]) : p[i];
+// Storage of a cache tensor's step and zero-point elements (the values of
+// kv_meta): fp32, IEEE binary16 or bfloat16.  With 16 bits the float
+// pointers of the arrays address 16-bit elements.
+constexpr int kMetaF32 = 0, kMetaF16 = 1, kMetaBF16 = 2;
+
+// A 16-bit step or zero-point element of kind mk as fp32 (exact: a bfloat16
+// pattern is the upper half of the fp32 one).
+__host__ __device__ inline float meta16_value(uint16_t h, int mk) {
+  if (mk == kMetaBF16) return __builtin_bit_cast(float, static_cast<uint32_t>(h) << 16);
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+// The 16-bit pattern of kind mk nearest to x (ties to even), as stored.
+// bfloat16: adding 0x7fff plus the kept half's lowest bit to the fp32 bits
+// carries into the kept half exactly when the dropped half exceeds one half
+// of its unit, or equals it with an odd kept half (NaN stays a quiet NaN).
+__host__ __device__ inline uint16_t meta16_bits(float x, int mk) {
+  if (mk == kMetaBF16) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+  }
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
+
+// The stored value of an fp32 step or zero point.
+__host__ __device__ inline float meta_round(float x, int mk) {
+  return mk == kMetaF32 ? x : meta16_value(meta16_bits(x, mk), mk);
+}
+
+// Metadata element i of a step or zero-point array of kind mk.
+__host__ __device__ inline float meta_at(const float *p, int64_t i, int mk) {
+  return mk == kMetaF32 ? p[i] : meta16_value(reinterpret_cast<const uint16_t *>(p)[i], mk);
 }
 
 // Everything a quantize launch needs, already validated by the host.
@@ -45,7 +74,7 @@ struct QuantizeLaunch {
   int32_t bits, group;
   int64_t cap, off;
   CacheLayout layout;
-  bool meta16;  // scale and zero are binary16 (the pointers are then read as such)
+  int meta;     // kind of the scale and zero arrays (kMetaF32 / kMetaF16 / kMetaBF16)
   bool tokens;  // groups along the tokens: scale/zero [row / group][d], row the cache row
   float *bound;  // [B][H] running bound of |z|, |z + top D| (atomic max), or nullptr
 };
@@ -57,10 +86,10 @@ struct QuantizeLaunch {
 struct AppendLaunch {
   bool on;
   uint8_t *codes[2];
-  float *scale[2], *zero[2];  // binary16 arrays when meta16
+  float *scale[2], *zero[2];  // 16-bit arrays unless meta is kMetaF32
   int32_t bits[2];
   int32_t group;
-  bool meta16;
+  int meta;  // kind of the caches' scale and zero arrays
   int64_t cap;
   CacheLayout layout;
   float *bound[2];  // the caches' running bounds [B][Hkv], or nullptr
@@ -80,7 +109,7 @@ struct AttnLaunch {
   int32_t kbits, vbits, group;
   int64_t cap;
   CacheLayout layout;  // of both caches
-  bool meta16;         // the caches' scale and zero are binary16 (pointers read as such)
+  int meta;            // kind of both caches' scale and zero arrays (kMetaF32 / kMetaF16 / kMetaBF16)
   bool ktok, vtok;     // K / V groups along the tokens (per channel): scale/zero [row >> log2 group][d]
   float tau;   // resolved softmax scale
   int corr;    // kv_corr
@@ -130,11 +159,15 @@ hipError_t launch_attention_fast_causal(const AttnLaunch &p, hipStream_t stream)
 hipError_t launch_attention_fast_paged(const AttnLaunch &p, hipStream_t stream);
 hipError_t launch_attention_fast_paged_causal(const AttnLaunch &p, hipStream_t stream);
 // Binary16 steps and zero points: the same four variants
-// (attention_fast_m16*.hip).
+// (attention_fast_m16*.hip); bfloat16 ones: attention_fast_mb16*.hip.
 hipError_t launch_attention_fast_m16(const AttnLaunch &p, hipStream_t stream);
 hipError_t launch_attention_fast_m16_causal(const AttnLaunch &p, hipStream_t stream);
 hipError_t launch_attention_fast_m16_paged(const AttnLaunch &p, hipStream_t stream);
 hipError_t launch_attention_fast_m16_paged_causal(const AttnLaunch &p, hipStream_t stream);
+hipError_t launch_attention_fast_mb16(const AttnLaunch &p, hipStream_t stream);
+hipError_t launch_attention_fast_mb16_causal(const AttnLaunch &p, hipStream_t stream);
+hipError_t launch_attention_fast_mb16_paged(const AttnLaunch &p, hipStream_t stream);
+hipError_t launch_attention_fast_mb16_paged_causal(const AttnLaunch &p, hipStream_t stream);
 // Pre-pass of the throughput kernel: per (b, KV head), 32 partial bounds of
 // |key| (dequantised cache and current chunk) and of |query|, from which the
 // kernel takes the exponent that balances its fp16 key and query operands.
@@ -160,18 +193,24 @@ int short_fast_splits(int64_t B, int64_t Hkv, int64_t rows_per_kvhead, int64_t N
 hipError_t launch_attention_short_fast(const AttnLaunch &p, hipStream_t stream);
 // The same over a paged cache, with binary16 metadata, and both (built in
 // attention_short_paged.hip, attention_short_m16.hip,
-// attention_short_m16_paged.hip).
+// attention_short_m16_paged.hip); with bfloat16 metadata
+// (attention_short_mb16.hip, attention_short_mb16_paged.hip).
 hipError_t launch_attention_short_fast_paged(const AttnLaunch &p, hipStream_t stream);
 hipError_t launch_attention_short_fast_m16(const AttnLaunch &p, hipStream_t stream);
 hipError_t launch_attention_short_fast_m16_paged(const AttnLaunch &p, hipStream_t stream);
+hipError_t launch_attention_short_fast_mb16(const AttnLaunch &p, hipStream_t stream);
+hipError_t launch_attention_short_fast_mb16_paged(const AttnLaunch &p, hipStream_t stream);
 // The short-query kernel on 16-row query tiles (attention_short16.hip), for
 // at most 16 query rows per KV head; its paged, binary16 and paged binary16
 // instances in attention_short16_paged.hip, attention_short16_m16.hip,
-// attention_short16_m16_paged.hip.  Same workspace and split count.
+// attention_short16_m16_paged.hip, the bfloat16 ones in
+// attention_short16_mb16*.hip.  Same workspace and split count.
 hipError_t launch_attention_short16(const AttnLaunch &p, hipStream_t stream);
 hipError_t launch_attention_short16_paged(const AttnLaunch &p, hipStream_t stream);
 hipError_t launch_attention_short16_m16(const AttnLaunch &p, hipStream_t stream);
 hipError_t launch_attention_short16_m16_paged(const AttnLaunch &p, hipStream_t stream);
+hipError_t launch_attention_short16_mb16(const AttnLaunch &p, hipStream_t stream);
+hipError_t launch_attention_short16_mb16_paged(const AttnLaunch &p, hipStream_t stream);
 
 // Everything a diagnostics launch needs, already validated by the host.
 struct DiagLaunch {
@@ -183,7 +222,7 @@ struct DiagLaunch {
   int32_t kbits, group;
   int64_t cap;
   CacheLayout layout;
-  bool meta16;
+  int meta;   // kind of the K cache's scale and zero arrays
   bool ktok;  // the K cache groups along the tokens (per channel)
   float tau;   // resolved softmax scale
   int corr;    // kv_corr

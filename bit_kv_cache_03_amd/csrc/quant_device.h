@@ -75,10 +75,10 @@ __device__ inline bool reciprocal_ok(float step) { return step >= 0x1p-120f && s
 
 // Codes of one lane's 8 consecutive values of a group that LANES adjacent,
 // aligned lanes hold (every lane of the group must execute this), packed
-// LSB-first; step and zp are the group's step and zero point as stored (M16:
-// rounded to binary16 before the codes are taken, so that z + D c uses
-// exactly the stored pair).
-template <int BITS, int LANES, bool M16>
+// LSB-first; step and zp are the group's step and zero point as stored (with
+// 16-bit metadata of kind MT, rounded to it before the codes are taken, so
+// that z + D c uses exactly the stored pair).
+template <int BITS, int LANES, int MT>
 __device__ inline uint32_t quantize8(const float (&v)[8], float &step, float &zp) {
 #pragma clang fp contract(off)
   constexpr int TOP = (1 << BITS) - 1;
@@ -93,9 +93,9 @@ __device__ inline uint32_t quantize8(const float (&v)[8], float &step, float &zp
   const float range = mx - mn;
   step = range / static_cast<float>(TOP);  // IEEE division
   zp = mn;
-  if (M16) {
-    step = static_cast<float>(static_cast<_Float16>(step));
-    zp = static_cast<float>(static_cast<_Float16>(mn));
+  if (MT != kMetaF32) {
+    step = meta_round(step, MT);
+    zp = meta_round(mn, MT);
   }
   uint32_t packed = 0;
   if (step > 0.0f) {
@@ -136,7 +136,7 @@ __device__ inline void raise_bound(float *bound, int64_t i, float b) {
 // Stores one lane's packed codes of token row `orow` (lane `chunk` of the
 // row's d/8) and, from the first lane of each group, the group's step and
 // zero point.
-template <int BITS, int LANES, bool M16>
+template <int BITS, int LANES, int MT>
 __device__ inline void store8(uint8_t *codes, float *scale, float *zero, int64_t orow, int32_t lanes_per_row,
                               int32_t chunk, uint32_t packed, float step, float zp) {
   uint8_t *dst = codes + orow * (static_cast<int64_t>(lanes_per_row) * BITS) + static_cast<int64_t>(chunk) * BITS;
@@ -146,9 +146,9 @@ __device__ inline void store8(uint8_t *codes, float *scale, float *zero, int64_t
     *reinterpret_cast<uint32_t *>(dst) = packed;
   if ((chunk % LANES) == 0) {
     const int64_t m = orow * (lanes_per_row / LANES) + chunk / LANES;
-    if (M16) {
-      reinterpret_cast<_Float16 *>(scale)[m] = static_cast<_Float16>(step);
-      reinterpret_cast<_Float16 *>(zero)[m] = static_cast<_Float16>(zp);
+    if (MT != kMetaF32) {  // step and zp already hold 16-bit values: the patterns are exact
+      reinterpret_cast<uint16_t *>(scale)[m] = meta16_bits(step, MT);
+      reinterpret_cast<uint16_t *>(zero)[m] = meta16_bits(zp, MT);
     } else {
       scale[m] = step;
       zero[m] = zp;
@@ -159,18 +159,18 @@ __device__ inline void store8(uint8_t *codes, float *scale, float *zero, int64_t
 // ---- the append fused into an attention call --------------------------------
 
 // Codes of one lane's 8 values with `bits` chosen at run time (uniform).
-template <int LANES, bool M16>
+template <int LANES, int MT>
 __device__ inline uint32_t quantize8_bits(int bits, const float (&v)[8], float &step, float &zp) {
-  return bits == 2 ? quantize8<2, LANES, M16>(v, step, zp) : quantize8<4, LANES, M16>(v, step, zp);
+  return bits == 2 ? quantize8<2, LANES, MT>(v, step, zp) : quantize8<4, LANES, MT>(v, step, zp);
 }
 
-template <int LANES, bool M16>
+template <int LANES, int MT>
 __device__ inline void store8_bits(int bits, uint8_t *codes, float *scale, float *zero, int64_t orow,
                                    int32_t lanes_per_row, int32_t chunk, uint32_t packed, float step, float zp) {
   if (bits == 2)
-    store8<2, LANES, M16>(codes, scale, zero, orow, lanes_per_row, chunk, packed, step, zp);
+    store8<2, LANES, MT>(codes, scale, zero, orow, lanes_per_row, chunk, packed, step, zp);
   else
-    store8<4, LANES, M16>(codes, scale, zero, orow, lanes_per_row, chunk, packed, step, zp);
+    store8<4, LANES, MT>(codes, scale, zero, orow, lanes_per_row, chunk, packed, step, zp);
 }
 
 // Token rows [r0, r1) of the bf16 current chunk ([B][Hkv][Ncur][d], rows
@@ -189,7 +189,7 @@ struct RowBounds {
   int64_t cur = 0;
 };
 
-template <int LANES, bool M16>
+template <int LANES, int MT>
 __device__ void append_rows_t(const AttnLaunch &p, int64_t r0, int64_t r1, bool write, int tid, int nthr, float &kb,
                               float &vb, RowBounds &rb) {
   const AppendLaunch &a = p.app;
@@ -226,16 +226,16 @@ __device__ void append_rows_t(const AttnLaunch &p, int64_t r0, int64_t r1, bool 
     }
     if (write) {
       float ks, kz, vs, vz;
-      const uint32_t kp = quantize8_bits<LANES, M16>(a.bits[0], k, ks, kz);
-      const uint32_t vp = quantize8_bits<LANES, M16>(a.bits[1], v, vs, vz);
+      const uint32_t kp = quantize8_bits<LANES, MT>(a.bits[0], k, ks, kz);
+      const uint32_t vp = quantize8_bits<LANES, MT>(a.bits[1], v, vs, vz);
       if (live) {
         const uint32_t o = tok0 + static_cast<uint32_t>(r - r0);  // < 2^23 + 2^31
         const uint32_t dq = o / ncur, tok = o - dq * ncur;
         const uint32_t bkv = static_cast<uint32_t>(bkv0) + dq;  // < 65536
         const uint32_t b = bkv / hkv, h = bkv - b * hkv;
         const int64_t orow = a.layout.row(a.cap, p.Hkv, b, h, p.Nc + tok);
-        store8_bits<LANES, M16>(a.bits[0], a.codes[0], a.scale[0], a.zero[0], orow, lanes_per_row, chunk, kp, ks, kz);
-        store8_bits<LANES, M16>(a.bits[1], a.codes[1], a.scale[1], a.zero[1], orow, lanes_per_row, chunk, vp, vs, vz);
+        store8_bits<LANES, MT>(a.bits[0], a.codes[0], a.scale[0], a.zero[0], orow, lanes_per_row, chunk, kp, ks, kz);
+        store8_bits<LANES, MT>(a.bits[1], a.codes[1], a.scale[1], a.zero[1], orow, lanes_per_row, chunk, vp, vs, vz);
         // the row's bound over its lanes (a row's lanes are live together),
         // kept by its first lane
         float kr = a.bits[0] == 2 ? group_bound<2>(ks, kz) : group_bound<4>(ks, kz);
@@ -262,32 +262,39 @@ __device__ void append_rows_t(const AttnLaunch &p, int64_t r0, int64_t r1, bool 
   rb.cur = cur;
 }
 
-// append_rows_t with the caches' group and metadata format (bounds only,
-// no group reduction and nothing stored, without `write`).  kb, vb are
-// raised to the bounds of the rows; rb receives the rows' running bounds
-// for the caller to raise (its workgroup's rows may share one entry).
+// append_rows_t with the caches' group and metadata kind MT (which must be
+// p.app.meta; bounds only, no group reduction and nothing stored, without
+// `write`).  kb, vb are raised to the bounds of the rows; rb receives the
+// rows' running bounds for the caller to raise (its workgroup's rows may
+// share one entry).
+template <int MT>
 __device__ inline void append_rows(const AttnLaunch &p, int64_t r0, int64_t r1, bool write, int tid, int nthr,
                                    float &kb, float &vb, RowBounds &rb) {
-  if (!write) return append_rows_t<4, false>(p, r0, r1, false, tid, nthr, kb, vb, rb);
+  if (!write) return append_rows_t<4, kMetaF32>(p, r0, r1, false, tid, nthr, kb, vb, rb);
   const int g = p.app.group;
-  if (p.app.meta16) {
-    if (g == 32) return append_rows_t<4, true>(p, r0, r1, true, tid, nthr, kb, vb, rb);
-    if (g == 64) return append_rows_t<8, true>(p, r0, r1, true, tid, nthr, kb, vb, rb);
-    return append_rows_t<16, true>(p, r0, r1, true, tid, nthr, kb, vb, rb);
-  }
-  if (g == 32) return append_rows_t<4, false>(p, r0, r1, true, tid, nthr, kb, vb, rb);
-  if (g == 64) return append_rows_t<8, false>(p, r0, r1, true, tid, nthr, kb, vb, rb);
-  return append_rows_t<16, false>(p, r0, r1, true, tid, nthr, kb, vb, rb);
+  if (g == 32) return append_rows_t<4, MT>(p, r0, r1, true, tid, nthr, kb, vb, rb);
+  if (g == 64) return append_rows_t<8, MT>(p, r0, r1, true, tid, nthr, kb, vb, rb);
+  return append_rows_t<16, MT>(p, r0, r1, true, tid, nthr, kb, vb, rb);
 }
 
-// Body of the append workgroups of a launch (ids p.app.wg0 .. + p.app.wgs):
-// workgroup a takes an equal share of the B*Hkv*Ncur rows of K and V (its
-// rows may span two entries of the running bounds: raised per wave).
+// The same with the metadata kind read from p.app.meta.
+__device__ inline void append_rows_any(const AttnLaunch &p, int64_t r0, int64_t r1, bool write, int tid, int nthr,
+                                       float &kb, float &vb, RowBounds &rb) {
+  if (p.app.meta == kMetaBF16) return append_rows<kMetaBF16>(p, r0, r1, write, tid, nthr, kb, vb, rb);
+  if (p.app.meta == kMetaF16) return append_rows<kMetaF16>(p, r0, r1, write, tid, nthr, kb, vb, rb);
+  return append_rows<kMetaF32>(p, r0, r1, write, tid, nthr, kb, vb, rb);
+}
+
+// Body of the append workgroups of a launch (ids p.app.wg0 .. + p.app.wgs)
+// over caches of metadata kind MT: workgroup a takes an equal share of the
+// B*Hkv*Ncur rows of K and V (its rows may span two entries of the running
+// bounds: raised per wave).
+template <int MT>
 __device__ inline void append_workgroup(const AttnLaunch &p, int64_t a, int tid, int nthr) {
   const int64_t n = p.B * p.Hkv * p.Ncur, w = p.app.wgs;
   float kb = 0.f, vb = 0.f;
   RowBounds rb;
-  append_rows(p, n * a / w, n * (a + 1) / w, true, tid, nthr, kb, vb, rb);
+  append_rows<MT>(p, n * a / w, n * (a + 1) / w, true, tid, nthr, kb, vb, rb);
   raise_bound(p.app.bound[0], rb.cur, rb.k);
   raise_bound(p.app.bound[1], rb.cur, rb.v);
 }

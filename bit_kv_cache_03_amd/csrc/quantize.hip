@@ -28,11 +28,12 @@ using namespace qdev;
 
 constexpr int kThreads = 256;
 
-// T: uint16_t (bf16 bits) or float.  LANES = group / 8.  M16: the step and
-// zero point are stored as binary16, rounded (nearest, ties to even) before
-// the codes are taken so that z + D c uses exactly what is stored.
+// T: uint16_t (bf16 bits) or float.  LANES = group / 8.  MT: the kind of the
+// step and zero-point arrays; with 16 bits (binary16 or bfloat16) they are
+// rounded (nearest, ties to even) before the codes are taken so that z + D c
+// uses exactly what is stored.
 // Grid: x over the N * d/8 lanes of one (b, h) = (blockIdx.z, blockIdx.y).
-template <typename T, int BITS, int LANES, bool M16>
+template <typename T, int BITS, int LANES, int MT>
 __global__ __launch_bounds__(kThreads) void quantize_pack(
     const T *__restrict__ x, int32_t lane_shift, int64_t N,
     uint8_t *__restrict__ codes, float *__restrict__ scale, float *__restrict__ zero,
@@ -49,15 +50,15 @@ __global__ __launch_bounds__(kThreads) void quantize_pack(
   load8<T>(x + ((bh * N + n) << (lane_shift + 3)) + chunk * 8, v);
 
   float step, zp;
-  const uint32_t packed = quantize8<BITS, LANES, M16>(v, step, zp);
+  const uint32_t packed = quantize8<BITS, LANES, MT>(v, step, zp);
   raise_bound(bound, bh, live ? group_bound<BITS>(step, zp) : 0.f);  // the block's (b, h)
 
   if (!live) return;
   const int64_t orow = layout.row(cap, H, blockIdx.z, blockIdx.y, off + n);  // the cache row of token off + n
-  store8<BITS, LANES, M16>(codes, scale, zero, orow, lanes_per_row, chunk, packed, step, zp);
+  store8<BITS, LANES, MT>(codes, scale, zero, orow, lanes_per_row, chunk, packed, step, zp);
 }
 
-template <typename T, int BITS, bool M16>
+template <typename T, int BITS, int MT>
 hipError_t launch_t(const QuantizeLaunch &p, hipStream_t stream) {
   const int32_t lane_shift = __builtin_ctz(static_cast<unsigned>(p.d / 8));  // d/8 lanes per token row
   const int64_t blocks = ((p.N << lane_shift) + kThreads - 1) / kThreads;
@@ -65,15 +66,15 @@ hipError_t launch_t(const QuantizeLaunch &p, hipStream_t stream) {
   const T *x = static_cast<const T *>(p.x);
   switch (p.group) {
     case 32:
-      quantize_pack<T, BITS, 4, M16><<<grid, dim3(kThreads), 0, stream>>>(
+      quantize_pack<T, BITS, 4, MT><<<grid, dim3(kThreads), 0, stream>>>(
           x, lane_shift, p.N, p.codes, p.scale, p.zero, p.cap, p.off, p.layout, p.H, p.bound);
       break;
     case 64:
-      quantize_pack<T, BITS, 8, M16><<<grid, dim3(kThreads), 0, stream>>>(
+      quantize_pack<T, BITS, 8, MT><<<grid, dim3(kThreads), 0, stream>>>(
           x, lane_shift, p.N, p.codes, p.scale, p.zero, p.cap, p.off, p.layout, p.H, p.bound);
       break;
     default:
-      quantize_pack<T, BITS, 16, M16><<<grid, dim3(kThreads), 0, stream>>>(
+      quantize_pack<T, BITS, 16, MT><<<grid, dim3(kThreads), 0, stream>>>(
           x, lane_shift, p.N, p.codes, p.scale, p.zero, p.cap, p.off, p.layout, p.H, p.bound);
       break;
   }
@@ -85,7 +86,7 @@ hipError_t launch_t(const QuantizeLaunch &p, hipStream_t stream) {
 // call's tokens [off, off + N) start at a multiple of G; the last group may
 // be shorter.  Metadata row of a group = cache row of its first token >> log2 G.
 // The body for one live thread; returns the bound of its channels' groups.
-template <typename T, int BITS, bool M16>
+template <typename T, int BITS, int MT>
 __device__ inline float quantize_token_group(const T *__restrict__ x, int64_t id, int32_t octets, int64_t groups,
                                              int64_t N, int32_t gshift, uint8_t *__restrict__ codes,
                                              float *__restrict__ scale, float *__restrict__ zero, int64_t cap,
@@ -121,21 +122,21 @@ __device__ inline float quantize_token_group(const T *__restrict__ x, int64_t id
     mx[e] = mx[e] + 0.0f;
     step[e] = (mx[e] - mn[e]) / static_cast<float>(TOP);  // IEEE division
     zp[e] = mn[e];
-    if (M16) {
-      step[e] = static_cast<float>(static_cast<_Float16>(step[e]));
-      zp[e] = static_cast<float>(static_cast<_Float16>(mn[e]));
+    if (MT != kMetaF32) {
+      step[e] = meta_round(step[e], MT);
+      zp[e] = meta_round(mn[e], MT);
     }
   }
   const int64_t b = bh / H, h = bh - b * H;
   const int64_t mrow = layout.row(cap, H, b, h, off + t0) >> gshift;
   const int64_t m = mrow * d + oc * 8;
-  if (M16) {
-    _Float16 *ps = reinterpret_cast<_Float16 *>(scale) + m;
-    _Float16 *pz = reinterpret_cast<_Float16 *>(zero) + m;
+  if (MT != kMetaF32) {
+    uint16_t *ps = reinterpret_cast<uint16_t *>(scale) + m;
+    uint16_t *pz = reinterpret_cast<uint16_t *>(zero) + m;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      ps[e] = static_cast<_Float16>(step[e]);
-      pz[e] = static_cast<_Float16>(zp[e]);
+      ps[e] = meta16_bits(step[e], MT);
+      pz[e] = meta16_bits(zp[e], MT);
     }
   } else {
     *reinterpret_cast<float4 *>(scale + m) = make_float4(step[0], step[1], step[2], step[3]);
@@ -173,7 +174,7 @@ __device__ inline float quantize_token_group(const T *__restrict__ x, int64_t id
 
 // The kernel: every lane of a wave, dead ones too, takes part in raising
 // the running bound.
-template <typename T, int BITS, bool M16>
+template <typename T, int BITS, int MT>
 __global__ __launch_bounds__(kThreads) void quantize_tokens_pack(
     const T *__restrict__ x, int64_t total, int32_t octets, int64_t groups, int64_t N, int32_t gshift,
     uint8_t *__restrict__ codes, float *__restrict__ scale, float *__restrict__ zero, int64_t cap, int64_t off,
@@ -181,48 +182,47 @@ __global__ __launch_bounds__(kThreads) void quantize_tokens_pack(
   const int64_t id = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   const bool live = id < total;
   float bnd = 0.f;
-  if (live) bnd = quantize_token_group<T, BITS, M16>(x, id, octets, groups, N, gshift, codes, scale, zero, cap, off,
+  if (live) bnd = quantize_token_group<T, BITS, MT>(x, id, octets, groups, N, gshift, codes, scale, zero, cap, off,
                                                      layout, H);
   // every lane of the wave takes part (dead lanes with 0): the group's (b, h)
   raise_bound(bound, live ? id / octets / groups : total / octets / groups - 1, bnd);
 }
 
 
-template <typename T, int BITS, bool M16>
+template <typename T, int BITS, int MT>
 hipError_t launch_tokens(const QuantizeLaunch &p, hipStream_t stream) {
   const int32_t gshift = __builtin_ctz(static_cast<unsigned>(p.group));
   const int64_t groups = (p.N + p.group - 1) / p.group;
   const int32_t octets = p.d / 8;
   const int64_t total = p.B * p.H * groups * octets;
   const int64_t blocks = (total + kThreads - 1) / kThreads;
-  quantize_tokens_pack<T, BITS, M16><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream>>>(
+  quantize_tokens_pack<T, BITS, MT><<<dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream>>>(
       static_cast<const T *>(p.x), total, octets, groups, p.N, gshift, p.codes, p.scale, p.zero, p.cap, p.off,
       p.layout, p.H, p.bound);
   return hipGetLastError();
 }
 
-template <typename T, bool M16>
+template <typename T, int MT>
 hipError_t launch_tokens_bits(const QuantizeLaunch &p, hipStream_t stream) {
-  return p.bits == 2 ? launch_tokens<T, 2, M16>(p, stream) : launch_tokens<T, 4, M16>(p, stream);
+  return p.bits == 2 ? launch_tokens<T, 2, MT>(p, stream) : launch_tokens<T, 4, MT>(p, stream);
+}
+
+template <int MT>
+hipError_t launch_meta(const QuantizeLaunch &p, hipStream_t stream) {
+  if (p.tokens)
+    return p.xdt == KV_BF16 ? launch_tokens_bits<uint16_t, MT>(p, stream) : launch_tokens_bits<float, MT>(p, stream);
+  if (p.xdt == KV_BF16)
+    return p.bits == 2 ? launch_t<uint16_t, 2, MT>(p, stream) : launch_t<uint16_t, 4, MT>(p, stream);
+  return p.bits == 2 ? launch_t<float, 2, MT>(p, stream) : launch_t<float, 4, MT>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_quantize(const QuantizeLaunch &p, hipStream_t stream) {
   if (p.B * p.H * p.N == 0) return hipSuccess;
-  if (p.tokens) {
-    if (p.xdt == KV_BF16)
-      return p.meta16 ? launch_tokens_bits<uint16_t, true>(p, stream) : launch_tokens_bits<uint16_t, false>(p, stream);
-    return p.meta16 ? launch_tokens_bits<float, true>(p, stream) : launch_tokens_bits<float, false>(p, stream);
-  }
-  if (p.meta16) {
-    if (p.xdt == KV_BF16)
-      return p.bits == 2 ? launch_t<uint16_t, 2, true>(p, stream) : launch_t<uint16_t, 4, true>(p, stream);
-    return p.bits == 2 ? launch_t<float, 2, true>(p, stream) : launch_t<float, 4, true>(p, stream);
-  }
-  if (p.xdt == KV_BF16)
-    return p.bits == 2 ? launch_t<uint16_t, 2, false>(p, stream) : launch_t<uint16_t, 4, false>(p, stream);
-  return p.bits == 2 ? launch_t<float, 2, false>(p, stream) : launch_t<float, 4, false>(p, stream);
+  if (p.meta == kMetaBF16) return launch_meta<kMetaBF16>(p, stream);
+  if (p.meta == kMetaF16) return launch_meta<kMetaF16>(p, stream);
+  return launch_meta<kMetaF32>(p, stream);
 }
 
 }  // namespace kvq

@@ -57,16 +57,20 @@ __device__ inline uint32_t ld32(Buf b, uint32_t off) { return __builtin_amdgcn_r
 __device__ inline u32x2 ld64(Buf b, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b64(b, off, 0, 0); }
 __device__ inline u32x4 ld128(Buf b, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b128(b, off, 0, 0); }
 
-// Step / zero-point elements (fp32, or binary16 when M16) at a byte offset:
-// one element, or two consecutive ones.
-template <bool M16>
+// Step / zero-point elements of kind MT (fp32, binary16 or bfloat16) at a
+// byte offset: one element, or two consecutive ones.
+template <int MT>
 __device__ inline float ld_meta1(Buf b, uint32_t off) {
-  if (M16) return static_cast<float>(__builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(b, off, 0, 0)));
+  if (MT != kMetaF32) return meta16_value(__builtin_amdgcn_raw_buffer_load_b16(b, off, 0, 0), MT);
   return __uint_as_float(ld32(b, off));
 }
-template <bool M16>
+template <int MT>
 __device__ inline float2 ld_meta2(Buf b, uint32_t off) {
-  if (M16) {
+  if (MT == kMetaBF16) {  // a bfloat16 pair is the upper halves of two fp32 values
+    const uint32_t w = ld32(b, off);
+    return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+  }
+  if (MT == kMetaF16) {
     const uint32_t w = ld32(b, off);
     return make_float2(static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w))),
                        static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16))));
@@ -75,9 +79,9 @@ __device__ inline float2 ld_meta2(Buf b, uint32_t off) {
   return make_float2(__uint_as_float(w.x), __uint_as_float(w.y));
 }
 // A step or zero-point array advanced by n elements.
-template <bool M16>
+template <int MT>
 __device__ inline const float *meta_adv(const float *p, int64_t n) {
-  return reinterpret_cast<const float *>(reinterpret_cast<const char *>(p) + n * (M16 ? 2 : 4));
+  return reinterpret_cast<const float *>(reinterpret_cast<const char *>(p) + n * (MT ? 2 : 4));
 }
 
 // floor(log2 x) for x > 0 (one v_frexp_exp_i32_f32).

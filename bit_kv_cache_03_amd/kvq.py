@@ -34,7 +34,7 @@ class QTensor(C.Structure):
                 ("meta", C.c_int32), ("axis", C.c_int32), ("bound", C.c_void_p)]
 
 
-META = {"f32": 0, "f16": 1}  # kv_meta: storage type of a cache tensor's step and zero point
+META = {"f32": 0, "f16": 1, "bf16": 2}  # kv_meta: storage type of a cache tensor's step and zero point
 AXIS = {"dim": 0, "tokens": 1}  # kv_axis: groups along the head dimension or along the tokens
 
 
@@ -122,8 +122,8 @@ class QCache:
     Contiguous: [B][H][cap][...].  Paged (``page_table`` given: an int32 GPU
     tensor [B][cap // page_size] of page indices): pools of ``num_pages``
     pages [num_pages][H][page_size][...]; token t of (b, h) lives in page
-    page_table[b][t // page_size] at row t % page_size.  ``meta``: "f32" or
-    "f16" (binary16 step and zero point).  ``axis``: "dim" (groups of
+    page_table[b][t // page_size] at row t % page_size.  ``meta``: "f32",
+    "f16" (binary16 step and zero point) or "bf16" (bfloat16).  ``axis``: "dim" (groups of
     ``group`` channels per token) or "tokens" (per channel, groups of
     ``group`` tokens: step and zero [B][H][cap // group][d], paged
     [num_pages][H][page_size // group][d]).  ``bound``: keep the running
@@ -143,7 +143,7 @@ class QCache:
         self.page_table, self.page_size, self.num_pages = page_table, page_size, num_pages
         self.meta, self.axis = meta, axis
         lead = (num_pages, H, page_size) if page_table is not None else (B, H, cap)
-        mdt = torch.float16 if meta == "f16" else torch.float32
+        mdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[meta]
         self.codes = torch.zeros(lead + (d * bits // 8,), dtype=torch.uint8, device=device)
         mshape = lead[:2] + (lead[2] // group, d) if axis == "tokens" else lead + (d // group,)
         self.scale = torch.zeros(mshape, dtype=mdt, device=device)

@@ -80,10 +80,13 @@ typedef enum KV_ENUM_TYPE {
 /* Storage type of a cache tensor's step D and zero point z. */
 typedef enum KV_ENUM_TYPE {
   KV_META_F32 = 0, /* fp32 (default) */
-  KV_META_F16 = 1  /* IEEE binary16: D and z rounded (nearest, ties to even) before
+  KV_META_F16 = 1, /* IEEE binary16: D and z rounded (nearest, ties to even) before
                       the codes are taken, so that z + D c uses what is stored; 2x less
                       metadata (INT2/INT2 at group 64 and d = 128: 80 instead of 96 bytes
                       per token per head); |values| must stay below 65504 */
+  KV_META_BF16 = 2 /* bfloat16: the same rounding rule and size as binary16 with fp32's
+                      range and 8 significant bits (D and z are each within 2^-9 of
+                      their fp32 values, relatively; the codes follow the rounded grid) */
 } kv_meta;
 
 /* Axis along which a cache tensor's groups run (agents-report.net page,

@@ -43,7 +43,9 @@ def build_cache(w, src: np.ndarray, bits: int, cap=None, chunk=None, meta="f32",
 
 
 def cache_to_host(c: kvq.QCache, nc: int):
-    return tuple(t.cpu().numpy() for t in c.logical(nc))
+    """(codes, step, zero) of tokens [0, nc) as numpy arrays (bfloat16 metadata
+    widened to fp32, exactly: numpy has no bfloat16)."""
+    return tuple((t.float() if t.dtype == torch.bfloat16 else t).cpu().numpy() for t in c.logical(nc))
 
 
 def run_attention(w, data, kc, vc, corr="taylor", path="auto", scale=0.0, splits=0, causal=False):

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(kvq):
 
 
 def test_version_and_status_strings(kvq):
-    assert kvq.lib.kv_version() == 9
+    assert kvq.lib.kv_version() == 10
     for s in range(1, 9):
         assert len(kvq.lib.kv_status_string(s)) > 10
     assert kvq.lib.kv_status_string(0) == b"ok"
@@ -96,7 +96,7 @@ def test_enum_values_match_header(kvq, tmp_path):
     prog = tmp_path / "enums.c"
     names = ["KV_OK", "KV_ERR_NULL", "KV_ERR_SHAPE", "KV_ERR_UNSUPPORTED", "KV_ERR_WORKSPACE", "KV_ERR_ALIGN",
              "KV_ERR_ALIAS", "KV_ERR_HIP", "KV_ERR_SCRATCH", "KV_BF16", "KV_F32", "KV_CORR_OFF", "KV_CORR_TAYLOR", "KV_CORR_EXACT",
-             "KV_PATH_AUTO", "KV_PATH_LONG", "KV_PATH_SHORT", "KV_META_F32", "KV_META_F16", "KV_AXIS_DIM",
+             "KV_PATH_AUTO", "KV_PATH_LONG", "KV_PATH_SHORT", "KV_META_F32", "KV_META_F16", "KV_META_BF16", "KV_AXIS_DIM",
              "KV_AXIS_TOKENS"]
     prog.write_text('#include <stdio.h>\n#include "kvq.h"\nint main(void) {\n' +
                     "".join(f'  printf("{n} %d\\n", (int){n});\n' for n in names) + "  return 0;\n}\n")
@@ -359,7 +359,8 @@ def test_contiguous_descriptor_with_page_fields(kvq):
     assert kvq.lib.kv_quantize(A, 0, 1, 2, 0, 128, C.byref(t), 0, None) == kvq.KV_ERR_SHAPE
 
 
-@pytest.mark.parametrize("meta,err", [(0, "KV_OK"), (1, "KV_OK"), (2, "KV_ERR_UNSUPPORTED"), (-1, "KV_ERR_UNSUPPORTED")])
+@pytest.mark.parametrize("meta,err", [(0, "KV_OK"), (1, "KV_OK"), (2, "KV_OK"), (3, "KV_ERR_UNSUPPORTED"),
+                                      (-1, "KV_ERR_UNSUPPORTED")])
 def test_quantize_meta_values(kvq, meta, err):
     t = _qt(kvq, 0x30000000)
     t.meta = meta
@@ -372,6 +373,10 @@ def test_attention_meta_must_match(kvq):
     assert kvq.lib.kv_attention_workspace_size(C.byref(a)) > 0  # both binary16: valid
     a._v.meta = 0
     assert _attn(kvq, a) == kvq.KV_ERR_UNSUPPORTED
+    a._k.meta, a._v.meta = 2, 2
+    assert kvq.lib.kv_attention_workspace_size(C.byref(a)) > 0  # both bfloat16: valid
+    a._v.meta = 1
+    assert _attn(kvq, a) == kvq.KV_ERR_UNSUPPORTED  # binary16 and bfloat16 mixed
     a._k.meta, a._v.meta = 3, 3
     assert _attn(kvq, a) == kvq.KV_ERR_UNSUPPORTED
 
@@ -383,8 +388,11 @@ def test_binding_meta_dtype():
     assert c.scale.dtype == torch.float16 and c.zero.dtype == torch.float16
     assert c.descriptor().meta == binding.META["f16"] == 1
     assert binding.QCache(1, 2, 64, 128, 4, 64, device="cpu").descriptor().meta == 0
+    b = binding.QCache(1, 2, 64, 128, 4, 64, device="cpu", meta="bf16")
+    assert b.scale.dtype == torch.bfloat16 and b.zero.dtype == torch.bfloat16
+    assert b.descriptor().meta == binding.META["bf16"] == 2
     with pytest.raises(ValueError):
-        binding.QCache(1, 2, 64, 128, 4, 64, device="cpu", meta="bf16")
+        binding.QCache(1, 2, 64, 128, 4, 64, device="cpu", meta="f8")
 
 
 @pytest.mark.parametrize("name,kw,off,err", [

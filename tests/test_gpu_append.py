@@ -7,9 +7,9 @@ kv_quantize calls followed by the same attention without append, the bytes
 of every cache array and the attention output are identical.  Every kernel
 path carries the append in its own place: the throughput kernel's pre-pass,
 extra workgroups of the short-query kernel, the general kernel's pre-pass.
-The cases cover first chunks (Nc = 0), paged pools, binary16 metadata,
-groups of 32/64/128, INT2 and INT4, the causal mask, forced splits, and two
-successive chunks.  The pages ("QuantWM：…" (pchao.org), section 方法概览)
+The cases cover first chunks (Nc = 0), paged pools, binary16 and bfloat16
+metadata, groups of 32/64/128, INT2 and INT4, the causal mask, forced
+splits, and two successive chunks.  The pages ("QuantWM：…" (pchao.org), section 方法概览)
 quantise each cache block once, after it is built."""
 import numpy as np
 import pytest
@@ -43,6 +43,13 @@ CASES = {
     "general_d64_first": (TINY.scaled(B=1, Hq=2, Hkv=1, Nq=16, Ncur=16, Nc=0), "taylor", "long", 0, False, "f32", 0),
     "general_small_pages": (GQA.scaled(B=2, Hq=8, Hkv=2, Nq=40, Ncur=40, Nc=500), "taylor", "long", 0, False, "f32",
                             16),
+    "fast_bf16": (H24.scaled(Hq=2, Hkv=2, Nq=200, Ncur=200, Nc=300), "taylor", "long", 0, False, "bf16", 0),
+    "fast_bf16_paged_causal": (GQA.scaled(B=2, Hq=8, Hkv=2, Nq=70, Ncur=70, Nc=320), "off", "long", 2, True, "bf16",
+                               64),
+    "short_bf16": (OUT.scaled(Hq=2, Hkv=2, Nq=24, Ncur=24, Nc=600), "taylor", "short", 0, False, "bf16", 0),
+    "short16_bf16_paged": (GQA.scaled(B=2, Hq=8, Hkv=2, Nq=2, Ncur=2, Nc=640), "taylor", "short", 0, False, "bf16",
+                           64),
+    "general_bf16": (H24.scaled(Hq=2, Hkv=2, Nq=64, Ncur=64, Nc=150, group=32), "exact", "long", 0, False, "bf16", 0),
 }
 
 
@@ -72,7 +79,8 @@ def _bytes_equal(a, b):
 
 def _check_rows(orc, c, src, bits, w, meta, label):
     """Rows [Nc, Nc + Ncur) of cache c against the oracle's quantizer of the chunk."""
-    codes, step, zero = (t.cpu().numpy() for t in c.logical(w.Nc + w.Ncur))
+    codes, step, zero = ((t.float() if t.dtype == torch.bfloat16 else t).cpu().numpy()
+                         for t in c.logical(w.Nc + w.Ncur))
     src = src if src.dtype == np.uint16 else W.bf16_bits(src)  # the call takes the chunk in bf16
     ref = orc.quantize(src, bits, w.group, meta=meta)
     assert np.array_equal(codes[:, :, w.Nc:], ref[0]), (label, "codes")

@@ -1,11 +1,12 @@
-"""Binary16 step and zero point (kv_meta KV_META_F16) on the GPU against the
-oracle run with the same storage type: kv_quantize's codes, steps and zero
-points bit-exact (the binary16 values read back as fp32 against the
-oracle's rounded fp32 values), and every attention path -- the throughput
-kernel (masked or not, split or not), the short-query kernel, the general
-kernel (exact correction, d = 64), the diagnostics -- within the output
-tolerance of the oracle over the rounded metadata, contiguous and paged.
-The paged results are also bit-identical to the contiguous ones."""
+"""16-bit steps and zero points (kv_meta KV_META_F16 binary16 and
+KV_META_BF16 bfloat16) on the GPU against the oracle run with the same
+storage type: kv_quantize's codes, steps and zero points bit-exact (the
+16-bit values read back as fp32 against the oracle's rounded fp32 values),
+and every attention path -- the throughput kernel (masked or not, split or
+not), the short-query kernels, the general kernel (exact correction,
+d = 64), the diagnostics -- within the output tolerance of the oracle over
+the rounded metadata, contiguous and paged.  The paged results are also
+bit-identical to the contiguous ones."""
 import numpy as np
 import pytest
 import torch
@@ -16,10 +17,13 @@ from bit_kv_cache_03_amd import workloads as W
 pytestmark = pytest.mark.gpu
 
 
+META = ["f16", "bf16"]
+
+
 def _meta_equal(got, ref):
-    """got: binary16 array read back from the GPU; ref: the oracle's fp32
-    array holding binary16 values."""
-    assert got.dtype == np.float16 and ref.dtype == np.float32
+    """got: 16-bit array read back from the GPU (binary16, or bfloat16 widened
+    to fp32); ref: the oracle's fp32 array holding 16-bit values."""
+    assert got.dtype in (np.float16, np.float32) and ref.dtype == np.float32
     return np.array_equal(got.astype(np.float32).view(np.uint32), ref.view(np.uint32))
 
 
@@ -29,17 +33,18 @@ def _check_cache(got, ref, label):
     assert _meta_equal(got[2], ref[2]), (label, "zero")
 
 
+@pytest.mark.parametrize("meta", META)
 @pytest.mark.parametrize("wname", sorted(W.WORKLOADS))
 @pytest.mark.parametrize("group", [32, 64, 128])
-def test_quantize_meta16_bit_exact(orc, wname, group):
+def test_quantize_meta16_bit_exact(orc, wname, group, meta):
     import _gpu
     w = W.WORKLOADS[wname]
     w = w.scaled(B=min(w.B, 2), Nc=333, Ncur=97, group=min(group, w.d))
     data = W.generate(w, parts=("kc", "vc"))
-    print(f"[quantize f16] {wname} group={w.group} B={w.B} Hkv={w.Hkv} Nc={w.Nc}", flush=True)
+    print(f"[quantize {meta}] {wname} group={w.group} B={w.B} Hkv={w.Hkv} Nc={w.Nc}", flush=True)
     for name, bits in (("kc", w.kbits), ("vc", w.vbits)):
-        gc = _gpu.build_cache(w, data[name], bits, cap=w.Nc + 5, meta="f16")
-        _check_cache(_gpu.cache_to_host(gc, w.Nc), orc.quantize(data[name], bits, w.group, meta="f16"), name)
+        gc = _gpu.build_cache(w, data[name], bits, cap=w.Nc + 5, meta=meta)
+        _check_cache(_gpu.cache_to_host(gc, w.Nc), orc.quantize(data[name], bits, w.group, meta=meta), name)
         assert torch.count_nonzero(gc.codes[:, :, w.Nc:]).item() == 0
         assert torch.count_nonzero(gc.scale[:, :, w.Nc:]).item() == 0
 
@@ -71,19 +76,48 @@ def _rows16(d):
     return np.stack(rows).astype(np.float32)
 
 
+def _rowsbf16(d):
+    """Groups whose step or zero point lands on the edges of bfloat16: exact
+    values, signed zeros, fp32- and bfloat16-subnormal steps, magnitudes
+    near the top of fp32's range, a zero point far larger than the step (its
+    rounding moves the grid by several steps), exact ties, and rounding of
+    ordinary values."""
+    rng = np.random.default_rng(6)
+    i = np.arange(d)
+    rows = [
+        np.full(d, 3.0),
+        np.where(i % 2 == 0, -1.0, 5.0),
+        np.where(i % 3 == 0, -0.0, 0.0),
+        np.concatenate([[-0.0], rng.uniform(0, 1, d - 1)]),
+        (i % 4) * 1e-45,                                  # fp32-subnormal steps
+        rng.uniform(0, 1, d) * 1e-39,                     # bfloat16-subnormal steps and zero points
+        np.linspace(-1e38, 1e38, d),
+        np.linspace(0.0, 3.3e38, d),                      # the step near fp32's largest values / 3
+        100.0 + np.linspace(0.0, 0.5, d),                 # |z| >> D
+        -7777.0 + rng.uniform(0, 1, d),
+        np.tile([0.0, 3.0, 0.5, 1.5, 2.5, 1.0], d)[:d],   # exact ties (INT2)
+        np.tile([0.0, 15.0, 0.5, 7.5, 8.5, 14.5], d)[:d],  # exact ties (INT4)
+        rng.standard_normal(d),
+        rng.standard_normal(d) * 1000.0 + 0.3,
+        rng.standard_normal(d) * 0.01 + 7.77,
+    ]
+    return np.stack(rows).astype(np.float32)
+
+
+@pytest.mark.parametrize("meta", META)
 @pytest.mark.parametrize("bits", [2, 4])
 @pytest.mark.parametrize("src", ["f32", "bf16"])
 @pytest.mark.parametrize("d,group", [(64, 64), (128, 32), (128, 64), (128, 128)])
-def test_quantize_meta16_edges(orc, bits, src, d, group):
+def test_quantize_meta16_edges(orc, bits, src, d, group, meta):
     import _gpu
-    x = _rows16(d)
+    x = _rows16(d) if meta == "f16" else _rowsbf16(d)
     if src == "bf16":
         x = W.bf16_bits(x)
     x4 = np.ascontiguousarray(x.reshape(1, 1, x.shape[0], d))
-    c = kvq.QCache(1, 1, x.shape[0], d, bits, group, meta="f16")
+    c = kvq.QCache(1, 1, x.shape[0], d, bits, group, meta=meta)
     kvq.quantize(_gpu.to_dev(x4), c, 0)
     torch.cuda.synchronize()
-    _check_cache(_gpu.cache_to_host(c, x.shape[0]), orc.quantize(x4, bits, group, meta="f16"), "edges")
+    _check_cache(_gpu.cache_to_host(c, x.shape[0]), orc.quantize(x4, bits, group, meta=meta), "edges")
 
 
 CASES = {
@@ -96,32 +130,46 @@ CASES = {
 }
 
 
+@pytest.mark.parametrize("meta", META)
 @pytest.mark.parametrize("case", sorted(CASES))
 @pytest.mark.parametrize("corr", ["off", "taylor", "exact"])
 @pytest.mark.parametrize("path", ["long", "short"])
-def test_attention_meta16_parity(orc, case, corr, path):
+def test_attention_meta16_parity(orc, case, corr, path, meta):
     from test_gpu_attention import _compare
-    _compare(orc, CASES[case], corr, path, meta="f16")
+    _compare(orc, CASES[case], corr, path, meta=meta)
 
 
+@pytest.mark.parametrize("meta", META)
 @pytest.mark.parametrize("path,splits", [("long", 0), ("long", 3), ("short", 0), ("short", 5)])
-def test_attention_meta16_causal(orc, path, splits):
+def test_attention_meta16_causal(orc, path, splits, meta):
     from test_gpu_attention import _compare
     w = W.WORKLOADS["gqa_prefill_b16_cache32k"].scaled(B=2, Hq=8, Hkv=2, Nq=40, Ncur=50, Nc=333)
-    _compare(orc, w, "taylor", path, splits=splits, causal=True, meta="f16")
+    _compare(orc, w, "taylor", path, splits=splits, causal=True, meta=meta)
 
 
+@pytest.mark.parametrize("meta", META)
+@pytest.mark.parametrize("nq", [1, 4])
+def test_attention_meta16_short16(orc, nq, meta):
+    """At most 16 query rows per KV head: the 16-row short kernel."""
+    from test_gpu_attention import _compare
+    w = W.WORKLOADS["gqa_prefill_b16_cache32k"].scaled(B=2, Hq=8, Hkv=2, Nq=nq, Ncur=nq, Nc=777)
+    for corr in ("off", "taylor"):
+        _compare(orc, w, corr, "short", meta=meta)
+
+
+@pytest.mark.parametrize("meta", META)
 @pytest.mark.parametrize("case", ["int4", "gqa", "tiny"])
 @pytest.mark.parametrize("corr", ["off", "taylor"])
-def test_diagnostics_meta16(orc, case, corr):
+def test_diagnostics_meta16(orc, case, corr, meta):
     from test_gpu_diagnostics import _compare
-    _compare(orc, CASES[case], case == "gqa", corr, meta="f16")
+    _compare(orc, CASES[case], case == "gqa", corr, meta=meta)
 
 
 PAGED = {
     "int4": (W.WORKLOADS["h24_int4_cache16k"].scaled(Hq=2, Hkv=2, Nq=200, Ncur=200, Nc=333), 64),
     "gqa": (W.WORKLOADS["gqa_prefill_b16_cache32k"].scaled(B=3, Hq=8, Hkv=2, Nq=50, Ncur=50, Nc=700), 128),
     "d64": (W.WORKLOADS["tiny_d64_int2"].scaled(B=2, Hq=4, Hkv=2, Nq=77, Ncur=40, Nc=300, group=32, kbits=4), 64),
+    "gqa_decode": (W.WORKLOADS["gqa_prefill_b16_cache32k"].scaled(B=3, Hq=8, Hkv=2, Nq=2, Ncur=2, Nc=700), 64),
 }
 
 
@@ -129,18 +177,19 @@ def _same(a, b):
     return torch.equal(a.contiguous().view(torch.int16), b.contiguous().view(torch.int16))
 
 
+@pytest.mark.parametrize("meta", META)
 @pytest.mark.parametrize("case", sorted(PAGED))
-def test_paged_meta16_matches_contiguous(case):
+def test_paged_meta16_matches_contiguous(case, meta):
     import _gpu
     w, ps = PAGED[case]
-    print(f"[paged f16] {case} page_size={ps} B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Ncur={w.Ncur} Nc={w.Nc}",
+    print(f"[paged {meta}] {case} page_size={ps} B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Ncur={w.Ncur} Nc={w.Nc}",
           flush=True)
     data = W.generate(w)
     cap = (w.Nc + ps - 1) // ps * ps
-    kc = _gpu.build_cache(w, data["kc"], w.kbits, cap=cap, meta="f16")
-    vc = _gpu.build_cache(w, data["vc"], w.vbits, cap=cap, meta="f16")
-    pk = _gpu.paged_cache(w, data["kc"], w.kbits, ps, cap=cap, seed=2, meta="f16")
-    pv = _gpu.paged_cache(w, data["vc"], w.vbits, ps, cap=cap, seed=2, meta="f16")
+    kc = _gpu.build_cache(w, data["kc"], w.kbits, cap=cap, meta=meta)
+    vc = _gpu.build_cache(w, data["vc"], w.vbits, cap=cap, meta=meta)
+    pk = _gpu.paged_cache(w, data["kc"], w.kbits, ps, cap=cap, seed=2, meta=meta)
+    pv = _gpu.paged_cache(w, data["vc"], w.vbits, ps, cap=cap, seed=2, meta=meta)
     pv.page_table = pk.page_table
     torch.cuda.synchronize()
     for c, p in ((kc, pk), (vc, pv)):
@@ -158,17 +207,18 @@ def test_paged_meta16_matches_contiguous(case):
     assert np.array_equal(ra[0], rb[0]) and np.array_equal(ra[1], rb[1])
 
 
-def test_meta16_halves_metadata_and_differs_from_f32(orc):
-    """The binary16 cache holds half the metadata bytes, and its attention
+@pytest.mark.parametrize("meta", META)
+def test_meta16_halves_metadata_and_differs_from_f32(orc, meta):
+    """The 16-bit cache holds half the metadata bytes, and its attention
     output is that of the rounded grid, not of the fp32 one (the two differ)."""
     import _gpu
     w = CASES["int4"]
     data = W.generate(w)
     k32 = _gpu.build_cache(w, data["kc"], w.kbits)
-    k16 = _gpu.build_cache(w, data["kc"], w.kbits, meta="f16")
+    k16 = _gpu.build_cache(w, data["kc"], w.kbits, meta=meta)
     assert k16.scale.numel() * k16.scale.element_size() * 2 == k32.scale.numel() * k32.scale.element_size()
     v32 = _gpu.build_cache(w, data["vc"], w.vbits)
-    v16 = _gpu.build_cache(w, data["vc"], w.vbits, meta="f16")
+    v16 = _gpu.build_cache(w, data["vc"], w.vbits, meta=meta)
     a = _gpu.out_rows(_gpu.run_attention(w, data, k32, v32, path="long"))
     b = _gpu.out_rows(_gpu.run_attention(w, data, k16, v16, path="long"))
     assert not np.array_equal(a, b)

@@ -1,6 +1,6 @@
 """Seeded random configurations against the oracle: every option of the
 attention call drawn together (shape, GQA ratio, bits, group, correction
-mode, path, key-range splits, causal mask, paged layout, binary16 metadata,
+mode, path, key-range splits, causal mask, paged layout, 16-bit metadata,
 groups along the tokens), at sizes the oracle finishes in well under a
 second.  The list is fixed by its seed; each case prints its options before
 it runs."""
@@ -43,7 +43,8 @@ def _cases(n=600, seed=20261203):
         paged = bool(rng.random() < 0.3) and nc > 0
         # pages of 16..128 tokens (token groups need whole groups per page)
         ps = max(int(rng.choice([16, 32, 64, 128])), group if "tokens" in (axis_k, axis_v) else 16) if paged else 0
-        meta = "f16" if rng.random() < 0.3 else "f32"
+        r = rng.random()  # one draw, as before bfloat16 took half of the 16-bit share
+        meta = "f16" if r < 0.15 else "bf16" if r < 0.3 else "f32"
         w = base.scaled(B=int(rng.choice([1, 2])), Hq=hkv * gq, Hkv=hkv, Nq=nq, Ncur=ncur, Nc=nc, group=group,
                         kbits=int(rng.choice([2, 4])), vbits=int(rng.choice([2, 4])))
         out.append((i, w, corr, path, splits, causal, ps, meta, axis_k, axis_v))

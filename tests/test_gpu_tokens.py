@@ -2,7 +2,7 @@
 consecutive tokens shares a step and a zero point) on the GPU against the
 oracle run with the same grouping: kv_quantize's codes, steps and zero
 points bit-exact (appended in chunks of whole groups, a shorter last group,
-fp32 or binary16 metadata, contiguous or paged), and the attention within
+fp32, binary16 or bfloat16 metadata, contiguous or paged), and the attention within
 the output tolerance on the long and short paths, with every correction
 mode, the causal mask, d = 64 and 128, K or V or both grouped this way, and
 the attention-balance diagnostics over such a K cache.  The paged results
@@ -36,7 +36,7 @@ QCASES = {
 
 @pytest.mark.parametrize("case", sorted(QCASES))
 @pytest.mark.parametrize("group", [32, 64, 128])
-@pytest.mark.parametrize("meta", ["f32", "f16"])
+@pytest.mark.parametrize("meta", ["f32", "f16", "bf16"])
 def test_quantize_tokens_bit_exact(orc, case, group, meta):
     import _gpu
     w, nc = QCASES[case]
