@@ -775,7 +775,11 @@ hipError_t launch_attention_long(const AttnLaunch &p, hipStream_t stream) {
 }
 
 hipError_t launch_attention_short(const AttnLaunch &p, hipStream_t stream) {
-  if (p.ktok || p.vtok) return launch_attention_tokens(p, stream, true);
+  if (p.ktok || p.vtok) {
+    if (short16_ktok_supported(p.d, p.corr, p.ktok, p.vtok, layout_page_size(p.layout), p.Nq * (p.Hq / p.Hkv)))
+      return launch_attention_short16_tok(p, stream);
+    return launch_attention_tokens(p, stream, true);
+  }
   if (short_fast_supported(p.d, p.corr, false, layout_page_size(p.layout))) return launch_attention_short_fast(p, stream);
   return p.d == 64 ? launch_d<64, true>(p, stream) : launch_d<128, true>(p, stream);
 }

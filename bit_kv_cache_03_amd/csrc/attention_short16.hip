@@ -24,6 +24,18 @@
 //  V (dequantisation): keys 4kq .. 4kq+3 (kq = lane % 8), dims 16dq .. 16dq+15
 //    (dq = lane / 8), written transposed into the V^T tile;
 //  O^T (16 x 16 per head-dim tile dt): query r, dims 16dt + 4j + i.
+//
+// Keys grouped along the tokens (KVQ_SHORT16_KTOK: one step D_c and zero
+// point z_c per channel c and token group, the page's per-channel reading of
+// D_{i,c}; values along the head dimension): a 32-key block lies in one token
+// group, so D folds into the query instead of the keys.  Per group a lane
+// forms q'_c = q_c D_c 2^-ed for its 32 dims (fp16, in the order of the code
+// words below) and one per-row term, q.z - (tau/24) sum_c q_c^2 D_c^2 (the
+// Taylor bias of "量化鍵值偷走注意力…" (agents-report.net) §方法 with per-channel
+// steps); the key operand is then the raw codes themselves, each in the low
+// bits of its 16-bit field, i.e. the fp16 subnormal c 2^-24 (exact: the MFMA
+// takes subnormal inputs as they are).  Each wave walks a contiguous range of
+// blocks so that consecutive blocks share their group's query terms.
 #include <math.h>
 
 #include "kvq_device.h"
@@ -36,6 +48,9 @@
 #endif
 #ifndef KVQ_SHORT16_META16
 #define KVQ_SHORT16_META16 0
+#endif
+#ifndef KVQ_SHORT16_KTOK
+#define KVQ_SHORT16_KTOK 0
 #endif
 
 namespace kvq {
@@ -54,6 +69,7 @@ constexpr int VT = D * VS;           // 16-bit elements of a wave's V^T tile
 constexpr int OS = D + 4;            // fp32 row of the merge buffer
 constexpr int MERGE = ROWS * OS + 2 * ROWS;  // floats of a wave's merge buffer (O rows, then m and l)
 constexpr int LDS_BYTES = WAVES * VT * 2 > WAVES * MERGE * 4 ? WAVES * VT * 2 : WAVES * MERGE * 4;
+constexpr int GM = 2 * D;  // floats of a wave's token-group staging (steps, then zero points)
 
 // V^T element (row = head-dim index, col = key slot 0..31); the 16-byte
 // chunks of a row are XOR-swizzled by (row / 16) % 4 so that the transposed
@@ -74,6 +90,7 @@ struct Fetch {
   uint32_t vw[4];     // V codes of keys 4kq+i at d in [16dq, 16dq+16): INT4 words
   uint32_t vw2[4];    //   d 16dq..+7 in vw, +8..+15 in vw2; INT2 all 16 in vw
   float vstep[4], vzero[4];
+  uint32_t gd[2], gz[2];  // keys along the tokens: two steps / zero points of the block's token group, as stored
 };
 
 // Byte offsets of the lane's data from the block's first cache row; NG is
@@ -96,8 +113,9 @@ __device__ inline Lanes lane_offsets(int lane) {
 // Loads one cached block (rows [k0, k0 + 32)); rows at or past the segment
 // end read as zero (their scores are masked).  Paged: the buffer range stops
 // at the block's end, inside its page.
-template <int KBITS, int VBITS, int NG, bool PAGED, int MT>
-__device__ inline void fetch_cached(const Ctx &c, int k0, const Lanes &o, Fetch &f, size_t pool_row = 0) {
+template <int KBITS, int VBITS, int NG, bool PAGED, int MT, bool KTOK = false>
+__device__ inline void fetch_cached(const Ctx &c, int k0, const Lanes &o, Fetch &f, size_t pool_row = 0,
+                                    int gshift = 0, bool newg = false) {
   constexpr uint32_t KROW = D * KBITS / 8, VROW = D * VBITS / 8, ES = MT ? 2 : 4;
   const uint32_t rows = static_cast<uint32_t>(PAGED ? min(c.nc - k0, BK) : c.nc - k0);
   const size_t r0 = PAGED ? pool_row : block_row<false>(c, k0);  // paged: looked up a block earlier
@@ -113,12 +131,30 @@ __device__ inline void fetch_cached(const Ctx &c, int k0, const Lanes &o, Fetch 
         f.kw[t][0] = a.x; f.kw[t][1] = a.y;
       }
     }
-    const Buf ks = buffer_at(meta_adv<MT>(c.kc_scale, r0 * NG), rows * NG * ES);
-    const Buf kz = buffer_at(meta_adv<MT>(c.kc_zero, r0 * NG), rows * NG * ES);
+    if (KTOK) {
+      // the token group's D row of steps and of zero points (at metadata row
+      // r0 >> gshift): two of each per lane, when the block starts a group
+      if (newg) {
+        const size_t mrow = r0 >> gshift;
+        const Buf ks = buffer_at(meta_adv<MT>(c.kc_scale, mrow * D), D * ES);
+        const Buf kz = buffer_at(meta_adv<MT>(c.kc_zero, mrow * D), D * ES);
+        const uint32_t off = static_cast<uint32_t>(__lane_id()) * 2 * ES;
+        if (MT == kMetaF32) {
+          const u32x2 a = ld64(ks, off), b = ld64(kz, off);
+          f.gd[0] = a.x; f.gd[1] = a.y; f.gz[0] = b.x; f.gz[1] = b.y;
+        } else {
+          f.gd[0] = ld32(ks, off);
+          f.gz[0] = ld32(kz, off);
+        }
+      }
+    } else {
+      const Buf ks = buffer_at(meta_adv<MT>(c.kc_scale, r0 * NG), rows * NG * ES);
+      const Buf kz = buffer_at(meta_adv<MT>(c.kc_zero, r0 * NG), rows * NG * ES);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      f.kstep[t] = ld_meta1<MT>(ks, o.km + t * 16 * NG * ES);
-      f.kzero[t] = ld_meta1<MT>(kz, o.km + t * 16 * NG * ES);
+      for (int t = 0; t < 2; ++t) {
+        f.kstep[t] = ld_meta1<MT>(ks, o.km + t * 16 * NG * ES);
+        f.kzero[t] = ld_meta1<MT>(kz, o.km + t * 16 * NG * ES);
+      }
     }
   }
   {
@@ -205,6 +241,100 @@ __device__ inline void unpack_k_cached(const Ctx &c, int lane, const Fetch &f, f
     if (!owner) x = make_uint4(0u, 0u, 0u, 0u);
     kext[t] = __builtin_bit_cast(bf16x8, x);
   }
+}
+
+// K operands of a cached block whose keys group along the tokens: the codes
+// of key 16t + r at dims 32j + 8s .. +7, each in the low bits of a 16-bit
+// field (the fp16 subnormal c 2^-24), word e holding dims e and e + 4 (the
+// query side takes the same order).
+template <int KBITS>
+__device__ inline void unpack_k_codes(const Ctx &c, const Fetch &f, f16x8 (&k)[2][4]) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t w = KBITS == 4 ? f.kw[t][s] : (f.kw[t][s >> 1] >> (16 * (s & 1)));
+      // INT2: code e + 4 of the 16-bit chunk moves next to code e, 16 bits up
+      const uint32_t x = KBITS == 4 ? w : (w & 0xffffu) | ((w & 0xffffu) << 8);
+      uint32_t m[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m[e] = (x >> (KBITS * e)) & c.kmask;
+      k[t][s] = __builtin_bit_cast(f16x8, make_uint4(m[0], m[1], m[2], m[3]));
+    }
+}
+
+// Two stored steps or zero points of a token group (one 32-bit word each in
+// fp32, both in one word with 16 bits) as fp32.
+template <int MT>
+__device__ inline void meta_pair(const uint32_t (&w)[2], float (&v)[2]) {
+  if (MT == kMetaF32) {
+    v[0] = __uint_as_float(w[0]);
+    v[1] = __uint_as_float(w[1]);
+  } else {
+    v[0] = meta16_value(static_cast<uint16_t>(w[0]), MT);
+    v[1] = meta16_value(static_cast<uint16_t>(w[0] >> 16), MT);
+  }
+}
+
+// Query terms of a token group (keys along the tokens), from the group's
+// steps D_c and zero points z_c in f (staged through the wave's LDS area Gm):
+// qk[s] word e = fp16(q_c D_c 2^-ed) of dims c = 32j + 8s + e and + 4, with
+// 2^ed above the group's largest step; the scores of the codes then read
+// sum_c q'_c c_c 2^-24 (units of 2^-(eq + ed + 24)), so the block's softmax
+// scale is alpha_g = alpha_q 2^(ed + 24) and the row adds
+// sadd = q.z - (tau/24) sum_c q_c^2 D_c^2 in those units (q.z over the
+// unscaled z; the bias from the rounded q').
+// qun = 2^eq undoes the query's scaling (q holds q 2^-eq).
+template <bool TAYLOR, int MT>
+__device__ inline void ktok_group(const Fetch &f, int lane, float *Gm, const f16x8 (&q)[4], float tau, float alpha_q,
+                                  float qun, f16x8 (&qk)[4], float &sadd, float &alpha_g) {
+  float dv[2], zv[2];
+  meta_pair<MT>(f.gd, dv);
+  meta_pair<MT>(f.gz, zv);
+  *reinterpret_cast<float2 *>(Gm + 2 * lane) = make_float2(dv[0], dv[1]);
+  *reinterpret_cast<float2 *>(Gm + D + 2 * lane) = make_float2(zv[0], zv[1]);
+  const float dmax = wave_max(fmaxf(dv[0], dv[1]));
+  const int ed = dmax > 0.f ? ilog2_pos(dmax) + 1 : 0;
+  const float ds = ldexpf(1.0f, -ed);
+  const int j = lane >> 4;
+  float s2 = 0.f, sz = 0.f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const float *gd = Gm + 32 * j + 8 * s, *gz = Gm + D + 32 * j + 8 * s;
+    const float4 d0 = *reinterpret_cast<const float4 *>(gd), d1 = *reinterpret_cast<const float4 *>(gd + 4);
+    const float4 z0 = *reinterpret_cast<const float4 *>(gz), z1 = *reinterpret_cast<const float4 *>(gz + 4);
+    const float dd[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+    const float zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+    const uint4 qw = __builtin_bit_cast(uint4, q[s]);  // word e: dims 2e, 2e + 1
+    const uint32_t u[4] = {qw.x, qw.y, qw.z, qw.w};
+    float qv[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const f16x2 h = __builtin_bit_cast(f16x2, u[e]);
+      qv[2 * e] = static_cast<float>(h.x);
+      qv[2 * e + 1] = static_cast<float>(h.y);
+    }
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const _Float16 a = static_cast<_Float16>(qv[e] * (dd[e] * ds));
+      const _Float16 b = static_cast<_Float16>(qv[e + 4] * (dd[e + 4] * ds));
+      w[e] = pair_h(a, b);
+      s2 = fmaf(static_cast<float>(a), static_cast<float>(a), s2);
+      s2 = fmaf(static_cast<float>(b), static_cast<float>(b), s2);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sz = fmaf(qv[e], zz[e], sz);
+    qk[s] = __builtin_bit_cast(f16x8, make_uint4(w[0], w[1], w[2], w[3]));
+  }
+  s2 += __shfl_xor(s2, 16, 64);
+  sz += __shfl_xor(sz, 16, 64);
+  s2 += __shfl_xor(s2, 32, 64);
+  sz += __shfl_xor(sz, 32, 64);
+  // in units of q' c: q.z 2^-eq 2^-ed = sz ds; bias (tau/24) 2^(eq+ed) s2
+  const float bias = TAYLOR ? (tau / 24.0f) * qun * ldexpf(s2, ed) : 0.f;
+  sadd = ldexpf(sz * ds - bias, -24);
+  alpha_g = ldexpf(alpha_q, ed + 24);
 }
 
 // V^T tile of a cached block: fp16 values v 2^-ev of keys 4kq..4kq+3 (slots
@@ -336,10 +466,11 @@ __device__ inline void unpack_current(int lane, const Cur &x, float kscale, floa
 // log2(e) 2^eq for keys not yet scaled), and the extra step's slots 8j ..
 // 8j+7 on the first quarter of each group: N_g = tau/24 ||q_g||^2 2^-eq as
 // (hi, hi, lo, 0) split into bf16 (zero without the correction), then the
-// group sum S_g = sum_{c in g} q_c 2^-eq as (hi, lo, 0, 0) with centring.
+// group sum S_g = sum_{c in g} q_c 2^-eq as (hi, lo, 0, 0) with centring;
+// qun = 2^eq.
 template <bool TAYLOR, int NG>
 __device__ inline void load_query(const uint16_t *qptr, int lane, float tau, f16x8 (&q)[4], bf16x8 &qext,
-                                  float &alpha) {
+                                  float &alpha, float &qun) {
   const int j = lane >> 4;
   uint4 qw[4];
   float nsum = 0.f, qsum = 0.f, qmax = 0.f;
@@ -375,7 +506,8 @@ __device__ inline void load_query(const uint16_t *qptr, int lane, float tau, f16
     for (int e = 0; e < 4; ++e) w[e] = pack2h(lo_f(u[e]) * qs_scale, hi_f(u[e]) * qs_scale);
     q[s] = __builtin_bit_cast(f16x8, make_uint4(w[0], w[1], w[2], w[3]));
   }
-  alpha = tau * kLog2e * ldexpf(1.0f, eq);
+  qun = ldexpf(1.0f, eq);
+  alpha = tau * kLog2e * qun;
   const float n = TAYLOR ? nsum * (tau / 24.0f) * qs_scale : 0.f;
   const float nh = lo_f(pack2(n, 0.f)), nl = n - nh;
   const float t = qsum * qs_scale;
@@ -394,11 +526,11 @@ struct Soft {
 // wave's V^T tile, the block's score scale alpha (scores are q.k 2^-(eq+ek))
 // and value exponent ev.  count < BK marks a ragged block; CORR adds the
 // correction steps.  CAUSAL: count is the lane's own (possibly <= 0), and a
-// row may have seen no key yet (m = -inf).
-template <bool CORR, bool CAUSAL = false>
+// row may have seen no key yet (m = -inf).  ADD: the row's scores add sadd.
+template <bool CORR, bool CAUSAL = false, bool ADD = false>
 __device__ inline void block_compute(const f16x8 (&k)[2][4], const bf16x8 (&kext)[2], const uint16_t *Vt,
                                      const f16x8 (&q)[4], bf16x8 qext, int count, float alpha, int ev, int lane,
-                                     Soft &st) {
+                                     Soft &st, float sadd = 0.f) {
   const float fev = static_cast<float>(ev);
   const int r = lane & 15, j = lane >> 4;
   f32x4 s[2];
@@ -408,6 +540,7 @@ __device__ inline void block_compute(const f16x8 (&k)[2][4], const bf16x8 (&kext
 #pragma unroll
     for (int i = 0; i < 4; ++i) s[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k[t][i], q[i], s[t], 0, 0, 0);
     if (CORR) s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kext[t], qext, s[t], 0, 0, 0);
+    if (ADD) s[t] += sadd;
   }
   if (CAUSAL || count < BK) {
 #pragma unroll
@@ -449,10 +582,13 @@ __device__ inline void block_compute(const f16x8 (&k)[2][4], const bf16x8 (&kext
                                                       pk, st.o[dt], 0, 0, 0);
 }
 
-template <int KBITS, int VBITS, bool TAYLOR, int NG, bool CAUSAL, bool PAGED, int MT>
+// KTOK: keys grouped along the tokens (values along the head dimension; NG
+// then counts the values' groups per row and p.group is also the keys' token
+// group).
+template <int KBITS, int VBITS, bool TAYLOR, int NG, bool CAUSAL, bool PAGED, int MT, bool KTOK = false>
 __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, int64_t rows_per_kvhead,
                                                                   int32_t nsplit, float *ws) {
-  __shared__ __attribute__((aligned(16))) uint16_t L[LDS_BYTES / 2];
+  __shared__ __attribute__((aligned(16))) uint16_t L[(LDS_BYTES + (KTOK ? WAVES * GM * 4 : 0)) / 2];
 
   const int tid = threadIdx.x;
   if (blockIdx.x >= p.app.wg0) {  // the chunk append's workgroups
@@ -480,12 +616,14 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
   f16x8 q[4];
   bf16x8 qext;
   Soft st;
-  load_query<TAYLOR, NG>(p.q + qrow * D, lane, p.tau, q, qext, st.alpha);
+  float qun;
+  load_query<TAYLOR, NG>(p.q + qrow * D, lane, p.tau, q, qext, st.alpha, qun);
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.m = -INFINITY;
   st.l = 0.f;
 
+  const int gshift = KTOK ? __builtin_ctz(static_cast<unsigned>(p.group)) : 0;
   Ctx c{};
   c.nc = static_cast<int>(p.Nc);
   c.ncur = static_cast<int>(p.Ncur);
@@ -501,8 +639,9 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
     const int64_t hrow = PAGED ? 0 : bkv * p.cap;  // paged: the pointers stay at the pool
     c.kc_codes = p.kc_codes + hrow * (D * KBITS / 8);
     c.vc_codes = p.vc_codes + hrow * (D * VBITS / 8);
-    c.kc_scale = meta_adv<MT>(p.kc_scale, hrow * NG);
-    c.kc_zero = meta_adv<MT>(p.kc_zero, hrow * NG);
+    // keys along the tokens: one metadata row of D per token group
+    c.kc_scale = meta_adv<MT>(p.kc_scale, KTOK ? (hrow >> gshift) * D : hrow * NG);
+    c.kc_zero = meta_adv<MT>(p.kc_zero, KTOK ? (hrow >> gshift) * D : hrow * NG);
     c.vc_scale = meta_adv<MT>(p.vc_scale, hrow * NG);
     c.vc_zero = meta_adv<MT>(p.vc_zero, hrow * NG);
   }
@@ -528,9 +667,17 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
     if (bend > cb) bend = cb;
   }
   uint16_t *Vt = L + wave * VT;
+  float *Gm = reinterpret_cast<float *>(L + WAVES * VT) + wave * GM;
 
-  int blk = bbeg + wave;
-  const int cend = bend < nbc ? bend : nbc;
+  // blocks dealt round-robin, or (KTOK) in contiguous ranges per wave
+  int blk = bbeg + wave, wend = bend, bstep = WAVES;
+  if (KTOK) {
+    const int per = (bend - bbeg + WAVES - 1) / WAVES;
+    blk = bbeg + wave * per;
+    wend = blk + per < bend ? blk + per : bend;
+    bstep = 1;
+  }
+  const int cend = wend < nbc ? wend : nbc;
   const Lanes lo = lane_offsets<KBITS, VBITS, NG, MT>(lane);
   Scales sc;
   // with the caches' running bounds the exponents of the cached blocks are
@@ -541,21 +688,41 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
   f16x8 kreg[2][4];
   bf16x8 kext[2] = {};
   Fetch f;
-  if (blk < cend) fetch_cached<KBITS, VBITS, NG, PAGED, MT>(c, blk * BK, lo, f, block_row<PAGED>(c, blk * BK));
+  // keys along the tokens: the query terms of the wave's current token group
+  f16x8 qk[4];
+  float sadd = 0.f, alpha_g = 0.f;
+  int gcur = -1;
+  if (blk < cend)
+    fetch_cached<KBITS, VBITS, NG, PAGED, MT, KTOK>(c, blk * BK, lo, f, block_row<PAGED>(c, blk * BK), gshift, true);
   // paged: the pool row of the next block to fetch, looked up one block ahead
   // so that its scalar load has completed when the fetch needs it
-  size_t prn = PAGED && blk + WAVES < cend ? block_row<PAGED>(c, (blk + WAVES) * BK) : 0;
-  for (; blk < cend; blk += WAVES) {
+  size_t prn = PAGED && blk + bstep < cend ? block_row<PAGED>(c, (blk + bstep) * BK) : 0;
+  for (; blk < cend; blk += bstep) {
     const int k0 = blk * BK;
     const int count = c.nc - k0 < BK ? c.nc - k0 : BK;
-    if (!cache_bounds) sc.update(k_bound<KBITS, NG>(f), v_bound<VBITS>(f), st.alpha);
-    unpack_k_cached<TAYLOR, KBITS, NG>(c, lane, f, sc.kscale, kreg, kext);
+    if (KTOK) {
+      if (!cache_bounds) sc.update(0.f, v_bound<VBITS>(f), st.alpha);
+      if ((k0 >> gshift) != gcur) {
+        ktok_group<TAYLOR, MT>(f, lane, Gm, q, p.tau, st.alpha, qun, qk, sadd, alpha_g);
+        gcur = k0 >> gshift;
+      }
+      unpack_k_codes<KBITS>(c, f, kreg);
+    } else {
+      if (!cache_bounds) sc.update(k_bound<KBITS, NG>(f), v_bound<VBITS>(f), st.alpha);
+      unpack_k_cached<TAYLOR, KBITS, NG>(c, lane, f, sc.kscale, kreg, kext);
+    }
     unpack_v_cached<VBITS>(c, lane, f, sc.vscale, Vt);
-    if (blk + WAVES < cend) fetch_cached<KBITS, VBITS, NG, PAGED, MT>(c, (blk + WAVES) * BK, lo, f, prn);
-    block_compute<TAYLOR || kCentre<NG>>(kreg, kext, Vt, q, qext, count, sc.alpha, sc.ev, lane, st);
-    if (PAGED && blk + 2 * WAVES < cend) prn = block_row<PAGED>(c, (blk + 2 * WAVES) * BK);
+    if (blk + bstep < cend) {
+      const int kn = (blk + bstep) * BK;
+      fetch_cached<KBITS, VBITS, NG, PAGED, MT, KTOK>(c, kn, lo, f, prn, gshift, (kn >> gshift) != (k0 >> gshift));
+    }
+    if (KTOK)
+      block_compute<false, false, true>(kreg, kext, Vt, qk, qext, count, alpha_g, sc.ev, lane, st, sadd);
+    else
+      block_compute<TAYLOR || kCentre<NG>>(kreg, kext, Vt, q, qext, count, sc.alpha, sc.ev, lane, st);
+    if (PAGED && blk + 2 * bstep < cend) prn = block_row<PAGED>(c, (blk + 2 * bstep) * BK);
   }
-  for (; blk < bend; blk += WAVES) {
+  for (; blk < wend; blk += bstep) {
     const int k0 = (blk - nbc) * BK;
     int count = c.ncur - k0 < BK ? c.ncur - k0 : BK;
     if (CAUSAL) count = min(count, climit - k0);
@@ -625,12 +792,12 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
 
 template <int KB, int VB, int NG>
 void launch_kernel(const AttnLaunch &p, hipStream_t stream, dim3 grid, int64_t rows, float *partials) {
-  constexpr bool PG = KVQ_SHORT16_PAGED != 0;
+  constexpr bool PG = KVQ_SHORT16_PAGED != 0, KT = KVQ_SHORT16_KTOK != 0;
   constexpr int MH = KVQ_SHORT16_META16;
-  auto kernel = p.corr == KV_CORR_TAYLOR ? (p.causal ? attn_short16_kernel<KB, VB, true, NG, true, PG, MH>
-                                                     : attn_short16_kernel<KB, VB, true, NG, false, PG, MH>)
-                                         : (p.causal ? attn_short16_kernel<KB, VB, false, NG, true, PG, MH>
-                                                     : attn_short16_kernel<KB, VB, false, NG, false, PG, MH>);
+  auto kernel = p.corr == KV_CORR_TAYLOR ? (p.causal ? attn_short16_kernel<KB, VB, true, NG, true, PG, MH, KT>
+                                                     : attn_short16_kernel<KB, VB, true, NG, false, PG, MH, KT>)
+                                         : (p.causal ? attn_short16_kernel<KB, VB, false, NG, true, PG, MH, KT>
+                                                     : attn_short16_kernel<KB, VB, false, NG, false, PG, MH, KT>);
   kernel<<<grid, dim3(THREADS), 0, stream>>>(p, rows, p.splits, partials);
 }
 
@@ -659,7 +826,21 @@ hipError_t launch_bits(const AttnLaunch &p, hipStream_t stream) {
 
 }  // namespace
 
+#if KVQ_SHORT16_KTOK
 #if KVQ_SHORT16_PAGED && KVQ_SHORT16_META16 == 2
+hipError_t launch_attention_short16_ktok_mb16_paged(const AttnLaunch &p, hipStream_t stream) {
+#elif KVQ_SHORT16_PAGED && KVQ_SHORT16_META16
+hipError_t launch_attention_short16_ktok_m16_paged(const AttnLaunch &p, hipStream_t stream) {
+#elif KVQ_SHORT16_PAGED
+hipError_t launch_attention_short16_ktok_paged(const AttnLaunch &p, hipStream_t stream) {
+#elif KVQ_SHORT16_META16 == 2
+hipError_t launch_attention_short16_ktok_mb16(const AttnLaunch &p, hipStream_t stream) {
+#elif KVQ_SHORT16_META16
+hipError_t launch_attention_short16_ktok_m16(const AttnLaunch &p, hipStream_t stream) {
+#else
+hipError_t launch_attention_short16_ktok(const AttnLaunch &p, hipStream_t stream) {
+#endif
+#elif KVQ_SHORT16_PAGED && KVQ_SHORT16_META16 == 2
 hipError_t launch_attention_short16_mb16_paged(const AttnLaunch &p, hipStream_t stream) {
 #elif KVQ_SHORT16_META16 == 2
 hipError_t launch_attention_short16_mb16(const AttnLaunch &p, hipStream_t stream) {
@@ -678,5 +859,24 @@ hipError_t launch_attention_short16(const AttnLaunch &p, hipStream_t stream) {
   if (kb == 4 && vb == 2) return launch_bits<4, 2>(p, stream);
   return launch_bits<4, 4>(p, stream);
 }
+
+#if !KVQ_SHORT16_PAGED && !KVQ_SHORT16_META16 && !KVQ_SHORT16_KTOK
+// Keys grouped along the tokens, values along the head dimension: d = 128,
+// correction off or Taylor, at most 16 query rows per KV head, and (paged)
+// pages that hold whole 32-key blocks.
+bool short16_ktok_supported(int32_t d, int corr, bool ktok, bool vtok, int32_t page_size, int64_t rows_per_kvhead) {
+  return d == D && corr != KV_CORR_EXACT && ktok && !vtok && rows_per_kvhead <= ROWS &&
+         (page_size == 0 || page_size >= BK);
+}
+
+hipError_t launch_attention_short16_tok(const AttnLaunch &p, hipStream_t stream) {
+  const bool paged = p.layout.page_table != nullptr;
+  if (p.meta == kMetaBF16)
+    return paged ? launch_attention_short16_ktok_mb16_paged(p, stream) : launch_attention_short16_ktok_mb16(p, stream);
+  if (p.meta == kMetaF16)
+    return paged ? launch_attention_short16_ktok_m16_paged(p, stream) : launch_attention_short16_ktok_m16(p, stream);
+  return paged ? launch_attention_short16_ktok_paged(p, stream) : launch_attention_short16_ktok(p, stream);
+}
+#endif
 
 }  // namespace kvq

@@ -1,0 +1,6 @@
+// Instances of the 16-row short-query kernel over paged-cache K caches grouped
+// along the tokens, built in their own translation unit; the kernel itself is
+// in attention_short16.hip.
+#define KVQ_SHORT16_KTOK 1
+#define KVQ_SHORT16_PAGED 1
+#include "attention_short16.hip"

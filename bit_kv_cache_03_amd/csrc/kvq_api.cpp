@@ -111,10 +111,13 @@ int32_t cache_page_size(const kv_attn_args *a) {
   return a->Nc > 0 && a->k_cache->page_table ? a->k_cache->page_size : 0;
 }
 
-// Either cache of a call groups along the tokens (general kernel only).
-bool tokens_axis(const kv_attn_args *a) {
-  return a->Nc > 0 && (a->k_cache->axis == KV_AXIS_TOKENS || a->v_cache->axis == KV_AXIS_TOKENS);
-}
+// The K / V cache of a call (when it reads one) groups along the tokens.
+bool k_tokens(const kv_attn_args *a) { return a->Nc > 0 && a->k_cache->axis == KV_AXIS_TOKENS; }
+bool v_tokens(const kv_attn_args *a) { return a->Nc > 0 && a->v_cache->axis == KV_AXIS_TOKENS; }
+
+// Either cache of a call groups along the tokens (the general kernel, or on
+// the short path with K alone along the tokens the 16-row kernel).
+bool tokens_axis(const kv_attn_args *a) { return k_tokens(a) || v_tokens(a); }
 
 bool debug_log() {
   const char *e = getenv("KVQ_LOG");
@@ -323,7 +326,8 @@ Plan plan_attention(const kv_attn_args *a, bool query_device, size_t limit = SIZ
   pl.path = path;
   if (path == KV_PATH_SHORT) {
     const int cus = query_device ? device_cu_count() : 256;
-    const bool fast = kvq::short_fast_supported(a->d, a->corr, tokens_axis(a), cache_page_size(a));
+    const bool fast = kvq::short_fast_supported(a->d, a->corr, tokens_axis(a), cache_page_size(a)) ||
+                      kvq::short16_ktok_supported(a->d, a->corr, k_tokens(a), v_tokens(a), cache_page_size(a), rows);
     auto bytes = [&](int s) {
       return fast ? kvq::short_path_workspace_bytes(a->B, a->Hq, a->Nq, a->d, s)
                   : kvq::general_path_workspace_bytes(a->B, a->Hq, a->Hkv, a->Nq, a->d, s, true);
