@@ -776,7 +776,7 @@ hipError_t launch_attention_long(const AttnLaunch &p, hipStream_t stream) {
 
 hipError_t launch_attention_short(const AttnLaunch &p, hipStream_t stream) {
   if (p.ktok || p.vtok) {
-    if (short16_ktok_supported(p.d, p.corr, p.ktok, p.vtok, layout_page_size(p.layout), p.Nq * (p.Hq / p.Hkv)))
+    if (short16_tok_supported(p.d, p.corr, p.ktok, p.vtok, layout_page_size(p.layout), p.meta, p.Nq * (p.Hq / p.Hkv)))
       return launch_attention_short16_tok(p, stream);
     return launch_attention_tokens(p, stream, true);
   }

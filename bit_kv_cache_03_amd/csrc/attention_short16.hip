@@ -36,6 +36,10 @@
 // bits of its 16-bit field, i.e. the fp16 subnormal c 2^-24 (exact: the MFMA
 // takes subnormal inputs as they are).  Each wave walks a contiguous range of
 // blocks so that consecutive blocks share their group's query terms.
+//
+// Values grouped along the tokens (KVQ_SHORT16_VTOK, with keys either way):
+// the values are dequantised as above, with per-channel operands instead of
+// per-key ones, staged per token group in the wave's LDS area.
 #include <math.h>
 
 #include "kvq_device.h"
@@ -51,6 +55,9 @@
 #endif
 #ifndef KVQ_SHORT16_KTOK
 #define KVQ_SHORT16_KTOK 0
+#endif
+#ifndef KVQ_SHORT16_VTOK
+#define KVQ_SHORT16_VTOK 0
 #endif
 
 namespace kvq {
@@ -69,7 +76,7 @@ constexpr int VT = D * VS;           // 16-bit elements of a wave's V^T tile
 constexpr int OS = D + 4;            // fp32 row of the merge buffer
 constexpr int MERGE = ROWS * OS + 2 * ROWS;  // floats of a wave's merge buffer (O rows, then m and l)
 constexpr int LDS_BYTES = WAVES * VT * 2 > WAVES * MERGE * 4 ? WAVES * VT * 2 : WAVES * MERGE * 4;
-constexpr int GM = 2 * D;  // floats of a wave's token-group staging (steps, then zero points)
+constexpr int GM = 2 * D;  // floats of a wave's token-group staging of K or of V (two per channel)
 
 // V^T element (row = head-dim index, col = key slot 0..31); the 16-byte
 // chunks of a row are XOR-swizzled by (row / 16) % 4 so that the transposed
@@ -91,6 +98,7 @@ struct Fetch {
   uint32_t vw2[4];    //   d 16dq..+7 in vw, +8..+15 in vw2; INT2 all 16 in vw
   float vstep[4], vzero[4];
   uint32_t gd[2], gz[2];  // keys along the tokens: two steps / zero points of the block's token group, as stored
+  uint32_t vgd[2], vgz[2];  // values along the tokens: the same for V
 };
 
 // Byte offsets of the lane's data from the block's first cache row; NG is
@@ -113,7 +121,7 @@ __device__ inline Lanes lane_offsets(int lane) {
 // Loads one cached block (rows [k0, k0 + 32)); rows at or past the segment
 // end read as zero (their scores are masked).  Paged: the buffer range stops
 // at the block's end, inside its page.
-template <int KBITS, int VBITS, int NG, bool PAGED, int MT, bool KTOK = false>
+template <int KBITS, int VBITS, int NG, bool PAGED, int MT, bool KTOK = false, bool VTOK = false>
 __device__ inline void fetch_cached(const Ctx &c, int k0, const Lanes &o, Fetch &f, size_t pool_row = 0,
                                     int gshift = 0, bool newg = false) {
   constexpr uint32_t KROW = D * KBITS / 8, VROW = D * VBITS / 8, ES = MT ? 2 : 4;
@@ -159,8 +167,6 @@ __device__ inline void fetch_cached(const Ctx &c, int k0, const Lanes &o, Fetch 
   }
   {
     const Buf vc = buffer_at(c.vc_codes + r0 * VROW, rows * VROW);
-    const Buf vs = buffer_at(meta_adv<MT>(c.vc_scale, r0 * NG), rows * NG * ES);
-    const Buf vz = buffer_at(meta_adv<MT>(c.vc_zero, r0 * NG), rows * NG * ES);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (VBITS == 4) {
@@ -170,8 +176,29 @@ __device__ inline void fetch_cached(const Ctx &c, int k0, const Lanes &o, Fetch 
       } else {
         f.vw[i] = ld32(vc, o.vc + i * VROW);
       }
-      f.vstep[i] = ld_meta1<MT>(vs, o.vm + i * NG * ES);
-      f.vzero[i] = ld_meta1<MT>(vz, o.vm + i * NG * ES);
+    }
+    if (VTOK) {
+      if (newg) {  // as for the keys: the token group's rows of steps and zero points
+        const size_t mrow = r0 >> gshift;
+        const Buf vs = buffer_at(meta_adv<MT>(c.vc_scale, mrow * D), D * ES);
+        const Buf vz = buffer_at(meta_adv<MT>(c.vc_zero, mrow * D), D * ES);
+        const uint32_t off = static_cast<uint32_t>(__lane_id()) * 2 * ES;
+        if (MT == kMetaF32) {
+          const u32x2 a = ld64(vs, off), b = ld64(vz, off);
+          f.vgd[0] = a.x; f.vgd[1] = a.y; f.vgz[0] = b.x; f.vgz[1] = b.y;
+        } else {
+          f.vgd[0] = ld32(vs, off);
+          f.vgz[0] = ld32(vz, off);
+        }
+      }
+    } else {
+      const Buf vs = buffer_at(meta_adv<MT>(c.vc_scale, r0 * NG), rows * NG * ES);
+      const Buf vz = buffer_at(meta_adv<MT>(c.vc_zero, r0 * NG), rows * NG * ES);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f.vstep[i] = ld_meta1<MT>(vs, o.vm + i * NG * ES);
+        f.vzero[i] = ld_meta1<MT>(vz, o.vm + i * NG * ES);
+      }
     }
   }
 }
@@ -337,6 +364,37 @@ __device__ inline void ktok_group(const Fetch &f, int lane, float *Gm, const f16
   alpha_g = ldexpf(alpha_q, ed + 24);
 }
 
+// Values along the tokens: the largest |v| the lane's two channels of the
+// block's token group can dequantise to.
+template <int VBITS, int MT>
+__device__ inline float vtok_bound(const Fetch &f) {
+  float dv[2], zv[2];
+  meta_pair<MT>(f.vgd, dv);
+  meta_pair<MT>(f.vgz, zv);
+  float b = 0.f;
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+    b = fmaxf(b, fmaxf(fabsf(zv[e]), fabsf(fmaf(dv[e], static_cast<float>((1 << VBITS) - 1), zv[e]))));
+  return b;
+}
+
+// Stages a token group's value operands in the wave's LDS area Gv: for
+// channel c, d_c = D_c vsc 2^-p and z_c = (z_c vsc) - 1024 d_c, p the
+// position of its code field in the byte pair the dequantisation reads (0
+// for even channels, 4 (INT4) or 2 (INT2) for odd ones); the lane writes
+// channels 2 lane and 2 lane + 1.
+template <int VBITS, int MT>
+__device__ inline void vtok_stage(const Fetch &f, int lane, float vsc, float *Gv) {
+  constexpr int P1 = VBITS == 4 ? 4 : 2;
+  float dv[2], zv[2];
+  meta_pair<MT>(f.vgd, dv);
+  meta_pair<MT>(f.vgz, zv);
+  const float d0 = dv[0] * vsc, d1 = dv[1] * vsc * (1.0f / (1 << P1));
+  *reinterpret_cast<float2 *>(Gv + 2 * lane) = make_float2(d0, d1);
+  *reinterpret_cast<float2 *>(Gv + D + 2 * lane) =
+      make_float2(fmaf(-1024.0f, d0, zv[0] * vsc), fmaf(-1024.0f, d1, zv[1] * vsc));
+}
+
 // V^T tile of a cached block: fp16 values v 2^-ev of keys 4kq..4kq+3 (slots
 // vslot4(kq) .. +3) at head-dim rows 16dq .. 16dq+15, one 8-byte store per
 // row.  One v_perm gathers the same code byte of two keys (bits 0..7 and
@@ -387,6 +445,54 @@ __device__ inline void unpack_v_cached(const Ctx &c, int lane, const Fetch &f, f
       if (VBITS == 2) {
         field(r[jp] >> 4, 0, x[NF - 2], jp);
         field(r[jp] >> 4, 1, x[NF - 1], jp);
+      }
+    }
+#pragma unroll
+    for (int fl = 0; fl < NF; ++fl)
+      *reinterpret_cast<uint2 *>(Vt + vts(16 * dq + NF * byte + fl, slot)) = make_uint2(x[fl][0], x[fl][1]);
+  }
+}
+
+// The same with values along the tokens: the operands of channel c =
+// 16dq + NF byte + fl (fl: the field within the byte) come from the staged
+// token group, the same for the four keys.
+template <int VBITS>
+__device__ inline void unpack_v_tok(const Ctx &c, int lane, const Fetch &f, const float *Gv, uint16_t *Vt) {
+  constexpr int NF = 8 / VBITS;
+  const int kq = lane & 7, dq = lane >> 3;
+  const int slot = vslot4(kq);
+  float dc[16], zc[16];
+#pragma unroll
+  for (int e = 0; e < 16; e += 4) {
+    const float4 a = *reinterpret_cast<const float4 *>(Gv + 16 * dq + e);
+    const float4 b = *reinterpret_cast<const float4 *>(Gv + D + 16 * dq + e);
+    dc[e] = a.x; dc[e + 1] = a.y; dc[e + 2] = a.z; dc[e + 3] = a.w;
+    zc[e] = b.x; zc[e + 1] = b.y; zc[e + 2] = b.z; zc[e + 3] = b.w;
+  }
+  auto field = [&](uint32_t r, int k, int e) {  // both keys of r at channel e, field k (0: p = 0, 1: p = P1)
+    const uint32_t m = (r & (k ? c.vmask1 : c.vmask0)) | 0x64006400u;
+    const f16x2 h = __builtin_bit_cast(f16x2, m);
+    return pair_h(dequant_h(static_cast<float>(h.x), dc[e], zc[e]), dequant_h(static_cast<float>(h.y), dc[e], zc[e]));
+  };
+#pragma unroll
+  for (int byte = 0; byte < (VBITS == 4 ? 8 : 4); ++byte) {
+    const int bw = byte & 3;
+    const uint32_t sel = static_cast<uint32_t>(bw) | 0x0c00u | (static_cast<uint32_t>(4 + bw) << 16) | 0x0c000000u;
+    uint32_t r[2];
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) {
+      const uint32_t w0 = byte >= 4 ? f.vw2[2 * jp] : f.vw[2 * jp];
+      const uint32_t w1 = byte >= 4 ? f.vw2[2 * jp + 1] : f.vw[2 * jp + 1];
+      r[jp] = __builtin_amdgcn_perm(w1, w0, sel);
+    }
+    uint32_t x[NF][2];
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) {
+      x[0][jp] = field(r[jp], 0, NF * byte);
+      x[1][jp] = field(r[jp], 1, NF * byte + 1);
+      if (VBITS == 2) {
+        x[NF - 2][jp] = field(r[jp] >> 4, 0, NF * byte + 2);
+        x[NF - 1][jp] = field(r[jp] >> 4, 1, NF * byte + 3);
       }
     }
 #pragma unroll
@@ -582,13 +688,15 @@ __device__ inline void block_compute(const f16x8 (&k)[2][4], const bf16x8 (&kext
                                                       pk, st.o[dt], 0, 0, 0);
 }
 
-// KTOK: keys grouped along the tokens (values along the head dimension; NG
-// then counts the values' groups per row and p.group is also the keys' token
-// group).
-template <int KBITS, int VBITS, bool TAYLOR, int NG, bool CAUSAL, bool PAGED, int MT, bool KTOK = false>
+// KTOK / VTOK: keys / values grouped along the tokens (p.group is then also
+// their token group; NG counts the groups per row of a cache grouped along
+// the head dimension).
+template <int KBITS, int VBITS, bool TAYLOR, int NG, bool CAUSAL, bool PAGED, int MT, bool KTOK = false,
+          bool VTOK = false>
 __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, int64_t rows_per_kvhead,
                                                                   int32_t nsplit, float *ws) {
-  __shared__ __attribute__((aligned(16))) uint16_t L[(LDS_BYTES + (KTOK ? WAVES * GM * 4 : 0)) / 2];
+  constexpr bool TOK = KTOK || VTOK;
+  __shared__ __attribute__((aligned(16))) uint16_t L[(LDS_BYTES + (TOK ? WAVES * 2 * GM * 4 : 0)) / 2];
 
   const int tid = threadIdx.x;
   if (blockIdx.x >= p.app.wg0) {  // the chunk append's workgroups
@@ -623,7 +731,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
   st.m = -INFINITY;
   st.l = 0.f;
 
-  const int gshift = KTOK ? __builtin_ctz(static_cast<unsigned>(p.group)) : 0;
+  const int gshift = TOK ? __builtin_ctz(static_cast<unsigned>(p.group)) : 0;
   Ctx c{};
   c.nc = static_cast<int>(p.Nc);
   c.ncur = static_cast<int>(p.Ncur);
@@ -642,8 +750,8 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
     // keys along the tokens: one metadata row of D per token group
     c.kc_scale = meta_adv<MT>(p.kc_scale, KTOK ? (hrow >> gshift) * D : hrow * NG);
     c.kc_zero = meta_adv<MT>(p.kc_zero, KTOK ? (hrow >> gshift) * D : hrow * NG);
-    c.vc_scale = meta_adv<MT>(p.vc_scale, hrow * NG);
-    c.vc_zero = meta_adv<MT>(p.vc_zero, hrow * NG);
+    c.vc_scale = meta_adv<MT>(p.vc_scale, VTOK ? (hrow >> gshift) * D : hrow * NG);
+    c.vc_zero = meta_adv<MT>(p.vc_zero, VTOK ? (hrow >> gshift) * D : hrow * NG);
   }
   if (p.Ncur > 0) {
     c.k_cur = p.k_cur + bkv * p.Ncur * D;
@@ -667,11 +775,13 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
     if (bend > cb) bend = cb;
   }
   uint16_t *Vt = L + wave * VT;
-  float *Gm = reinterpret_cast<float *>(L + WAVES * VT) + wave * GM;
+  float *Gm = reinterpret_cast<float *>(L + WAVES * VT) + wave * 2 * GM;  // token-group staging of K
+  float *Gv = Gm + GM;                                                     // and of V
 
-  // blocks dealt round-robin, or (KTOK) in contiguous ranges per wave
+  // blocks dealt round-robin, or (groups along the tokens) in contiguous
+  // ranges per wave
   int blk = bbeg + wave, wend = bend, bstep = WAVES;
-  if (KTOK) {
+  if (TOK) {
     const int per = (bend - bbeg + WAVES - 1) / WAVES;
     blk = bbeg + wave * per;
     wend = blk + per < bend ? blk + per : bend;
@@ -693,28 +803,36 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
   float sadd = 0.f, alpha_g = 0.f;
   int gcur = -1;
   if (blk < cend)
-    fetch_cached<KBITS, VBITS, NG, PAGED, MT, KTOK>(c, blk * BK, lo, f, block_row<PAGED>(c, blk * BK), gshift, true);
+    fetch_cached<KBITS, VBITS, NG, PAGED, MT, KTOK, VTOK>(c, blk * BK, lo, f, block_row<PAGED>(c, blk * BK), gshift,
+                                                          true);
   // paged: the pool row of the next block to fetch, looked up one block ahead
   // so that its scalar load has completed when the fetch needs it
   size_t prn = PAGED && blk + bstep < cend ? block_row<PAGED>(c, (blk + bstep) * BK) : 0;
   for (; blk < cend; blk += bstep) {
     const int k0 = blk * BK;
     const int count = c.nc - k0 < BK ? c.nc - k0 : BK;
+    const bool newg = TOK && (k0 >> gshift) != gcur;  // the block starts the wave's next token group
+    // values along the tokens: their bound per token group, checked when one starts
+    const float vb = VTOK ? (newg ? vtok_bound<VBITS, MT>(f) : 0.f) : v_bound<VBITS>(f);
     if (KTOK) {
-      if (!cache_bounds) sc.update(0.f, v_bound<VBITS>(f), st.alpha);
-      if ((k0 >> gshift) != gcur) {
-        ktok_group<TAYLOR, MT>(f, lane, Gm, q, p.tau, st.alpha, qun, qk, sadd, alpha_g);
-        gcur = k0 >> gshift;
-      }
+      if (!cache_bounds) sc.update(0.f, vb, st.alpha);
+      if (newg) ktok_group<TAYLOR, MT>(f, lane, Gm, q, p.tau, st.alpha, qun, qk, sadd, alpha_g);
       unpack_k_codes<KBITS>(c, f, kreg);
     } else {
-      if (!cache_bounds) sc.update(k_bound<KBITS, NG>(f), v_bound<VBITS>(f), st.alpha);
+      if (!cache_bounds) sc.update(k_bound<KBITS, NG>(f), vb, st.alpha);
       unpack_k_cached<TAYLOR, KBITS, NG>(c, lane, f, sc.kscale, kreg, kext);
     }
-    unpack_v_cached<VBITS>(c, lane, f, sc.vscale, Vt);
+    if (VTOK) {
+      if (newg) vtok_stage<VBITS, MT>(f, lane, sc.vscale, Gv);
+      unpack_v_tok<VBITS>(c, lane, f, Gv, Vt);
+    } else {
+      unpack_v_cached<VBITS>(c, lane, f, sc.vscale, Vt);
+    }
+    if (newg) gcur = k0 >> gshift;
     if (blk + bstep < cend) {
       const int kn = (blk + bstep) * BK;
-      fetch_cached<KBITS, VBITS, NG, PAGED, MT, KTOK>(c, kn, lo, f, prn, gshift, (kn >> gshift) != (k0 >> gshift));
+      fetch_cached<KBITS, VBITS, NG, PAGED, MT, KTOK, VTOK>(c, kn, lo, f, prn, gshift,
+                                                            (kn >> gshift) != (k0 >> gshift));
     }
     if (KTOK)
       block_compute<false, false, true>(kreg, kext, Vt, qk, qext, count, alpha_g, sc.ev, lane, st, sadd);
@@ -790,15 +908,29 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
   }
 }
 
+template <int KB, int VB, int NG, bool KT, bool VT>
+void launch_kernel_t(const AttnLaunch &p, hipStream_t stream, dim3 grid, int64_t rows, float *partials) {
+  constexpr bool PG = KVQ_SHORT16_PAGED != 0;
+  constexpr int MH = KVQ_SHORT16_META16;
+  auto kernel = p.corr == KV_CORR_TAYLOR ? (p.causal ? attn_short16_kernel<KB, VB, true, NG, true, PG, MH, KT, VT>
+                                                     : attn_short16_kernel<KB, VB, true, NG, false, PG, MH, KT, VT>)
+                                         : (p.causal ? attn_short16_kernel<KB, VB, false, NG, true, PG, MH, KT, VT>
+                                                     : attn_short16_kernel<KB, VB, false, NG, false, PG, MH, KT, VT>);
+  kernel<<<grid, dim3(THREADS), 0, stream>>>(p, rows, p.splits, partials);
+}
+
+// The unit's instances: keys along the tokens (KVQ_SHORT16_KTOK), values
+// along the tokens with keys either way (KVQ_SHORT16_VTOK), or neither.
 template <int KB, int VB, int NG>
 void launch_kernel(const AttnLaunch &p, hipStream_t stream, dim3 grid, int64_t rows, float *partials) {
-  constexpr bool PG = KVQ_SHORT16_PAGED != 0, KT = KVQ_SHORT16_KTOK != 0;
-  constexpr int MH = KVQ_SHORT16_META16;
-  auto kernel = p.corr == KV_CORR_TAYLOR ? (p.causal ? attn_short16_kernel<KB, VB, true, NG, true, PG, MH, KT>
-                                                     : attn_short16_kernel<KB, VB, true, NG, false, PG, MH, KT>)
-                                         : (p.causal ? attn_short16_kernel<KB, VB, false, NG, true, PG, MH, KT>
-                                                     : attn_short16_kernel<KB, VB, false, NG, false, PG, MH, KT>);
-  kernel<<<grid, dim3(THREADS), 0, stream>>>(p, rows, p.splits, partials);
+  if constexpr (KVQ_SHORT16_VTOK != 0) {
+    if (p.ktok)
+      launch_kernel_t<KB, VB, NG, true, true>(p, stream, grid, rows, partials);
+    else
+      launch_kernel_t<KB, VB, NG, false, true>(p, stream, grid, rows, partials);
+  } else {
+    launch_kernel_t<KB, VB, NG, KVQ_SHORT16_KTOK != 0, false>(p, stream, grid, rows, partials);
+  }
 }
 
 template <int KB, int VB>
@@ -826,7 +958,13 @@ hipError_t launch_bits(const AttnLaunch &p, hipStream_t stream) {
 
 }  // namespace
 
-#if KVQ_SHORT16_KTOK
+#if KVQ_SHORT16_VTOK
+#if KVQ_SHORT16_PAGED
+hipError_t launch_attention_short16_vtok_paged(const AttnLaunch &p, hipStream_t stream) {
+#else
+hipError_t launch_attention_short16_vtok(const AttnLaunch &p, hipStream_t stream) {
+#endif
+#elif KVQ_SHORT16_KTOK
 #if KVQ_SHORT16_PAGED && KVQ_SHORT16_META16 == 2
 hipError_t launch_attention_short16_ktok_mb16_paged(const AttnLaunch &p, hipStream_t stream) {
 #elif KVQ_SHORT16_PAGED && KVQ_SHORT16_META16
@@ -860,17 +998,19 @@ hipError_t launch_attention_short16(const AttnLaunch &p, hipStream_t stream) {
   return launch_bits<4, 4>(p, stream);
 }
 
-#if !KVQ_SHORT16_PAGED && !KVQ_SHORT16_META16 && !KVQ_SHORT16_KTOK
-// Keys grouped along the tokens, values along the head dimension: d = 128,
-// correction off or Taylor, at most 16 query rows per KV head, and (paged)
-// pages that hold whole 32-key blocks.
-bool short16_ktok_supported(int32_t d, int corr, bool ktok, bool vtok, int32_t page_size, int64_t rows_per_kvhead) {
-  return d == D && corr != KV_CORR_EXACT && ktok && !vtok && rows_per_kvhead <= ROWS &&
-         (page_size == 0 || page_size >= BK);
+#if !KVQ_SHORT16_PAGED && !KVQ_SHORT16_META16 && !KVQ_SHORT16_KTOK && !KVQ_SHORT16_VTOK
+// Caches grouped along the tokens: d = 128, correction off or Taylor, at most
+// 16 query rows per KV head, (paged) pages that hold whole 32-key blocks,
+// and with values along the tokens fp32 metadata.
+bool short16_tok_supported(int32_t d, int corr, bool ktok, bool vtok, int32_t page_size, int meta,
+                           int64_t rows_per_kvhead) {
+  return d == D && corr != KV_CORR_EXACT && (ktok || vtok) && rows_per_kvhead <= ROWS &&
+         (page_size == 0 || page_size >= BK) && (!vtok || meta == kMetaF32);
 }
 
 hipError_t launch_attention_short16_tok(const AttnLaunch &p, hipStream_t stream) {
   const bool paged = p.layout.page_table != nullptr;
+  if (p.vtok) return paged ? launch_attention_short16_vtok_paged(p, stream) : launch_attention_short16_vtok(p, stream);
   if (p.meta == kMetaBF16)
     return paged ? launch_attention_short16_ktok_mb16_paged(p, stream) : launch_attention_short16_ktok_mb16(p, stream);
   if (p.meta == kMetaF16)

@@ -327,7 +327,8 @@ Plan plan_attention(const kv_attn_args *a, bool query_device, size_t limit = SIZ
   if (path == KV_PATH_SHORT) {
     const int cus = query_device ? device_cu_count() : 256;
     const bool fast = kvq::short_fast_supported(a->d, a->corr, tokens_axis(a), cache_page_size(a)) ||
-                      kvq::short16_ktok_supported(a->d, a->corr, k_tokens(a), v_tokens(a), cache_page_size(a), rows);
+                      kvq::short16_tok_supported(a->d, a->corr, k_tokens(a), v_tokens(a), cache_page_size(a),
+                                                 a->Nc > 0 ? static_cast<int>(a->k_cache->meta) : 0, rows);
     auto bytes = [&](int s) {
       return fast ? kvq::short_path_workspace_bytes(a->B, a->Hq, a->Nq, a->d, s)
                   : kvq::general_path_workspace_bytes(a->B, a->Hq, a->Hkv, a->Nq, a->d, s, true);

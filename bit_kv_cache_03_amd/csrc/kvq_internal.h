@@ -211,12 +211,16 @@ hipError_t launch_attention_short16_m16(const AttnLaunch &p, hipStream_t stream)
 hipError_t launch_attention_short16_m16_paged(const AttnLaunch &p, hipStream_t stream);
 hipError_t launch_attention_short16_mb16(const AttnLaunch &p, hipStream_t stream);
 hipError_t launch_attention_short16_mb16_paged(const AttnLaunch &p, hipStream_t stream);
-// The 16-row kernel over a K cache grouped along the tokens (values along the
-// head dimension): whether it serves a call, its dispatch over the layout and
-// metadata kind, and the instances (attention_short16_ktok*.hip).  Same
-// workspace and split count as the short-query kernels.
-bool short16_ktok_supported(int32_t d, int corr, bool ktok, bool vtok, int32_t page_size, int64_t rows_per_kvhead);
+// The 16-row kernel over caches grouped along the tokens (K, V or both):
+// whether it serves a call, its dispatch over the layout and metadata kind,
+// and the instances (attention_short16_ktok*.hip: K along the tokens, V
+// along the head dimension; attention_short16_vtok*.hip: V along the tokens,
+// fp32 metadata).  Same workspace and split count as the short-query kernels.
+bool short16_tok_supported(int32_t d, int corr, bool ktok, bool vtok, int32_t page_size, int meta,
+                           int64_t rows_per_kvhead);
 hipError_t launch_attention_short16_tok(const AttnLaunch &p, hipStream_t stream);
+hipError_t launch_attention_short16_vtok(const AttnLaunch &p, hipStream_t stream);
+hipError_t launch_attention_short16_vtok_paged(const AttnLaunch &p, hipStream_t stream);
 hipError_t launch_attention_short16_ktok(const AttnLaunch &p, hipStream_t stream);
 hipError_t launch_attention_short16_ktok_paged(const AttnLaunch &p, hipStream_t stream);
 hipError_t launch_attention_short16_ktok_m16(const AttnLaunch &p, hipStream_t stream);

@@ -1,16 +1,19 @@
-"""Keys grouped along the tokens (per channel, KIVI-style), values along the
-head dimension, at most 16 query rows per KV head: the 16-row short-query
-kernel's token-axis instances, on the GPU against the oracle.
+"""Caches grouped along the tokens (per channel) with at most 16 query rows
+per KV head: the 16-row short-query kernel's token-axis instances, on the
+GPU against the oracle.
 
-The kernel folds each token group's steps into the query and feeds the raw
+Keys along the tokens (KIVI-style, values along the head dimension): the
+kernel folds each token group's steps into the query and feeds the raw
 codes to the MFMA, adding q.z and the per-channel Taylor bias per row
 ("量化鍵值偷走注意力…" (agents-report.net) §方法: one step per group or per
-channel).  Cases: token groups of 32/64/128, INT2 and INT4 keys and
-values, decode and GQA chunks (1-16 rows), ragged and tiny caches (the last
-token group shorter, fewer keys than a block, one key), forced split counts,
-the causal mask, binary16 and bfloat16 metadata, paged pools (bit-identical
-to contiguous), keys with large per-channel offsets (outlier channels) and
-log-uniform scales.  Bar: that of every attention parity test."""
+channel).  Values along the tokens (with keys either way, fp32 metadata):
+dequantised with per-channel operands staged per token group.  Cases: token
+groups of 32/64/128, INT2 and INT4 keys and values, decode and GQA chunks
+(1-16 rows), ragged and tiny caches (the last token group shorter, fewer
+keys than a block, one key), forced split counts, the causal mask, binary16
+and bfloat16 metadata, paged pools (bit-identical to contiguous), keys with
+large per-channel offsets (outlier channels) and log-uniform scales.  Bar:
+that of every attention parity test."""
 import numpy as np
 import pytest
 import torch
@@ -39,28 +42,29 @@ CASES = {
 }
 
 
-def _caches(w, data, meta="f32", page=0, seed=0):
+def _caches(w, data, meta="f32", page=0, seed=0, kaxis="tokens", vaxis="dim"):
     import _gpu
     cap = -(-w.Nc // w.group) * w.group
     if page:
         cap = -(-cap // page) * page
-        kc = _gpu.paged_cache(w, data["kc"], w.kbits, page, cap=cap, seed=seed, meta=meta, axis="tokens")
-        vc = _gpu.paged_cache(w, data["vc"], w.vbits, page, cap=cap, seed=seed, meta=meta)
+        kc = _gpu.paged_cache(w, data["kc"], w.kbits, page, cap=cap, seed=seed, meta=meta, axis=kaxis)
+        vc = _gpu.paged_cache(w, data["vc"], w.vbits, page, cap=cap, seed=seed, meta=meta, axis=vaxis)
         vc.page_table = kc.page_table  # one table, as the attention call requires
         return kc, vc
-    return (_gpu.build_cache(w, data["kc"], w.kbits, cap=cap, meta=meta, axis="tokens"),
-            _gpu.build_cache(w, data["vc"], w.vbits, cap=cap, meta=meta))
+    return (_gpu.build_cache(w, data["kc"], w.kbits, cap=cap, meta=meta, axis=kaxis),
+            _gpu.build_cache(w, data["vc"], w.vbits, cap=cap, meta=meta, axis=vaxis))
 
 
-def _compare(orc, w, corr, splits=0, causal=False, meta="f32", page=0):
+def _compare(orc, w, corr, splits=0, causal=False, meta="f32", page=0, kaxis="tokens", vaxis="dim"):
     import _gpu
     assert w.Nq * (w.Hq // w.Hkv) <= 16
     data = W.generate(w)
     print(f"[tokens short] B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Ncur={w.Ncur} Nc={w.Nc} bits={w.kbits}/{w.vbits} "
-          f"group={w.group} corr={corr} splits={splits} causal={causal} meta={meta} page={page}", flush=True)
-    kc, vc = _caches(w, data, meta, page)
+          f"group={w.group} corr={corr} splits={splits} causal={causal} meta={meta} page={page} "
+          f"axes={kaxis}/{vaxis}", flush=True)
+    kc, vc = _caches(w, data, meta, page, kaxis=kaxis, vaxis=vaxis)
     out = _gpu.run_attention(w, data, kc, vc, corr=corr, path="short", splits=splits, causal=causal)
-    ref = oracle_problem(orc, w, corr, data=data, causal=causal, meta=meta, kaxis="tokens", vaxis="dim").attention()
+    ref = oracle_problem(orc, w, corr, data=data, causal=causal, meta=meta, kaxis=kaxis, vaxis=vaxis).attention()
     _gpu.check(_gpu.out_rows(out), ref)
     return out
 
@@ -137,3 +141,46 @@ def test_offsets_far_from_zero(orc):
     out = _gpu.run_attention(w, data, kc, vc, corr="taylor", path="short")
     ref = oracle_problem(orc, w, "taylor", data=data, kaxis="tokens", vaxis="dim").attention()
     _gpu.check(_gpu.out_rows(out), ref)
+
+
+VAXES = [("tokens", "tokens"), ("dim", "tokens")]
+
+
+@pytest.mark.parametrize("axes", VAXES)
+@pytest.mark.parametrize("case", sorted(CASES))
+@pytest.mark.parametrize("corr", ["off", "taylor"])
+def test_values_along_tokens(orc, axes, case, corr):
+    _compare(orc, CASES[case], corr, kaxis=axes[0], vaxis=axes[1])
+
+
+@pytest.mark.parametrize("axes", VAXES)
+@pytest.mark.parametrize("kbits,vbits", [(2, 2), (2, 4), (4, 2), (4, 4)])
+@pytest.mark.parametrize("group", [32, 64, 128])
+def test_values_along_tokens_bits_and_groups(orc, axes, kbits, vbits, group):
+    w = GQA.scaled(B=2, Hq=8, Hkv=2, Nq=2, Ncur=3, Nc=600, group=group, kbits=kbits, vbits=vbits)
+    _compare(orc, w, "taylor", kaxis=axes[0], vaxis=axes[1])
+
+
+@pytest.mark.parametrize("axes", VAXES)
+@pytest.mark.parametrize("splits,causal", [(3, False), (40, False), (0, True), (5, True)])
+def test_values_along_tokens_splits_causal(orc, axes, splits, causal):
+    w = GQA.scaled(B=2, Hq=8, Hkv=2, Nq=4, Ncur=9, Nc=500, group=64)
+    _compare(orc, w, "taylor", splits=splits, causal=causal, kaxis=axes[0], vaxis=axes[1])
+
+
+@pytest.mark.parametrize("axes", VAXES)
+@pytest.mark.parametrize("page", [32, 128])
+def test_values_along_tokens_paged(orc, axes, page):
+    import _gpu
+    w = GQA.scaled(B=3, Hq=8, Hkv=2, Nq=2, Ncur=2, Nc=700, group=32 if page == 32 else 64)
+    data = W.generate(w)
+    a = _compare(orc, w, "taylor", page=page, kaxis=axes[0], vaxis=axes[1])
+    kc, vc = _caches(w, data, kaxis=axes[0], vaxis=axes[1])
+    b = _gpu.run_attention(w, data, kc, vc, corr="taylor", path="short")
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("meta", ["f16", "bf16"])
+def test_values_along_tokens_meta16_general(orc, meta):
+    """16-bit metadata with values along the tokens stays on the general kernel."""
+    _compare(orc, CASES["gqa_chunk4_g32"], "taylor", meta=meta, kaxis="tokens", vaxis="tokens")
