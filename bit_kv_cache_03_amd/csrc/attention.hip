@@ -778,6 +778,8 @@ hipError_t launch_attention_short(const AttnLaunch &p, hipStream_t stream) {
   if (p.ktok || p.vtok) {
     if (short16_tok_supported(p.d, p.corr, p.ktok, p.vtok, layout_page_size(p.layout), p.meta, p.Nq * (p.Hq / p.Hkv)))
       return launch_attention_short16_tok(p, stream);
+    if (short_tok_supported(p.d, p.corr, p.ktok, p.vtok, layout_page_size(p.layout), p.meta))
+      return p.layout.page_table ? launch_attention_short_tok_paged(p, stream) : launch_attention_short_tok(p, stream);
     return launch_attention_tokens(p, stream, true);
   }
   if (short_fast_supported(p.d, p.corr, false, layout_page_size(p.layout))) return launch_attention_short_fast(p, stream);

@@ -29,6 +29,14 @@
 // the next block, S^T = K Q^T (8 fp16 MFMA + 1 correction step), mask the
 // ragged block, lazy max, exponentials, O^T += V^T P^T (8 fp16 MFMA).
 //
+// Caches grouped along the tokens (KVQ_SHORT_TOK units, fp32 metadata): as in
+// the 16-row kernel, keys along the tokens fold each token group's steps into
+// the query (q' = q D 2^-ed, rebuilt per group from the workgroup's fp16
+// query tile in LDS) and take their raw codes as the fp16 subnormals c 2^-24,
+// with q.z and the per-channel Taylor bias as one term per row; values along
+// the tokens dequantise with per-channel operands staged per token group.
+// Each wave then walks a contiguous range of blocks.
+//
 // Paged caches and 16-bit metadata: the instances for them are built from
 // this file in translation units of their own (attention_short_paged.hip,
 // attention_short_m16*.hip and attention_short_mb16*.hip define
@@ -43,6 +51,9 @@
 
 #ifndef KVQ_SHORT_PAGED
 #define KVQ_SHORT_PAGED 0
+#endif
+#ifndef KVQ_SHORT_TOK
+#define KVQ_SHORT_TOK 0
 #endif
 #ifndef KVQ_SHORT_META16
 #define KVQ_SHORT_META16 0
@@ -61,6 +72,12 @@ constexpr int VT = D * VS;      // 16-bit elements of a wave's V^T tile
 constexpr int OS = D + 4;       // fp32 row of the merge buffer
 constexpr int MERGE = 32 * OS + 64;  // floats of a wave's merge buffer (O rows, then m and l)
 constexpr int LDS_BYTES = WAVES * VT * 2 > WAVES * MERGE * 4 ? WAVES * VT * 2 : WAVES * MERGE * 4;
+// groups along the tokens, inside the merge buffer's span (used only after
+// the block loop): the workgroup's fp16 query tile [32][D] after the V^T
+// tiles, then each wave's token-group staging of K and of V (2 D floats each)
+constexpr int LQ = WAVES * VT;       // 16-bit offset of the query tile
+constexpr int GSTAGE = LQ + 32 * D;  // 16-bit offset of the staging areas
+static_assert((GSTAGE + WAVES * 4 * D * 2) * 2 <= LDS_BYTES, "token-group staging fits the merge buffer's span");
 
 // V^T element (row = head-dim index, col = permuted key slot 0..31); the
 // 16-byte chunks of a row are XOR-swizzled by (row / 16) % 4 so that the
@@ -77,6 +94,8 @@ struct Fetch {
   uint32_t vw[4];      // V codes of keys 4kq+j at d in [16dq, 16dq+16): INT4 words
   uint32_t vw2[4];     //   d 16dq..+7 in vw, +8..+15 in vw2; INT2 all 16 in vw
   float vstep[4], vzero[4];
+  uint32_t gd[2], gz[2], vgd[2], vgz[2];  // groups along the tokens: two steps / zero points of the
+                                          // block's token group per lane (K, then V; fp32 bits)
 };
 
 // Lane roles (per wave):
@@ -103,11 +122,28 @@ __device__ inline Lanes lane_offsets(int lane) {
 // Loads one cached block (rows [k0, k0 + 32)); rows at or past the segment
 // end read as zero (their scores are masked).  Paged: the buffer range stops
 // at the block's end, inside its page.
-template <int KBITS, int VBITS, int NG, bool PAGED, int MT>
-__device__ inline void fetch_cached(const Ctx &c, int k0, const Lanes &o, int h, Fetch &f, size_t pool_row = 0) {
+// Two fp32 steps and two zero points of a token group (at metadata row
+// r0 >> gshift of the arrays s and z, one row of D per group) for the lane.
+__device__ inline void fetch_group(const float *s, const float *z, size_t r0, int gshift, uint32_t (&gd)[2],
+                                   uint32_t (&gz)[2]) {
+  const size_t mrow = r0 >> gshift;
+  const Buf bs = buffer_at(s + mrow * D, D * 4), bz = buffer_at(z + mrow * D, D * 4);
+  const uint32_t off = static_cast<uint32_t>(__lane_id()) * 8;
+  const u32x2 a = ld64(bs, off), b = ld64(bz, off);
+  gd[0] = a.x; gd[1] = a.y;
+  gz[0] = b.x; gz[1] = b.y;
+}
+
+template <int KBITS, int VBITS, int NG, bool PAGED, int MT, bool KTOK = false, bool VTOK = false>
+__device__ inline void fetch_cached(const Ctx &c, int k0, const Lanes &o, int h, Fetch &f, size_t pool_row = 0,
+                                    int gshift = 0, bool newg = false) {
   constexpr uint32_t KROW = D * KBITS / 8, VROW = D * VBITS / 8, ES = MT ? 2 : 4;
   const uint32_t rows = static_cast<uint32_t>(PAGED ? min(c.nc - k0, BK) : c.nc - k0);
   const size_t r0 = PAGED ? pool_row : block_row<false>(c, k0);  // paged: looked up a block earlier
+  if (newg) {  // groups along the tokens: the block starts the wave's next token group
+    if (KTOK) fetch_group(c.kc_scale, c.kc_zero, r0, gshift, f.gd, f.gz);
+    if (VTOK) fetch_group(c.vc_scale, c.vc_zero, r0, gshift, f.vgd, f.vgz);
+  }
   {
     const Buf kc = buffer_at(c.kc_codes + r0 * KROW, rows * KROW);
     const u32x4 a = ld128(kc, o.kc);
@@ -116,6 +152,8 @@ __device__ inline void fetch_cached(const Ctx &c, int k0, const Lanes &o, int h,
       const u32x4 b = ld128(kc, o.kc + 16);
       f.kw[4] = b.x; f.kw[5] = b.y; f.kw[6] = b.z; f.kw[7] = b.w;
     }
+  }
+  if (!KTOK) {
     const Buf ks = buffer_at(meta_adv<MT>(c.kc_scale, r0 * NG), rows * NG * ES);
     const Buf kz = buffer_at(meta_adv<MT>(c.kc_zero, r0 * NG), rows * NG * ES);
     // the groups of d = 64h + 32j, j = 0, 1 (the lane's own values)
@@ -148,10 +186,107 @@ __device__ inline void fetch_cached(const Ctx &c, int k0, const Lanes &o, int h,
       } else {
         f.vw[j] = ld32(vc, o.vc + j * VROW);
       }
-      f.vstep[j] = ld_meta1<MT>(vs, o.vm + j * NG * ES);
-      f.vzero[j] = ld_meta1<MT>(vz, o.vm + j * NG * ES);
+      if (!VTOK) {
+        f.vstep[j] = ld_meta1<MT>(vs, o.vm + j * NG * ES);
+        f.vzero[j] = ld_meta1<MT>(vz, o.vm + j * NG * ES);
+      }
     }
   }
+}
+
+// ---- groups along the tokens (fp32 metadata) --------------------------------
+
+// K operands of a cached block whose keys group along the tokens: the lane's
+// codes (key kr, d = 64h + 8i .. +7 in k[i]), each in the low bits of a
+// 16-bit field (the fp16 subnormal c 2^-24), word e holding dims e and e + 4.
+template <int KBITS>
+__device__ inline void unpack_k_codes(const Ctx &c, const Fetch &f, f16x8 (&k)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t w = KBITS == 4 ? f.kw[i] : (f.kw[i >> 1] >> (16 * (i & 1)));
+    const uint32_t x = KBITS == 4 ? w : (w & 0xffffu) | ((w & 0xffffu) << 8);  // INT2: code e + 4 next to e
+    uint32_t m[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m[e] = (x >> (KBITS * e)) & c.kmask;
+    k[i] = __builtin_bit_cast(f16x8, make_uint4(m[0], m[1], m[2], m[3]));
+  }
+}
+
+// Query terms of a token group for keys along the tokens: the group's steps
+// D_c and zero points z_c (two each per lane in f, staged through the wave's
+// area Gm) and the workgroup's query tile Lq (row qc: fp16 q 2^-eq) give
+// qk[i] word e = fp16(q_c D_c 2^-ed) of d = 64h + 8i + e and + 4 (2^ed above
+// the group's largest step), the block scale alpha_g = alpha_q 2^(ed + 24)
+// and the row's term sadd = q.z - (tau/24) sum_c q_c^2 D_c^2 in the scores'
+// units 2^-(eq + ed + 24) (qun = 2^eq).
+template <bool TAYLOR>
+__device__ inline void ktok_group(const Fetch &f, int lane, float *Gm, const uint16_t *Lq, float tau, float alpha_q,
+                                  float qun, f16x8 (&qk)[8], float &sadd, float &alpha_g) {
+  *reinterpret_cast<float2 *>(Gm + 2 * lane) = make_float2(__uint_as_float(f.gd[0]), __uint_as_float(f.gd[1]));
+  *reinterpret_cast<float2 *>(Gm + D + 2 * lane) = make_float2(__uint_as_float(f.gz[0]), __uint_as_float(f.gz[1]));
+  const float dmax = wave_max(fmaxf(__uint_as_float(f.gd[0]), __uint_as_float(f.gd[1])));
+  const int ed = dmax > 0.f ? ilog2_pos(dmax) + 1 : 0;
+  const float ds = ldexpf(1.0f, -ed);
+  const int qc = lane & 31, h = lane >> 5;
+  float s2 = 0.f, sz = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int d0 = 64 * h + 8 * i;
+    const float4 a0 = *reinterpret_cast<const float4 *>(Gm + d0), a1 = *reinterpret_cast<const float4 *>(Gm + d0 + 4);
+    const float4 b0 = *reinterpret_cast<const float4 *>(Gm + D + d0);
+    const float4 b1 = *reinterpret_cast<const float4 *>(Gm + D + d0 + 4);
+    const float dd[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    const float zz[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+    const uint4 qw = *reinterpret_cast<const uint4 *>(Lq + qc * D + d0);  // word e: dims 2e, 2e + 1
+    const uint32_t u[4] = {qw.x, qw.y, qw.z, qw.w};
+    float qv[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const f16x2 hh = __builtin_bit_cast(f16x2, u[e]);
+      qv[2 * e] = static_cast<float>(hh.x);
+      qv[2 * e + 1] = static_cast<float>(hh.y);
+    }
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const _Float16 a = static_cast<_Float16>(qv[e] * (dd[e] * ds));
+      const _Float16 b = static_cast<_Float16>(qv[e + 4] * (dd[e + 4] * ds));
+      w[e] = pair_h(a, b);
+      s2 = fmaf(static_cast<float>(a), static_cast<float>(a), s2);
+      s2 = fmaf(static_cast<float>(b), static_cast<float>(b), s2);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sz = fmaf(qv[e], zz[e], sz);
+    qk[i] = __builtin_bit_cast(f16x8, make_uint4(w[0], w[1], w[2], w[3]));
+  }
+  s2 += __shfl_xor(s2, 32, 64);
+  sz += __shfl_xor(sz, 32, 64);
+  const float bias = TAYLOR ? (tau / 24.0f) * qun * ldexpf(s2, ed) : 0.f;
+  sadd = ldexpf(sz * ds - bias, -24);
+  alpha_g = ldexpf(alpha_q, ed + 24);
+}
+
+// Values along the tokens: the largest |v| the lane's two channels of the
+// token group can dequantise to, and their staged operands in the wave's
+// area Gv (channel c: d_c = D_c vsc 2^-p, z_c vsc - 1024 d_c, p = 0 for even
+// channels and the odd field's position 4 (INT4) or 2 (INT2) for odd ones).
+template <int VBITS>
+__device__ inline float vtok_bound(const Fetch &f) {
+  float b = 0.f;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const float d = __uint_as_float(f.vgd[e]), z = __uint_as_float(f.vgz[e]);
+    b = fmaxf(b, fmaxf(fabsf(z), fabsf(fmaf(d, static_cast<float>((1 << VBITS) - 1), z))));
+  }
+  return b;
+}
+template <int VBITS>
+__device__ inline void vtok_stage(const Fetch &f, int lane, float vsc, float *Gv) {
+  constexpr int P1 = VBITS == 4 ? 4 : 2;
+  const float d0 = __uint_as_float(f.vgd[0]) * vsc, d1 = __uint_as_float(f.vgd[1]) * vsc * (1.0f / (1 << P1));
+  *reinterpret_cast<float2 *>(Gv + 2 * lane) = make_float2(d0, d1);
+  *reinterpret_cast<float2 *>(Gv + D + 2 * lane) =
+      make_float2(fmaf(-1024.0f, d0, __uint_as_float(f.vgz[0]) * vsc), fmaf(-1024.0f, d1, __uint_as_float(f.vgz[1]) * vsc));
 }
 
 // Largest |k| (|v|) a lane's share of a cached block can dequantise to:
@@ -292,6 +427,55 @@ __device__ inline void unpack_v_cached(const Ctx &c, int lane, const Fetch &f, f
   }
 }
 
+// unpack_v_cached with values along the tokens: the operands of channel
+// c = 16dq + NF byte + fl come from the staged token group (area Gv), the
+// same for the four keys.
+template <int VBITS>
+__device__ inline void unpack_v_tok(const Ctx &c, int lane, const Fetch &f, const float *Gv, uint16_t *Vt) {
+  constexpr int NF = 8 / VBITS;
+  const int kq = lane & 7, dq = lane >> 3;
+  const int a = kq & 3;
+  const int slot = 16 * (kq >> 2) + 4 * (a >> 1) + 8 * (a & 1);
+  float dc[16], zc[16];
+#pragma unroll
+  for (int e = 0; e < 16; e += 4) {
+    const float4 x = *reinterpret_cast<const float4 *>(Gv + 16 * dq + e);
+    const float4 y = *reinterpret_cast<const float4 *>(Gv + D + 16 * dq + e);
+    dc[e] = x.x; dc[e + 1] = x.y; dc[e + 2] = x.z; dc[e + 3] = x.w;
+    zc[e] = y.x; zc[e + 1] = y.y; zc[e + 2] = y.z; zc[e + 3] = y.w;
+  }
+  auto field = [&](uint32_t r, int k, int e) {  // both keys of r at channel e, field k (0: p = 0, 1: p = P1)
+    const uint32_t m = (r & (k ? c.vmask1 : c.vmask0)) | 0x64006400u;
+    const f16x2 hh = __builtin_bit_cast(f16x2, m);
+    return pair_h(dequant_h(static_cast<float>(hh.x), dc[e], zc[e]), dequant_h(static_cast<float>(hh.y), dc[e], zc[e]));
+  };
+#pragma unroll
+  for (int byte = 0; byte < (VBITS == 4 ? 8 : 4); ++byte) {
+    const int bw = byte & 3;
+    const uint32_t sel = static_cast<uint32_t>(bw) | 0x0c00u | (static_cast<uint32_t>(4 + bw) << 16) | 0x0c000000u;
+    uint32_t r[2];
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) {
+      const uint32_t w0 = byte >= 4 ? f.vw2[2 * jp] : f.vw[2 * jp];
+      const uint32_t w1 = byte >= 4 ? f.vw2[2 * jp + 1] : f.vw[2 * jp + 1];
+      r[jp] = __builtin_amdgcn_perm(w1, w0, sel);
+    }
+    uint32_t x[NF][2];
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) {
+      x[0][jp] = field(r[jp], 0, NF * byte);
+      x[1][jp] = field(r[jp], 1, NF * byte + 1);
+      if (VBITS == 2) {
+        x[NF - 2][jp] = field(r[jp] >> 4, 0, NF * byte + 2);
+        x[NF - 1][jp] = field(r[jp] >> 4, 1, NF * byte + 3);
+      }
+    }
+#pragma unroll
+    for (int fl = 0; fl < NF; ++fl)
+      *reinterpret_cast<uint2 *>(Vt + vts(16 * dq + NF * byte + fl, slot)) = make_uint2(x[fl][0], x[fl][1]);
+  }
+}
+
 // Current-chunk block (bf16 keys and values): the lane's raw rows (same
 // lane roles as the cached blocks; rows past the end clamp to the last one,
 // their scores are masked) and the largest |k| and |v| among them.
@@ -361,16 +545,19 @@ struct Soft {
 // the wave's V^T tile, the block's score scale alpha (scores are
 // q.k 2^-(eq+ek)) and value exponent ev.  count < BK marks a ragged block;
 // CORR adds the correction step.  CAUSAL: count is the lane's own (possibly
-// <= 0), and a row may have seen no key yet (m = -inf).
-template <bool CORR, bool CAUSAL = false>
+// <= 0), and a row may have seen no key yet (m = -inf).  ADD: the row's
+// scores add sadd.
+template <bool CORR, bool CAUSAL = false, bool ADD = false>
 __device__ inline void block_compute(const f16x8 (&k)[8], bf16x8 kext, const uint16_t *Vt, const f16x8 (&q)[8],
-                                     bf16x8 qext, int count, float alpha, int ev, int lane, Soft &st) {
+                                     bf16x8 qext, int count, float alpha, int ev, int lane, Soft &st,
+                                     float sadd = 0.f) {
   const float fev = static_cast<float>(ev);
   const int qc = lane & 31, h = lane >> 5;
   f32x16 s = f32x16{};
 #pragma unroll
   for (int j = 0; j < 8; ++j) s = __builtin_amdgcn_mfma_f32_32x32x16_f16(k[j], q[j], s, 0, 0, 0);
   if (CORR) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kext, qext, s, 0, 0, 0);
+  if (ADD) s += sadd;
   if (CAUSAL || count < BK) {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
@@ -416,9 +603,13 @@ __device__ inline void block_compute(const f16x8 (&k)[8], bf16x8 kext, const uin
     }
 }
 
-template <int KBITS, int VBITS, bool TAYLOR, int NG, bool CAUSAL, bool PAGED, int MT>
+// KTOK / VTOK: keys / values grouped along the tokens (fp32 metadata; p.group
+// is then also their token group).
+template <int KBITS, int VBITS, bool TAYLOR, int NG, bool CAUSAL, bool PAGED, int MT, bool KTOK = false,
+          bool VTOK = false>
 __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, int64_t rows_per_kvhead,
                                                                 int32_t row_groups, int32_t nsplit, float *ws) {
+  constexpr bool TOK = KTOK || VTOK;
   __shared__ __attribute__((aligned(16))) uint16_t L[LDS_BYTES / 2];
 
   const int tid = threadIdx.x;
@@ -452,12 +643,22 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
   f16x8 q[8];
   bf16x8 qext;
   Soft st;
-  load_query<TAYLOR, true>(p.q + qrow * D, h, group_shift, p.tau, 0, q, qext, st.alpha);
+  float qun = 1.f;
+  load_query<TAYLOR, true>(p.q + qrow * D, h, group_shift, p.tau, 0, q, qext, st.alpha, &qun);
+  const uint16_t *Lq = L + LQ;
+  if (KTOK) {  // the workgroup's query tile for the token groups' query terms (every wave holds it)
+    if (wave == 0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) *reinterpret_cast<f16x8 *>(L + LQ + qc * D + 64 * h + 8 * i) = q[i];
+    }
+    __syncthreads();
+  }
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) st.o[db] = f32x16{};
   st.m = -INFINITY;
   st.l = 0.f;
 
+  const int gshift = TOK ? __builtin_ctz(static_cast<unsigned>(p.group)) : 0;
   Ctx c{};
   c.nc = static_cast<int>(p.Nc);
   c.ncur = static_cast<int>(p.Ncur);
@@ -473,10 +674,11 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
     const int64_t hrow = PAGED ? 0 : bkv * p.cap;  // paged: the pointers stay at the pool
     c.kc_codes = p.kc_codes + hrow * (D * KBITS / 8);
     c.vc_codes = p.vc_codes + hrow * (D * VBITS / 8);
-    c.kc_scale = meta_adv<MT>(p.kc_scale, hrow * ng);
-    c.kc_zero = meta_adv<MT>(p.kc_zero, hrow * ng);
-    c.vc_scale = meta_adv<MT>(p.vc_scale, hrow * ng);
-    c.vc_zero = meta_adv<MT>(p.vc_zero, hrow * ng);
+    // groups along the tokens: one metadata row of D per token group
+    c.kc_scale = meta_adv<MT>(p.kc_scale, KTOK ? (hrow >> gshift) * D : hrow * ng);
+    c.kc_zero = meta_adv<MT>(p.kc_zero, KTOK ? (hrow >> gshift) * D : hrow * ng);
+    c.vc_scale = meta_adv<MT>(p.vc_scale, VTOK ? (hrow >> gshift) * D : hrow * ng);
+    c.vc_zero = meta_adv<MT>(p.vc_zero, VTOK ? (hrow >> gshift) * D : hrow * ng);
   }
   if (p.Ncur > 0) {
     c.k_cur = p.k_cur + bkv * p.Ncur * D;
@@ -500,9 +702,19 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
     if (bend > cb) bend = cb;
   }
   uint16_t *Vt = L + wave * VT;
+  float *Gm = reinterpret_cast<float *>(L + GSTAGE) + wave * 4 * D;  // token-group staging of K
+  float *Gv = Gm + 2 * D;                                             // and of V
 
-  int blk = bbeg + wave;
-  const int cend = bend < nbc ? bend : nbc;
+  // blocks dealt round-robin, or (groups along the tokens) in contiguous
+  // ranges per wave
+  int blk = bbeg + wave, wend = bend, bstep = WAVES;
+  if (TOK) {
+    const int per = (bend - bbeg + WAVES - 1) / WAVES;
+    blk = bbeg + wave * per;
+    wend = blk + per < bend ? blk + per : bend;
+    bstep = 1;
+  }
+  const int cend = wend < nbc ? wend : nbc;
   const Lanes lo = lane_offsets<KBITS, VBITS, NG, MT>(lane);
   Scales sc;
   // with the caches' running bounds the exponents of the cached blocks are
@@ -513,21 +725,49 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
   f16x8 kreg[8];
   bf16x8 kext = {};
   Fetch f;
-  if (blk < cend) fetch_cached<KBITS, VBITS, NG, PAGED, MT>(c, blk * BK, lo, h, f, block_row<PAGED>(c, blk * BK));
+  // groups along the tokens: the wave's current token group and, for keys
+  // along the tokens, its query terms
+  f16x8 qk[8];
+  float sadd = 0.f, alpha_g = 0.f;
+  int gcur = -1;
+  if (blk < cend)
+    fetch_cached<KBITS, VBITS, NG, PAGED, MT, KTOK, VTOK>(c, blk * BK, lo, h, f, block_row<PAGED>(c, blk * BK),
+                                                          gshift, TOK);
   // paged: the pool row of the next block to fetch, looked up one block ahead
   // so that its scalar load has completed when the fetch needs it
-  size_t prn = PAGED && blk + WAVES < cend ? block_row<PAGED>(c, (blk + WAVES) * BK) : 0;
-  for (; blk < cend; blk += WAVES) {
+  size_t prn = PAGED && blk + bstep < cend ? block_row<PAGED>(c, (blk + bstep) * BK) : 0;
+  for (; blk < cend; blk += bstep) {
     const int k0 = blk * BK;
     const int count = c.nc - k0 < BK ? c.nc - k0 : BK;
-    if (!cache_bounds) sc.update(k_bound<KBITS, NG>(f), v_bound<VBITS>(f), st.alpha);
-    unpack_k_cached<TAYLOR, KBITS, NG>(c, lane, f, sc.kscale, kreg, kext);
-    unpack_v_cached<VBITS>(c, lane, f, sc.vscale, Vt);
-    if (blk + WAVES < cend) fetch_cached<KBITS, VBITS, NG, PAGED, MT>(c, (blk + WAVES) * BK, lo, h, f, prn);
-    block_compute<TAYLOR || kCentre<NG>>(kreg, kext, Vt, q, qext, count, sc.alpha, sc.ev, lane, st);
-    if (PAGED && blk + 2 * WAVES < cend) prn = block_row<PAGED>(c, (blk + 2 * WAVES) * BK);
+    const bool newg = TOK && (k0 >> gshift) != gcur;  // the block starts the wave's next token group
+    const float vb = VTOK ? (newg ? vtok_bound<VBITS>(f) : 0.f) : v_bound<VBITS>(f);
+    if (KTOK) {
+      if (!cache_bounds) sc.update(0.f, vb, st.alpha);
+      if (newg) ktok_group<TAYLOR>(f, lane, Gm, Lq, p.tau, st.alpha, qun, qk, sadd, alpha_g);
+      unpack_k_codes<KBITS>(c, f, kreg);
+    } else {
+      if (!cache_bounds) sc.update(k_bound<KBITS, NG>(f), vb, st.alpha);
+      unpack_k_cached<TAYLOR, KBITS, NG>(c, lane, f, sc.kscale, kreg, kext);
+    }
+    if (VTOK) {
+      if (newg) vtok_stage<VBITS>(f, lane, sc.vscale, Gv);
+      unpack_v_tok<VBITS>(c, lane, f, Gv, Vt);
+    } else {
+      unpack_v_cached<VBITS>(c, lane, f, sc.vscale, Vt);
+    }
+    if (newg) gcur = k0 >> gshift;
+    if (blk + bstep < cend) {
+      const int kn = (blk + bstep) * BK;
+      fetch_cached<KBITS, VBITS, NG, PAGED, MT, KTOK, VTOK>(c, kn, lo, h, f, prn, gshift,
+                                                            TOK && (kn >> gshift) != (k0 >> gshift));
+    }
+    if (KTOK)
+      block_compute<false, false, true>(kreg, kext, Vt, qk, qext, count, alpha_g, sc.ev, lane, st, sadd);
+    else
+      block_compute<TAYLOR || kCentre<NG>>(kreg, kext, Vt, q, qext, count, sc.alpha, sc.ev, lane, st);
+    if (PAGED && blk + 2 * bstep < cend) prn = block_row<PAGED>(c, (blk + 2 * bstep) * BK);
   }
-  for (; blk < bend; blk += WAVES) {
+  for (; blk < wend; blk += bstep) {
     const int k0 = (blk - nbc) * BK;
     int count = c.ncur - k0 < BK ? c.ncur - k0 : BK;
     if (CAUSAL) count = min(count, climit - k0);
@@ -598,16 +838,33 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short_kernel(AttnLaunch p, in
   }
 }
 
+template <int KB, int VB, int NG, bool KT, bool VT>
+void launch_kernel_t(const AttnLaunch &p, hipStream_t stream, dim3 grid, int64_t rows, int32_t row_groups,
+                     float *partials) {
+  constexpr bool PG = KVQ_SHORT_PAGED != 0;
+  constexpr int MH = KVQ_SHORT_META16;
+  auto kernel = p.corr == KV_CORR_TAYLOR ? (p.causal ? attn_short_kernel<KB, VB, true, NG, true, PG, MH, KT, VT>
+                                                     : attn_short_kernel<KB, VB, true, NG, false, PG, MH, KT, VT>)
+                                         : (p.causal ? attn_short_kernel<KB, VB, false, NG, true, PG, MH, KT, VT>
+                                                     : attn_short_kernel<KB, VB, false, NG, false, PG, MH, KT, VT>);
+  kernel<<<grid, dim3(THREADS), 0, stream>>>(p, rows, row_groups, p.splits, partials);
+}
+
+// The unit's instances: caches along the head dimension, or (KVQ_SHORT_TOK)
+// K, V or both grouped along the tokens.
 template <int KB, int VB, int NG>
 void launch_kernel(const AttnLaunch &p, hipStream_t stream, dim3 grid, int64_t rows, int32_t row_groups,
                    float *partials) {
-  constexpr bool PG = KVQ_SHORT_PAGED != 0;
-  constexpr int MH = KVQ_SHORT_META16;
-  auto kernel = p.corr == KV_CORR_TAYLOR ? (p.causal ? attn_short_kernel<KB, VB, true, NG, true, PG, MH>
-                                                     : attn_short_kernel<KB, VB, true, NG, false, PG, MH>)
-                                         : (p.causal ? attn_short_kernel<KB, VB, false, NG, true, PG, MH>
-                                                     : attn_short_kernel<KB, VB, false, NG, false, PG, MH>);
-  kernel<<<grid, dim3(THREADS), 0, stream>>>(p, rows, row_groups, p.splits, partials);
+  if constexpr (KVQ_SHORT_TOK != 0) {
+    if (p.ktok && p.vtok)
+      launch_kernel_t<KB, VB, NG, true, true>(p, stream, grid, rows, row_groups, partials);
+    else if (p.ktok)
+      launch_kernel_t<KB, VB, NG, true, false>(p, stream, grid, rows, row_groups, partials);
+    else
+      launch_kernel_t<KB, VB, NG, false, true>(p, stream, grid, rows, row_groups, partials);
+  } else {
+    launch_kernel_t<KB, VB, NG, false, false>(p, stream, grid, rows, row_groups, partials);
+  }
 }
 
 template <int KB, int VB>
@@ -636,7 +893,19 @@ hipError_t launch_bits(const AttnLaunch &p, hipStream_t stream) {
 
 }  // namespace
 
-#if KVQ_SHORT_PAGED || KVQ_SHORT_META16
+#if KVQ_SHORT_TOK
+#if KVQ_SHORT_PAGED
+hipError_t launch_attention_short_tok_paged(const AttnLaunch &p, hipStream_t stream) {
+#else
+hipError_t launch_attention_short_tok(const AttnLaunch &p, hipStream_t stream) {
+#endif
+  const int kb = p.Nc > 0 ? p.kbits : 2, vb = p.Nc > 0 ? p.vbits : 2;
+  if (kb == 2 && vb == 2) return launch_bits<2, 2>(p, stream);
+  if (kb == 2 && vb == 4) return launch_bits<2, 4>(p, stream);
+  if (kb == 4 && vb == 2) return launch_bits<4, 2>(p, stream);
+  return launch_bits<4, 4>(p, stream);
+}
+#elif KVQ_SHORT_PAGED || KVQ_SHORT_META16
 #if KVQ_SHORT_PAGED && KVQ_SHORT_META16 == 2
 hipError_t launch_attention_short_fast_mb16_paged(const AttnLaunch &p, hipStream_t stream) {
 #elif KVQ_SHORT_META16 == 2
@@ -659,6 +928,13 @@ hipError_t launch_attention_short_fast_m16(const AttnLaunch &p, hipStream_t stre
 // (paged) pages that hold whole 32-key blocks.
 bool short_fast_supported(int32_t d, int corr, bool tokens_axis, int32_t page_size) {
   return d == D && corr != KV_CORR_EXACT && !tokens_axis && (page_size == 0 || page_size >= BK);
+}
+
+// Caches grouped along the tokens on the 32-row tiles: as short_fast_supported
+// with fp32 metadata (K, V or both along the tokens).
+bool short_tok_supported(int32_t d, int corr, bool ktok, bool vtok, int32_t page_size, int meta) {
+  return d == D && corr != KV_CORR_EXACT && (ktok || vtok) && (page_size == 0 || page_size >= BK) &&
+         meta == kMetaF32;
 }
 
 int short_fast_splits(int64_t B, int64_t Hkv, int64_t rows_per_kvhead, int64_t Nc, int64_t Ncur, int cu_count) {

@@ -328,7 +328,9 @@ Plan plan_attention(const kv_attn_args *a, bool query_device, size_t limit = SIZ
     const int cus = query_device ? device_cu_count() : 256;
     const bool fast = kvq::short_fast_supported(a->d, a->corr, tokens_axis(a), cache_page_size(a)) ||
                       kvq::short16_tok_supported(a->d, a->corr, k_tokens(a), v_tokens(a), cache_page_size(a),
-                                                 a->Nc > 0 ? static_cast<int>(a->k_cache->meta) : 0, rows);
+                                                 a->Nc > 0 ? static_cast<int>(a->k_cache->meta) : 0, rows) ||
+                      kvq::short_tok_supported(a->d, a->corr, k_tokens(a), v_tokens(a), cache_page_size(a),
+                                               a->Nc > 0 ? static_cast<int>(a->k_cache->meta) : 0);
     auto bytes = [&](int s) {
       return fast ? kvq::short_path_workspace_bytes(a->B, a->Hq, a->Nq, a->d, s)
                   : kvq::general_path_workspace_bytes(a->B, a->Hq, a->Hkv, a->Nq, a->d, s, true);

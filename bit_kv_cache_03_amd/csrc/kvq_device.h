@@ -164,10 +164,10 @@ __device__ inline void pin(T &x) {
 // (N_hi, N_hi, N_lo, 0, S_hi, S_lo, 0, 0) with the group sum
 // S_g = sum_{c in g} q_c 2^-eq, which the centres of centred cached keys
 // multiply (see group_centre); half 1 is zero with one group.  The row's
-// other half sits in lane l^32.
+// other half sits in lane l^32.  qun (when given) receives 2^eq.
 template <bool TAYLOR, bool HALVES = false>
 __device__ inline void load_query(const uint16_t *qptr, int h, int group_shift, float tau, int ek, f16x8 (&q)[8],
-                                  bf16x8 &qext, float &alpha) {
+                                  bf16x8 &qext, float &alpha, float *qun = nullptr) {
   const int ng = 128 >> group_shift;
   uint4 qw[8];
   float nsum[4] = {0.f, 0.f, 0.f, 0.f}, qsum[2] = {0.f, 0.f};
@@ -203,6 +203,7 @@ __device__ inline void load_query(const uint16_t *qptr, int h, int group_shift, 
   }
   const float unscale = ldexpf(1.0f, eq + ek);
   alpha = tau * kLog2e * unscale;
+  if (qun) *qun = ldexpf(1.0f, eq);
   float nh[4], nl[4];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {

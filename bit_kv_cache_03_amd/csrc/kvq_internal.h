@@ -219,6 +219,11 @@ hipError_t launch_attention_short16_mb16_paged(const AttnLaunch &p, hipStream_t 
 bool short16_tok_supported(int32_t d, int corr, bool ktok, bool vtok, int32_t page_size, int meta,
                            int64_t rows_per_kvhead);
 hipError_t launch_attention_short16_tok(const AttnLaunch &p, hipStream_t stream);
+// The 32-row kernel over caches grouped along the tokens (fp32 metadata;
+// attention_short_tok*.hip), for calls the 16-row kernel does not take.
+bool short_tok_supported(int32_t d, int corr, bool ktok, bool vtok, int32_t page_size, int meta);
+hipError_t launch_attention_short_tok(const AttnLaunch &p, hipStream_t stream);
+hipError_t launch_attention_short_tok_paged(const AttnLaunch &p, hipStream_t stream);
 hipError_t launch_attention_short16_vtok(const AttnLaunch &p, hipStream_t stream);
 hipError_t launch_attention_short16_vtok_paged(const AttnLaunch &p, hipStream_t stream);
 hipError_t launch_attention_short16_ktok(const AttnLaunch &p, hipStream_t stream);

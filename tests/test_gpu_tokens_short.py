@@ -1,6 +1,7 @@
-"""Caches grouped along the tokens (per channel) with at most 16 query rows
-per KV head: the 16-row short-query kernel's token-axis instances, on the
-GPU against the oracle.
+"""Caches grouped along the tokens (per channel) on the short-query path: the
+16-row kernel's token-axis instances (at most 16 query rows per KV head) and
+the 32-row kernel's (more rows, fp32 metadata), on the GPU against the
+oracle.
 
 Keys along the tokens (KIVI-style, values along the head dimension): the
 kernel folds each token group's steps into the query and feeds the raw
@@ -57,7 +58,6 @@ def _caches(w, data, meta="f32", page=0, seed=0, kaxis="tokens", vaxis="dim"):
 
 def _compare(orc, w, corr, splits=0, causal=False, meta="f32", page=0, kaxis="tokens", vaxis="dim"):
     import _gpu
-    assert w.Nq * (w.Hq // w.Hkv) <= 16
     data = W.generate(w)
     print(f"[tokens short] B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Ncur={w.Ncur} Nc={w.Nc} bits={w.kbits}/{w.vbits} "
           f"group={w.group} corr={corr} splits={splits} causal={causal} meta={meta} page={page} "
@@ -184,3 +184,54 @@ def test_values_along_tokens_paged(orc, axes, page):
 def test_values_along_tokens_meta16_general(orc, meta):
     """16-bit metadata with values along the tokens stays on the general kernel."""
     _compare(orc, CASES["gqa_chunk4_g32"], "taylor", meta=meta, kaxis="tokens", vaxis="tokens")
+
+
+# More than 16 query rows per KV head: the 32-row tiles (row groups of 32).
+ROWS32 = {
+    "gqa_rows20_g64": GQA.scaled(B=2, Hq=8, Hkv=2, Nq=5, Ncur=5, Nc=900, group=64),
+    "gqa_rows32_g32": GQA.scaled(B=2, Hq=8, Hkv=2, Nq=8, Ncur=8, Nc=700, group=32),
+    "gqa_rows64_g128": GQA.scaled(B=1, Hq=8, Hkv=2, Nq=16, Ncur=16, Nc=1100, group=128),
+    "int4_rows40_ragged": H24.scaled(B=1, Hq=2, Hkv=2, Nq=40, Ncur=23, Nc=513, group=64),
+    "outliers_rows24": OUT.scaled(Hq=4, Hkv=2, Nq=12, Ncur=12, Nc=800, group=64),
+    "longvideo_rows17": LV.scaled(Hq=1, Hkv=1, Nq=17, Ncur=17, Nc=1000, group=64),
+    "small_cache_rows24": GQA.scaled(B=2, Hq=8, Hkv=2, Nq=6, Ncur=6, Nc=20, group=32),
+}
+AXES3 = [("tokens", "dim"), ("tokens", "tokens"), ("dim", "tokens")]
+
+
+@pytest.mark.parametrize("axes", AXES3)
+@pytest.mark.parametrize("case", sorted(ROWS32))
+@pytest.mark.parametrize("corr", ["off", "taylor"])
+def test_rows32(orc, axes, case, corr):
+    _compare(orc, ROWS32[case], corr, kaxis=axes[0], vaxis=axes[1])
+
+
+@pytest.mark.parametrize("axes", AXES3)
+@pytest.mark.parametrize("kbits,vbits", [(2, 4), (4, 2)])
+def test_rows32_bits_splits_causal(orc, axes, kbits, vbits):
+    w = GQA.scaled(B=2, Hq=8, Hkv=2, Nq=8, Ncur=11, Nc=600, group=64, kbits=kbits, vbits=vbits)
+    _compare(orc, w, "taylor", splits=3, kaxis=axes[0], vaxis=axes[1])
+    _compare(orc, w, "taylor", splits=0, causal=True, kaxis=axes[0], vaxis=axes[1])
+
+
+@pytest.mark.parametrize("axes", AXES3)
+def test_rows32_paged_matches_contiguous(orc, axes):
+    import _gpu
+    w = GQA.scaled(B=3, Hq=8, Hkv=2, Nq=6, Ncur=6, Nc=700, group=64)
+    data = W.generate(w)
+    a = _compare(orc, w, "taylor", page=128, kaxis=axes[0], vaxis=axes[1])
+    kc, vc = _caches(w, data, kaxis=axes[0], vaxis=axes[1])
+    b = _gpu.run_attention(w, data, kc, vc, corr="taylor", path="short")
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_rows_above_64_forced_short(orc):
+    """A forced short path at 100 rows per KV head: four row groups."""
+    w = H24.scaled(B=1, Hq=2, Hkv=2, Nq=100, Ncur=100, Nc=400, group=64)
+    _compare(orc, w, "taylor", kaxis="tokens", vaxis="tokens")
+
+
+@pytest.mark.parametrize("meta", ["f16", "bf16"])
+def test_rows32_meta16_general(orc, meta):
+    """16-bit metadata above 16 rows stays on the general kernel."""
+    _compare(orc, ROWS32["gqa_rows20_g64"], "taylor", meta=meta, kaxis="tokens", vaxis="dim")
