@@ -207,8 +207,8 @@ __global__ __launch_bounds__(256) void key_scale_kernel(AttnLaunch p, int32_t ng
     // the rows are all of (b, KV head) bkv: one atomic per cache for the workgroup
     const float rk = block_max<NT>(rb.k, red, tid), rv = block_max<NT>(rb.v, red, tid);
     if (tid == 0) {
-      if (p.app.bound[0] && rk > 0.f) atomicMax(reinterpret_cast<int *>(p.app.bound[0]) + bkv, __float_as_int(rk));
-      if (p.app.bound[1] && rv > 0.f) atomicMax(reinterpret_cast<int *>(p.app.bound[1]) + bkv, __float_as_int(rv));
+      if (p.app.bound[0]) qdev::bound_max(p.app.bound[0], bkv, rk);
+      if (p.app.bound[1]) qdev::bound_max(p.app.bound[1], bkv, rv);
     }
   } else if (p.Ncur > 0) {
     const int64_t n = p.Ncur * D / 8, lo = n * ch / KCHUNKS, hi = n * (ch + 1) / KCHUNKS;

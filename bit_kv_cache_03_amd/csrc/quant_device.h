@@ -115,10 +115,19 @@ __device__ inline float group_bound(float step, float zp) {
   return fmaxf(fabsf(zp), fabsf(fmaf(step, static_cast<float>((1 << BITS) - 1), zp)));
 }
 
-// Raise the running bound of (b, h) = entry i to b (b >= 0, so the order of
-// the float bits is that of the integers: one atomic max).  Every lane of
-// the wave must call this together: when all lanes name the same entry the
-// wave maximum goes in with one atomic, otherwise each lane adds its own.
+// Raise entry i of a running bound to b (b >= 0, so the order of the float
+// bits is that of the integers: one atomic max), only when b exceeds the
+// value read first.  The bound never falls, so a stale read can only be
+// lower than the entry: it may cost a needless atomic, never a lost raise;
+// and the many waves that write one entry (a long append) stop contending
+// for it once it holds their group's maximum.
+__device__ inline void bound_max(float *bound, int64_t i, float b) {
+  if (b > 0.f && b > __builtin_nontemporal_load(bound + i)) atomicMax(reinterpret_cast<int *>(bound) + i, __float_as_int(b));
+}
+
+// Raise the running bound of (b, h) = entry i to b.  Every lane of the wave
+// must call this together: when all lanes name the same entry the wave
+// maximum goes in from one lane, otherwise each lane raises its own.
 __device__ inline void raise_bound(float *bound, int64_t i, float b) {
   if (!bound) return;
   const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(i));
@@ -127,9 +136,9 @@ __device__ inline void raise_bound(float *bound, int64_t i, float b) {
   if (__all(i == i0)) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) b = fmaxf(b, __shfl_xor(b, o, 64));
-    if (__lane_id() == 0 && b > 0.f) atomicMax(reinterpret_cast<int *>(bound) + i0, __float_as_int(b));
-  } else if (b > 0.f) {
-    atomicMax(reinterpret_cast<int *>(bound) + i, __float_as_int(b));
+    if (__lane_id() == 0) bound_max(bound, i0, b);
+  } else {
+    bound_max(bound, i, b);
   }
 }
 
@@ -246,8 +255,8 @@ __device__ void append_rows_t(const AttnLaunch &p, int64_t r0, int64_t r1, bool 
         }
         if (chunk == 0) {
           if (bkv != cur) {  // the lane's rows crossed into the next (b, KV head): hand the last one over
-            if (a.bound[0] && kbnd > 0.f) atomicMax(reinterpret_cast<int *>(a.bound[0]) + cur, __float_as_int(kbnd));
-            if (a.bound[1] && vbnd > 0.f) atomicMax(reinterpret_cast<int *>(a.bound[1]) + cur, __float_as_int(vbnd));
+            if (a.bound[0]) bound_max(a.bound[0], cur, kbnd);
+            if (a.bound[1]) bound_max(a.bound[1], cur, vbnd);
             cur = bkv;
             kbnd = vbnd = 0.f;
           }

@@ -51,7 +51,20 @@ __global__ __launch_bounds__(kThreads) void quantize_pack(
 
   float step, zp;
   const uint32_t packed = quantize8<BITS, LANES, MT>(v, step, zp);
-  raise_bound(bound, bh, live ? group_bound<BITS>(step, zp) : 0.f);  // the block's (b, h)
+  if (bound) {  // the workgroup's largest group bound (all its lanes are of (b, h)), raised once
+    __shared__ float red[kThreads / 64];
+    float gb = live ? group_bound<BITS>(step, zp) : 0.f;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) gb = fmaxf(gb, __shfl_xor(gb, o, 64));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = gb;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float m = red[0];
+#pragma unroll
+      for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, red[w]);
+      bound_max(bound, bh, m);
+    }
+  }
 
   if (!live) return;
   const int64_t orow = layout.row(cap, H, blockIdx.z, blockIdx.y, off + n);  // the cache row of token off + n
