@@ -322,7 +322,18 @@ Plan plan_attention(const kv_attn_args *a, bool query_device, size_t limit = SIZ
   Plan pl{KV_PATH_LONG, 0, 0, 0};
   const int64_t rows = a->Nq * (a->Hq / a->Hkv);
   int path = a->path;
-  if (path == KV_PATH_AUTO) path = (rows <= kShortRows && a->Nc > 0) ? KV_PATH_SHORT : KV_PATH_LONG;
+  if (path == KV_PATH_AUTO) {
+    // caches grouped along the tokens take the short-query kernels at any row
+    // count where they can (the throughput kernel takes head-dimension groups
+    // only, and the general kernel is 2-2.5x slower than row groups of 32 on
+    // the short-query tiles)
+    const int meta = a->Nc > 0 ? static_cast<int>(a->k_cache->meta) : 0;
+    const bool tok_short = tokens_axis(a) &&
+                           (kvq::short16_tok_supported(a->d, a->corr, k_tokens(a), v_tokens(a), cache_page_size(a),
+                                                       meta, rows) ||
+                            kvq::short_tok_supported(a->d, a->corr, k_tokens(a), v_tokens(a), cache_page_size(a), meta));
+    path = ((rows <= kShortRows || tok_short) && a->Nc > 0) ? KV_PATH_SHORT : KV_PATH_LONG;
+  }
   pl.path = path;
   if (path == KV_PATH_SHORT) {
     const int cus = query_device ? device_cu_count() : 256;

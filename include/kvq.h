@@ -104,7 +104,8 @@ typedef enum KV_ENUM_TYPE {
 
 /* Kernel path.  AUTO picks by rows per KV head; tests may force either. */
 typedef enum KV_ENUM_TYPE {
-  KV_PATH_AUTO = 0,
+  KV_PATH_AUTO = 0,  /* SHORT for at most 64 query rows per KV head, and for caches grouped
+                        along the tokens that the short-query kernels take; else LONG */
   KV_PATH_LONG = 1,  /* MFMA tile kernel, query rows tiled, one pass over keys */
   KV_PATH_SHORT = 2  /* split over cached tokens + log-sum-exp combine */
 } kv_path;

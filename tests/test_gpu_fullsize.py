@@ -7,7 +7,9 @@ the oracle computed row by row.  Same bar as the small parity tests: max
 |out - ref| <= 2e-2 against the fp64 oracle, mean |out - bf16(ref)| <= 1e-3.
 
 Also the short-query regime on the GQA workload's cache (few query rows per
-KV head, the split-over-cache path)."""
+KV head, the split-over-cache path), with the cache grouped along the head
+dimension and, at decode sizes, along the tokens (the 16-row kernel's
+token-axis instances)."""
 import numpy as np
 import pytest
 
@@ -23,15 +25,16 @@ def _bits_equal(a, b):
     return np.array_equal(np.ascontiguousarray(a).view(np.uint8), np.ascontiguousarray(b).view(np.uint8))
 
 
-def _run(orc, w, corrs, nsample=48, check_cache=True):
+def _run(orc, w, corrs, nsample=48, check_cache=True, kaxis="dim", vaxis="dim"):
     import _gpu
     print(f"[fullsize] {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Ncur={w.Ncur} Nc={w.Nc} "
-          f"bits={w.kbits}/{w.vbits}", flush=True)
+          f"bits={w.kbits}/{w.vbits} axes={kaxis}/{vaxis}", flush=True)
     data = W.generate(w)
-    kc = _gpu.build_cache(w, data["kc"], w.kbits, cap=w.Nc + w.Ncur)
-    vc = _gpu.build_cache(w, data["vc"], w.vbits, cap=w.Nc + w.Ncur)
-    okc = orc.quantize(data["kc"], w.kbits, w.group)
-    ovc = orc.quantize(data["vc"], w.vbits, w.group)
+    cap = -(-(w.Nc + w.Ncur) // w.group) * w.group  # whole token groups
+    kc = _gpu.build_cache(w, data["kc"], w.kbits, cap=cap, axis=kaxis)
+    vc = _gpu.build_cache(w, data["vc"], w.vbits, cap=cap, axis=vaxis)
+    okc = orc.quantize(data["kc"], w.kbits, w.group, axis=kaxis)
+    ovc = orc.quantize(data["vc"], w.vbits, w.group, axis=vaxis)
     if check_cache:
         for gc, ref, name in ((kc, okc, "K"), (vc, ovc, "V")):
             got = _gpu.cache_to_host(gc, w.Nc)
@@ -43,7 +46,7 @@ def _run(orc, w, corrs, nsample=48, check_cache=True):
         out = _gpu.run_attention(w, data, kc, vc, corr=corr)
         got = _gpu.out_rows(out, rows)
         prob = orc.Problem(as_bf16(data["q"]), as_bf16(data["k"]), as_bf16(data["v"]), okc, ovc, w.Nc,
-                           w.kbits, w.vbits, w.group, corr=corr)
+                           w.kbits, w.vbits, w.group, corr=corr, kaxis=kaxis, vaxis=vaxis)
         ref = prob.attention(rows=rows)
         _gpu.check(got, ref, label=f"{corr:7s} rows={rows.size} ")
 
@@ -60,3 +63,21 @@ def test_short_query_on_gqa_cache(orc, nq):
     query rows per KV head)."""
     w = W.WORKLOADS["gqa_prefill_b16_cache32k"].scaled(Nq=nq, Ncur=nq)
     _run(orc, w, ("taylor", "exact"), nsample=64, check_cache=False)
+
+
+@pytest.mark.parametrize("axes", [("tokens", "dim"), ("tokens", "tokens")])
+@pytest.mark.parametrize("nq", [1, 4])
+def test_tokens_short_query_on_gqa_cache(orc, axes, nq):
+    """Decode (4 and 16 query rows per KV head) over the full 32k-token GQA
+    cache grouped along the tokens, 64 tokens per group."""
+    w = W.WORKLOADS["gqa_prefill_b16_cache32k"].scaled(Nq=nq, Ncur=nq)
+    _run(orc, w, ("taylor", "off"), nsample=64, check_cache=False, kaxis=axes[0], vaxis=axes[1])
+
+
+@pytest.mark.parametrize("wname,axes", [("h24_int4_cache16k", ("tokens", "dim")), ("h24_int4_cache16k", ("tokens", "tokens")),
+                                        ("gqa_prefill_b16_cache32k", ("tokens", "dim"))])
+def test_tokens_prefill_full(orc, wname, axes):
+    """Prefill at full size on caches grouped along the tokens (64 tokens per
+    group), in the path the library picks (the short-query tiles)."""
+    w = W.WORKLOADS[wname].scaled(group=64)
+    _run(orc, w, (w.corr,), nsample=48, check_cache=False, kaxis=axes[0], vaxis=axes[1])

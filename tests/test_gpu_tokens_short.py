@@ -235,3 +235,18 @@ def test_rows_above_64_forced_short(orc):
 def test_rows32_meta16_general(orc, meta):
     """16-bit metadata above 16 rows stays on the general kernel."""
     _compare(orc, ROWS32["gqa_rows20_g64"], "taylor", meta=meta, kaxis="tokens", vaxis="dim")
+
+
+@pytest.mark.parametrize("axes", AXES3)
+def test_prefill_auto_path(orc, axes):
+    """300 rows per KV head with the path left to the library: caches grouped
+    along the tokens run on the short-query tiles (ten row groups), not on
+    the general kernel."""
+    import _gpu
+    w = H24.scaled(B=1, Hq=2, Hkv=2, Nq=300, Ncur=300, Nc=700, group=64)
+    data = W.generate(w)
+    print(f"[tokens prefill] axes={axes} Nq={w.Nq} Nc={w.Nc}", flush=True)
+    kc, vc = _caches(w, data, kaxis=axes[0], vaxis=axes[1])
+    out = _gpu.run_attention(w, data, kc, vc, corr="taylor", path="auto")
+    ref = oracle_problem(orc, w, "taylor", data=data, kaxis=axes[0], vaxis=axes[1]).attention()
+    _gpu.check(_gpu.out_rows(out), ref)
