@@ -146,19 +146,28 @@ def cpu_baseline(w, data, corr: str, target_s: float = 12.0, causal: bool = Fals
                       f"plus the chunk's quantize prorated; {t:.1f} s wall on {threads} threads"}
 
 
-def arithmetic(w, corr: str, page_size: int, kaxis: str, vaxis: str) -> dict:
+def arithmetic(w, corr: str, page_size: int, kaxis: str, vaxis: str, meta: str = "f32", path: str = "auto") -> dict:
     """The arithmetic the attention call computes in, by the kernel that
-    serves it: head dim 128 with correction off or Taylor, groups along the
-    head dimension and pages of at least one 32/64-key tile run the fp16
-    kernels; the rest runs the general kernel (bf16 hi + lo keys)."""
-    fp16 = (w.d == 128 and corr != "exact" and kaxis == "dim" and vaxis == "dim" and
-            (page_size == 0 or page_size >= 32))
+    serves it: head dim 128 with correction off or Taylor and pages of at
+    least one 32/64-key tile run the fp16 kernels (caches grouped along the
+    tokens on the short-query path: any metadata with keys alone along the
+    tokens at up to 16 rows per KV head, fp32 metadata otherwise); the rest
+    runs the general kernel (bf16 hi + lo keys)."""
+    tok = "tokens" in (kaxis, vaxis)
+    rows = w.Nq * (w.Hq // w.Hkv)
+    fp16 = w.d == 128 and corr != "exact" and (page_size == 0 or page_size >= 32)
+    if tok:
+        fp16 = fp16 and path != "long" and (meta == "f32" or (rows <= 16 and vaxis == "dim"))
     if fp16:
+        keys = ("keys grouped along the tokens enter as their codes (exact fp16 subnormals c 2^-24) against queries "
+                "scaled per channel by the token group's steps, with q.z and the per-channel Taylor bias in fp32; "
+                if kaxis == "tokens" else
+                "keys and values scaled by powers of two into the fp16 range; the correction and running-max step "
+                "on bf16 MFMA (hi + lo splits); ")
         return {"dtype": "fp16",
-                "dtype_detail": "Q K^T and P V on fp16 MFMA (v_mfma_f32_32x32x16_f16) with fp32 accumulation, "
-                                "keys and values scaled by powers of two into the fp16 range; the correction and "
-                                "running-max step on bf16 MFMA (hi + lo splits); softmax in fp32; bf16 inputs and "
-                                "outputs; INT%d keys / INT%d values dequantised in-kernel" % (w.kbits, w.vbits)}
+                "dtype_detail": "Q K^T and P V on fp16 MFMA with fp32 accumulation, " + keys +
+                                "softmax in fp32; bf16 inputs and outputs; INT%d keys / INT%d values dequantised "
+                                "in-kernel" % (w.kbits, w.vbits)}
     return {"dtype": "bf16",
             "dtype_detail": "Q K^T on bf16 MFMA with keys split into bf16 hi + lo parts, P V on fp16 MFMA, fp32 "
                             "accumulation and softmax; bf16 inputs and outputs"}
@@ -520,7 +529,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        **arithmetic(w, corr, args.page_size, args.kaxis, args.vaxis),
+        **arithmetic(w, corr, args.page_size, args.kaxis, args.vaxis, args.meta, args.path),
         "data": "synthetic: seeded N(0,1) q/k/v with the workload's key structure, bf16; cache INT%d/INT%d group %d%s" % (
             w.kbits, w.vbits, w.group, ({"f16": ", binary16 step/zero", "bf16": ", bfloat16 step/zero"}.get(args.meta, "")) +
             (f", K/V groups along {args.kaxis}/{args.vaxis}" if "tokens" in (args.kaxis, args.vaxis) else "")),

@@ -46,5 +46,12 @@ def test_dtype_names_the_arithmetic_of_the_kernel():
     w = W.WORKLOADS["gqa_prefill_b16_cache32k"]
     assert bench.arithmetic(w, "taylor", 0, "dim", "dim")["dtype"] == "fp16"
     assert bench.arithmetic(w, "exact", 0, "dim", "dim")["dtype"] == "bf16"
-    assert bench.arithmetic(w, "taylor", 0, "tokens", "dim")["dtype"] == "bf16"
     assert bench.arithmetic(W.WORKLOADS["tiny_d64_int2"], "off", 0, "dim", "dim")["dtype"] == "bf16"
+    # caches grouped along the tokens: the short-query kernels (fp16) where they serve the call
+    assert bench.arithmetic(w, "taylor", 0, "tokens", "dim")["dtype"] == "fp16"
+    assert bench.arithmetic(w, "taylor", 0, "tokens", "tokens", "f32")["dtype"] == "fp16"
+    assert bench.arithmetic(w, "taylor", 0, "tokens", "dim", "f32", "long")["dtype"] == "bf16"
+    assert bench.arithmetic(w, "taylor", 0, "tokens", "dim", "f16")["dtype"] == "bf16"  # 2048 rows per KV head
+    assert bench.arithmetic(w.scaled(Nq=4, Ncur=4), "taylor", 0, "tokens", "dim", "f16")["dtype"] == "fp16"
+    assert bench.arithmetic(w.scaled(Nq=4, Ncur=4), "taylor", 0, "tokens", "tokens", "bf16")["dtype"] == "bf16"
+    assert "subnormals" in bench.arithmetic(w, "taylor", 0, "tokens", "dim")["dtype_detail"]
