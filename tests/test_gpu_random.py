@@ -4,6 +4,8 @@ mode, path, key-range splits, causal mask, paged layout, 16-bit metadata,
 groups along the tokens), at sizes the oracle finishes in well under a
 second.  The list is fixed by its seed; each case prints its options before
 it runs."""
+import os
+
 import numpy as np
 import pytest
 
@@ -51,10 +53,14 @@ def _cases(n=600, seed=20261203):
     return out
 
 
-CASES = _cases()
+# KVQ_RANDOM_SEEDS="1,2" (and KVQ_RANDOM_N, cases per seed) swaps in other
+# lists; by default the one list above, 600 cases.
+_SEEDS = [int(x) for x in os.environ.get("KVQ_RANDOM_SEEDS", "20261203").split(",") if x]
+CASES = [c for sd in _SEEDS for c in _cases(int(os.environ.get("KVQ_RANDOM_N", "600")), sd)]
 
 
-@pytest.mark.parametrize("case", CASES, ids=[f"r{c[0]}" for c in CASES])
+@pytest.mark.parametrize("case", CASES, ids=[f"r{c[0]}" if len(_SEEDS) == 1 else f"s{j // max(1, len(CASES) // len(_SEEDS))}r{c[0]}"
+                                             for j, c in enumerate(CASES)])
 def test_random_configuration(orc, case):
     import _gpu
     i, w, corr, path, splits, causal, ps, meta, axis_k, axis_v = case
