@@ -77,6 +77,15 @@ constexpr int OS = D + 4;            // fp32 row of the merge buffer
 constexpr int MERGE = ROWS * OS + 2 * ROWS;  // floats of a wave's merge buffer (O rows, then m and l)
 constexpr int LDS_BYTES = WAVES * VT * 2 > WAVES * MERGE * 4 ? WAVES * VT * 2 : WAVES * MERGE * 4;
 constexpr int GM = 2 * D;  // floats of a wave's token-group staging of K or of V (two per channel)
+// Cached values as raw codes (groups along the head dimension): a wave's
+// per-key steps Ds (4 groups x 32 keys) and zero-point operand Zs (16 rows x
+// ZS: rows g and NG + g the hi and lo parts of group g's zero points, the
+// rest zero; 80-byte rows keep the 16 rows' reads on distinct banks), fp16.
+// kVcodeScale keeps p D 2^-ev kVcodeScale < 2^15.42 for p <= 2^8 and
+// |v| 2^-ev < 2^14 (D <= 2^15 / 3), inside the fp16 range.
+constexpr int ZS = 40;
+constexpr int VCODE_HALVES = 4 * 32 + 16 * ZS;
+constexpr float kVcodeScale = 1.0f / 64.0f;
 
 // V^T element (row = head-dim index, col = key slot 0..31); the 16-byte
 // chunks of a row are XOR-swizzled by (row / 16) % 4 so that the transposed
@@ -395,35 +404,41 @@ __device__ inline void vtok_stage(const Fetch &f, int lane, float vsc, float *Gv
       make_float2(fmaf(-1024.0f, d0, zv[0] * vsc), fmaf(-1024.0f, d1, zv[1] * vsc));
 }
 
-// V^T tile of a cached block: fp16 values v 2^-ev of keys 4kq..4kq+3 (slots
-// vslot4(kq) .. +3) at head-dim rows 16dq .. 16dq+15, one 8-byte store per
-// row.  One v_perm gathers the same code byte of two keys (bits 0..7 and
-// 16..23); one v_and_or turns a code field at bit p of both into the fp16
-// magic numbers 1024 + c 2^p (exact: the fp16 spacing at 1024 is 1); then
-// v 2^-ev = fma(1024 + c 2^p, D 2^-(p+ev), (z - 1024 D 2^-p) 2^-ev) with fp32
-// operands, one v_fma_mix per value rounded once to fp16.  INT4 fields sit
-// at p = 0 and 4; INT2 fields at p = 0 and 2 of the byte and of the byte
-// shifted right by 4.
-template <int VBITS>
-__device__ inline void unpack_v_cached(const Ctx &c, int lane, const Fetch &f, float vsc, uint16_t *Vt) {
-  constexpr int P1 = VBITS == 4 ? 4 : 2;
+// V^T tile of a cached block as raw codes, and the block's per-key value
+// operands.  The value product then needs no dequantisation per value:
+//   sum_i p_i (z_ig + D_ig c_i) = sum_i (p_i D_ig) c_i + sum_i p_i z_ig,
+// so the codes enter the MFMA as they are and each group's step D_ig rides
+// on the probabilities (one B operand per group), the zero points on one
+// extra MFMA step per block.
+//  - Codes: one v_perm gathers the same code byte of two keys (bits 0..7 and
+//    16..23), one AND keeps a code field at bit p of both: the fp16
+//    subnormals c 2^(p-24), exact.  INT4 fields sit at p = 0 and 4, INT2 at
+//    p = 0 and 2 of the byte and of the byte shifted right by 4; head-dim row
+//    16dq + NF byte + fl holds field fl, so odd rows carry 2^P1.
+//  - Per key (slots vslot4(kq) .. +3, from the first lane of each group):
+//    Ds row g = D 2^-ev kVcodeScale and Zs rows g, NG + g = z 2^-ev split
+//    into hi + lo, all fp16 (the other rows of Zs stay zero).
+template <int VBITS, int NG>
+__device__ inline void unpack_v_raw(const Ctx &c, int lane, const Fetch &f, float vsc, uint16_t *Vt, uint16_t *Ds,
+                                    uint16_t *Zs) {
   const int kq = lane & 7, dq = lane >> 3;
   const int slot = vslot4(kq);
-  float dd[4][2], zz[4][2];  // per key: operands of the fields at p = 0 and p = P1
+  constexpr int DQG = 8 / NG;  // lanes' dq values per group (16 dims each)
+  if (dq % DQG == 0) {
+    const int g = dq / DQG;
+    const float ds = vsc * kVcodeScale;
+    _Float16 zh[4], zl[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float d0 = f.vstep[i] * vsc, z0 = f.vzero[i] * vsc;
-    dd[i][0] = d0;
-    dd[i][1] = d0 * (1.0f / (1 << P1));
-    zz[i][0] = fmaf(-1024.0f, dd[i][0], z0);
-    zz[i][1] = fmaf(-1024.0f, dd[i][1], z0);
+    for (int i = 0; i < 4; ++i) {
+      const float z = f.vzero[i] * vsc;
+      zh[i] = static_cast<_Float16>(z);
+      zl[i] = static_cast<_Float16>(z - static_cast<float>(zh[i]));
+    }
+    *reinterpret_cast<uint2 *>(Ds + 32 * g + slot) =
+        make_uint2(pack2h(f.vstep[0] * ds, f.vstep[1] * ds), pack2h(f.vstep[2] * ds, f.vstep[3] * ds));
+    *reinterpret_cast<uint2 *>(Zs + ZS * g + slot) = make_uint2(pair_h(zh[0], zh[1]), pair_h(zh[2], zh[3]));
+    *reinterpret_cast<uint2 *>(Zs + ZS * (NG + g) + slot) = make_uint2(pair_h(zl[0], zl[1]), pair_h(zl[2], zl[3]));
   }
-  auto field = [&](uint32_t r, int k, uint32_t (&x)[2], int jp) {  // k: 0 (p = 0) or 1 (p = P1)
-    const uint32_t m = (r & (k ? c.vmask1 : c.vmask0)) | 0x64006400u;
-    const f16x2 h = __builtin_bit_cast(f16x2, m);
-    x[jp] = pair_h(dequant_h(static_cast<float>(h.x), dd[2 * jp][k], zz[2 * jp][k]),
-                   dequant_h(static_cast<float>(h.y), dd[2 * jp + 1][k], zz[2 * jp + 1][k]));
-  };
 #pragma unroll
   for (int byte = 0; byte < (VBITS == 4 ? 8 : 4); ++byte) {
     // INT4: d = 16dq + 2byte + {0, 1} (bytes 4.. from vw2); INT2: d = 16dq + 4byte + {0, 1, 2, 3}
@@ -440,11 +455,11 @@ __device__ inline void unpack_v_cached(const Ctx &c, int lane, const Fetch &f, f
     uint32_t x[NF][2];
 #pragma unroll
     for (int jp = 0; jp < 2; ++jp) {
-      field(r[jp], 0, x[0], jp);
-      field(r[jp], 1, x[1], jp);
+      x[0][jp] = r[jp] & c.vmask0;
+      x[1][jp] = r[jp] & c.vmask1;
       if (VBITS == 2) {
-        field(r[jp] >> 4, 0, x[NF - 2], jp);
-        field(r[jp] >> 4, 1, x[NF - 1], jp);
+        x[NF - 2][jp] = (r[jp] >> 4) & c.vmask0;
+        x[NF - 1][jp] = (r[jp] >> 4) & c.vmask1;
       }
     }
 #pragma unroll
@@ -625,6 +640,7 @@ __device__ inline void load_query(const uint16_t *qptr, int lane, float tau, f16
 
 struct Soft {
   f32x4 o[D / 16];
+  f32x4 oz;  // raw-code values: the zero points' sums (rows: Zs rows), query r
   float m, l, alpha;
 };
 
@@ -633,10 +649,13 @@ struct Soft {
 // and value exponent ev.  count < BK marks a ragged block; CORR adds the
 // correction steps.  CAUSAL: count is the lane's own (possibly <= 0), and a
 // row may have seen no key yet (m = -inf).  ADD: the row's scores add sadd.
-template <bool CORR, bool CAUSAL = false, bool ADD = false>
+// VCODE: the V^T tile holds raw codes (unpack_v_raw), with the block's steps
+// in Ds and zero points in Zs.
+template <bool CORR, bool CAUSAL = false, bool ADD = false, bool VCODE = false, int NG = 1>
 __device__ inline void block_compute(const f16x8 (&k)[2][4], const bf16x8 (&kext)[2], const uint16_t *Vt,
                                      const f16x8 (&q)[4], bf16x8 qext, int count, float alpha, int ev, int lane,
-                                     Soft &st, float sadd = 0.f) {
+                                     Soft &st, float sadd = 0.f, const uint16_t *Ds = nullptr,
+                                     const uint16_t *Zs = nullptr) {
   const float fev = static_cast<float>(ev);
   const int r = lane & 15, j = lane >> 4;
   f32x4 s[2];
@@ -666,6 +685,7 @@ __device__ inline void block_compute(const f16x8 (&k)[2][4], const bf16x8 (&kext
     st.l *= sc;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) st.o[dt] *= sc;
+    if (VCODE) st.oz *= sc;
     st.m = m_new;
   }
   const float shift = fev - st.m;
@@ -682,10 +702,46 @@ __device__ inline void block_compute(const f16x8 (&k)[2][4], const bf16x8 (&kext
                         pack2h(e[1][2], e[1][3])));
   st.l = fmaf(sum8h(pk, 0.f), ldexpf(1.0f, -ev), st.l);
   // O^T += V^T P^T: head-dim tile dt, the block's 32 keys in one k-step
+  if (VCODE) {
+    // group g's operand: the probabilities times the keys' steps (the slots
+    // 8j .. 8j+7 of Ds row g, the same for the 16 lanes of a quarter)
+    f16x8 pg[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) pg[g] = pk * *reinterpret_cast<const f16x8 *>(Ds + 32 * g + 8 * j);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+      st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+          *reinterpret_cast<const f16x8 *>(Vt + vts(16 * dt + r, 8 * j)), pg[(16 * dt * NG) / D], st.o[dt], 0, 0, 0);
+    st.oz = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const f16x8 *>(Zs + ZS * r + 8 * j), pk, st.oz,
+                                                   0, 0, 0);
+  } else {
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+      st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+          *reinterpret_cast<const f16x8 *>(Vt + vts(16 * dt + r, 8 * j)), pk, st.o[dt], 0, 0, 0);
+  }
+}
+
+// Raw-code values: the accumulators of the cached blocks back to the units
+// of dequantised values, o = o_codes 2^(24-p) / kVcodeScale + the group's
+// zero-point sum (p = P1 on odd head-dim rows), before the current chunk's
+// blocks add to them.
+template <int VBITS, int NG>
+__device__ inline void vcode_finish(Soft &st, int lane) {
+  constexpr int P1 = VBITS == 4 ? 4 : 2;
+  const int r = lane & 15;
+  float zs[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    // rows g (hi) and NG + g (lo) of the query's column: lane 16 (row / 4) + r, element row % 4
+    const int hrow = g, lrow = NG + g;
+    zs[g] = __shfl(st.oz[hrow & 3], 16 * (hrow >> 2) + r, 64) + __shfl(st.oz[lrow & 3], 16 * (lrow >> 2) + r, 64);
+  }
+  const float f0 = 16777216.0f / kVcodeScale, f1 = f0 * (1.0f / (1 << P1));
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt)
-    st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const f16x8 *>(Vt + vts(16 * dt + r, 8 * j)),
-                                                      pk, st.o[dt], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st.o[dt][i] = fmaf(st.o[dt][i], (i & 1) ? f1 : f0, zs[(16 * dt * NG) / D]);
 }
 
 // KTOK / VTOK: keys / values grouped along the tokens (p.group is then also
@@ -696,7 +752,10 @@ template <int KBITS, int VBITS, bool TAYLOR, int NG, bool CAUSAL, bool PAGED, in
 __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, int64_t rows_per_kvhead,
                                                                   int32_t nsplit, float *ws) {
   constexpr bool TOK = KTOK || VTOK;
-  __shared__ __attribute__((aligned(16))) uint16_t L[(LDS_BYTES + (TOK ? WAVES * 2 * GM * 4 : 0)) / 2];
+  constexpr bool VCODE = !VTOK;  // cached values as raw codes
+  constexpr int TOK_BYTES = TOK ? WAVES * 2 * GM * 4 : 0;
+  __shared__ __attribute__((aligned(16)))
+  uint16_t L[(LDS_BYTES + TOK_BYTES + (VCODE ? WAVES * VCODE_HALVES * 2 : 0)) / 2];
 
   const int tid = threadIdx.x;
   if (blockIdx.x >= p.app.wg0) {  // the chunk append's workgroups
@@ -728,6 +787,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
   load_query<TAYLOR, NG>(p.q + qrow * D, lane, p.tau, q, qext, st.alpha, qun);
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.oz = f32x4{0.f, 0.f, 0.f, 0.f};
   st.m = -INFINITY;
   st.l = 0.f;
 
@@ -777,6 +837,11 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
   uint16_t *Vt = L + wave * VT;
   float *Gm = reinterpret_cast<float *>(L + WAVES * VT) + wave * 2 * GM;  // token-group staging of K
   float *Gv = Gm + GM;                                                     // and of V
+  uint16_t *Ds = L + (LDS_BYTES + TOK_BYTES) / 2 + wave * VCODE_HALVES;
+  uint16_t *Zs = Ds + 4 * 32;
+  if (VCODE) {  // rows 2 NG .. 15 of Zs stay zero (16 rows x 80 bytes: 80 chunks of 16)
+    for (int ch = lane; ch < 16 * ZS / 8; ch += 64) *reinterpret_cast<uint4 *>(Zs + 8 * ch) = make_uint4(0u, 0u, 0u, 0u);
+  }
 
   // blocks dealt round-robin, or (groups along the tokens) in contiguous
   // ranges per wave
@@ -826,7 +891,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
       if (newg) vtok_stage<VBITS, MT>(f, lane, sc.vscale, Gv);
       unpack_v_tok<VBITS>(c, lane, f, Gv, Vt);
     } else {
-      unpack_v_cached<VBITS>(c, lane, f, sc.vscale, Vt);
+      unpack_v_raw<VBITS, NG>(c, lane, f, sc.vscale, Vt, Ds, Zs);
     }
     if (newg) gcur = k0 >> gshift;
     if (blk + bstep < cend) {
@@ -835,11 +900,14 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
                                                             (kn >> gshift) != (k0 >> gshift));
     }
     if (KTOK)
-      block_compute<false, false, true>(kreg, kext, Vt, qk, qext, count, alpha_g, sc.ev, lane, st, sadd);
+      block_compute<false, false, true, VCODE, NG>(kreg, kext, Vt, qk, qext, count, alpha_g, sc.ev, lane, st, sadd,
+                                                   Ds, Zs);
     else
-      block_compute<TAYLOR || kCentre<NG>>(kreg, kext, Vt, q, qext, count, sc.alpha, sc.ev, lane, st);
+      block_compute<TAYLOR || kCentre<NG>, false, false, VCODE, NG>(kreg, kext, Vt, q, qext, count, sc.alpha, sc.ev,
+                                                                      lane, st, 0.f, Ds, Zs);
     if (PAGED && blk + 2 * bstep < cend) prn = block_row<PAGED>(c, (blk + 2 * bstep) * BK);
   }
+  if (VCODE) vcode_finish<VBITS, NG>(st, lane);
   for (; blk < wend; blk += bstep) {
     const int k0 = (blk - nbc) * BK;
     int count = c.ncur - k0 < BK ? c.ncur - k0 : BK;
