@@ -624,7 +624,7 @@ constexpr float kShrink = 0.0009765625f;     // 2^-10
 template <bool MASK, bool QK>
 __device__ inline void fix_growth(const f32x16 (&s)[2], f32x16 (&sn)[2], QState &qs, Soft &st, float l0, int count,
                                   int h, f16x8 (&pk)[4]) {
-  const float lt = st.l + __shfl_xor(st.l, 32, 64);
+  const float lt = xor32_sum(st.l);
   const bool need = !(lt < kGrowth && (lt > kShrink || (MASK && lt == 0.f && count <= 0)));
   if (!__any(need)) return;
   float mt = -INFINITY;
@@ -633,7 +633,7 @@ __device__ inline void fix_growth(const f32x16 (&s)[2], f32x16 (&sn)[2], QState 
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       if (!MASK || kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3) < count) mt = fmaxf(mt, s[kb][i]);
-  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+  mt = xor32_max(mt);
   const float m_new = set_max_slots(qs, need && mt > -INFINITY ? st.m + mt : st.m, h);
   const float shift = m_new - st.m;
   // A shrink (shift < 0) only happens to a row whose sum was still empty, so

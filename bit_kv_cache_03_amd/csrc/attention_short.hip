@@ -566,7 +566,7 @@ __device__ inline void block_compute(const f16x8 (&k)[8], bf16x8 kext, const uin
   float mt = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[i]);
-  mt = fmaf(fmaxf(mt, __shfl_xor(mt, 32, 64)), alpha, fev);
+  mt = fmaf(xor32_max(mt), alpha, fev);
   const bool grow = mt > st.m + kLazy;
   if (__any(grow)) {
     const float m_new = grow ? mt : st.m;

@@ -212,6 +212,133 @@ __device__ inline void fetch_cached(const Ctx &c, int k0, const Lanes &o, Fetch 
   }
 }
 
+// ---- staged fetch: cached blocks through per-wave LDS stages ----------------
+// A register prefetch keeps one block in flight per wave, and only while the
+// block before it is being multiplied: too few bytes in flight to cover the
+// HBM latency with two waves per SIMD.  Instead each wave streams its blocks
+// through two LDS stages filled by buffer loads that write LDS directly
+// (buffer_load ... lds: lane l of a 16-byte load lands at 16 l past the
+// address in M0, of a 4-byte load at 4 l), so two blocks are in flight
+// while a third is unpacked and multiplied, and no registers are held for
+// them.  A stage mirrors the block's bytes in HBM: K codes, V codes, then
+// the four step / zero-point arrays (each padded to 256 bytes, the span of
+// one 4-byte load); rows past the segment end read as zero.
+//
+// The loads are issued from inline assembly, so the compiler's wait
+// counting does not see them (it would otherwise wait for every load into
+// LDS before any LDS read it cannot tell apart from the stages, the V^T
+// tile's included); the kernel waits for a stage itself (s_waitcnt vmcnt
+// with the count of the loads issued after the stage's own, which every
+// step issues in the same number, past-the-end blocks as empty ranges).
+// Each asm block saves and restores M0, keeps the 5 wait states between an
+// SGPR written by the VALU and a memory instruction reading it, and the one
+// between writing M0 and a load into LDS.
+template <int KBITS, int VBITS, int NG, int MT>
+struct StageLayout {
+  static constexpr uint32_t KROW = D * KBITS / 8, VROW = D * VBITS / 8, ES = MT ? 2 : 4;
+  static constexpr uint32_t KC = BK * KROW, VC = BK * VROW;     // code bytes (multiples of 1 KB)
+  static constexpr uint32_t MB = BK * NG * ES;                  // bytes of one metadata array
+  static constexpr uint32_t MR = MB < 256 ? 256 : MB;           // its region
+  static constexpr uint32_t KS = KC + VC, KZ = KS + MR, VSC = KZ + MR, VZ = VSC + MR;
+  static constexpr uint32_t BYTES = VZ + MR;
+  static constexpr int LOADS = (KC + VC) / 1024 + 4 * (MR / 256);  // load instructions per block
+};
+
+// Buffer descriptor words over `bytes` bytes at p (stride 0, the same flags
+// as buffer_at).
+__device__ inline u32x4 rsrc_words(const void *p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  return u32x4{static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+__device__ inline uint32_t lds_addr(const uint8_t *p) {
+  return static_cast<uint32_t>(reinterpret_cast<size_t>((__attribute__((address_space(3))) const void *)(p)));
+}
+// One load into LDS at lds (wave-uniform), lane offset voff.  WAIT: first
+// wait for the wave's outstanding LDS reads (the stage being refilled was
+// just read).
+#define KVQ_DMA_ASM(WAITSTR, LOAD)                                                                              \
+  asm volatile(WAITSTR "s_mov_b32 %[t], m0\n\ts_nop 4\n\ts_mov_b32 m0, %[a]\n\ts_nop 0\n\t" LOAD            \
+                       " %[v], %[r], 0 offen lds\n\ts_nop 0\n\ts_mov_b32 m0, %[t]"                                 \
+               : [t] "=&s"(saved)                                                                               \
+               : [a] "s"(a), [v] "v"(voff), [r] "s"(rs)                                                         \
+               : "memory")
+template <int BYTES, bool WAIT>
+__device__ inline void dma(u32x4 rs, const uint8_t *lds, uint32_t voff) {
+  static_assert(BYTES == 16 || BYTES == 4, "16- or 4-byte loads");
+  uint32_t saved;
+  const uint32_t a = lds_addr(lds);
+  if (BYTES == 16 && WAIT) KVQ_DMA_ASM("s_waitcnt lgkmcnt(0)\n\t", "buffer_load_dwordx4");
+  if (BYTES == 16 && !WAIT) KVQ_DMA_ASM("", "buffer_load_dwordx4");
+  if (BYTES == 4 && WAIT) KVQ_DMA_ASM("s_waitcnt lgkmcnt(0)\n\t", "buffer_load_dword");
+  if (BYTES == 4 && !WAIT) KVQ_DMA_ASM("", "buffer_load_dword");
+}
+#undef KVQ_DMA_ASM
+
+// Starts the loads of the cached block at rows [r0, r0 + 32) (rows: rows
+// left in the segment from r0, 0 for an empty range) into the wave's stage
+// st, after the wave's outstanding LDS reads.
+template <int KBITS, int VBITS, int NG, int MT>
+__device__ inline void stage_issue(const Ctx &c, size_t r0, uint32_t rows, const uint8_t *st, int lane) {
+  using SL = StageLayout<KBITS, VBITS, NG, MT>;
+  const uint32_t l16 = static_cast<uint32_t>(lane) * 16, l4 = static_cast<uint32_t>(lane) * 4;
+  const u32x4 kc = rsrc_words(c.kc_codes + r0 * SL::KROW, rows * SL::KROW);
+  dma<16, true>(kc, st, l16);
+#pragma unroll
+  for (uint32_t i = 1; i < SL::KC / 1024; ++i) dma<16, false>(kc, st + 1024 * i, l16 + 1024 * i);
+  const u32x4 vc = rsrc_words(c.vc_codes + r0 * SL::VROW, rows * SL::VROW);
+#pragma unroll
+  for (uint32_t i = 0; i < SL::VC / 1024; ++i) dma<16, false>(vc, st + SL::KC + 1024 * i, l16 + 1024 * i);
+  const uint32_t mbytes = rows * NG * SL::ES;
+  const u32x4 m[4] = {rsrc_words(meta_adv<MT>(c.kc_scale, r0 * NG), mbytes),
+                      rsrc_words(meta_adv<MT>(c.kc_zero, r0 * NG), mbytes),
+                      rsrc_words(meta_adv<MT>(c.vc_scale, r0 * NG), mbytes),
+                      rsrc_words(meta_adv<MT>(c.vc_zero, r0 * NG), mbytes)};
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (uint32_t i = 0; i < SL::MR / 256; ++i) dma<4, false>(m[a], st + SL::KS + a * SL::MR + 256 * i, l4 + 256 * i);
+}
+
+template <int MT>
+__device__ inline float lds_meta(const uint8_t *p) {
+  if (MT != kMetaF32) return meta16_value(*reinterpret_cast<const uint16_t *>(p), MT);
+  return *reinterpret_cast<const float *>(p);
+}
+
+// The lane's share of a staged block, at the offsets fetch_cached loads it
+// from HBM.
+template <int KBITS, int VBITS, int NG, int MT, bool VCODES = true>
+__device__ inline void stage_read(const uint8_t *st, const Lanes &o, Fetch &f) {
+  using SL = StageLayout<KBITS, VBITS, NG, MT>;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const uint8_t *k = st + o.kc + t * 16 * SL::KROW;
+    if (KBITS == 4) {
+      const uint4 a = *reinterpret_cast<const uint4 *>(k);
+      f.kw[t][0] = a.x; f.kw[t][1] = a.y; f.kw[t][2] = a.z; f.kw[t][3] = a.w;
+    } else {
+      const uint2 a = *reinterpret_cast<const uint2 *>(k);
+      f.kw[t][0] = a.x; f.kw[t][1] = a.y;
+    }
+    f.kstep[t] = lds_meta<MT>(st + SL::KS + o.km + t * 16 * NG * SL::ES);
+    f.kzero[t] = lds_meta<MT>(st + SL::KZ + o.km + t * 16 * NG * SL::ES);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint8_t *v = st + SL::KC + o.vc + i * SL::VROW;
+    if (!VCODES) {
+    } else if (VBITS == 4) {
+      const uint2 w = *reinterpret_cast<const uint2 *>(v);
+      f.vw[i] = w.x;
+      f.vw2[i] = w.y;
+    } else {
+      f.vw[i] = *reinterpret_cast<const uint32_t *>(v);
+    }
+    f.vstep[i] = lds_meta<MT>(st + SL::VSC + o.vm + i * NG * SL::ES);
+    f.vzero[i] = lds_meta<MT>(st + SL::VZ + o.vm + i * NG * SL::ES);
+  }
+}
+
 // The cached keys are centred per group (group_centre) when a row has at
 // most two groups; the extra bf16 steps carry centre x query group sum.
 template <int NG>
@@ -418,7 +545,7 @@ __device__ inline void vtok_stage(const Fetch &f, int lane, float vsc, float *Gv
 //  - Per key (slots vslot4(kq) .. +3, from the first lane of each group):
 //    Ds row g = D 2^-ev kVcodeScale and Zs rows g, NG + g = z 2^-ev split
 //    into hi + lo, all fp16 (the other rows of Zs stay zero).
-template <int VBITS, int NG>
+template <int VBITS, int NG, bool TILE = true>
 __device__ inline void unpack_v_raw(const Ctx &c, int lane, const Fetch &f, float vsc, uint16_t *Vt, uint16_t *Ds,
                                     uint16_t *Zs) {
   const int kq = lane & 7, dq = lane >> 3;
@@ -439,6 +566,7 @@ __device__ inline void unpack_v_raw(const Ctx &c, int lane, const Fetch &f, floa
     *reinterpret_cast<uint2 *>(Zs + ZS * g + slot) = make_uint2(pair_h(zh[0], zh[1]), pair_h(zh[2], zh[3]));
     *reinterpret_cast<uint2 *>(Zs + ZS * (NG + g) + slot) = make_uint2(pair_h(zl[0], zl[1]), pair_h(zl[2], zl[3]));
   }
+  if (!TILE) return;  // the value operands come from registers (v_operands)
 #pragma unroll
   for (int byte = 0; byte < (VBITS == 4 ? 8 : 4); ++byte) {
     // INT4: d = 16dq + 2byte + {0, 1} (bytes 4.. from vw2); INT2: d = 16dq + 4byte + {0, 1, 2, 3}
@@ -466,6 +594,61 @@ __device__ inline void unpack_v_raw(const Ctx &c, int lane, const Fetch &f, floa
     for (int fl = 0; fl < NF; ++fl)
       *reinterpret_cast<uint2 *>(Vt + vts(16 * dq + NF * byte + fl, slot)) = make_uint2(x[fl][0], x[fl][1]);
   }
+}
+
+// Value operands in registers (staged caches, at most two groups per row):
+// the A operand of the value product for head-dim tile dt is built by the
+// lane from the staged codes instead of a V^T tile in LDS, which saves the
+// transposed LDS stores and their reads on every block.  The tile's rows are
+// a permutation of the head dimension chosen so that a lane's eight tiles
+// cover dims 4r .. 4r+3 and 64 + 4r .. 64 + 4r+3 (r = lane % 16), i.e. two
+// 16-bit (INT4) or 8-bit (INT2) pieces of each code row, and every tile lies
+// in one quantisation group: row r of tile dt is dim vrow<true>(dt, r).
+// A lane's k-slots 8j .. 8j+7 (j = lane / 16) are the keys of its P^T
+// operand, 4j .. 4j+3 and 16 + 4j .. 16 + 4j+3.
+template <bool PERM>
+__device__ inline int vrow(int dt, int r) {
+  return PERM ? 64 * (dt >> 2) + 4 * r + (dt & 3) : 16 * dt + r;
+}
+
+// The lane's code pieces of its eight keys from the stage: y[i] holds the
+// piece of dims 4r .. 4r+3 in its low half and that of 64 + 4r .. in its
+// high half (INT4: two bytes each; INT2: one byte each, at bytes 0 and 2).
+template <int VBITS>
+__device__ inline void stage_read_vcodes(const uint8_t *vc, int lane, uint32_t (&y)[8]) {
+  constexpr uint32_t VROW = D * VBITS / 8;
+  const int r = lane & 15, j = lane >> 4;
+  const uint32_t sel = VBITS == 4 ? ((r & 1) ? 0x07060302u : 0x05040100u)
+                                  : static_cast<uint32_t>(r & 3) | 0x0c00u | (static_cast<uint32_t>(4 + (r & 3)) << 16) |
+                                        0x0c000000u;
+  const uint32_t off = VBITS == 4 ? 4 * (r >> 1) : 4 * (r >> 2);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int key = i < 4 ? 4 * j + i : 16 + 4 * j + (i - 4);
+    const uint8_t *row = vc + key * VROW + off;
+    const uint32_t lo = *reinterpret_cast<const uint32_t *>(row);
+    const uint32_t hi = *reinterpret_cast<const uint32_t *>(row + VROW / 2);
+    y[i] = __builtin_amdgcn_perm(hi, lo, sel);
+  }
+}
+
+// Tile dt's operand from the pieces: word w holds keys of slots 2w, 2w+1,
+// each as the fp16 subnormal of its code field (dim 4r + f of the tile's
+// half, f = dt % 4) at bit p: odd f sits at p = P1, like the odd rows of
+// unpack_v_raw.
+template <int VBITS>
+__device__ inline f16x8 v_operand(const Ctx &c, const uint32_t (&y)[8], int dt) {
+  const int h = dt >> 2, f = dt & 3;
+  const int b = VBITS == 4 ? 2 * h + (f >> 1) : 2 * h;
+  const uint32_t sel = static_cast<uint32_t>(b) | 0x0c00u | (static_cast<uint32_t>(4 + b) << 16) | 0x0c000000u;
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    uint32_t x = __builtin_amdgcn_perm(y[2 * e + 1], y[2 * e], sel);
+    if (VBITS == 2 && f >= 2) x >>= 4;
+    w[e] = x & ((f & 1) ? c.vmask1 : c.vmask0);
+  }
+  return __builtin_bit_cast(f16x8, make_uint4(w[0], w[1], w[2], w[3]));
 }
 
 // The same with values along the tokens: the operands of channel c =
@@ -651,11 +834,13 @@ struct Soft {
 // row may have seen no key yet (m = -inf).  ADD: the row's scores add sadd.
 // VCODE: the V^T tile holds raw codes (unpack_v_raw), with the block's steps
 // in Ds and zero points in Zs.
-template <bool CORR, bool CAUSAL = false, bool ADD = false, bool VCODE = false, int NG = 1>
+template <bool CORR, bool CAUSAL = false, bool ADD = false, bool VCODE = false, int NG = 1, bool PERM = false,
+          int VREG = 0>
 __device__ inline void block_compute(const f16x8 (&k)[2][4], const bf16x8 (&kext)[2], const uint16_t *Vt,
                                      const f16x8 (&q)[4], bf16x8 qext, int count, float alpha, int ev, int lane,
                                      Soft &st, float sadd = 0.f, const uint16_t *Ds = nullptr,
-                                     const uint16_t *Zs = nullptr) {
+                                     const uint16_t *Zs = nullptr, const Ctx *c = nullptr,
+                                     const uint32_t (*vy)[8] = nullptr) {
   const float fev = static_cast<float>(ev);
   const int r = lane & 15, j = lane >> 4;
   f32x4 s[2];
@@ -676,8 +861,7 @@ __device__ inline void block_compute(const f16x8 (&k)[2][4], const bf16x8 (&kext
   }
   float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                    fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-  mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-  mt = fmaf(fmaxf(mt, __shfl_xor(mt, 32, 64)), alpha, fev);
+  mt = fmaf(xor32_max(xor16_max(mt)), alpha, fev);
   const bool grow = mt > st.m + kLazy;
   if (__any(grow)) {
     const float m_new = grow ? mt : st.m;
@@ -709,16 +893,21 @@ __device__ inline void block_compute(const f16x8 (&k)[2][4], const bf16x8 (&kext
 #pragma unroll
     for (int g = 0; g < NG; ++g) pg[g] = pk * *reinterpret_cast<const f16x8 *>(Ds + 32 * g + 8 * j);
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-      st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-          *reinterpret_cast<const f16x8 *>(Vt + vts(16 * dt + r, 8 * j)), pg[(16 * dt * NG) / D], st.o[dt], 0, 0, 0);
+    for (int dt = 0; dt < D / 16; ++dt) {
+      f16x8 a;
+      if (VREG)
+        a = v_operand<VREG>(*c, *vy, dt);
+      else
+        a = *reinterpret_cast<const f16x8 *>(Vt + vts(vrow<PERM>(dt, r), 8 * j));
+      st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pg[(vrow<PERM>(dt, 0) * NG) / D], st.o[dt], 0, 0, 0);
+    }
     st.oz = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const f16x8 *>(Zs + ZS * r + 8 * j), pk, st.oz,
                                                    0, 0, 0);
   } else {
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
       st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-          *reinterpret_cast<const f16x8 *>(Vt + vts(16 * dt + r, 8 * j)), pk, st.o[dt], 0, 0, 0);
+          *reinterpret_cast<const f16x8 *>(Vt + vts(vrow<PERM>(dt, r), 8 * j)), pk, st.o[dt], 0, 0, 0);
   }
 }
 
@@ -726,7 +915,7 @@ __device__ inline void block_compute(const f16x8 (&k)[2][4], const bf16x8 (&kext
 // of dequantised values, o = o_codes 2^(24-p) / kVcodeScale + the group's
 // zero-point sum (p = P1 on odd head-dim rows), before the current chunk's
 // blocks add to them.
-template <int VBITS, int NG>
+template <int VBITS, int NG, bool PERM = false>
 __device__ inline void vcode_finish(Soft &st, int lane) {
   constexpr int P1 = VBITS == 4 ? 4 : 2;
   const int r = lane & 15;
@@ -741,7 +930,8 @@ __device__ inline void vcode_finish(Soft &st, int lane) {
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) st.o[dt][i] = fmaf(st.o[dt][i], (i & 1) ? f1 : f0, zs[(16 * dt * NG) / D]);
+    for (int i = 0; i < 4; ++i)  // element i: dim vrow<PERM>(dt, 4 (lane / 16) + i); odd dims at 2^P1
+      st.o[dt][i] = fmaf(st.o[dt][i], ((PERM ? dt : i) & 1) ? f1 : f0, zs[(vrow<PERM>(dt, 0) * NG) / D]);
 }
 
 // KTOK / VTOK: keys / values grouped along the tokens (p.group is then also
@@ -754,8 +944,19 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
   constexpr bool TOK = KTOK || VTOK;
   constexpr bool VCODE = !VTOK;  // cached values as raw codes
   constexpr int TOK_BYTES = TOK ? WAVES * 2 * GM * 4 : 0;
-  __shared__ __attribute__((aligned(16)))
-  uint16_t L[(LDS_BYTES + TOK_BYTES + (VCODE ? WAVES * VCODE_HALVES * 2 : 0)) / 2];
+  constexpr int BASE_BYTES = LDS_BYTES + TOK_BYTES + (VCODE ? WAVES * VCODE_HALVES * 2 : 0);
+  __shared__ __attribute__((aligned(16))) uint16_t L[BASE_BYTES / 2];
+  // staged fetch (head-dimension groups, contiguous caches) where its two
+  // stages per wave still leave room for two workgroups per CU, and a row's
+  // steps (zero points) span whole 4-byte words: the range check of a
+  // 4-byte load that straddles the segment's end zeroes the whole word
+  using SL = StageLayout<KBITS, VBITS, NG, MT>;
+  constexpr bool STAGED = !TOK && !PAGED && (NG * SL::ES) % 4 == 0 && BASE_BYTES + 2 * WAVES * SL::BYTES <= 80 * 1024;
+  // staged caches with at most two groups per row take their value operands
+  // from registers, on permuted head-dim rows (vrow)
+  constexpr bool PERM = STAGED && NG <= 2;
+  __shared__ __attribute__((aligned(16))) uint8_t S0[STAGED ? WAVES * SL::BYTES : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t S1[STAGED ? WAVES * SL::BYTES : 16];
 
   const int tid = threadIdx.x;
   if (blockIdx.x >= p.app.wg0) {  // the chunk append's workgroups
@@ -867,13 +1068,57 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
   f16x8 qk[4];
   float sadd = 0.f, alpha_g = 0.f;
   int gcur = -1;
-  if (blk < cend)
+  if constexpr (STAGED) {
+    const uint8_t *s0 = S0 + wave * SL::BYTES, *s1 = S1 + wave * SL::BYTES;
+    // both stages start zeroed, so that a byte no load writes is a finite zero
+    for (uint32_t o = static_cast<uint32_t>(lane) * 16; o < SL::BYTES; o += 1024) {
+      *reinterpret_cast<uint4 *>(S0 + wave * SL::BYTES + o) = make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4 *>(S1 + wave * SL::BYTES + o) = make_uint4(0u, 0u, 0u, 0u);
+    }
+    // every step issues one block's loads (an empty range past the wave's
+    // last block), so a stage is ready once at most one block's loads are
+    // outstanding
+    auto issue = [&](const uint8_t *stg, int bk) {
+      const int k0 = bk * BK;
+      const bool in = bk < cend;
+      stage_issue<KBITS, VBITS, NG, MT>(c, in ? static_cast<size_t>(k0) : 0,
+                                        in ? static_cast<uint32_t>(c.nc - k0) : 0u, stg, lane);
+    };
+    issue(s0, blk);
+    issue(s1, blk + bstep);
+    // one block from stage stg: read the lane's share, refill the stage with
+    // the block two steps on, then unpack and multiply
+    auto body = [&](const uint8_t *stg) {
+      const int k0 = blk * BK;
+      const int count = c.nc - k0 < BK ? c.nc - k0 : BK;
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(SL::LOADS) : "memory");
+      stage_read<KBITS, VBITS, NG, MT, !PERM>(stg, lo, f);
+      uint32_t vy[8];
+      if (PERM) stage_read_vcodes<VBITS>(stg + SL::KC, lane, vy);
+      issue(stg, blk + 2 * bstep);
+      if (!cache_bounds) sc.update(k_bound<KBITS, NG>(f), v_bound<VBITS>(f), st.alpha);
+      unpack_k_cached<TAYLOR, KBITS, NG>(c, lane, f, sc.kscale, kreg, kext);
+      unpack_v_raw<VBITS, NG, !PERM>(c, lane, f, sc.vscale, Vt, Ds, Zs);
+      block_compute<TAYLOR || kCentre<NG>, false, false, true, NG, PERM, PERM ? VBITS : 0>(
+          kreg, kext, Vt, q, qext, count, sc.alpha, sc.ev, lane, st, 0.f, Ds, Zs, &c, &vy);
+    };
+    for (;;) {
+      if (blk >= cend) break;
+      body(s0);
+      blk += bstep;
+      if (blk >= cend) break;
+      body(s1);
+      blk += bstep;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load into LDS outlives the loop
+  }
+  if (!STAGED && blk < cend)
     fetch_cached<KBITS, VBITS, NG, PAGED, MT, KTOK, VTOK>(c, blk * BK, lo, f, block_row<PAGED>(c, blk * BK), gshift,
                                                           true);
   // paged: the pool row of the next block to fetch, looked up one block ahead
   // so that its scalar load has completed when the fetch needs it
   size_t prn = PAGED && blk + bstep < cend ? block_row<PAGED>(c, (blk + bstep) * BK) : 0;
-  for (; blk < cend; blk += bstep) {
+  for (; !STAGED && blk < cend; blk += bstep) {
     const int k0 = blk * BK;
     const int count = c.nc - k0 < BK ? c.nc - k0 : BK;
     const bool newg = TOK && (k0 >> gshift) != gcur;  // the block starts the wave's next token group
@@ -907,7 +1152,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
                                                                       lane, st, 0.f, Ds, Zs);
     if (PAGED && blk + 2 * bstep < cend) prn = block_row<PAGED>(c, (blk + 2 * bstep) * BK);
   }
-  if (VCODE) vcode_finish<VBITS, NG>(st, lane);
+  if (VCODE) vcode_finish<VBITS, NG, PERM>(st, lane);
   for (; blk < wend; blk += bstep) {
     const int k0 = (blk - nbc) * BK;
     int count = c.ncur - k0 < BK ? c.ncur - k0 : BK;
@@ -917,7 +1162,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
     load_current(c, k0, lane, x, kb, vb);
     sc.update(kb, vb, st.alpha);
     unpack_current(lane, x, sc.kscale, sc.vscale, kreg, Vt);
-    block_compute<false, CAUSAL>(kreg, kext, Vt, q, qext, count, sc.alpha, sc.ev, lane, st);
+    block_compute<false, CAUSAL, false, false, 1, PERM>(kreg, kext, Vt, q, qext, count, sc.alpha, sc.ev, lane, st);
   }
 
   // ---- merge the 4 waves (log-sum-exp), then the split partial or output ----
@@ -927,10 +1172,19 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
   float *Ob = reinterpret_cast<float *>(L) + wave * MERGE;
   float *ml = Ob + ROWS * OS;
   const int j = lane >> 4;
+  if (PERM) {  // element i of tile dt: dim 64 (dt / 4) + 16 j + 4 i + dt % 4
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt)
-    *reinterpret_cast<float4 *>(Ob + r * OS + 16 * dt + 4 * j) =
-        make_float4(st.o[dt][0], st.o[dt][1], st.o[dt][2], st.o[dt][3]);
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<float4 *>(Ob + r * OS + 64 * h + 16 * j + 4 * i) =
+            make_float4(st.o[4 * h][i], st.o[4 * h + 1][i], st.o[4 * h + 2][i], st.o[4 * h + 3][i]);
+  } else {
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+      *reinterpret_cast<float4 *>(Ob + r * OS + 16 * dt + 4 * j) =
+          make_float4(st.o[dt][0], st.o[dt][1], st.o[dt][2], st.o[dt][3]);
+  }
   if (j == 0) {
     ml[2 * r] = st.m;
     ml[2 * r + 1] = l_tot;

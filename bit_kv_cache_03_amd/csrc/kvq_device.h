@@ -33,6 +33,24 @@ __device__ inline uint32_t pack2h(float lo, float hi) {
 __device__ inline float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float hi_f(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// Max / sum of x over lanes l and l ^ 32 (l ^ 16), in the vector ALU: with
+// both operands holding x, v_permlane32_swap (v_permlane16_swap) leaves a
+// lane's own value in one result and its partner's in the other, so each
+// lane combines the same two values; an LDS permute (ds_bpermute) would
+// put an LDS round trip on the path of every key block.
+__device__ inline float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Sum of the 8 bf16 values of v, added to acc (two per v_dot2_f32_bf16).
 __device__ inline float sum8(bf16x8 v, float acc) {
   const uint4 w = __builtin_bit_cast(uint4, v);
