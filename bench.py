@@ -364,6 +364,9 @@ def main():
     ap.add_argument("--evict", default="auto", choices=["auto", "on", "off"],
                     help="write a 512 MiB buffer between timed steps so that no launch finds the cache in the "
                          "MALL (auto: on for HBM-graded runs, i.e. at most 64 query rows per KV head)")
+    ap.add_argument("--evict-by", default="write", choices=["write", "read"],
+                    help="how the eviction passes over the 512 MiB buffer: a write (leaves dirty lines that are "
+                         "written back while the next step runs) or a read (leaves clean lines)")
     args = ap.parse_args()
     if "tokens" in (args.kaxis, args.vaxis):
         args.append = "separate"  # the fused append takes caches grouped along the head dimension
@@ -448,6 +451,14 @@ def main():
     hbm_bound = w.rows_per_kvhead <= 64
     evict = args.evict == "on" or (args.evict == "auto" and hbm_bound)
     scratch = torch.empty(MALL_EVICT_BYTES // 4, dtype=torch.float32, device="cuda") if evict else None
+    if scratch is not None:
+        scratch.zero_()
+
+    def evict_pass(buf, i):
+        if args.evict_by == "read":
+            buf.amax()
+        else:
+            buf.fill_(float(i))
     for _ in range(args.warmup):
         step(args_c)
     torch.cuda.synchronize()
@@ -461,7 +472,7 @@ def main():
     t_start.record(stream)
     for i in range(args.steps):
         if scratch is not None:
-            scratch.fill_(float(i))  # evicts the cache's lines from the MALL; outside the step's events
+            evict_pass(scratch, i)  # evicts the cache's lines from the MALL; outside the step's events
         step(args_c, evs[i])
         s_end[i].record(stream)
     t_end.record(stream)
@@ -497,7 +508,7 @@ def main():
         for i in range(args.steps):
             for n, a in runs.items():
                 if scratch is not None:
-                    scratch.fill_(float(i))
+                    evict_pass(scratch, i)
                 ev_runs[n][i][0].record(stream); attention(a); ev_runs[n][i][1].record(stream)
         del scratch
         torch.cuda.synchronize()
@@ -547,6 +558,7 @@ def main():
         "wall_s": wall,
         "kernel_sha": sha,
         "mall_evict_between_steps": evict,
+        "mall_evict_by": args.evict_by if evict else None,
         "clocks": clocks,
         "roofline": dict(roof, frac=roof["achieved"] / roof["peak"], traffic=traffic),
         "cpu_baseline": None,
