@@ -307,11 +307,11 @@ __device__ inline float lds_meta(const uint8_t *p) {
 
 // The lane's share of a staged block, at the offsets fetch_cached loads it
 // from HBM.
-template <int KBITS, int VBITS, int NG, int MT, bool VCODES = true>
+template <int KBITS, int VBITS, int NG, int MT, bool VCODES = true, bool KCODES = true>
 __device__ inline void stage_read(const uint8_t *st, const Lanes &o, Fetch &f) {
   using SL = StageLayout<KBITS, VBITS, NG, MT>;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < 2 && KCODES; ++t) {
     const uint8_t *k = st + o.kc + t * 16 * SL::KROW;
     if (KBITS == 4) {
       const uint4 a = *reinterpret_cast<const uint4 *>(k);
@@ -651,6 +651,135 @@ __device__ inline f16x8 v_operand(const Ctx &c, const uint32_t (&y)[8], int dt) 
   return __builtin_bit_cast(f16x8, make_uint4(w[0], w[1], w[2], w[3]));
 }
 
+// Key operands as raw codes (staged caches, at most two groups per row).
+// The score of a cached key is split by quantisation group,
+//   s = sum_g D_g (q_g . c_g) + sum_g z_g S_g - tau/24 sum_g D_g^2 ||q_g||^2
+// (S_g the query's group sum), so the codes enter the score MFMAs as they
+// are, one accumulator per group, each group's step multiplies its
+// accumulator per score, and the zero points and the Taylor term
+// ("量化鍵值偷走注意力…" (agents-report.net), §方法) come from the extra bf16
+// step.  The keys are never rounded to fp16.  For that the MFMA k-steps
+// must not mix groups: k-step i covers dims 32i .. 32i+31 (the lane's eight
+// of them 32i + 8j .. +7, j = lane / 16), and a 16-bit word e of an operand
+// holds dims e and e + 4 of the lane's eight.  The query and the current
+// chunk's keys use the same order (kraw_dims).
+//
+// The lane's dims of k-step i: 32 i + 8 j + (e, e + 4) in word e.
+__device__ inline uint32_t kraw_dim0(int i, int j) { return static_cast<uint32_t>(32 * i + 8 * j); }
+// Eight bf16 values (one uint4, consecutive dims) to an fp16 operand in the
+// (e, e + 4) word order, scaled by sc.
+__device__ inline f16x8 kraw_pack(uint4 w, float sc) {
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t a = u[e >> 1], b = u[2 + (e >> 1)];
+    o[e] = (e & 1) ? pack2h(hi_f(a) * sc, hi_f(b) * sc) : pack2h(lo_f(a) * sc, lo_f(b) * sc);
+  }
+  return __builtin_bit_cast(f16x8, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
+// The lane's query operands in that order (query row r of the tile), q
+// scaled by its own power of two 2^-eq; the extra step's slots on quarter
+// j < NG carry group j: N_j = tau/24 ||q_j||^2 2^-eq as (hi, hi, lo, 0) (zero
+// without the correction), then S_j = sum q 2^-eq as (hi, lo, hi, 0), both
+// times 2^-24, the unit of the code products (the scores' softmax scale is
+// alpha 2^24).
+template <bool TAYLOR, int NG>
+__device__ inline void load_query_kraw(const uint16_t *qptr, int lane, float tau, f16x8 (&q)[4], bf16x8 &qext,
+                                       float &alpha, float &qun) {
+  const int j = lane >> 4;
+  uint4 qw[4];
+  float nsum[NG], qsum[NG], qmax = 0.f;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) nsum[g] = qsum[g] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    qw[i] = *reinterpret_cast<const uint4 *>(qptr + kraw_dim0(i, j));
+    const uint32_t u[4] = {qw[i].x, qw[i].y, qw[i].z, qw[i].w};
+    const int g = (32 * i * NG) / D;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      nsum[g] += lo_f(u[e]) * lo_f(u[e]) + hi_f(u[e]) * hi_f(u[e]);
+      qsum[g] += lo_f(u[e]) + hi_f(u[e]);
+      qmax = fmaxf(qmax, fmaxf(fabsf(lo_f(u[e])), fabsf(hi_f(u[e]))));
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {  // over the four quarters
+    nsum[g] += __shfl_xor(nsum[g], 16, 64);
+    nsum[g] += __shfl_xor(nsum[g], 32, 64);
+    qsum[g] += __shfl_xor(qsum[g], 16, 64);
+    qsum[g] += __shfl_xor(qsum[g], 32, 64);
+  }
+  qmax = fmaxf(qmax, __shfl_xor(qmax, 16, 64));
+  qmax = fmaxf(qmax, __shfl_xor(qmax, 32, 64));
+  const int eq = scale_exponent(qmax);
+  const float qs_scale = ldexpf(1.0f, -eq);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q[i] = kraw_pack(qw[i], qs_scale);
+  qun = ldexpf(1.0f, eq);
+  alpha = tau * kLog2e * qun;
+  float ns = 0.f, ts = 0.f;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    ns = j == g ? nsum[g] : ns;
+    ts = j == g ? qsum[g] : ts;
+  }
+  const float n = TAYLOR ? ns * (tau / 24.0f) * qs_scale * 0x1p-24f : 0.f;
+  const float nh = lo_f(pack2(n, 0.f)), nl = n - nh;
+  const float t = ts * qs_scale * 0x1p-24f;
+  const float th = lo_f(pack2(t, 0.f)), tl = t - th;
+  uint4 x = make_uint4(pack2(nh, nh), pack2(nl, 0.f), pack2(th, tl), pack2(th, 0.f));
+  if (j >= NG) x = make_uint4(0u, 0u, 0u, 0u);
+  qext = __builtin_bit_cast(bf16x8, x);
+}
+
+// A cached block's key operands from the stage (codes at sk, steps at ks,
+// zero points at kz): k[t][i] = the codes of key 16t + r at the lane's dims
+// of k-step i as fp16 subnormals c 2^-24 (exact); kext[t] on quarter j < NG
+// = group j's (-D^2 split hi, lo, hi; 0; z split into its bf16 rounding
+// z_h twice and z - z_h; 0) for the key; dk[t][g][i] = D of key 16t + 4j + i
+// in group g (the scores' layout).  The scores come out in units of 2^-24.
+template <bool TAYLOR, int KBITS, int NG, int MT>
+__device__ inline void stage_k_raw(const Ctx &c, const uint8_t *sk, const uint8_t *ks, const uint8_t *kz, int lane,
+                                   f16x8 (&k)[2][4], bf16x8 (&kext)[2], float (&dk)[2][NG][4]) {
+  constexpr uint32_t KROW = D * KBITS / 8, ES = MT ? 2 : 4;
+  const int r = lane & 15, j = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const uint8_t *row = sk + (16 * t + r) * KROW;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t x;
+      if (KBITS == 4) {
+        x = *reinterpret_cast<const uint32_t *>(row + kraw_dim0(i, j) / 2);
+      } else {  // the 16 bits of the lane's eight codes; code e + 4 moves next to code e, 16 bits up
+        const uint32_t w = *reinterpret_cast<const uint32_t *>(row + 8 * i + 4 * (j >> 1)) >> (16 * (j & 1));
+        x = (w & 0xffffu) | ((w & 0xffffu) << 8);
+      }
+      uint32_t m[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m[e] = (x >> (KBITS * e)) & c.kmask;
+      k[t][i] = __builtin_bit_cast(f16x8, make_uint4(m[0], m[1], m[2], m[3]));
+    }
+    const int g = j < NG ? j : 0;
+    const float d = lds_meta<MT>(ks + ((16 * t + r) * NG + g) * ES);
+    const float z = lds_meta<MT>(kz + ((16 * t + r) * NG + g) * ES);
+    const float sq = TAYLOR ? d * d : 0.f;
+    const float hsq = lo_f(pack2(sq, 0.f));
+    const float zh = lo_f(pack2(z, 0.f));
+    uint4 x = make_uint4(pack2(-hsq, -(sq - hsq)), pack2(-hsq, 0.f), pack2(zh, zh), pack2(z - zh, 0.f));
+    if (j >= NG) x = make_uint4(0u, 0u, 0u, 0u);
+    kext[t] = __builtin_bit_cast(bf16x8, x);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg)
+        dk[t][gg][i] = lds_meta<MT>(ks + ((16 * t + 4 * j + i) * NG + gg) * ES);
+  }
+}
+
 // The same with values along the tokens: the operands of channel c =
 // 16dq + NF byte + fl (fl: the field within the byte) come from the staged
 // token group, the same for the four keys.
@@ -706,6 +835,7 @@ struct Cur {
   uint4 k[2][4];     // keys 16t + r, d = 32j + 8s .. +7
   uint32_t v[4][8];  // keys 4kq+i, bf16 pairs of d = 16dq + 2e, +1
 };
+template <bool KRAW = false>
 __device__ inline void load_current(const Ctx &c, int k0, int lane, Cur &x, float &kb, float &vb) {
   const int last = c.ncur - 1;
   kb = vb = 0.f;
@@ -714,10 +844,10 @@ __device__ inline void load_current(const Ctx &c, int k0, int lane, Cur &x, floa
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const uint32_t row = static_cast<uint32_t>(k0 + 16 * t + r <= last ? k0 + 16 * t + r : last);
-      const uint4 *ks = reinterpret_cast<const uint4 *>(c.k_cur + (row * D + 32u * j));
+      const uint16_t *ks = c.k_cur + row * D;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        x.k[t][s] = ks[s];
+      for (int s = 0; s < 4; ++s) {  // KRAW: the dims of k-step s in kraw_dim0's order
+        x.k[t][s] = *reinterpret_cast<const uint4 *>(ks + (KRAW ? kraw_dim0(s, j) : 32u * j + 8u * s));
         const uint32_t u[4] = {x.k[t][s].x, x.k[t][s].y, x.k[t][s].z, x.k[t][s].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) kb = fmaxf(kb, fmaxf(fabsf(lo_f(u[e])), fabsf(hi_f(u[e]))));
@@ -741,12 +871,17 @@ __device__ inline void load_current(const Ctx &c, int k0, int lane, Cur &x, floa
 
 // Keys to MFMA operand registers (no correction) and values to the V^T
 // tile, both rescaled to fp16.
+template <bool KRAW = false>
 __device__ inline void unpack_current(int lane, const Cur &x, float kscale, float vsc, f16x8 (&k)[2][4],
                                       uint16_t *Vt) {
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
+      if (KRAW) {
+        k[t][s] = kraw_pack(x.k[t][s], kscale);
+        continue;
+      }
       const uint32_t u[4] = {x.k[t][s].x, x.k[t][s].y, x.k[t][s].z, x.k[t][s].w};
       uint32_t w[4];
 #pragma unroll
@@ -835,17 +970,33 @@ struct Soft {
 // VCODE: the V^T tile holds raw codes (unpack_v_raw), with the block's steps
 // in Ds and zero points in Zs.
 template <bool CORR, bool CAUSAL = false, bool ADD = false, bool VCODE = false, int NG = 1, bool PERM = false,
-          int VREG = 0>
+          int VREG = 0, bool KRAW = false>
 __device__ inline void block_compute(const f16x8 (&k)[2][4], const bf16x8 (&kext)[2], const uint16_t *Vt,
                                      const f16x8 (&q)[4], bf16x8 qext, int count, float alpha, int ev, int lane,
                                      Soft &st, float sadd = 0.f, const uint16_t *Ds = nullptr,
                                      const uint16_t *Zs = nullptr, const Ctx *c = nullptr,
-                                     const uint32_t (*vy)[8] = nullptr) {
+                                     const uint32_t (*vy)[8] = nullptr, const float *dk = nullptr) {
   const float fev = static_cast<float>(ev);
   const int r = lane & 15, j = lane >> 4;
   f32x4 s[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
+    if (KRAW) {  // raw codes: one accumulator per group, scaled per score by the keys' steps dk (t, g, element)
+      f32x4 a[NG];
+#pragma unroll
+      for (int g = 0; g < NG; ++g) a[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int g = (32 * i * NG) / D;
+        a[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k[t][i], q[i], a[g], 0, 0, 0);
+      }
+      s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kext[t], qext, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int g = 0; g < NG; ++g) s[t][e] = fmaf(dk[(t * NG + g) * 4 + e], a[g][e], s[t][e]);
+      continue;
+    }
     s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) s[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k[t][i], q[i], s[t], 0, 0, 0);
@@ -946,15 +1097,16 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
   constexpr int TOK_BYTES = TOK ? WAVES * 2 * GM * 4 : 0;
   constexpr int BASE_BYTES = LDS_BYTES + TOK_BYTES + (VCODE ? WAVES * VCODE_HALVES * 2 : 0);
   __shared__ __attribute__((aligned(16))) uint16_t L[BASE_BYTES / 2];
-  // staged fetch (head-dimension groups, contiguous caches) where its two
-  // stages per wave still leave room for two workgroups per CU, and a row's
+  // staged fetch (head-dimension groups) where its two stages per wave
+  // still leave room for two workgroups per CU, and a row's
   // steps (zero points) span whole 4-byte words: the range check of a
   // 4-byte load that straddles the segment's end zeroes the whole word
   using SL = StageLayout<KBITS, VBITS, NG, MT>;
-  constexpr bool STAGED = !TOK && !PAGED && (NG * SL::ES) % 4 == 0 && BASE_BYTES + 2 * WAVES * SL::BYTES <= 80 * 1024;
+  constexpr bool STAGED = !TOK && (NG * SL::ES) % 4 == 0 && BASE_BYTES + 2 * WAVES * SL::BYTES <= 80 * 1024;
   // staged caches with at most two groups per row take their value operands
   // from registers, on permuted head-dim rows (vrow)
   constexpr bool PERM = STAGED && NG <= 2;
+  constexpr bool KRAW = PERM;  // and their keys enter the score MFMAs as raw codes
   __shared__ __attribute__((aligned(16))) uint8_t S0[STAGED ? WAVES * SL::BYTES : 16];
   __shared__ __attribute__((aligned(16))) uint8_t S1[STAGED ? WAVES * SL::BYTES : 16];
 
@@ -985,7 +1137,10 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
   bf16x8 qext;
   Soft st;
   float qun;
-  load_query<TAYLOR, NG>(p.q + qrow * D, lane, p.tau, q, qext, st.alpha, qun);
+  if (KRAW)
+    load_query_kraw<TAYLOR, NG>(p.q + qrow * D, lane, p.tau, q, qext, st.alpha, qun);
+  else
+    load_query<TAYLOR, NG>(p.q + qrow * D, lane, p.tau, q, qext, st.alpha, qun);
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.oz = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1078,29 +1233,38 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
     // every step issues one block's loads (an empty range past the wave's
     // last block), so a stage is ready once at most one block's loads are
     // outstanding
-    auto issue = [&](const uint8_t *stg, int bk) {
+    // paged: pr is the block's pool row (a 32-key block lies in one page),
+    // looked up a step before its loads are issued
+    auto issue = [&](const uint8_t *stg, int bk, size_t pr) {
       const int k0 = bk * BK;
       const bool in = bk < cend;
-      stage_issue<KBITS, VBITS, NG, MT>(c, in ? static_cast<size_t>(k0) : 0,
-                                        in ? static_cast<uint32_t>(c.nc - k0) : 0u, stg, lane);
+      const uint32_t rows = static_cast<uint32_t>(PAGED ? min(c.nc - k0, BK) : c.nc - k0);
+      stage_issue<KBITS, VBITS, NG, MT>(c, in ? (PAGED ? pr : static_cast<size_t>(k0)) : 0, in ? rows : 0u, stg,
+                                        lane);
     };
-    issue(s0, blk);
-    issue(s1, blk + bstep);
+    auto lookup = [&](int bk) -> size_t { return PAGED && bk < cend ? block_row<PAGED>(c, bk * BK) : 0; };
+    issue(s0, blk, lookup(blk));
+    issue(s1, blk + bstep, lookup(blk + bstep));
+    size_t prn = lookup(blk + 2 * bstep);
     // one block from stage stg: read the lane's share, refill the stage with
     // the block two steps on, then unpack and multiply
     auto body = [&](const uint8_t *stg) {
       const int k0 = blk * BK;
       const int count = c.nc - k0 < BK ? c.nc - k0 : BK;
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(SL::LOADS) : "memory");
-      stage_read<KBITS, VBITS, NG, MT, !PERM>(stg, lo, f);
+      stage_read<KBITS, VBITS, NG, MT, !PERM, !KRAW>(stg, lo, f);
       uint32_t vy[8];
       if (PERM) stage_read_vcodes<VBITS>(stg + SL::KC, lane, vy);
-      issue(stg, blk + 2 * bstep);
-      if (!cache_bounds) sc.update(k_bound<KBITS, NG>(f), v_bound<VBITS>(f), st.alpha);
-      unpack_k_cached<TAYLOR, KBITS, NG>(c, lane, f, sc.kscale, kreg, kext);
+      float dk[2][NG][4];
+      if (KRAW) stage_k_raw<TAYLOR, KBITS, NG, MT>(c, stg, stg + SL::KS, stg + SL::KZ, lane, kreg, kext, dk);
+      issue(stg, blk + 2 * bstep, prn);
+      prn = lookup(blk + 3 * bstep);
+      if (!cache_bounds) sc.update(KRAW ? 0.f : k_bound<KBITS, NG>(f), v_bound<VBITS>(f), st.alpha);
+      if (!KRAW) unpack_k_cached<TAYLOR, KBITS, NG>(c, lane, f, sc.kscale, kreg, kext);
       unpack_v_raw<VBITS, NG, !PERM>(c, lane, f, sc.vscale, Vt, Ds, Zs);
-      block_compute<TAYLOR || kCentre<NG>, false, false, true, NG, PERM, PERM ? VBITS : 0>(
-          kreg, kext, Vt, q, qext, count, sc.alpha, sc.ev, lane, st, 0.f, Ds, Zs, &c, &vy);
+      block_compute<TAYLOR || kCentre<NG> || KRAW, false, false, true, NG, PERM, PERM ? VBITS : 0, KRAW>(
+          kreg, kext, Vt, q, qext, count, KRAW ? st.alpha * 16777216.0f : sc.alpha, sc.ev, lane, st, 0.f, Ds, Zs, &c, &vy,
+          &dk[0][0][0]);
     };
     for (;;) {
       if (blk >= cend) break;
@@ -1159,9 +1323,9 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
     if (CAUSAL) count = min(count, climit - k0);
     Cur x;
     float kb, vb;
-    load_current(c, k0, lane, x, kb, vb);
+    load_current<KRAW>(c, k0, lane, x, kb, vb);
     sc.update(kb, vb, st.alpha);
-    unpack_current(lane, x, sc.kscale, sc.vscale, kreg, Vt);
+    unpack_current<KRAW>(lane, x, sc.kscale, sc.vscale, kreg, Vt);
     block_compute<false, CAUSAL, false, false, 1, PERM>(kreg, kext, Vt, q, qext, count, sc.alpha, sc.ev, lane, st);
   }
 
