@@ -362,11 +362,11 @@ def main():
     ap.add_argument("--append", default="fused", choices=["fused", "separate"],
                     help="append the chunk to the cache inside the attention call, or by kv_quantize after it")
     ap.add_argument("--evict", default="auto", choices=["auto", "on", "off"],
-                    help="write a 512 MiB buffer between timed steps so that no launch finds the cache in the "
+                    help="pass over a 512 MiB buffer between timed steps so that no launch finds the cache in the "
                          "MALL (auto: on for HBM-graded runs, i.e. at most 64 query rows per KV head)")
-    ap.add_argument("--evict-by", default="write", choices=["write", "read"],
-                    help="how the eviction passes over the 512 MiB buffer: a write (leaves dirty lines that are "
-                         "written back while the next step runs) or a read (leaves clean lines)")
+    ap.add_argument("--evict-by", default="read", choices=["read", "write"],
+                    help="how the eviction passes over the 512 MiB buffer: a read (leaves clean lines) or a write "
+                         "(leaves dirty lines whose write-back falls inside the next timed step)")
     args = ap.parse_args()
     if "tokens" in (args.kaxis, args.vaxis):
         args.append = "separate"  # the fused append takes caches grouped along the head dimension

@@ -78,13 +78,13 @@ constexpr int MERGE = ROWS * OS + 2 * ROWS;  // floats of a wave's merge buffer 
 constexpr int LDS_BYTES = WAVES * VT * 2 > WAVES * MERGE * 4 ? WAVES * VT * 2 : WAVES * MERGE * 4;
 constexpr int GM = 2 * D;  // floats of a wave's token-group staging of K or of V (two per channel)
 // Cached values as raw codes (groups along the head dimension): a wave's
-// per-key steps Ds (4 groups x 32 keys) and zero-point operand Zs (16 rows x
-// ZS: rows g and NG + g the hi and lo parts of group g's zero points, the
-// rest zero; 80-byte rows keep the 16 rows' reads on distinct banks), fp16.
-// kVcodeScale keeps p D 2^-ev kVcodeScale < 2^15.42 for p <= 2^8 and
-// |v| 2^-ev < 2^14 (D <= 2^15 / 3), inside the fp16 range.
+// per-key steps Ds (4 groups x 32 keys, fp32) and zero-point operand Zs (16
+// rows x ZS fp16: rows g and NG + g the hi and lo parts of group g's zero
+// points, the rest zero; 80-byte rows keep the 16 rows' reads on distinct
+// banks).  kVcodeScale keeps p D 2^-ev kVcodeScale < 2^15.42 for p <= 2^8
+// and |v| 2^-ev < 2^14 (D <= 2^15 / 3), inside the fp16 range.
 constexpr int ZS = 40;
-constexpr int VCODE_HALVES = 4 * 32 + 16 * ZS;
+constexpr int VCODE_HALVES = 2 * 4 * 32 + 16 * ZS;
 constexpr float kVcodeScale = 1.0f / 64.0f;
 
 // V^T element (row = head-dim index, col = key slot 0..31); the 16-byte
@@ -561,8 +561,8 @@ __device__ inline void unpack_v_raw(const Ctx &c, int lane, const Fetch &f, floa
       zh[i] = static_cast<_Float16>(z);
       zl[i] = static_cast<_Float16>(z - static_cast<float>(zh[i]));
     }
-    *reinterpret_cast<uint2 *>(Ds + 32 * g + slot) =
-        make_uint2(pack2h(f.vstep[0] * ds, f.vstep[1] * ds), pack2h(f.vstep[2] * ds, f.vstep[3] * ds));
+    *reinterpret_cast<float4 *>(reinterpret_cast<float *>(Ds) + 32 * g + slot) =
+        make_float4(f.vstep[0] * ds, f.vstep[1] * ds, f.vstep[2] * ds, f.vstep[3] * ds);
     *reinterpret_cast<uint2 *>(Zs + ZS * g + slot) = make_uint2(pair_h(zh[0], zh[1]), pair_h(zh[2], zh[3]));
     *reinterpret_cast<uint2 *>(Zs + ZS * (NG + g) + slot) = make_uint2(pair_h(zl[0], zl[1]), pair_h(zl[2], zl[3]));
   }
@@ -1035,14 +1035,29 @@ __device__ inline void block_compute(const f16x8 (&k)[2][4], const bf16x8 (&kext
   const f16x8 pk = __builtin_bit_cast(
       f16x8, make_uint4(pack2h(e[0][0], e[0][1]), pack2h(e[0][2], e[0][3]), pack2h(e[1][0], e[1][1]),
                         pack2h(e[1][2], e[1][3])));
-  st.l = fmaf(sum8h(pk, 0.f), ldexpf(1.0f, -ev), st.l);
   // O^T += V^T P^T: head-dim tile dt, the block's 32 keys in one k-step
   if (VCODE) {
+    // The raw codes multiply p D, and nothing averages its rounding when a
+    // row sees few keys (one cached key: the output is that key's value), so
+    // p D is carried as fp16 hi + lo, formed in fp32 from the fp16 p (the p
+    // of the row sum and of the zero points) and the fp32 step: two MFMAs per
+    // tile.
+    st.l = fmaf(sum8h(pk, 0.f), ldexpf(1.0f, -ev), st.l);
     // group g's operand: the probabilities times the keys' steps (the slots
     // 8j .. 8j+7 of Ds row g, the same for the 16 lanes of a quarter)
-    f16x8 pg[NG];
+    f16x8 pgh[NG], pgl[NG];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) pg[g] = pk * *reinterpret_cast<const f16x8 *>(Ds + 32 * g + 8 * j);
+    for (int g = 0; g < NG; ++g) {
+      const float *dsf = reinterpret_cast<const float *>(Ds) + 32 * g + 8 * j;
+      const float4 d0 = *reinterpret_cast<const float4 *>(dsf), d1 = *reinterpret_cast<const float4 *>(dsf + 4);
+      const float dv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float x = static_cast<float>(pk[k]) * dv[k];
+        pgh[g][k] = static_cast<_Float16>(x);
+        pgl[g][k] = static_cast<_Float16>(fmaf(-1.0f, static_cast<float>(pgh[g][k]), x));
+      }
+    }
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
       f16x8 a;
@@ -1050,11 +1065,14 @@ __device__ inline void block_compute(const f16x8 (&k)[2][4], const bf16x8 (&kext
         a = v_operand<VREG>(*c, *vy, dt);
       else
         a = *reinterpret_cast<const f16x8 *>(Vt + vts(vrow<PERM>(dt, r), 8 * j));
-      st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pg[(vrow<PERM>(dt, 0) * NG) / D], st.o[dt], 0, 0, 0);
+      const int g = (vrow<PERM>(dt, 0) * NG) / D;
+      st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pgh[g], st.o[dt], 0, 0, 0);
+      st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pgl[g], st.o[dt], 0, 0, 0);
     }
-    st.oz = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const f16x8 *>(Zs + ZS * r + 8 * j), pk, st.oz,
-                                                   0, 0, 0);
+    const f16x8 za = *reinterpret_cast<const f16x8 *>(Zs + ZS * r + 8 * j);
+    st.oz = __builtin_amdgcn_mfma_f32_16x16x32_f16(za, pk, st.oz, 0, 0, 0);
   } else {
+    st.l = fmaf(sum8h(pk, 0.f), ldexpf(1.0f, -ev), st.l);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
       st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
@@ -1194,7 +1212,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
   float *Gm = reinterpret_cast<float *>(L + WAVES * VT) + wave * 2 * GM;  // token-group staging of K
   float *Gv = Gm + GM;                                                     // and of V
   uint16_t *Ds = L + (LDS_BYTES + TOK_BYTES) / 2 + wave * VCODE_HALVES;
-  uint16_t *Zs = Ds + 4 * 32;
+  uint16_t *Zs = Ds + 2 * 4 * 32;
   if (VCODE) {  // rows 2 NG .. 15 of Zs stay zero (16 rows x 80 bytes: 80 chunks of 16)
     for (int ch = lane; ch < 16 * ZS / 8; ch += 64) *reinterpret_cast<uint4 *>(Zs + 8 * ch) = make_uint4(0u, 0u, 0u, 0u);
   }

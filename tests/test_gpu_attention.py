@@ -53,6 +53,11 @@ EDGE = {
     "no_current": W.WORKLOADS["h24_int4_cache16k"].scaled(Hq=2, Hkv=2, Nq=70, Ncur=0, Nc=150),
     "one_query": W.WORKLOADS["gqa_prefill_b16_cache32k"].scaled(B=1, Nq=1, Ncur=1, Nc=700),
     "one_key": W.WORKLOADS["h40_int2_outliers_cache25k"].scaled(Hq=1, Hkv=1, Nq=33, Ncur=0, Nc=1),
+    # one cached key on the 16-row tiles: the output is that key's value, so
+    # no averaging over keys hides the rounding of the value product
+    "one_key_16rows": W.WORKLOADS["h40_int2_outliers_cache25k"].scaled(Hq=1, Hkv=1, Nq=16, Ncur=0, Nc=1),
+    "one_key_gqa": W.WORKLOADS["gqa_prefill_b16_cache32k"].scaled(B=1, Nq=4, Ncur=0, Nc=1),
+    "two_keys_int4": W.WORKLOADS["h24_int4_cache16k"].scaled(Hq=2, Hkv=1, Nq=8, Ncur=1, Nc=1),
     "d64_group32": W.WORKLOADS["tiny_d64_int2"].scaled(Hq=4, Hkv=2, Nq=77, Ncur=40, Nc=130, group=32, kbits=4),
     "group32": W.WORKLOADS["h40_int2_outliers_cache25k"].scaled(Hq=2, Hkv=2, Nq=64, Ncur=64, Nc=200, group=32),
     "group128": W.WORKLOADS["long_video_cache61k"].scaled(Hq=2, Hkv=2, Nq=64, Ncur=64, Nc=200, group=128),
