@@ -78,7 +78,8 @@ constexpr int MERGE = ROWS * OS + 2 * ROWS;  // floats of a wave's merge buffer 
 constexpr int LDS_BYTES = WAVES * VT * 2 > WAVES * MERGE * 4 ? WAVES * VT * 2 : WAVES * MERGE * 4;
 constexpr int GM = 2 * D;  // floats of a wave's token-group staging of K or of V (two per channel)
 // Cached values as raw codes (groups along the head dimension): a wave's
-// per-key steps Ds (4 groups x 32 keys, fp32) and zero-point operand Zs (16
+// per-key steps Ds (4 groups x 32 keys, as fp16 hi then lo) and zero-point
+// operand Zs (16
 // rows x ZS fp16: rows g and NG + g the hi and lo parts of group g's zero
 // points, the rest zero; 80-byte rows keep the 16 rows' reads on distinct
 // banks).  kVcodeScale keeps p D 2^-ev kVcodeScale < 2^15.42 for p <= 2^8
@@ -543,8 +544,9 @@ __device__ inline void vtok_stage(const Fetch &f, int lane, float vsc, float *Gv
 //    p = 0 and 2 of the byte and of the byte shifted right by 4; head-dim row
 //    16dq + NF byte + fl holds field fl, so odd rows carry 2^P1.
 //  - Per key (slots vslot4(kq) .. +3, from the first lane of each group):
-//    Ds row g = D 2^-ev kVcodeScale and Zs rows g, NG + g = z 2^-ev split
-//    into hi + lo, all fp16 (the other rows of Zs stay zero).
+//    Ds rows 2g, 2g + 1 = D 2^-ev kVcodeScale and Zs rows g, NG + g =
+//    z 2^-ev, each split into hi + lo, all fp16 (the other rows of Zs stay
+//    zero).
 template <int VBITS, int NG, bool TILE = true>
 __device__ inline void unpack_v_raw(const Ctx &c, int lane, const Fetch &f, float vsc, uint16_t *Vt, uint16_t *Ds,
                                     uint16_t *Zs) {
@@ -561,8 +563,15 @@ __device__ inline void unpack_v_raw(const Ctx &c, int lane, const Fetch &f, floa
       zh[i] = static_cast<_Float16>(z);
       zl[i] = static_cast<_Float16>(z - static_cast<float>(zh[i]));
     }
-    *reinterpret_cast<float4 *>(reinterpret_cast<float *>(Ds) + 32 * g + slot) =
-        make_float4(f.vstep[0] * ds, f.vstep[1] * ds, f.vstep[2] * ds, f.vstep[3] * ds);
+    _Float16 dh[4], dl[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float d = f.vstep[i] * ds;
+      dh[i] = static_cast<_Float16>(d);
+      dl[i] = static_cast<_Float16>(d - static_cast<float>(dh[i]));
+    }
+    *reinterpret_cast<uint2 *>(Ds + 64 * g + slot) = make_uint2(pair_h(dh[0], dh[1]), pair_h(dh[2], dh[3]));
+    *reinterpret_cast<uint2 *>(Ds + 64 * g + 32 + slot) = make_uint2(pair_h(dl[0], dl[1]), pair_h(dl[2], dl[3]));
     *reinterpret_cast<uint2 *>(Zs + ZS * g + slot) = make_uint2(pair_h(zh[0], zh[1]), pair_h(zh[2], zh[3]));
     *reinterpret_cast<uint2 *>(Zs + ZS * (NG + g) + slot) = make_uint2(pair_h(zl[0], zl[1]), pair_h(zl[2], zl[3]));
   }
@@ -1039,24 +1048,19 @@ __device__ inline void block_compute(const f16x8 (&k)[2][4], const bf16x8 (&kext
   if (VCODE) {
     // The raw codes multiply p D, and nothing averages its rounding when a
     // row sees few keys (one cached key: the output is that key's value), so
-    // p D is carried as fp16 hi + lo, formed in fp32 from the fp16 p (the p
-    // of the row sum and of the zero points) and the fp32 step: two MFMAs per
-    // tile.
+    // p D is carried as fp16 hi + lo: hi = p D_hi rounded, lo = its exact
+    // rounding error (one fp16 fma) plus p D_lo, with p the fp16 p of the row
+    // sum and the zero points; two MFMAs per tile.
     st.l = fmaf(sum8h(pk, 0.f), ldexpf(1.0f, -ev), st.l);
     // group g's operand: the probabilities times the keys' steps (the slots
     // 8j .. 8j+7 of Ds row g, the same for the 16 lanes of a quarter)
     f16x8 pgh[NG], pgl[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      const float *dsf = reinterpret_cast<const float *>(Ds) + 32 * g + 8 * j;
-      const float4 d0 = *reinterpret_cast<const float4 *>(dsf), d1 = *reinterpret_cast<const float4 *>(dsf + 4);
-      const float dv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float x = static_cast<float>(pk[k]) * dv[k];
-        pgh[g][k] = static_cast<_Float16>(x);
-        pgl[g][k] = static_cast<_Float16>(fmaf(-1.0f, static_cast<float>(pgh[g][k]), x));
-      }
+      const f16x8 dh = *reinterpret_cast<const f16x8 *>(Ds + 64 * g + 8 * j);
+      const f16x8 dl = *reinterpret_cast<const f16x8 *>(Ds + 64 * g + 32 + 8 * j);
+      pgh[g] = pk * dh;
+      pgl[g] = __builtin_elementwise_fma(pk, dl, __builtin_elementwise_fma(pk, dh, -pgh[g]));
     }
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
