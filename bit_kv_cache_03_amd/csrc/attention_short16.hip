@@ -747,7 +747,7 @@ __device__ inline void load_query_kraw(const uint16_t *qptr, int lane, float tau
 // A cached block's key operands from the stage (codes at sk, steps at ks,
 // zero points at kz): k[t][i] = the codes of key 16t + r at the lane's dims
 // of k-step i as fp16 subnormals c 2^-24 (exact); kext[t] on quarter j < NG
-// = group j's (-D^2 split hi, lo, hi; 0; z split into its bf16 rounding
+// = group j's (-D^2 split hi, lo, hi; 0; z split into its bf16 truncation
 // z_h twice and z - z_h; 0) for the key; dk[t][g][i] = D of key 16t + 4j + i
 // in group g (the scores' layout).  The scores come out in units of 2^-24.
 template <bool TAYLOR, int KBITS, int NG, int MT>
@@ -775,9 +775,10 @@ __device__ inline void stage_k_raw(const Ctx &c, const uint8_t *sk, const uint8_
     const int g = j < NG ? j : 0;
     const float d = lds_meta<MT>(ks + ((16 * t + r) * NG + g) * ES);
     const float z = lds_meta<MT>(kz + ((16 * t + r) * NG + g) * ES);
+    // bf16 hi parts by truncation (exact bf16 values; the remainder is exact in fp32)
     const float sq = TAYLOR ? d * d : 0.f;
-    const float hsq = lo_f(pack2(sq, 0.f));
-    const float zh = lo_f(pack2(z, 0.f));
+    const float hsq = __uint_as_float(__float_as_uint(sq) & 0xffff0000u);
+    const float zh = __uint_as_float(__float_as_uint(z) & 0xffff0000u);
     uint4 x = make_uint4(pack2(-hsq, -(sq - hsq)), pack2(-hsq, 0.f), pack2(zh, zh), pack2(z - zh, 0.f));
     if (j >= NG) x = make_uint4(0u, 0u, 0u, 0u);
     kext[t] = __builtin_bit_cast(bf16x8, x);
