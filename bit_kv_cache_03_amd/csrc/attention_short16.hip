@@ -1118,20 +1118,27 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
   constexpr bool TOK = KTOK || VTOK;
   constexpr bool VCODE = !VTOK;  // cached values as raw codes
   constexpr int TOK_BYTES = TOK ? WAVES * 2 * GM * 4 : 0;
-  constexpr int BASE_BYTES = LDS_BYTES + TOK_BYTES + (VCODE ? WAVES * VCODE_HALVES * 2 : 0);
-  __shared__ __attribute__((aligned(16))) uint16_t L[BASE_BYTES / 2];
-  // staged fetch (head-dimension groups) where its two stages per wave
-  // still leave room for two workgroups per CU, and a row's
-  // steps (zero points) span whole 4-byte words: the range check of a
-  // 4-byte load that straddles the segment's end zeroes the whole word
   using SL = StageLayout<KBITS, VBITS, NG, MT>;
-  constexpr bool STAGED = !TOK && (NG * SL::ES) % 4 == 0 && BASE_BYTES + 2 * WAVES * SL::BYTES <= 80 * 1024;
-  // staged caches with at most two groups per row take their value operands
-  // from registers, on permuted head-dim rows (vrow)
-  constexpr bool PERM = STAGED && NG <= 2;
-  constexpr bool KRAW = PERM;  // and their keys enter the score MFMAs as raw codes
-  __shared__ __attribute__((aligned(16))) uint8_t S0[STAGED ? WAVES * SL::BYTES : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t S1[STAGED ? WAVES * SL::BYTES : 16];
+  constexpr int STAGE_BYTES = 2 * WAVES * SL::BYTES;  // two stages per wave
+  // Caches with head-dimension groups, at most two per row and metadata rows
+  // of whole 4-byte words (the range check of a 4-byte load that straddles
+  // the segment's end zeroes the whole word) are staged and take raw-code
+  // operands (PERM: value operands from registers on permuted head-dim rows;
+  // KRAW: keys as raw codes).  Their V^T tiles (current chunk) and merge
+  // buffer are used only after the cached blocks, so they share one array
+  // with the stages (a barrier between the two uses).
+  constexpr int ALIAS_BYTES = STAGE_BYTES > LDS_BYTES ? STAGE_BYTES : LDS_BYTES;
+  constexpr bool PERM = !TOK && NG <= 2 && (NG * SL::ES) % 4 == 0 &&
+                        WAVES * VCODE_HALVES * 2 + ALIAS_BYTES <= 80 * 1024;
+  constexpr bool KRAW = PERM;
+  constexpr int BASE_BYTES =
+      PERM ? WAVES * VCODE_HALVES * 2 : LDS_BYTES + TOK_BYTES + (VCODE ? WAVES * VCODE_HALVES * 2 : 0);
+  __shared__ __attribute__((aligned(16))) uint16_t L[BASE_BYTES / 2];
+  // other head-dimension caches (four groups per row) stage where the stages
+  // still leave room for two workgroups per CU
+  constexpr bool STAGED = PERM || (!TOK && (NG * SL::ES) % 4 == 0 && BASE_BYTES + STAGE_BYTES <= 80 * 1024);
+  __shared__ __attribute__((aligned(16))) uint8_t S[PERM ? ALIAS_BYTES : STAGED ? STAGE_BYTES : 16];
+  uint16_t *const T = PERM ? reinterpret_cast<uint16_t *>(S) : L;  // V^T tiles and merge buffer
 
   const int tid = threadIdx.x;
   if (blockIdx.x >= p.app.wg0) {  // the chunk append's workgroups
@@ -1213,10 +1220,10 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
     const int cb = nbc + static_cast<int>(wlim > 0 ? (wlim + BK - 1) / BK : 0);
     if (bend > cb) bend = cb;
   }
-  uint16_t *Vt = L + wave * VT;
+  uint16_t *Vt = T + wave * VT;
   float *Gm = reinterpret_cast<float *>(L + WAVES * VT) + wave * 2 * GM;  // token-group staging of K
   float *Gv = Gm + GM;                                                     // and of V
-  uint16_t *Ds = L + (LDS_BYTES + TOK_BYTES) / 2 + wave * VCODE_HALVES;
+  uint16_t *Ds = (PERM ? L : L + (LDS_BYTES + TOK_BYTES) / 2) + wave * VCODE_HALVES;
   uint16_t *Zs = Ds + 2 * 4 * 32;
   if (VCODE) {  // rows 2 NG .. 15 of Zs stay zero (16 rows x 80 bytes: 80 chunks of 16)
     for (int ch = lane; ch < 16 * ZS / 8; ch += 64) *reinterpret_cast<uint4 *>(Zs + 8 * ch) = make_uint4(0u, 0u, 0u, 0u);
@@ -1247,11 +1254,11 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
   float sadd = 0.f, alpha_g = 0.f;
   int gcur = -1;
   if constexpr (STAGED) {
-    const uint8_t *s0 = S0 + wave * SL::BYTES, *s1 = S1 + wave * SL::BYTES;
+    uint8_t *const s0 = S + wave * SL::BYTES, *const s1 = S + (WAVES + wave) * SL::BYTES;
     // both stages start zeroed, so that a byte no load writes is a finite zero
     for (uint32_t o = static_cast<uint32_t>(lane) * 16; o < SL::BYTES; o += 1024) {
-      *reinterpret_cast<uint4 *>(S0 + wave * SL::BYTES + o) = make_uint4(0u, 0u, 0u, 0u);
-      *reinterpret_cast<uint4 *>(S1 + wave * SL::BYTES + o) = make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4 *>(s0 + o) = make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4 *>(s1 + o) = make_uint4(0u, 0u, 0u, 0u);
     }
     // every step issues one block's loads (an empty range past the wave's
     // last block), so a stage is ready once at most one block's loads are
@@ -1298,6 +1305,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
       blk += bstep;
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load into LDS outlives the loop
+    if (PERM) __syncthreads();  // every wave is done with its stages before any V^T tile reuses them
   }
   if (!STAGED && blk < cend)
     fetch_cached<KBITS, VBITS, NG, PAGED, MT, KTOK, VTOK>(c, blk * BK, lo, f, block_row<PAGED>(c, blk * BK), gshift,
@@ -1356,7 +1364,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
   float l_tot = st.l + __shfl_xor(st.l, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
   __syncthreads();  // every wave is done with its tiles
-  float *Ob = reinterpret_cast<float *>(L) + wave * MERGE;
+  float *Ob = reinterpret_cast<float *>(T) + wave * MERGE;
   float *ml = Ob + ROWS * OS;
   const int j = lane >> 4;
   if (PERM) {  // element i of tile dt: dim 64 (dt / 4) + 16 j + 4 i + dt % 4
@@ -1383,7 +1391,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
       float mw[WAVES], m = -INFINITY;
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) {
-        mw[w] = reinterpret_cast<const float *>(L)[w * MERGE + ROWS * OS + 2 * row];
+        mw[w] = reinterpret_cast<const float *>(T)[w * MERGE + ROWS * OS + 2 * row];
         m = fmaxf(m, mw[w]);
       }
       float acc[8], l = 0.f;
@@ -1391,7 +1399,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
       for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) {
-        const float *base = reinterpret_cast<const float *>(L) + w * MERGE;
+        const float *base = reinterpret_cast<const float *>(T) + w * MERGE;
         const float fw = mw[w] == -INFINITY ? 0.f : exp2f(mw[w] - m);
         l += fw * base[ROWS * OS + 2 * row + 1];
 #pragma unroll
