@@ -1,19 +1,28 @@
 // Short-query kernel for at most 16 query rows per KV head (decode and
 // small chunks of GQA heads) on gfx950: head dim 128, correction off or
-// Taylor, groups along the head dimension.
+// Taylor.
 //
 // The same split of the cache as attention_short.hip (many workgroups per
-// KV head; inside one, 4 waves that stream their own 32-key blocks with
-// private LDS tiles and merge at the end), but on 16 x 16 x 32 MFMA tiles:
-// one 16-row query tile instead of a 32-row one, so a block's scores are 8
-// per lane instead of 16 (half the exponentials, maxima and packing) and
-// the accumulators take half the registers.  The dequantisation per block is
-// the same (64 key and 64 value codes per lane).  The scores of the cached
-// keys carry the Taylor correction in extra bf16 MFMA steps ("量化鍵值偷走注意力…"
-// (agents-report.net), §方法 and §為何校正有效), with the current chunk's
-// keys left alone; everything goes through one online softmax.
+// KV head; inside one, 4 waves that stream their own 32-key blocks and
+// merge at the end), but on 16 x 16 x 32 MFMA tiles: one 16-row query tile
+// instead of a 32-row one, so a block's scores are 8 per lane instead of 16
+// (half the exponentials, maxima and packing) and the accumulators take half
+// the registers.  The scores of the cached keys carry the Taylor correction
+// in extra bf16 MFMA steps ("量化鍵值偷走注意力…" (agents-report.net), §方法
+// and §為何校正有效), with the current chunk's keys left alone; everything
+// goes through one online softmax.
 //
-// Lane roles (r = lane % 16, j = lane / 16):
+// Caches grouped along the head dimension with at most two groups per row
+// (the common case) take the staged, raw-operand form: each wave streams its
+// blocks through two LDS stages filled by direct-to-LDS buffer loads (two
+// blocks in flight, no registers held; see "staged fetch"), the keys enter
+// the score MFMAs as raw codes with one accumulator per group (stage_k_raw),
+// and the value operands are built in registers from the staged codes on a
+// permuted head-dim order (v_operand), the codes multiplying p D carried as
+// fp16 hi + lo.  Other caches dequantise keys into fp16 MFMA operands and
+// values into a V^T tile in LDS, with a one-block register prefetch.
+//
+// Lane roles of the dequantising form (r = lane % 16, j = lane / 16):
 //  K (A operand of S^T = K Q^T): keys 16t + r of the block (t = 0, 1), head
 //    dims 32j .. 32j+31 (k-step s: 32j + 8s .. +7) -- one group per lane;
 //  Q (B operand): query row r of the tile, the same dims;
@@ -24,6 +33,8 @@
 //  V (dequantisation): keys 4kq .. 4kq+3 (kq = lane % 8), dims 16dq .. 16dq+15
 //    (dq = lane / 8), written transposed into the V^T tile;
 //  O^T (16 x 16 per head-dim tile dt): query r, dims 16dt + 4j + i.
+// The raw-operand form changes the K and Q dims of k-step i to
+// 32i + 8j .. +7 (kraw_dim0) and the O^T rows to vrow<true>.
 //
 // Keys grouped along the tokens (KVQ_SHORT16_KTOK: one step D_c and zero
 // point z_c per channel c and token group, the page's per-channel reading of
