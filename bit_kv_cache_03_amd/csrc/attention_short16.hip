@@ -686,6 +686,11 @@ __device__ inline f16x8 v_operand(const Ctx &c, const uint32_t (&y)[8], int dt) 
 //
 // The lane's dims of k-step i: 32 i + 8 j + (e, e + 4) in word e.
 __device__ inline uint32_t kraw_dim0(int i, int j) { return static_cast<uint32_t>(32 * i + 8 * j); }
+// Unit of a raw code in its fp16 field, and so of the code products: INT4
+// codes sit at bits 0..3 (c 2^-24), INT2 codes at bits 8..9 (c 2^-16: one
+// byte permute and a mask per two codes, see stage_k_raw).
+template <int KBITS>
+constexpr float kRawUnit = KBITS == 4 ? 0x1p-24f : 0x1p-16f;
 // Eight bf16 values (one uint4, consecutive dims) to an fp16 operand in the
 // (e, e + 4) word order, scaled by sc.
 __device__ inline f16x8 kraw_pack(uint4 w, float sc) {
@@ -703,9 +708,9 @@ __device__ inline f16x8 kraw_pack(uint4 w, float sc) {
 // scaled by its own power of two 2^-eq; the extra step's slots on quarter
 // j < NG carry group j: N_j = tau/24 ||q_j||^2 2^-eq as (hi, hi, lo, 0) (zero
 // without the correction), then S_j = sum q 2^-eq as (hi, lo, hi, 0), both
-// times 2^-24, the unit of the code products (the scores' softmax scale is
-// alpha 2^24).
-template <bool TAYLOR, int NG>
+// times kRawUnit, the unit of the code products (the scores' softmax scale
+// is alpha / kRawUnit).
+template <bool TAYLOR, int NG, int KBITS>
 __device__ inline void load_query_kraw(const uint16_t *qptr, int lane, float tau, f16x8 (&q)[4], bf16x8 &qext,
                                        float &alpha, float &qun) {
   const int j = lane >> 4;
@@ -746,9 +751,9 @@ __device__ inline void load_query_kraw(const uint16_t *qptr, int lane, float tau
     ns = j == g ? nsum[g] : ns;
     ts = j == g ? qsum[g] : ts;
   }
-  const float n = TAYLOR ? ns * (tau / 24.0f) * qs_scale * 0x1p-24f : 0.f;
+  const float n = TAYLOR ? ns * (tau / 24.0f) * qs_scale * kRawUnit<KBITS> : 0.f;
   const float nh = lo_f(pack2(n, 0.f)), nl = n - nh;
-  const float t = ts * qs_scale * 0x1p-24f;
+  const float t = ts * qs_scale * kRawUnit<KBITS>;
   const float th = lo_f(pack2(t, 0.f)), tl = t - th;
   uint4 x = make_uint4(pack2(nh, nh), pack2(nl, 0.f), pack2(th, tl), pack2(th, 0.f));
   if (j >= NG) x = make_uint4(0u, 0u, 0u, 0u);
@@ -757,10 +762,10 @@ __device__ inline void load_query_kraw(const uint16_t *qptr, int lane, float tau
 
 // A cached block's key operands from the stage (codes at sk, steps at ks,
 // zero points at kz): k[t][i] = the codes of key 16t + r at the lane's dims
-// of k-step i as fp16 subnormals c 2^-24 (exact); kext[t] on quarter j < NG
+// of k-step i as fp16 subnormals c kRawUnit (exact); kext[t] on quarter j < NG
 // = group j's (-D^2 split hi, lo, hi; 0; z split into its bf16 truncation
 // z_h twice and z - z_h; 0) for the key; dk[t][g][i] = D of key 16t + 4j + i
-// in group g (the scores' layout).  The scores come out in units of 2^-24.
+// in group g (the scores' layout).  The scores come out in units of kRawUnit.
 template <bool TAYLOR, int KBITS, int NG, int MT>
 __device__ inline void stage_k_raw(const Ctx &c, const uint8_t *sk, const uint8_t *ks, const uint8_t *kz, int lane,
                                    f16x8 (&k)[2][4], bf16x8 (&kext)[2], float (&dk)[2][NG][4]) {
@@ -774,13 +779,17 @@ __device__ inline void stage_k_raw(const Ctx &c, const uint8_t *sk, const uint8_
       uint32_t x;
       if (KBITS == 4) {
         x = *reinterpret_cast<const uint32_t *>(row + kraw_dim0(i, j) / 2);
-      } else {  // the 16 bits of the lane's eight codes; code e + 4 moves next to code e, 16 bits up
-        const uint32_t w = *reinterpret_cast<const uint32_t *>(row + 8 * i + 4 * (j >> 1)) >> (16 * (j & 1));
-        x = (w & 0xffffu) | ((w & 0xffffu) << 8);
+      } else {
+        // the lane's 16-bit chunk (half j % 2 of the word): its low byte (codes
+        // 0..3) to byte 1, its high byte (codes 4..7) to byte 3, so that code e
+        // sits at bit 8 + 2e and code e + 4 at bit 24 + 2e
+        const uint32_t w = *reinterpret_cast<const uint32_t *>(row + 8 * i + 4 * (j >> 1));
+        const uint32_t b = 2u * static_cast<uint32_t>(j & 1);
+        x = __builtin_amdgcn_perm(w, w, 0x0cu | (b << 8) | (0x0cu << 16) | ((b + 1) << 24));
       }
       uint32_t m[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) m[e] = (x >> (KBITS * e)) & c.kmask;
+      for (int e = 0; e < 4; ++e) m[e] = (x >> (KBITS * e)) & (KBITS == 4 ? c.kmask : c.kmask << 8);
       k[t][i] = __builtin_bit_cast(f16x8, make_uint4(m[0], m[1], m[2], m[3]));
     }
     const int g = j < NG ? j : 0;
@@ -1179,7 +1188,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
   Soft st;
   float qun;
   if (KRAW)
-    load_query_kraw<TAYLOR, NG>(p.q + qrow * D, lane, p.tau, q, qext, st.alpha, qun);
+    load_query_kraw<TAYLOR, NG, KBITS>(p.q + qrow * D, lane, p.tau, q, qext, st.alpha, qun);
   else
     load_query<TAYLOR, NG>(p.q + qrow * D, lane, p.tau, q, qext, st.alpha, qun);
 #pragma unroll
@@ -1304,7 +1313,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
       if (!KRAW) unpack_k_cached<TAYLOR, KBITS, NG>(c, lane, f, sc.kscale, kreg, kext);
       unpack_v_raw<VBITS, NG, !PERM>(c, lane, f, sc.vscale, Vt, Ds, Zs);
       block_compute<TAYLOR || kCentre<NG> || KRAW, false, false, true, NG, PERM, PERM ? VBITS : 0, KRAW>(
-          kreg, kext, Vt, q, qext, count, KRAW ? st.alpha * 16777216.0f : sc.alpha, sc.ev, lane, st, 0.f, Ds, Zs, &c, &vy,
+          kreg, kext, Vt, q, qext, count, KRAW ? st.alpha / kRawUnit<KBITS> : sc.alpha, sc.ev, lane, st, 0.f, Ds, Zs, &c, &vy,
           &dk[0][0][0]);
     };
     for (;;) {
