@@ -631,40 +631,46 @@ __device__ inline int vrow(int dt, int r) {
   return PERM ? 64 * (dt >> 2) + 4 * r + (dt & 3) : 16 * dt + r;
 }
 
-// The lane's code pieces of its eight keys from the stage: y[i] holds the
-// piece of dims 4r .. 4r+3 in its low half and that of 64 + 4r .. in its
-// high half (INT4: two bytes each; INT2: one byte each, at bytes 0 and 2).
+// The lane's code words of its eight keys from the stage: y[i][0] the
+// 4-byte word holding the piece of dims 4r .. 4r+3 of key i (INT4: bytes
+// 2 (r % 2), +1 of it; INT2: byte r % 4), y[i][1] the word holding the piece of
+// dims 64 + 4r .. +3 (the same bytes, half a code row further).
 template <int VBITS>
-__device__ inline void stage_read_vcodes(const uint8_t *vc, int lane, uint32_t (&y)[8]) {
+__device__ inline void stage_read_vcodes(const uint8_t *vc, int lane, uint32_t (&y)[8][2]) {
   constexpr uint32_t VROW = D * VBITS / 8;
   const int r = lane & 15, j = lane >> 4;
-  const uint32_t sel = VBITS == 4 ? ((r & 1) ? 0x07060302u : 0x05040100u)
-                                  : static_cast<uint32_t>(r & 3) | 0x0c00u | (static_cast<uint32_t>(4 + (r & 3)) << 16) |
-                                        0x0c000000u;
   const uint32_t off = VBITS == 4 ? 4 * (r >> 1) : 4 * (r >> 2);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int key = i < 4 ? 4 * j + i : 16 + 4 * j + (i - 4);
     const uint8_t *row = vc + key * VROW + off;
-    const uint32_t lo = *reinterpret_cast<const uint32_t *>(row);
-    const uint32_t hi = *reinterpret_cast<const uint32_t *>(row + VROW / 2);
-    y[i] = __builtin_amdgcn_perm(hi, lo, sel);
+    y[i][0] = *reinterpret_cast<const uint32_t *>(row);
+    y[i][1] = *reinterpret_cast<const uint32_t *>(row + VROW / 2);
   }
 }
 
-// Tile dt's operand from the pieces: word w holds keys of slots 2w, 2w+1,
-// each as the fp16 subnormal of its code field (dim 4r + f of the tile's
-// half, f = dt % 4) at bit p: odd f sits at p = P1, like the odd rows of
-// unpack_v_raw.
+// Byte selector of v_operand for code byte fb of the lane's piece (INT4:
+// fb = 0, 1; INT2: 0): that byte of two keys' words to bits 0..7 and
+// 16..23.
 template <int VBITS>
-__device__ inline f16x8 v_operand(const Ctx &c, const uint32_t (&y)[8], int dt) {
+__device__ inline uint32_t vcode_sel(int lane, int fb) {
+  const int r = lane & 15;
+  const uint32_t b = static_cast<uint32_t>(VBITS == 4 ? 2 * (r & 1) + fb : (r & 3));
+  return b | 0x0c00u | ((4 + b) << 16) | 0x0c000000u;
+}
+
+// Tile dt's operand from the code words: word w holds keys of slots 2w,
+// 2w+1, each as the fp16 subnormal of its code field (dim 4r + f of the
+// tile's half h, f = dt % 4) at bit p: odd f sits at p = P1, like the odd
+// rows of unpack_v_raw.  sel[fb]: vcode_sel.
+template <int VBITS>
+__device__ inline f16x8 v_operand(const Ctx &c, const uint32_t (&y)[8][2], const uint32_t (&sel)[2], int dt) {
   const int h = dt >> 2, f = dt & 3;
-  const int b = VBITS == 4 ? 2 * h + (f >> 1) : 2 * h;
-  const uint32_t sel = static_cast<uint32_t>(b) | 0x0c00u | (static_cast<uint32_t>(4 + b) << 16) | 0x0c000000u;
+  const uint32_t sl = sel[VBITS == 4 ? (f >> 1) : 0];
   uint32_t w[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    uint32_t x = __builtin_amdgcn_perm(y[2 * e + 1], y[2 * e], sel);
+    uint32_t x = __builtin_amdgcn_perm(y[2 * e + 1][h], y[2 * e][h], sl);
     if (VBITS == 2 && f >= 2) x >>= 4;
     w[e] = x & ((f & 1) ? c.vmask1 : c.vmask0);
   }
@@ -1005,8 +1011,9 @@ __device__ inline void block_compute(const f16x8 (&k)[2][4], const bf16x8 (&kext
                                      const f16x8 (&q)[4], bf16x8 qext, int count, float alpha, int ev, int lane,
                                      Soft &st, float sadd = 0.f, const uint16_t *Ds = nullptr,
                                      const uint16_t *Zs = nullptr, const Ctx *c = nullptr,
-                                     const uint32_t (*vy)[8] = nullptr, const float *dk = nullptr) {
+                                     const uint32_t (*vy)[8][2] = nullptr, const float *dk = nullptr) {
   const float fev = static_cast<float>(ev);
+  const uint32_t vsel[2] = {VREG ? vcode_sel<VREG ? VREG : 4>(lane, 0) : 0u, VREG ? vcode_sel<VREG ? VREG : 4>(lane, 1) : 0u};
   const int r = lane & 15, j = lane >> 4;
   f32x4 s[2];
 #pragma unroll
@@ -1087,7 +1094,7 @@ __device__ inline void block_compute(const f16x8 (&k)[2][4], const bf16x8 (&kext
     for (int dt = 0; dt < D / 16; ++dt) {
       f16x8 a;
       if (VREG)
-        a = v_operand<VREG>(*c, *vy, dt);
+        a = v_operand<VREG>(*c, *vy, vsel, dt);
       else
         a = *reinterpret_cast<const f16x8 *>(Vt + vts(vrow<PERM>(dt, r), 8 * j));
       const int g = (vrow<PERM>(dt, 0) * NG) / D;
@@ -1303,7 +1310,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_short16_kernel(AttnLaunch p, 
       const int count = c.nc - k0 < BK ? c.nc - k0 : BK;
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(SL::LOADS) : "memory");
       stage_read<KBITS, VBITS, NG, MT, !PERM, !KRAW>(stg, lo, f);
-      uint32_t vy[8];
+      uint32_t vy[8][2];
       if (PERM) stage_read_vcodes<VBITS>(stg + SL::KC, lane, vy);
       float dk[2][NG][4];
       if (KRAW) stage_k_raw<TAYLOR, KBITS, NG, MT>(c, stg, stg + SL::KS, stg + SL::KZ, lane, kreg, kext, dk);
